@@ -1,0 +1,259 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module only draws random numbers and lays them out in the cache formats the
+library consumes. It holds none of the attention, softmax, planning, RMSNorm or
+rotary arithmetic; both the HIP path and the fp64 oracle read what it produces.
+Value encodings (fp32 -> bf16, fp32 -> OCP E4M3) are delegated to PyTorch's own
+dtype casts, so no rounding rule is restated here.
+
+Layouts (little-endian bit patterns held in numpy integer arrays):
+
+* ``q``        uint16 bf16 bits, ``[B, Hq, D]``
+* ``k_cache``  ``[num_pages, Hkv, 64, D]``  (token-major inside a page)
+* ``v_cache``  ``[num_pages, Hkv, D, 64]``  (dim-major inside a page)
+  uint16 bf16 bits, or uint8 OCP E4M3 codes with per-KV-head fp32 scales
+* ``page_table`` int32 ``[B, max_pages]``; entries past a request's pages are -1
+* ``seq_lens`` int32 ``[B]`` live KV length of each request (for workloads with
+  the fused prologue: the length before the new token is appended)
+
+Draw order for one workload (one fresh ``numpy.random.default_rng(seed)``):
+lengths (one vectorised call of size B, when drawn) -> page permutation -> q ->
+K -> V -> (new q, new k, new v, q-norm weight, k-norm weight). K and V are drawn
+in their token-major shape, in chunks of ``_CHUNK_PAGES`` pages, as standard
+normal float32; V is transposed to dim-major per page after drawing.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+PAGE = 64
+HEAD_DIM = 128
+_CHUNK_PAGES = 1024
+BF16_NAN = 0x7FC0
+E4M3_NAN = 0x7F
+E4M3_MAX = 448.0
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    batch: int
+    hq: int
+    hkv: int
+    kv_dtype: str                  # "bf16" or "fp8"
+    seq_lens: np.ndarray           # int32 [B]
+    page_table: np.ndarray         # int32 [B, max_pages]
+    num_pages: int
+    q: np.ndarray                  # uint16 [B, Hq, D]
+    k_cache: np.ndarray            # uint16|uint8 [P, Hkv, 64, D]
+    v_cache: np.ndarray            # uint16|uint8 [P, Hkv, D, 64]
+    k_scale: Optional[np.ndarray] = None   # float32 [Hkv] (fp8 only)
+    v_scale: Optional[np.ndarray] = None
+    sm_scale: float = float(np.float32(1.0 / math.sqrt(HEAD_DIM)))
+    # fused-prologue inputs (None when the workload has no prologue)
+    q_new: Optional[np.ndarray] = None     # uint16 [B, Hq, D]
+    k_new: Optional[np.ndarray] = None     # uint16 [B, Hkv, D]
+    v_new: Optional[np.ndarray] = None     # uint16 [B, Hkv, D]
+    q_norm_w: Optional[np.ndarray] = None  # float32 [D]
+    k_norm_w: Optional[np.ndarray] = None  # float32 [D]
+    eps: float = 1e-6
+    rope_theta: float = 1e6
+    seed: int = 0
+
+    @property
+    def head_dim(self) -> int:
+        return HEAD_DIM
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.page_table.shape[1])
+
+    @property
+    def has_prologue(self) -> bool:
+        return self.q_new is not None
+
+    def attended_lens(self) -> np.ndarray:
+        """Tokens attention covers: the live length, plus one when a token is appended."""
+        return self.seq_lens + (1 if self.has_prologue else 0)
+
+    def kv_bytes(self) -> int:
+        """Bytes of valid K and V tokens (padding rows excluded)."""
+        e = 2 if self.kv_dtype == "bf16" else 1
+        return int(self.attended_lens().astype(np.int64).sum()) * self.hkv * 2 * HEAD_DIM * e
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (PyTorch's round-to-nearest-even cast)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """float32 already within [-448, 448] -> OCP E4M3 codes (PyTorch's float8_e4m3fn cast)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(np.clip(x, -E4M3_MAX, E4M3_MAX), dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _draw_pool(rng, num_pages, hkv):
+    """Standard normal float32 [num_pages, hkv, 64, D], drawn in page chunks."""
+    out = np.empty((num_pages, hkv, PAGE, HEAD_DIM), np.float32)
+    for p0 in range(0, num_pages, _CHUNK_PAGES):
+        n = min(_CHUNK_PAGES, num_pages - p0)
+        out[p0:p0 + n] = rng.standard_normal((n, hkv, PAGE, HEAD_DIM), dtype=np.float32)
+    return out
+
+
+def _draw_pool_bf16(rng, num_pages, hkv, transpose):
+    out_shape = (num_pages, hkv, HEAD_DIM, PAGE) if transpose else (num_pages, hkv, PAGE, HEAD_DIM)
+    out = np.empty(out_shape, np.uint16)
+    for p0 in range(0, num_pages, _CHUNK_PAGES):
+        n = min(_CHUNK_PAGES, num_pages - p0)
+        x = rng.standard_normal((n, hkv, PAGE, HEAD_DIM), dtype=np.float32)
+        bits = bf16_bits(x)
+        out[p0:p0 + n] = bits.transpose(0, 1, 3, 2) if transpose else bits
+    return out
+
+
+def build_workload(name: str, seq_lens, hq: int, hkv: int, kv_dtype: str = "bf16",
+                   seed: int = 0, rng=None, pool_pages: Optional[int] = None,
+                   poison: bool = False, prologue: bool = False) -> Workload:
+    """Lay out a paged KV cache for the given live lengths.
+
+    ``rng`` continues an existing generator (lengths already drawn from it);
+    otherwise a fresh ``default_rng(seed)`` is used. Pages are handed to requests
+    in request order from one random permutation of the pool. With
+    ``prologue=True`` every request also owns the page its new token lands in.
+    With ``poison=True`` every padding slot and unused page holds NaN.
+    """
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    B = int(seq_lens.shape[0])
+    assert kv_dtype in ("bf16", "fp8")
+    assert hq % hkv == 0
+    owned = seq_lens + (1 if prologue else 0)
+    npages = (owned + PAGE - 1) // PAGE
+    used = int(npages.sum())
+    num_pages = used if pool_pages is None else int(pool_pages)
+    assert num_pages >= used
+    max_pages = max(1, int(npages.max()) if B else 1)
+
+    perm = rng.permutation(num_pages).astype(np.int32)
+    page_table = np.full((B, max_pages), -1, np.int32)
+    off = 0
+    for b in range(B):
+        n = int(npages[b])
+        page_table[b, :n] = perm[off:off + n]
+        off += n
+
+    q = bf16_bits(rng.standard_normal((B, hq, HEAD_DIM), dtype=np.float32))
+    k_scale = v_scale = None
+    if kv_dtype == "bf16":
+        k_cache = _draw_pool_bf16(rng, num_pages, hkv, transpose=False)
+        v_cache = _draw_pool_bf16(rng, num_pages, hkv, transpose=True)
+    else:
+        kf = _draw_pool(rng, num_pages, hkv)
+        vf = _draw_pool(rng, num_pages, hkv)
+        # one scale per KV head, fixed when the cache is built: amax / 448
+        k_scale = (np.abs(kf).max(axis=(0, 2, 3)) / E4M3_MAX).astype(np.float32)
+        v_scale = (np.abs(vf).max(axis=(0, 2, 3)) / E4M3_MAX).astype(np.float32)
+        k_cache = np.empty(kf.shape, np.uint8)
+        v_cache = np.empty((num_pages, hkv, HEAD_DIM, PAGE), np.uint8)
+        for p0 in range(0, num_pages, _CHUNK_PAGES):
+            sl = slice(p0, min(num_pages, p0 + _CHUNK_PAGES))
+            k_cache[sl] = e4m3_codes(kf[sl] / k_scale[None, :, None, None])
+            v_cache[sl] = e4m3_codes(vf[sl] / v_scale[None, :, None, None]).transpose(0, 1, 3, 2)
+        del kf, vf
+
+    w = Workload(name=name, batch=B, hq=hq, hkv=hkv, kv_dtype=kv_dtype,
+                 seq_lens=seq_lens.astype(np.int32), page_table=page_table, num_pages=num_pages,
+                 q=q, k_cache=k_cache, v_cache=v_cache, k_scale=k_scale, v_scale=v_scale, seed=seed)
+    if prologue:
+        w.q_new = bf16_bits(rng.standard_normal((B, hq, HEAD_DIM), dtype=np.float32))
+        w.k_new = bf16_bits(rng.standard_normal((B, hkv, HEAD_DIM), dtype=np.float32))
+        w.v_new = bf16_bits(rng.standard_normal((B, hkv, HEAD_DIM), dtype=np.float32))
+        w.q_norm_w = rng.uniform(0.5, 1.5, HEAD_DIM).astype(np.float32)
+        w.k_norm_w = rng.uniform(0.5, 1.5, HEAD_DIM).astype(np.float32)
+    if poison:
+        poison_padding(w)
+    return w
+
+
+def poison_padding(w: Workload) -> None:
+    """Fill every KV slot no request may read (padding rows, unused pages) with NaN.
+
+    For a workload with a prologue the append slot counts as padding too: the
+    prologue must overwrite it before attention reads it.
+    """
+    nan = BF16_NAN if w.kv_dtype == "bf16" else E4M3_NAN
+    used = np.zeros(w.num_pages, bool)
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        n = (L + (1 if w.has_prologue else 0) + PAGE - 1) // PAGE
+        pages = w.page_table[b, :n]
+        used[pages] = True
+        if n == 0:
+            continue
+        last = int(pages[-1])
+        valid_in_last = L - (n - 1) * PAGE       # may be 0..64 (0: new token starts the page)
+        if valid_in_last < PAGE:
+            w.k_cache[last, :, valid_in_last:, :] = nan
+            w.v_cache[last, :, :, valid_in_last:] = nan
+    w.k_cache[~used] = nan
+    w.v_cache[~used] = nan
+
+
+# --- the five workloads -----------------------------------------------------
+
+CONFIG_NAMES = {
+    0: "tiny: B=4 lens{37,64,200,513} Hq8:Hkv1 D128 page64 bf16, pool 16 pages",
+    1: "uniform: B=64 x 512 Hq8:Hkv1 D128 page64 bf16",
+    2: "skewed: B=32 1x131072+31x4096 Hq8:Hkv1 D128 page64 bf16",
+    3: "mix: B=32 log-uniform[1024,65536] Hq32:Hkv4 D128 page64 bf16",
+    4: "fp8+prologue: B=128 lognormal(8192,1)[128,131072] Hq8:Hkv1 D128 page64 e4m3",
+}
+
+
+def config_lengths(index: int, rng) -> np.ndarray:
+    if index == 0:
+        return np.array([37, 64, 200, 513], np.int64)
+    if index == 1:
+        return np.full(64, 512, np.int64)
+    if index == 2:
+        return np.array([131072] + [4096] * 31, np.int64)
+    if index == 3:
+        u = rng.uniform(math.log(1024), math.log(65536), size=32)
+        return np.clip(np.rint(np.exp(u)), 1024, 65536).astype(np.int64)
+    if index == 4:
+        x = rng.lognormal(mean=math.log(8192), sigma=1.0, size=128)
+        return np.clip(np.rint(x), 128, 131072).astype(np.int64)
+    raise ValueError(f"no workload {index}")
+
+
+def config_workload(index: int, seed: int = 0, poison: bool = False) -> Workload:
+    rng = np.random.default_rng(seed)
+    lens = config_lengths(index, rng)
+    if index == 0:
+        return build_workload("cfg0_tiny", lens, 8, 1, "bf16", seed, rng, pool_pages=16, poison=poison)
+    if index == 1:
+        return build_workload("cfg1_uniform", lens, 8, 1, "bf16", seed, rng, poison=poison)
+    if index == 2:
+        return build_workload("cfg2_skewed", lens, 8, 1, "bf16", seed, rng, poison=poison)
+    if index == 3:
+        return build_workload("cfg3_mix", lens, 32, 4, "bf16", seed, rng, poison=poison)
+    if index == 4:
+        return build_workload("cfg4_fp8_prologue", lens, 8, 1, "fp8", seed, rng,
+                              poison=poison, prologue=True)
+    raise ValueError(index)
+
+
+def config_lengths_only(index: int, seed: int = 0) -> np.ndarray:
+    """The lengths a workload would draw, without building its cache."""
+    return config_lengths(index, np.random.default_rng(seed))

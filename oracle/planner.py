@@ -1,0 +1,124 @@
+"""Work partitions of split-KV decode attention, as plain integer Python.
+
+TEST INFRASTRUCTURE ONLY (see the package header).
+
+Balanced plan -- xiaodao.ai "HPC-Ops 把 TPOT 降 48.8%，用户未必快一半", section
+"为什么 batch 越大，数字越漂亮": each request's live KV is cut into 64-token tiles
+and the global tile list is spread as evenly as possible over persistent
+workers, so long sequences get more work and short ones only what they have;
+bitbyai.com "vLLM × HPC-Ops: …", section "Breaking Down the Kernels": the
+schedule is recomputed every decode step from the live lengths.
+
+Readings taken where the pages are silent (all integer, so the GPU planner
+must reproduce them bit for bit):
+
+* sequence s = b * Hkv + g (request-major); n_s = ceil(L_b / 64) tiles;
+  C = exclusive prefix sum of n_s; N = C[S].
+* "as evenly as possible" = contiguous floor partition of the global tile
+  list: W' = 0 if N == 0 else min(W, max(1, N // min_tiles)); worker w owns
+  global tiles [w*N // W', (w+1)*N // W') (64-bit products).
+* a worker's range is cut at sequence boundaries into items (s, t0, t1) in
+  sequence order; items are listed worker by worker.
+* split(item) = rank of the item among the items of its sequence;
+  num_splits[s] = number of such items; sequences with more than one item get
+  consecutive partial slots partial_base[s] + split, where partial_base is
+  the exclusive prefix sum of (num_splits if num_splits > 1 else 0); items of
+  unsplit sequences have slot -1 (they write the output directly).
+* merge_list = sequences whose num_splits != 1 (split ones are combined,
+  empty ones get a zero output row), in increasing s.
+
+Static split-KV (the comparison the pages describe in the same section):
+flavour "splits" fixes the number of splits per sequence,
+S_split = clamp(ceil(W / S), 1, max_pages), chunk_s = ceil(n_s / S_split);
+flavour "chunk" fixes the split size from the longest request the page table
+can hold, chunk = ceil(max_pages / S_split), and reserves S_split slots for
+every sequence (short ones carry empty tasks). Partial slot = s * S_split + k
+when a sequence has more than one non-empty chunk.
+
+Parity pins (tests/test_oracle_planner.py): a hand-derived plan for the tiny
+workload (tests/golden/plan_tiny_w4.json); a brute-force tile-by-tile
+construction on random small cases; coverage, balance and slot properties.
+"""
+
+PAGE = 64
+
+
+def tile_counts(seq_lens, hkv):
+    return [(int(L) + PAGE - 1) // PAGE for L in seq_lens for _ in range(hkv)]
+
+
+def active_workers(N, num_workers, min_tiles):
+    if N == 0:
+        return 0
+    return min(num_workers, max(1, N // min_tiles))
+
+
+def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1):
+    n = tile_counts(seq_lens, hkv)
+    S = len(n)
+    C = [0] * (S + 1)
+    for s in range(S):
+        C[s + 1] = C[s] + n[s]
+    N = C[S]
+    Wp = active_workers(N, num_workers, min_tiles)
+
+    items = []                                   # (worker, s, t0, t1)
+    worker_off = [0]
+    for w in range(Wp):
+        a = w * N // Wp
+        e = (w + 1) * N // Wp
+        s = 0
+        while not (C[s] <= a < C[s + 1]):
+            s += 1
+        while a < e:
+            t1 = min(e, C[s + 1])
+            items.append((w, s, a - C[s], t1 - C[s]))
+            a = t1
+            s += 1
+            while a < e and n[s] == 0:
+                s += 1
+        worker_off.append(len(items))
+
+    num_splits = [0] * S
+    split = []
+    for _, s, _, _ in items:
+        split.append(num_splits[s])
+        num_splits[s] += 1
+    partial_base = [0] * S
+    acc = 0
+    for s in range(S):
+        partial_base[s] = acc
+        if num_splits[s] > 1:
+            acc += num_splits[s]
+    slots = [partial_base[s] + k if num_splits[s] > 1 else -1
+             for (_, s, _, _), k in zip(items, split)]
+    return dict(
+        C=C, N=N, S=S, Wp=Wp, n_items=len(items), worker_off=worker_off,
+        item_s=[it[1] for it in items], item_t0=[it[2] for it in items],
+        item_t1=[it[3] for it in items], item_split=split, item_slot=slots,
+        num_splits=num_splits, partial_base=partial_base, n_partials=acc,
+        merge_list=[s for s in range(S) if num_splits[s] != 1],
+    )
+
+
+def static_splits(num_seqs, num_workers, max_pages):
+    return max(1, min(-(-num_workers // max(num_seqs, 1)), max_pages))
+
+
+def static_partition(seq_lens, hkv, num_workers, max_pages, flavour="splits"):
+    """Items (s, k, t0, t1, slot) of the static split-KV schedule."""
+    n = tile_counts(seq_lens, hkv)
+    S = len(n)
+    ss = static_splits(S, num_workers, max_pages)
+    fixed_chunk = -(-max_pages // ss)
+    items = []
+    for s in range(S):
+        if n[s] == 0:
+            continue
+        chunk = -(-n[s] // ss) if flavour == "splits" else fixed_chunk
+        nchunks = -(-n[s] // chunk)
+        for k in range(ss):
+            t0, t1 = k * chunk, min((k + 1) * chunk, n[s])
+            if t0 < t1:
+                items.append((s, k, t0, t1, s * ss + k if nchunks > 1 else -1))
+    return dict(S_split=ss, items=items)

@@ -1,0 +1,143 @@
+"""Pins of the CPU planner: a hand-worked plan, brute force over tiles, properties."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import planner as op
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_hand_worked_tiny_plan():
+    g = json.load(open(os.path.join(GOLDEN, "plan_tiny_w4.json")))
+    p = op.balanced_plan(g["seq_lens"], g["hkv"], g["num_workers"], g["min_tiles"])
+    for key in ("C", "N", "Wp", "worker_off", "item_s", "item_t0", "item_t1", "item_split",
+                "item_slot", "num_splits", "partial_base", "n_partials", "merge_list"):
+        assert p[key] == g[key], key
+
+
+def brute_force_plan(seq_lens, hkv, W, min_tiles):
+    """Enumerate global tiles one by one: owner worker by scanning the worker
+    boundaries, owner sequence by scanning the sequence boundaries, then group."""
+    seqs = []
+    for b, L in enumerate(seq_lens):
+        for g in range(hkv):
+            seqs.append(-(-int(L) // 64))
+    N = sum(seqs)
+    if N == 0:
+        return []
+    Wp = min(W, max(1, N // min_tiles))
+    bounds = [w * N // Wp for w in range(Wp + 1)]
+    groups = {}
+    k = 0
+    for s, n in enumerate(seqs):
+        for t in range(n):
+            w = max(i for i in range(Wp) if bounds[i] <= k)
+            groups.setdefault((w, s), []).append(t)
+            k += 1
+    return [(w, s, ts[0], ts[-1] + 1) for (w, s), ts in sorted(groups.items())]
+
+
+def test_against_brute_force_random():
+    rng = np.random.default_rng(0)
+    for trial in range(300):
+        B = int(rng.integers(1, 9))
+        hkv = int(rng.integers(1, 4))
+        lens = rng.choice([0, 1, 63, 64, 65, 127, 128, 129, 500, 1000], size=B)
+        W = int(rng.integers(1, 40))
+        mt = int(rng.integers(1, 4))
+        p = op.balanced_plan(lens, hkv, W, mt)
+        items = []
+        for w in range(p["Wp"]):
+            for i in range(p["worker_off"][w], p["worker_off"][w + 1]):
+                items.append((w, p["item_s"][i], p["item_t0"][i], p["item_t1"][i]))
+        assert items == brute_force_plan(lens, hkv, W, mt)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_plan_properties(seed):
+    rng = np.random.default_rng(seed)
+    for trial in range(200):
+        B = int(rng.integers(0, 40))
+        hkv = int(rng.integers(1, 5))
+        lens = rng.integers(0, 5000, size=B)
+        lens[rng.random(B) < 0.2] = 0
+        W = int(rng.integers(1, 600))
+        mt = int(rng.integers(1, 9))
+        p = op.balanced_plan(lens, hkv, W, mt)
+        N, Wp = p["N"], p["Wp"]
+        n = op.tile_counts(lens, hkv)
+        assert N == sum(n)
+        if N == 0:
+            assert Wp == 0 and p["n_items"] == 0
+            continue
+        assert 1 <= Wp <= W and (Wp == 1 or N // Wp >= mt or Wp == W)
+        # every (s, tile) covered exactly once
+        cover = [np.zeros(x, int) for x in n]
+        for s, t0, t1 in zip(p["item_s"], p["item_t0"], p["item_t1"]):
+            assert 0 <= t0 < t1 <= n[s]
+            cover[s][t0:t1] += 1
+        assert all((c == 1).all() for c in cover)
+        # per-worker load differs by at most one tile
+        loads = [sum(p["item_t1"][i] - p["item_t0"][i] for i in range(p["worker_off"][w], p["worker_off"][w + 1]))
+                 for w in range(Wp)]
+        assert set(loads) <= {N // Wp, -(-N // Wp)}
+        # items of a sequence: consecutive ranks, contiguous tiles, consecutive slots
+        per_seq = {}
+        for i, s in enumerate(p["item_s"]):
+            per_seq.setdefault(s, []).append(i)
+        slots = []
+        for s, idx in per_seq.items():
+            assert [p["item_split"][i] for i in idx] == list(range(len(idx)))
+            assert p["num_splits"][s] == len(idx)
+            assert p["item_t0"][idx[0]] == 0 and p["item_t1"][idx[-1]] == n[s]
+            for a, b in zip(idx[:-1], idx[1:]):
+                assert p["item_t1"][a] == p["item_t0"][b]
+            if len(idx) == 1:
+                assert p["item_slot"][idx[0]] == -1
+            else:
+                sl = [p["item_slot"][i] for i in idx]
+                assert sl == list(range(p["partial_base"][s], p["partial_base"][s] + len(idx)))
+                slots += sl
+        assert sorted(slots) == list(range(p["n_partials"]))
+        assert p["n_items"] <= Wp + len(n)
+        assert p["merge_list"] == [s for s in range(len(n)) if p["num_splits"][s] != 1]
+
+
+@pytest.mark.parametrize("flavour", ["splits", "chunk"])
+def test_static_partition_covers_every_tile(flavour):
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        B = int(rng.integers(1, 20))
+        hkv = int(rng.integers(1, 3))
+        lens = rng.integers(0, 3000, size=B)
+        maxp = max(1, int(-(-lens.max() // 64)))
+        W = int(rng.integers(1, 300))
+        p = op.static_partition(lens, hkv, W, maxp, flavour)
+        n = op.tile_counts(lens, hkv)
+        cover = [np.zeros(x, int) for x in n]
+        nslot = {}
+        for s, k, t0, t1, slot in p["items"]:
+            assert k < p["S_split"]
+            cover[s][t0:t1] += 1
+            nslot.setdefault(s, []).append(slot)
+        assert all((c == 1).all() for c in cover)
+        for s, sl in nslot.items():
+            assert (sl == [-1]) if len(sl) == 1 else all(x >= 0 for x in sl)
+
+
+def test_skewed_workload_static_vs_balanced_shape():
+    """1 x 131072 + 31 x 4096 tokens, 512 workers: the balanced plan gives every
+    worker 7 or 8 tiles, the static one leaves the long request's 16 chunks at
+    128 tiles each -- the long tail the pages describe."""
+    lens = [131072] + [4096] * 31
+    p = op.balanced_plan(lens, 1, 512, 1)
+    loads = [sum(p["item_t1"][i] - p["item_t0"][i] for i in range(p["worker_off"][w], p["worker_off"][w + 1]))
+             for w in range(p["Wp"])]
+    assert p["N"] == 4032 and max(loads) == 8 and min(loads) == 7
+    st = op.static_partition(lens, 1, 512, 2048, "splits")
+    assert st["S_split"] == 16
+    assert max(t1 - t0 for _, _, t0, t1, _ in st["items"]) == 128
