@@ -1,0 +1,251 @@
+"""Benchmark: load-balanced split-KV decode attention on one MI355X.
+
+A step is the whole hot path over one batch resident in HBM: plan -> attention
+-> merge (plus the fused prologue for the E4M3 workload). The default workload
+is the skewed batch (1 x 131072 + 31 x 4096 tokens, 8:1 GQA, head dim 128,
+64-token pages, bf16 KV), where the pages report their kernel-level gain.
+
+Timing:
+* headline: K steps replayed from HIP graphs, back to back, bracketed by a
+  device synchronise; the batch is held in R copies used round-robin so that
+  R - 1 other copies (more than twice the 256 MB Infinity Cache) are read
+  between two uses of the same bytes -- each step reads its KV from HBM.
+* per kernel: a second pass where each step follows a 1 GiB scratch overwrite
+  (cache flush; it also lets the host run ahead) and HIP events on the launch
+  stream bracket the planner, the attention kernel and the merge kernel.
+* comparison: the same two passes for the static split-KV schedules.
+* CPU baseline: the fp64 oracle timed on the host on the same batch.
+
+Prints ONE JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn μs/step + achieved KV-read HBM GB/s (% of peak), mixed-length batch"
+PEAK_HBM_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", type=int, default=2, help="0..4 (2 = skewed 1x128K + 31x4K)")
+    p.add_argument("--num-workers", type=int, default=0)
+    p.add_argument("--event-steps", type=int, default=30)
+    p.add_argument("--no-static", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move per step (valid tokens only): KV + q + out +
+    page ids + lengths (+ scales); the prologue's reads and writes on top."""
+    from load_balanced_split_amd.inputs import HEAD_DIM
+    kv = w.kv_bytes()
+    lens = w.attended_lens().astype(np.int64)
+    pages = int(((lens + 63) // 64).sum())
+    other = 2 * w.batch * w.hq * HEAD_DIM * 2 + pages * 4 + w.batch * 4
+    if w.kv_dtype == "fp8":
+        other += 8 * w.hkv
+    pro = 0
+    if w.has_prologue:
+        pro = w.batch * (w.hq + 2 * w.hkv) * HEAD_DIM * 2 + w.batch * 2 * w.hkv * HEAD_DIM + 2 * HEAD_DIM * 4
+    return kv, kv + other, pro
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU, "
+              "see the sharding note in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from load_balanced_split_amd import _lib, inputs
+    from load_balanced_split_amd.runner import DeviceStep
+
+    assert torch.cuda.is_available(), "no GPU"
+    _lib.lib()                               # fails loudly if libhpa.so is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W = args.num_workers or _lib.hpa_default_num_workers(0)
+
+    w = inputs.config_workload(args.workload)
+    kv_bytes, alg_bytes, pro_bytes = algorithmic_bytes(w)
+    pool_bytes = w.k_cache.nbytes + w.v_cache.nbytes
+    R = max(2, math.ceil(2 * MALL_BYTES / max(pool_bytes, 1)) + 1)
+    R = min(R, 16)
+    copies = [DeviceStep(w, num_workers=W, device="cuda:0") for _ in range(R)]
+    print(f"[bench] workload {args.workload} ({w.name}): KV {kv_bytes / 1e6:.1f} MB, {R} copies, W={W}",
+          file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    def run_step(d, sched):
+        d.step(sched)
+
+    # eager reference outputs (also the warm-up of every code path)
+    scheds = ["balanced"] + ([] if args.no_static else ["static_splits", "static_chunk"])
+    eager = {}
+    for s in scheds:
+        for d in copies:
+            run_step(d, s)
+        torch.cuda.synchronize()
+        eager[s] = copies[0].out.clone()
+        assert copies[0].device_error() == 0
+
+    def graph_time(sched):
+        graphs = []
+        for d in copies:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(d, sched)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        # every copy's graph output equals the eager output, bit for bit
+        for d in copies:
+            assert torch.equal(d.out, eager[sched]), f"graph replay of {sched} differs from eager"
+        del graphs
+        return (t1 - t0) / args.steps
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def event_time(sched):
+        """Per-kernel durations (ms) after a cache flush, from events on the launch stream."""
+        res = {"prologue": [], "plan": [], "attn": [], "merge": [], "step": []}
+        for i in range(args.event_steps):
+            d = copies[i % R]
+            flush.fill_(i & 0xFF)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            ev[0].record(stream)
+            if w.has_prologue:
+                d.prologue()
+            ev[1].record(stream)
+            if sched == "balanced":
+                d.plan()
+            ev[2].record(stream)
+            d.attend(sched, flags=_lib.ATTN_NO_MERGE)
+            ev[3].record(stream)
+            d.attend(sched, flags=_lib.ATTN_MERGE_ONLY)
+            ev[4].record(stream)
+            torch.cuda.synchronize()
+            res["prologue"].append(ev[0].elapsed_time(ev[1]))
+            res["plan"].append(ev[1].elapsed_time(ev[2]))
+            res["attn"].append(ev[2].elapsed_time(ev[3]))
+            res["merge"].append(ev[3].elapsed_time(ev[4]))
+            res["step"].append(ev[0].elapsed_time(ev[4]))
+            assert torch.equal(d.out, eager[sched])
+        return {k: float(np.mean(v)) for k, v in res.items()}
+
+    # balanced (the method) -- headline
+    step_s = graph_time("balanced")
+    ev = event_time("balanced")
+    us = step_s * 1e6
+    kv_gbps = kv_bytes / step_s / 1e9
+    attn_s = ev["attn"] * 1e-3
+    achieved = alg_bytes / attn_s / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(kv_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 q/out",
+        "data": "synthetic (seeded; shapes and length mix of the pages' kernel benchmark)",
+        "config": {"workload": inputs.CONFIG_NAMES[args.workload], "schedule": "balanced",
+                   "num_workers": W, "rotating_copies": R, "kv_bytes": kv_bytes,
+                   "algorithmic_bytes": alg_bytes},
+        "us_per_step": round(us, 2),
+        "kv_frac_of_peak": round(kv_gbps / PEAK_HBM_GBPS, 4),
+        "kernels_us_cold": {k: round(v * 1e3, 2) for k, v in ev.items()},
+        "attn_plus_merge_kv_gbps_cold": round(kv_bytes / ((ev["attn"] + ev["merge"]) * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "attn_balanced_kernel<bf16>" if w.kv_dtype == "bf16"
+                     else "attn_balanced_kernel<fp8>",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None},
+    }
+    if pro_bytes:
+        result["config"]["prologue_bytes"] = pro_bytes
+    if not args.no_static:
+        st = {}
+        for s in scheds[1:]:
+            t = graph_time(s)
+            e = event_time(s)
+            st[s] = {"us_per_step": round(t * 1e6, 2), "attn_us_cold": round(e["attn"] * 1e3, 2),
+                     "merge_us_cold": round(e["merge"] * 1e3, 2),
+                     "balanced_speedup": round(t / step_s, 3)}
+        result["static_split_kv"] = st
+    # measured read bandwidth of a plain reduction over 4 GiB (context for the 8 TB/s peak)
+    x = torch.empty(1 << 31, dtype=torch.bfloat16, device=dev).fill_(1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    x.sum()
+    e0.record()
+    for _ in range(5):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    result["stream_read_gbps_measured"] = round(5 * x.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del x
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, kv_bytes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, kv_bytes, budget_s):
+    """The fp64 oracle, as it stands, on the host cores over the same batch."""
+    import threadpoolctl
+    from oracle import attention as oa
+    from oracle import prologue as opro
+
+    def once():
+        if w.has_prologue:
+            pr = opro.prologue(w)
+            oa.decode_attention(pr["q_rot"], pr["k_cache"], pr["v_cache"], pr["seq_lens"], w.page_table, w.hkv,
+                                w.sm_scale, w.kv_dtype, w.k_scale, w.v_scale)
+        else:
+            oa.decode_attention(w.q, w.k_cache, w.v_cache, w.seq_lens, w.page_table, w.hkv, w.sm_scale,
+                                w.kv_dtype, w.k_scale, w.v_scale)
+
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        once()
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end or len(times) >= 50:
+            break
+    t = float(np.median(times))
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    return {"value": round(kv_bytes / t / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "us_per_step": round(t * 1e6, 1),
+            "sample": f"the whole batch, {len(times)} runs (median), numpy fp64 gather-then-softmax"}
+
+
+if __name__ == "__main__":
+    main()

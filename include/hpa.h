@@ -1,0 +1,170 @@
+/*
+ * hpa.h -- C ABI of libhpa: load-balanced split-KV decode attention over a
+ * paged KV cache, for MI355X (gfx950).
+ *
+ * The method (xiaodao.ai, "HPC-Ops 把 TPOT 降 48.8%，用户未必快一半", section
+ * "为什么 batch 越大，数字越漂亮"; bitbyai.com, "vLLM × HPC-Ops: High-Performance
+ * Attention and MoE Backends from Tencent Hunyuan", section "Breaking Down the
+ * Kernels"): each decode step, cut every request's live KV into 64-token
+ * tiles, spread the global tile list evenly over persistent workers, let each
+ * worker produce softmax partials (acc, m, l) for the ranges it owns and merge
+ * split sequences with a log-sum-exp combine. A static split-KV schedule is
+ * provided for comparison, and a fused prologue (q/k RMSNorm, RoPE, paged KV
+ * append) that runs ahead of attention.
+ *
+ * Conventions for every call:
+ *  - Tensors are caller-owned device memory; the library allocates nothing.
+ *    Workspace sizes come from the *_workspace_size queries.
+ *  - Calls are asynchronous on the given stream and never synchronise, except
+ *    hpa_read_device_error and hpa_default_num_workers (device query, cached).
+ *  - Host-side validation failures return a non-OK status and launch nothing.
+ *  - Device-side data errors (a length < 0 or beyond the page table, a page id
+ *    outside [0, num_pages)) OR a bit into the sticky error word held in the
+ *    plan workspace; the offending work is skipped (its output is undefined).
+ *  - No C++ exception crosses this boundary. All entry points are thread-safe.
+ *
+ * Layouts (row-major, innermost last):
+ *  q, q_out        [B, Hq, 128]                    bf16
+ *  out             [B, Hq, 128]                    bf16
+ *  k_cache         [num_pages, Hkv, 64, 128]       bf16 or OCP E4M3 codes (token-major page)
+ *  v_cache         [num_pages, Hkv, 128, 64]       bf16 or OCP E4M3 codes (dim-major page)
+ *  k_scale,v_scale [Hkv]                           fp32 (E4M3 caches only; value = code * scale)
+ *  seq_lens        [B]                             int32, live KV length per request
+ *  page_table      [B, max_pages_per_seq]          int32 physical page of each 64-token tile
+ * Query head h reads KV head h / (Hq / Hkv). Sequence s = b * Hkv + g.
+ */
+#ifndef HPA_H
+#define HPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HPA_OK = 0,
+  HPA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, Hq % Hkv != 0, ... */
+  HPA_ERR_UNSUPPORTED = 2,  /* head_dim != 128, page_size != 64, Hq/Hkv > 16 */
+  HPA_ERR_WORKSPACE = 3,    /* workspace smaller than the size query returns */
+  HPA_ERR_DEVICE = 4,       /* a HIP runtime call failed */
+  HPA_ERR_LAUNCH = 5        /* a kernel launch failed */
+} hpa_status;
+
+typedef enum { HPA_KV_BF16 = 0, HPA_KV_FP8_E4M3 = 1 } hpa_kv_dtype;
+
+typedef enum {
+  HPA_SCHED_BALANCED = 0,      /* work list from hpa_plan (persistent workers) */
+  HPA_SCHED_STATIC_SPLITS = 1, /* fixed number of splits per sequence          */
+  HPA_SCHED_STATIC_CHUNK = 2   /* fixed split size, grid sized for the longest */
+} hpa_sched;
+
+/* Sticky device error bits (hpa_read_device_error). */
+enum {
+  HPA_DEVERR_SEQ_LEN = 1,      /* seq_len < 0 or > max_pages_per_seq * 64 */
+  HPA_DEVERR_PAGE_ID = 2,      /* page id outside [0, num_pages) */
+  HPA_DEVERR_PROLOGUE = 4,     /* append position outside the page table */
+  HPA_DEVERR_PLAN = 8          /* attention launched with a different worker count than planned */
+};
+
+typedef struct {
+  int32_t batch;               /* B  >= 0 */
+  int32_t num_q_heads;         /* Hq >= 1 */
+  int32_t num_kv_heads;        /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 16 */
+  int32_t head_dim;            /* must be 128 */
+  int32_t page_size;           /* must be 64 (one page = one tile) */
+  int32_t max_pages_per_seq;   /* page_table row length, >= 1 */
+  int32_t num_pages;           /* physical pages in each cache pool */
+  hpa_kv_dtype kv_dtype;
+  float sm_scale;              /* softmax scale, e.g. 1/sqrt(128) */
+} hpa_attn_desc;
+
+/* Byte offsets of the arrays inside a plan workspace (for inspection and tests).
+ * All arrays are int32. header[0..15]: 0 W' (active workers), 1 N (tiles),
+ * 2 S (sequences), 3 n_items, 4 n_merge, 5 n_partials, 6 sticky error word,
+ * 7 W (workers the plan was made for). */
+typedef struct {
+  size_t header, C, worker_off, item_s, item_t0, item_t1, item_split, item_slot,
+         num_splits, partial_base, merge_list, total_bytes;
+  int32_t max_items;           /* W + S */
+} hpa_plan_layout;
+
+/* Workers = compute units x resident attention workgroups per CU (cached per device). */
+hpa_status hpa_default_num_workers(int device, int32_t* num_workers);
+
+/* Size and layout of the plan workspace for up to num_workers workers (0 = default). */
+hpa_status hpa_plan_workspace_size(const hpa_attn_desc* desc, int32_t num_workers, size_t* bytes);
+hpa_status hpa_plan_workspace_layout(const hpa_attn_desc* desc, int32_t num_workers,
+                                     hpa_plan_layout* layout);
+
+/* Size of the partial-result workspace: (W + S) slots of Hq/Hkv x 128 fp32
+ * accumulators plus a max and a sum per head. Enough for every schedule. */
+hpa_status hpa_partial_workspace_size(const hpa_attn_desc* desc, int32_t num_workers, size_t* bytes);
+
+/* Balanced planner (one workgroup): tile counts ceil(L/64) per sequence, their
+ * prefix sum, W' = min(W, max(1, N / min_tiles_per_worker)) active workers,
+ * worker w owning global tiles [w*N/W', (w+1)*N/W'), items cut at sequence
+ * boundaries, split ranks, partial slots and the list of sequences to merge.
+ * seq_lens and page_table stay on the device (no host synchronisation).
+ * The plan workspace must be zero-filled before its first use (it holds the
+ * sticky error word, which hpa_plan never clears). */
+hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t num_workers,
+                    int32_t min_tiles_per_worker, void* plan_ws, size_t plan_ws_bytes,
+                    hipStream_t stream);
+
+/* Flags of hpa_decode_attn. The default (0) runs both launches. */
+enum {
+  HPA_ATTN_NO_MERGE = 1,    /* launch only the attention kernel (partials + unsplit rows) */
+  HPA_ATTN_MERGE_ONLY = 2   /* launch only the merge of an earlier HPA_ATTN_NO_MERGE call */
+};
+
+/* Decode attention: out[b, h] = softmax(sm_scale * q K^T) V over the first
+ * seq_lens[b] tokens of request b (a zero row when seq_lens[b] == 0).
+ * HPA_SCHED_BALANCED runs the persistent kernel over the plan made by hpa_plan
+ * with the same num_workers, then the merge kernel. The static schedules
+ * ignore the plan (plan_ws may still be given to receive device errors; NULL
+ * otherwise) and size their grid from num_workers. k_scale/v_scale are
+ * required for E4M3 caches and ignored for bf16. partial_ws must hold
+ * hpa_partial_workspace_size bytes. Two kernel launches (attention, then merge);
+ * flags may split them into two calls with identical arguments, so a caller can
+ * time or overlap them separately. */
+hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const void* q,
+                           const void* k_cache, const void* v_cache, const float* k_scale,
+                           const float* v_scale, const int32_t* seq_lens,
+                           const int32_t* page_table, int32_t num_workers, void* plan_ws,
+                           size_t plan_ws_bytes, void* partial_ws, size_t partial_ws_bytes,
+                           void* out, int32_t flags, hipStream_t stream);
+
+/* Fused decode prologue (bitbyai.com "vLLM × HPC-Ops …", "Breaking Down the
+ * Kernels"): for each request b at position pos = positions[b]:
+ *   q_out[b,h] = RoPE(RMSNorm(q_in[b,h]; q_norm_w, eps), pos)     (bf16)
+ *   k          = RoPE(RMSNorm(k_in[b,g]; k_norm_w, eps), pos)
+ *   k_cache[page_table[b, pos/64], g, pos%64, :] = encode(k / k_scale[g])
+ *   v_cache[page_table[b, pos/64], g, :, pos%64] = encode(v_in[b,g] / v_scale[g])
+ *   seq_lens_out[b] = pos + 1
+ * RMSNorm is over the 128 dims of a head row with one weight vector per
+ * projection; RoPE rotates the pairs (i, i+64) by pos * rope_theta^(-i/64).
+ * encode is round-to-nearest-even bf16, or saturating round-to-nearest-even
+ * OCP E4M3 (scales required). positions and seq_lens_out must not alias.
+ * plan_ws (may be NULL) receives HPA_DEVERR_PROLOGUE. One kernel launch. */
+hpa_status hpa_decode_prologue(const hpa_attn_desc* desc, const void* q_in, const void* k_in,
+                               const void* v_in, const float* q_norm_w, const float* k_norm_w,
+                               float eps, double rope_theta, const int32_t* positions,
+                               const int32_t* page_table, void* k_cache, void* v_cache,
+                               const float* k_scale, const float* v_scale, void* q_out,
+                               int32_t* seq_lens_out, void* plan_ws, hipStream_t stream);
+
+/* Synchronises the stream, then reads (and, if clear != 0, zeroes) the sticky
+ * device error word of a plan workspace. */
+hpa_status hpa_read_device_error(void* plan_ws, int32_t* code, int32_t clear, hipStream_t stream);
+
+const char* hpa_status_string(hpa_status status);
+/* Message of the last non-OK status returned on the calling thread. */
+const char* hpa_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HPA_H */

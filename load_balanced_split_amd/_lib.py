@@ -1,0 +1,183 @@
+"""ctypes binding of libhpa (include/hpa.h): argument marshalling only.
+
+Every call takes torch tensors that already live on the GPU, passes their
+device pointers and the current HIP stream to the C ABI, and raises HpaError on
+a non-OK status. All arithmetic happens in the library's HIP kernels; there is
+no CPU fallback: if libhpa.so is missing the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhpa.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "hpa.h")
+
+HPA_KV_BF16, HPA_KV_FP8_E4M3 = 0, 1
+HPA_SCHED_BALANCED, HPA_SCHED_STATIC_SPLITS, HPA_SCHED_STATIC_CHUNK = 0, 1, 2
+SCHED = {"balanced": 0, "static_splits": 1, "static_chunk": 2}
+DEVERR_SEQ_LEN, DEVERR_PAGE_ID, DEVERR_PROLOGUE, DEVERR_PLAN = 1, 2, 4, 8
+ATTN_NO_MERGE, ATTN_MERGE_ONLY = 1, 2
+HEADER_SLOTS = dict(Wp=0, N=1, S=2, n_items=3, n_merge=4, n_partials=5, error=6, W=7)
+
+
+class HpaError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: status {status}: {message}")
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float)]
+
+
+class PlanLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "header", "C", "worker_off", "item_s", "item_t0", "item_t1", "item_split", "item_slot",
+        "num_splits", "partial_base", "merge_list", "total_bytes")] + [("max_items", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        # One HIP runtime per process: torch brings its own libamdhip64 (same soname as
+        # the one libhpa links), so load torch first and libhpa binds to that copy.
+        import torch  # noqa: F401
+        if not os.path.exists(LIB_PATH):
+            raise HpaError(-1, "load", f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        D = ctypes.POINTER(AttnDesc)
+        sig = {
+            "hpa_default_num_workers": [ctypes.c_int, ctypes.POINTER(ctypes.c_int32)],
+            "hpa_plan_workspace_size": [D, _I, ctypes.POINTER(ctypes.c_size_t)],
+            "hpa_plan_workspace_layout": [D, _I, ctypes.POINTER(PlanLayout)],
+            "hpa_partial_workspace_size": [D, _I, ctypes.POINTER(ctypes.c_size_t)],
+            "hpa_plan": [D, _P, _I, _I, _P, ctypes.c_size_t, _P],
+            "hpa_decode_attn": [D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I, _P, ctypes.c_size_t,
+                                _P, ctypes.c_size_t, _P, _I, _P],
+            "hpa_decode_prologue": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
+                                    _P, _P, _P, _P, _P, _P, _P, _P],
+            "hpa_read_device_error": [_P, ctypes.POINTER(ctypes.c_int32), _I, _P],
+            "hpa_status_string": [ctypes.c_int],
+            "hpa_last_error_message": [],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name in ("hpa_status_string", "hpa_last_error_message") else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def declared_symbols() -> list:
+    """Names of the functions include/hpa.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:hpa_status|const char\*)\s+(hpa_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise HpaError(status, where, lib().hpa_last_error_message().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_desc(batch, num_q_heads, num_kv_heads, max_pages_per_seq, num_pages, kv_dtype="bf16",
+              sm_scale=None) -> AttnDesc:
+    import math
+    return AttnDesc(batch, num_q_heads, num_kv_heads, 128, 64, max_pages_per_seq, num_pages,
+                    HPA_KV_FP8_E4M3 if kv_dtype == "fp8" else HPA_KV_BF16,
+                    1.0 / math.sqrt(128) if sm_scale is None else sm_scale)
+
+
+def hpa_default_num_workers(device: int = 0) -> int:
+    n = ctypes.c_int32(0)
+    _check(lib().hpa_default_num_workers(device, ctypes.byref(n)), "hpa_default_num_workers")
+    return n.value
+
+
+def hpa_plan_workspace_size(desc: AttnDesc, num_workers: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().hpa_plan_workspace_size(ctypes.byref(desc), num_workers, ctypes.byref(n)), "hpa_plan_workspace_size")
+    return n.value
+
+
+def hpa_plan_workspace_layout(desc: AttnDesc, num_workers: int = 0) -> dict:
+    lay = PlanLayout()
+    _check(lib().hpa_plan_workspace_layout(ctypes.byref(desc), num_workers, ctypes.byref(lay)),
+           "hpa_plan_workspace_layout")
+    return {name: getattr(lay, name) for name, _ in PlanLayout._fields_}
+
+
+def hpa_partial_workspace_size(desc: AttnDesc, num_workers: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().hpa_partial_workspace_size(ctypes.byref(desc), num_workers, ctypes.byref(n)),
+           "hpa_partial_workspace_size")
+    return n.value
+
+
+def hpa_plan(desc, seq_lens, num_workers, min_tiles_per_worker, plan_ws, stream=None):
+    _check(lib().hpa_plan(ctypes.byref(desc), _ptr(seq_lens), num_workers, min_tiles_per_worker,
+                          _ptr(plan_ws), plan_ws.numel() * plan_ws.element_size(), _stream(stream)), "hpa_plan")
+
+
+def hpa_decode_attn(desc, sched, q, k_cache, v_cache, k_scale, v_scale, seq_lens, page_table,
+                    num_workers, plan_ws, partial_ws, out, flags=0, stream=None):
+    sched = SCHED[sched] if isinstance(sched, str) else int(sched)
+    pbytes = 0 if plan_ws is None else plan_ws.numel() * plan_ws.element_size()
+    _check(lib().hpa_decode_attn(ctypes.byref(desc), sched, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens), _ptr(page_table),
+                                 num_workers, _ptr(plan_ws), pbytes, _ptr(partial_ws),
+                                 partial_ws.numel() * partial_ws.element_size(), _ptr(out), flags,
+                                 _stream(stream)), "hpa_decode_attn")
+
+
+def hpa_decode_prologue(desc, q_in, k_in, v_in, q_norm_w, k_norm_w, eps, rope_theta, positions,
+                        page_table, k_cache, v_cache, k_scale, v_scale, q_out, seq_lens_out,
+                        plan_ws=None, stream=None):
+    _check(lib().hpa_decode_prologue(ctypes.byref(desc), _ptr(q_in), _ptr(k_in), _ptr(v_in),
+                                     _ptr(q_norm_w), _ptr(k_norm_w), eps, rope_theta, _ptr(positions),
+                                     _ptr(page_table), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                     _ptr(v_scale), _ptr(q_out), _ptr(seq_lens_out), _ptr(plan_ws),
+                                     _stream(stream)), "hpa_decode_prologue")
+
+
+def hpa_read_device_error(plan_ws, clear: bool = False, stream=None) -> int:
+    code = ctypes.c_int32(0)
+    _check(lib().hpa_read_device_error(_ptr(plan_ws), ctypes.byref(code), 1 if clear else 0, _stream(stream)),
+           "hpa_read_device_error")
+    return code.value
+
+
+def hpa_status_string(status: int) -> str:
+    return lib().hpa_status_string(status).decode()
+
+
+def hpa_last_error_message() -> str:
+    return lib().hpa_last_error_message().decode()

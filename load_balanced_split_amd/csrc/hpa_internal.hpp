@@ -1,0 +1,109 @@
+// Internal declarations shared by the host library and the HIP kernels of libhpa.
+// gfx950 (CDNA4) only: wave64, MFMA 16x16x32 bf16, OCP E4M3 converts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+#include "hpa.h"
+
+namespace hpa {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 64;          // tokens per page == tokens per tile
+constexpr int kMaxGroup = 16;      // query heads per KV head (MFMA N width)
+constexpr int kWaves = 4;          // waves per attention workgroup (one worker)
+constexpr int kAttnThreads = 64 * kWaves;
+constexpr int kPlanThreads = 1024;
+constexpr int kHeaderInts = 16;
+
+// Header slots of the plan workspace (int32).
+enum : int {
+  H_WP = 0, H_N = 1, H_S = 2, H_NITEMS = 3, H_NMERGE = 4, H_NPART = 5, H_ERR = 6, H_W = 7
+};
+
+// Offsets of the plan arrays, in int32 elements.
+struct PlanOffsets {
+  int64_t header, C, worker_off, item_s, item_t0, item_t1, item_split, item_slot,
+          num_splits, partial_base, merge_list, ne, total;
+  int32_t max_items;
+};
+
+inline PlanOffsets plan_offsets(int64_t S, int64_t W) {
+  PlanOffsets o{};
+  auto al = [](int64_t x) { return (x + 63) & ~int64_t(63); };   // 256-byte aligned arrays
+  const int64_t mi = W + S;
+  int64_t p = 0;
+  o.header = p;       p += al(kHeaderInts);
+  o.C = p;            p += al(S + 1);
+  o.worker_off = p;   p += al(W + 1);
+  o.item_s = p;       p += al(mi);
+  o.item_t0 = p;      p += al(mi);
+  o.item_t1 = p;      p += al(mi);
+  o.item_split = p;   p += al(mi);
+  o.item_slot = p;    p += al(mi);
+  o.num_splits = p;   p += al(S);
+  o.partial_base = p; p += al(S);
+  o.merge_list = p;   p += al(S);
+  o.ne = p;           p += al(S + 1);
+  o.total = p;
+  o.max_items = static_cast<int32_t>(mi);
+  return o;
+}
+
+// Partial-result workspace: acc [slots][G][128] fp32, then m [slots][G], l [slots][G].
+struct PartialLayout {
+  int64_t slots, acc, m, l, total_bytes;
+};
+
+inline PartialLayout partial_layout(int64_t slots, int64_t G) {
+  PartialLayout p{};
+  p.slots = slots;
+  p.acc = 0;
+  p.m = slots * G * kHeadDim * 4;
+  p.l = p.m + slots * G * 4;
+  p.total_bytes = p.l + slots * G * 4;
+  return p;
+}
+
+// Everything an attention kernel needs, passed by value.
+struct AttnArgs {
+  const uint16_t* q;           // [B, Hq, 128] bf16
+  const uint8_t* k_cache;      // [P, Hkv, 64, 128] x elem
+  const uint8_t* v_cache;      // [P, Hkv, 128, 64] x elem
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int32_t* plan;               // plan workspace (may be null for static schedules)
+  float* part_acc;
+  float* part_m;
+  float* part_l;
+  uint16_t* out;               // [B, Hq, 128] bf16
+  PlanOffsets po;
+  int batch, hq, hkv, group, max_pages, num_pages;
+  int workers;                 // W the kernels were launched for (plan header must agree)
+  int64_t slots;               // partial slots available (W + S)
+  float sm_scale;
+  // static schedules
+  int static_splits;           // S_split
+  int static_chunk;            // fixed chunk (flavour "chunk"), 0 for flavour "splits"
+};
+
+// Launch wrappers (defined in the .hip files). Return hipSuccess or the launch error.
+hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_pages, int num_workers,
+                       int min_tiles, int32_t* plan, const PlanOffsets& po, hipStream_t stream);
+hipError_t launch_attn_balanced(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream);
+hipError_t launch_attn_static(const AttnArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_merge(const AttnArgs& a, bool balanced, hipStream_t stream);
+hipError_t launch_prologue(const hpa_attn_desc& d, const uint16_t* q_in, const uint16_t* k_in,
+                           const uint16_t* v_in, const float* q_norm_w, const float* k_norm_w,
+                           float eps, double rope_theta, const int32_t* positions,
+                           const int32_t* page_table, uint8_t* k_cache, uint8_t* v_cache,
+                           const float* k_scale, const float* v_scale, uint16_t* q_out,
+                           int32_t* seq_lens_out, int32_t* err_word, hipStream_t stream);
+hipError_t launch_clear_word(int32_t* word, hipStream_t stream);
+int attn_blocks_per_cu(bool fp8);
+
+}  // namespace hpa

@@ -1,0 +1,147 @@
+// Fused decode prologue: q/k RMSNorm, rotate-half RoPE, KV quantise and paged append.
+//
+// bitbyai.com "vLLM × HPC-Ops: High-Performance Attention and MoE Backends from
+// Tencent Hunyuan", section "Breaking Down the Kernels": RoPE, query-key
+// normalisation and the KV write run as one prologue ahead of attention, to
+// save launches and HBM round trips.
+//
+// One workgroup per request; each wave takes whole head rows (Hq query rows,
+// Hkv key rows, Hkv value rows). Lane i owns the rotation pair (i, i + 64).
+// RMSNorm (Zhang & Sennrich 2019): y = x / sqrt(mean(x^2) + eps) * w, fp32.
+// RoPE (Su et al. 2021, rotate-half form): angle_i = pos * theta^(-i/64) is
+// formed and reduced modulo 2*pi in fp64 (positions reach 131072, where an fp32
+// angle would be off by ~0.016 rad), then rotated in fp32.
+#include "hpa_internal.hpp"
+
+#include <cmath>
+
+namespace hpa {
+namespace {
+
+constexpr int kProThreads = 256;
+
+__device__ inline float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
+}
+
+__device__ inline uint16_t f32_to_bf16(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// fp32 -> OCP E4M3, round to nearest even, saturating at 448, NaN -> 0x7f.
+__device__ inline uint8_t f32_to_e4m3(float x) {
+  if (x != x) return 0x7f;
+  const uint8_t sign = __builtin_signbit(x) ? 0x80 : 0x00;
+  float a = fminf(fabsf(x), 448.0f);
+  if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9 (codes 0..8)
+    const int q = static_cast<int>(rintf(a * 512.0f));
+    return sign | static_cast<uint8_t>(q);
+  }
+  int e;
+  frexpf(a, &e);                             // a = f * 2^e, f in [0.5, 1)
+  int E = e - 1;                             // a in [2^E, 2^(E+1))
+  int qm = static_cast<int>(rintf(ldexpf(a, 3 - E)));   // in [8, 16]
+  if (qm == 16) {
+    qm = 8;
+    ++E;
+  }
+  return sign | static_cast<uint8_t>(((E + 7) << 3) | (qm - 8));
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(kProThreads) void prologue_kernel(
+    const uint16_t* __restrict__ q_in, const uint16_t* __restrict__ k_in,
+    const uint16_t* __restrict__ v_in, const float* __restrict__ q_norm_w,
+    const float* __restrict__ k_norm_w, float eps, double rope_theta,
+    const int32_t* __restrict__ positions, const int32_t* __restrict__ page_table,
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, uint16_t* __restrict__ q_out, int32_t* __restrict__ seq_lens_out,
+    int32_t* err_word, int hq, int hkv, int max_pages, int num_pages, int fp8) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int pos = positions[b];
+  int pid = -1;
+  if (pos >= 0 && pos < max_pages * kPage) pid = page_table[int64_t(b) * max_pages + pos / kPage];
+  if (pid < 0 || pid >= num_pages) {
+    if (threadIdx.x == 0 && err_word) atomicOr(err_word, HPA_DEVERR_PROLOGUE);
+    return;
+  }
+  if (threadIdx.x == 0) seq_lens_out[b] = pos + 1;
+  const int slot = pos % kPage;
+
+  // rotation of pair (lane, lane + 64)
+  const double two_pi = 6.283185307179586476925286766559;
+  const double ang = static_cast<double>(pos) * pow(rope_theta, -static_cast<double>(lane) / 64.0);
+  const double red = ang - two_pi * rint(ang / two_pi);
+  const float cs = static_cast<float>(cos(red)), sn = static_cast<float>(sin(red));
+
+  const int rows = hq + 2 * hkv;
+  for (int r = wave; r < rows; r += kProThreads / 64) {
+    if (r < hq + hkv) {
+      const bool is_q = r < hq;
+      const uint16_t* src = is_q ? q_in + (int64_t(b) * hq + r) * kHeadDim
+                                 : k_in + (int64_t(b) * hkv + (r - hq)) * kHeadDim;
+      const float* w = is_q ? q_norm_w : k_norm_w;
+      const float x0 = bf16_to_f32(src[lane]), x1 = bf16_to_f32(src[lane + 64]);
+      const float ms = wave_sum(x0 * x0 + x1 * x1) * (1.0f / kHeadDim);
+      const float inv = 1.0f / sqrtf(ms + eps);
+      const float y0 = x0 * inv * w[lane], y1 = x1 * inv * w[lane + 64];
+      const float o0 = y0 * cs - y1 * sn, o1 = y1 * cs + y0 * sn;
+      if (is_q) {
+        uint16_t* dst = q_out + (int64_t(b) * hq + r) * kHeadDim;
+        dst[lane] = f32_to_bf16(o0);
+        dst[lane + 64] = f32_to_bf16(o1);
+      } else {
+        const int g = r - hq;
+        const int64_t row = ((int64_t(pid) * hkv + g) * kPage + slot) * kHeadDim;
+        if (fp8) {
+          const float sc = k_scale[g];
+          k_cache[row + lane] = f32_to_e4m3(o0 / sc);
+          k_cache[row + lane + 64] = f32_to_e4m3(o1 / sc);
+        } else {
+          uint16_t* kc = reinterpret_cast<uint16_t*>(k_cache);
+          kc[row + lane] = f32_to_bf16(o0);
+          kc[row + lane + 64] = f32_to_bf16(o1);
+        }
+      }
+    } else {
+      const int g = r - hq - hkv;
+      const uint16_t* src = v_in + (int64_t(b) * hkv + g) * kHeadDim;
+      const int64_t base = (int64_t(pid) * hkv + g) * kHeadDim * kPage + slot;   // dim-major page
+      if (fp8) {
+        const float sc = v_scale[g];
+        v_cache[base + int64_t(lane) * kPage] = f32_to_e4m3(bf16_to_f32(src[lane]) / sc);
+        v_cache[base + int64_t(lane + 64) * kPage] = f32_to_e4m3(bf16_to_f32(src[lane + 64]) / sc);
+      } else {
+        uint16_t* vc = reinterpret_cast<uint16_t*>(v_cache);
+        vc[base + int64_t(lane) * kPage] = src[lane];
+        vc[base + int64_t(lane + 64) * kPage] = src[lane + 64];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prologue(const hpa_attn_desc& d, const uint16_t* q_in, const uint16_t* k_in,
+                           const uint16_t* v_in, const float* q_norm_w, const float* k_norm_w,
+                           float eps, double rope_theta, const int32_t* positions,
+                           const int32_t* page_table, uint8_t* k_cache, uint8_t* v_cache,
+                           const float* k_scale, const float* v_scale, uint16_t* q_out,
+                           int32_t* seq_lens_out, int32_t* err_word, hipStream_t stream) {
+  if (d.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(prologue_kernel, dim3(d.batch), dim3(kProThreads), 0, stream, q_in, k_in, v_in,
+                     q_norm_w, k_norm_w, eps, rope_theta, positions, page_table, k_cache, v_cache,
+                     k_scale, v_scale, q_out, seq_lens_out, err_word, d.num_q_heads, d.num_kv_heads,
+                     d.max_pages_per_seq, d.num_pages, d.kv_dtype == HPA_KV_FP8_E4M3 ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace hpa

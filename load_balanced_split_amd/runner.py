@@ -1,0 +1,101 @@
+"""Device-side plumbing around the C ABI: upload a workload, own its workspaces,
+run one decode step (prologue -> plan -> attention -> merge) on the GPU.
+
+PyTorch is used only to hold device memory and to name the stream.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import _lib
+
+
+class DeviceStep:
+    """One workload resident in HBM plus the workspaces its decode step needs."""
+
+    def __init__(self, w, num_workers: int = 0, device: str = "cuda"):
+        import torch
+        self.torch = torch
+        self.w = w
+        dev = torch.device(device)
+        self.device = dev
+
+        def up(a, dtype=None):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            if dtype is not None:
+                t = t.view(dtype)
+            return t.to(dev)
+
+        self.q = up(w.q.view(np.int16), torch.bfloat16)
+        self.k_cache = up(w.k_cache.view(np.int16) if w.kv_dtype == "bf16" else w.k_cache)
+        self.v_cache = up(w.v_cache.view(np.int16) if w.kv_dtype == "bf16" else w.v_cache)
+        self.k_scale = up(w.k_scale) if w.k_scale is not None else None
+        self.v_scale = up(w.v_scale) if w.v_scale is not None else None
+        self.seq_lens = up(w.seq_lens)
+        self.page_table = up(w.page_table)
+        self.desc = _lib.make_desc(w.batch, w.hq, w.hkv, w.max_pages, w.num_pages, w.kv_dtype, w.sm_scale)
+        self.num_workers = num_workers or _lib.hpa_default_num_workers(dev.index or 0)
+        self.plan_ws = torch.zeros(_lib.hpa_plan_workspace_size(self.desc, self.num_workers),
+                                   dtype=torch.uint8, device=dev)
+        self.partial_ws = torch.empty(_lib.hpa_partial_workspace_size(self.desc, self.num_workers),
+                                      dtype=torch.uint8, device=dev)
+        self.out = torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device=dev)
+        if w.has_prologue:
+            self.q_new = up(w.q_new.view(np.int16), torch.bfloat16)
+            self.k_new = up(w.k_new.view(np.int16), torch.bfloat16)
+            self.v_new = up(w.v_new.view(np.int16), torch.bfloat16)
+            self.q_norm_w = up(w.q_norm_w)
+            self.k_norm_w = up(w.k_norm_w)
+            self.q_rot = torch.empty_like(self.q_new)
+            self.lens_after = torch.empty_like(self.seq_lens)
+
+    def prologue(self, stream=None):
+        w = self.w
+        _lib.hpa_decode_prologue(self.desc, self.q_new, self.k_new, self.v_new, self.q_norm_w, self.k_norm_w,
+                                 w.eps, w.rope_theta, self.seq_lens, self.page_table, self.k_cache,
+                                 self.v_cache, self.k_scale, self.v_scale, self.q_rot, self.lens_after,
+                                 self.plan_ws, stream)
+
+    def attn_inputs(self):
+        if self.w.has_prologue:
+            return self.q_rot, self.lens_after
+        return self.q, self.seq_lens
+
+    def plan(self, min_tiles: int = 1, stream=None):
+        _, lens = self.attn_inputs()
+        _lib.hpa_plan(self.desc, lens, self.num_workers, min_tiles, self.plan_ws, stream)
+
+    def attend(self, sched: str = "balanced", stream=None, flags: int = 0):
+        q, lens = self.attn_inputs()
+        _lib.hpa_decode_attn(self.desc, sched, q, self.k_cache, self.v_cache, self.k_scale, self.v_scale,
+                             lens, self.page_table, self.num_workers, self.plan_ws, self.partial_ws,
+                             self.out, flags, stream)
+
+    def step(self, sched: str = "balanced", min_tiles: int = 1, stream=None):
+        """The whole hot path of one decode step; returns the bf16 output tensor."""
+        if self.w.has_prologue:
+            self.prologue(stream)
+        if sched == "balanced":
+            self.plan(min_tiles, stream)
+        self.attend(sched, stream)
+        return self.out
+
+    def device_error(self, clear: bool = False) -> int:
+        return _lib.hpa_read_device_error(self.plan_ws, clear)
+
+    def plan_arrays(self) -> dict:
+        """The plan workspace as host int32 arrays (after the stream is synchronised)."""
+        lay = _lib.hpa_plan_workspace_layout(self.desc, self.num_workers)
+        ws = self.plan_ws.cpu().numpy().view(np.int32)
+        hdr = ws[lay["header"] // 4: lay["header"] // 4 + 16]
+        Wp, N, S, nit, nm, npart = (int(x) for x in hdr[:6])
+        g = lambda key, n: ws[lay[key] // 4: lay[key] // 4 + n].tolist()
+        return dict(Wp=Wp, N=N, S=S, n_items=nit, n_partials=npart, error=int(hdr[6]), W=int(hdr[7]),
+                    C=g("C", S + 1), worker_off=g("worker_off", Wp + 1), item_s=g("item_s", nit),
+                    item_t0=g("item_t0", nit), item_t1=g("item_t1", nit), item_split=g("item_split", nit),
+                    item_slot=g("item_slot", nit), num_splits=g("num_splits", S),
+                    partial_base=g("partial_base", S), merge_list=g("merge_list", nm))
+
+    def output_f64(self) -> np.ndarray:
+        return self.out.float().cpu().numpy().astype(np.float64)

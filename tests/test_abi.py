@@ -1,0 +1,91 @@
+"""The C-ABI library loads, exports every declared symbol, and its host-side
+validation answers without touching a GPU."""
+
+import ctypes
+
+import pytest
+
+from load_balanced_split_amd import _lib
+from tests.helpers import ensure_built
+
+
+@pytest.fixture(scope="module")
+def L():
+    ensure_built()
+    return _lib.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _lib.declared_symbols()
+    assert {"hpa_plan", "hpa_decode_attn", "hpa_decode_prologue"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _desc(**kw):
+    d = _lib.make_desc(4, 8, 1, 9, 16)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_status_strings(L):
+    assert _lib.hpa_status_string(0) == "ok"
+    assert "workspace" in _lib.hpa_status_string(3)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, 2), ("page_size", 16, 2), ("num_kv_heads", 5, 1), ("num_q_heads", 34, 1),
+    ("batch", -1, 1), ("max_pages_per_seq", 0, 1), ("sm_scale", 0.0, 1), ("kv_dtype", 7, 1)])
+def test_descriptor_validation(L, field, value, status):
+    d = _desc(**{field: value})
+    if field == "num_q_heads" and value == 34:
+        d.num_kv_heads = 2          # group 17 > 16
+        status = 2
+    n = ctypes.c_size_t(0)
+    assert L.hpa_plan_workspace_size(ctypes.byref(d), 512, ctypes.byref(n)) == status
+    assert _lib.hpa_last_error_message()
+
+
+def test_workspace_sizes_and_layout(L):
+    d = _desc()
+    lay = _lib.hpa_plan_workspace_layout(d, 512)
+    assert lay["max_items"] == 512 + 4
+    offs = [lay[k] for k in ("header", "C", "worker_off", "item_s", "item_t0", "item_t1", "item_split",
+                             "item_slot", "num_splits", "partial_base", "merge_list")]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert _lib.hpa_plan_workspace_size(d, 512) == lay["total_bytes"]
+    # (W + S) slots x G heads x (128 acc + m + l) fp32
+    assert _lib.hpa_partial_workspace_size(d, 512) == (512 + 4) * 8 * (128 + 2) * 4
+
+
+def test_calls_reject_bad_arguments_before_launching(L):
+    d = _desc()
+    with pytest.raises(_lib.HpaError) as e:
+        L_status = L.hpa_plan(ctypes.byref(d), None, 512, 1, None, 0, None)
+        _lib._check(L_status, "hpa_plan")
+    assert e.value.status == 1
+    # undersized plan workspace -> HPA_ERR_WORKSPACE, nothing launched
+    fake = ctypes.c_void_p(0x1000)
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, fake, 16, None) == 3
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 0, fake, 1 << 30, None) == 1     # min_tiles < 1
+    # balanced attention without a plan, fp8 without scales
+    args = [fake] * 7
+    assert L.hpa_decode_attn(ctypes.byref(d), 0, *args, 512, None, 0, fake, 1 << 30, fake, 0, None) == 1
+    d8 = _desc(kv_dtype=1)
+    assert L.hpa_decode_attn(ctypes.byref(d8), 1, fake, fake, fake, None, None, fake, fake, 512, None, 0,
+                             fake, 1 << 30, fake, 0, None) == 1
+    # partial workspace too small
+    assert L.hpa_decode_attn(ctypes.byref(d), 1, fake, fake, fake, None, None, fake, fake, 512, None, 0,
+                             fake, 100, fake, 0, None) == 3
+    # unknown flags, or both halves switched off
+    for bad in (3, 4, -1):
+        assert L.hpa_decode_attn(ctypes.byref(d), 1, fake, fake, fake, None, None, fake, fake, 512, None, 0,
+                                 fake, 1 << 30, fake, bad, None) == 1
+    # prologue: aliasing positions / seq_lens_out is refused
+    assert L.hpa_decode_prologue(ctypes.byref(d), fake, fake, fake, fake, fake, 1e-6, 1e6, fake, fake, fake,
+                                 fake, None, None, fake, fake, None, None) == 1
+    # empty batch is a no-op
+    d0 = _desc(batch=0)
+    assert L.hpa_decode_attn(ctypes.byref(d0), 1, None, None, None, None, None, None, None, 512, None, 0,
+                             None, 0, None, 0, None) == 0

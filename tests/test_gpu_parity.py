@@ -1,0 +1,278 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Planner work lists must be bit-identical to the CPU planner; attention outputs
+must match the oracle within |gpu - ref| <= atol + rtol |ref| per element
+(bf16 KV: 1e-2 / 1e-2, E4M3 KV: 3e-2 / 3e-2).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from load_balanced_split_amd import _lib, inputs
+from oracle import attention as oa
+from oracle import planner as op
+from oracle import prologue as opro
+from tests.helpers import TOL, assert_within, ensure_built, tolerance_report
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+PLAN_KEYS = ("C", "worker_off", "item_s", "item_t0", "item_t1", "item_split", "item_slot",
+             "num_splits", "partial_base", "merge_list")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ensure_built()
+    _lib.lib()
+    return torch.device("cuda")
+
+
+def device_plan(lens, hkv, W, min_tiles):
+    """Run the GPU planner on a length vector; return its arrays as host lists."""
+    B = len(lens)
+    maxp = max(1, max([(int(L) + 63) // 64 for L in lens] or [1]))
+    desc = _lib.make_desc(B, hkv, hkv, maxp, 1)
+    size = _lib.hpa_plan_workspace_size(desc, W)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    sl = torch.tensor(np.asarray(lens, np.int32), device="cuda")
+    _lib.hpa_plan(desc, sl, W, min_tiles, ws)
+    torch.cuda.synchronize()
+    lay = _lib.hpa_plan_workspace_layout(desc, W)
+    h = ws.cpu().numpy().view(np.int32)
+    hdr = h[:16]
+    Wp, N, S, nit, nm, npart = (int(x) for x in hdr[:6])
+    g = lambda k, n: h[lay[k] // 4: lay[k] // 4 + n].tolist()
+    return dict(Wp=Wp, N=N, S=S, n_items=nit, n_partials=npart, err=int(hdr[6]),
+                C=g("C", S + 1), worker_off=g("worker_off", Wp + 1), item_s=g("item_s", nit),
+                item_t0=g("item_t0", nit), item_t1=g("item_t1", nit), item_split=g("item_split", nit),
+                item_slot=g("item_slot", nit), num_splits=g("num_splits", S),
+                partial_base=g("partial_base", S), merge_list=g("merge_list", nm))
+
+
+def check_plan(lens, hkv, W, mt):
+    got = device_plan(lens, hkv, W, mt)
+    want = op.balanced_plan(lens, hkv, W, mt)
+    assert got["err"] == 0
+    for k in ("Wp", "N", "n_items", "n_partials") + PLAN_KEYS:
+        assert got[k] == want[k], (k, lens, hkv, W, mt)
+
+
+# ---------------------------------------------------------------- planner ---
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("W,mt", [(0, 1), (1, 1), (7, 1), (512, 1), (512, 4), (1024, 1), (3000, 2)])
+def test_plan_bit_exact_workload_lengths(cfg, W, mt):
+    lens = inputs.config_lengths_only(cfg) + (1 if cfg == 4 else 0)
+    hkv = 4 if cfg == 3 else 1
+    if W == 0:
+        W = _lib.hpa_default_num_workers(0)
+    print(f"plan cfg{cfg} W={W} mt={mt}", flush=True)
+    check_plan(lens.tolist(), hkv, W, mt)
+
+
+def test_plan_bit_exact_random_lengths():
+    rng = np.random.default_rng(123)
+    for trial in range(300):
+        B = int(rng.integers(1, 300))
+        hkv = int(rng.integers(1, 5))
+        lens = rng.integers(0, 20000, size=B)
+        lens[rng.random(B) < 0.3] = 0
+        if trial % 5 == 0:
+            lens[:] = rng.choice([0, 1, 63, 64, 65, 4096, 65535, 65536, 65537], size=B)
+        W = int(rng.integers(1, 4000))
+        mt = int(rng.integers(1, 6))
+        check_plan(lens.tolist(), hkv, W, mt)
+    check_plan([0, 0, 0], 2, 16, 1)              # N == 0: no active workers
+    check_plan([5000], 1, 100000 // 64, 1)       # W > N tiles
+
+
+# -------------------------------------------------------------- attention ---
+
+def run_and_compare(w, sched="balanced", W=0, min_tiles=1, ref=None, what=""):
+    from load_balanced_split_amd.runner import DeviceStep
+    d = DeviceStep(w, num_workers=W)
+    print(f"attn {what} {w.name} sched={sched} W={d.num_workers}", flush=True)
+    d.step(sched, min_tiles)
+    torch.cuda.synchronize()
+    assert d.device_error() == 0
+    if ref is None:
+        ref = oracle_out(w)
+    got = d.output_f64()
+    r = assert_within(got, ref, w.kv_dtype, f"{w.name} {sched} W={W}")
+    return got, r, d
+
+
+def oracle_out(w):
+    if w.has_prologue:
+        pr = opro.prologue(w)
+        return oa.decode_attention(pr["q_rot"], pr["k_cache"], pr["v_cache"], pr["seq_lens"], w.page_table,
+                                   w.hkv, w.sm_scale, w.kv_dtype, w.k_scale, w.v_scale)
+    return oa.decode_attention(w.q, w.k_cache, w.v_cache, w.seq_lens, w.page_table, w.hkv, w.sm_scale,
+                               w.kv_dtype, w.k_scale, w.v_scale)
+
+
+EDGE_LENS = [0, 1, 2, 31, 32, 33, 63, 64, 65, 96, 127, 128, 129, 700, 1000]
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("heads", [(8, 1), (32, 4), (4, 1), (16, 1), (2, 2)])
+def test_edge_lengths_all_schedules(kv_dtype, heads):
+    hq, hkv = heads
+    w = inputs.build_workload("edge", EDGE_LENS, hq, hkv, kv_dtype, seed=5, pool_pages=60, poison=True)
+    ref = oracle_out(w)
+    for sched, W in [("balanced", 0), ("balanced", 1), ("balanced", 3), ("balanced", 37),
+                     ("static_splits", 0), ("static_splits", 5), ("static_chunk", 0), ("static_chunk", 9)]:
+        got, r, _ = run_and_compare(w, sched, W, ref=ref, what=f"{kv_dtype} {hq}:{hkv}")
+        assert np.all(got[0] == 0)                      # empty request -> zero row
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_random_batches(kv_dtype):
+    rng = np.random.default_rng(77)
+    for trial in range(6):
+        B = int(rng.integers(1, 24))
+        lens = rng.integers(0, 3000, size=B)
+        w = inputs.build_workload("rand", lens, 8, 1, kv_dtype, seed=int(rng.integers(1 << 30)), poison=trial % 2 == 0)
+        ref = oracle_out(w)
+        for sched, W in [("balanced", 0), ("balanced", int(rng.integers(1, 50))), ("static_splits", 0)]:
+            run_and_compare(w, sched, W, min_tiles=int(rng.integers(1, 4)), ref=ref, what=f"trial{trial}")
+
+
+def test_tiny_workload():
+    w = inputs.config_workload(0)
+    ref = oracle_out(w)
+    for sched in ("balanced", "static_splits", "static_chunk"):
+        run_and_compare(w, sched, ref=ref)
+    run_and_compare(w, "balanced", W=4, ref=ref)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_full_size_bf16_workloads(cfg):
+    w = inputs.config_workload(cfg)
+    ref = oracle_out(w)
+    outs = {}
+    for sched in ("balanced", "static_splits", "static_chunk"):
+        got, r, _ = run_and_compare(w, sched, ref=ref, what=f"cfg{cfg}")
+        print(f"cfg{cfg} {sched}: {r}", flush=True)
+        outs[sched] = got
+    # one worker (no split at all) agrees with the default within tolerance
+    if cfg != 3:
+        run_and_compare(w, "balanced", W=1, ref=ref, what=f"cfg{cfg} single worker")
+
+
+def test_fp8_prologue_workload():
+    w = inputs.config_workload(4)
+    pr = opro.prologue(w)
+    ref = oa.decode_attention(pr["q_rot"], pr["k_cache"], pr["v_cache"], pr["seq_lens"], w.page_table, w.hkv,
+                              w.sm_scale, w.kv_dtype, w.k_scale, w.v_scale)
+    from load_balanced_split_amd.runner import DeviceStep
+    d = DeviceStep(w)
+    print(f"cfg4 W={d.num_workers}", flush=True)
+    d.step("balanced")
+    torch.cuda.synchronize()
+    assert d.device_error() == 0
+    assert np.array_equal(d.lens_after.cpu().numpy(), pr["seq_lens"])
+    # rotated q: bf16 rounding of the fp64 value
+    q_rot = d.q_rot.float().cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(q_rot, pr["q_rot"], rtol=2 ** -8, atol=1e-6)
+    # appended codes: equal except a neighbouring code at rounding ties (fp32 vs fp64)
+    kc = d.k_cache.cpu().numpy()
+    vc = d.v_cache.cpu().numpy()
+    diffs = 0
+    for b, L in enumerate(w.seq_lens):
+        p, r = w.page_table[b, L // 64], L % 64
+        for got, want in ((kc[p, :, r, :], pr["k_codes"][b]), (vc[p, :, :, r], pr["v_codes"][b])):
+            dif = np.abs(got.astype(int) - want.astype(int))
+            assert dif.max() <= 1
+            diffs += int((dif > 0).sum())
+    print(f"cfg4 appended E4M3 codes off by one code: {diffs}", flush=True)
+    assert diffs <= 4
+    got = d.output_f64()
+    r = assert_within(got, ref, "fp8", "cfg4")
+    print(f"cfg4 attention: {r}", flush=True)
+    # static schedules on the same (already appended) cache
+    for sched in ("static_splits", "static_chunk"):
+        d.attend(sched)
+        torch.cuda.synchronize()
+        assert_within(d.output_f64(), ref, "fp8", f"cfg4 {sched}")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_bf16_and_fp8_prologue_small(kv_dtype):
+    w = inputs.build_workload("pro", [0, 5, 63, 64, 127, 128, 1000, 4000], 16, 2, kv_dtype, seed=9,
+                              prologue=True, poison=True)
+    pr = opro.prologue(w)
+    got, r, d = run_and_compare(w, "balanced", what="prologue")
+    q_rot = d.q_rot.float().cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(q_rot, pr["q_rot"], rtol=2 ** -8, atol=1e-6)
+
+
+def test_page_permutation_bit_identical_on_gpu():
+    w = inputs.build_workload("perm", [70, 300, 1, 129, 1500], 8, 1, "bf16", seed=3, pool_pages=60)
+    g1, _, _ = run_and_compare(w, "balanced", W=5)
+    perm = np.random.default_rng(4).permutation(w.num_pages)
+    kc = np.empty_like(w.k_cache)
+    vc = np.empty_like(w.v_cache)
+    kc[perm] = w.k_cache
+    vc[perm] = w.v_cache
+    w.k_cache, w.v_cache = kc, vc
+    w.page_table = np.where(w.page_table >= 0, perm[np.maximum(w.page_table, 0)], -1).astype(np.int32)
+    g2, _, _ = run_and_compare(w, "balanced", W=5)
+    assert np.array_equal(g1, g2)
+
+
+def test_constant_v_returns_it_on_gpu():
+    w = inputs.build_workload("constv", [1, 64, 333, 2000], 8, 1, "bf16", seed=6)
+    u = inputs.bf16_bits(np.random.default_rng(7).standard_normal(128).astype(np.float32))
+    w.v_cache[:] = u[None, None, :, None]
+    from load_balanced_split_amd.runner import DeviceStep
+    d = DeviceStep(w, num_workers=9)
+    d.step("balanced")
+    torch.cuda.synchronize()
+    want = (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    got = d.output_f64()
+    for b in range(4):
+        np.testing.assert_allclose(got[b], np.broadcast_to(want, (8, 128)), rtol=2 ** -7, atol=1e-6)
+
+
+def test_device_errors_are_reported_not_faulted():
+    w = inputs.build_workload("bad", [100, 200, 300], 8, 1, "bf16", seed=8)
+    w.page_table[1, 2] = w.num_pages + 5            # out-of-range page id for request 1
+    from load_balanced_split_amd.runner import DeviceStep
+    d = DeviceStep(w, num_workers=6)
+    d.step("balanced")
+    torch.cuda.synchronize()
+    assert d.device_error(clear=True) & _lib.DEVERR_PAGE_ID
+    assert d.device_error() == 0
+    ref = oracle_out(inputs.build_workload("bad", [100, 200, 300], 8, 1, "bf16", seed=8))
+    got = d.output_f64()
+    assert_within(got[[0, 2]], ref[[0, 2]], "bf16", "requests with valid pages")
+    # a length beyond the page table is reported by the planner
+    d.seq_lens[0] = 64 * w.max_pages + 1
+    d.step("balanced")
+    torch.cuda.synchronize()
+    assert d.device_error(clear=True) & _lib.DEVERR_SEQ_LEN
+    # attention launched with a different worker count than the plan
+    _lib.hpa_plan(d.desc, d.seq_lens, 5, 1, d.plan_ws)
+    d.attend("balanced")
+    torch.cuda.synchronize()
+    assert d.device_error(clear=True) & _lib.DEVERR_PLAN
+
+
+def test_all_empty_and_zero_batch():
+    w = inputs.build_workload("empty", [0, 0, 0], 8, 1, "bf16", seed=1, pool_pages=2)
+    from load_balanced_split_amd.runner import DeviceStep
+    d = DeviceStep(w, num_workers=4)
+    d.out.fill_(1.0)
+    d.step("balanced")
+    torch.cuda.synchronize()
+    assert np.all(d.output_f64() == 0)
+    d.out.fill_(1.0)
+    d.step("static_splits")
+    torch.cuda.synchronize()
+    assert np.all(d.output_f64() == 0)
