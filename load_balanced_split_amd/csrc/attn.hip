@@ -56,13 +56,22 @@ __device__ inline int chunk_dim(int c, int j) {
   return FP8 ? 64 * (c >> 1) + 16 * j + 8 * (c & 1) : 32 * c + 8 * j;
 }
 
-__device__ inline u32x4 load16(const uint8_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+// Raw buffer resources (gfx9 dword3: 32-bit data format). A load whose offset is
+// past num_records returns zeros without touching memory, which turns "no such
+// unit" and "bad page" into ordinary straight-line loads.
+constexpr int kBufDword3 = 0x00020000;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufDword3);
 }
 
-// Uniform base + 32-bit lane offset (lets the compiler use the SGPR-base form).
-__device__ inline u32x4 load16(const uint8_t* base, uint32_t off) {
-  return *reinterpret_cast<const u32x4*>(base + off);
+__device__ inline u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+}
+
+__device__ inline int bload_i32(rsrc_t r, uint32_t soff) {
+  return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(r, 0, static_cast<int>(soff), 0));
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -106,38 +115,40 @@ struct ItemRunner {
   const AttnArgs& a;
   CombineLds& lds;
   int lane, wave, m16, j;
+  uint32_t koff, voff;   // per-lane byte offsets of a unit's K rows and V^T rows
 
   __device__ ItemRunner(const AttnArgs& args, CombineLds& l)
-      : a(args), lds(l), lane(threadIdx.x & 63), wave(threadIdx.x >> 6), m16(threadIdx.x & 15),
-        j((threadIdx.x & 63) >> 4) {}
-
-  // Issue the 16 loads of one unit: tokens [half * UNIT, half * UNIT + UNIT) of page
-  // `pid`, KV head g. Page bases are wave-uniform; per-lane offsets are 32-bit.
-  __device__ void issue(UnitBuf& buf, int pid, int g, int half) {
+      : a(args), lds(l), lane(threadIdx.x & 63),
+        wave(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6))),
+        m16(threadIdx.x & 15), j((threadIdx.x & 63) >> 4) {
     using C = Cfg<FP8>;
-    constexpr uint32_t page_bytes = kPage * kHeadDim * C::EB;
-    const uint8_t* kp = a.k_cache + (uint64_t(pid) * a.hkv + g) * page_bytes;
-    const uint8_t* vp = a.v_cache + (uint64_t(pid) * a.hkv + g) * page_bytes;
+    koff = (row_token<FP8>(0, m16) * kHeadDim + chunk_dim<FP8>(0, j)) * C::EB;
+    voff = (m16 * kPage + C::TS * j) * C::EB;
+  }
+
+  // Issue the 16 loads of one unit: tokens [half * UNIT, half * UNIT + UNIT) of one
+  // (page, KV head). rk / rv cover that page's K and V (num_records 0 when the
+  // unit does not exist or its page id is bad: the loads then return zeros).
+  // Lane offsets are fixed for the kernel; the unit offset goes into soffset.
+  __device__ void issue(UnitBuf& buf, rsrc_t rk, rsrc_t rv, int half) const {
+    using C = Cfg<FP8>;
     const uint32_t tb = half * C::UNIT;
-    // K rows: block b adds 4*b tokens to block 0's row (row_token), chunk c adds dims
-    const uint32_t koff = ((tb + row_token<FP8>(0, m16)) * kHeadDim + chunk_dim<FP8>(0, j)) * C::EB;
+    const uint32_t ks = tb * kHeadDim * C::EB;
     if constexpr (!FP8) {
 #pragma unroll
       for (int b = 0; b < C::NBLK; ++b)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          buf.k[b * 4 + c] = load16(kp + (4 * b * kHeadDim + 32 * c) * 2, koff);
+          buf.k[b * 4 + c] = bload16(rk, koff + (4 * b * kHeadDim + 32 * c) * 2, ks);
     } else {
 #pragma unroll
       for (int b = 0; b < C::NBLK; ++b)
 #pragma unroll
         for (int p = 0; p < 2; ++p)
-          buf.k[b * 2 + p] = load16(kp + 4 * b * kHeadDim + 64 * p, koff);
+          buf.k[b * 2 + p] = bload16(rk, koff + 4 * b * kHeadDim + 64 * p, ks);
     }
-    // V^T rows: dim 16n + m16, tokens tb + TS*j .. +16 bytes
-    const uint32_t voff = (m16 * kPage + tb + C::TS * j) * C::EB;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) buf.v[n] = load16(vp + 16 * n * kPage * C::EB, voff);
+    for (int n = 0; n < 8; ++n) buf.v[n] = bload16(rv, voff, (16 * n * kPage + tb) * C::EB);
   }
 
   __device__ inline bf16x8 k_operand(const UnitBuf& buf, int b, int c) const {
@@ -159,7 +170,7 @@ struct ItemRunner {
   }
 
   // Online-softmax update with one unit: tokens [tok0, tok0 + UNIT) of the sequence.
-  __device__ void compute(const UnitBuf& buf, const bf16x8 (&q)[4], int tok0, int L, float qk_scale,
+  __device__ void compute(UnitBuf& buf, const bf16x8 (&q)[4], int tok0, int L, float qk_scale,
                           float& m_run, float& l_part, f32x4 (&o)[8]) {
     using C = Cfg<FP8>;
     f32x4 sc[C::NBLK];
@@ -209,29 +220,38 @@ struct ItemRunner {
         pk[ks][4 + i] = static_cast<__bf16>(sc[2 * ks + 1][i]);
       }
     }
+    if (partial) {
+      // padding rows may hold anything (NaN included): zero their V bytes, never multiply.
+      // Lane group j holds tokens TS*j .. TS*j + TS-1 of the unit in each V register.
+      const int nvalid = L - tok0 - C::TS * j;     // tokens of this lane's run that are live
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // dword e holds tokens [e * 4 / EB, (e + 1) * 4 / EB) of the run
+          constexpr int per = 4 / C::EB;
+          const int first = e * per;
+          uint32_t keep = 0;
+          if (nvalid >= first + per) keep = 0xffffffffu;
+          else if (nvalid > first) keep = (1u << (8 * C::EB * (nvalid - first))) - 1u;
+          buf.v[n][e] &= keep;
+        }
+      }
+    }
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
 #pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks) {
-        bf16x8 vop = v_operand(buf, n, ks);
-        if (partial) {
-          // padding rows may hold anything (NaN included): zero them, never multiply
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (tok0 + C::TS * j + 8 * ks + e >= L) vop[e] = static_cast<__bf16>(0.f);
-        }
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pk[ks], o[n], 0, 0, 0);
-      }
+      for (int ks = 0; ks < C::KSTEPS; ++ks)
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand(buf, n, ks), pk[ks], o[n], 0, 0, 0);
     }
   }
-
-  __device__ int load_pid(int b, int tile) const { return a.page_table[int64_t(b) * a.max_pages + tile]; }
 
   __device__ bool bad_pid(int pid) const { return pid < 0 || pid >= a.num_pages; }
 
   // One item: all 4 waves; ends with the combine and the output / partial write.
   __device__ void run(const Item it) {
     using C = Cfg<FP8>;
+    constexpr uint32_t page_bytes = kPage * kHeadDim * C::EB;
     const int b = it.s / a.hkv, g = it.s - b * a.hkv;
     const int L = a.seq_lens[b];
     // units: UPT per tile, minus a trailing half-tile that starts past L
@@ -239,60 +259,60 @@ struct ItemRunner {
     if (C::UPT > 1 && it.t1 * kPage - C::UNIT >= L) nu -= 1;
     const float qk_scale = a.sm_scale * kLog2e * (FP8 ? a.k_scale[g] : 1.f);
 
-    // Q^T operand: lane holds head m16, dims chunk_dim(c, j) .. +8
+    // Q^T operand: lane holds head m16, dims chunk_dim(c, j) .. +8 (zeros for heads >= G)
+    const rsrc_t rq = make_rsrc(a.q + (int64_t(b) * a.hq + g * a.group) * kHeadDim,
+                                a.group * kHeadDim * 2);
     bf16x8 q[4];
-    const int h = g * a.group + m16;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (m16 < a.group)
-        v = load16(reinterpret_cast<const uint8_t*>(a.q + (int64_t(b) * a.hq + h) * kHeadDim +
-                                                    chunk_dim<FP8>(c, j)));
-      q[c] = as_bf16x8(v);
-    }
+    for (int c = 0; c < 4; ++c) q[c] = as_bf16x8(bload16(rq, (m16 * kHeadDim + chunk_dim<FP8>(c, j)) * 2, 0));
 
     float m_run = -INFINITY, l_part = 0.f;
     f32x4 o[8];
 #pragma unroll
     for (int n = 0; n < 8; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    int u = wave;
-    if (u < nu) {
+    // page ids come through a buffer resource too (vector loads, ordered with the data)
+    const rsrc_t rpt = make_rsrc(a.page_table + int64_t(b) * a.max_pages, a.max_pages * 4);
+    const uint8_t* kbase = a.k_cache + uint64_t(g) * page_bytes;
+    const uint8_t* vbase = a.v_cache + uint64_t(g) * page_bytes;
+    const uint64_t pstride = uint64_t(a.hkv) * page_bytes;
+    auto tile_of = [&](int u) { return it.t0 + (u < nu ? u : 0) / C::UPT; };
+    // unit u -> resources (empty when u is past the item or its page id is bad)
+    auto unit_rsrc = [&](int u, int pid_raw, rsrc_t& rk, rsrc_t& rv) -> bool {
+      const int pid = __builtin_amdgcn_readfirstlane(pid_raw);
+      const bool ok = u < nu && !bad_pid(pid);
+      const uint64_t off = ok ? uint64_t(pid) * pstride : 0;
+      rk = make_rsrc(kbase + off, ok ? page_bytes : 0);
+      rv = make_rsrc(vbase + off, ok ? page_bytes : 0);
+      return ok;
+    };
+
+    const int u0 = wave;
+    bool any_bad = false;
+    if (u0 < nu) {
       UnitBuf bufA, bufB;
-      bool badA = false, badB = false, any_bad = false;
-      // page id of the unit after the one being issued (tile t0 stands in past the end)
-      int pid_next = load_pid(b, u + kWaves < nu ? it.t0 + (u + kWaves) / C::UPT : it.t0);
-      {
-        int pid = __builtin_amdgcn_readfirstlane(load_pid(b, it.t0 + u / C::UPT));
-        badA = bad_pid(pid);
-        any_bad |= badA;
-        issue(bufA, badA ? 0 : pid, g, u % C::UPT);
-      }
-      for (;;) {
-        // prefetch unit u+4 into B while A is consumed
-        const int uB = u + kWaves;
-        if (uB < nu) {
-          int pid = __builtin_amdgcn_readfirstlane(pid_next);
-          const int un = uB + kWaves;
-          pid_next = load_pid(b, un < nu ? it.t0 + un / C::UPT : it.t0);
-          badB = bad_pid(pid);
-          any_bad |= badB;
-          issue(bufB, badB ? 0 : pid, g, uB % C::UPT);
-        }
-        if (!badA) compute(bufA, q, (it.t0 + u / C::UPT) * kPage + (u % C::UPT) * C::UNIT, L, qk_scale, m_run, l_part, o);
+      rsrc_t rk, rv;
+      int pidA = bload_i32(rpt, tile_of(u0) * 4);
+      int pidB = bload_i32(rpt, tile_of(u0 + kWaves) * 4);
+      bool okA = unit_rsrc(u0, pidA, rk, rv), okB;
+      any_bad |= !okA;
+      issue(bufA, rk, rv, u0 % C::UPT);
+      for (int u = u0;; u += 2 * kWaves) {
+        // unit u + 4 -> B (loads always issued; empty resources past the end)
+        const int uB = u + kWaves, uA = uB + kWaves;
+        okB = unit_rsrc(uB, pidB, rk, rv);
+        any_bad |= uB < nu && !okB;
+        pidA = bload_i32(rpt, tile_of(uA) * 4);
+        issue(bufB, rk, rv, uB % C::UPT);
+        if (okA) compute(bufA, q, (it.t0 + u / C::UPT) * kPage + (u % C::UPT) * C::UNIT, L, qk_scale, m_run, l_part, o);
         if (uB >= nu) break;
-        const int uA = uB + kWaves;
-        if (uA < nu) {
-          int pid = __builtin_amdgcn_readfirstlane(pid_next);
-          const int un = uA + kWaves;
-          pid_next = load_pid(b, un < nu ? it.t0 + un / C::UPT : it.t0);
-          badA = bad_pid(pid);
-          any_bad |= badA;
-          issue(bufA, badA ? 0 : pid, g, uA % C::UPT);
-        }
-        if (!badB) compute(bufB, q, (it.t0 + uB / C::UPT) * kPage + (uB % C::UPT) * C::UNIT, L, qk_scale, m_run, l_part, o);
+        // unit u + 8 -> A
+        okA = unit_rsrc(uA, pidA, rk, rv);
+        any_bad |= uA < nu && !okA;
+        pidB = bload_i32(rpt, tile_of(uA + kWaves) * 4);
+        issue(bufA, rk, rv, uA % C::UPT);
+        if (okB) compute(bufB, q, (it.t0 + uB / C::UPT) * kPage + (uB % C::UPT) * C::UNIT, L, qk_scale, m_run, l_part, o);
         if (uA >= nu) break;
-        u = uA;
       }
       if (any_bad && lane == 0 && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PAGE_ID);
     }
@@ -387,15 +407,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a
   r.run(Item{s, t0, t1, nchunks > 1 ? s * a.static_splits + k : -1});
 }
 
-// Merge: block (i, h) combines head h of the i-th sequence to merge. 512 threads =
-// 32 dim-quads x 16 split-groups. Empty sequences get a zero row.
-constexpr int kMergeThreads = 512;
-constexpr int kMergeGroups = kMergeThreads / 32;
+// Merge: block (i, h, c) combines dims [32c, 32c + 32) of head h of the i-th
+// sequence to merge: out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k with
+// M = max_k m_k. One pass: 256 threads = 8 dim-quads x 32 split groups; each
+// group folds its splits k = kg, kg + 32, ... with a running max, then the 32
+// group states are combined the same way. Empty sequences get a zero row.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeDims = 32;
+constexpr int kMergeQuads = kMergeDims / 4;
+constexpr int kMergeGroups = kMergeThreads / kMergeQuads;
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int balanced) {
-  __shared__ float red[kMergeThreads / 64];
-  __shared__ f32x4 part[kMergeGroups][32];
-  const int hh = blockIdx.y;
+  __shared__ float gm[kMergeGroups], gl[kMergeGroups];
+  __shared__ f32x4 gacc[kMergeGroups][kMergeQuads];
+  const int hh = blockIdx.y, d0 = blockIdx.z * kMergeDims;
   int s, n, base;
   if (balanced) {
     const int32_t* hdr = a.plan + a.po.header;
@@ -416,47 +441,49 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int ba
     base = s * a.static_splits;
   }
   const int b = s / a.hkv, g = s - b * a.hkv;
-  uint16_t* orow = a.out + (int64_t(b) * a.hq + g * a.group + hh) * kHeadDim;
-  const int tid = threadIdx.x, q4 = tid & 31, kg = tid >> 5;
+  uint16_t* orow = a.out + (int64_t(b) * a.hq + g * a.group + hh) * kHeadDim + d0;
+  const int tid = threadIdx.x;
   if (n == 0) {
-    if (tid < kHeadDim) orow[tid] = 0;
+    if (tid < kMergeDims) orow[tid] = 0;
     return;
   }
-  // M = max_k m_k
-  float mx = -INFINITY;
-  for (int k = tid; k < n; k += kMergeThreads) mx = fmaxf(mx, a.part_m[int64_t(base + k) * a.group + hh]);
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  float M = red[0];
-  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w]);
-  __syncthreads();
-  // Lsum = sum_k l_k 2^(m_k - M)
-  float ls = 0.f;
-  for (int k = tid; k < n; k += kMergeThreads) {
-    const int64_t i = int64_t(base + k) * a.group + hh;
-    ls += a.part_l[i] * __builtin_amdgcn_exp2f(a.part_m[i] - M);
-  }
-  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
-  if ((tid & 63) == 0) red[tid >> 6] = ls;
-  __syncthreads();
-  float Ls = 0.f;
-  for (int w = 0; w < kMergeThreads / 64; ++w) Ls += red[w];
-  // acc over splits k = kg, kg + 16, ... for dims 4*q4 .. +3
+  const int q4 = tid % kMergeQuads, kg = tid / kMergeQuads;
+  const int64_t row = int64_t(base) * a.group + hh;            // (slot, head) row of split 0
+  const float* pm = a.part_m + row;
+  const float* pl = a.part_l + row;
+  const float* pa = a.part_acc + row * kHeadDim + d0 + 4 * q4;
+  const int G = a.group;
+  float M = -INFINITY, Ls = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int k = kg; k < n; k += kMergeGroups) {
-    const int64_t i = int64_t(base + k) * a.group + hh;
-    const float f = __builtin_amdgcn_exp2f(a.part_m[i] - M);
-    acc += f * *reinterpret_cast<const f32x4*>(a.part_acc + i * kHeadDim + 4 * q4);
+    const float mk = pm[int64_t(k) * G], lk = pl[int64_t(k) * G];
+    const f32x4 ak = *reinterpret_cast<const f32x4*>(pa + int64_t(k) * G * kHeadDim);
+    const float Mn = fmaxf(M, mk);
+    const float fo = __builtin_amdgcn_exp2f(M - Mn), fk = __builtin_amdgcn_exp2f(mk - Mn);
+    Ls = Ls * fo + lk * fk;
+    acc = acc * fo + ak * fk;
+    M = Mn;
   }
-  part[kg][q4] = acc;
+  if (q4 == 0) {
+    gm[kg] = M;
+    gl[kg] = Ls;
+  }
+  gacc[kg][q4] = acc;
   __syncthreads();
-  if (kg == 0) {
-    f32x4 t = part[0][q4];
-    for (int k = 1; k < kMergeGroups; ++k) t += part[k][q4];
-    const float inv = 1.f / Ls;
+  if (tid < kMergeQuads) {
+    float Mt = -INFINITY;
+    for (int k = 0; k < kMergeGroups; ++k) Mt = fmaxf(Mt, gm[k]);
+    float Lt = 0.f;
+    f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < kMergeGroups; ++k) {
+      const float f = __builtin_amdgcn_exp2f(gm[k] - Mt);      // 0 for groups without splits
+      Lt += f * gl[k];
+      t += f * gacc[k][tid];
+    }
+    const float inv = 1.f / Lt;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) orow[4 * q4 + e] = f32_to_bf16_rne(t[e] * inv);
+    for (int e = 0; e < 4; ++e) orow[4 * tid + e] = f32_to_bf16_rne(t[e] * inv);
   }
 }
 
@@ -490,7 +517,8 @@ hipError_t launch_attn_static(const AttnArgs& a, bool fp8, hipStream_t stream) {
 hipError_t launch_merge(const AttnArgs& a, bool balanced, hipStream_t stream) {
   const int S = a.batch * a.hkv;
   if (S == 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(S, a.group), dim3(kMergeThreads), 0, stream, a, balanced ? 1 : 0);
+  hipLaunchKernelGGL(merge_kernel, dim3(S, a.group, kHeadDim / kMergeDims), dim3(kMergeThreads), 0, stream, a,
+                     balanced ? 1 : 0);
   return hipGetLastError();
 }
 

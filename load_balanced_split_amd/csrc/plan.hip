@@ -17,34 +17,43 @@
 namespace hpa {
 namespace {
 
-// Exclusive scan of one int per thread over the whole block; also returns the total.
-__device__ int block_exclusive_scan(int v, int* tmp /* kPlanThreads/64 + 1 */, int& total) {
+// Exclusive scans of two ints per thread over the whole block (one set of
+// barriers for both); also returns the two totals.
+__device__ void block_exclusive_scan2(int va, int vb, int2* tmp /* kPlanThreads/64 + 1 */, int& ra,
+                                      int& rb, int& ta, int& tb) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   constexpr int nw = kPlanThreads / 64;
-  int x = v;
+  int xa = va, xb = vb;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
+    const int ya = __shfl_up(xa, o, 64), yb = __shfl_up(xb, o, 64);
+    if (lane >= o) {
+      xa += ya;
+      xb += yb;
+    }
   }
-  if (lane == 63) tmp[wid] = x;
+  if (lane == 63) tmp[wid] = make_int2(xa, xb);
   __syncthreads();
   if (wid == 0) {
-    int t = lane < nw ? tmp[lane] : 0;
-    int u = t;
+    const int2 t = lane < nw ? tmp[lane] : make_int2(0, 0);
+    int ua = t.x, ub = t.y;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(u, o, 64);
-      if (lane >= o) u += y;
+      const int ya = __shfl_up(ua, o, 64), yb = __shfl_up(ub, o, 64);
+      if (lane >= o) {
+        ua += ya;
+        ub += yb;
+      }
     }
-    if (lane < nw) tmp[lane] = u - t;
-    if (lane == nw - 1) tmp[nw] = u;
+    if (lane < nw) tmp[lane] = make_int2(ua - t.x, ub - t.y);
+    if (lane == nw - 1) tmp[nw] = make_int2(ua, ub);
   }
   __syncthreads();
-  int r = x - v + tmp[wid];
-  total = tmp[nw];
+  ra = xa - va + tmp[wid].x;
+  rb = xb - vb + tmp[wid].y;
+  ta = tmp[nw].x;
+  tb = tmp[nw].y;
   __syncthreads();
-  return r;
 }
 
 __device__ inline int tiles_of(int L) { return (L + kPage - 1) / kPage; }
@@ -59,20 +68,37 @@ __device__ inline int seq_of_tile(const int32_t* C, int S, int t) {
   return lo;
 }
 
-__device__ inline int owner_of_tile(int64_t t, int64_t Wp, int64_t N) {
-  return static_cast<int>(((t + 1) * Wp - 1) / N);
+// Products (t+1)*W' and (w+1)*N stay below 2^31 for all but huge batches; the
+// 32-bit forms are exact whenever `small` holds.
+__device__ inline int owner_of_tile(int t, int Wp, int N, bool small) {
+  if (small) return static_cast<int>((static_cast<uint32_t>(t + 1) * Wp - 1) / static_cast<uint32_t>(N));
+  return static_cast<int>(((int64_t(t) + 1) * Wp - 1) / N);
 }
 
+__device__ inline int range_begin(int w, int Wp, int N, bool small) {
+  if (small) return static_cast<int>(static_cast<uint32_t>(w) * N / static_cast<uint32_t>(Wp));
+  return static_cast<int>(int64_t(w) * N / Wp);
+}
+
+// Batches up to this many sequences keep the planner's arrays in LDS; larger ones
+// work on the copies in the workspace.
+constexpr int kPlanLdsSeqs = 3072;
+
+template <bool LDS>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ seq_lens, int B, int Hkv, int max_pages, int W, int min_tiles,
     int32_t* __restrict__ ws, PlanOffsets po) {
-  __shared__ int tmp[kPlanThreads / 64 + 1];
+  __shared__ int2 tmp[kPlanThreads / 64 + 1];
   __shared__ int sh_bad;
+  __shared__ int sC[LDS ? kPlanLdsSeqs + 1 : 1];
+  __shared__ int sNE[LDS ? kPlanLdsSeqs + 1 : 1];
+  __shared__ int sNS[LDS ? kPlanLdsSeqs : 1];
+  __shared__ int sPB[LDS ? kPlanLdsSeqs : 1];
   const int tid = threadIdx.x;
   const int S = B * Hkv;
   int32_t* hdr = ws + po.header;
-  int32_t* C = ws + po.C;
-  int32_t* NE = ws + po.ne;
+  int32_t* C = LDS ? sC : ws + po.C;
+  int32_t* NE = LDS ? sNE : ws + po.ne;
   if (tid == 0) sh_bad = 0;
   __syncthreads();
 
@@ -89,9 +115,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       }
       n = tiles_of(L);
     }
-    int tot, tot_ne;
-    int ex = block_exclusive_scan(n, tmp, tot);
-    int ex_ne = block_exclusive_scan(n > 0 ? 1 : 0, tmp, tot_ne);
+    int ex, ex_ne, tot, tot_ne;
+    block_exclusive_scan2(n, n > 0 ? 1 : 0, tmp, ex, ex_ne, tot, tot_ne);
     if (s < S) {
       C[s] = carry + ex;
       NE[s] = carry_ne + ex_ne;
@@ -106,10 +131,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   __syncthreads();
   const int N = carry;
   const int Wp = N == 0 ? 0 : min(W, max(1, N / min_tiles));
+  const bool small = (int64_t(N) + 1) * (int64_t(Wp) + 1) < (int64_t(1) << 31);
 
   // 2. splits per sequence, partial slot bases, merge list
-  int32_t* num_splits = ws + po.num_splits;
-  int32_t* pbase = ws + po.partial_base;
+  int32_t* num_splits = LDS ? sNS : ws + po.num_splits;
+  int32_t* pbase = LDS ? sPB : ws + po.partial_base;
   int32_t* mlist = ws + po.merge_list;
   int carry_p = 0, carry_m = 0;
   for (int base = 0; base < S; base += kPlanThreads) {
@@ -117,12 +143,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     int ns = 0;
     if (s < S) {
       const int c0 = C[s], c1 = C[s + 1];
-      if (c1 > c0) ns = owner_of_tile(c1 - 1, Wp, N) - owner_of_tile(c0, Wp, N) + 1;
+      if (c1 > c0) ns = owner_of_tile(c1 - 1, Wp, N, small) - owner_of_tile(c0, Wp, N, small) + 1;
       num_splits[s] = ns;
     }
-    int tot_p, tot_m;
-    int ex_p = block_exclusive_scan((s < S && ns > 1) ? ns : 0, tmp, tot_p);
-    int ex_m = block_exclusive_scan((s < S && ns != 1) ? 1 : 0, tmp, tot_m);
+    int ex_p, ex_m, tot_p, tot_m;
+    block_exclusive_scan2((s < S && ns > 1) ? ns : 0, (s < S && ns != 1) ? 1 : 0, tmp, ex_p, ex_m, tot_p, tot_m);
     if (s < S) {
       pbase[s] = carry_p + ex_p;
       if (ns != 1) mlist[carry_m + ex_m] = s;
@@ -138,13 +163,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int w = base + tid;
     int cnt = 0;
     if (w < Wp) {
-      const int a = static_cast<int>(int64_t(w) * N / Wp);
-      const int e = static_cast<int>(int64_t(w + 1) * N / Wp);
+      const int a = range_begin(w, Wp, N, small);
+      const int e = range_begin(w + 1, Wp, N, small);
       const int sf = seq_of_tile(C, S, a), sl = seq_of_tile(C, S, e - 1);
       cnt = NE[sl] - NE[sf] + 1;
     }
-    int tot;
-    int ex = block_exclusive_scan(cnt, tmp, tot);
+    int ex, unused, tot, unused_t;
+    block_exclusive_scan2(cnt, 0, tmp, ex, unused, tot, unused_t);
     if (w < Wp) woff[w] = carry_i + ex;
     carry_i += tot;
   }
@@ -158,15 +183,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   int32_t* isp = ws + po.item_split;
   int32_t* isl = ws + po.item_slot;
   for (int w = tid; w < Wp; w += kPlanThreads) {
-    int a = static_cast<int>(int64_t(w) * N / Wp);
-    const int e = static_cast<int>(int64_t(w + 1) * N / Wp);
+    int a = range_begin(w, Wp, N, small);
+    const int e = range_begin(w + 1, Wp, N, small);
     int s = seq_of_tile(C, S, a);
     int pos = woff[w];
     while (a < e) {
       const int c0 = C[s], c1 = C[s + 1];
       if (c1 > c0) {
         const int t1 = min(e, c1);
-        const int split = w - owner_of_tile(c0, Wp, N);
+        const int split = w - owner_of_tile(c0, Wp, N, small);
         is[pos] = s;
         it0[pos] = a - c0;
         it1[pos] = t1 - c0;
@@ -176,6 +201,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         a = t1;
       }
       ++s;
+    }
+  }
+  if (LDS) {
+    // publish the per-sequence arrays
+    for (int s = tid; s <= S; s += kPlanThreads) {
+      ws[po.C + s] = C[s];
+      if (s < S) {
+        ws[po.num_splits + s] = num_splits[s];
+        ws[po.partial_base + s] = pbase[s];
+      }
     }
   }
   if (tid == 0) {
@@ -196,8 +231,12 @@ __global__ void clear_word_kernel(int32_t* w) { *w = 0; }
 
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_pages, int num_workers,
                        int min_tiles, int32_t* plan, const PlanOffsets& po, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch, hkv,
-                     max_pages, num_workers, min_tiles, plan, po);
+  if (int64_t(batch) * hkv <= kPlanLdsSeqs)
+    hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch, hkv,
+                       max_pages, num_workers, min_tiles, plan, po);
+  else
+    hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch, hkv,
+                       max_pages, num_workers, min_tiles, plan, po);
   return hipGetLastError();
 }
 
