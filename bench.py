@@ -10,9 +10,9 @@ Timing:
   device synchronise; the batch is held in R copies used round-robin so that
   R - 1 other copies (more than twice the 256 MB Infinity Cache) are read
   between two uses of the same bytes -- each step reads its KV from HBM.
-* per kernel: a second pass where each step follows a 1 GiB scratch overwrite
-  (cache flush; it also lets the host run ahead) and HIP events on the launch
-  stream bracket the planner, the attention kernel and the merge kernel.
+* per kernel: for each launch kind (planner, attention, merge) a loop of
+  back-to-back launches of that kind alone over the same rotating copies,
+  bracketed by HIP events on the launch stream; average = span / launches.
 * comparison: the same two passes for the static split-KV schedules.
 * CPU baseline: the fp64 oracle timed on the host on the same batch.
 
@@ -43,11 +43,69 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", type=int, default=2, help="0..4 (2 = skewed 1x128K + 31x4K)")
     p.add_argument("--num-workers", type=int, default=0)
-    p.add_argument("--event-steps", type=int, default=30)
+    p.add_argument("--event-steps", type=int, default=60)
     p.add_argument("--no-static", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--trace", action="store_true",
+                   help="use the instrumented build and report per-CU busy time (tail balance) instead")
     return p.parse_args()
+
+
+def balance_report(rec):
+    """Tail balance of one attention launch from per-wave records [blocks, waves, 4]:
+    makespan, per-CU busy time (union of its waves' intervals), worker end times."""
+    t0, t1, hw = rec[..., 0].astype(np.int64), rec[..., 1].astype(np.int64), rec[..., 2]
+    live = t0 > 0
+    start, end = t0[live].min(), t1[live].max()
+    tick_us = 0.01                                   # 100 MHz realtime counter
+    hwid = (hw & 0xFFFFFFFF).astype(np.int64)
+    key = ((hw >> 32).astype(np.int64) << 8) | (((hwid >> 13) & 7) << 5) | (((hwid >> 12) & 1) << 4) | ((hwid >> 8) & 15)
+    busy = {}
+    for k in np.unique(key[live]):
+        sel = live & (key == k)
+        iv = sorted(zip(t0[sel].tolist(), t1[sel].tolist()))
+        tot, cs, ce = 0, iv[0][0], iv[0][1]
+        for a, b in iv[1:]:
+            if a > ce:
+                tot += ce - cs
+                cs, ce = a, b
+            else:
+                ce = max(ce, b)
+        busy[int(k)] = tot + ce - cs
+    bv = np.array(list(busy.values()), np.float64) * tick_us
+    wend = (np.where(live, t1, 0).max(axis=1) - start)[live.any(axis=1)] * tick_us
+    makespan = (end - start) * tick_us
+    return {"makespan_us": round(makespan, 2), "cus": len(bv), "cu_busy_mean_us": round(bv.mean(), 2),
+            "cu_busy_max_us": round(bv.max(), 2), "cu_busy_min_us": round(bv.min(), 2),
+            "cu_busy_max_over_mean": round(bv.max() / bv.mean(), 3),
+            "utilisation": round(bv.mean() / makespan, 3),
+            "worker_end_p50_us": round(float(np.percentile(wend, 50)), 2),
+            "worker_end_p99_us": round(float(np.percentile(wend, 99)), 2),
+            "workgroups": int(live.any(axis=1).sum())}
+
+
+def trace_main(args):
+    """Per-CU busy time of the attention kernel, balanced vs static split-KV."""
+    os.environ["HPA_TRACE"] = "1"
+    import torch
+    from load_balanced_split_amd import _lib, inputs
+    from load_balanced_split_amd.runner import DeviceStep
+    _lib.lib()
+    W = args.num_workers or _lib.hpa_default_num_workers(0)
+    w = inputs.config_workload(args.workload)
+    d = DeviceStep(w, num_workers=W)
+    out = {"metric": "attention tail balance (instrumented build)", "workload": inputs.CONFIG_NAMES[args.workload],
+           "num_workers": W}
+    for sched in ("balanced", "static_splits", "static_chunk"):
+        reps = []
+        for r in range(5):
+            d.partial_ws.zero_()
+            d.step(sched)
+            torch.cuda.synchronize()
+            reps.append(balance_report(d.trace_records()))
+        out[sched] = min(reps, key=lambda x: x["makespan_us"])
+    print(json.dumps(out), flush=True)
 
 
 def algorithmic_bytes(w):
@@ -68,6 +126,8 @@ def algorithmic_bytes(w):
 
 def main():
     args = parse()
+    if args.trace:
+        return trace_main(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU, "
               "see the sharding note in DESIGN.md", file=sys.stderr)
@@ -127,38 +187,35 @@ def main():
         del graphs
         return (t1 - t0) / args.steps
 
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-
-    def event_time(sched):
-        """Per-kernel durations (ms) after a cache flush, from events on the launch stream."""
-        res = {"prologue": [], "plan": [], "attn": [], "merge": [], "step": []}
-        for i in range(args.event_steps):
-            d = copies[i % R]
-            flush.fill_(i & 0xFF)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-            ev[0].record(stream)
-            if w.has_prologue:
-                d.prologue()
-            ev[1].record(stream)
-            if sched == "balanced":
-                d.plan()
-            ev[2].record(stream)
-            d.attend(sched, flags=_lib.ATTN_NO_MERGE)
-            ev[3].record(stream)
-            d.attend(sched, flags=_lib.ATTN_MERGE_ONLY)
-            ev[4].record(stream)
+    def kernel_times(sched):
+        """Average duration (ms) of each launch kind, from HIP events on the launch stream
+        around a loop of back-to-back launches of that kind alone (rotating copies)."""
+        kinds = (["prologue"] if w.has_prologue else []) + (["plan"] if sched == "balanced" else [])
+        kinds += ["attn", "merge"]
+        launch = {
+            "prologue": lambda d: d.prologue(),
+            "plan": lambda d: d.plan(),
+            "attn": lambda d: d.attend(sched, flags=_lib.ATTN_NO_MERGE),
+            "merge": lambda d: d.attend(sched, flags=_lib.ATTN_MERGE_ONLY),
+        }
+        res = {}
+        for kind in kinds:
+            for i in range(R):
+                launch[kind](copies[i])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(args.event_steps):
+                launch[kind](copies[i % R])
+            e1.record(stream)
             torch.cuda.synchronize()
-            res["prologue"].append(ev[0].elapsed_time(ev[1]))
-            res["plan"].append(ev[1].elapsed_time(ev[2]))
-            res["attn"].append(ev[2].elapsed_time(ev[3]))
-            res["merge"].append(ev[3].elapsed_time(ev[4]))
-            res["step"].append(ev[0].elapsed_time(ev[4]))
+            res[kind] = e0.elapsed_time(e1) / args.event_steps
+        for d in copies:
             assert torch.equal(d.out, eager[sched])
-        return {k: float(np.mean(v)) for k, v in res.items()}
+        return res
 
     # balanced (the method) -- headline
     step_s = graph_time("balanced")
-    ev = event_time("balanced")
+    ev = kernel_times("balanced")
     us = step_s * 1e6
     kv_gbps = kv_bytes / step_s / 1e9
     attn_s = ev["attn"] * 1e-3
@@ -181,8 +238,8 @@ def main():
                    "algorithmic_bytes": alg_bytes},
         "us_per_step": round(us, 2),
         "kv_frac_of_peak": round(kv_gbps / PEAK_HBM_GBPS, 4),
-        "kernels_us_cold": {k: round(v * 1e3, 2) for k, v in ev.items()},
-        "attn_plus_merge_kv_gbps_cold": round(kv_bytes / ((ev["attn"] + ev["merge"]) * 1e-3) / 1e9, 1),
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in ev.items()},
+        "attn_plus_merge_kv_gbps": round(kv_bytes / ((ev["attn"] + ev["merge"]) * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "attn_balanced_kernel<bf16>" if w.kv_dtype == "bf16"
                      else "attn_balanced_kernel<fp8>",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -194,24 +251,12 @@ def main():
         st = {}
         for s in scheds[1:]:
             t = graph_time(s)
-            e = event_time(s)
-            st[s] = {"us_per_step": round(t * 1e6, 2), "attn_us_cold": round(e["attn"] * 1e3, 2),
-                     "merge_us_cold": round(e["merge"] * 1e3, 2),
-                     "balanced_speedup": round(t / step_s, 3)}
+            e = kernel_times(s)
+            st[s] = {"us_per_step": round(t * 1e6, 2), "attn_us": round(e["attn"] * 1e3, 2),
+                     "merge_us": round(e["merge"] * 1e3, 2),
+                     "balanced_speedup": round(t / step_s, 3),
+                     "balanced_attn_speedup": round(e["attn"] / ev["attn"], 3)}
         result["static_split_kv"] = st
-    # measured read bandwidth of a plain reduction over 4 GiB (context for the 8 TB/s peak)
-    x = torch.empty(1 << 31, dtype=torch.bfloat16, device=dev).fill_(1)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    x.sum()
-    e0.record()
-    for _ in range(5):
-        x.sum()
-    e1.record()
-    torch.cuda.synchronize()
-    result["stream_read_gbps_measured"] = round(5 * x.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
-    del x
-
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, kv_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -13,7 +13,11 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libhpa.so")
+# HPA_TRACE=1 selects the instrumented build (per-wave timestamps and CU ids of
+# the attention kernels, written after the partial results in the workspace).
+TRACE = os.environ.get("HPA_TRACE", "0") == "1"
+LIB_PATH = os.path.join(PKG, "libhpa_trace.so" if TRACE else "libhpa.so")
+TRACE_WAVES, TRACE_WORDS = 4, 4
 HEADER = os.path.join(os.path.dirname(PKG), "include", "hpa.h")
 
 HPA_KV_BF16, HPA_KV_FP8_E4M3 = 0, 1

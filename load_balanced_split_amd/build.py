@@ -25,15 +25,21 @@ def hipcc():
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(verbose: bool = False) -> str:
+TRACE_LIB = os.path.join(PKG, "libhpa_trace.so")
+
+
+def build(verbose: bool = False, trace: bool = False) -> str:
+    """Compile libhpa.so, or with trace=True the instrumented libhpa_trace.so
+    (per-wave realtime stamps and CU ids of the attention kernels)."""
     cc = hipcc()
-    objdir = os.path.join(PKG, "_build")
+    objdir = os.path.join(PKG, "_build_trace" if trace else "_build")
+    extra = ["-DHPA_TRACE=1"] if trace else []
     os.makedirs(objdir, exist_ok=True)
 
     def compile_one(src):
         obj = os.path.join(objdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
         if r.returncode != 0:
@@ -44,14 +50,16 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    target = TRACE_LIB if trace else LIB
+    tmp = target + ".tmp"
     cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build(verbose=True, trace=True))

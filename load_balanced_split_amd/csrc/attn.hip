@@ -94,6 +94,29 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Per-wave record of the instrumented build, written by lane 0 when the wave ends.
+struct WaveTrace {
+  uint64_t* rec;
+  uint64_t t0;
+  uint32_t units = 0;
+  __device__ explicit WaveTrace(const AttnArgs& a) {
+    rec = (kTraceBuild && a.trace) ? a.trace + (uint64_t(blockIdx.x) * kWaves + (threadIdx.x >> 6)) * kTraceWords
+                                   : nullptr;
+    t0 = kTraceBuild ? __builtin_amdgcn_s_memrealtime() : 0;
+  }
+  __device__ ~WaveTrace() {
+    if (kTraceBuild && rec && (threadIdx.x & 63) == 0) {
+      const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+      const uint64_t hw = static_cast<uint32_t>(__builtin_amdgcn_s_getreg((31 << 11) | 4));   // HW_ID
+      const uint64_t xcc = static_cast<uint32_t>(__builtin_amdgcn_s_getreg((15 << 11) | 20)); // XCC_ID
+      rec[0] = t0;
+      rec[1] = t1;
+      rec[2] = hw | (xcc << 32);
+      rec[3] = units;
+    }
+  }
+};
+
 struct UnitBuf {
   u32x4 k[8];
   u32x4 v[8];
@@ -114,6 +137,7 @@ template <bool FP8>
 struct ItemRunner {
   const AttnArgs& a;
   CombineLds& lds;
+  uint32_t units_done = 0;
   int lane, wave, m16, j;
   uint32_t koff, voff;   // per-lane byte offsets of a unit's K rows and V^T rows
 
@@ -173,6 +197,7 @@ struct ItemRunner {
   __device__ void compute(UnitBuf& buf, const bf16x8 (&q)[4], int tok0, int L, float qk_scale,
                           float& m_run, float& l_part, f32x4 (&o)[8]) {
     using C = Cfg<FP8>;
+    if (kTraceBuild) ++units_done;
     f32x4 sc[C::NBLK];
 #pragma unroll
     for (int b = 0; b < C::NBLK; ++b) {
@@ -364,6 +389,7 @@ struct ItemRunner {
 template <bool FP8>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_balanced_kernel(AttnArgs a) {
   __shared__ CombineLds lds;
+  WaveTrace tr(a);
   const int32_t* hdr = a.plan + a.po.header;
   const int w = blockIdx.x;
   if (hdr[H_W] != static_cast<int>(gridDim.x)) {
@@ -384,12 +410,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_balanced_kernel(AttnArgs
     }
     r.run(it);
   }
+  tr.units = r.units_done;
 }
 
 // Static split-KV: block (s, k) handles chunk k of sequence s.
 template <bool FP8>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a) {
   __shared__ CombineLds lds;
+  WaveTrace tr(a);
   const int s = blockIdx.x / a.static_splits, k = blockIdx.x - s * a.static_splits;
   const int b = s / a.hkv;
   int L = a.seq_lens[b];
@@ -405,6 +433,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a
   const int nchunks = (n + chunk - 1) / chunk;
   ItemRunner<FP8> r(a, lds);
   r.run(Item{s, t0, t1, nchunks > 1 ? s * a.static_splits + k : -1});
+  tr.units = r.units_done;
 }
 
 // Merge: block (i, h, c) combines dims [32c, 32c + 32) of head h of the i-th

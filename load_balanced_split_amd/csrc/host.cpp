@@ -147,7 +147,8 @@ hpa_status hpa_partial_workspace_size(const hpa_attn_desc* desc, int32_t num_wor
   int32_t W = 0;
   if ((st = resolve_workers(num_workers, &W)) != HPA_OK) return st;
   const int64_t S = int64_t(desc->batch) * desc->num_kv_heads;
-  *bytes = static_cast<size_t>(hpa::partial_layout(W + S, desc->num_q_heads / desc->num_kv_heads).total_bytes);
+  *bytes = static_cast<size_t>(hpa::partial_layout(W + S, desc->num_q_heads / desc->num_kv_heads).total_bytes +
+                               hpa::trace_bytes(W + S));
   return HPA_OK;
 }
 
@@ -190,8 +191,9 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   const int64_t S = int64_t(desc->batch) * desc->num_kv_heads;
   const int G = desc->num_q_heads / desc->num_kv_heads;
   const hpa::PartialLayout pl = hpa::partial_layout(W + S, G);
-  if (partial_ws_bytes < static_cast<size_t>(pl.total_bytes))
-    return fail(HPA_ERR_WORKSPACE, "partial workspace %zu bytes < %lld", partial_ws_bytes, (long long)pl.total_bytes);
+  const int64_t need = pl.total_bytes + hpa::trace_bytes(W + S);
+  if (partial_ws_bytes < static_cast<size_t>(need))
+    return fail(HPA_ERR_WORKSPACE, "partial workspace %zu bytes < %lld", partial_ws_bytes, (long long)need);
   const hpa::PlanOffsets po = hpa::plan_offsets(S, W);
   if (sched == HPA_SCHED_BALANCED) {
     if (!plan_ws) return fail(HPA_ERR_INVALID_ARG, "balanced schedule needs plan_ws");
@@ -214,6 +216,7 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   a.part_acc = reinterpret_cast<float*>(pw + pl.acc);
   a.part_m = reinterpret_cast<float*>(pw + pl.m);
   a.part_l = reinterpret_cast<float*>(pw + pl.l);
+  a.trace = hpa::kTraceBuild ? reinterpret_cast<uint64_t*>(pw + pl.total_bytes) : nullptr;
   a.out = static_cast<uint16_t*>(out);
   a.po = po;
   a.batch = desc->batch;

@@ -89,7 +89,21 @@ struct AttnArgs {
   // static schedules
   int static_splits;           // S_split
   int static_chunk;            // fixed chunk (flavour "chunk"), 0 for flavour "splits"
+  // instrumented builds only: per-wave records [block][wave][4] (see kTraceWords)
+  uint64_t* trace;
 };
+
+// Instrumented builds (HPA_TRACE) append a per-wave record area to the partial
+// workspace: for each workgroup (up to W + S of them) and wave, 4 words:
+// start and end of the wave on the 100 MHz realtime counter, the hardware
+// wave/CU id register with the XCC id in the upper half, and the units computed.
+constexpr int kTraceWords = 4;
+#ifdef HPA_TRACE
+constexpr bool kTraceBuild = true;
+#else
+constexpr bool kTraceBuild = false;
+#endif
+inline int64_t trace_bytes(int64_t blocks) { return kTraceBuild ? blocks * kWaves * kTraceWords * 8 : 0; }
 
 // Launch wrappers (defined in the .hip files). Return hipSuccess or the launch error.
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_pages, int num_workers,

@@ -97,5 +97,17 @@ class DeviceStep:
                     item_slot=g("item_slot", nit), num_splits=g("num_splits", S),
                     partial_base=g("partial_base", S), merge_list=g("merge_list", nm))
 
+    def trace_records(self) -> np.ndarray:
+        """Instrumented build only: per-wave records [blocks, waves, 4] of the last
+        attention launch (start, end on the 100 MHz counter; HW_ID | XCC_ID << 32; units)."""
+        if not _lib.TRACE:
+            raise RuntimeError("trace records need the instrumented build (HPA_TRACE=1)")
+        w = self.w
+        S = w.batch * w.hkv
+        base = (self.num_workers + S) * (w.hq // w.hkv) * (128 + 2) * 4
+        raw = self.partial_ws[base:].cpu().numpy()
+        n = (self.num_workers + S) * _lib.TRACE_WAVES * _lib.TRACE_WORDS
+        return raw[: n * 8].view(np.uint64).reshape(self.num_workers + S, _lib.TRACE_WAVES, _lib.TRACE_WORDS)
+
     def output_f64(self) -> np.ndarray:
         return self.out.float().cpu().numpy().astype(np.float64)
