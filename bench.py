@@ -6,8 +6,9 @@ is the skewed batch (1 x 131072 + 31 x 4096 tokens, 8:1 GQA, head dim 128,
 64-token pages, bf16 KV), where the pages report their kernel-level gain.
 
 Timing:
-* headline: K steps replayed from HIP graphs, back to back, bracketed by a
-  device synchronise; the batch is held in R copies used round-robin so that
+* headline: K steps (rounded down to a multiple of R) replayed from one HIP
+  graph holding R steps, back to back, bracketed by a device synchronise; the
+  batch is held in R copies used round-robin so that
   R - 1 other copies (more than twice the 256 MB Infinity Cache) are read
   between two uses of the same bytes -- each step reads its KV from HBM.
 * per kernel: for each launch kind (planner, attention, merge) a loop of
@@ -34,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attn μs/step + achieved KV-read HBM GB/s (% of peak), mixed-length batch"
 PEAK_HBM_GBPS = 8000.0
 MALL_BYTES = 256 << 20
+REALTIME_MHZ = 100.0      # the shader's constant "realtime" counter (s_memrealtime)
 
 
 def parse():
@@ -58,7 +60,7 @@ def balance_report(rec):
     t0, t1, hw = rec[..., 0].astype(np.int64), rec[..., 1].astype(np.int64), rec[..., 2]
     live = t0 > 0
     start, end = t0[live].min(), t1[live].max()
-    tick_us = 0.01                                   # 100 MHz realtime counter
+    tick_us = 1.0 / REALTIME_MHZ
     hwid = (hw & 0xFFFFFFFF).astype(np.int64)
     key = ((hw >> 32).astype(np.int64) << 8) | (((hwid >> 13) & 7) << 5) | (((hwid >> 12) & 1) << 4) | ((hwid >> 8) & 15)
     busy = {}
@@ -96,14 +98,21 @@ def trace_main(args):
     w = inputs.config_workload(args.workload)
     d = DeviceStep(w, num_workers=W)
     out = {"metric": "attention tail balance (instrumented build)", "workload": inputs.CONFIG_NAMES[args.workload],
-           "num_workers": W}
-    for sched in ("balanced", "static_splits", "static_chunk"):
+           "num_workers": W, "realtime_clock_mhz": REALTIME_MHZ}
+    for sched in ("balanced", "fused", "static_splits", "static_chunk"):
         reps = []
         for r in range(5):
-            d.partial_ws.zero_()
-            d.step(sched)
+            d.step(sched)                     # planner (if any) and a full step first
             torch.cuda.synchronize()
-            reps.append(balance_report(d.trace_records()))
+            d.partial_ws[-(W + w.batch * w.hkv) * _lib.TRACE_WAVES * _lib.TRACE_WORDS * 8:].zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            d.attend(sched, flags=_lib.ATTN_NO_MERGE)
+            e1.record()
+            torch.cuda.synchronize()
+            rep = balance_report(d.trace_records())
+            rep["launch_event_us"] = round(e0.elapsed_time(e1) * 1e3, 2)
+            reps.append(rep)
         out[sched] = min(reps, key=lambda x: x["makespan_us"])
     print(json.dumps(out), flush=True)
 
@@ -156,7 +165,7 @@ def main():
         d.step(sched)
 
     # eager reference outputs (also the warm-up of every code path)
-    scheds = ["balanced"] + ([] if args.no_static else ["static_splits", "static_chunk"])
+    scheds = ["balanced", "fused"] + ([] if args.no_static else ["static_splits", "static_chunk"])
     eager = {}
     for s in scheds:
         for d in copies:
@@ -166,26 +175,27 @@ def main():
         assert copies[0].device_error() == 0
 
     def graph_time(sched):
-        graphs = []
-        for d in copies:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+        """Seconds per step: one HIP graph holds one step per copy (R steps), replayed
+        back to back, so host launch cost is paid once per R steps."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for d in copies:
                 run_step(d, sched)
-            graphs.append(g)
         torch.cuda.synchronize()
-        for i in range(args.warmup):
-            graphs[i % R].replay()
+        for i in range(max(1, args.warmup // R)):
+            g.replay()
         torch.cuda.synchronize()
+        reps = max(1, args.steps // R)
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            graphs[i % R].replay()
+        for i in range(reps):
+            g.replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         # every copy's graph output equals the eager output, bit for bit
         for d in copies:
             assert torch.equal(d.out, eager[sched]), f"graph replay of {sched} differs from eager"
-        del graphs
-        return (t1 - t0) / args.steps
+        del g
+        return (t1 - t0) / (reps * R)
 
     def kernel_times(sched):
         """Average duration (ms) of each launch kind, from HIP events on the launch stream
@@ -225,7 +235,7 @@ def main():
         "value": round(kv_gbps, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": max(1, args.steps // R) * R,
         "warmup": args.warmup,
         "ms_per_step": round(step_s * 1e3, 5),
         "higher_is_better": True,
@@ -247,9 +257,15 @@ def main():
     }
     if pro_bytes:
         result["config"]["prologue_bytes"] = pro_bytes
+    # the same work list computed inside the persistent kernel (one launch less)
+    tf = graph_time("fused")
+    ef = kernel_times("fused")
+    result["balanced_fused"] = {"us_per_step": round(tf * 1e6, 2), "kv_gbps": round(kv_bytes / tf / 1e9, 1),
+                                "attn_us": round(ef["attn"] * 1e3, 2), "merge_us": round(ef["merge"] * 1e3, 2),
+                                "kv_frac_of_peak": round(kv_bytes / tf / 1e9 / PEAK_HBM_GBPS, 4)}
     if not args.no_static:
         st = {}
-        for s in scheds[1:]:
+        for s in scheds[2:]:
             t = graph_time(s)
             e = kernel_times(s)
             st[s] = {"us_per_step": round(t * 1e6, 2), "attn_us": round(e["attn"] * 1e3, 2),

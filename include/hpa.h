@@ -58,7 +58,11 @@ typedef enum { HPA_KV_BF16 = 0, HPA_KV_FP8_E4M3 = 1 } hpa_kv_dtype;
 typedef enum {
   HPA_SCHED_BALANCED = 0,      /* work list from hpa_plan (persistent workers) */
   HPA_SCHED_STATIC_SPLITS = 1, /* fixed number of splits per sequence          */
-  HPA_SCHED_STATIC_CHUNK = 2   /* fixed split size, grid sized for the longest */
+  HPA_SCHED_STATIC_CHUNK = 2,  /* fixed split size, grid sized for the longest */
+  HPA_SCHED_BALANCED_FUSED = 3 /* the same balanced work list, computed inside the
+                                  persistent kernel from seq_lens (no hpa_plan call,
+                                  one launch less); at most 2048 sequences, one
+                                  tile per worker minimum */
 } hpa_sched;
 
 /* Sticky device error bits (hpa_read_device_error). */
@@ -123,7 +127,11 @@ enum {
 /* Decode attention: out[b, h] = softmax(sm_scale * q K^T) V over the first
  * seq_lens[b] tokens of request b (a zero row when seq_lens[b] == 0).
  * HPA_SCHED_BALANCED runs the persistent kernel over the plan made by hpa_plan
- * with the same num_workers, then the merge kernel. The static schedules
+ * with the same num_workers, then the merge kernel. HPA_SCHED_BALANCED_FUSED
+ * needs no hpa_plan call: the persistent kernel evaluates the planner's closed
+ * forms itself (same items and slots as hpa_plan with min_tiles 1) and records
+ * each split sequence's split count and slot base in plan_ws for the merge
+ * kernel; both balanced schedules produce identical bits. The static schedules
  * ignore the plan (plan_ws may still be given to receive device errors; NULL
  * otherwise) and size their grid from num_workers. k_scale/v_scale are
  * required for E4M3 caches and ignored for bf16. partial_ws must hold

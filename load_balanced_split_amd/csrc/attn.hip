@@ -62,8 +62,15 @@ __device__ inline int chunk_dim(int c, int j) {
 constexpr int kBufDword3 = 0x00020000;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// Descriptors must live in SGPRs; every base and size here is workgroup-uniform, so
+// readfirstlane only pins them there (a no-op when they already are) and keeps the
+// compiler from wrapping buffer loads in per-lane loops.
 __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufDword3);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), kBufDword3);
 }
 
 __device__ inline u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -124,7 +131,20 @@ struct UnitBuf {
 
 struct Item {
   int s, t0, t1, slot;
+  int nsplit, pbase;     // splits of sequence s and its first partial slot (fused schedule)
 };
+
+// One step of the split combine: fold (mk, lk, ak) into the running (M, L, A).
+// Every combine of split results goes through this function, in the order fixed
+// by kMergeGroup, so all schedules produce the same bits.
+__device__ inline void fold(float& M, float& L, f32x4& A, float mk, float lk, const f32x4& ak) {
+  const float Mn = fmaxf(M, mk);
+  const float fo = __builtin_amdgcn_exp2f(M - Mn), fk = __builtin_amdgcn_exp2f(mk - Mn);
+  L = fmaf(L, fo, lk * fk);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) A[e] = fmaf(A[e], fo, ak[e] * fk);
+  M = Mn;
+}
 
 // Shared state of the 4 waves for the end-of-item combine.
 struct CombineLds {
@@ -133,15 +153,29 @@ struct CombineLds {
   float o[kWaves][kMaxGroup][kORow];
 };
 
+// Everything about one item that is uniform across the workgroup (kept small:
+// descriptors and pointers are re-derived where they are used).
+struct ItemState {
+  Item it;
+  int b, g, nu;
+};
+
+// Per-workgroup driver: 4 waves on one item at a time; wave w takes the item's
+// units w, w+4, ... While one item is combined, the next item's q and page ids
+// are already in flight, and its first unit is issued right after the combine.
 template <bool FP8>
-struct ItemRunner {
+struct Worker {
   const AttnArgs& a;
   CombineLds& lds;
   uint32_t units_done = 0;
   int lane, wave, m16, j;
   uint32_t koff, voff;   // per-lane byte offsets of a unit's K rows and V^T rows
+  // carried from one item to the next
+  bf16x8 q[4];
+  UnitBuf bufA, bufB;
+  int pidA, pidB;
 
-  __device__ ItemRunner(const AttnArgs& args, CombineLds& l)
+  __device__ Worker(const AttnArgs& args, CombineLds& l)
       : a(args), lds(l), lane(threadIdx.x & 63),
         wave(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6))),
         m16(threadIdx.x & 15), j((threadIdx.x & 63) >> 4) {
@@ -273,76 +307,98 @@ struct ItemRunner {
 
   __device__ bool bad_pid(int pid) const { return pid < 0 || pid >= a.num_pages; }
 
-  // One item: all 4 waves; ends with the combine and the output / partial write.
-  __device__ void run(const Item it) {
+  // tile of unit u of the item (clamped into the item, so the page-table read is in bounds)
+  __device__ int tile_of(const ItemState& st, int u) const {
+    using C = Cfg<FP8>;
+    return st.it.t0 + min(u / C::UPT, st.it.t1 - st.it.t0 - 1);
+  }
+
+  __device__ rsrc_t page_row(const ItemState& st) const {
+    return make_rsrc(a.page_table + int64_t(st.b) * a.max_pages, a.max_pages * 4);
+  }
+
+  // unit u -> K/V resources of its (page, KV head) (empty past the item or for a bad page id)
+  __device__ bool unit_rsrc(const ItemState& st, int u, int pid_raw, rsrc_t& rk, rsrc_t& rv) const {
     using C = Cfg<FP8>;
     constexpr uint32_t page_bytes = kPage * kHeadDim * C::EB;
-    const int b = it.s / a.hkv, g = it.s - b * a.hkv;
-    const int L = a.seq_lens[b];
-    // units: UPT per tile, minus a trailing half-tile that starts past L
-    int nu = (it.t1 - it.t0) * C::UPT;
-    if (C::UPT > 1 && it.t1 * kPage - C::UNIT >= L) nu -= 1;
-    const float qk_scale = a.sm_scale * kLog2e * (FP8 ? a.k_scale[g] : 1.f);
+    const int pid = __builtin_amdgcn_readfirstlane(pid_raw);
+    const bool ok = u < st.nu && !bad_pid(pid);
+    const uint64_t off = ok ? (uint64_t(pid) * a.hkv + st.g) * page_bytes : 0;
+    rk = make_rsrc(a.k_cache + off, ok ? page_bytes : 0);
+    rv = make_rsrc(a.v_cache + off, ok ? page_bytes : 0);
+    return ok;
+  }
 
-    // Q^T operand: lane holds head m16, dims chunk_dim(c, j) .. +8 (zeros for heads >= G)
-    const rsrc_t rq = make_rsrc(a.q + (int64_t(b) * a.hq + g * a.group) * kHeadDim,
+  // Scalar facts of an item (one scalar load: the request's length).
+  __device__ ItemState prepare(const Item it) const {
+    using C = Cfg<FP8>;
+    ItemState st;
+    st.it = it;
+    // integer division runs on the VALU: bring the (uniform) results back to SGPRs
+    st.b = __builtin_amdgcn_readfirstlane(it.s / a.hkv);
+    st.g = it.s - st.b * a.hkv;
+    const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[st.b]);
+    // units: UPT per tile, minus a trailing half-tile that starts past L
+    st.nu = (it.t1 - it.t0) * C::UPT;
+    if (C::UPT > 1 && it.t1 * kPage - C::UNIT >= L) st.nu -= 1;
+    st.nu = __builtin_amdgcn_readfirstlane(st.nu);
+    return st;
+  }
+
+  // Q^T operand (lane: head m16, dims chunk_dim(c, j) .. +8; zeros for heads >= G)
+  // and the page ids of this wave's first two units. Vector loads only.
+  __device__ void fetch_meta(const ItemState& st) {
+    const rsrc_t rq = make_rsrc(a.q + (int64_t(st.b) * a.hq + st.g * a.group) * kHeadDim,
                                 a.group * kHeadDim * 2);
-    bf16x8 q[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) q[c] = as_bf16x8(bload16(rq, (m16 * kHeadDim + chunk_dim<FP8>(c, j)) * 2, 0));
+    const rsrc_t rpt = page_row(st);
+    pidA = bload_i32(rpt, tile_of(st, wave) * 4);
+    pidB = bload_i32(rpt, tile_of(st, wave + kWaves) * 4);
+  }
 
-    float m_run = -INFINITY, l_part = 0.f;
-    f32x4 o[8];
-#pragma unroll
-    for (int n = 0; n < 8; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Issue this wave's first unit of the item into bufA.
+  __device__ bool issue_first(const ItemState& st) {
+    using C = Cfg<FP8>;
+    rsrc_t rk, rv;
+    const bool ok = unit_rsrc(st, wave, pidA, rk, rv);
+    issue(bufA, rk, rv, wave % C::UPT);
+    if (wave < st.nu && !ok && lane == 0 && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PAGE_ID);
+    return ok;
+  }
 
-    // page ids come through a buffer resource too (vector loads, ordered with the data)
-    const rsrc_t rpt = make_rsrc(a.page_table + int64_t(b) * a.max_pages, a.max_pages * 4);
-    const uint8_t* kbase = a.k_cache + uint64_t(g) * page_bytes;
-    const uint8_t* vbase = a.v_cache + uint64_t(g) * page_bytes;
-    const uint64_t pstride = uint64_t(a.hkv) * page_bytes;
-    auto tile_of = [&](int u) { return it.t0 + (u < nu ? u : 0) / C::UPT; };
-    // unit u -> resources (empty when u is past the item or its page id is bad)
-    auto unit_rsrc = [&](int u, int pid_raw, rsrc_t& rk, rsrc_t& rv) -> bool {
-      const int pid = __builtin_amdgcn_readfirstlane(pid_raw);
-      const bool ok = u < nu && !bad_pid(pid);
-      const uint64_t off = ok ? uint64_t(pid) * pstride : 0;
-      rk = make_rsrc(kbase + off, ok ? page_bytes : 0);
-      rv = make_rsrc(vbase + off, ok ? page_bytes : 0);
-      return ok;
-    };
-
+  // Stream this wave's units of the item (the first one already in bufA): the
+  // next unit's 16 loads are always issued before the current one is computed.
+  __device__ void stream(const ItemState& st, bool okA, float& m_run, float& l_part, f32x4 (&o)[8]) {
+    using C = Cfg<FP8>;
+    const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[st.b]);
     const int u0 = wave;
-    bool any_bad = false;
-    if (u0 < nu) {
-      UnitBuf bufA, bufB;
-      rsrc_t rk, rv;
-      int pidA = bload_i32(rpt, tile_of(u0) * 4);
-      int pidB = bload_i32(rpt, tile_of(u0 + kWaves) * 4);
-      bool okA = unit_rsrc(u0, pidA, rk, rv), okB;
-      any_bad |= !okA;
-      issue(bufA, rk, rv, u0 % C::UPT);
-      for (int u = u0;; u += 2 * kWaves) {
-        // unit u + 4 -> B (loads always issued; empty resources past the end)
-        const int uB = u + kWaves, uA = uB + kWaves;
-        okB = unit_rsrc(uB, pidB, rk, rv);
-        any_bad |= uB < nu && !okB;
-        pidA = bload_i32(rpt, tile_of(uA) * 4);
-        issue(bufB, rk, rv, uB % C::UPT);
-        if (okA) compute(bufA, q, (it.t0 + u / C::UPT) * kPage + (u % C::UPT) * C::UNIT, L, qk_scale, m_run, l_part, o);
-        if (uB >= nu) break;
-        // unit u + 8 -> A
-        okA = unit_rsrc(uA, pidA, rk, rv);
-        any_bad |= uA < nu && !okA;
-        pidB = bload_i32(rpt, tile_of(uA + kWaves) * 4);
-        issue(bufA, rk, rv, uA % C::UPT);
-        if (okB) compute(bufB, q, (it.t0 + uB / C::UPT) * kPage + (uB % C::UPT) * C::UNIT, L, qk_scale, m_run, l_part, o);
-        if (uA >= nu) break;
-      }
-      if (any_bad && lane == 0 && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PAGE_ID);
+    if (u0 >= st.nu) return;
+    const float qk_scale = a.sm_scale * kLog2e * (FP8 ? a.k_scale[st.g] : 1.f);
+    const rsrc_t rpt = page_row(st);
+    bool any_bad = false, okB;
+    rsrc_t rk, rv;
+    for (int u = u0;; u += 2 * kWaves) {
+      const int uB = u + kWaves, uA = uB + kWaves;
+      okB = unit_rsrc(st, uB, pidB, rk, rv);
+      any_bad |= uB < st.nu && !okB;
+      pidA = bload_i32(rpt, tile_of(st, uA) * 4);
+      issue(bufB, rk, rv, uB % C::UPT);
+      if (okA) compute(bufA, q, (st.it.t0 + u / C::UPT) * kPage + (u % C::UPT) * C::UNIT, L, qk_scale, m_run, l_part, o);
+      if (uB >= st.nu) break;
+      okA = unit_rsrc(st, uA, pidA, rk, rv);
+      any_bad |= uA < st.nu && !okA;
+      pidB = bload_i32(rpt, tile_of(st, uA + kWaves) * 4);
+      issue(bufA, rk, rv, uA % C::UPT);
+      if (okB) compute(bufB, q, (st.it.t0 + uB / C::UPT) * kPage + (uB % C::UPT) * C::UNIT, L, qk_scale, m_run, l_part, o);
+      if (uA >= st.nu) break;
     }
+    if (any_bad && lane == 0 && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PAGE_ID);
+  }
 
-    // wave state -> LDS: l summed over the 4 lane groups
+  // The 4 waves' (m, l, acc) meet in LDS; one log-sum-exp combine; the output row
+  // (unsplit sequence) or a partial slot (split sequence) is written.
+  __device__ void combine(const ItemState& st, float m_run, float l_part, const f32x4 (&o)[8]) {
     float l_tot = l_part + __shfl_xor(l_part, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
     if (m16 < a.group) {
@@ -355,9 +411,7 @@ struct ItemRunner {
         *reinterpret_cast<f32x4*>(&lds.o[wave][m16][16 * n + 4 * j]) = o[n];
     }
     __syncthreads();
-
-    // combine the 4 waves; write the output row or a partial slot
-    const float vscale = FP8 ? a.v_scale[g] : 1.f;
+    const float vscale = FP8 ? a.v_scale[st.g] : 1.f;
     for (int idx = threadIdx.x; idx < a.group * kHeadDim; idx += kAttnThreads) {
       const int hh = idx >> 7, d = idx & (kHeadDim - 1);
       float M = -INFINITY;
@@ -371,10 +425,10 @@ struct ItemRunner {
         acc += f * lds.o[w][hh][d];
       }
       acc *= vscale;
-      if (it.slot < 0) {
-        a.out[(int64_t(b) * a.hq + g * a.group + hh) * kHeadDim + d] = f32_to_bf16_rne(acc / Ls);
+      if (st.it.slot < 0) {
+        a.out[(int64_t(st.b) * a.hq + st.g * a.group + hh) * kHeadDim + d] = f32_to_bf16_rne(acc / Ls);
       } else {
-        const int64_t sl = it.slot;
+        const int64_t sl = st.it.slot;
         a.part_acc[(sl * a.group + hh) * kHeadDim + d] = acc;
         if (d == 0) {
           a.part_m[sl * a.group + hh] = M;
@@ -383,6 +437,59 @@ struct ItemRunner {
       }
     }
     __syncthreads();
+  }
+
+  // Walk the items a source hands out (src.next(Item&) -> bool, uniform). While
+  // one item is combined, the next item's q and page ids are already in flight;
+  // its first unit is issued right after the combine.
+  template <class Source>
+  __device__ void run(Source& src) {
+    Item it;
+    if (!src.next(it)) return;
+    ItemState st = prepare(it);
+    fetch_meta(st);
+    bool okA = issue_first(st);
+    for (;;) {
+      float m_run = -INFINITY, l_part = 0.f;
+      f32x4 o[8];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      stream(st, okA, m_run, l_part, o);
+      Item nit;
+      const bool more = src.next(nit);
+      ItemState nst;
+      if (more) {
+        nst = prepare(nit);
+        fetch_meta(nst);           // in flight during the combine
+      }
+      combine(st, m_run, l_part, o);
+      if (!more) break;
+      st = nst;
+      okA = issue_first(st);
+    }
+  }
+};
+
+// Items of worker w from the planner's work list.
+struct PlanSource {
+  const AttnArgs& a;
+  int i, i1, S;
+  __device__ bool next(Item& it) {
+    while (i < i1) {
+      // the work list is uniform per workgroup: keep it in scalar registers
+      it = Item{__builtin_amdgcn_readfirstlane(a.plan[a.po.item_s + i]),
+                __builtin_amdgcn_readfirstlane(a.plan[a.po.item_t0 + i]),
+                __builtin_amdgcn_readfirstlane(a.plan[a.po.item_t1 + i]),
+                __builtin_amdgcn_readfirstlane(a.plan[a.po.item_slot + i]), 0, 0};
+      ++i;
+      // a work list that does not fit this launch is reported, never followed
+      if (it.s < 0 || it.s >= S || it.t0 < 0 || it.t1 <= it.t0 || it.t1 > a.max_pages || it.slot >= a.slots) {
+        if (threadIdx.x == 0) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PLAN);
+        continue;
+      }
+      return true;
+    }
+    return false;
   }
 };
 
@@ -397,23 +504,25 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_balanced_kernel(AttnArgs
     return;
   }
   if (w >= hdr[H_WP]) return;
-  const int i0 = a.plan[a.po.worker_off + w], i1 = a.plan[a.po.worker_off + w + 1];
-  ItemRunner<FP8> r(a, lds);
-  const int S = a.batch * a.hkv;
-  for (int i = i0; i < i1; ++i) {
-    Item it{a.plan[a.po.item_s + i], a.plan[a.po.item_t0 + i], a.plan[a.po.item_t1 + i],
-            a.plan[a.po.item_slot + i]};
-    // a work list that does not fit this launch is reported, never followed
-    if (it.s < 0 || it.s >= S || it.t0 < 0 || it.t1 <= it.t0 || it.t1 > a.max_pages || it.slot >= a.slots) {
-      if (threadIdx.x == 0) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PLAN);
-      continue;
-    }
-    r.run(it);
-  }
+  PlanSource src{a, __builtin_amdgcn_readfirstlane(a.plan[a.po.worker_off + w]),
+                 __builtin_amdgcn_readfirstlane(a.plan[a.po.worker_off + w + 1]), a.batch * a.hkv};
+  Worker<FP8> r(a, lds);
+  r.run(src);
   tr.units = r.units_done;
 }
 
-// Static split-KV: block (s, k) handles chunk k of sequence s.
+// One item per workgroup: chunk k of sequence s (static split-KV).
+struct SingleSource {
+  Item item;
+  bool given;
+  __device__ bool next(Item& it) {
+    if (given) return false;
+    given = true;
+    it = item;
+    return true;
+  }
+};
+
 template <bool FP8>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a) {
   __shared__ CombineLds lds;
@@ -431,27 +540,170 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a
   const int t0 = k * chunk, t1 = min(n, t0 + chunk);
   if (t0 >= t1) return;
   const int nchunks = (n + chunk - 1) / chunk;
-  ItemRunner<FP8> r(a, lds);
-  r.run(Item{s, t0, t1, nchunks > 1 ? s * a.static_splits + k : -1});
+  SingleSource src{Item{s, t0, t1, nchunks > 1 ? s * a.static_splits + k : -1, 0, 0}, false};
+  Worker<FP8> r(a, lds);
+  r.run(src);
+  tr.units = r.units_done;
+}
+
+// ---- fused schedule: the planner's closed forms evaluated inside the persistent kernel ----
+// Each workgroup recomputes the tile prefix sum C and the partial-slot bases PB
+// from seq_lens in LDS (the same integer arithmetic as plan_kernel, so the items
+// and slots are identical), then walks its own range. The worker holding split 0
+// of a sequence records (num_splits, partial_base) for the merge kernel.
+struct FusedPlanLds {
+  int C[kFusedMaxSeqs + 1];
+  int PB[kFusedMaxSeqs];
+  int tot[kFusedMaxSeqs / 64];
+};
+
+__device__ inline int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive-scan the per-chunk totals P.tot[0..nch) and add each chunk's offset to
+// arr[chunk * 64 + lane] for the chunks this wave owns; returns the grand total.
+__device__ inline int add_chunk_offsets(FusedPlanLds& P, int* arr, int S, int nch, int lane, int wave) {
+  const int t = lane < nch ? P.tot[lane] : 0;
+  const int xi = wave_incl_scan(t, lane);
+  const int total = __builtin_amdgcn_readfirstlane(__shfl(xi, 63, 64));   // same in every lane
+  const int off = xi - t;
+  for (int ch = wave; ch < nch; ch += kWaves) {
+    const int o = __shfl(off, ch, 64);
+    const int s = ch * 64 + lane;
+    if (s < S) arr[s] += o;
+  }
+  return total;
+}
+
+struct FusedSource {
+  const AttnArgs& a;
+  const FusedPlanLds& P;
+  int w, Wp, N, S;
+  bool small;
+  int pos, e, s;
+  __device__ bool next(Item& it) {
+    while (pos < e) {
+      const int c0 = __builtin_amdgcn_readfirstlane(P.C[s]);
+      const int c1 = __builtin_amdgcn_readfirstlane(P.C[s + 1]);
+      if (c1 > c0) {
+        const int t1 = min(e, c1);
+        const int first = __builtin_amdgcn_readfirstlane(owner_of_tile(c0, Wp, N, small));
+        const int split = w - first;
+        const int ns = __builtin_amdgcn_readfirstlane(owner_of_tile(c1 - 1, Wp, N, small)) - first + 1;
+        const int pb = __builtin_amdgcn_readfirstlane(P.PB[s]);
+        it = Item{s, pos - c0, t1 - c0, ns > 1 ? pb + split : -1, ns, pb};
+        if (split == 0 && threadIdx.x == 0) {          // record for the merge kernel
+          a.plan[a.po.num_splits + s] = ns;
+          a.plan[a.po.partial_base + s] = pb;
+        }
+        pos = t1;
+        ++s;
+        return true;
+      }
+      ++s;
+    }
+    return false;
+  }
+};
+
+template <bool FP8>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_fused_kernel(AttnArgs a) {
+  __shared__ CombineLds lds;
+  __shared__ FusedPlanLds P;
+  WaveTrace tr(a);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int S = a.batch * a.hkv, nch = (S + 63) / 64;
+  // tile counts and their chunk-local exclusive prefix sums
+  int bad = 0;
+  for (int ch = wave; ch < nch; ch += kWaves) {
+    const int s = ch * 64 + lane;
+    int n = 0;
+    if (s < S) {
+      const int L = a.seq_lens[s / a.hkv];
+      if (L < 0 || L > a.max_pages * kPage) bad = 1;
+      else n = tiles_of(L);
+    }
+    const int x = wave_incl_scan(n, lane);
+    if (s < S) P.C[s] = x - n;
+    if (lane == 63) P.tot[ch] = x;
+  }
+  bad = __builtin_amdgcn_readfirstlane(__syncthreads_or(bad));
+  const int N = add_chunk_offsets(P, P.C, S, nch, lane, wave);
+  if (threadIdx.x == 0) P.C[S] = N;
+  __syncthreads();
+  const int W = gridDim.x;
+  const int Wp = __builtin_amdgcn_readfirstlane(N == 0 ? 0 : min(W, max(1, N / a.min_tiles)));
+  const bool small = small_products(N, Wp);
+  // partial-slot bases: exclusive prefix of (num_splits > 1 ? num_splits : 0)
+  for (int ch = wave; ch < nch; ch += kWaves) {
+    const int s = ch * 64 + lane;
+    int v = 0;
+    if (s < S) {
+      const int c0 = P.C[s], c1 = P.C[s + 1];
+      if (c1 > c0) {
+        const int ns = owner_of_tile(c1 - 1, Wp, N, small) - owner_of_tile(c0, Wp, N, small) + 1;
+        v = ns > 1 ? ns : 0;
+      }
+    }
+    const int x = wave_incl_scan(v, lane);
+    if (s < S) P.PB[s] = x - v;
+    if (lane == 63) P.tot[ch] = x;
+  }
+  __syncthreads();
+  add_chunk_offsets(P, P.PB, S, nch, lane, wave);
+  __syncthreads();
+  const int w = blockIdx.x;
+  if (w == 0 && threadIdx.x == 0 && bad && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_SEQ_LEN);
+  // empty (or invalid) sequences own no tile: their zero rows are spread over the workers
+  for (int s = w; s < S; s += W) {
+    if (P.C[s + 1] == P.C[s]) {
+      const int b = s / a.hkv, g = s - b * a.hkv;
+      uint16_t* row = a.out + (int64_t(b) * a.hq + g * a.group) * kHeadDim;
+      for (int i = threadIdx.x; i < a.group * kHeadDim; i += kAttnThreads) row[i] = 0;
+    }
+  }
+  if (w >= Wp) return;
+  const int pos = __builtin_amdgcn_readfirstlane(range_begin(w, Wp, N, small));
+  const int pend = __builtin_amdgcn_readfirstlane(range_begin(w + 1, Wp, N, small));
+  const int s0 = __builtin_amdgcn_readfirstlane(seq_of_tile(P.C, S, pos));
+  FusedSource src{a, P, w, Wp, N, S, small, pos, pend, s0};
+  Worker<FP8> r(a, lds);
+  r.run(src);
   tr.units = r.units_done;
 }
 
 // Merge: block (i, h, c) combines dims [32c, 32c + 32) of head h of the i-th
-// sequence to merge: out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k with
-// M = max_k m_k. One pass: 256 threads = 8 dim-quads x 32 split groups; each
-// group folds its splits k = kg, kg + 32, ... with a running max, then the 32
-// group states are combined the same way. Empty sequences get a zero row.
+// sequence to merge. 256 threads = 8 dim-quads x 32 group lanes: lane group j
+// folds splits [16j, 16j + 16) in order (fold), then the group results are folded
+// in group order -- the same arithmetic, in the same order, as the fused
+// schedule's in-kernel combine. Empty sequences get a zero row.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeDims = 32;
 constexpr int kMergeQuads = kMergeDims / 4;
-constexpr int kMergeGroups = kMergeThreads / kMergeQuads;
+constexpr int kMergeLanes = kMergeThreads / kMergeQuads;
 
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int balanced) {
-  __shared__ float gm[kMergeGroups], gl[kMergeGroups];
-  __shared__ f32x4 gacc[kMergeGroups][kMergeQuads];
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int mode) {
+  __shared__ float gm[kMergeLanes], gl[kMergeLanes];
+  __shared__ f32x4 gacc[kMergeLanes][kMergeQuads];
   const int hh = blockIdx.y, d0 = blockIdx.z * kMergeDims;
   int s, n, base;
-  if (balanced) {
+  if (mode == MERGE_FUSED) {
+    // zero rows of empty requests were written by the attention kernel; the others
+    // read the split count and slot base recorded by their split-0 worker
+    s = blockIdx.x;
+    const int L = a.seq_lens[s / a.hkv];
+    if (L <= 0 || L > a.max_pages * kPage) return;
+    n = a.plan[a.po.num_splits + s];
+    base = a.plan[a.po.partial_base + s];
+    if (n <= 1 || base < 0 || base + n > a.slots) return;
+  } else if (mode == MERGE_PLAN) {
     const int32_t* hdr = a.plan + a.po.header;
     if (hdr[H_W] != a.workers || static_cast<int>(blockIdx.x) >= hdr[H_NMERGE]) return;
     s = a.plan[a.po.merge_list + blockIdx.x];
@@ -476,53 +728,51 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int ba
     if (tid < kMergeDims) orow[tid] = 0;
     return;
   }
-  const int q4 = tid % kMergeQuads, kg = tid / kMergeQuads;
-  const int64_t row = int64_t(base) * a.group + hh;            // (slot, head) row of split 0
-  const float* pm = a.part_m + row;
-  const float* pl = a.part_l + row;
-  const float* pa = a.part_acc + row * kHeadDim + d0 + 4 * q4;
+  const int q4 = tid % kMergeQuads, lj = tid / kMergeQuads;
   const int G = a.group;
-  float M = -INFINITY, Ls = 0.f;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int k = kg; k < n; k += kMergeGroups) {
-    const float mk = pm[int64_t(k) * G], lk = pl[int64_t(k) * G];
-    const f32x4 ak = *reinterpret_cast<const f32x4*>(pa + int64_t(k) * G * kHeadDim);
-    const float Mn = fmaxf(M, mk);
-    const float fo = __builtin_amdgcn_exp2f(M - Mn), fk = __builtin_amdgcn_exp2f(mk - Mn);
-    Ls = Ls * fo + lk * fk;
-    acc = acc * fo + ak * fk;
-    M = Mn;
-  }
-  if (q4 == 0) {
-    gm[kg] = M;
-    gl[kg] = Ls;
-  }
-  gacc[kg][q4] = acc;
-  __syncthreads();
-  if (tid < kMergeQuads) {
-    float Mt = -INFINITY;
-    for (int k = 0; k < kMergeGroups; ++k) Mt = fmaxf(Mt, gm[k]);
-    float Lt = 0.f;
-    f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < kMergeGroups; ++k) {
-      const float f = __builtin_amdgcn_exp2f(gm[k] - Mt);      // 0 for groups without splits
-      Lt += f * gl[k];
-      t += f * gacc[k][tid];
+  const int ngrp = (n + kMergeGroup - 1) / kMergeGroup;
+  float FM = -INFINITY, FL = 0.f;
+  f32x4 FA = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int g0 = 0; g0 < ngrp; g0 += kMergeLanes) {
+    const int gg = g0 + lj;
+    float M = -INFINITY, L = 0.f;
+    f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (gg < ngrp) {
+      const int k1 = min(n, (gg + 1) * kMergeGroup);
+      for (int k = gg * kMergeGroup; k < k1; ++k) {
+        const int64_t r = (int64_t(base) + k) * G + hh;
+        const f32x4 ak = *reinterpret_cast<const f32x4*>(a.part_acc + r * kHeadDim + d0 + 4 * q4);
+        fold(M, L, A, a.part_m[r], a.part_l[r], ak);
+      }
     }
-    const float inv = 1.f / Lt;
+    if (q4 == 0) {
+      gm[lj] = M;
+      gl[lj] = L;
+    }
+    gacc[lj][q4] = A;
+    __syncthreads();
+    if (lj == 0) {
+      const int cnt = min(kMergeLanes, ngrp - g0);
+      for (int j = 0; j < cnt; ++j) fold(FM, FL, FA, gm[j], gl[j], gacc[j][q4]);
+    }
+    __syncthreads();
+  }
+  if (lj == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) orow[4 * tid + e] = f32_to_bf16_rne(t[e] * inv);
+    for (int e = 0; e < 4; ++e) orow[4 * q4 + e] = f32_to_bf16_rne(FA[e] / FL);
   }
 }
 
 }  // namespace
 
 int attn_blocks_per_cu(bool fp8) {
-  int nb = 0;
+  int nb = 0, nf = 0;
   hipError_t e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_balanced_kernel<true>, kAttnThreads, 0)
                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_balanced_kernel<false>, kAttnThreads, 0);
-  return (e == hipSuccess && nb > 0) ? nb : 1;
+  hipError_t f = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, attn_fused_kernel<true>, kAttnThreads, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, attn_fused_kernel<false>, kAttnThreads, 0);
+  if (e != hipSuccess || f != hipSuccess || nb <= 0 || nf <= 0) return 1;
+  return nb < nf ? nb : nf;
 }
 
 hipError_t launch_attn_balanced(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream) {
@@ -543,11 +793,19 @@ hipError_t launch_attn_static(const AttnArgs& a, bool fp8, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const AttnArgs& a, bool balanced, hipStream_t stream) {
+hipError_t launch_attn_fused(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream) {
+  if (fp8)
+    hipLaunchKernelGGL(attn_fused_kernel<true>, dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_fused_kernel<false>, dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const AttnArgs& a, MergeMode mode, hipStream_t stream) {
   const int S = a.batch * a.hkv;
   if (S == 0) return hipSuccess;
   hipLaunchKernelGGL(merge_kernel, dim3(S, a.group, kHeadDim / kMergeDims), dim3(kMergeThreads), 0, stream, a,
-                     balanced ? 1 : 0);
+                     static_cast<int>(mode));
   return hipGetLastError();
 }
 

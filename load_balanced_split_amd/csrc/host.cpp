@@ -177,8 +177,13 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
                            void* out, int32_t flags, hipStream_t stream) {
   hpa_status st = check_desc(desc);
   if (st != HPA_OK) return st;
-  if (sched != HPA_SCHED_BALANCED && sched != HPA_SCHED_STATIC_SPLITS && sched != HPA_SCHED_STATIC_CHUNK)
+  if (sched != HPA_SCHED_BALANCED && sched != HPA_SCHED_STATIC_SPLITS && sched != HPA_SCHED_STATIC_CHUNK &&
+      sched != HPA_SCHED_BALANCED_FUSED)
     return fail(HPA_ERR_INVALID_ARG, "sched %d", static_cast<int>(sched));
+  if (sched == HPA_SCHED_BALANCED_FUSED && int64_t(desc->batch) * desc->num_kv_heads > hpa::kFusedMaxSeqs)
+    return fail(HPA_ERR_UNSUPPORTED, "fused schedule plans at most %d sequences (batch x kv heads)",
+                hpa::kFusedMaxSeqs);
+
   if (flags & ~(HPA_ATTN_NO_MERGE | HPA_ATTN_MERGE_ONLY) || flags == (HPA_ATTN_NO_MERGE | HPA_ATTN_MERGE_ONLY))
     return fail(HPA_ERR_INVALID_ARG, "flags %d", flags);
   if (desc->batch == 0) return HPA_OK;
@@ -195,8 +200,8 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   if (partial_ws_bytes < static_cast<size_t>(need))
     return fail(HPA_ERR_WORKSPACE, "partial workspace %zu bytes < %lld", partial_ws_bytes, (long long)need);
   const hpa::PlanOffsets po = hpa::plan_offsets(S, W);
-  if (sched == HPA_SCHED_BALANCED) {
-    if (!plan_ws) return fail(HPA_ERR_INVALID_ARG, "balanced schedule needs plan_ws");
+  if (sched == HPA_SCHED_BALANCED || sched == HPA_SCHED_BALANCED_FUSED) {
+    if (!plan_ws) return fail(HPA_ERR_INVALID_ARG, "balanced schedules need plan_ws");
     if (plan_ws_bytes < static_cast<size_t>(po.total * 4))
       return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)(po.total * 4));
   } else if (plan_ws && plan_ws_bytes < static_cast<size_t>(po.total * 4)) {
@@ -230,10 +235,13 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   a.slots = W + S;
 
   const bool do_attn = !(flags & HPA_ATTN_MERGE_ONLY), do_merge = !(flags & HPA_ATTN_NO_MERGE);
-  if (sched == HPA_SCHED_BALANCED) {
-    if (do_attn && hpa::launch_attn_balanced(a, fp8, W, stream) != hipSuccess)
+  a.min_tiles = 1;
+  if (sched == HPA_SCHED_BALANCED || sched == HPA_SCHED_BALANCED_FUSED) {
+    const bool fused = sched == HPA_SCHED_BALANCED_FUSED;
+    if (do_attn && (fused ? hpa::launch_attn_fused(a, fp8, W, stream) : hpa::launch_attn_balanced(a, fp8, W, stream)) !=
+                       hipSuccess)
       return fail(HPA_ERR_LAUNCH, "attention launch failed");
-    if (do_merge && hpa::launch_merge(a, true, stream) != hipSuccess)
+    if (do_merge && hpa::launch_merge(a, fused ? hpa::MERGE_FUSED : hpa::MERGE_PLAN, stream) != hipSuccess)
       return fail(HPA_ERR_LAUNCH, "merge launch failed");
     return HPA_OK;
   }
@@ -244,7 +252,8 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
                        ? static_cast<int>((desc->max_pages_per_seq + ss - 1) / ss) : 0;
   if (do_attn && hpa::launch_attn_static(a, fp8, stream) != hipSuccess)
     return fail(HPA_ERR_LAUNCH, "attention launch failed");
-  if (do_merge && hpa::launch_merge(a, false, stream) != hipSuccess) return fail(HPA_ERR_LAUNCH, "merge launch failed");
+  if (do_merge && hpa::launch_merge(a, hpa::MERGE_STATIC, stream) != hipSuccess)
+    return fail(HPA_ERR_LAUNCH, "merge launch failed");
   return HPA_OK;
 }
 

@@ -67,6 +67,11 @@ inline PartialLayout partial_layout(int64_t slots, int64_t G) {
   return p;
 }
 
+// Split results of one sequence are combined in a fixed order: contiguous groups
+// of kMergeGroup splits are folded in split order with a running max, then the
+// group results are folded in group order.
+constexpr int kMergeGroup = 16;
+
 // Everything an attention kernel needs, passed by value.
 struct AttnArgs {
   const uint16_t* q;           // [B, Hq, 128] bf16
@@ -89,6 +94,7 @@ struct AttnArgs {
   // static schedules
   int static_splits;           // S_split
   int static_chunk;            // fixed chunk (flavour "chunk"), 0 for flavour "splits"
+  int min_tiles;               // fused schedule: minimum tiles per active worker
   // instrumented builds only: per-wave records [block][wave][4] (see kTraceWords)
   uint64_t* trace;
 };
@@ -105,12 +111,46 @@ constexpr bool kTraceBuild = false;
 #endif
 inline int64_t trace_bytes(int64_t blocks) { return kTraceBuild ? blocks * kWaves * kTraceWords * 8 : 0; }
 
+// Closed forms of the balanced partition, shared by the planner kernel and the
+// in-kernel planning of the fused schedule. Worker w owns global tiles
+// [w*N/W', (w+1)*N/W'); the owner of tile t is floor(((t+1)*W' - 1)/N).
+// `small` (both products below 2^31) selects exact 32-bit arithmetic.
+__device__ inline int owner_of_tile(int t, int Wp, int N, bool small) {
+  if (small) return static_cast<int>((static_cast<uint32_t>(t + 1) * Wp - 1) / static_cast<uint32_t>(N));
+  return static_cast<int>(((int64_t(t) + 1) * Wp - 1) / N);
+}
+
+__device__ inline int range_begin(int w, int Wp, int N, bool small) {
+  if (small) return static_cast<int>(static_cast<uint32_t>(w) * N / static_cast<uint32_t>(Wp));
+  return static_cast<int>(int64_t(w) * N / Wp);
+}
+
+__device__ inline bool small_products(int N, int Wp) {
+  return (int64_t(N) + 1) * (int64_t(Wp) + 1) < (int64_t(1) << 31);
+}
+
+// Largest s in [0, S) with C[s] <= t, for 0 <= t < C[S].
+__device__ inline int seq_of_tile(const int32_t* C, int S, int t) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (C[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ inline int tiles_of(int L) { return (L + kPage - 1) / kPage; }
+
 // Launch wrappers (defined in the .hip files). Return hipSuccess or the launch error.
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_pages, int num_workers,
                        int min_tiles, int32_t* plan, const PlanOffsets& po, hipStream_t stream);
 hipError_t launch_attn_balanced(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream);
 hipError_t launch_attn_static(const AttnArgs& a, bool fp8, hipStream_t stream);
-hipError_t launch_merge(const AttnArgs& a, bool balanced, hipStream_t stream);
+hipError_t launch_attn_fused(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream);
+// merge modes: which schedule produced the partials
+enum MergeMode : int { MERGE_PLAN = 0, MERGE_STATIC = 1, MERGE_FUSED = 2 };
+hipError_t launch_merge(const AttnArgs& a, MergeMode mode, hipStream_t stream);
+constexpr int kFusedMaxSeqs = 2048;  // sequences (B x Hkv) the fused schedule plans in LDS
 hipError_t launch_prologue(const hpa_attn_desc& d, const uint16_t* q_in, const uint16_t* k_in,
                            const uint16_t* v_in, const float* q_norm_w, const float* k_norm_w,
                            float eps, double rope_theta, const int32_t* positions,

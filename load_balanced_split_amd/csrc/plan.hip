@@ -56,30 +56,6 @@ __device__ void block_exclusive_scan2(int va, int vb, int2* tmp /* kPlanThreads/
   __syncthreads();
 }
 
-__device__ inline int tiles_of(int L) { return (L + kPage - 1) / kPage; }
-
-// Largest s in [0, S) with C[s] <= t, for 0 <= t < C[S].
-__device__ inline int seq_of_tile(const int32_t* C, int S, int t) {
-  int lo = 0, hi = S - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (C[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-// Products (t+1)*W' and (w+1)*N stay below 2^31 for all but huge batches; the
-// 32-bit forms are exact whenever `small` holds.
-__device__ inline int owner_of_tile(int t, int Wp, int N, bool small) {
-  if (small) return static_cast<int>((static_cast<uint32_t>(t + 1) * Wp - 1) / static_cast<uint32_t>(N));
-  return static_cast<int>(((int64_t(t) + 1) * Wp - 1) / N);
-}
-
-__device__ inline int range_begin(int w, int Wp, int N, bool small) {
-  if (small) return static_cast<int>(static_cast<uint32_t>(w) * N / static_cast<uint32_t>(Wp));
-  return static_cast<int>(int64_t(w) * N / Wp);
-}
-
 // Batches up to this many sequences keep the planner's arrays in LDS; larger ones
 // work on the copies in the workspace.
 constexpr int kPlanLdsSeqs = 3072;
@@ -131,7 +107,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   __syncthreads();
   const int N = carry;
   const int Wp = N == 0 ? 0 : min(W, max(1, N / min_tiles));
-  const bool small = (int64_t(N) + 1) * (int64_t(Wp) + 1) < (int64_t(1) << 31);
+  const bool small = small_products(N, Wp);
 
   // 2. splits per sequence, partial slot bases, merge list
   int32_t* num_splits = LDS ? sNS : ws + po.num_splits;

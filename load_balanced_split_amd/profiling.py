@@ -1,0 +1,137 @@
+"""Summaries of rocprofv3 output for the kernels of this library.
+
+    python -m load_balanced_split_amd.profiling stats <rocprof-dir> <title> <command>
+    python -m load_balanced_split_amd.profiling pmc <fetch-dir> <write-dir> <title> <command>
+
+`stats` reads a `--kernel-trace --stats` run (CSV or rocpd database) and prints
+per-kernel call counts and durations. `pmc` reads two `--pmc` runs (FETCH_SIZE,
+then WRITE_SIZE, KiB per dispatch), calibrates both counters on the plain copy
+kernel that `bench.py --pmc-run` launches over a buffer of known size, and
+prints the HBM bytes per launch of each kernel, plus a JSON block that bench.py
+reads back (tagged with a hash of the kernel sources, so a stale reading is
+never reported for changed kernels).
+"""
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sqlite3
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CALIBRATION_BYTES = 1 << 30          # bench.py --pmc-run copies this many bytes
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    for key in ("attn_balanced_kernel<false>", "attn_balanced_kernel<true>", "attn_fused_kernel<false>",
+                "attn_fused_kernel<true>", "attn_static_kernel<false>", "attn_static_kernel<true>",
+                "merge_kernel", "plan_kernel", "prologue_kernel"):
+        if key in name:
+            return key
+    if "copy" in name.lower() or "CopyFunctor" in name:
+        return "copy:" + name[:60]
+    return name[:70]
+
+
+def _kernel_rows(d):
+    """(name, duration_ns) of every dispatch in a rocprofv3 output directory."""
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            rows.append((r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    if rows:
+        return rows
+    for f in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+        db = sqlite3.connect(f)
+        rows += [(n, e - s) for n, s, e in db.execute("select name, start, end from kernels")]
+    return rows
+
+
+def stats(d, title, command):
+    agg = {}
+    for name, dur in _kernel_rows(d):
+        agg.setdefault(short_name(name), []).append(dur / 1000.0)
+    lines = [f"# {title}", "", f"command: {command}", "",
+             f"{'kernel':44s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_us':>10s}"]
+    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{k:44s} {len(v):6d} {sum(v) / len(v):9.2f} {min(v):9.2f} {max(v):9.2f} {sum(v):10.1f}")
+    return "\n".join(lines)
+
+
+def _pmc_rows(d, counter):
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if rows:
+        return rows
+    for f in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+        db = sqlite3.connect(f)
+        try:
+            q = ("select k.name, sum(p.value) from pmc_events p join kernels k on p.event_id = k.id "
+                 "where p.counter_name = ? group by p.event_id")
+            rows += list(db.execute(q, (counter,)))
+        except sqlite3.Error:
+            pass
+    return rows
+
+
+def pmc(fetch_dir, write_dir, title, command):
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for name, kib in _pmc_rows(d, counter):
+            per.setdefault(short_name(name), {}).setdefault(counter, []).append(kib)
+    copy = [k for k in per if k.startswith("copy:")]
+    if not copy:
+        raise SystemExit("no copy kernel in the PMC runs: cannot calibrate")
+    c = per[copy[0]]
+    known_kib = CALIBRATION_BYTES / 1024.0
+    f_fetch = known_kib / (sum(c["FETCH_SIZE"]) / len(c["FETCH_SIZE"]))
+    f_write = known_kib / (sum(c["WRITE_SIZE"]) / len(c["WRITE_SIZE"]))
+    lines = [f"# {title}", "", f"command: {command}", "",
+             f"calibration: copy of {CALIBRATION_BYTES} bytes -> FETCH_SIZE x {f_fetch:.4f}, WRITE_SIZE x {f_write:.4f}",
+             "", f"{'kernel':44s} {'fetch_KiB':>12s} {'write_KiB':>12s} {'hbm_bytes_per_launch':>22s}"]
+    out = {"source_hash": source_hash(), "fetch_factor": f_fetch, "write_factor": f_write, "kernels": {}}
+    for k, v in sorted(per.items()):
+        fe = sum(v.get("FETCH_SIZE", [0])) / max(1, len(v.get("FETCH_SIZE", [])))
+        wr = sum(v.get("WRITE_SIZE", [0])) / max(1, len(v.get("WRITE_SIZE", [])))
+        hbm = (fe * f_fetch + wr * f_write) * 1024.0
+        out["kernels"][k] = {"fetch_kib": fe, "write_kib": wr, "hbm_bytes": hbm}
+        lines.append(f"{k:44s} {fe:12.1f} {wr:12.1f} {hbm:22.0f}")
+    lines += ["", "json: " + json.dumps(out)]
+    return "\n".join(lines)
+
+
+def read_traffic(summary_path, kernel):
+    """HBM bytes per launch of `kernel` from a pmc summary, or None when the summary is
+    missing or was taken on different kernel sources."""
+    if not os.path.exists(summary_path):
+        return None
+    for line in open(summary_path):
+        if line.startswith("json: "):
+            data = json.loads(line[6:])
+            if data.get("source_hash") != source_hash():
+                return None
+            k = data["kernels"].get(kernel)
+            return None if k is None else k["hbm_bytes"]
+    return None
+
+
+if __name__ == "__main__":
+    mode = sys.argv[1]
+    if mode == "stats":
+        print(stats(sys.argv[2], sys.argv[3], sys.argv[4]))
+    elif mode == "pmc":
+        print(pmc(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5]))
+    else:
+        raise SystemExit(__doc__)

@@ -125,10 +125,16 @@ def test_edge_lengths_all_schedules(kv_dtype, heads):
     hq, hkv = heads
     w = inputs.build_workload("edge", EDGE_LENS, hq, hkv, kv_dtype, seed=5, pool_pages=60, poison=True)
     ref = oracle_out(w)
+    outs = {}
     for sched, W in [("balanced", 0), ("balanced", 1), ("balanced", 3), ("balanced", 37),
+                     ("fused", 0), ("fused", 1), ("fused", 3), ("fused", 37),
                      ("static_splits", 0), ("static_splits", 5), ("static_chunk", 0), ("static_chunk", 9)]:
         got, r, _ = run_and_compare(w, sched, W, ref=ref, what=f"{kv_dtype} {hq}:{hkv}")
         assert np.all(got[0] == 0)                      # empty request -> zero row
+        outs[(sched, W)] = got
+    # the fused schedule computes the planner's work list in-kernel: identical bits
+    for W in (0, 1, 3, 37):
+        assert np.array_equal(outs[("balanced", W)], outs[("fused", W)])
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
@@ -139,7 +145,8 @@ def test_random_batches(kv_dtype):
         lens = rng.integers(0, 3000, size=B)
         w = inputs.build_workload("rand", lens, 8, 1, kv_dtype, seed=int(rng.integers(1 << 30)), poison=trial % 2 == 0)
         ref = oracle_out(w)
-        for sched, W in [("balanced", 0), ("balanced", int(rng.integers(1, 50))), ("static_splits", 0)]:
+        W_r = int(rng.integers(1, 50))
+        for sched, W in [("balanced", 0), ("balanced", W_r), ("fused", W_r), ("static_splits", 0)]:
             run_and_compare(w, sched, W, min_tiles=int(rng.integers(1, 4)), ref=ref, what=f"trial{trial}")
 
 
@@ -156,10 +163,11 @@ def test_full_size_bf16_workloads(cfg):
     w = inputs.config_workload(cfg)
     ref = oracle_out(w)
     outs = {}
-    for sched in ("balanced", "static_splits", "static_chunk"):
+    for sched in ("balanced", "fused", "static_splits", "static_chunk"):
         got, r, _ = run_and_compare(w, sched, ref=ref, what=f"cfg{cfg}")
         print(f"cfg{cfg} {sched}: {r}", flush=True)
         outs[sched] = got
+    assert np.array_equal(outs["balanced"], outs["fused"])
     # one worker (no split at all) agrees with the default within tolerance
     if cfg != 3:
         run_and_compare(w, "balanced", W=1, ref=ref, what=f"cfg{cfg} single worker")
@@ -195,8 +203,8 @@ def test_fp8_prologue_workload():
     got = d.output_f64()
     r = assert_within(got, ref, "fp8", "cfg4")
     print(f"cfg4 attention: {r}", flush=True)
-    # static schedules on the same (already appended) cache
-    for sched in ("static_splits", "static_chunk"):
+    # the other schedules on the same (already appended) cache
+    for sched in ("fused", "static_splits", "static_chunk"):
         d.attend(sched)
         torch.cuda.synchronize()
         assert_within(d.output_f64(), ref, "fp8", f"cfg4 {sched}")
@@ -264,6 +272,21 @@ def test_device_errors_are_reported_not_faulted():
     assert d.device_error(clear=True) & _lib.DEVERR_PLAN
 
 
+def test_fused_reports_bad_lengths_and_large_batches_are_refused():
+    w = inputs.build_workload("badf", [100, 200, 300], 8, 1, "bf16", seed=8)
+    from load_balanced_split_amd.runner import DeviceStep
+    d = DeviceStep(w, num_workers=6)
+    d.seq_lens[1] = 64 * w.max_pages + 1
+    d.step("fused")
+    torch.cuda.synchronize()
+    assert d.device_error(clear=True) & _lib.DEVERR_SEQ_LEN
+    big = inputs.build_workload("big", [1] * 2100, 1, 1, "bf16", seed=1)
+    db = DeviceStep(big, num_workers=8)
+    with pytest.raises(_lib.HpaError) as e:
+        db.step("fused")
+    assert e.value.status == 2
+
+
 def test_all_empty_and_zero_batch():
     w = inputs.build_workload("empty", [0, 0, 0], 8, 1, "bf16", seed=1, pool_pages=2)
     from load_balanced_split_amd.runner import DeviceStep
@@ -272,7 +295,8 @@ def test_all_empty_and_zero_batch():
     d.step("balanced")
     torch.cuda.synchronize()
     assert np.all(d.output_f64() == 0)
-    d.out.fill_(1.0)
-    d.step("static_splits")
-    torch.cuda.synchronize()
-    assert np.all(d.output_f64() == 0)
+    for sched in ("static_splits", "fused"):
+        d.out.fill_(1.0)
+        d.step(sched)
+        torch.cuda.synchronize()
+        assert np.all(d.output_f64() == 0)
