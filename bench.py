@@ -51,12 +51,40 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--trace", action="store_true",
                    help="use the instrumented build and report per-CU busy time (tail balance) instead")
+    p.add_argument("--pmc-run", action="store_true",
+                   help="short run for rocprofv3 counter passes: a 1 GiB calibration copy, then a few "
+                        "steps of each balanced schedule over rotating copies")
     return p.parse_args()
 
 
-def balance_report(rec):
+def pmc_main(args):
+    import torch
+    from load_balanced_split_amd import _lib, inputs
+    from load_balanced_split_amd.profiling import CALIBRATION_BYTES
+    from load_balanced_split_amd.runner import DeviceStep
+    _lib.lib()
+    W = args.num_workers or _lib.hpa_default_num_workers(0)
+    w = inputs.config_workload(args.workload)
+    R = max(2, math.ceil(2 * MALL_BYTES / (w.k_cache.nbytes + w.v_cache.nbytes)) + 1)
+    copies = [DeviceStep(w, num_workers=W) for _ in range(min(R, 16))]
+    src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)                                   # the calibration kernel: 1 GiB read + 1 GiB written
+    torch.cuda.synchronize()
+    del src, dst
+    for sched in ("balanced", "fused"):
+        for rep in range(2):
+            for d in copies:
+                d.step(sched)
+        torch.cuda.synchronize()
+    print(json.dumps({"pmc_run": True, "workload": args.workload, "copies": len(copies)}), flush=True)
+
+
+def balance_report(rec, items_per_worker=None):
     """Tail balance of one attention launch from per-wave records [blocks, waves, 4]:
-    makespan, per-CU busy time (union of its waves' intervals), worker end times."""
+    makespan, per-CU busy time (union of its waves' intervals), worker end times
+    (overall, per XCD, and by the number of items a worker had)."""
     t0, t1, hw = rec[..., 0].astype(np.int64), rec[..., 1].astype(np.int64), rec[..., 2]
     live = t0 > 0
     start, end = t0[live].min(), t1[live].max()
@@ -76,14 +104,31 @@ def balance_report(rec):
                 ce = max(ce, b)
         busy[int(k)] = tot + ce - cs
     bv = np.array(list(busy.values()), np.float64) * tick_us
-    wend = (np.where(live, t1, 0).max(axis=1) - start)[live.any(axis=1)] * tick_us
+    xcc_of_worker = ((hw[:, 0] >> 32).astype(np.int64))
+    wl = live.any(axis=1)
+    wend = (np.where(live, t1, 0).max(axis=1) - start)[wl] * tick_us
+    wstart = (np.where(live, t0, np.iinfo(np.int64).max).min(axis=1) - start)[wl] * tick_us
     makespan = (end - start) * tick_us
-    return {"makespan_us": round(makespan, 2), "cus": len(bv), "cu_busy_mean_us": round(bv.mean(), 2),
+    extra = {}
+    wend_all = (np.where(live, t1, 0).max(axis=1) - start) * tick_us
+    extra["worker_end_mean_by_xcd_us"] = {int(x): round(float(wend_all[wl & (xcc_of_worker == x)].mean()), 2)
+                                          for x in np.unique(xcc_of_worker[wl])}
+    if items_per_worker is not None:
+        ipw = np.asarray(items_per_worker)
+        n = min(len(ipw), len(wend_all))
+        extra["worker_end_mean_by_items_us"] = {
+            int(k): [round(float(wend_all[:n][wl[:n] & (ipw[:n] == k)].mean()), 2), int((wl[:n] & (ipw[:n] == k)).sum())]
+            for k in np.unique(ipw[:n][wl[:n]])}
+    return {**extra, "makespan_us": round(makespan, 2), "cus": len(bv), "cu_busy_mean_us": round(bv.mean(), 2),
             "cu_busy_max_us": round(bv.max(), 2), "cu_busy_min_us": round(bv.min(), 2),
             "cu_busy_max_over_mean": round(bv.max() / bv.mean(), 3),
             "utilisation": round(bv.mean() / makespan, 3),
             "worker_end_p50_us": round(float(np.percentile(wend, 50)), 2),
             "worker_end_p99_us": round(float(np.percentile(wend, 99)), 2),
+            "worker_start_p50_us": round(float(np.percentile(wstart, 50)), 2),
+            "worker_start_max_us": round(float(wstart.max()), 2),
+            "worker_busy_p50_us": round(float(np.percentile(wend - wstart, 50)), 2),
+            "worker_busy_p99_us": round(float(np.percentile(wend - wstart, 99)), 2),
             "workgroups": int(live.any(axis=1).sum())}
 
 
@@ -110,7 +155,11 @@ def trace_main(args):
             d.attend(sched, flags=_lib.ATTN_NO_MERGE)
             e1.record()
             torch.cuda.synchronize()
-            rep = balance_report(d.trace_records())
+            ipw = None
+            if sched == "balanced":
+                pa = d.plan_arrays()
+                ipw = np.diff(np.array(pa["worker_off"]))
+            rep = balance_report(d.trace_records(), ipw)
             rep["launch_event_us"] = round(e0.elapsed_time(e1) * 1e3, 2)
             reps.append(rep)
         out[sched] = min(reps, key=lambda x: x["makespan_us"])
@@ -137,6 +186,8 @@ def main():
     args = parse()
     if args.trace:
         return trace_main(args)
+    if args.pmc_run:
+        return pmc_main(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU, "
               "see the sharding note in DESIGN.md", file=sys.stderr)

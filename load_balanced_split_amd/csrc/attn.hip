@@ -738,12 +738,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int mo
     float M = -INFINITY, L = 0.f;
     f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
     if (gg < ngrp) {
-      const int k1 = min(n, (gg + 1) * kMergeGroup);
-      for (int k = gg * kMergeGroup; k < k1; ++k) {
-        const int64_t r = (int64_t(base) + k) * G + hh;
-        const f32x4 ak = *reinterpret_cast<const f32x4*>(a.part_acc + r * kHeadDim + d0 + 4 * q4);
-        fold(M, L, A, a.part_m[r], a.part_l[r], ak);
+      // all of the group's loads go out before the first fold: one round trip per group
+      const int k0 = gg * kMergeGroup, k1 = min(n, k0 + kMergeGroup);
+      float mk[kMergeGroup], lk[kMergeGroup];
+      f32x4 ak[kMergeGroup];
+#pragma unroll
+      for (int i = 0; i < kMergeGroup; ++i) {
+        const int64_t r = (int64_t(base) + min(k0 + i, k1 - 1)) * G + hh;   // in bounds; extra ones unused
+        mk[i] = a.part_m[r];
+        lk[i] = a.part_l[r];
+        ak[i] = *reinterpret_cast<const f32x4*>(a.part_acc + r * kHeadDim + d0 + 4 * q4);
       }
+#pragma unroll
+      for (int i = 0; i < kMergeGroup; ++i)
+        if (k0 + i < k1) fold(M, L, A, mk[i], lk[i], ak[i]);
     }
     if (q4 == 0) {
       gm[lj] = M;
