@@ -27,6 +27,17 @@ must reproduce them bit for bit):
 * merge_list = sequences whose num_splits != 1 (split ones are combined,
   empty ones get a zero output row), in increasing s.
 
+Per-item cost (bitbyai.com "vLLM × HPC-Ops: …", section "Breaking Down the
+Kernels": the scheduler weighs work by progress; here, the plainest form of it):
+each item a worker starts costs a fixed overhead on top of its tiles, so with
+item_cost c > 0 every non-empty sequence is preceded in the global list by c
+virtual tiles. Positions: C'[s] = C[s] + c * (non-empty sequences before s),
+N' = N + c * (non-empty sequences); W' = 0 if N == 0 else min(W, max(1, N' // min_tiles));
+worker w owns positions [w*N' // W', (w+1)*N' // W'); its items are the real
+tiles [C'[s] + c, C'[s] + c + n_s) it owns. c = 0 is the plain partition above.
+A worker whose range covers only virtual positions of a sequence gets no item
+for it, and may get no item at all.
+
 Static split-KV (the comparison the pages describe in the same section):
 flavour "splits" fixes the number of splits per sequence,
 S_split = clamp(ceil(W / S), 1, max_pages), chunk_s = ceil(n_s / S_split);
@@ -53,30 +64,32 @@ def active_workers(N, num_workers, min_tiles):
     return min(num_workers, max(1, N // min_tiles))
 
 
-def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1):
+def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1, item_cost=0):
     n = tile_counts(seq_lens, hkv)
     S = len(n)
     C = [0] * (S + 1)
     for s in range(S):
         C[s + 1] = C[s] + n[s]
     N = C[S]
-    Wp = active_workers(N, num_workers, min_tiles)
+    # global positions: c virtual tiles in front of every non-empty sequence
+    start = [0] * (S + 1)                        # first position of sequence s (virtual part)
+    for s in range(S):
+        start[s + 1] = start[s] + (n[s] + item_cost if n[s] > 0 else 0)
+    Np = start[S]
+    Wp = 0 if N == 0 else min(num_workers, max(1, Np // min_tiles))
 
     items = []                                   # (worker, s, t0, t1)
     worker_off = [0]
     for w in range(Wp):
-        a = w * N // Wp
-        e = (w + 1) * N // Wp
-        s = 0
-        while not (C[s] <= a < C[s + 1]):
-            s += 1
-        while a < e:
-            t1 = min(e, C[s + 1])
-            items.append((w, s, a - C[s], t1 - C[s]))
-            a = t1
-            s += 1
-            while a < e and n[s] == 0:
-                s += 1
+        a = w * Np // Wp
+        e = (w + 1) * Np // Wp
+        for s in range(S):
+            if n[s] == 0:
+                continue
+            r0 = start[s] + item_cost            # real tiles of s: positions [r0, r0 + n_s)
+            lo, hi = max(a, r0), min(e, r0 + n[s])
+            if lo < hi:
+                items.append((w, s, lo - r0, hi - r0))
         worker_off.append(len(items))
 
     num_splits = [0] * S
@@ -93,7 +106,7 @@ def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1):
     slots = [partial_base[s] + k if num_splits[s] > 1 else -1
              for (_, s, _, _), k in zip(items, split)]
     return dict(
-        C=C, N=N, S=S, Wp=Wp, n_items=len(items), worker_off=worker_off,
+        C=C, N=N, Np=Np, S=S, Wp=Wp, n_items=len(items), worker_off=worker_off,
         item_s=[it[1] for it in items], item_t0=[it[2] for it in items],
         item_t1=[it[3] for it in items], item_split=split, item_slot=slots,
         num_splits=num_splits, partial_base=partial_base, n_partials=acc,

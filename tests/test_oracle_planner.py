@@ -19,6 +19,89 @@ def test_hand_worked_tiny_plan():
         assert p[key] == g[key], key
 
 
+def test_hand_worked_item_cost_plans():
+    g = json.load(open(os.path.join(GOLDEN, "plan_item_cost.json")))
+    for case in g["cases"]:
+        p = op.balanced_plan(case["seq_lens"], case["hkv"], case["num_workers"], case["min_tiles"],
+                             case["item_cost"])
+        for key in ("C", "N", "Np", "Wp", "worker_off", "item_s", "item_t0", "item_t1", "item_split",
+                    "item_slot", "num_splits", "partial_base", "n_partials", "merge_list"):
+            assert p[key] == case[key], key
+
+
+def brute_force_cost_plan(seq_lens, hkv, W, min_tiles, cost):
+    """Lay the global list out position by position (cost virtual entries, then the
+    real tiles, for every non-empty sequence), give each position to the worker whose
+    range holds it by scanning the boundaries, then group real tiles by (worker, seq)."""
+    seqs = [-(-int(L) // 64) for L in seq_lens for _ in range(hkv)]
+    layout = []
+    for s, n in enumerate(seqs):
+        if n:
+            layout += [None] * cost + [(s, t) for t in range(n)]
+    Np = len(layout)
+    if sum(seqs) == 0:
+        return []
+    Wp = min(W, max(1, Np // min_tiles))
+    bounds = [w * Np // Wp for w in range(Wp + 1)]
+    groups = {}
+    for k, e in enumerate(layout):
+        w = max(i for i in range(Wp) if bounds[i] <= k)
+        if e is not None:
+            groups.setdefault((w, e[0]), []).append(e[1])
+    return [(w, s, ts[0], ts[-1] + 1) for (w, s), ts in sorted(groups.items())]
+
+
+def test_item_cost_against_brute_force_random():
+    rng = np.random.default_rng(1)
+    for trial in range(300):
+        B = int(rng.integers(1, 9))
+        hkv = int(rng.integers(1, 4))
+        lens = rng.choice([0, 1, 63, 64, 65, 127, 128, 129, 500, 1000], size=B)
+        W = int(rng.integers(1, 40))
+        mt = int(rng.integers(1, 4))
+        c = int(rng.integers(0, 5))
+        p = op.balanced_plan(lens, hkv, W, mt, c)
+        items = []
+        for w in range(p["Wp"]):
+            for i in range(p["worker_off"][w], p["worker_off"][w + 1]):
+                items.append((w, p["item_s"][i], p["item_t0"][i], p["item_t1"][i]))
+        assert items == brute_force_cost_plan(lens, hkv, W, mt, c)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_item_cost_properties(seed):
+    """Every tile once; a worker's charged work (tiles + cost per item) is within
+    one item cost of its share of the extended list; cost 0 is the plain plan."""
+    rng = np.random.default_rng(100 + seed)
+    for trial in range(200):
+        B = int(rng.integers(0, 30))
+        hkv = int(rng.integers(1, 5))
+        lens = rng.integers(0, 5000, size=B)
+        lens[rng.random(B) < 0.2] = 0
+        W = int(rng.integers(1, 600))
+        mt = int(rng.integers(1, 5))
+        c = int(rng.integers(0, 9))
+        p = op.balanced_plan(lens, hkv, W, mt, c)
+        n = op.tile_counts(lens, hkv)
+        if p["N"] == 0:
+            assert p["Wp"] == 0 and p["n_items"] == 0
+            continue
+        assert p["Np"] == p["N"] + c * sum(1 for x in n if x > 0)
+        cover = [np.zeros(x, int) for x in n]
+        for s, t0, t1 in zip(p["item_s"], p["item_t0"], p["item_t1"]):
+            cover[s][t0:t1] += 1
+        assert all((x == 1).all() for x in cover)
+        Np, Wp = p["Np"], p["Wp"]
+        for w in range(Wp):
+            share = (w + 1) * Np // Wp - w * Np // Wp
+            idx = range(p["worker_off"][w], p["worker_off"][w + 1])
+            charged = sum(p["item_t1"][i] - p["item_t0"][i] for i in idx) + c * len(idx)
+            assert share - c <= charged <= share + c
+        if c == 0:
+            q = op.balanced_plan(lens, hkv, W, mt)
+            assert all(p[k] == q[k] for k in q)
+
+
 def brute_force_plan(seq_lens, hkv, W, min_tiles):
     """Enumerate global tiles one by one: owner worker by scanning the worker
     boundaries, owner sequence by scanning the sequence boundaries, then group."""
