@@ -132,6 +132,44 @@ def balance_report(rec, items_per_worker=None):
             "workgroups": int(live.any(axis=1).sum())}
 
 
+def item_phase_report(rec, item_tiles=None):
+    """Per-item phases from the instrumented build (wave 0 of each workgroup): time
+    from the kernel's first wave to its first item, stream time of the first and of
+    later items (per tile when the plan's item sizes are given), the combine, and
+    the gap between one item's combine and the next item's first issue."""
+    from load_balanced_split_amd import _lib
+    t0w = rec[..., 0].astype(np.int64)
+    live = t0w > 0
+    start = t0w[live].min()
+    tick_us = 1.0 / REALTIME_MHZ
+    o = 4 + _lib.TRACE_START
+    ph = rec[:, 0, o:o + 3 * _lib.TRACE_ITEMS].astype(np.int64).reshape(len(rec), _lib.TRACE_ITEMS, 3)
+    su = rec[:, 0, 4:o].astype(np.int64)
+    ok = (su > 0).all(axis=1)
+    startup = [round(float(((su[ok, k] - start) * tick_us).mean()), 3) for k in range(_lib.TRACE_START)] if ok.any() else None
+    first, later, comb, gap, lead = [], [], [], [], []
+    for b in range(len(rec)):
+        for k in range(_lib.TRACE_ITEMS):
+            t_issue, t_end, t_comb = ph[b, k]
+            if t_issue == 0 or t_end == 0 or t_comb == 0:
+                break
+            dur = (t_end - t_issue) * tick_us
+            if item_tiles is not None and b < len(item_tiles) and k < len(item_tiles[b]):
+                dur /= max(1, item_tiles[b][k])
+            (first if k == 0 else later).append(dur)
+            comb.append((t_comb - t_end) * tick_us)
+            if k == 0:
+                lead.append((t_issue - start) * tick_us)
+            elif ph[b, k - 1, 2] > 0:
+                gap.append((t_issue - ph[b, k - 1, 2]) * tick_us)
+    m = lambda x: round(float(np.mean(x)), 3) if x else None
+    unit = "us_per_tile" if item_tiles is not None else "us"
+    return {f"stream_first_item_{unit}": m(first), f"stream_later_items_{unit}": m(later),
+            "later_items": len(later), "combine_us": m(comb), "issue_gap_us": m(gap),
+            "first_issue_after_start_us": m(lead),
+            "startup_us (range, item, length, q+page ids)": startup}
+
+
 def trace_main(args):
     """Per-CU busy time of the attention kernel, balanced vs static split-KV."""
     os.environ["HPA_TRACE"] = "1"
@@ -155,11 +193,16 @@ def trace_main(args):
             d.attend(sched, flags=_lib.ATTN_NO_MERGE)
             e1.record()
             torch.cuda.synchronize()
-            ipw = None
+            ipw, tiles = None, None
             if sched == "balanced":
                 pa = d.plan_arrays()
-                ipw = np.diff(np.array(pa["worker_off"]))
-            rep = balance_report(d.trace_records(), ipw)
+                off = np.array(pa["worker_off"])
+                ipw = np.diff(off)
+                sz = np.array(pa["item_t1"]) - np.array(pa["item_t0"])
+                tiles = [sz[off[i]:off[i + 1]] for i in range(len(off) - 1)]
+            recs = d.trace_records()
+            rep = balance_report(recs, ipw)
+            rep["items"] = item_phase_report(recs, tiles)
             rep["launch_event_us"] = round(e0.elapsed_time(e1) * 1e3, 2)
             reps.append(rep)
         out[sched] = min(reps, key=lambda x: x["makespan_us"])

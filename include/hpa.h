@@ -26,12 +26,23 @@
  * Layouts (row-major, innermost last):
  *  q, q_out        [B, Hq, 128]                    bf16
  *  out             [B, Hq, 128]                    bf16
- *  k_cache         [num_pages, Hkv, 64, 128]       bf16 or OCP E4M3 codes (token-major page)
- *  v_cache         [num_pages, Hkv, 128, 64]       bf16 or OCP E4M3 codes (dim-major page)
+ *  k_cache         [num_pages, Hkv, 8192]          bf16 or OCP E4M3 codes, tiled page blocks
+ *  v_cache         [num_pages, Hkv, 8192]          bf16 or OCP E4M3 codes, tiled page blocks
  *  k_scale,v_scale [Hkv]                           fp32 (E4M3 caches only; value = code * scale)
  *  seq_lens        [B]                             int32, live KV length per request
  *  page_table      [B, max_pages_per_seq]          int32 physical page of each 64-token tile
  * Query head h reads KV head h / (Hq / Hkv). Sequence s = b * Hkv + g.
+ *
+ * Tiled page blocks: block (p, g) holds the 64 tokens x 128 dims of page p for
+ * KV head g, element (token t, dim d) at index
+ *   bf16 K:  t%32 = 8a + 4b + q, d = 32c + 8j + e:  4096 (t/32) + 512 (4b + c) + 8 (16j + 4a + q) + e
+ *   bf16 V:  t%32 = 8j + e,      d = 16n + m:       4096 (t/32) + 512 n + 8 (16j + m) + e
+ *   E4M3 K:  t = 16a + 4b + q,   d = 64p + 16j + e: 1024 (2b + p) + 16 (16j + 4a + q) + e
+ *   E4M3 V:  t = 16j + e,        d = 16n + m:       1024 n + 16 (16j + m) + e
+ * (all digits non-negative and below their radix). Every 1 KB of a block is what
+ * one wave of the attention kernel loads in one 16-byte-per-lane instruction and
+ * feeds to a 16x16x32 matrix-core product, so K and V stream as whole cache lines.
+ * hpa_decode_prologue writes new tokens in this order.
  */
 #ifndef HPA_H
 #define HPA_H
@@ -149,8 +160,8 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
  * Kernels"): for each request b at position pos = positions[b]:
  *   q_out[b,h] = RoPE(RMSNorm(q_in[b,h]; q_norm_w, eps), pos)     (bf16)
  *   k          = RoPE(RMSNorm(k_in[b,g]; k_norm_w, eps), pos)
- *   k_cache[page_table[b, pos/64], g, pos%64, :] = encode(k / k_scale[g])
- *   v_cache[page_table[b, pos/64], g, :, pos%64] = encode(v_in[b,g] / v_scale[g])
+ *   K row pos%64 of block (page_table[b, pos/64], g) = encode(k / k_scale[g])
+ *   V row pos%64 of block (page_table[b, pos/64], g) = encode(v_in[b,g] / v_scale[g])
  *   seq_lens_out[b] = pos + 1
  * RMSNorm is over the 128 dims of a head row with one weight vector per
  * projection; RoPE rotates the pairs (i, i+64) by pos * rope_theta^(-i/64).

@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # the attention kernels, written after the partial results in the workspace).
 TRACE = os.environ.get("HPA_TRACE", "0") == "1"
 LIB_PATH = os.path.join(PKG, "libhpa_trace.so" if TRACE else "libhpa.so")
-TRACE_WAVES, TRACE_WORDS = 4, 4
+TRACE_WAVES, TRACE_WORDS, TRACE_START, TRACE_ITEMS, TRACE_UNITS = 4, 68, 4, 4, 48
 HEADER = os.path.join(os.path.dirname(PKG), "include", "hpa.h")
 
 HPA_KV_BF16, HPA_KV_FP8_E4M3 = 0, 1

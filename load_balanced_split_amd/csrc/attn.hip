@@ -15,10 +15,13 @@
 // (16-byte loads, one unit prefetched while the previous one is computed).
 //   scores  S^T[tok x head] = K[tok x 32 dims] * Q^T[32 dims x head]  (16x16x32, 4 k-chunks)
 //   output  O^T[dim x head] += V^T[dim x 32 tok] * P^T[32 tok x head] (16x16x32)
-// The 8 query heads of a KV head fill half of the 16-wide N side. The V page is
-// stored dim-major so the MFMA A operand (8 consecutive tokens of one dim) is a
-// single 16-byte load. Rows of K are assigned to MFMA rows so that the score
-// registers a lane holds after Q*K^T are exactly the tokens it feeds into P*V.
+// The 8 query heads of a KV head fill half of the 16-wide N side. The pages are
+// stored pre-tiled for these products (layout in hpa_internal.hpp): every load
+// is 16 bytes per lane and reads one contiguous 1 KB, i.e. whole 128-byte lines,
+// so the K/V stream can use the non-temporal (streaming) policy without a line
+// ever being fetched twice. Rows of K are assigned to MFMA rows so that the
+// score registers a lane holds after Q*K^T are exactly the tokens it feeds into
+// P*V.
 #include "hpa_internal.hpp"
 
 #include <cmath>
@@ -73,8 +76,13 @@ __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(ub, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), kBufDword3);
 }
 
+// Cache policy bits of a buffer load: 2 = nt (streaming: KV bytes are read once).
+constexpr int kPolicyDefault = 0;
+constexpr int kPolicyStream = 2;
+
+template <int POLICY = kPolicyDefault>
 __device__ inline u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), POLICY);
 }
 
 __device__ inline int bload_i32(rsrc_t r, uint32_t soff) {
@@ -168,8 +176,10 @@ struct Worker {
   const AttnArgs& a;
   CombineLds& lds;
   uint32_t units_done = 0;
+  uint64_t* trec = nullptr;   // instrumented build: this wave's record
+  int titem = 0;
   int lane, wave, m16, j;
-  uint32_t koff, voff;   // per-lane byte offsets of a unit's K rows and V^T rows
+  uint32_t loff;         // per-lane byte offset inside each 1 KB load
   // carried from one item to the next
   bf16x8 q[4];
   UnitBuf bufA, bufB;
@@ -179,34 +189,24 @@ struct Worker {
       : a(args), lds(l), lane(threadIdx.x & 63),
         wave(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6))),
         m16(threadIdx.x & 15), j((threadIdx.x & 63) >> 4) {
-    using C = Cfg<FP8>;
-    koff = (row_token<FP8>(0, m16) * kHeadDim + chunk_dim<FP8>(0, j)) * C::EB;
-    voff = (m16 * kPage + C::TS * j) * C::EB;
+    loff = 16 * lane;
   }
 
   // Issue the 16 loads of one unit: tokens [half * UNIT, half * UNIT + UNIT) of one
   // (page, KV head). rk / rv cover that page's K and V (num_records 0 when the
   // unit does not exist or its page id is bad: the loads then return zeros).
-  // Lane offsets are fixed for the kernel; the unit offset goes into soffset.
+  // Load i of K (of V) reads unit bytes [1024 i, 1024 i + 1024): register k[i]
+  // is then score block i / 4, k-chunk i % 4 (bf16) or block i / 2, k-chunks
+  // 2 (i % 2), +1 (E4M3); register v[i] is output rows 16 i .. 16 i + 15.
   __device__ void issue(UnitBuf& buf, rsrc_t rk, rsrc_t rv, int half) const {
     using C = Cfg<FP8>;
-    const uint32_t tb = half * C::UNIT;
-    const uint32_t ks = tb * kHeadDim * C::EB;
-    if constexpr (!FP8) {
+    const uint32_t ub = half * C::UNIT * kHeadDim * C::EB;
 #pragma unroll
-      for (int b = 0; b < C::NBLK; ++b)
+    for (int i = 0; i < 8; ++i)   // the immediate offset field holds < 4096: 4 KB steps go to soffset
+      buf.k[i] = bload16<kPolicyStream>(rk, loff + 1024 * (i & 3), ub + 4096 * (i >> 2));
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          buf.k[b * 4 + c] = bload16(rk, koff + (4 * b * kHeadDim + 32 * c) * 2, ks);
-    } else {
-#pragma unroll
-      for (int b = 0; b < C::NBLK; ++b)
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-          buf.k[b * 2 + p] = bload16(rk, koff + 4 * b * kHeadDim + 64 * p, ks);
-    }
-#pragma unroll
-    for (int n = 0; n < 8; ++n) buf.v[n] = bload16(rv, voff, (16 * n * kPage + tb) * C::EB);
+    for (int i = 0; i < 8; ++i)
+      buf.v[i] = bload16<kPolicyStream>(rv, loff + 1024 * (i & 3), ub + 4096 * (i >> 2));
   }
 
   __device__ inline bf16x8 k_operand(const UnitBuf& buf, int b, int c) const {
@@ -231,7 +231,7 @@ struct Worker {
   __device__ void compute(UnitBuf& buf, const bf16x8 (&q)[4], int tok0, int L, float qk_scale,
                           float& m_run, float& l_part, f32x4 (&o)[8]) {
     using C = Cfg<FP8>;
-    if (kTraceBuild) ++units_done;
+
     f32x4 sc[C::NBLK];
 #pragma unroll
     for (int b = 0; b < C::NBLK; ++b) {
@@ -302,6 +302,11 @@ struct Worker {
 #pragma unroll
       for (int ks = 0; ks < C::KSTEPS; ++ks)
         o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand(buf, n, ks), pk[ks], o[n], 0, 0, 0);
+    }
+    if (kTraceBuild) {   // the unit's data has been consumed by now
+      if (trec && lane == 0 && units_done < kTraceUnits)
+        trec[4 + kTraceStart + 3 * kTraceItems + units_done] = __builtin_amdgcn_s_memrealtime();
+      ++units_done;
     }
   }
 
@@ -442,19 +447,38 @@ struct Worker {
   // Walk the items a source hands out (src.next(Item&) -> bool, uniform). While
   // one item is combined, the next item's q and page ids are already in flight;
   // its first unit is issued right after the combine.
+  __device__ void stamp(int k) {
+    if (kTraceBuild && trec && titem < kTraceItems && lane == 0)
+      trec[4 + kTraceStart + 3 * titem + k] = __builtin_amdgcn_s_memrealtime();
+  }
+
+  // start-up stamp k of the instrumented build, after all of the wave's loads so far
+  __device__ void start_stamp(int k) {
+    if (kTraceBuild && trec) {
+      __builtin_amdgcn_s_waitcnt(0);
+      if (lane == 0) trec[4 + k] = __builtin_amdgcn_s_memrealtime();
+    }
+  }
+
   template <class Source>
   __device__ void run(Source& src) {
+    start_stamp(0);
     Item it;
     if (!src.next(it)) return;
+    start_stamp(1);
     ItemState st = prepare(it);
+    start_stamp(2);
     fetch_meta(st);
+    start_stamp(3);
     bool okA = issue_first(st);
     for (;;) {
       float m_run = -INFINITY, l_part = 0.f;
       f32x4 o[8];
 #pragma unroll
       for (int n = 0; n < 8; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      stamp(0);
       stream(st, okA, m_run, l_part, o);
+      stamp(1);
       Item nit;
       const bool more = src.next(nit);
       ItemState nst;
@@ -463,6 +487,8 @@ struct Worker {
         fetch_meta(nst);           // in flight during the combine
       }
       combine(st, m_run, l_part, o);
+      stamp(2);
+      ++titem;
       if (!more) break;
       st = nst;
       okA = issue_first(st);
@@ -507,6 +533,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_balanced_kernel(AttnArgs
   PlanSource src{a, __builtin_amdgcn_readfirstlane(a.plan[a.po.worker_off + w]),
                  __builtin_amdgcn_readfirstlane(a.plan[a.po.worker_off + w + 1]), a.batch * a.hkv};
   Worker<FP8> r(a, lds);
+  r.trec = tr.rec;
   r.run(src);
   tr.units = r.units_done;
 }
@@ -542,6 +569,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a
   const int nchunks = (n + chunk - 1) / chunk;
   SingleSource src{Item{s, t0, t1, nchunks > 1 ? s * a.static_splits + k : -1, 0, 0}, false};
   Worker<FP8> r(a, lds);
+  r.trec = tr.rec;
   r.run(src);
   tr.units = r.units_done;
 }
@@ -675,6 +703,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fused_kernel(AttnArgs a)
   const int s0 = __builtin_amdgcn_readfirstlane(seq_of_tile(P.C, S, pos));
   FusedSource src{a, P, w, Wp, N, S, small, pos, pend, s0};
   Worker<FP8> r(a, lds);
+  r.trec = tr.rec;
   r.run(src);
   tr.units = r.units_done;
 }

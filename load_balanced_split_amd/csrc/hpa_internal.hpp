@@ -18,6 +18,35 @@ constexpr int kAttnThreads = 64 * kWaves;
 constexpr int kPlanThreads = 1024;
 constexpr int kHeaderInts = 16;
 
+// In-page layout of the KV pools. Each (page, KV head) block holds 64 tokens x
+// 128 dims (16 KB bf16, 8 KB E4M3), ordered so that every 16-byte-per-lane load
+// the attention kernel issues reads one contiguous 1 KB: lane l of load i reads
+// block bytes [i*1024 + 16 l, +16) of its unit (bf16: units of 32 tokens at byte
+// 8192 * (t / 32); E4M3: one unit per block). The element index of (token t,
+// dim d) inside a block:
+//   bf16 K:  t%32 = 8a + 4b + q, d = 32c + 8j + e  ->  4096 (t/32) + 512 (4b + c) + 8 (16j + 4a + q) + e
+//   bf16 V:  t%32 = 8j + e,      d = 16n + m       ->  4096 (t/32) + 512 n + 8 (16j + m) + e
+//   E4M3 K:  t = 16a + 4b + q,   d = 64p + 16j + e ->  1024 (2b + p) + 16 (16j + 4a + q) + e
+//   E4M3 V:  t = 16j + e,        d = 16n + m       ->  1024 n + 16 (16j + m) + e
+// so that lane l = 16j + m of load i holds MFMA operand row m and k-slice j of
+// the 16x16x32 products the kernel forms (scores from K, output from V).
+constexpr int kBlockElems = kPage * kHeadDim;
+__host__ __device__ inline int k_block_index(int t, int d, bool fp8) {
+  if (!fp8) {
+    const int r = t & 31;
+    return 4096 * (t >> 5) + 512 * (4 * ((r >> 2) & 1) + (d >> 5)) +
+           8 * (16 * ((d >> 3) & 3) + 4 * (r >> 3) + (r & 3)) + (d & 7);
+  }
+  return 1024 * (2 * ((t >> 2) & 3) + (d >> 6)) + 16 * (16 * ((d >> 4) & 3) + 4 * (t >> 4) + (t & 3)) + (d & 15);
+}
+__host__ __device__ inline int v_block_index(int t, int d, bool fp8) {
+  if (!fp8) {
+    const int r = t & 31;
+    return 4096 * (t >> 5) + 512 * (d >> 4) + 8 * (16 * (r >> 3) + (d & 15)) + (r & 7);
+  }
+  return 1024 * (d >> 4) + 16 * (16 * (t >> 4) + (d & 15)) + (t & 15);
+}
+
 // Header slots of the plan workspace (int32).
 enum : int {
   H_WP = 0, H_N = 1, H_S = 2, H_NITEMS = 3, H_NMERGE = 4, H_NPART = 5, H_ERR = 6, H_W = 7
@@ -95,15 +124,23 @@ struct AttnArgs {
   int static_splits;           // S_split
   int static_chunk;            // fixed chunk (flavour "chunk"), 0 for flavour "splits"
   int min_tiles;               // fused schedule: minimum tiles per active worker
-  // instrumented builds only: per-wave records [block][wave][4] (see kTraceWords)
+  // instrumented builds only: per-wave records [block][wave][kTraceWords]
   uint64_t* trace;
 };
 
 // Instrumented builds (HPA_TRACE) append a per-wave record area to the partial
-// workspace: for each workgroup (up to W + S of them) and wave, 4 words:
+// workspace: for each workgroup (up to W + S of them) and wave, 16 words:
 // start and end of the wave on the 100 MHz realtime counter, the hardware
-// wave/CU id register with the XCC id in the upper half, and the units computed.
-constexpr int kTraceWords = 4;
+// wave/CU id register with the XCC id in the upper half, the units computed,
+// four start-up times (each after waiting for all of the wave's loads so far:
+// work range known, first item known, its length known, its q and page ids
+// known), then for each of the wave's first kTraceItems items three times: its
+// first unit issued, its last unit computed, its combine done; then the
+// completion times of the wave's first kTraceUnits units.
+constexpr int kTraceItems = 4;
+constexpr int kTraceStart = 4;
+constexpr int kTraceUnits = 48;
+constexpr int kTraceWords = 4 + kTraceStart + 3 * kTraceItems + kTraceUnits;
 #ifdef HPA_TRACE
 constexpr bool kTraceBuild = true;
 #else

@@ -100,29 +100,31 @@ __global__ __launch_bounds__(kProThreads) void prologue_kernel(
         dst[lane + 64] = f32_to_bf16(o1);
       } else {
         const int g = r - hq;
-        const int64_t row = ((int64_t(pid) * hkv + g) * kPage + slot) * kHeadDim;
+        const int64_t blk = (int64_t(pid) * hkv + g) * kBlockElems;
+        const int64_t i0 = blk + k_block_index(slot, lane, fp8), i1 = blk + k_block_index(slot, lane + 64, fp8);
         if (fp8) {
           const float sc = k_scale[g];
-          k_cache[row + lane] = f32_to_e4m3(o0 / sc);
-          k_cache[row + lane + 64] = f32_to_e4m3(o1 / sc);
+          k_cache[i0] = f32_to_e4m3(o0 / sc);
+          k_cache[i1] = f32_to_e4m3(o1 / sc);
         } else {
           uint16_t* kc = reinterpret_cast<uint16_t*>(k_cache);
-          kc[row + lane] = f32_to_bf16(o0);
-          kc[row + lane + 64] = f32_to_bf16(o1);
+          kc[i0] = f32_to_bf16(o0);
+          kc[i1] = f32_to_bf16(o1);
         }
       }
     } else {
       const int g = r - hq - hkv;
       const uint16_t* src = v_in + (int64_t(b) * hkv + g) * kHeadDim;
-      const int64_t base = (int64_t(pid) * hkv + g) * kHeadDim * kPage + slot;   // dim-major page
+      const int64_t blk = (int64_t(pid) * hkv + g) * kBlockElems;
+      const int64_t i0 = blk + v_block_index(slot, lane, fp8), i1 = blk + v_block_index(slot, lane + 64, fp8);
       if (fp8) {
         const float sc = v_scale[g];
-        v_cache[base + int64_t(lane) * kPage] = f32_to_e4m3(bf16_to_f32(src[lane]) / sc);
-        v_cache[base + int64_t(lane + 64) * kPage] = f32_to_e4m3(bf16_to_f32(src[lane + 64]) / sc);
+        v_cache[i0] = f32_to_e4m3(bf16_to_f32(src[lane]) / sc);
+        v_cache[i1] = f32_to_e4m3(bf16_to_f32(src[lane + 64]) / sc);
       } else {
         uint16_t* vc = reinterpret_cast<uint16_t*>(v_cache);
-        vc[base + int64_t(lane) * kPage] = src[lane];
-        vc[base + int64_t(lane + 64) * kPage] = src[lane + 64];
+        vc[i0] = src[lane];
+        vc[i1] = src[lane + 64];
       }
     }
   }

@@ -9,9 +9,10 @@ dtype casts, so no rounding rule is restated here.
 Layouts (little-endian bit patterns held in numpy integer arrays):
 
 * ``q``        uint16 bf16 bits, ``[B, Hq, D]``
-* ``k_cache``  ``[num_pages, Hkv, 64, D]``  (token-major inside a page)
-* ``v_cache``  ``[num_pages, Hkv, D, 64]``  (dim-major inside a page)
-  uint16 bf16 bits, or uint8 OCP E4M3 codes with per-KV-head fp32 scales
+* ``k_cache``, ``v_cache``  ``[num_pages, Hkv, 64 * D]``: one block of 64 tokens
+  x 128 dims per (page, KV head), in the library's tiled in-page order (see
+  ``tile_k`` / ``tile_v``); uint16 bf16 bits, or uint8 OCP E4M3 codes with
+  per-KV-head fp32 scales
 * ``page_table`` int32 ``[B, max_pages]``; entries past a request's pages are -1
 * ``seq_lens`` int32 ``[B]`` live KV length of each request (for workloads with
   the fused prologue: the length before the new token is appended)
@@ -19,8 +20,8 @@ Layouts (little-endian bit patterns held in numpy integer arrays):
 Draw order for one workload (one fresh ``numpy.random.default_rng(seed)``):
 lengths (one vectorised call of size B, when drawn) -> page permutation -> q ->
 K -> V -> (new q, new k, new v, q-norm weight, k-norm weight). K and V are drawn
-in their token-major shape, in chunks of ``_CHUNK_PAGES`` pages, as standard
-normal float32; V is transposed to dim-major per page after drawing.
+in their logical [page, head, token, dim] shape, in chunks of ``_CHUNK_PAGES``
+pages, as standard normal float32, and tiled after encoding.
 """
 
 from __future__ import annotations
@@ -50,8 +51,8 @@ class Workload:
     page_table: np.ndarray         # int32 [B, max_pages]
     num_pages: int
     q: np.ndarray                  # uint16 [B, Hq, D]
-    k_cache: np.ndarray            # uint16|uint8 [P, Hkv, 64, D]
-    v_cache: np.ndarray            # uint16|uint8 [P, Hkv, D, 64]
+    k_cache: np.ndarray            # uint16|uint8 [P, Hkv, 64 * D], tiled (tile_k)
+    v_cache: np.ndarray            # uint16|uint8 [P, Hkv, 64 * D], tiled (tile_v)
     k_scale: Optional[np.ndarray] = None   # float32 [Hkv] (fp8 only)
     v_scale: Optional[np.ndarray] = None
     sm_scale: float = float(np.float32(1.0 / math.sqrt(HEAD_DIM)))
@@ -101,6 +102,43 @@ def e4m3_codes(x: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+# --- the tiled in-page order -------------------------------------------------
+# A page block X[t, d] (64 tokens x 128 dims) is stored as a reordering of its
+# elements: split t and d into digit groups and permute the groups. Token and
+# dim digits (most significant first):
+#   bf16 K:  t -> (h:2, a:4, b:2, q:4), d -> (c:4, j:4, e:8); stored as (h, b, c, j, a, q, e)
+#   bf16 V:  t -> (h:2, j:4, e:8),      d -> (n:8, m:16);     stored as (h, n, j, m, e)
+#   E4M3 K:  t -> (a:4, b:4, q:4),      d -> (p:2, j:4, e:16); stored as (b, p, j, a, q, e)
+#   E4M3 V:  t -> (j:4, e:16),          d -> (n:8, m:16);     stored as (n, j, m, e)
+
+def tile_k(x: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """[..., 64, 128] logical K pages -> [..., 8192] in the tiled order."""
+    lead = x.shape[:-2]
+    k = len(lead)
+    if kv_dtype == "bf16":
+        y = x.reshape(*lead, 2, 4, 2, 4, 4, 4, 8)
+        perm = (0, 2, 4, 5, 1, 3, 6)
+    else:
+        y = x.reshape(*lead, 4, 4, 4, 2, 4, 16)
+        perm = (1, 3, 4, 0, 2, 5)
+    y = y.transpose(*range(k), *(k + i for i in perm))
+    return np.ascontiguousarray(y).reshape(*lead, PAGE * HEAD_DIM)
+
+
+def tile_v(x: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """[..., 64, 128] logical V pages -> [..., 8192] in the tiled order."""
+    lead = x.shape[:-2]
+    k = len(lead)
+    if kv_dtype == "bf16":
+        y = x.reshape(*lead, 2, 4, 8, 8, 16)
+        perm = (0, 3, 1, 4, 2)
+    else:
+        y = x.reshape(*lead, 4, 16, 8, 16)
+        perm = (2, 0, 3, 1)
+    y = y.transpose(*range(k), *(k + i for i in perm))
+    return np.ascontiguousarray(y).reshape(*lead, PAGE * HEAD_DIM)
+
+
 def _draw_pool(rng, num_pages, hkv):
     """Standard normal float32 [num_pages, hkv, 64, D], drawn in page chunks."""
     out = np.empty((num_pages, hkv, PAGE, HEAD_DIM), np.float32)
@@ -110,14 +148,12 @@ def _draw_pool(rng, num_pages, hkv):
     return out
 
 
-def _draw_pool_bf16(rng, num_pages, hkv, transpose):
-    out_shape = (num_pages, hkv, HEAD_DIM, PAGE) if transpose else (num_pages, hkv, PAGE, HEAD_DIM)
-    out = np.empty(out_shape, np.uint16)
+def _draw_pool_bf16(rng, num_pages, hkv, tile):
+    out = np.empty((num_pages, hkv, PAGE * HEAD_DIM), np.uint16)
     for p0 in range(0, num_pages, _CHUNK_PAGES):
         n = min(_CHUNK_PAGES, num_pages - p0)
         x = rng.standard_normal((n, hkv, PAGE, HEAD_DIM), dtype=np.float32)
-        bits = bf16_bits(x)
-        out[p0:p0 + n] = bits.transpose(0, 1, 3, 2) if transpose else bits
+        out[p0:p0 + n] = tile(bf16_bits(x), "bf16")
     return out
 
 
@@ -156,20 +192,20 @@ def build_workload(name: str, seq_lens, hq: int, hkv: int, kv_dtype: str = "bf16
     q = bf16_bits(rng.standard_normal((B, hq, HEAD_DIM), dtype=np.float32))
     k_scale = v_scale = None
     if kv_dtype == "bf16":
-        k_cache = _draw_pool_bf16(rng, num_pages, hkv, transpose=False)
-        v_cache = _draw_pool_bf16(rng, num_pages, hkv, transpose=True)
+        k_cache = _draw_pool_bf16(rng, num_pages, hkv, tile_k)
+        v_cache = _draw_pool_bf16(rng, num_pages, hkv, tile_v)
     else:
         kf = _draw_pool(rng, num_pages, hkv)
         vf = _draw_pool(rng, num_pages, hkv)
         # one scale per KV head, fixed when the cache is built: amax / 448
         k_scale = (np.abs(kf).max(axis=(0, 2, 3)) / E4M3_MAX).astype(np.float32)
         v_scale = (np.abs(vf).max(axis=(0, 2, 3)) / E4M3_MAX).astype(np.float32)
-        k_cache = np.empty(kf.shape, np.uint8)
-        v_cache = np.empty((num_pages, hkv, HEAD_DIM, PAGE), np.uint8)
+        k_cache = np.empty((num_pages, hkv, PAGE * HEAD_DIM), np.uint8)
+        v_cache = np.empty((num_pages, hkv, PAGE * HEAD_DIM), np.uint8)
         for p0 in range(0, num_pages, _CHUNK_PAGES):
             sl = slice(p0, min(num_pages, p0 + _CHUNK_PAGES))
-            k_cache[sl] = e4m3_codes(kf[sl] / k_scale[None, :, None, None])
-            v_cache[sl] = e4m3_codes(vf[sl] / v_scale[None, :, None, None]).transpose(0, 1, 3, 2)
+            k_cache[sl] = tile_k(e4m3_codes(kf[sl] / k_scale[None, :, None, None]), "fp8")
+            v_cache[sl] = tile_v(e4m3_codes(vf[sl] / v_scale[None, :, None, None]), "fp8")
         del kf, vf
 
     w = Workload(name=name, batch=B, hq=hq, hkv=hkv, kv_dtype=kv_dtype,
@@ -194,6 +230,7 @@ def poison_padding(w: Workload) -> None:
     """
     nan = BF16_NAN if w.kv_dtype == "bf16" else E4M3_NAN
     used = np.zeros(w.num_pages, bool)
+    rows = np.arange(PAGE)[:, None] + np.zeros((1, HEAD_DIM), np.int64)
     for b in range(w.batch):
         L = int(w.seq_lens[b])
         n = (L + (1 if w.has_prologue else 0) + PAGE - 1) // PAGE
@@ -204,8 +241,9 @@ def poison_padding(w: Workload) -> None:
         last = int(pages[-1])
         valid_in_last = L - (n - 1) * PAGE       # may be 0..64 (0: new token starts the page)
         if valid_in_last < PAGE:
-            w.k_cache[last, :, valid_in_last:, :] = nan
-            w.v_cache[last, :, :, valid_in_last:] = nan
+            pad = rows >= valid_in_last          # logical [64, 128] mask of padding rows
+            w.k_cache[last][:, tile_k(pad, w.kv_dtype)] = nan
+            w.v_cache[last][:, tile_v(pad, w.kv_dtype)] = nan
     w.k_cache[~used] = nan
     w.v_cache[~used] = nan
 

@@ -98,8 +98,10 @@ class DeviceStep:
                     partial_base=g("partial_base", S), merge_list=g("merge_list", nm))
 
     def trace_records(self) -> np.ndarray:
-        """Instrumented build only: per-wave records [blocks, waves, 4] of the last
-        attention launch (start, end on the 100 MHz counter; HW_ID | XCC_ID << 32; units)."""
+        """Instrumented build only: per-wave records [blocks, waves, 68] of the last
+        attention launch (start, end on the 100 MHz counter; HW_ID | XCC_ID << 32; units;
+        4 start-up times; per item: first unit issued, last unit computed, combine done;
+        then the completion times of the first 48 units)."""
         if not _lib.TRACE:
             raise RuntimeError("trace records need the instrumented build (HPA_TRACE=1)")
         w = self.w

@@ -23,6 +23,7 @@ Sources the oracle follows (cited by page title and section):
 Modules:
 
 * ``formats``   bf16 and OCP E4M3 decode/encode (OCP OFP8 spec v1.0)
+* ``kv_layout`` the cache's in-page element order, element by element
 * ``attention`` gather pages, then exact two-pass softmax attention; partial
                 (acc, m, l) states and their log-sum-exp combination
 * ``planner``   the balanced work list (bit-exact contract) and the static

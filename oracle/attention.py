@@ -10,7 +10,8 @@ KV cache -- xiaodao.ai "HPC-Ops 把 TPOT 降 48.8%，用户未必快一半", sec
 
 For request b, query head h, KV head g = h // (Hq/Hkv) and token j < L_b,
 page p = page_table[b, j // 64], slot r = j % 64:
-    K_j = k_cache[p, g, r, :]   V_j = v_cache[p, g, :, r]   (fp8: code value * scale_g)
+    K_j = row r of block k_cache[p, g]   V_j = row r of block v_cache[p, g]
+    (blocks decoded by kv_layout; fp8: code value * scale_g)
     z_j = sm_scale * <q[b,h], K_j>,  m = max_j z_j,  w_j = exp(z_j - m)
     out[b,h] = sum_j w_j V_j / sum_j w_j;  L_b == 0 gives a zero row.
 
@@ -30,6 +31,7 @@ within a group permutes outputs; split-then-merge equals unsplit to 1e-12).
 import numpy as np
 
 from .formats import bf16_to_f64, e4m3_to_f64
+from .kv_layout import HEAD_DIM, page_rows
 
 PAGE = 64
 
@@ -42,16 +44,16 @@ def decode_kv(codes, kv_dtype, scale=None):
 
 def gather_kv(k_cache, v_cache, page_table, b, g, L, kv_dtype, k_scale=None, v_scale=None):
     """Contiguous fp64 K [L, D] and V [L, D] of request b, KV head g."""
-    D = k_cache.shape[-1]
+    D = HEAD_DIM
     K = np.empty((L, D))
     V = np.empty((L, D))
     for j0 in range(0, L, PAGE):
         n = min(PAGE, L - j0)
         p = int(page_table[b, j0 // PAGE])
-        K[j0:j0 + n] = decode_kv(k_cache[p, g, :n, :], kv_dtype,
+        K[j0:j0 + n] = decode_kv(page_rows(k_cache[p, g], "k", kv_dtype)[:n], kv_dtype,
                                  None if k_scale is None else k_scale[g])
-        V[j0:j0 + n] = decode_kv(v_cache[p, g, :, :n], kv_dtype,
-                                 None if v_scale is None else v_scale[g]).T
+        V[j0:j0 + n] = decode_kv(page_rows(v_cache[p, g], "v", kv_dtype)[:n], kv_dtype,
+                                 None if v_scale is None else v_scale[g])
     return K, V
 
 

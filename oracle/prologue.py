@@ -29,6 +29,7 @@ form; the E4M3 encoder's own pins (formats).
 import numpy as np
 
 from .formats import bf16_to_f64, e4m3_encode
+from .kv_layout import index_table
 
 PAGE = 64
 
@@ -76,10 +77,11 @@ def prologue(w):
         v_codes = bf16_encode(v)
     k_cache = w.k_cache.copy()
     v_cache = w.v_cache.copy()
+    kt, vt = index_table("k", w.kv_dtype), index_table("v", w.kv_dtype)
     for b in range(B):
         p = int(w.page_table[b, pos[b] // PAGE])
         r = int(pos[b] % PAGE)
-        k_cache[p, :, r, :] = k_codes[b]
-        v_cache[p, :, :, r] = v_codes[b]
+        k_cache[p][:, kt[r]] = k_codes[b]
+        v_cache[p][:, vt[r]] = v_codes[b]
     return dict(q_rot=q_rot, k_rot=k_rot, k_codes=k_codes, v_codes=v_codes,
                 k_cache=k_cache, v_cache=v_cache, seq_lens=(pos + 1).astype(np.int32))

@@ -14,6 +14,7 @@ from load_balanced_split_amd import _lib, inputs
 from oracle import attention as oa
 from oracle import planner as op
 from oracle import prologue as opro
+from oracle.kv_layout import index_table
 from tests.helpers import TOL, assert_within, ensure_built, tolerance_report
 
 torch = pytest.importorskip("torch")
@@ -194,7 +195,8 @@ def test_fp8_prologue_workload():
     diffs = 0
     for b, L in enumerate(w.seq_lens):
         p, r = w.page_table[b, L // 64], L % 64
-        for got, want in ((kc[p, :, r, :], pr["k_codes"][b]), (vc[p, :, :, r], pr["v_codes"][b])):
+        kt, vt = index_table("k", "fp8")[r], index_table("v", "fp8")[r]
+        for got, want in ((kc[p][:, kt], pr["k_codes"][b]), (vc[p][:, vt], pr["v_codes"][b])):
             dif = np.abs(got.astype(int) - want.astype(int))
             assert dif.max() <= 1
             diffs += int((dif > 0).sum())
@@ -237,7 +239,7 @@ def test_page_permutation_bit_identical_on_gpu():
 def test_constant_v_returns_it_on_gpu():
     w = inputs.build_workload("constv", [1, 64, 333, 2000], 8, 1, "bf16", seed=6)
     u = inputs.bf16_bits(np.random.default_rng(7).standard_normal(128).astype(np.float32))
-    w.v_cache[:] = u[None, None, :, None]
+    w.v_cache[:] = inputs.tile_v(np.broadcast_to(u, (64, 128)), "bf16")[None, None, :]
     from load_balanced_split_amd.runner import DeviceStep
     d = DeviceStep(w, num_workers=9)
     d.step("balanced")

@@ -3,6 +3,7 @@
 import numpy as np
 
 from load_balanced_split_amd import inputs
+from oracle.kv_layout import page_rows
 
 
 def test_seed0_lengths():
@@ -17,7 +18,7 @@ def test_tiny_layout_and_determinism():
     w = inputs.config_workload(0)
     w2 = inputs.config_workload(0)
     assert np.array_equal(w.k_cache, w2.k_cache) and np.array_equal(w.page_table, w2.page_table)
-    assert w.k_cache.shape == (16, 1, 64, 128) and w.v_cache.shape == (16, 1, 128, 64)
+    assert w.k_cache.shape == (16, 1, 8192) and w.v_cache.shape == (16, 1, 8192)
     assert w.page_table.shape == (4, 9)
     used = w.page_table[w.page_table >= 0]
     assert len(used) == 15 and len(set(used.tolist())) == 15
@@ -27,16 +28,20 @@ def test_tiny_layout_and_determinism():
 def test_poison_marks_only_unreadable_slots():
     w = inputs.build_workload("p", [37, 64, 0, 129], 8, 1, "bf16", seed=1, pool_pages=8, poison=True)
     nan = w.k_cache == inputs.BF16_NAN
+    vnan = w.v_cache == inputs.BF16_NAN
     for b, L in enumerate(w.seq_lens):
         for t in range((L + 63) // 64):
             p = w.page_table[b, t]
             n = min(64, L - 64 * t)
-            assert not nan[p, :, :n].any() and nan[p, :, n:].all()
-            assert (w.v_cache[p, :, :, n:] == inputs.BF16_NAN).all()
+            for g in range(w.hkv):
+                kr = page_rows(nan[p, g], "k", "bf16")
+                vr = page_rows(vnan[p, g], "v", "bf16")
+                assert not kr[:n].any() and kr[n:].all()
+                assert not vr[:n].any() and vr[n:].all()
     used = set(w.page_table[w.page_table >= 0].tolist())
     for p in range(w.num_pages):
         if p not in used:
-            assert nan[p].all()
+            assert nan[p].all() and vnan[p].all()
 
 
 def test_fp8_scales_cover_pool():

@@ -10,20 +10,21 @@ import torch
 from load_balanced_split_amd import inputs
 from oracle import attention as oa
 from oracle.formats import bf16_to_f64, e4m3_to_f64
+from oracle.kv_layout import page_rows
 
 D = 128
 SCALE = 1.0 / math.sqrt(D)
 
 
 def paged_from_contiguous(Ks, Vs, rng, extra_pages=3, dtype=np.uint16):
-    """Test-side scatter of contiguous per-request K/V codes [Hkv, L, D] into the
-    page pool layout (K token-major, V dim-major inside a page)."""
+    """Test-side scatter of contiguous per-request K/V codes [Hkv, L, D] into pages,
+    then into the cache's tiled in-page order (the input generator's tiling)."""
     hkv = Ks[0].shape[0]
     npages = [(k.shape[1] + 63) // 64 for k in Ks]
     P = sum(npages) + extra_pages
     perm = rng.permutation(P)
     kc = np.zeros((P, hkv, 64, D), dtype)
-    vc = np.zeros((P, hkv, D, 64), dtype)
+    vc = np.zeros((P, hkv, 64, D), dtype)
     pt = np.full((len(Ks), max(1, max(npages))), -1, np.int32)
     off = 0
     for b, (K, V) in enumerate(zip(Ks, Vs)):
@@ -33,8 +34,9 @@ def paged_from_contiguous(Ks, Vs, rng, extra_pages=3, dtype=np.uint16):
             pt[b, t] = p
             rows = K[:, t * 64:(t + 1) * 64, :]
             kc[p, :, :rows.shape[1], :] = rows
-            vc[p, :, :, :rows.shape[1]] = V[:, t * 64:(t + 1) * 64, :].transpose(0, 2, 1)
-    return kc, vc, pt
+            vc[p, :, :rows.shape[1], :] = V[:, t * 64:(t + 1) * 64, :]
+    kv_dtype = "bf16" if dtype == np.uint16 else "fp8"
+    return inputs.tile_k(kc, kv_dtype), inputs.tile_v(vc, kv_dtype), pt
 
 
 def sdpa(q, K, V, scale):
@@ -81,8 +83,8 @@ def test_oracle_tiny_workload_matches_sdpa():
     for b in range(w.batch):
         L = int(w.seq_lens[b])
         pages = w.page_table[b, :(L + 63) // 64]
-        K = np.concatenate([bf16_to_f64(w.k_cache[p, 0]) for p in pages])[:L][None]
-        V = np.concatenate([bf16_to_f64(w.v_cache[p, 0]).T for p in pages])[:L][None]
+        K = np.concatenate([bf16_to_f64(page_rows(w.k_cache[p, 0], "k", "bf16")) for p in pages])[:L][None]
+        V = np.concatenate([bf16_to_f64(page_rows(w.v_cache[p, 0], "v", "bf16")) for p in pages])[:L][None]
         np.testing.assert_allclose(out[b], sdpa(bf16_to_f64(w.q[b]), K, V, w.sm_scale), rtol=1e-12, atol=1e-13)
 
 

@@ -6,6 +6,7 @@ import torch
 
 from load_balanced_split_amd import inputs
 from oracle import prologue as opro
+from oracle.kv_layout import page_rows
 from oracle.formats import bf16_to_f64, e4m3_encode
 
 D = 128
@@ -73,9 +74,10 @@ def test_prologue_appends_at_live_length(kv_dtype):
     assert list(r["seq_lens"]) == [1, 6, 64, 65, 201]
     for b, L in enumerate(w.seq_lens):
         p = w.page_table[b, L // 64]
-        assert np.array_equal(r["k_cache"][p, :, L % 64, :], r["k_codes"][b])
-        assert np.array_equal(r["v_cache"][p, :, :, L % 64], r["v_codes"][b])
-    changed = (r["k_cache"] != w.k_cache).any(axis=(1, 2, 3))
+        for g in range(w.hkv):
+            assert np.array_equal(page_rows(r["k_cache"][p, g], "k", kv_dtype)[L % 64], r["k_codes"][b, g])
+            assert np.array_equal(page_rows(r["v_cache"][p, g], "v", kv_dtype)[L % 64], r["v_codes"][b, g])
+    changed = (r["k_cache"] != w.k_cache).any(axis=(1, 2))
     assert changed.sum() <= w.batch
     if kv_dtype == "fp8":
         np.testing.assert_array_equal(r["k_codes"], e4m3_encode(r["k_rot"] / w.k_scale[None, :, None]))
