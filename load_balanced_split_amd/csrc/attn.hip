@@ -161,16 +161,31 @@ struct CombineLds {
   float o[kWaves][kMaxGroup][kORow];
 };
 
-// Everything about one item that is uniform across the workgroup (kept small:
-// descriptors and pointers are re-derived where they are used).
+// Scalar view of read-only device arrays: a load through it returns one value
+// for the whole wave into scalar registers and is waited for on the scalar
+// counter, so it never orders behind the K/V stream's vector loads. Only for
+// memory no kernel of the step writes while this one runs.
+typedef const __attribute__((address_space(4))) int32_t cint32_t;
+typedef const __attribute__((address_space(4))) float cfloat_t;
+__device__ inline int sload(const int32_t* base, int64_t i) { return ((cint32_t*)base)[i]; }
+__device__ inline float sloadf(const float* base, int64_t i) { return ((cfloat_t*)base)[i]; }
+
+// Everything about one item that is uniform across the workgroup. open() issues
+// the scalar loads (length, scales) and returns at once; they are first waited
+// for one item later, when the item becomes current.
 struct ItemState {
   Item it;
-  int b, g, nu;
+  int b, g;         // request and KV head of sequence it.s
+  int L;            // live length of request b
+  float kscale, vscale;
+  bool valid;       // a work-list entry that fits this launch
 };
 
 // Per-workgroup driver: 4 waves on one item at a time; wave w takes the item's
-// units w, w+4, ... While one item is combined, the next item's q and page ids
-// are already in flight, and its first unit is issued right after the combine.
+// units w, w+4, ... Items are software-pipelined: while item k streams, item
+// k+1's length, q and first page ids are in flight and item k+2's descriptor is
+// being read; the issue slot after a wave's last unit of item k takes its first
+// unit of item k+1, so the K/V stream of a wave never drains at an item boundary.
 template <bool FP8>
 struct Worker {
   const AttnArgs& a;
@@ -180,10 +195,8 @@ struct Worker {
   int titem = 0;
   int lane, wave, m16, j;
   uint32_t loff;         // per-lane byte offset inside each 1 KB load
-  // carried from one item to the next
-  bf16x8 q[4];
+  bf16x8 q[4], qn[4];    // q operand of the current and of the next item
   UnitBuf bufA, bufB;
-  int pidA, pidB;
 
   __device__ Worker(const AttnArgs& args, CombineLds& l)
       : a(args), lds(l), lane(threadIdx.x & 63),
@@ -312,93 +325,107 @@ struct Worker {
 
   __device__ bool bad_pid(int pid) const { return pid < 0 || pid >= a.num_pages; }
 
-  // tile of unit u of the item (clamped into the item, so the page-table read is in bounds)
-  __device__ int tile_of(const ItemState& st, int u) const {
-    using C = Cfg<FP8>;
-    return st.it.t0 + min(u / C::UPT, st.it.t1 - st.it.t0 - 1);
+  // Descriptor -> uniform facts of the item; issues its scalar loads, waits for none.
+  __device__ ItemState open(const Item& it) const {
+    ItemState st;
+    st.it = it;
+    st.valid = it.s >= 0 && it.s < a.batch * a.hkv && it.t0 >= 0 && it.t1 > it.t0 &&
+               it.t1 <= a.max_pages && it.slot < a.slots;
+    const int s = st.valid ? it.s : 0;
+    // integer division runs on the VALU: bring the (uniform) result back to an SGPR
+    st.b = __builtin_amdgcn_readfirstlane(s / a.hkv);
+    st.g = s - st.b * a.hkv;
+    st.L = sload(a.seq_lens, st.b);
+    st.kscale = FP8 ? sloadf(a.k_scale, st.g) : 1.f;
+    st.vscale = FP8 ? sloadf(a.v_scale, st.g) : 1.f;
+    if (!st.valid && threadIdx.x == 0 && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PLAN);
+    return st;
   }
 
-  __device__ rsrc_t page_row(const ItemState& st) const {
-    return make_rsrc(a.page_table + int64_t(st.b) * a.max_pages, a.max_pages * 4);
+  // units of the item: UPT per tile, minus a trailing half-tile that starts past L
+  __device__ int units(const ItemState& st) const {
+    using C = Cfg<FP8>;
+    if (!st.valid) return 0;
+    int nu = (st.it.t1 - st.it.t0) * C::UPT;
+    if (C::UPT > 1 && st.it.t1 * kPage - C::UNIT >= st.L) nu -= 1;
+    return nu;
+  }
+
+  // page id of unit u's tile (tile clamped into the item, so the read is in
+  // bounds); a scalar load, -1 for an invalid item
+  __device__ int page_of(const ItemState& st, int u) const {
+    using C = Cfg<FP8>;
+    if (!st.valid) return -1;
+    const int t = st.it.t0 + min(u / C::UPT, st.it.t1 - st.it.t0 - 1);
+    return sload(a.page_table, int64_t(st.b) * a.max_pages + t);
+  }
+
+  // first token of unit u
+  __device__ int tok0(const ItemState& st, int u) const {
+    using C = Cfg<FP8>;
+    return (st.it.t0 + u / C::UPT) * kPage + (u % C::UPT) * C::UNIT;
   }
 
   // unit u -> K/V resources of its (page, KV head) (empty past the item or for a bad page id)
-  __device__ bool unit_rsrc(const ItemState& st, int u, int pid_raw, rsrc_t& rk, rsrc_t& rv) const {
+  __device__ bool unit_rsrc(const ItemState& st, int nu, int u, int pid, rsrc_t& rk, rsrc_t& rv) const {
     using C = Cfg<FP8>;
     constexpr uint32_t page_bytes = kPage * kHeadDim * C::EB;
-    const int pid = __builtin_amdgcn_readfirstlane(pid_raw);
-    const bool ok = u < st.nu && !bad_pid(pid);
+    const bool ok = u < nu && !bad_pid(pid);
     const uint64_t off = ok ? (uint64_t(pid) * a.hkv + st.g) * page_bytes : 0;
     rk = make_rsrc(a.k_cache + off, ok ? page_bytes : 0);
     rv = make_rsrc(a.v_cache + off, ok ? page_bytes : 0);
     return ok;
   }
 
-  // Scalar facts of an item (one scalar load: the request's length).
-  __device__ ItemState prepare(const Item it) const {
-    using C = Cfg<FP8>;
-    ItemState st;
-    st.it = it;
-    // integer division runs on the VALU: bring the (uniform) results back to SGPRs
-    st.b = __builtin_amdgcn_readfirstlane(it.s / a.hkv);
-    st.g = it.s - st.b * a.hkv;
-    const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[st.b]);
-    // units: UPT per tile, minus a trailing half-tile that starts past L
-    st.nu = (it.t1 - it.t0) * C::UPT;
-    if (C::UPT > 1 && it.t1 * kPage - C::UNIT >= L) st.nu -= 1;
-    st.nu = __builtin_amdgcn_readfirstlane(st.nu);
-    return st;
-  }
-
-  // Q^T operand (lane: head m16, dims chunk_dim(c, j) .. +8; zeros for heads >= G)
-  // and the page ids of this wave's first two units. Vector loads only.
-  __device__ void fetch_meta(const ItemState& st) {
+  // Q^T operand of an item (lane: head m16, dims chunk_dim(c, j) .. +8; zeros for
+  // heads >= G and for an invalid item). Vector loads, waited for at first use.
+  __device__ void load_q(const ItemState& st, bf16x8 (&dst)[4]) const {
     const rsrc_t rq = make_rsrc(a.q + (int64_t(st.b) * a.hq + st.g * a.group) * kHeadDim,
-                                a.group * kHeadDim * 2);
+                                st.valid ? a.group * kHeadDim * 2 : 0);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) q[c] = as_bf16x8(bload16(rq, (m16 * kHeadDim + chunk_dim<FP8>(c, j)) * 2, 0));
-    const rsrc_t rpt = page_row(st);
-    pidA = bload_i32(rpt, tile_of(st, wave) * 4);
-    pidB = bload_i32(rpt, tile_of(st, wave + kWaves) * 4);
+    for (int c = 0; c < 4; ++c) dst[c] = as_bf16x8(bload16(rq, (m16 * kHeadDim + chunk_dim<FP8>(c, j)) * 2, 0));
   }
 
-  // Issue this wave's first unit of the item into bufA.
-  __device__ bool issue_first(const ItemState& st) {
-    using C = Cfg<FP8>;
-    rsrc_t rk, rv;
-    const bool ok = unit_rsrc(st, wave, pidA, rk, rv);
-    issue(bufA, rk, rv, wave % C::UPT);
-    if (wave < st.nu && !ok && lane == 0 && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PAGE_ID);
-    return ok;
+  __device__ void report_bad_page() const {
+    if (lane == 0 && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PAGE_ID);
   }
 
-  // Stream this wave's units of the item (the first one already in bufA): the
-  // next unit's 16 loads are always issued before the current one is computed.
-  __device__ void stream(const ItemState& st, bool okA, float& m_run, float& l_part, f32x4 (&o)[8]) {
+  // Stream this wave's units of item st; unit `wave` is already in bufA (okA: it
+  // exists) and pidB is the page of unit wave + 4. The next unit's 16 loads are
+  // always issued before the current unit is computed; after the wave's last
+  // unit of st, that slot takes its first unit of the next item (nst, npid), so
+  // on return bufA holds it. Returns whether that unit exists.
+  __device__ bool stream(const ItemState& st, bool okA, int pidB, float& m_run, float& l_part,
+                         f32x4 (&o)[8], bool more, const ItemState& nst, int npid) {
     using C = Cfg<FP8>;
-    const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[st.b]);
-    const int u0 = wave;
-    if (u0 >= st.nu) return;
-    const float qk_scale = a.sm_scale * kLog2e * (FP8 ? a.k_scale[st.g] : 1.f);
-    const rsrc_t rpt = page_row(st);
-    bool any_bad = false, okB;
+    const int nu = units(st);
+    const float qk_scale = a.sm_scale * kLog2e * st.kscale;
+    bool any_bad = false;
     rsrc_t rk, rv;
-    for (int u = u0;; u += 2 * kWaves) {
+    int pidA = -1;
+    for (int u = wave;; u += 2 * kWaves) {
       const int uB = u + kWaves, uA = uB + kWaves;
-      okB = unit_rsrc(st, uB, pidB, rk, rv);
-      any_bad |= uB < st.nu && !okB;
-      pidA = bload_i32(rpt, tile_of(st, uA) * 4);
+      const bool okB = unit_rsrc(st, nu, uB, pidB, rk, rv);
+      any_bad |= uB < nu && !okB;
       issue(bufB, rk, rv, uB % C::UPT);
-      if (okA) compute(bufA, q, (st.it.t0 + u / C::UPT) * kPage + (u % C::UPT) * C::UNIT, L, qk_scale, m_run, l_part, o);
-      if (uB >= st.nu) break;
-      okA = unit_rsrc(st, uA, pidA, rk, rv);
-      any_bad |= uA < st.nu && !okA;
-      pidB = bload_i32(rpt, tile_of(st, uA + kWaves) * 4);
-      issue(bufA, rk, rv, uA % C::UPT);
-      if (okB) compute(bufB, q, (st.it.t0 + uB / C::UPT) * kPage + (uB % C::UPT) * C::UNIT, L, qk_scale, m_run, l_part, o);
-      if (uA >= st.nu) break;
+      if (uA < nu) pidA = page_of(st, uA);
+      if (okA) compute(bufA, q, tok0(st, u), st.L, qk_scale, m_run, l_part, o);
+      if (uA < nu) {
+        okA = unit_rsrc(st, nu, uA, pidA, rk, rv);
+        any_bad |= !okA;
+        if (uA + kWaves < nu) pidB = page_of(st, uA + kWaves);
+        issue(bufA, rk, rv, uA % C::UPT);
+      } else {
+        const int nnu = more ? units(nst) : 0;
+        okA = unit_rsrc(nst, nnu, wave, npid, rk, rv);
+        any_bad |= wave < nnu && !okA;
+        issue(bufA, rk, rv, wave % C::UPT);
+      }
+      if (okB) compute(bufB, q, tok0(st, uB), st.L, qk_scale, m_run, l_part, o);
+      if (uA >= nu) break;
     }
-    if (any_bad && lane == 0 && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PAGE_ID);
+    if (any_bad) report_bad_page();
+    return okA;
   }
 
   // The 4 waves' (m, l, acc) meet in LDS; one log-sum-exp combine; the output row
@@ -416,8 +443,12 @@ struct Worker {
         *reinterpret_cast<f32x4*>(&lds.o[wave][m16][16 * n + 4 * j]) = o[n];
     }
     __syncthreads();
-    const float vscale = FP8 ? a.v_scale[st.g] : 1.f;
-    for (int idx = threadIdx.x; idx < a.group * kHeadDim; idx += kAttnThreads) {
+    // a fixed trip count keeps the number of stores static, so the wait for the
+    // next item's first unit (issued before this combine) stays exact
+#pragma unroll
+    for (int r = 0; r < kMaxGroup * kHeadDim / kAttnThreads; ++r) {
+      const int idx = threadIdx.x + r * kAttnThreads;
+      if (!st.valid || idx >= a.group * kHeadDim) break;
       const int hh = idx >> 7, d = idx & (kHeadDim - 1);
       float M = -INFINITY;
 #pragma unroll
@@ -429,7 +460,7 @@ struct Worker {
         Ls += f * lds.l[w][hh];
         acc += f * lds.o[w][hh][d];
       }
-      acc *= vscale;
+      acc *= st.vscale;
       if (st.it.slot < 0) {
         a.out[(int64_t(st.b) * a.hq + st.g * a.group + hh) * kHeadDim + d] = f32_to_bf16_rne(acc / Ls);
       } else {
@@ -444,9 +475,6 @@ struct Worker {
     __syncthreads();
   }
 
-  // Walk the items a source hands out (src.next(Item&) -> bool, uniform). While
-  // one item is combined, the next item's q and page ids are already in flight;
-  // its first unit is issued right after the combine.
   __device__ void stamp(int k) {
     if (kTraceBuild && trec && titem < kTraceItems && lane == 0)
       trec[4 + kTraceStart + 3 * titem + k] = __builtin_amdgcn_s_memrealtime();
@@ -460,78 +488,91 @@ struct Worker {
     }
   }
 
+  // Walk the items a source hands out (src.next(Item&) -> bool, uniform; it only
+  // issues the descriptor's loads, which are first used one item later).
   template <class Source>
   __device__ void run(Source& src) {
+    using C = Cfg<FP8>;
     start_stamp(0);
     Item it;
     if (!src.next(it)) return;
     start_stamp(1);
-    ItemState st = prepare(it);
+    ItemState st = open(it);
+    load_q(st, q);
+    int pidB = page_of(st, wave + kWaves);
+    const int pid0 = page_of(st, wave);
     start_stamp(2);
-    fetch_meta(st);
+    const int nu0 = units(st);
+    rsrc_t rk, rv;
+    bool okA = unit_rsrc(st, nu0, wave, pid0, rk, rv);
+    if (wave < nu0 && !okA) report_bad_page();
+    issue(bufA, rk, rv, wave % C::UPT);
     start_stamp(3);
-    bool okA = issue_first(st);
+    Item nit;
+    bool more = src.next(nit);
     for (;;) {
+      ItemState nst{};
+      int npid = -1, npidB = -1;
+      if (more) {                  // prefetch: the next item's length, q and first pages
+        nst = open(nit);
+        load_q(nst, qn);
+        npid = page_of(nst, wave);
+        npidB = page_of(nst, wave + kWaves);
+      }
+      Item nnit;
+      const bool more2 = more && src.next(nnit);
       float m_run = -INFINITY, l_part = 0.f;
       f32x4 o[8];
 #pragma unroll
       for (int n = 0; n < 8; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
       stamp(0);
-      stream(st, okA, m_run, l_part, o);
+      okA = stream(st, okA, pidB, m_run, l_part, o, more, nst, npid);
       stamp(1);
-      Item nit;
-      const bool more = src.next(nit);
-      ItemState nst;
-      if (more) {
-        nst = prepare(nit);
-        fetch_meta(nst);           // in flight during the combine
-      }
       combine(st, m_run, l_part, o);
       stamp(2);
       ++titem;
       if (!more) break;
       st = nst;
-      okA = issue_first(st);
+      pidB = npidB;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) q[c] = qn[c];
+      nit = nnit;
+      more = more2;
     }
   }
 };
 
-// Items of worker w from the planner's work list.
+// Items of worker w from the planner's work list (scalar loads; next() only
+// issues them, the entry is checked when the driver opens it).
 struct PlanSource {
   const AttnArgs& a;
-  int i, i1, S;
+  int i, i1;
   __device__ bool next(Item& it) {
-    while (i < i1) {
-      // the work list is uniform per workgroup: keep it in scalar registers
-      it = Item{__builtin_amdgcn_readfirstlane(a.plan[a.po.item_s + i]),
-                __builtin_amdgcn_readfirstlane(a.plan[a.po.item_t0 + i]),
-                __builtin_amdgcn_readfirstlane(a.plan[a.po.item_t1 + i]),
-                __builtin_amdgcn_readfirstlane(a.plan[a.po.item_slot + i]), 0, 0};
-      ++i;
-      // a work list that does not fit this launch is reported, never followed
-      if (it.s < 0 || it.s >= S || it.t0 < 0 || it.t1 <= it.t0 || it.t1 > a.max_pages || it.slot >= a.slots) {
-        if (threadIdx.x == 0) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PLAN);
-        continue;
-      }
-      return true;
-    }
-    return false;
+    if (i >= i1) return false;
+    it = Item{sload(a.plan, a.po.item_s + i), sload(a.plan, a.po.item_t0 + i), sload(a.plan, a.po.item_t1 + i),
+              sload(a.plan, a.po.item_slot + i), 0, 0};
+    ++i;
+    return true;
   }
 };
 
 template <bool FP8>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_balanced_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_balanced_kernel(AttnArgs a) {
   __shared__ CombineLds lds;
   WaveTrace tr(a);
-  const int32_t* hdr = a.plan + a.po.header;
   const int w = blockIdx.x;
-  if (hdr[H_W] != static_cast<int>(gridDim.x)) {
+  if (sload(a.plan, a.po.header + H_W) != static_cast<int>(gridDim.x)) {
     if (w == 0 && threadIdx.x == 0) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PLAN);
     return;
   }
-  if (w >= hdr[H_WP]) return;
-  PlanSource src{a, __builtin_amdgcn_readfirstlane(a.plan[a.po.worker_off + w]),
-                 __builtin_amdgcn_readfirstlane(a.plan[a.po.worker_off + w + 1]), a.batch * a.hkv};
+  if (w >= sload(a.plan, a.po.header + H_WP)) return;
+  int i0 = sload(a.plan, a.po.worker_off + w), i1 = sload(a.plan, a.po.worker_off + w + 1);
+  const int cap = a.workers + a.batch * a.hkv;      // the work list holds at most W + S items
+  if (i0 < 0 || i1 < i0 || i1 > cap) {
+    if (threadIdx.x == 0) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PLAN);
+    return;
+  }
+  PlanSource src{a, i0, i1};
   Worker<FP8> r(a, lds);
   r.trec = tr.rec;
   r.run(src);
@@ -551,7 +592,7 @@ struct SingleSource {
 };
 
 template <bool FP8>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_static_kernel(AttnArgs a) {
   __shared__ CombineLds lds;
   WaveTrace tr(a);
   const int s = blockIdx.x / a.static_splits, k = blockIdx.x - s * a.static_splits;
@@ -641,7 +682,7 @@ struct FusedSource {
 };
 
 template <bool FP8>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_fused_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_kernel(AttnArgs a) {
   __shared__ CombineLds lds;
   __shared__ FusedPlanLds P;
   WaveTrace tr(a);

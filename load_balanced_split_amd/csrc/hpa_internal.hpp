@@ -15,6 +15,7 @@ constexpr int kPage = 64;          // tokens per page == tokens per tile
 constexpr int kMaxGroup = 16;      // query heads per KV head (MFMA N width)
 constexpr int kWaves = 4;          // waves per attention workgroup (one worker)
 constexpr int kAttnThreads = 64 * kWaves;
+constexpr int kAttnBlocksPerCu = 1;  // one worker per CU: the full register file for the K/V pipeline
 constexpr int kPlanThreads = 1024;
 constexpr int kHeaderInts = 16;
 
