@@ -63,10 +63,9 @@ def pmc_main(args):
     from load_balanced_split_amd.profiling import CALIBRATION_BYTES
     from load_balanced_split_amd.runner import DeviceStep
     _lib.lib()
-    W = args.num_workers or _lib.hpa_default_num_workers(0)
     w = inputs.config_workload(args.workload)
     R = max(2, math.ceil(2 * MALL_BYTES / (w.k_cache.nbytes + w.v_cache.nbytes)) + 1)
-    copies = [DeviceStep(w, num_workers=W) for _ in range(min(R, 16))]
+    copies = [DeviceStep(w, num_workers=args.num_workers) for _ in range(min(R, 16))]
     src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -177,9 +176,9 @@ def trace_main(args):
     from load_balanced_split_amd import _lib, inputs
     from load_balanced_split_amd.runner import DeviceStep
     _lib.lib()
-    W = args.num_workers or _lib.hpa_default_num_workers(0)
     w = inputs.config_workload(args.workload)
-    d = DeviceStep(w, num_workers=W)
+    d = DeviceStep(w, num_workers=args.num_workers)
+    W = d.num_workers
     out = {"metric": "attention tail balance (instrumented build)", "workload": inputs.CONFIG_NAMES[args.workload],
            "num_workers": W, "realtime_clock_mhz": REALTIME_MHZ}
     for sched in ("balanced", "fused", "static_splits", "static_chunk"):
@@ -187,7 +186,7 @@ def trace_main(args):
         for r in range(5):
             d.step(sched)                     # planner (if any) and a full step first
             torch.cuda.synchronize()
-            d.partial_ws[-(W + w.batch * w.hkv) * _lib.TRACE_WAVES * _lib.TRACE_WORDS * 8:].zero_()
+            d.partial_ws.zero_()              # partials and the record area of the traced launch
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             d.attend(sched, flags=_lib.ATTN_NO_MERGE)
@@ -243,14 +242,14 @@ def main():
     _lib.lib()                               # fails loudly if libhpa.so is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    W = args.num_workers or _lib.hpa_default_num_workers(0)
-
     w = inputs.config_workload(args.workload)
     kv_bytes, alg_bytes, pro_bytes = algorithmic_bytes(w)
     pool_bytes = w.k_cache.nbytes + w.v_cache.nbytes
     R = max(2, math.ceil(2 * MALL_BYTES / max(pool_bytes, 1)) + 1)
     R = min(R, 16)
-    copies = [DeviceStep(w, num_workers=W, device="cuda:0") for _ in range(R)]
+    # num_workers 0: each schedule takes the library's default for it
+    copies = [DeviceStep(w, num_workers=args.num_workers, device="cuda:0") for _ in range(R)]
+    W = copies[0].num_workers
     print(f"[bench] workload {args.workload} ({w.name}): KV {kv_bytes / 1e6:.1f} MB, {R} copies, W={W}",
           file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
@@ -338,7 +337,8 @@ def main():
         "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 q/out",
         "data": "synthetic (seeded; shapes and length mix of the pages' kernel benchmark)",
         "config": {"workload": inputs.CONFIG_NAMES[args.workload], "schedule": "balanced",
-                   "num_workers": W, "rotating_copies": R, "kv_bytes": kv_bytes,
+                   "num_workers": W, "static_num_workers": copies[0].static_workers,
+                   "rotating_copies": R, "kv_bytes": kv_bytes,
                    "algorithmic_bytes": alg_bytes},
         "us_per_step": round(us, 2),
         "kv_frac_of_peak": round(kv_gbps / PEAK_HBM_GBPS, 4),

@@ -106,8 +106,13 @@ typedef struct {
   int32_t max_items;           /* W + S */
 } hpa_plan_layout;
 
-/* Workers = compute units x resident attention workgroups per CU (cached per device). */
-hpa_status hpa_default_num_workers(int device, int32_t* num_workers);
+/* Default worker count of a schedule on a device: compute units x workgroups of
+ * that schedule's attention kernel that fit on one CU at once (cached per device).
+ * For the balanced schedules it is the persistent grid; for the static ones, the
+ * W their split count is derived from. num_workers = 0 in the calls below means
+ * this default for the schedule concerned (for the workspace size queries: the
+ * largest default over all schedules). */
+hpa_status hpa_default_num_workers(int device, hpa_sched sched, int32_t* num_workers);
 
 /* Size and layout of the plan workspace for up to num_workers workers (0 = default). */
 hpa_status hpa_plan_workspace_size(const hpa_attn_desc* desc, int32_t num_workers, size_t* bytes);

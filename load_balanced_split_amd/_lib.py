@@ -64,7 +64,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         D = ctypes.POINTER(AttnDesc)
         sig = {
-            "hpa_default_num_workers": [ctypes.c_int, ctypes.POINTER(ctypes.c_int32)],
+            "hpa_default_num_workers": [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int32)],
             "hpa_plan_workspace_size": [D, _I, ctypes.POINTER(ctypes.c_size_t)],
             "hpa_plan_workspace_layout": [D, _I, ctypes.POINTER(PlanLayout)],
             "hpa_partial_workspace_size": [D, _I, ctypes.POINTER(ctypes.c_size_t)],
@@ -120,9 +120,9 @@ def make_desc(batch, num_q_heads, num_kv_heads, max_pages_per_seq, num_pages, kv
                     1.0 / math.sqrt(128) if sm_scale is None else sm_scale)
 
 
-def hpa_default_num_workers(device: int = 0) -> int:
+def hpa_default_num_workers(device: int = 0, sched: str = "balanced") -> int:
     n = ctypes.c_int32(0)
-    _check(lib().hpa_default_num_workers(device, ctypes.byref(n)), "hpa_default_num_workers")
+    _check(lib().hpa_default_num_workers(device, SCHED[sched], ctypes.byref(n)), "hpa_default_num_workers")
     return n.value
 
 

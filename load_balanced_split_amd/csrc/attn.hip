@@ -592,7 +592,7 @@ struct SingleSource {
 };
 
 template <bool FP8>
-__global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_static_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a) {
   __shared__ CombineLds lds;
   WaveTrace tr(a);
   const int s = blockIdx.x / a.static_splits, k = blockIdx.x - s * a.static_splits;
@@ -626,20 +626,11 @@ struct FusedPlanLds {
   int tot[kFusedMaxSeqs / 64];
 };
 
-__device__ inline int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-
 // Exclusive-scan the per-chunk totals P.tot[0..nch) and add each chunk's offset to
 // arr[chunk * 64 + lane] for the chunks this wave owns; returns the grand total.
 __device__ inline int add_chunk_offsets(FusedPlanLds& P, int* arr, int S, int nch, int lane, int wave) {
   const int t = lane < nch ? P.tot[lane] : 0;
-  const int xi = wave_incl_scan(t, lane);
+  const int xi = wave_incl_scan(t);
   const int total = __builtin_amdgcn_readfirstlane(__shfl(xi, 63, 64));   // same in every lane
   const int off = xi - t;
   for (int ch = wave; ch < nch; ch += kWaves) {
@@ -699,7 +690,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
       if (L < 0 || L > a.max_pages * kPage) bad = 1;
       else n = tiles_of(L);
     }
-    const int x = wave_incl_scan(n, lane);
+    const int x = wave_incl_scan(n);
     if (s < S) P.C[s] = x - n;
     if (lane == 63) P.tot[ch] = x;
   }
@@ -721,7 +712,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
         v = ns > 1 ? ns : 0;
       }
     }
-    const int x = wave_incl_scan(v, lane);
+    const int x = wave_incl_scan(v);
     if (s < S) P.PB[s] = x - v;
     if (lane == 63) P.tot[ch] = x;
   }
@@ -749,13 +740,14 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
   tr.units = r.units_done;
 }
 
-// Merge: block (i, h, c) combines dims [32c, 32c + 32) of head h of the i-th
-// sequence to merge. 256 threads = 8 dim-quads x 32 group lanes: lane group j
-// folds splits [16j, 16j + 16) in order (fold), then the group results are folded
-// in group order -- the same arithmetic, in the same order, as the fused
-// schedule's in-kernel combine. Empty sequences get a zero row.
+// Merge: block (s, h) combines the 128 dims of head h of sequence s; blocks of
+// unsplit sequences return at once. 256 threads = 32 dim-quads x 8 lane groups:
+// lane group j folds split groups j, j + 8, ... (16 consecutive splits each, in
+// order, with fold), then the group results are folded in group order, so every
+// schedule's partials combine with the same arithmetic in the same order.
+// Empty sequences get a zero row.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeDims = 32;
+constexpr int kMergeDims = kHeadDim;
 constexpr int kMergeQuads = kMergeDims / 4;
 constexpr int kMergeLanes = kMergeThreads / kMergeQuads;
 
@@ -763,34 +755,28 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int mo
   __shared__ float gm[kMergeLanes], gl[kMergeLanes];
   __shared__ f32x4 gacc[kMergeLanes][kMergeQuads];
   const int hh = blockIdx.y, d0 = blockIdx.z * kMergeDims;
-  int s, n, base;
-  if (mode == MERGE_FUSED) {
-    // zero rows of empty requests were written by the attention kernel; the others
-    // read the split count and slot base recorded by their split-0 worker
-    s = blockIdx.x;
-    const int L = a.seq_lens[s / a.hkv];
-    if (L <= 0 || L > a.max_pages * kPage) return;
-    n = a.plan[a.po.num_splits + s];
-    base = a.plan[a.po.partial_base + s];
-    if (n <= 1 || base < 0 || base + n > a.slots) return;
-  } else if (mode == MERGE_PLAN) {
-    const int32_t* hdr = a.plan + a.po.header;
-    if (hdr[H_W] != a.workers || static_cast<int>(blockIdx.x) >= hdr[H_NMERGE]) return;
-    s = a.plan[a.po.merge_list + blockIdx.x];
-    if (s < 0 || s >= a.batch * a.hkv) return;
-    n = a.plan[a.po.num_splits + s];
-    base = a.plan[a.po.partial_base + s];
-    if (n < 0 || base < 0 || base + n > a.slots) return;
-  } else {
-    s = blockIdx.x;
-    const int L = a.seq_lens[s / a.hkv];
+  const int s = blockIdx.x;
+  // every fact this block needs is one scalar load away from its sequence index
+  const int L = sload(a.seq_lens, s / a.hkv);
+  int n, base;
+  if (mode == MERGE_STATIC) {
     if (L < 0 || L > a.max_pages * kPage) return;
     const int nt = (L + kPage - 1) / kPage;
     const int chunk = nt == 0 ? 1 : (a.static_chunk > 0 ? a.static_chunk : (nt + a.static_splits - 1) / a.static_splits);
     n = (nt + chunk - 1) / chunk;
-    if (n == 1) return;
     base = s * a.static_splits;
+  } else {
+    n = sload(a.plan, a.po.num_splits + s);
+    base = sload(a.plan, a.po.partial_base + s);
+    if (mode == MERGE_FUSED) {
+      // zero rows of empty requests were written by the attention kernel; the others
+      // read the split count and slot base recorded by their split-0 worker
+      if (L <= 0 || L > a.max_pages * kPage) return;
+    } else if (sload(a.plan, a.po.header + H_W) != a.workers) {
+      return;                               // a plan made for another launch shape
+    }
   }
+  if (n == 1 || n < 0 || (n > 1 && (base < 0 || base + n > a.slots))) return;
   const int b = s / a.hkv, g = s - b * a.hkv;
   uint16_t* orow = a.out + (int64_t(b) * a.hq + g * a.group + hh) * kHeadDim + d0;
   const int tid = threadIdx.x;
@@ -851,6 +837,13 @@ int attn_blocks_per_cu(bool fp8) {
                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, attn_fused_kernel<false>, kAttnThreads, 0);
   if (e != hipSuccess || f != hipSuccess || nb <= 0 || nf <= 0) return 1;
   return nb < nf ? nb : nf;
+}
+
+int attn_static_blocks_per_cu(bool fp8) {
+  int n = 0;
+  hipError_t e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_static_kernel<true>, kAttnThreads, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_static_kernel<false>, kAttnThreads, 0);
+  return (e != hipSuccess || n <= 0) ? 1 : n;
 }
 
 hipError_t launch_attn_balanced(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream) {

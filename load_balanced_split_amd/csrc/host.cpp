@@ -51,12 +51,17 @@ hpa_status check_desc(const hpa_attn_desc* d) {
 struct DeviceInfo {
   bool ready = false;
   int cus = 0;
-  int per_cu = 0;
+  int per_cu = 0;          // persistent (balanced) attention workgroups per CU
+  int per_cu_static = 0;   // static split-KV attention workgroups per CU
 };
 std::mutex g_dev_mu;
 std::vector<DeviceInfo> g_dev;
 
-hpa_status resolve_workers(int32_t requested, int32_t* out) {
+bool is_static(hpa_sched s) { return s == HPA_SCHED_STATIC_SPLITS || s == HPA_SCHED_STATIC_CHUNK; }
+
+// num_workers as given, or (0) the default of the schedule; sched < 0: the
+// largest default over all schedules (workspace sizing).
+hpa_status resolve_workers(int32_t requested, int sched, int32_t* out) {
   if (requested < 0) return fail(HPA_ERR_INVALID_ARG, "num_workers %d < 0", requested);
   if (requested > 0) {
     *out = requested;
@@ -64,7 +69,12 @@ hpa_status resolve_workers(int32_t requested, int32_t* out) {
   }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(HPA_ERR_DEVICE, "hipGetDevice failed");
-  return hpa_default_num_workers(dev, out);
+  if (sched >= 0) return hpa_default_num_workers(dev, static_cast<hpa_sched>(sched), out);
+  int32_t a = 0, b = 0;
+  hpa_status st = hpa_default_num_workers(dev, HPA_SCHED_BALANCED, &a);
+  if (st == HPA_OK) st = hpa_default_num_workers(dev, HPA_SCHED_STATIC_SPLITS, &b);
+  *out = std::max(a, b);
+  return st;
 }
 
 }  // namespace
@@ -85,8 +95,11 @@ const char* hpa_status_string(hpa_status s) {
 
 const char* hpa_last_error_message(void) { return g_last_error.c_str(); }
 
-hpa_status hpa_default_num_workers(int device, int32_t* num_workers) {
+hpa_status hpa_default_num_workers(int device, hpa_sched sched, int32_t* num_workers) {
   if (!num_workers) return fail(HPA_ERR_INVALID_ARG, "num_workers is NULL");
+  if (sched != HPA_SCHED_BALANCED && sched != HPA_SCHED_STATIC_SPLITS && sched != HPA_SCHED_STATIC_CHUNK &&
+      sched != HPA_SCHED_BALANCED_FUSED)
+    return fail(HPA_ERR_INVALID_ARG, "sched %d", static_cast<int>(sched));
   std::lock_guard<std::mutex> lock(g_dev_mu);
   if (device < 0) return fail(HPA_ERR_INVALID_ARG, "device %d", device);
   if (static_cast<size_t>(device) >= g_dev.size()) g_dev.resize(device + 1);
@@ -98,13 +111,15 @@ hpa_status hpa_default_num_workers(int device, int32_t* num_workers) {
     int cus = 0;
     hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
     const int per_cu = std::min(hpa::attn_blocks_per_cu(false), hpa::attn_blocks_per_cu(true));
+    const int per_cu_static = std::min(hpa::attn_static_blocks_per_cu(false), hpa::attn_static_blocks_per_cu(true));
     (void)hipSetDevice(cur);
     if (e != hipSuccess || cus <= 0) return fail(HPA_ERR_DEVICE, "cannot read the CU count of device %d", device);
     di.cus = cus;
     di.per_cu = per_cu;
+    di.per_cu_static = per_cu_static;
     di.ready = true;
   }
-  *num_workers = di.cus * di.per_cu;
+  *num_workers = di.cus * (is_static(sched) ? di.per_cu_static : di.per_cu);
   return HPA_OK;
 }
 
@@ -113,7 +128,7 @@ hpa_status hpa_plan_workspace_layout(const hpa_attn_desc* desc, int32_t num_work
   if (st != HPA_OK) return st;
   if (!layout) return fail(HPA_ERR_INVALID_ARG, "layout is NULL");
   int32_t W = 0;
-  if ((st = resolve_workers(num_workers, &W)) != HPA_OK) return st;
+  if ((st = resolve_workers(num_workers, -1, &W)) != HPA_OK) return st;
   const hpa::PlanOffsets o = hpa::plan_offsets(int64_t(desc->batch) * desc->num_kv_heads, W);
   layout->header = o.header * 4;
   layout->C = o.C * 4;
@@ -145,7 +160,7 @@ hpa_status hpa_partial_workspace_size(const hpa_attn_desc* desc, int32_t num_wor
   if (st != HPA_OK) return st;
   if (!bytes) return fail(HPA_ERR_INVALID_ARG, "bytes is NULL");
   int32_t W = 0;
-  if ((st = resolve_workers(num_workers, &W)) != HPA_OK) return st;
+  if ((st = resolve_workers(num_workers, -1, &W)) != HPA_OK) return st;
   const int64_t S = int64_t(desc->batch) * desc->num_kv_heads;
   *bytes = static_cast<size_t>(hpa::partial_layout(W + S, desc->num_q_heads / desc->num_kv_heads).total_bytes +
                                hpa::trace_bytes(W + S));
@@ -160,7 +175,7 @@ hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t 
   if (!plan_ws) return fail(HPA_ERR_INVALID_ARG, "plan_ws is NULL");
   if (desc->batch > 0 && !seq_lens) return fail(HPA_ERR_INVALID_ARG, "seq_lens is NULL");
   int32_t W = 0;
-  if ((st = resolve_workers(num_workers, &W)) != HPA_OK) return st;
+  if ((st = resolve_workers(num_workers, HPA_SCHED_BALANCED, &W)) != HPA_OK) return st;
   const hpa::PlanOffsets o = hpa::plan_offsets(int64_t(desc->batch) * desc->num_kv_heads, W);
   if (plan_ws_bytes < static_cast<size_t>(o.total * 4))
     return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)(o.total * 4));
@@ -192,7 +207,7 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   const bool fp8 = desc->kv_dtype == HPA_KV_FP8_E4M3;
   if (fp8 && (!k_scale || !v_scale)) return fail(HPA_ERR_INVALID_ARG, "E4M3 cache needs k_scale and v_scale");
   int32_t W = 0;
-  if ((st = resolve_workers(num_workers, &W)) != HPA_OK) return st;
+  if ((st = resolve_workers(num_workers, static_cast<int>(sched), &W)) != HPA_OK) return st;
   const int64_t S = int64_t(desc->batch) * desc->num_kv_heads;
   const int G = desc->num_q_heads / desc->num_kv_heads;
   const hpa::PartialLayout pl = hpa::partial_layout(W + S, G);

@@ -179,6 +179,20 @@ __device__ inline int seq_of_tile(const int32_t* C, int S, int t) {
 
 __device__ inline int tiles_of(int L) { return (L + kPage - 1) / kPage; }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves: shifts
+// by 1, 2, 4, 8 within each row of 16 lanes (lanes whose source falls outside
+// the row add 0), then lane 15 of rows 0 and 2 is added to rows 1 and 3, and
+// lane 31 to rows 2 and 3. Every lane must be active.
+__device__ inline int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 // Launch wrappers (defined in the .hip files). Return hipSuccess or the launch error.
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_pages, int num_workers,
                        int min_tiles, int32_t* plan, const PlanOffsets& po, hipStream_t stream);
@@ -196,6 +210,7 @@ hipError_t launch_prologue(const hpa_attn_desc& d, const uint16_t* q_in, const u
                            const float* k_scale, const float* v_scale, uint16_t* q_out,
                            int32_t* seq_lens_out, int32_t* err_word, hipStream_t stream);
 hipError_t launch_clear_word(int32_t* word, hipStream_t stream);
-int attn_blocks_per_cu(bool fp8);
+int attn_blocks_per_cu(bool fp8);         // persistent attention kernels
+int attn_static_blocks_per_cu(bool fp8);  // static split-KV attention kernel
 
 }  // namespace hpa

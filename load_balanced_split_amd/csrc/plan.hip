@@ -23,28 +23,12 @@ __device__ void block_exclusive_scan2(int va, int vb, int2* tmp /* kPlanThreads/
                                       int& rb, int& ta, int& tb) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   constexpr int nw = kPlanThreads / 64;
-  int xa = va, xb = vb;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int ya = __shfl_up(xa, o, 64), yb = __shfl_up(xb, o, 64);
-    if (lane >= o) {
-      xa += ya;
-      xb += yb;
-    }
-  }
+  const int xa = wave_incl_scan(va), xb = wave_incl_scan(vb);
   if (lane == 63) tmp[wid] = make_int2(xa, xb);
   __syncthreads();
   if (wid == 0) {
     const int2 t = lane < nw ? tmp[lane] : make_int2(0, 0);
-    int ua = t.x, ub = t.y;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int ya = __shfl_up(ua, o, 64), yb = __shfl_up(ub, o, 64);
-      if (lane >= o) {
-        ua += ya;
-        ub += yb;
-      }
-    }
+    const int ua = wave_incl_scan(t.x), ub = wave_incl_scan(t.y);
     if (lane < nw) tmp[lane] = make_int2(ua - t.x, ub - t.y);
     if (lane == nw - 1) tmp[nw] = make_int2(ua, ub);
   }
@@ -135,6 +119,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   // 3. items per worker and their CSR offsets
   int32_t* woff = ws + po.worker_off;
   int carry_i = 0;
+  int my_off = 0;                     // worker tid's first item (kept when one pass covers all workers)
   for (int base = 0; base < Wp; base += kPlanThreads) {
     const int w = base + tid;
     int cnt = 0;
@@ -146,7 +131,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     }
     int ex, unused, tot, unused_t;
     block_exclusive_scan2(cnt, 0, tmp, ex, unused, tot, unused_t);
-    if (w < Wp) woff[w] = carry_i + ex;
+    if (w < Wp) woff[w] = my_off = carry_i + ex;
     carry_i += tot;
   }
   if (tid == 0) woff[Wp] = carry_i;
@@ -162,7 +147,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     int a = range_begin(w, Wp, N, small);
     const int e = range_begin(w + 1, Wp, N, small);
     int s = seq_of_tile(C, S, a);
-    int pos = woff[w];
+    int pos = Wp <= kPlanThreads ? my_off : woff[w];
     while (a < e) {
       const int c0 = C[s], c1 = C[s + 1];
       if (c1 > c0) {

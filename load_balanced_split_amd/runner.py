@@ -35,11 +35,17 @@ class DeviceStep:
         self.seq_lens = up(w.seq_lens)
         self.page_table = up(w.page_table)
         self.desc = _lib.make_desc(w.batch, w.hq, w.hkv, w.max_pages, w.num_pages, w.kv_dtype, w.sm_scale)
-        self.num_workers = num_workers or _lib.hpa_default_num_workers(dev.index or 0)
-        self.plan_ws = torch.zeros(_lib.hpa_plan_workspace_size(self.desc, self.num_workers),
+        # an explicit worker count serves every schedule; otherwise each schedule takes
+        # its own default (persistent grid, or the W static split-KV sizes its splits by)
+        di = dev.index or 0
+        self.num_workers = num_workers or _lib.hpa_default_num_workers(di, "balanced")
+        self.static_workers = num_workers or _lib.hpa_default_num_workers(di, "static_splits")
+        ws_workers = max(self.num_workers, self.static_workers)
+        self.plan_ws = torch.zeros(_lib.hpa_plan_workspace_size(self.desc, ws_workers),
                                    dtype=torch.uint8, device=dev)
-        self.partial_ws = torch.empty(_lib.hpa_partial_workspace_size(self.desc, self.num_workers),
+        self.partial_ws = torch.empty(_lib.hpa_partial_workspace_size(self.desc, ws_workers),
                                       dtype=torch.uint8, device=dev)
+        self.last_workers = self.num_workers
         self.out = torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device=dev)
         if w.has_prologue:
             self.q_new = up(w.q_new.view(np.int16), torch.bfloat16)
@@ -68,8 +74,10 @@ class DeviceStep:
 
     def attend(self, sched: str = "balanced", stream=None, flags: int = 0):
         q, lens = self.attn_inputs()
+        W = self.static_workers if sched.startswith("static") else self.num_workers
+        self.last_workers = W
         _lib.hpa_decode_attn(self.desc, sched, q, self.k_cache, self.v_cache, self.k_scale, self.v_scale,
-                             lens, self.page_table, self.num_workers, self.plan_ws, self.partial_ws,
+                             lens, self.page_table, W, self.plan_ws, self.partial_ws,
                              self.out, flags, stream)
 
     def step(self, sched: str = "balanced", min_tiles: int = 1, stream=None):
@@ -106,10 +114,11 @@ class DeviceStep:
             raise RuntimeError("trace records need the instrumented build (HPA_TRACE=1)")
         w = self.w
         S = w.batch * w.hkv
-        base = (self.num_workers + S) * (w.hq // w.hkv) * (128 + 2) * 4
+        W = self.last_workers
+        base = (W + S) * (w.hq // w.hkv) * (128 + 2) * 4
         raw = self.partial_ws[base:].cpu().numpy()
-        n = (self.num_workers + S) * _lib.TRACE_WAVES * _lib.TRACE_WORDS
-        return raw[: n * 8].view(np.uint64).reshape(self.num_workers + S, _lib.TRACE_WAVES, _lib.TRACE_WORDS)
+        n = (W + S) * _lib.TRACE_WAVES * _lib.TRACE_WORDS
+        return raw[: n * 8].view(np.uint64).reshape(W + S, _lib.TRACE_WAVES, _lib.TRACE_WORDS)
 
     def output_f64(self) -> np.ndarray:
         return self.out.float().cpu().numpy().astype(np.float64)

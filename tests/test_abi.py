@@ -85,6 +85,10 @@ def test_calls_reject_bad_arguments_before_launching(L):
     # prologue: aliasing positions / seq_lens_out is refused
     assert L.hpa_decode_prologue(ctypes.byref(d), fake, fake, fake, fake, fake, 1e-6, 1e6, fake, fake, fake,
                                  fake, None, None, fake, fake, None, None) == 1
+    # default worker count: an unknown schedule or a NULL output is refused before any device query
+    n = ctypes.c_int32(0)
+    assert L.hpa_default_num_workers(0, 7, ctypes.byref(n)) == 1
+    assert L.hpa_default_num_workers(0, 0, None) == 1
     # empty batch is a no-op
     d0 = _desc(batch=0)
     assert L.hpa_decode_attn(ctypes.byref(d0), 1, None, None, None, None, None, None, None, 512, None, 0,
