@@ -1,9 +1,12 @@
 """Benchmark: load-balanced split-KV decode attention on one MI355X.
 
 A step is the whole hot path over one batch resident in HBM: plan -> attention
--> merge (plus the fused prologue for the E4M3 workload). The default workload
-is the skewed batch (1 x 131072 + 31 x 4096 tokens, 8:1 GQA, head dim 128,
-64-token pages, bf16 KV), where the pages report their kernel-level gain.
+-> merge (plus the fused prologue for the E4M3 workload). The headline schedule
+(--schedule, default fused) evaluates the planner's closed forms inside the
+persistent attention kernel; the other balanced schedule (a separate planner
+launch, same work list, same output bits) is reported beside it. The default
+workload is the skewed batch (1 x 131072 + 31 x 4096 tokens, 8:1 GQA, head dim
+128, 64-token pages, bf16 KV), where the pages report their kernel-level gain.
 
 Timing:
 * headline: K steps (rounded down to a multiple of R) replayed from one HIP
@@ -45,6 +48,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", type=int, default=2, help="0..4 (2 = skewed 1x128K + 31x4K)")
     p.add_argument("--num-workers", type=int, default=0)
+    p.add_argument("--schedule", choices=["fused", "balanced"], default="fused",
+                   help="headline balanced schedule: planner inside the persistent kernel (fused) "
+                        "or a separate planner launch (balanced)")
     p.add_argument("--event-steps", type=int, default=60)
     p.add_argument("--no-static", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -52,8 +58,8 @@ def parse():
     p.add_argument("--trace", action="store_true",
                    help="use the instrumented build and report per-CU busy time (tail balance) instead")
     p.add_argument("--pmc-run", action="store_true",
-                   help="short run for rocprofv3 counter passes: a 1 GiB calibration copy, then a few "
-                        "steps of each balanced schedule over rotating copies")
+                   help="short run for rocprofv3 counter passes: 1 GiB calibration read and write "
+                        "kernels, then a few steps of each balanced schedule over rotating copies")
     return p.parse_args()
 
 
@@ -66,12 +72,14 @@ def pmc_main(args):
     w = inputs.config_workload(args.workload)
     R = max(2, math.ceil(2 * MALL_BYTES / (w.k_cache.nbytes + w.v_cache.nbytes)) + 1)
     copies = [DeviceStep(w, num_workers=args.num_workers) for _ in range(min(R, 16))]
-    src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
+    # calibration kernels: a reduction that reads CALIBRATION_BYTES and writes one value,
+    # and a fill that writes CALIBRATION_BYTES and reads nothing
+    buf = torch.empty(CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
     for _ in range(3):
-        dst.copy_(src)                                   # the calibration kernel: 1 GiB read + 1 GiB written
+        buf.fill_(1.0)
+        _ = buf.sum()
     torch.cuda.synchronize()
-    del src, dst
+    del buf
     for sched in ("balanced", "fused"):
         for rep in range(2):
             for d in copies:
@@ -316,9 +324,11 @@ def main():
             assert torch.equal(d.out, eager[sched])
         return res
 
-    # balanced (the method) -- headline
-    step_s = graph_time("balanced")
-    ev = kernel_times("balanced")
+    # the balanced method -- headline schedule, the other balanced schedule beside it
+    head = args.schedule
+    other = "balanced" if head == "fused" else "fused"
+    step_s = graph_time(head)
+    ev = kernel_times(head)
     us = step_s * 1e6
     kv_gbps = kv_bytes / step_s / 1e9
     attn_s = ev["attn"] * 1e-3
@@ -336,7 +346,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 q/out",
         "data": "synthetic (seeded; shapes and length mix of the pages' kernel benchmark)",
-        "config": {"workload": inputs.CONFIG_NAMES[args.workload], "schedule": "balanced",
+        "config": {"workload": inputs.CONFIG_NAMES[args.workload], "schedule": SCHED_NAMES[head],
                    "num_workers": W, "static_num_workers": copies[0].static_workers,
                    "rotating_copies": R, "kv_bytes": kv_bytes,
                    "algorithmic_bytes": alg_bytes},
@@ -344,19 +354,19 @@ def main():
         "kv_frac_of_peak": round(kv_gbps / PEAK_HBM_GBPS, 4),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in ev.items()},
         "attn_plus_merge_kv_gbps": round(kv_bytes / ((ev["attn"] + ev["merge"]) * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "hbm", "kernel": "attn_balanced_kernel<bf16>" if w.kv_dtype == "bf16"
-                     else "attn_balanced_kernel<fp8>",
+        "roofline": {"bound": "hbm", "kernel": attn_kernel_name(head, w.kv_dtype),
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic_per_launch(head, w.kv_dtype, args.workload)},
     }
     if pro_bytes:
         result["config"]["prologue_bytes"] = pro_bytes
-    # the same work list computed inside the persistent kernel (one launch less)
-    tf = graph_time("fused")
-    ef = kernel_times("fused")
-    result["balanced_fused"] = {"us_per_step": round(tf * 1e6, 2), "kv_gbps": round(kv_bytes / tf / 1e9, 1),
-                                "attn_us": round(ef["attn"] * 1e3, 2), "merge_us": round(ef["merge"] * 1e3, 2),
-                                "kv_frac_of_peak": round(kv_bytes / tf / 1e9 / PEAK_HBM_GBPS, 4)}
+    # the other balanced schedule: same work list and bits, planner inside / outside the kernel
+    tf = graph_time(other)
+    ef = kernel_times(other)
+    result[SCHED_NAMES[other]] = {"us_per_step": round(tf * 1e6, 2), "kv_gbps": round(kv_bytes / tf / 1e9, 1),
+                                  "kernel_us": {k: round(v * 1e3, 2) for k, v in ef.items()},
+                                  "kv_frac_of_peak": round(kv_bytes / tf / 1e9 / PEAK_HBM_GBPS, 4)}
     if not args.no_static:
         st = {}
         for s in scheds[2:]:
@@ -370,6 +380,27 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, kv_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+SCHED_NAMES = {"fused": "balanced_fused", "balanced": "balanced_planned"}
+WORKLOAD_KEYS = {0: "tiny", 1: "uniform", 2: "skewed", 3: "mix", 4: "fp8_prologue"}
+
+
+def attn_kernel_name(sched, kv_dtype):
+    base = "attn_fused_kernel" if sched == "fused" else "attn_balanced_kernel"
+    return f"{base}<{'bf16' if kv_dtype == 'bf16' else 'fp8'}>"
+
+
+def traffic_per_launch(sched, kv_dtype, workload):
+    """HBM bytes per launch of the headline attention kernel from the committed
+    rocprofv3 counter summary of this workload; None when there is none or it was
+    taken on other kernel sources."""
+    from load_balanced_split_amd.profiling import read_traffic
+    key = ("attn_fused_kernel" if sched == "fused" else "attn_balanced_kernel") + \
+          ("<false>" if kv_dtype == "bf16" else "<true>")
+    path = os.path.join(ROOT, "profiles", f"attn_hbm_traffic_{WORKLOAD_KEYS[workload]}.txt")
+    t = read_traffic(path, key)
+    return None if t is None else int(round(t))
 
 
 def cpu_baseline(w, kv_bytes, budget_s):

@@ -24,6 +24,7 @@
 // P*V.
 #include "hpa_internal.hpp"
 
+#include <algorithm>
 #include <cmath>
 
 namespace hpa {
@@ -139,7 +140,7 @@ struct UnitBuf {
 
 struct Item {
   int s, t0, t1, slot;
-  int nsplit, pbase;     // splits of sequence s and its first partial slot (fused schedule)
+  int L;                 // live length of the item's request when the source knows it, else -1
 };
 
 // One step of the split combine: fold (mk, lk, ak) into the running (M, L, A).
@@ -335,7 +336,7 @@ struct Worker {
     // integer division runs on the VALU: bring the (uniform) result back to an SGPR
     st.b = __builtin_amdgcn_readfirstlane(s / a.hkv);
     st.g = s - st.b * a.hkv;
-    st.L = sload(a.seq_lens, st.b);
+    st.L = it.L >= 0 ? it.L : sload(a.seq_lens, st.b);
     st.kscale = FP8 ? sloadf(a.k_scale, st.g) : 1.f;
     st.vscale = FP8 ? sloadf(a.v_scale, st.g) : 1.f;
     if (!st.valid && threadIdx.x == 0 && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PLAN);
@@ -550,7 +551,7 @@ struct PlanSource {
   __device__ bool next(Item& it) {
     if (i >= i1) return false;
     it = Item{sload(a.plan, a.po.item_s + i), sload(a.plan, a.po.item_t0 + i), sload(a.plan, a.po.item_t1 + i),
-              sload(a.plan, a.po.item_slot + i), 0, 0};
+              sload(a.plan, a.po.item_slot + i), -1};
     ++i;
     return true;
   }
@@ -608,7 +609,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a
   const int t0 = k * chunk, t1 = min(n, t0 + chunk);
   if (t0 >= t1) return;
   const int nchunks = (n + chunk - 1) / chunk;
-  SingleSource src{Item{s, t0, t1, nchunks > 1 ? s * a.static_splits + k : -1, 0, 0}, false};
+  SingleSource src{Item{s, t0, t1, nchunks > 1 ? s * a.static_splits + k : -1, L}, false};
   Worker<FP8> r(a, lds);
   r.trec = tr.rec;
   r.run(src);
@@ -623,6 +624,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a
 struct FusedPlanLds {
   int C[kFusedMaxSeqs + 1];
   int PB[kFusedMaxSeqs];
+  int L[kFusedMaxSeqs];       // live length of each sequence's request (0 if invalid)
   int tot[kFusedMaxSeqs / 64];
 };
 
@@ -657,7 +659,7 @@ struct FusedSource {
         const int split = w - first;
         const int ns = __builtin_amdgcn_readfirstlane(owner_of_tile(c1 - 1, Wp, N, small)) - first + 1;
         const int pb = __builtin_amdgcn_readfirstlane(P.PB[s]);
-        it = Item{s, pos - c0, t1 - c0, ns > 1 ? pb + split : -1, ns, pb};
+        it = Item{s, pos - c0, t1 - c0, ns > 1 ? pb + split : -1, __builtin_amdgcn_readfirstlane(P.L[s])};
         if (split == 0 && threadIdx.x == 0) {          // record for the merge kernel
           a.plan[a.po.num_splits + s] = ns;
           a.plan[a.po.partial_base + s] = pb;
@@ -672,6 +674,56 @@ struct FusedSource {
   }
 };
 
+// Register planner for batches of up to kRegPlanSeqs sequences: every wave
+// evaluates the per-sequence prefix sums by itself (lane l of chunk k holds
+// sequence 64k + l; DPP scans, no LDS, no barrier); wave 0 then publishes them
+// to LDS. Same integer arithmetic as plan_kernel.
+constexpr int kRegPlanChunks = kRegPlanSeqs / 64;
+
+struct RegPlan {
+  int L[kRegPlanChunks], C[kRegPlanChunks], n[kRegPlanChunks], PB[kRegPlanChunks];
+  int N, Wp;
+  bool small, bad;
+
+  __device__ void build(const AttnArgs& a, int S, int W, int lane) {
+    int carry = 0;
+    bool bad_lane = false;
+#pragma unroll
+    for (int k = 0; k < kRegPlanChunks; ++k) {
+      const int s = 64 * k + lane;
+      int Lk = 0;
+      if (64 * k < S && s < S) {
+        Lk = a.seq_lens[s / a.hkv];
+        if (Lk < 0 || Lk > a.max_pages * kPage) {
+          bad_lane = true;
+          Lk = 0;
+        }
+      }
+      L[k] = Lk;
+      n[k] = tiles_of(Lk);
+      const int incl = wave_incl_scan(n[k]);
+      C[k] = carry + incl - n[k];
+      carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+    N = carry;
+    Wp = N == 0 ? 0 : min(W, max(1, N / a.min_tiles));
+    small = small_products(N, Wp);
+    bad = __builtin_amdgcn_ballot_w64(bad_lane) != 0;
+    carry = 0;
+#pragma unroll
+    for (int k = 0; k < kRegPlanChunks; ++k) {
+      int v = 0;
+      if (n[k] > 0) {
+        const int ns = owner_of_tile(C[k] + n[k] - 1, Wp, N, small) - owner_of_tile(C[k], Wp, N, small) + 1;
+        v = ns > 1 ? ns : 0;
+      }
+      const int incl = wave_incl_scan(v);
+      PB[k] = carry + incl - v;
+      carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+};
+
 template <bool FP8>
 __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_kernel(AttnArgs a) {
   __shared__ CombineLds lds;
@@ -680,45 +732,73 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int S = a.batch * a.hkv, nch = (S + 63) / 64;
-  // tile counts and their chunk-local exclusive prefix sums
-  int bad = 0;
-  for (int ch = wave; ch < nch; ch += kWaves) {
-    const int s = ch * 64 + lane;
-    int n = 0;
-    if (s < S) {
-      const int L = a.seq_lens[s / a.hkv];
-      if (L < 0 || L > a.max_pages * kPage) bad = 1;
-      else n = tiles_of(L);
-    }
-    const int x = wave_incl_scan(n);
-    if (s < S) P.C[s] = x - n;
-    if (lane == 63) P.tot[ch] = x;
-  }
-  bad = __builtin_amdgcn_readfirstlane(__syncthreads_or(bad));
-  const int N = add_chunk_offsets(P, P.C, S, nch, lane, wave);
-  if (threadIdx.x == 0) P.C[S] = N;
-  __syncthreads();
   const int W = gridDim.x;
-  const int Wp = __builtin_amdgcn_readfirstlane(N == 0 ? 0 : min(W, max(1, N / a.min_tiles)));
-  const bool small = small_products(N, Wp);
-  // partial-slot bases: exclusive prefix of (num_splits > 1 ? num_splits : 0)
-  for (int ch = wave; ch < nch; ch += kWaves) {
-    const int s = ch * 64 + lane;
-    int v = 0;
-    if (s < S) {
-      const int c0 = P.C[s], c1 = P.C[s + 1];
-      if (c1 > c0) {
-        const int ns = owner_of_tile(c1 - 1, Wp, N, small) - owner_of_tile(c0, Wp, N, small) + 1;
-        v = ns > 1 ? ns : 0;
+  int N, Wp, bad;
+  bool small;
+  if (S <= kRegPlanSeqs) {
+    RegPlan R;
+    R.build(a, S, W, lane);
+    N = R.N;
+    Wp = R.Wp;
+    small = R.small;
+    bad = R.bad;
+    if (wave == 0) {
+#pragma unroll
+      for (int k = 0; k < kRegPlanChunks; ++k) {
+        const int s = 64 * k + lane;
+        if (s < S) {
+          P.C[s] = R.C[k];
+          P.PB[s] = R.PB[k];
+          P.L[s] = R.L[k];
+        }
       }
+      if (lane == 0) P.C[S] = N;
     }
-    const int x = wave_incl_scan(v);
-    if (s < S) P.PB[s] = x - v;
-    if (lane == 63) P.tot[ch] = x;
+    __syncthreads();
+  } else {
+    // tile counts and their chunk-local exclusive prefix sums
+    bad = 0;
+    for (int ch = wave; ch < nch; ch += kWaves) {
+      const int s = ch * 64 + lane;
+      int n = 0;
+      if (s < S) {
+        int L = a.seq_lens[s / a.hkv];
+        if (L < 0 || L > a.max_pages * kPage) {
+          bad = 1;
+          L = 0;
+        }
+        n = tiles_of(L);
+        P.L[s] = L;
+      }
+      const int x = wave_incl_scan(n);
+      if (s < S) P.C[s] = x - n;
+      if (lane == 63) P.tot[ch] = x;
+    }
+    bad = __builtin_amdgcn_readfirstlane(__syncthreads_or(bad));
+    N = add_chunk_offsets(P, P.C, S, nch, lane, wave);
+    if (threadIdx.x == 0) P.C[S] = N;
+    __syncthreads();
+    Wp = __builtin_amdgcn_readfirstlane(N == 0 ? 0 : min(W, max(1, N / a.min_tiles)));
+    small = small_products(N, Wp);
+    // partial-slot bases: exclusive prefix of (num_splits > 1 ? num_splits : 0)
+    for (int ch = wave; ch < nch; ch += kWaves) {
+      const int s = ch * 64 + lane;
+      int v = 0;
+      if (s < S) {
+        const int c0 = P.C[s], c1 = P.C[s + 1];
+        if (c1 > c0) {
+          const int ns = owner_of_tile(c1 - 1, Wp, N, small) - owner_of_tile(c0, Wp, N, small) + 1;
+          v = ns > 1 ? ns : 0;
+        }
+      }
+      const int x = wave_incl_scan(v);
+      if (s < S) P.PB[s] = x - v;
+      if (lane == 63) P.tot[ch] = x;
+    }
+    __syncthreads();
+    add_chunk_offsets(P, P.PB, S, nch, lane, wave);
+    __syncthreads();
   }
-  __syncthreads();
-  add_chunk_offsets(P, P.PB, S, nch, lane, wave);
-  __syncthreads();
   const int w = blockIdx.x;
   if (w == 0 && threadIdx.x == 0 && bad && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_SEQ_LEN);
   // empty (or invalid) sequences own no tile: their zero rows are spread over the workers
@@ -836,7 +916,7 @@ int attn_blocks_per_cu(bool fp8) {
   hipError_t f = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, attn_fused_kernel<true>, kAttnThreads, 0)
                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, attn_fused_kernel<false>, kAttnThreads, 0);
   if (e != hipSuccess || f != hipSuccess || nb <= 0 || nf <= 0) return 1;
-  return nb < nf ? nb : nf;
+  return std::min(nb, nf);
 }
 
 int attn_static_blocks_per_cu(bool fp8) {

@@ -203,6 +203,7 @@ hipError_t launch_attn_fused(const AttnArgs& a, bool fp8, int num_workers, hipSt
 enum MergeMode : int { MERGE_PLAN = 0, MERGE_STATIC = 1, MERGE_FUSED = 2 };
 hipError_t launch_merge(const AttnArgs& a, MergeMode mode, hipStream_t stream);
 constexpr int kFusedMaxSeqs = 2048;  // sequences (B x Hkv) the fused schedule plans in LDS
+constexpr int kRegPlanSeqs = 256;    // up to this many, every wave plans in registers instead
 hipError_t launch_prologue(const hpa_attn_desc& d, const uint16_t* q_in, const uint16_t* k_in,
                            const uint16_t* v_in, const float* q_norm_w, const float* k_norm_w,
                            float eps, double rope_theta, const int32_t* positions,

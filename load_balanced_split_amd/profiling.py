@@ -5,11 +5,12 @@
 
 `stats` reads a `--kernel-trace --stats` run (CSV or rocpd database) and prints
 per-kernel call counts and durations. `pmc` reads two `--pmc` runs (FETCH_SIZE,
-then WRITE_SIZE, KiB per dispatch), calibrates both counters on the plain copy
-kernel that `bench.py --pmc-run` launches over a buffer of known size, and
-prints the HBM bytes per launch of each kernel, plus a JSON block that bench.py
-reads back (tagged with a hash of the kernel sources, so a stale reading is
-never reported for changed kernels).
+then WRITE_SIZE, KiB per dispatch), calibrates FETCH_SIZE on the reduction and
+WRITE_SIZE on the fill that `bench.py --pmc-run` launches over a buffer of known
+size (each touches the buffer once in one direction), and prints the HBM bytes
+per launch of each kernel, plus a JSON block that bench.py reads back (tagged
+with a hash of the kernel sources, so a stale reading is never reported for
+changed kernels).
 """
 
 import csv
@@ -37,8 +38,10 @@ def short_name(name: str) -> str:
                 "merge_kernel", "plan_kernel", "prologue_kernel"):
         if key in name:
             return key
-    if "copy" in name.lower() or "CopyFunctor" in name:
-        return "copy:" + name[:60]
+    if "reduce_kernel" in name:
+        return "calib_read:reduce_kernel"
+    if "FillFunctor" in name:
+        return "calib_write:fill"
     return name[:70]
 
 
@@ -91,18 +94,21 @@ def pmc(fetch_dir, write_dir, title, command):
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         for name, kib in _pmc_rows(d, counter):
             per.setdefault(short_name(name), {}).setdefault(counter, []).append(kib)
-    copy = [k for k in per if k.startswith("copy:")]
-    if not copy:
-        raise SystemExit("no copy kernel in the PMC runs: cannot calibrate")
-    c = per[copy[0]]
+    rd, wr = per.get("calib_read:reduce_kernel"), per.get("calib_write:fill")
+    if not rd or not wr or "FETCH_SIZE" not in rd or "WRITE_SIZE" not in wr:
+        raise SystemExit("calibration kernels missing from the PMC runs")
     known_kib = CALIBRATION_BYTES / 1024.0
-    f_fetch = known_kib / (sum(c["FETCH_SIZE"]) / len(c["FETCH_SIZE"]))
-    f_write = known_kib / (sum(c["WRITE_SIZE"]) / len(c["WRITE_SIZE"]))
+    # the 1 GiB dispatches are the largest of their kind (workspace fills are small)
+    f_fetch = known_kib / max(rd["FETCH_SIZE"])
+    f_write = known_kib / max(wr["WRITE_SIZE"])
     lines = [f"# {title}", "", f"command: {command}", "",
-             f"calibration: copy of {CALIBRATION_BYTES} bytes -> FETCH_SIZE x {f_fetch:.4f}, WRITE_SIZE x {f_write:.4f}",
+             f"calibration: a reduction reading {CALIBRATION_BYTES} bytes -> FETCH_SIZE x {f_fetch:.4f}; "
+             f"a fill writing {CALIBRATION_BYTES} bytes -> WRITE_SIZE x {f_write:.4f}",
              "", f"{'kernel':44s} {'fetch_KiB':>12s} {'write_KiB':>12s} {'hbm_bytes_per_launch':>22s}"]
     out = {"source_hash": source_hash(), "fetch_factor": f_fetch, "write_factor": f_write, "kernels": {}}
     for k, v in sorted(per.items()):
+        if k.startswith("calib_"):
+            continue
         fe = sum(v.get("FETCH_SIZE", [0])) / max(1, len(v.get("FETCH_SIZE", [])))
         wr = sum(v.get("WRITE_SIZE", [0])) / max(1, len(v.get("WRITE_SIZE", [])))
         hbm = (fe * f_fetch + wr * f_write) * 1024.0

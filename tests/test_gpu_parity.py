@@ -274,6 +274,22 @@ def test_device_errors_are_reported_not_faulted():
     assert d.device_error(clear=True) & _lib.DEVERR_PLAN
 
 
+@pytest.mark.parametrize("hkv", [1, 2])
+def test_fused_schedule_both_planners(hkv):
+    """Up to 256 sequences the fused kernel plans in registers, above that in LDS: both
+    give the planned schedule's bits, with empty requests and a bad length among them."""
+    rng = np.random.default_rng(31)
+    for B in (250 // hkv, 300 // hkv):
+        lens = rng.integers(0, 400, size=B)
+        lens[rng.random(B) < 0.1] = 0
+        w = inputs.build_workload("fusedplan", lens, 4 * hkv, hkv, "bf16", seed=int(B), poison=True)
+        ref = oracle_out(w)
+        W = int(rng.integers(20, 300))
+        g_bal, _, _ = run_and_compare(w, "balanced", W, ref=ref, what=f"S={B * hkv}")
+        g_fus, _, _ = run_and_compare(w, "fused", W, ref=ref, what=f"S={B * hkv}")
+        assert np.array_equal(g_bal, g_fus)
+
+
 def test_fused_reports_bad_lengths_and_large_batches_are_refused():
     w = inputs.build_workload("badf", [100, 200, 300], 8, 1, "bf16", seed=8)
     from load_balanced_split_amd.runner import DeviceStep
@@ -282,6 +298,13 @@ def test_fused_reports_bad_lengths_and_large_batches_are_refused():
     d.step("fused")
     torch.cuda.synchronize()
     assert d.device_error(clear=True) & _lib.DEVERR_SEQ_LEN
+    # the same on a batch planned in LDS (more than 256 sequences)
+    wl = inputs.build_workload("badl", [100] * 300, 2, 1, "bf16", seed=8)
+    dl = DeviceStep(wl, num_workers=40)
+    dl.seq_lens[7] = -3
+    dl.step("fused")
+    torch.cuda.synchronize()
+    assert dl.device_error(clear=True) & _lib.DEVERR_SEQ_LEN
     big = inputs.build_workload("big", [1] * 2100, 1, 1, "bf16", seed=1)
     db = DeviceStep(big, num_workers=8)
     with pytest.raises(_lib.HpaError) as e:
