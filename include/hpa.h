@@ -123,16 +123,29 @@ hpa_status hpa_plan_workspace_layout(const hpa_attn_desc* desc, int32_t num_work
  * accumulators plus a max and a sum per head. Enough for every schedule. */
 hpa_status hpa_partial_workspace_size(const hpa_attn_desc* desc, int32_t num_workers, size_t* bytes);
 
-/* Balanced planner (one workgroup): tile counts ceil(L/64) per sequence, their
- * prefix sum, W' = min(W, max(1, N / min_tiles_per_worker)) active workers,
- * worker w owning global tiles [w*N/W', (w+1)*N/W'), items cut at sequence
- * boundaries, split ranks, partial slots and the list of sequences to merge.
- * seq_lens and page_table stay on the device (no host synchronisation).
- * The plan workspace must be zero-filled before its first use (it holds the
- * sticky error word, which hpa_plan never clears). */
+/* Balanced planner (one workgroup; xiaodao.ai "HPC-Ops 把 TPOT 降 48.8%，用户未必
+ * 快一半", section "为什么 batch 越大，数字越漂亮"): tile counts n_s = ceil(L/64)
+ * per sequence and their prefix sum C. Starting an item is charged item_cost
+ * tiles (bitbyai.com "vLLM × HPC-Ops …", "Breaking Down the Kernels": the
+ * scheduler weighs work by progress): every non-empty sequence s occupies
+ * positions [P[s], P[s+1]) of the global list, P[s] = C[s] + item_cost * (non-empty
+ * sequences before s), its real tiles last. With N' = P[S] positions, W' =
+ * min(W, max(1, N' / min_tiles_per_worker)) workers (0 when there is no tile);
+ * worker w owns positions [w*N'/W', (w+1)*N'/W') and its items are the real
+ * tiles among them, cut at sequence boundaries (a worker may get none); then
+ * split ranks, partial slots and the list of sequences to merge. item_cost 0 is
+ * the plain even split of the tiles. 0 <= item_cost <= 64.
+ * seq_lens stays on the device (no host synchronisation). The plan workspace
+ * must be zero-filled before its first use (it holds the sticky error word,
+ * which hpa_plan never clears). */
 hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t num_workers,
-                    int32_t min_tiles_per_worker, void* plan_ws, size_t plan_ws_bytes,
-                    hipStream_t stream);
+                    int32_t min_tiles_per_worker, int32_t item_cost, void* plan_ws,
+                    size_t plan_ws_bytes, hipStream_t stream);
+
+/* The item cost and minimum tiles per worker the fused schedule plans with; an
+ * hpa_plan call with these values gives the fused schedule's items exactly. */
+#define HPA_FUSED_ITEM_COST 4
+#define HPA_FUSED_MIN_TILES 1
 
 /* Flags of hpa_decode_attn. The default (0) runs both launches. */
 enum {
@@ -145,7 +158,8 @@ enum {
  * HPA_SCHED_BALANCED runs the persistent kernel over the plan made by hpa_plan
  * with the same num_workers, then the merge kernel. HPA_SCHED_BALANCED_FUSED
  * needs no hpa_plan call: the persistent kernel evaluates the planner's closed
- * forms itself (same items and slots as hpa_plan with min_tiles 1) and records
+ * forms itself (same items and slots as hpa_plan with HPA_FUSED_MIN_TILES and
+ * HPA_FUSED_ITEM_COST) and records
  * each split sequence's split count and slot base in plan_ws for the merge
  * kernel; both balanced schedules produce identical bits. The static schedules
  * ignore the plan (plan_ws may still be given to receive device errors; NULL

@@ -28,6 +28,18 @@ ATTN_NO_MERGE, ATTN_MERGE_ONLY = 1, 2
 HEADER_SLOTS = dict(Wp=0, N=1, S=2, n_items=3, n_merge=4, n_partials=5, error=6, W=7)
 
 
+def _header_define(name: str) -> int:
+    m = re.search(rf"^#define\s+{name}\s+(\d+)", open(HEADER).read(), re.M)
+    if not m:
+        raise RuntimeError(f"{name} not defined in {HEADER}")
+    return int(m.group(1))
+
+
+# what the fused schedule plans with (hpa_plan with these gives its items exactly)
+FUSED_ITEM_COST = _header_define("HPA_FUSED_ITEM_COST")
+FUSED_MIN_TILES = _header_define("HPA_FUSED_MIN_TILES")
+
+
 class HpaError(RuntimeError):
     def __init__(self, status: int, where: str, message: str):
         super().__init__(f"{where}: status {status}: {message}")
@@ -68,7 +80,7 @@ def lib() -> ctypes.CDLL:
             "hpa_plan_workspace_size": [D, _I, ctypes.POINTER(ctypes.c_size_t)],
             "hpa_plan_workspace_layout": [D, _I, ctypes.POINTER(PlanLayout)],
             "hpa_partial_workspace_size": [D, _I, ctypes.POINTER(ctypes.c_size_t)],
-            "hpa_plan": [D, _P, _I, _I, _P, ctypes.c_size_t, _P],
+            "hpa_plan": [D, _P, _I, _I, _I, _P, ctypes.c_size_t, _P],
             "hpa_decode_attn": [D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I, _P, ctypes.c_size_t,
                                 _P, ctypes.c_size_t, _P, _I, _P],
             "hpa_decode_prologue": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
@@ -146,8 +158,8 @@ def hpa_partial_workspace_size(desc: AttnDesc, num_workers: int = 0) -> int:
     return n.value
 
 
-def hpa_plan(desc, seq_lens, num_workers, min_tiles_per_worker, plan_ws, stream=None):
-    _check(lib().hpa_plan(ctypes.byref(desc), _ptr(seq_lens), num_workers, min_tiles_per_worker,
+def hpa_plan(desc, seq_lens, num_workers, min_tiles_per_worker, item_cost, plan_ws, stream=None):
+    _check(lib().hpa_plan(ctypes.byref(desc), _ptr(seq_lens), num_workers, min_tiles_per_worker, item_cost,
                           _ptr(plan_ws), plan_ws.numel() * plan_ws.element_size(), _stream(stream)), "hpa_plan")
 
 

@@ -617,9 +617,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a
 }
 
 // ---- fused schedule: the planner's closed forms evaluated inside the persistent kernel ----
-// Each workgroup recomputes the tile prefix sum C and the partial-slot bases PB
-// from seq_lens in LDS (the same integer arithmetic as plan_kernel, so the items
-// and slots are identical), then walks its own range. The worker holding split 0
+// Each workgroup recomputes the position prefix sum C (tiles plus item_cost
+// virtual tiles per non-empty sequence) and the partial-slot bases PB from
+// seq_lens in LDS (the same integer arithmetic as plan_kernel, so the items and
+// slots are identical), then walks its own range. The worker holding split 0
 // of a sequence records (num_splits, partial_base) for the merge kernel.
 struct FusedPlanLds {
   int C[kFusedMaxSeqs + 1];
@@ -649,24 +650,28 @@ struct FusedSource {
   int w, Wp, N, S;
   bool small;
   int pos, e, s;
+  // positions [C[s], C[s+1]) of a non-empty sequence: item_cost virtual ones, then its tiles
   __device__ bool next(Item& it) {
     while (pos < e) {
       const int c0 = __builtin_amdgcn_readfirstlane(P.C[s]);
       const int c1 = __builtin_amdgcn_readfirstlane(P.C[s + 1]);
       if (c1 > c0) {
-        const int t1 = min(e, c1);
-        const int first = __builtin_amdgcn_readfirstlane(owner_of_tile(c0, Wp, N, small));
-        const int split = w - first;
-        const int ns = __builtin_amdgcn_readfirstlane(owner_of_tile(c1 - 1, Wp, N, small)) - first + 1;
-        const int pb = __builtin_amdgcn_readfirstlane(P.PB[s]);
-        it = Item{s, pos - c0, t1 - c0, ns > 1 ? pb + split : -1, __builtin_amdgcn_readfirstlane(P.L[s])};
-        if (split == 0 && threadIdx.x == 0) {          // record for the merge kernel
-          a.plan[a.po.num_splits + s] = ns;
-          a.plan[a.po.partial_base + s] = pb;
-        }
+        const int r0 = c0 + a.item_cost;
+        const int t1 = min(e, c1), lo = max(pos, r0);
         pos = t1;
-        ++s;
-        return true;
+        if (lo < t1) {
+          const int first = __builtin_amdgcn_readfirstlane(owner_of_tile(r0, Wp, N, small));
+          const int split = w - first;
+          const int ns = __builtin_amdgcn_readfirstlane(owner_of_tile(c1 - 1, Wp, N, small)) - first + 1;
+          const int pb = __builtin_amdgcn_readfirstlane(P.PB[s]);
+          it = Item{s, lo - r0, t1 - r0, ns > 1 ? pb + split : -1, __builtin_amdgcn_readfirstlane(P.L[s])};
+          if (split == 0 && threadIdx.x == 0) {          // record for the merge kernel
+            a.plan[a.po.num_splits + s] = ns;
+            a.plan[a.po.partial_base + s] = pb;
+          }
+          ++s;
+          return true;
+        }
       }
       ++s;
     }
@@ -677,7 +682,8 @@ struct FusedSource {
 // Register planner for batches of up to kRegPlanSeqs sequences: every wave
 // evaluates the per-sequence prefix sums by itself (lane l of chunk k holds
 // sequence 64k + l; DPP scans, no LDS, no barrier); wave 0 then publishes them
-// to LDS. Same integer arithmetic as plan_kernel.
+// to LDS. Same integer arithmetic as plan_kernel; C holds positions (tiles plus
+// item_cost virtual tiles per non-empty sequence), N their total.
 constexpr int kRegPlanChunks = kRegPlanSeqs / 64;
 
 struct RegPlan {
@@ -701,8 +707,9 @@ struct RegPlan {
       }
       L[k] = Lk;
       n[k] = tiles_of(Lk);
-      const int incl = wave_incl_scan(n[k]);
-      C[k] = carry + incl - n[k];
+      const int np = n[k] > 0 ? n[k] + a.item_cost : 0;   // positions: virtual tiles first
+      const int incl = wave_incl_scan(np);
+      C[k] = carry + incl - np;
       carry += __builtin_amdgcn_readlane(incl, 63);
     }
     N = carry;
@@ -714,7 +721,8 @@ struct RegPlan {
     for (int k = 0; k < kRegPlanChunks; ++k) {
       int v = 0;
       if (n[k] > 0) {
-        const int ns = owner_of_tile(C[k] + n[k] - 1, Wp, N, small) - owner_of_tile(C[k], Wp, N, small) + 1;
+        const int r0 = C[k] + a.item_cost;
+        const int ns = owner_of_tile(r0 + n[k] - 1, Wp, N, small) - owner_of_tile(r0, Wp, N, small) + 1;
         v = ns > 1 ? ns : 0;
       }
       const int incl = wave_incl_scan(v);
@@ -768,6 +776,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
           L = 0;
         }
         n = tiles_of(L);
+        if (n > 0) n += a.item_cost;                 // positions: virtual tiles first
         P.L[s] = L;
       }
       const int x = wave_incl_scan(n);
@@ -787,7 +796,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
       if (s < S) {
         const int c0 = P.C[s], c1 = P.C[s + 1];
         if (c1 > c0) {
-          const int ns = owner_of_tile(c1 - 1, Wp, N, small) - owner_of_tile(c0, Wp, N, small) + 1;
+          const int ns = owner_of_tile(c1 - 1, Wp, N, small) - owner_of_tile(c0 + a.item_cost, Wp, N, small) + 1;
           v = ns > 1 ? ns : 0;
         }
       }

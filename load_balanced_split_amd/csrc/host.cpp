@@ -168,10 +168,12 @@ hpa_status hpa_partial_workspace_size(const hpa_attn_desc* desc, int32_t num_wor
 }
 
 hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t num_workers,
-                    int32_t min_tiles_per_worker, void* plan_ws, size_t plan_ws_bytes, hipStream_t stream) {
+                    int32_t min_tiles_per_worker, int32_t item_cost, void* plan_ws, size_t plan_ws_bytes,
+                    hipStream_t stream) {
   hpa_status st = check_desc(desc);
   if (st != HPA_OK) return st;
   if (min_tiles_per_worker < 1) return fail(HPA_ERR_INVALID_ARG, "min_tiles_per_worker %d < 1", min_tiles_per_worker);
+  if (item_cost < 0 || item_cost > 64) return fail(HPA_ERR_INVALID_ARG, "item_cost %d outside [0, 64]", item_cost);
   if (!plan_ws) return fail(HPA_ERR_INVALID_ARG, "plan_ws is NULL");
   if (desc->batch > 0 && !seq_lens) return fail(HPA_ERR_INVALID_ARG, "seq_lens is NULL");
   int32_t W = 0;
@@ -180,7 +182,7 @@ hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t 
   if (plan_ws_bytes < static_cast<size_t>(o.total * 4))
     return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)(o.total * 4));
   if (hpa::launch_plan(seq_lens, desc->batch, desc->num_kv_heads, desc->max_pages_per_seq, W,
-                       min_tiles_per_worker, static_cast<int32_t*>(plan_ws), o, stream) != hipSuccess)
+                       min_tiles_per_worker, item_cost, static_cast<int32_t*>(plan_ws), o, stream) != hipSuccess)
     return fail(HPA_ERR_LAUNCH, "planner launch failed");
   return HPA_OK;
 }
@@ -250,7 +252,8 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   a.slots = W + S;
 
   const bool do_attn = !(flags & HPA_ATTN_MERGE_ONLY), do_merge = !(flags & HPA_ATTN_NO_MERGE);
-  a.min_tiles = 1;
+  a.min_tiles = HPA_FUSED_MIN_TILES;
+  a.item_cost = HPA_FUSED_ITEM_COST;
   if (sched == HPA_SCHED_BALANCED || sched == HPA_SCHED_BALANCED_FUSED) {
     const bool fused = sched == HPA_SCHED_BALANCED_FUSED;
     if (do_attn && (fused ? hpa::launch_attn_fused(a, fp8, W, stream) : hpa::launch_attn_balanced(a, fp8, W, stream)) !=

@@ -125,6 +125,7 @@ struct AttnArgs {
   int static_splits;           // S_split
   int static_chunk;            // fixed chunk (flavour "chunk"), 0 for flavour "splits"
   int min_tiles;               // fused schedule: minimum tiles per active worker
+  int item_cost;               // fused schedule: virtual tiles charged per item
   // instrumented builds only: per-wave records [block][wave][kTraceWords]
   uint64_t* trace;
 };
@@ -150,8 +151,9 @@ constexpr bool kTraceBuild = false;
 inline int64_t trace_bytes(int64_t blocks) { return kTraceBuild ? blocks * kWaves * kTraceWords * 8 : 0; }
 
 // Closed forms of the balanced partition, shared by the planner kernel and the
-// in-kernel planning of the fused schedule. Worker w owns global tiles
-// [w*N/W', (w+1)*N/W'); the owner of tile t is floor(((t+1)*W' - 1)/N).
+// in-kernel planning of the fused schedule. Worker w owns global positions
+// [w*N/W', (w+1)*N/W'); the owner of position t is floor(((t+1)*W' - 1)/N)
+// (N counts tiles, plus the virtual per-item tiles when items carry a cost).
 // `small` (both products below 2^31) selects exact 32-bit arithmetic.
 __device__ inline int owner_of_tile(int t, int Wp, int N, bool small) {
   if (small) return static_cast<int>((static_cast<uint32_t>(t + 1) * Wp - 1) / static_cast<uint32_t>(N));
@@ -195,7 +197,7 @@ __device__ inline int wave_incl_scan(int x) {
 
 // Launch wrappers (defined in the .hip files). Return hipSuccess or the launch error.
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_pages, int num_workers,
-                       int min_tiles, int32_t* plan, const PlanOffsets& po, hipStream_t stream);
+                       int min_tiles, int item_cost, int32_t* plan, const PlanOffsets& po, hipStream_t stream);
 hipError_t launch_attn_balanced(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream);
 hipError_t launch_attn_static(const AttnArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_attn_fused(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream);

@@ -6,12 +6,19 @@
 // HPC-Ops …", section "Breaking Down the Kernels": recomputed every decode step.
 //
 // Output (all int32, see PlanOffsets): prefix sum C over per-sequence tile
-// counts, W' active workers, worker w owning global tiles [w*N/W', (w+1)*N/W'),
-// items (s, t0, t1, split, slot) cut at sequence boundaries, num_splits,
-// partial_base and the list of sequences to merge (num_splits != 1).
+// counts, W' active workers, items (s, t0, t1, split, slot) cut at sequence
+// boundaries, num_splits, partial_base and the list of sequences to merge
+// (num_splits != 1).
+// Item cost c (bitbyai.com, same section: the scheduler weighs work by
+// progress): starting an item costs as much as c tiles, so c virtual tiles stand
+// in front of every non-empty sequence of the global list. Sequence s then
+// occupies positions [P[s], P[s+1]) with P[s] = C[s] + c * NE[s] (NE: non-empty
+// sequences before s), its real tiles at [P[s] + c, P[s+1]); N' = P[S]. Worker w
+// owns positions [w*N'/W', (w+1)*N'/W'), W' = min(W, max(1, N'/min_tiles)), and
+// its items are the real tiles it owns; c = 0 is the plain even split.
 // Every quantity is closed-form, so no thread walks another worker's range:
-//   worker owning tile t      = floor(((t+1) * W' - 1) / N)
-//   first worker of sequence s = owner of tile C[s], last = owner of C[s+1]-1.
+//   worker owning position p  = floor(((p+1) * W' - 1) / N')
+//   first worker of sequence s = owner of P[s] + c, last = owner of P[s+1] - 1.
 #include "hpa_internal.hpp"
 
 namespace hpa {
@@ -44,10 +51,20 @@ __device__ void block_exclusive_scan2(int va, int vb, int2* tmp /* kPlanThreads/
 // work on the copies in the workspace.
 constexpr int kPlanLdsSeqs = 3072;
 
+// Largest s in [0, S) with P[s] = C[s] + c * NE[s] <= t, for 0 <= t < P[S].
+__device__ inline int seq_of_pos(const int32_t* C, const int32_t* NE, int c, int S, int t) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (C[mid] + c * NE[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 template <bool LDS>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ seq_lens, int B, int Hkv, int max_pages, int W, int min_tiles,
-    int32_t* __restrict__ ws, PlanOffsets po) {
+    int cost, int32_t* __restrict__ ws, PlanOffsets po) {
   __shared__ int2 tmp[kPlanThreads / 64 + 1];
   __shared__ int sh_bad;
   __shared__ int sC[LDS ? kPlanLdsSeqs + 1 : 1];
@@ -90,8 +107,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   }
   __syncthreads();
   const int N = carry;
-  const int Wp = N == 0 ? 0 : min(W, max(1, N / min_tiles));
-  const bool small = small_products(N, Wp);
+  const int Np = N + cost * carry_ne;               // positions: real plus virtual tiles
+  const int Wp = N == 0 ? 0 : min(W, max(1, Np / min_tiles));
+  const bool small = small_products(Np, Wp);
+  auto P = [&](int s) { return C[s] + cost * NE[s]; };
 
   // 2. splits per sequence, partial slot bases, merge list
   int32_t* num_splits = LDS ? sNS : ws + po.num_splits;
@@ -102,8 +121,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int s = base + tid;
     int ns = 0;
     if (s < S) {
-      const int c0 = C[s], c1 = C[s + 1];
-      if (c1 > c0) ns = owner_of_tile(c1 - 1, Wp, N, small) - owner_of_tile(c0, Wp, N, small) + 1;
+      if (C[s + 1] > C[s])
+        ns = owner_of_tile(P(s + 1) - 1, Wp, Np, small) - owner_of_tile(P(s) + cost, Wp, Np, small) + 1;
       num_splits[s] = ns;
     }
     int ex_p, ex_m, tot_p, tot_m;
@@ -124,10 +143,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int w = base + tid;
     int cnt = 0;
     if (w < Wp) {
-      const int a = range_begin(w, Wp, N, small);
-      const int e = range_begin(w + 1, Wp, N, small);
-      const int sf = seq_of_tile(C, S, a), sl = seq_of_tile(C, S, e - 1);
-      cnt = NE[sl] - NE[sf] + 1;
+      const int a = range_begin(w, Wp, Np, small);
+      const int e = range_begin(w + 1, Wp, Np, small);
+      // sf / sl hold positions a / e - 1 (both non-empty); the sequences between them
+      // lie inside [a, e); sf and sl count when their real tiles start before e
+      const int sf = seq_of_pos(C, NE, cost, S, a), sl = seq_of_pos(C, NE, cost, S, e - 1);
+      cnt = NE[sl] - NE[sf] + 1 - (P(sf) + cost >= e ? 1 : 0) - (sl != sf && P(sl) + cost >= e ? 1 : 0);
     }
     int ex, unused, tot, unused_t;
     block_exclusive_scan2(cnt, 0, tmp, ex, unused, tot, unused_t);
@@ -144,24 +165,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   int32_t* isp = ws + po.item_split;
   int32_t* isl = ws + po.item_slot;
   for (int w = tid; w < Wp; w += kPlanThreads) {
-    int a = range_begin(w, Wp, N, small);
-    const int e = range_begin(w + 1, Wp, N, small);
-    int s = seq_of_tile(C, S, a);
+    const int a = range_begin(w, Wp, Np, small);
+    const int e = range_begin(w + 1, Wp, Np, small);
+    int s = seq_of_pos(C, NE, cost, S, a);
     int pos = Wp <= kPlanThreads ? my_off : woff[w];
-    while (a < e) {
-      const int c0 = C[s], c1 = C[s + 1];
-      if (c1 > c0) {
-        const int t1 = min(e, c1);
-        const int split = w - owner_of_tile(c0, Wp, N, small);
-        is[pos] = s;
-        it0[pos] = a - c0;
-        it1[pos] = t1 - c0;
-        isp[pos] = split;
-        isl[pos] = num_splits[s] > 1 ? pbase[s] + split : -1;
-        ++pos;
-        a = t1;
-      }
-      ++s;
+    for (; s < S && P(s) < e; ++s) {
+      if (C[s + 1] == C[s]) continue;
+      const int r0 = P(s) + cost, r1 = P(s + 1);      // the real tiles of s
+      const int lo = max(a, r0), hi = min(e, r1);
+      if (lo >= hi) continue;
+      const int split = w - owner_of_tile(r0, Wp, Np, small);
+      is[pos] = s;
+      it0[pos] = lo - r0;
+      it1[pos] = hi - r0;
+      isp[pos] = split;
+      isl[pos] = num_splits[s] > 1 ? pbase[s] + split : -1;
+      ++pos;
     }
   }
   if (LDS) {
@@ -191,13 +210,13 @@ __global__ void clear_word_kernel(int32_t* w) { *w = 0; }
 }  // namespace
 
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_pages, int num_workers,
-                       int min_tiles, int32_t* plan, const PlanOffsets& po, hipStream_t stream) {
+                       int min_tiles, int item_cost, int32_t* plan, const PlanOffsets& po, hipStream_t stream) {
   if (int64_t(batch) * hkv <= kPlanLdsSeqs)
     hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch, hkv,
-                       max_pages, num_workers, min_tiles, plan, po);
+                       max_pages, num_workers, min_tiles, item_cost, plan, po);
   else
     hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch, hkv,
-                       max_pages, num_workers, min_tiles, plan, po);
+                       max_pages, num_workers, min_tiles, item_cost, plan, po);
   return hipGetLastError();
 }
 

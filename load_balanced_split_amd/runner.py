@@ -68,9 +68,9 @@ class DeviceStep:
             return self.q_rot, self.lens_after
         return self.q, self.seq_lens
 
-    def plan(self, min_tiles: int = 1, stream=None):
+    def plan(self, min_tiles: int = _lib.FUSED_MIN_TILES, item_cost: int = _lib.FUSED_ITEM_COST, stream=None):
         _, lens = self.attn_inputs()
-        _lib.hpa_plan(self.desc, lens, self.num_workers, min_tiles, self.plan_ws, stream)
+        _lib.hpa_plan(self.desc, lens, self.num_workers, min_tiles, item_cost, self.plan_ws, stream)
 
     def attend(self, sched: str = "balanced", stream=None, flags: int = 0):
         q, lens = self.attn_inputs()
@@ -80,12 +80,13 @@ class DeviceStep:
                              lens, self.page_table, W, self.plan_ws, self.partial_ws,
                              self.out, flags, stream)
 
-    def step(self, sched: str = "balanced", min_tiles: int = 1, stream=None):
+    def step(self, sched: str = "balanced", min_tiles: int = _lib.FUSED_MIN_TILES,
+             item_cost: int = _lib.FUSED_ITEM_COST, stream=None):
         """The whole hot path of one decode step; returns the bf16 output tensor."""
         if self.w.has_prologue:
             self.prologue(stream)
         if sched == "balanced":
-            self.plan(min_tiles, stream)
+            self.plan(min_tiles, item_cost, stream)
         self.attend(sched, stream)
         return self.out
 

@@ -80,16 +80,20 @@ def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1, item_cost=0):
 
     items = []                                   # (worker, s, t0, t1)
     worker_off = [0]
+    first = 0                                    # first sequence not wholly before the worker
     for w in range(Wp):
         a = w * Np // Wp
         e = (w + 1) * Np // Wp
-        for s in range(S):
-            if n[s] == 0:
-                continue
-            r0 = start[s] + item_cost            # real tiles of s: positions [r0, r0 + n_s)
-            lo, hi = max(a, r0), min(e, r0 + n[s])
-            if lo < hi:
-                items.append((w, s, lo - r0, hi - r0))
+        while first < S and start[first + 1] <= a:
+            first += 1
+        s = first
+        while s < S and start[s] < e:            # sequences overlapping positions [a, e)
+            if n[s] > 0:
+                r0 = start[s] + item_cost        # real tiles of s: positions [r0, r0 + n_s)
+                lo, hi = max(a, r0), min(e, r0 + n[s])
+                if lo < hi:
+                    items.append((w, s, lo - r0, hi - r0))
+            s += 1
         worker_off.append(len(items))
 
     num_splits = [0] * S

@@ -62,13 +62,15 @@ def test_workspace_sizes_and_layout(L):
 def test_calls_reject_bad_arguments_before_launching(L):
     d = _desc()
     with pytest.raises(_lib.HpaError) as e:
-        L_status = L.hpa_plan(ctypes.byref(d), None, 512, 1, None, 0, None)
+        L_status = L.hpa_plan(ctypes.byref(d), None, 512, 1, 0, None, 0, None)
         _lib._check(L_status, "hpa_plan")
     assert e.value.status == 1
     # undersized plan workspace -> HPA_ERR_WORKSPACE, nothing launched
     fake = ctypes.c_void_p(0x1000)
-    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, fake, 16, None) == 3
-    assert L.hpa_plan(ctypes.byref(d), fake, 512, 0, fake, 1 << 30, None) == 1     # min_tiles < 1
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, fake, 16, None) == 3
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 0, 0, fake, 1 << 30, None) == 1     # min_tiles < 1
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, -1, fake, 1 << 30, None) == 1    # item cost < 0
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 65, fake, 1 << 30, None) == 1    # item cost > 64
     # balanced attention without a plan, fp8 without scales
     args = [fake] * 7
     assert L.hpa_decode_attn(ctypes.byref(d), 0, *args, 512, None, 0, fake, 1 << 30, fake, 0, None) == 1

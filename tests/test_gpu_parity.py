@@ -33,7 +33,7 @@ def gpu():
     return torch.device("cuda")
 
 
-def device_plan(lens, hkv, W, min_tiles):
+def device_plan(lens, hkv, W, min_tiles, item_cost=0):
     """Run the GPU planner on a length vector; return its arrays as host lists."""
     B = len(lens)
     maxp = max(1, max([(int(L) + 63) // 64 for L in lens] or [1]))
@@ -41,7 +41,7 @@ def device_plan(lens, hkv, W, min_tiles):
     size = _lib.hpa_plan_workspace_size(desc, W)
     ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
     sl = torch.tensor(np.asarray(lens, np.int32), device="cuda")
-    _lib.hpa_plan(desc, sl, W, min_tiles, ws)
+    _lib.hpa_plan(desc, sl, W, min_tiles, item_cost, ws)
     torch.cuda.synchronize()
     lay = _lib.hpa_plan_workspace_layout(desc, W)
     h = ws.cpu().numpy().view(np.int32)
@@ -55,9 +55,9 @@ def device_plan(lens, hkv, W, min_tiles):
                 partial_base=g("partial_base", S), merge_list=g("merge_list", nm))
 
 
-def check_plan(lens, hkv, W, mt):
-    got = device_plan(lens, hkv, W, mt)
-    want = op.balanced_plan(lens, hkv, W, mt)
+def check_plan(lens, hkv, W, mt, cost=0):
+    got = device_plan(lens, hkv, W, mt, cost)
+    want = op.balanced_plan(lens, hkv, W, mt, cost)
     assert got["err"] == 0
     for k in ("Wp", "N", "n_items", "n_partials") + PLAN_KEYS:
         assert got[k] == want[k], (k, lens, hkv, W, mt)
@@ -65,15 +65,16 @@ def check_plan(lens, hkv, W, mt):
 
 # ---------------------------------------------------------------- planner ---
 
+@pytest.mark.parametrize("cost", [0, 3])
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("W,mt", [(0, 1), (1, 1), (7, 1), (512, 1), (512, 4), (1024, 1), (3000, 2)])
-def test_plan_bit_exact_workload_lengths(cfg, W, mt):
+def test_plan_bit_exact_workload_lengths(cfg, W, mt, cost):
     lens = inputs.config_lengths_only(cfg) + (1 if cfg == 4 else 0)
     hkv = 4 if cfg == 3 else 1
     if W == 0:
         W = _lib.hpa_default_num_workers(0)
-    print(f"plan cfg{cfg} W={W} mt={mt}", flush=True)
-    check_plan(lens.tolist(), hkv, W, mt)
+    print(f"plan cfg{cfg} W={W} mt={mt} cost={cost}", flush=True)
+    check_plan(lens.tolist(), hkv, W, mt, cost)
 
 
 def test_plan_bit_exact_random_lengths():
@@ -87,9 +88,13 @@ def test_plan_bit_exact_random_lengths():
             lens[:] = rng.choice([0, 1, 63, 64, 65, 4096, 65535, 65536, 65537], size=B)
         W = int(rng.integers(1, 4000))
         mt = int(rng.integers(1, 6))
-        check_plan(lens.tolist(), hkv, W, mt)
+        cost = int(rng.integers(0, 6)) if trial % 2 else 0
+        check_plan(lens.tolist(), hkv, W, mt, cost)
     check_plan([0, 0, 0], 2, 16, 1)              # N == 0: no active workers
+    check_plan([0, 0, 0], 2, 16, 1, 4)
     check_plan([5000], 1, 100000 // 64, 1)       # W > N tiles
+    check_plan([64, 64], 1, 4, 1, 2)             # workers owning only virtual tiles get no item
+    check_plan([64] * 40, 1, 300, 1, 64)         # the largest cost
 
 
 # -------------------------------------------------------------- attention ---
@@ -268,7 +273,7 @@ def test_device_errors_are_reported_not_faulted():
     torch.cuda.synchronize()
     assert d.device_error(clear=True) & _lib.DEVERR_SEQ_LEN
     # attention launched with a different worker count than the plan
-    _lib.hpa_plan(d.desc, d.seq_lens, 5, 1, d.plan_ws)
+    _lib.hpa_plan(d.desc, d.seq_lens, 5, 1, 0, d.plan_ws)
     d.attend("balanced")
     torch.cuda.synchronize()
     assert d.device_error(clear=True) & _lib.DEVERR_PLAN
