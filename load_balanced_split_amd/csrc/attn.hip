@@ -334,7 +334,7 @@ struct Worker {
                it.t1 <= a.max_pages && it.slot < a.slots;
     const int s = st.valid ? it.s : 0;
     // integer division runs on the VALU: bring the (uniform) result back to an SGPR
-    st.b = __builtin_amdgcn_readfirstlane(s / a.hkv);
+    st.b = a.hkv == 1 ? s : __builtin_amdgcn_readfirstlane(s / a.hkv);
     st.g = s - st.b * a.hkv;
     st.L = it.L >= 0 ? it.L : sload(a.seq_lens, st.b);
     st.kscale = FP8 ? sloadf(a.k_scale, st.g) : 1.f;
@@ -691,15 +691,19 @@ struct RegPlan {
   int N, Wp;
   bool small, bad;
 
+  // chunks at or past S (a uniform test) are skipped whole: their lanes would hold
+  // no sequence, and nothing reads them
   __device__ void build(const AttnArgs& a, int S, int W, int lane) {
     int carry = 0;
     bool bad_lane = false;
 #pragma unroll
     for (int k = 0; k < kRegPlanChunks; ++k) {
+      L[k] = n[k] = C[k] = PB[k] = 0;
+      if (64 * k >= S) continue;
       const int s = 64 * k + lane;
       int Lk = 0;
-      if (64 * k < S && s < S) {
-        Lk = a.seq_lens[s / a.hkv];
+      if (s < S) {
+        Lk = a.seq_lens[a.hkv == 1 ? s : s / a.hkv];
         if (Lk < 0 || Lk > a.max_pages * kPage) {
           bad_lane = true;
           Lk = 0;
@@ -719,6 +723,7 @@ struct RegPlan {
     carry = 0;
 #pragma unroll
     for (int k = 0; k < kRegPlanChunks; ++k) {
+      if (64 * k >= S) continue;
       int v = 0;
       if (n[k] > 0) {
         const int r0 = C[k] + a.item_cost;
@@ -740,8 +745,8 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int S = a.batch * a.hkv, nch = (S + 63) / 64;
-  const int W = gridDim.x;
-  int N, Wp, bad;
+  const int W = gridDim.x, w = blockIdx.x;
+  int N, Wp, bad, pos = 0, pend = 0, s0 = 0;
   bool small;
   if (S <= kRegPlanSeqs) {
     RegPlan R;
@@ -750,6 +755,17 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
     Wp = R.Wp;
     small = R.small;
     bad = R.bad;
+    if (w < Wp) {
+      // this worker's positions and the sequence holding the first one (largest s
+      // with C[s] <= pos: C is non-decreasing, so count the lanes at or below pos)
+      pos = __builtin_amdgcn_readfirstlane(range_begin(w, Wp, N, small));
+      pend = __builtin_amdgcn_readfirstlane(range_begin(w + 1, Wp, N, small));
+      int cnt = 0;
+#pragma unroll
+      for (int k = 0; k < kRegPlanChunks; ++k)
+        if (64 * k < S) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(64 * k + lane < S && R.C[k] <= pos));
+      s0 = cnt - 1;
+    }
     if (wave == 0) {
 #pragma unroll
       for (int k = 0; k < kRegPlanChunks; ++k) {
@@ -807,8 +823,12 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
     __syncthreads();
     add_chunk_offsets(P, P.PB, S, nch, lane, wave);
     __syncthreads();
+    if (w < Wp) {
+      pos = __builtin_amdgcn_readfirstlane(range_begin(w, Wp, N, small));
+      pend = __builtin_amdgcn_readfirstlane(range_begin(w + 1, Wp, N, small));
+      s0 = __builtin_amdgcn_readfirstlane(seq_of_tile(P.C, S, pos));
+    }
   }
-  const int w = blockIdx.x;
   if (w == 0 && threadIdx.x == 0 && bad && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_SEQ_LEN);
   // empty (or invalid) sequences own no tile: their zero rows are spread over the workers
   for (int s = w; s < S; s += W) {
@@ -819,10 +839,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
     }
   }
   if (w >= Wp) return;
-  const int pos = __builtin_amdgcn_readfirstlane(range_begin(w, Wp, N, small));
-  const int pend = __builtin_amdgcn_readfirstlane(range_begin(w + 1, Wp, N, small));
-  const int s0 = __builtin_amdgcn_readfirstlane(seq_of_tile(P.C, S, pos));
-  FusedSource src{a, P, w, Wp, N, S, small, pos, pend, s0};
+  FusedSource src{a, P, w, Wp, N, S, small, pos, pend, __builtin_amdgcn_readfirstlane(s0)};
   Worker<FP8> r(a, lds);
   r.trec = tr.rec;
   r.run(src);
