@@ -189,7 +189,7 @@ def trace_main(args):
     W = d.num_workers
     out = {"metric": "attention tail balance (instrumented build)", "workload": inputs.CONFIG_NAMES[args.workload],
            "num_workers": W, "realtime_clock_mhz": REALTIME_MHZ}
-    for sched in ("balanced", "fused", "static_splits", "static_chunk"):
+    for sched in ("balanced", "fused", "single", "static_splits", "static_chunk"):
         reps = []
         for r in range(5):
             d.step(sched)                     # planner (if any) and a full step first
@@ -266,7 +266,7 @@ def main():
         d.step(sched)
 
     # eager reference outputs (also the warm-up of every code path)
-    scheds = ["balanced", "fused"] + ([] if args.no_static else ["static_splits", "static_chunk"])
+    scheds = ["balanced", "fused", "single"] + ([] if args.no_static else ["static_splits", "static_chunk"])
     eager = {}
     for s in scheds:
         for d in copies:
@@ -302,7 +302,7 @@ def main():
         """Average duration (ms) of each launch kind, from HIP events on the launch stream
         around a loop of back-to-back launches of that kind alone (rotating copies)."""
         kinds = (["prologue"] if w.has_prologue else []) + (["plan"] if sched == "balanced" else [])
-        kinds += ["attn", "merge"]
+        kinds += ["attn"] if sched == "single" else ["attn", "merge"]    # single: one launch merges too
         launch = {
             "prologue": lambda d: d.prologue(),
             "plan": lambda d: d.plan(),
@@ -353,7 +353,7 @@ def main():
         "us_per_step": round(us, 2),
         "kv_frac_of_peak": round(kv_gbps / PEAK_HBM_GBPS, 4),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in ev.items()},
-        "attn_plus_merge_kv_gbps": round(kv_bytes / ((ev["attn"] + ev["merge"]) * 1e-3) / 1e9, 1),
+        "attn_plus_merge_kv_gbps": round(kv_bytes / ((ev["attn"] + ev.get("merge", 0.0)) * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": attn_kernel_name(head, w.kv_dtype),
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
@@ -367,9 +367,14 @@ def main():
     result[SCHED_NAMES[other]] = {"us_per_step": round(tf * 1e6, 2), "kv_gbps": round(kv_bytes / tf / 1e9, 1),
                                   "kernel_us": {k: round(v * 1e3, 2) for k, v in ef.items()},
                                   "kv_frac_of_peak": round(kv_bytes / tf / 1e9 / PEAK_HBM_GBPS, 4)}
+    # single launch: planner, attention and merge in one persistent kernel
+    t1 = graph_time("single")
+    e1 = kernel_times("single")
+    result["balanced_single_launch"] = {"us_per_step": round(t1 * 1e6, 2), "kv_gbps": round(kv_bytes / t1 / 1e9, 1),
+                                        "kernel_us": {k: round(v * 1e3, 2) for k, v in e1.items()}}
     if not args.no_static:
         st = {}
-        for s in scheds[2:]:
+        for s in scheds[3:]:
             t = graph_time(s)
             e = kernel_times(s)
             st[s] = {"us_per_step": round(t * 1e6, 2), "attn_us": round(e["attn"] * 1e3, 2),

@@ -70,10 +70,12 @@ typedef enum {
   HPA_SCHED_BALANCED = 0,      /* work list from hpa_plan (persistent workers) */
   HPA_SCHED_STATIC_SPLITS = 1, /* fixed number of splits per sequence          */
   HPA_SCHED_STATIC_CHUNK = 2,  /* fixed split size, grid sized for the longest */
-  HPA_SCHED_BALANCED_FUSED = 3 /* the same balanced work list, computed inside the
-                                  persistent kernel from seq_lens (no hpa_plan call,
-                                  one launch less); at most 2048 sequences, one
-                                  tile per worker minimum */
+  HPA_SCHED_BALANCED_FUSED = 3, /* the same balanced work list, computed inside the
+                                   persistent kernel from seq_lens (no hpa_plan call,
+                                   one launch less); at most 2048 sequences */
+  HPA_SCHED_BALANCED_SINGLE = 4 /* as FUSED, and split sequences are merged inside the
+                                   same kernel by the workgroup that completes them
+                                   (one launch per step) */
 } hpa_sched;
 
 /* Sticky device error bits (hpa_read_device_error). */
@@ -161,13 +163,20 @@ enum {
  * forms itself (same items and slots as hpa_plan with HPA_FUSED_MIN_TILES and
  * HPA_FUSED_ITEM_COST) and records
  * each split sequence's split count and slot base in plan_ws for the merge
- * kernel; both balanced schedules produce identical bits. The static schedules
+ * kernel. HPA_SCHED_BALANCED_SINGLE merges inside the persistent kernel: a
+ * split's partial is written with device-coherent stores, then its workgroup
+ * counts itself in on an atomic counter of its group of 16 consecutive splits;
+ * the workgroup completing a group folds it (and the one completing the last
+ * group folds the group results) in the merge kernel's order; no workgroup
+ * waits on another, and the counters in plan_ws return to zero. All balanced
+ * schedules produce identical bits. The static schedules
  * ignore the plan (plan_ws may still be given to receive device errors; NULL
  * otherwise) and size their grid from num_workers. k_scale/v_scale are
  * required for E4M3 caches and ignored for bf16. partial_ws must hold
- * hpa_partial_workspace_size bytes. Two kernel launches (attention, then merge);
- * flags may split them into two calls with identical arguments, so a caller can
- * time or overlap them separately. */
+ * hpa_partial_workspace_size bytes. Two kernel launches (attention, then merge;
+ * one for HPA_SCHED_BALANCED_SINGLE, which ignores flags); flags may split them
+ * into two calls with identical arguments, so a caller can time or overlap them
+ * separately. */
 hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const void* q,
                            const void* k_cache, const void* v_cache, const float* k_scale,
                            const float* v_scale, const int32_t* seq_lens,

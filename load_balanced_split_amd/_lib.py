@@ -22,7 +22,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "hpa.h")
 
 HPA_KV_BF16, HPA_KV_FP8_E4M3 = 0, 1
 HPA_SCHED_BALANCED, HPA_SCHED_STATIC_SPLITS, HPA_SCHED_STATIC_CHUNK, HPA_SCHED_BALANCED_FUSED = 0, 1, 2, 3
-SCHED = {"balanced": 0, "static_splits": 1, "static_chunk": 2, "fused": 3}
+HPA_SCHED_BALANCED_SINGLE = 4
+SCHED = {"balanced": 0, "static_splits": 1, "static_chunk": 2, "fused": 3, "single": 4}
 DEVERR_SEQ_LEN, DEVERR_PAGE_ID, DEVERR_PROLOGUE, DEVERR_PLAN = 1, 2, 4, 8
 ATTN_NO_MERGE, ATTN_MERGE_ONLY = 1, 2
 HEADER_SLOTS = dict(Wp=0, N=1, S=2, n_items=3, n_merge=4, n_partials=5, error=6, W=7)

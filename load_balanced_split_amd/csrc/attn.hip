@@ -77,9 +77,11 @@ __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(ub, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), kBufDword3);
 }
 
-// Cache policy bits of a buffer load: 2 = nt (streaming: KV bytes are read once).
+// Cache policy bits of a buffer load: 2 = nt (streaming: KV bytes are read once),
+// 16 = sc1 (device scope).
 constexpr int kPolicyDefault = 0;
 constexpr int kPolicyStream = 2;
+constexpr int kPolicyAgent = 16;   // sc1: coherent across the device (every XCD's L2)
 
 template <int POLICY = kPolicyDefault>
 __device__ inline u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -141,6 +143,7 @@ struct UnitBuf {
 struct Item {
   int s, t0, t1, slot;
   int L;                 // live length of the item's request when the source knows it, else -1
+  int nsplit, pbase;     // splits of sequence s and its first partial slot (fused schedule)
 };
 
 // One step of the split combine: fold (mk, lk, ak) into the running (M, L, A).
@@ -160,6 +163,7 @@ struct CombineLds {
   float m[kWaves][kMaxGroup];
   float l[kWaves][kMaxGroup];
   float o[kWaves][kMaxGroup][kORow];
+  int flag;                   // an arrival count, broadcast to the workgroup
 };
 
 // Scalar view of read-only device arrays: a load through it returns one value
@@ -187,7 +191,7 @@ struct ItemState {
 // k+1's length, q and first page ids are in flight and item k+2's descriptor is
 // being read; the issue slot after a wave's last unit of item k takes its first
 // unit of item k+1, so the K/V stream of a wave never drains at an item boundary.
-template <bool FP8>
+template <bool FP8, bool INMERGE = false>
 struct Worker {
   const AttnArgs& a;
   CombineLds& lds;
@@ -466,14 +470,109 @@ struct Worker {
         a.out[(int64_t(st.b) * a.hq + st.g * a.group + hh) * kHeadDim + d] = f32_to_bf16_rne(acc / Ls);
       } else {
         const int64_t sl = st.it.slot;
-        a.part_acc[(sl * a.group + hh) * kHeadDim + d] = acc;
+        store_partial(a.part_acc + (sl * a.group + hh) * kHeadDim + d, acc);
         if (d == 0) {
-          a.part_m[sl * a.group + hh] = M;
-          a.part_l[sl * a.group + hh] = Ls;
+          store_partial(a.part_m + sl * a.group + hh, M);
+          store_partial(a.part_l + sl * a.group + hh, Ls);
         }
       }
     }
     __syncthreads();
+    if (INMERGE && st.valid && st.it.slot >= 0) arrive(st);
+  }
+
+  // Partials are read by other workgroups in the in-kernel merge: there every
+  // access to them is device-coherent (sc1: the compiler's agent-scope atomic
+  // store/load), so no L2-wide write-back or invalidate is ever needed.
+  __device__ static void store_partial(float* p, float v) {
+    if (INMERGE) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+  }
+  __device__ static float load_partial(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // In-kernel merge of split sequences (fused schedule). A split's partial is
+  // complete in memory before its workgroup counts itself in (wait for its own
+  // stores, barrier, one device-scope atomic add on the counter of its group of
+  // kMergeGroup consecutive splits). The workgroup that sees the group's last
+  // arrival folds the group's splits in split order -- the merge kernel's group
+  // step -- and either writes the output (one group) or stores the group result
+  // in the group's first slot and counts the group in on the sequence's counter;
+  // the workgroup that sees the last group folds the group results in group
+  // order and writes the output. Counters are returned to 0 by whoever saw the
+  // last arrival. Nothing waits on another workgroup.
+  __device__ int count_in(int32_t* ctr) {
+    __builtin_amdgcn_s_waitcnt(0);          // this thread's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) lds.flag = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int seen = __builtin_amdgcn_readfirstlane(lds.flag);
+    __syncthreads();                        // lds.flag is reused by the next arrival
+    return seen;
+  }
+
+  __device__ void write_row(const ItemState& st, int hh, int q4, float FL, const f32x4& FA) const {
+    uint16_t* orow = a.out + (int64_t(st.b) * a.hq + st.g * a.group + hh) * kHeadDim + 4 * q4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) orow[e] = f32_to_bf16_rne(FA[e] / FL);
+  }
+
+  __device__ void arrive(const ItemState& st) {
+    const int n = st.it.nsplit, pb = st.it.pbase, G = a.group;
+    const int gg = (st.it.slot - pb) / kMergeGroup;
+    const int gslot = pb + gg * kMergeGroup, gsize = min(kMergeGroup, n - gg * kMergeGroup);
+    const int ngrp = (n + kMergeGroup - 1) / kMergeGroup;
+    if (count_in(a.gctr + gslot) != gsize - 1) return;
+    if (threadIdx.x == 0) __hip_atomic_store(a.gctr + gslot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const rsrc_t racc = make_rsrc(a.part_acc, static_cast<uint32_t>(int64_t(a.slots) * G * kHeadDim * 4));
+    // one thread per (head, 4-dim quad)
+    for (int idx = threadIdx.x; idx < G * (kHeadDim / 4); idx += kAttnThreads) {
+      const int hh = idx / (kHeadDim / 4), q4 = idx % (kHeadDim / 4);
+      float mk[kMergeGroup], lk[kMergeGroup];
+      f32x4 ak[kMergeGroup];
+#pragma unroll
+      for (int i = 0; i < kMergeGroup; ++i) {
+        const int64_t r = int64_t(gslot + min(i, gsize - 1)) * G + hh;   // in bounds; extra ones unused
+        mk[i] = load_partial(a.part_m + r);
+        lk[i] = load_partial(a.part_l + r);
+        ak[i] = __builtin_bit_cast(f32x4, bload16<kPolicyAgent>(racc, static_cast<uint32_t>((r * kHeadDim + 4 * q4) * 4), 0));
+      }
+      float M = -INFINITY, L = 0.f;
+      f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kMergeGroup; ++i)
+        if (i < gsize) fold(M, L, A, mk[i], lk[i], ak[i]);
+      if (ngrp == 1) {
+        float FM = -INFINITY, FL = 0.f;
+        f32x4 FA = f32x4{0.f, 0.f, 0.f, 0.f};
+        fold(FM, FL, FA, M, L, A);
+        write_row(st, hh, q4, FL, FA);
+      } else {
+        const int64_t r = int64_t(gslot) * G + hh;       // the group result replaces split 0 of the group
+        float* pa = a.part_acc + r * kHeadDim + 4 * q4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) __hip_atomic_store(pa + e, A[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (q4 == 0) {
+          __hip_atomic_store(a.part_m + r, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(a.part_l + r, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    if (ngrp == 1) return;
+    if (count_in(a.sctr + st.it.s) != ngrp - 1) return;
+    if (threadIdx.x == 0) __hip_atomic_store(a.sctr + st.it.s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int idx = threadIdx.x; idx < G * (kHeadDim / 4); idx += kAttnThreads) {
+      const int hh = idx / (kHeadDim / 4), q4 = idx % (kHeadDim / 4);
+      float FM = -INFINITY, FL = 0.f;
+      f32x4 FA = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int g = 0; g < ngrp; ++g) {
+        const int64_t r = int64_t(pb + g * kMergeGroup) * G + hh;
+        const f32x4 ag = __builtin_bit_cast(f32x4, bload16<kPolicyAgent>(racc, static_cast<uint32_t>((r * kHeadDim + 4 * q4) * 4), 0));
+        fold(FM, FL, FA, load_partial(a.part_m + r), load_partial(a.part_l + r), ag);
+      }
+      write_row(st, hh, q4, FL, FA);
+    }
   }
 
   __device__ void stamp(int k) {
@@ -551,7 +650,7 @@ struct PlanSource {
   __device__ bool next(Item& it) {
     if (i >= i1) return false;
     it = Item{sload(a.plan, a.po.item_s + i), sload(a.plan, a.po.item_t0 + i), sload(a.plan, a.po.item_t1 + i),
-              sload(a.plan, a.po.item_slot + i), -1};
+              sload(a.plan, a.po.item_slot + i), -1, 0, 0};
     ++i;
     return true;
   }
@@ -609,7 +708,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a
   const int t0 = k * chunk, t1 = min(n, t0 + chunk);
   if (t0 >= t1) return;
   const int nchunks = (n + chunk - 1) / chunk;
-  SingleSource src{Item{s, t0, t1, nchunks > 1 ? s * a.static_splits + k : -1, L}, false};
+  SingleSource src{Item{s, t0, t1, nchunks > 1 ? s * a.static_splits + k : -1, L, 0, 0}, false};
   Worker<FP8> r(a, lds);
   r.trec = tr.rec;
   r.run(src);
@@ -644,6 +743,7 @@ __device__ inline int add_chunk_offsets(FusedPlanLds& P, int* arr, int S, int nc
   return total;
 }
 
+template <bool INMERGE>
 struct FusedSource {
   const AttnArgs& a;
   const FusedPlanLds& P;
@@ -664,8 +764,8 @@ struct FusedSource {
           const int split = w - first;
           const int ns = __builtin_amdgcn_readfirstlane(owner_of_tile(c1 - 1, Wp, N, small)) - first + 1;
           const int pb = __builtin_amdgcn_readfirstlane(P.PB[s]);
-          it = Item{s, lo - r0, t1 - r0, ns > 1 ? pb + split : -1, __builtin_amdgcn_readfirstlane(P.L[s])};
-          if (split == 0 && threadIdx.x == 0) {          // record for the merge kernel
+          it = Item{s, lo - r0, t1 - r0, ns > 1 ? pb + split : -1, __builtin_amdgcn_readfirstlane(P.L[s]), ns, pb};
+          if (!INMERGE && split == 0 && threadIdx.x == 0) {   // record for the merge kernel
             a.plan[a.po.num_splits + s] = ns;
             a.plan[a.po.partial_base + s] = pb;
           }
@@ -737,7 +837,7 @@ struct RegPlan {
   }
 };
 
-template <bool FP8>
+template <bool FP8, bool INMERGE>
 __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_kernel(AttnArgs a) {
   __shared__ CombineLds lds;
   __shared__ FusedPlanLds P;
@@ -839,8 +939,8 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
     }
   }
   if (w >= Wp) return;
-  FusedSource src{a, P, w, Wp, N, S, small, pos, pend, __builtin_amdgcn_readfirstlane(s0)};
-  Worker<FP8> r(a, lds);
+  FusedSource<INMERGE> src{a, P, w, Wp, N, S, small, pos, pend, __builtin_amdgcn_readfirstlane(s0)};
+  Worker<FP8, INMERGE> r(a, lds);
   r.trec = tr.rec;
   r.run(src);
   tr.units = r.units_done;
@@ -939,10 +1039,13 @@ int attn_blocks_per_cu(bool fp8) {
   int nb = 0, nf = 0;
   hipError_t e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_balanced_kernel<true>, kAttnThreads, 0)
                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_balanced_kernel<false>, kAttnThreads, 0);
-  hipError_t f = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, attn_fused_kernel<true>, kAttnThreads, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, attn_fused_kernel<false>, kAttnThreads, 0);
-  if (e != hipSuccess || f != hipSuccess || nb <= 0 || nf <= 0) return 1;
-  return std::min(nb, nf);
+  hipError_t f = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, attn_fused_kernel<true, false>, kAttnThreads, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, attn_fused_kernel<false, false>, kAttnThreads, 0);
+  int ns = 0;
+  hipError_t g = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&ns, attn_fused_kernel<true, true>, kAttnThreads, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&ns, attn_fused_kernel<false, true>, kAttnThreads, 0);
+  if (e != hipSuccess || f != hipSuccess || g != hipSuccess || nb <= 0 || nf <= 0 || ns <= 0) return 1;
+  return std::min(nb, std::min(nf, ns));
 }
 
 int attn_static_blocks_per_cu(bool fp8) {
@@ -970,11 +1073,15 @@ hipError_t launch_attn_static(const AttnArgs& a, bool fp8, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fused(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream) {
-  if (fp8)
-    hipLaunchKernelGGL(attn_fused_kernel<true>, dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+hipError_t launch_attn_fused(const AttnArgs& a, bool fp8, bool merge_in_kernel, int num_workers, hipStream_t stream) {
+  if (fp8 && merge_in_kernel)
+    hipLaunchKernelGGL((attn_fused_kernel<true, true>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+  else if (fp8)
+    hipLaunchKernelGGL((attn_fused_kernel<true, false>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+  else if (merge_in_kernel)
+    hipLaunchKernelGGL((attn_fused_kernel<false, true>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_fused_kernel<false>, dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fused_kernel<false, false>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -98,7 +98,7 @@ const char* hpa_last_error_message(void) { return g_last_error.c_str(); }
 hpa_status hpa_default_num_workers(int device, hpa_sched sched, int32_t* num_workers) {
   if (!num_workers) return fail(HPA_ERR_INVALID_ARG, "num_workers is NULL");
   if (sched != HPA_SCHED_BALANCED && sched != HPA_SCHED_STATIC_SPLITS && sched != HPA_SCHED_STATIC_CHUNK &&
-      sched != HPA_SCHED_BALANCED_FUSED)
+      sched != HPA_SCHED_BALANCED_FUSED && sched != HPA_SCHED_BALANCED_SINGLE)
     return fail(HPA_ERR_INVALID_ARG, "sched %d", static_cast<int>(sched));
   std::lock_guard<std::mutex> lock(g_dev_mu);
   if (device < 0) return fail(HPA_ERR_INVALID_ARG, "device %d", device);
@@ -195,9 +195,10 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   hpa_status st = check_desc(desc);
   if (st != HPA_OK) return st;
   if (sched != HPA_SCHED_BALANCED && sched != HPA_SCHED_STATIC_SPLITS && sched != HPA_SCHED_STATIC_CHUNK &&
-      sched != HPA_SCHED_BALANCED_FUSED)
+      sched != HPA_SCHED_BALANCED_FUSED && sched != HPA_SCHED_BALANCED_SINGLE)
     return fail(HPA_ERR_INVALID_ARG, "sched %d", static_cast<int>(sched));
-  if (sched == HPA_SCHED_BALANCED_FUSED && int64_t(desc->batch) * desc->num_kv_heads > hpa::kFusedMaxSeqs)
+  if ((sched == HPA_SCHED_BALANCED_FUSED || sched == HPA_SCHED_BALANCED_SINGLE) &&
+      int64_t(desc->batch) * desc->num_kv_heads > hpa::kFusedMaxSeqs)
     return fail(HPA_ERR_UNSUPPORTED, "fused schedule plans at most %d sequences (batch x kv heads)",
                 hpa::kFusedMaxSeqs);
 
@@ -217,7 +218,7 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   if (partial_ws_bytes < static_cast<size_t>(need))
     return fail(HPA_ERR_WORKSPACE, "partial workspace %zu bytes < %lld", partial_ws_bytes, (long long)need);
   const hpa::PlanOffsets po = hpa::plan_offsets(S, W);
-  if (sched == HPA_SCHED_BALANCED || sched == HPA_SCHED_BALANCED_FUSED) {
+  if (sched == HPA_SCHED_BALANCED || sched == HPA_SCHED_BALANCED_FUSED || sched == HPA_SCHED_BALANCED_SINGLE) {
     if (!plan_ws) return fail(HPA_ERR_INVALID_ARG, "balanced schedules need plan_ws");
     if (plan_ws_bytes < static_cast<size_t>(po.total * 4))
       return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)(po.total * 4));
@@ -234,6 +235,8 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   a.seq_lens = seq_lens;
   a.page_table = page_table;
   a.plan = static_cast<int32_t*>(plan_ws);
+  a.gctr = a.plan ? a.plan + po.gctr : nullptr;
+  a.sctr = a.plan ? a.plan + po.sctr : nullptr;
   char* pw = static_cast<char*>(partial_ws);
   a.part_acc = reinterpret_cast<float*>(pw + pl.acc);
   a.part_m = reinterpret_cast<float*>(pw + pl.m);
@@ -254,10 +257,16 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   const bool do_attn = !(flags & HPA_ATTN_MERGE_ONLY), do_merge = !(flags & HPA_ATTN_NO_MERGE);
   a.min_tiles = HPA_FUSED_MIN_TILES;
   a.item_cost = HPA_FUSED_ITEM_COST;
-  if (sched == HPA_SCHED_BALANCED || sched == HPA_SCHED_BALANCED_FUSED) {
+  if (sched == HPA_SCHED_BALANCED || sched == HPA_SCHED_BALANCED_FUSED || sched == HPA_SCHED_BALANCED_SINGLE) {
+    if (sched == HPA_SCHED_BALANCED_SINGLE) {
+      // one launch: the persistent kernel plans, attends and merges (flags have no effect)
+      if (hpa::launch_attn_fused(a, fp8, true, W, stream) != hipSuccess)
+        return fail(HPA_ERR_LAUNCH, "attention launch failed");
+      return HPA_OK;
+    }
     const bool fused = sched == HPA_SCHED_BALANCED_FUSED;
-    if (do_attn && (fused ? hpa::launch_attn_fused(a, fp8, W, stream) : hpa::launch_attn_balanced(a, fp8, W, stream)) !=
-                       hipSuccess)
+    if (do_attn && (fused ? hpa::launch_attn_fused(a, fp8, false, W, stream)
+                          : hpa::launch_attn_balanced(a, fp8, W, stream)) != hipSuccess)
       return fail(HPA_ERR_LAUNCH, "attention launch failed");
     if (do_merge && hpa::launch_merge(a, fused ? hpa::MERGE_FUSED : hpa::MERGE_PLAN, stream) != hipSuccess)
       return fail(HPA_ERR_LAUNCH, "merge launch failed");

@@ -56,7 +56,7 @@ enum : int {
 // Offsets of the plan arrays, in int32 elements.
 struct PlanOffsets {
   int64_t header, C, worker_off, item_s, item_t0, item_t1, item_split, item_slot,
-          num_splits, partial_base, merge_list, ne, total;
+          num_splits, partial_base, merge_list, ne, gctr, sctr, total;
   int32_t max_items;
 };
 
@@ -77,6 +77,11 @@ inline PlanOffsets plan_offsets(int64_t S, int64_t W) {
   o.partial_base = p; p += al(S);
   o.merge_list = p;   p += al(S);
   o.ne = p;           p += al(S + 1);
+  // arrival counters of the in-kernel merge (fused schedule): one per split group,
+  // indexed by the group's first partial slot, and one per sequence; each is
+  // returned to 0 by the workgroup that sees the last arrival
+  o.gctr = p;         p += al(mi);
+  o.sctr = p;         p += al(S);
   o.total = p;
   o.max_items = static_cast<int32_t>(mi);
   return o;
@@ -105,13 +110,15 @@ constexpr int kMergeGroup = 16;
 // Everything an attention kernel needs, passed by value.
 struct AttnArgs {
   const uint16_t* q;           // [B, Hq, 128] bf16
-  const uint8_t* k_cache;      // [P, Hkv, 64, 128] x elem
-  const uint8_t* v_cache;      // [P, Hkv, 128, 64] x elem
+  const uint8_t* k_cache;      // [P, Hkv, 8192] x elem, tiled page blocks
+  const uint8_t* v_cache;      // [P, Hkv, 8192] x elem, tiled page blocks
   const float* k_scale;
   const float* v_scale;
   const int32_t* seq_lens;
   const int32_t* page_table;
   int32_t* plan;               // plan workspace (may be null for static schedules)
+  int32_t* gctr;               // in-kernel merge arrival counters (fused schedule), in plan
+  int32_t* sctr;
   float* part_acc;
   float* part_m;
   float* part_l;
@@ -200,7 +207,7 @@ hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_page
                        int min_tiles, int item_cost, int32_t* plan, const PlanOffsets& po, hipStream_t stream);
 hipError_t launch_attn_balanced(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream);
 hipError_t launch_attn_static(const AttnArgs& a, bool fp8, hipStream_t stream);
-hipError_t launch_attn_fused(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream);
+hipError_t launch_attn_fused(const AttnArgs& a, bool fp8, bool merge_in_kernel, int num_workers, hipStream_t stream);
 // merge modes: which schedule produced the partials
 enum MergeMode : int { MERGE_PLAN = 0, MERGE_STATIC = 1, MERGE_FUSED = 2 };
 hipError_t launch_merge(const AttnArgs& a, MergeMode mode, hipStream_t stream);

@@ -134,13 +134,16 @@ def test_edge_lengths_all_schedules(kv_dtype, heads):
     outs = {}
     for sched, W in [("balanced", 0), ("balanced", 1), ("balanced", 3), ("balanced", 37),
                      ("fused", 0), ("fused", 1), ("fused", 3), ("fused", 37),
+                     ("single", 0), ("single", 1), ("single", 3), ("single", 37),
                      ("static_splits", 0), ("static_splits", 5), ("static_chunk", 0), ("static_chunk", 9)]:
         got, r, _ = run_and_compare(w, sched, W, ref=ref, what=f"{kv_dtype} {hq}:{hkv}")
         assert np.all(got[0] == 0)                      # empty request -> zero row
         outs[(sched, W)] = got
-    # the fused schedule computes the planner's work list in-kernel: identical bits
+    # the fused schedules compute the planner's work list in-kernel (and the single-launch
+    # one merges in-kernel, in the merge kernel's order): identical bits
     for W in (0, 1, 3, 37):
         assert np.array_equal(outs[("balanced", W)], outs[("fused", W)])
+        assert np.array_equal(outs[("balanced", W)], outs[("single", W)])
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
@@ -169,11 +172,12 @@ def test_full_size_bf16_workloads(cfg):
     w = inputs.config_workload(cfg)
     ref = oracle_out(w)
     outs = {}
-    for sched in ("balanced", "fused", "static_splits", "static_chunk"):
+    for sched in ("balanced", "fused", "single", "static_splits", "static_chunk"):
         got, r, _ = run_and_compare(w, sched, ref=ref, what=f"cfg{cfg}")
         print(f"cfg{cfg} {sched}: {r}", flush=True)
         outs[sched] = got
     assert np.array_equal(outs["balanced"], outs["fused"])
+    assert np.array_equal(outs["balanced"], outs["single"])
     # one worker (no split at all) agrees with the default within tolerance
     if cfg != 3:
         run_and_compare(w, "balanced", W=1, ref=ref, what=f"cfg{cfg} single worker")
@@ -211,7 +215,7 @@ def test_fp8_prologue_workload():
     r = assert_within(got, ref, "fp8", "cfg4")
     print(f"cfg4 attention: {r}", flush=True)
     # the other schedules on the same (already appended) cache
-    for sched in ("fused", "static_splits", "static_chunk"):
+    for sched in ("fused", "single", "static_splits", "static_chunk"):
         d.attend(sched)
         torch.cuda.synchronize()
         assert_within(d.output_f64(), ref, "fp8", f"cfg4 {sched}")
@@ -292,7 +296,33 @@ def test_fused_schedule_both_planners(hkv):
         W = int(rng.integers(20, 300))
         g_bal, _, _ = run_and_compare(w, "balanced", W, ref=ref, what=f"S={B * hkv}")
         g_fus, _, _ = run_and_compare(w, "fused", W, ref=ref, what=f"S={B * hkv}")
-        assert np.array_equal(g_bal, g_fus)
+        g_one, _, _ = run_and_compare(w, "single", W, ref=ref, what=f"S={B * hkv}")
+        assert np.array_equal(g_bal, g_fus) and np.array_equal(g_bal, g_one)
+
+
+def test_single_launch_merge_counters_reset_across_steps():
+    """The in-kernel merge's arrival counters return to zero: repeated steps (and a
+    different batch on the same workspace) keep giving the planned schedule's bits."""
+    from load_balanced_split_amd.runner import DeviceStep
+    w = inputs.build_workload("repeat", [5000, 64, 3000, 1, 700], 8, 1, "bf16", seed=12)
+    d = DeviceStep(w, num_workers=23)
+    d.step("balanced")
+    torch.cuda.synchronize()
+    want = d.out.clone()
+    for rep in range(4):
+        d.out.zero_()
+        d.step("single")
+        torch.cuda.synchronize()
+        assert torch.equal(d.out, want), rep
+    # shorter lengths on the same buffers: other split structure, same workspace
+    d.seq_lens.copy_(torch.tensor([4000, 0, 2900, 1, 1], dtype=torch.int32))
+    d.step("balanced")
+    torch.cuda.synchronize()
+    want2 = d.out.clone()
+    d.step("single")
+    torch.cuda.synchronize()
+    assert torch.equal(d.out, want2)
+    assert d.device_error() == 0
 
 
 def test_fused_reports_bad_lengths_and_large_batches_are_refused():
