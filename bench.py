@@ -80,7 +80,7 @@ def pmc_main(args):
         _ = buf.sum()
     torch.cuda.synchronize()
     del buf
-    for sched in ("balanced", "fused"):
+    for sched in ("balanced", "fused", "single"):
         for rep in range(2):
             for d in copies:
                 d.step(sched)
@@ -401,8 +401,8 @@ def traffic_per_launch(sched, kv_dtype, workload):
     rocprofv3 counter summary of this workload; None when there is none or it was
     taken on other kernel sources."""
     from load_balanced_split_amd.profiling import read_traffic
-    key = ("attn_fused_kernel" if sched == "fused" else "attn_balanced_kernel") + \
-          ("<false>" if kv_dtype == "bf16" else "<true>")
+    fp8 = "false" if kv_dtype == "bf16" else "true"
+    key = f"attn_fused_kernel<{fp8},false>" if sched == "fused" else f"attn_balanced_kernel<{fp8}>"
     path = os.path.join(ROOT, "profiles", f"attn_hbm_traffic_{WORKLOAD_KEYS[workload]}.txt")
     t = read_traffic(path, key)
     return None if t is None else int(round(t))

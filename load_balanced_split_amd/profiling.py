@@ -18,6 +18,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sqlite3
 import sys
 
@@ -33,11 +34,11 @@ def source_hash() -> str:
 
 
 def short_name(name: str) -> str:
-    for key in ("attn_balanced_kernel<false>", "attn_balanced_kernel<true>", "attn_fused_kernel<false>",
-                "attn_fused_kernel<true>", "attn_static_kernel<false>", "attn_static_kernel<true>",
-                "merge_kernel", "plan_kernel", "prologue_kernel"):
-        if key in name:
-            return key
+    """Library kernels as name<template args> without spaces (attn_fused_kernel<false,true>
+    is the E4M3-less fused kernel with the in-kernel merge); calibration kernels tagged."""
+    m = re.search(r"(attn_\w+_kernel|merge_kernel|plan_kernel|prologue_kernel)(<[^>]*>)?", name)
+    if m:
+        return m.group(1) + (m.group(2) or "").replace(" ", "")
     if "reduce_kernel" in name:
         return "calib_read:reduce_kernel"
     if "FillFunctor" in name:
