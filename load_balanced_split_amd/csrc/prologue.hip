@@ -10,7 +10,7 @@
 // RMSNorm (Zhang & Sennrich 2019): y = x / sqrt(mean(x^2) + eps) * w, fp32.
 // RoPE (Su et al. 2021, rotate-half form): angle_i = pos * theta^(-i/64) is
 // formed and reduced modulo 2*pi in fp64 (positions reach 131072, where an fp32
-// angle would be off by ~0.016 rad), then rotated in fp32.
+// angle would be off by ~0.016 rad); sine, cosine and the rotation are fp32.
 #include "hpa_internal.hpp"
 
 #include <cmath>
@@ -56,6 +56,10 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
+// Rows of one request a wave handles per pass (loads of a pass are issued before
+// any of its arithmetic, so a pass costs one memory round trip).
+constexpr int kProRowsPerPass = 4;
+
 __global__ __launch_bounds__(kProThreads) void prologue_kernel(
     const uint16_t* __restrict__ q_in, const uint16_t* __restrict__ k_in,
     const uint16_t* __restrict__ v_in, const float* __restrict__ q_norm_w,
@@ -66,7 +70,29 @@ __global__ __launch_bounds__(kProThreads) void prologue_kernel(
     int32_t* err_word, int hq, int hkv, int max_pages, int num_pages, int fp8) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kProWaves = kProThreads / 64;
+  const int rows = hq + 2 * hkv;
+  // rows base + wave + kProWaves * i of a pass, zero past the last row
+  auto load_pass = [&](int base, float (&x0)[kProRowsPerPass], float (&x1)[kProRowsPerPass]) {
+#pragma unroll
+    for (int i = 0; i < kProRowsPerPass; ++i) {
+      const int r = base + wave + kProWaves * i;
+      x0[i] = x1[i] = 0.f;
+      if (r < rows) {
+        const uint16_t* src = r < hq ? q_in + (int64_t(b) * hq + r) * kHeadDim
+                            : r < hq + hkv ? k_in + (int64_t(b) * hkv + (r - hq)) * kHeadDim
+                                           : v_in + (int64_t(b) * hkv + (r - hq - hkv)) * kHeadDim;
+        x0[i] = bf16_to_f32(src[lane]);
+        x1[i] = bf16_to_f32(src[lane + 64]);
+      }
+    }
+  };
+  // everything that does not depend on the position goes out first
   const int pos = positions[b];
+  const float wq0 = q_norm_w[lane], wq1 = q_norm_w[lane + 64];
+  const float wk0 = k_norm_w[lane], wk1 = k_norm_w[lane + 64];
+  float x0[kProRowsPerPass], x1[kProRowsPerPass];
+  load_pass(0, x0, x1);
   int pid = -1;
   if (pos >= 0 && pos < max_pages * kPage) pid = page_table[int64_t(b) * max_pages + pos / kPage];
   if (pid < 0 || pid >= num_pages) {
@@ -76,55 +102,57 @@ __global__ __launch_bounds__(kProThreads) void prologue_kernel(
   if (threadIdx.x == 0) seq_lens_out[b] = pos + 1;
   const int slot = pos % kPage;
 
-  // rotation of pair (lane, lane + 64)
+  // rotation of pair (lane, lane + 64): the angle is formed and reduced mod 2 pi in
+  // fp64; its sine and cosine are then taken in fp32 on the reduced angle
   const double two_pi = 6.283185307179586476925286766559;
   const double ang = static_cast<double>(pos) * pow(rope_theta, -static_cast<double>(lane) / 64.0);
-  const double red = ang - two_pi * rint(ang / two_pi);
-  const float cs = static_cast<float>(cos(red)), sn = static_cast<float>(sin(red));
+  const float red = static_cast<float>(ang - two_pi * rint(ang / two_pi));
+  float sn, cs;
+  sincosf(red, &sn, &cs);
 
-  const int rows = hq + 2 * hkv;
-  for (int r = wave; r < rows; r += kProThreads / 64) {
-    if (r < hq + hkv) {
-      const bool is_q = r < hq;
-      const uint16_t* src = is_q ? q_in + (int64_t(b) * hq + r) * kHeadDim
-                                 : k_in + (int64_t(b) * hkv + (r - hq)) * kHeadDim;
-      const float* w = is_q ? q_norm_w : k_norm_w;
-      const float x0 = bf16_to_f32(src[lane]), x1 = bf16_to_f32(src[lane + 64]);
-      const float ms = wave_sum(x0 * x0 + x1 * x1) * (1.0f / kHeadDim);
-      const float inv = 1.0f / sqrtf(ms + eps);
-      const float y0 = x0 * inv * w[lane], y1 = x1 * inv * w[lane + 64];
-      const float o0 = y0 * cs - y1 * sn, o1 = y1 * cs + y0 * sn;
-      if (is_q) {
-        uint16_t* dst = q_out + (int64_t(b) * hq + r) * kHeadDim;
-        dst[lane] = f32_to_bf16(o0);
-        dst[lane + 64] = f32_to_bf16(o1);
-      } else {
-        const int g = r - hq;
-        const int64_t blk = (int64_t(pid) * hkv + g) * kBlockElems;
-        const int64_t i0 = blk + k_block_index(slot, lane, fp8), i1 = blk + k_block_index(slot, lane + 64, fp8);
-        if (fp8) {
-          const float sc = k_scale[g];
-          k_cache[i0] = f32_to_e4m3(o0 / sc);
-          k_cache[i1] = f32_to_e4m3(o1 / sc);
+  for (int base = 0; base < rows; base += kProWaves * kProRowsPerPass) {
+    if (base > 0) load_pass(base, x0, x1);
+#pragma unroll
+    for (int i = 0; i < kProRowsPerPass; ++i) {
+      const int r = base + wave + kProWaves * i;
+      if (r >= rows) break;                   // uniform per wave
+      if (r < hq + hkv) {
+        const bool is_q = r < hq;
+        const float ms = wave_sum(x0[i] * x0[i] + x1[i] * x1[i]) * (1.0f / kHeadDim);
+        const float inv = 1.0f / sqrtf(ms + eps);
+        const float y0 = x0[i] * inv * (is_q ? wq0 : wk0), y1 = x1[i] * inv * (is_q ? wq1 : wk1);
+        const float o0 = y0 * cs - y1 * sn, o1 = y1 * cs + y0 * sn;
+        if (is_q) {
+          uint16_t* dst = q_out + (int64_t(b) * hq + r) * kHeadDim;
+          dst[lane] = f32_to_bf16(o0);
+          dst[lane + 64] = f32_to_bf16(o1);
         } else {
-          uint16_t* kc = reinterpret_cast<uint16_t*>(k_cache);
-          kc[i0] = f32_to_bf16(o0);
-          kc[i1] = f32_to_bf16(o1);
+          const int g = r - hq;
+          const int64_t blk = (int64_t(pid) * hkv + g) * kBlockElems;
+          const int64_t i0 = blk + k_block_index(slot, lane, fp8), i1 = blk + k_block_index(slot, lane + 64, fp8);
+          if (fp8) {
+            const float sc = k_scale[g];
+            k_cache[i0] = f32_to_e4m3(o0 / sc);
+            k_cache[i1] = f32_to_e4m3(o1 / sc);
+          } else {
+            uint16_t* kc = reinterpret_cast<uint16_t*>(k_cache);
+            kc[i0] = f32_to_bf16(o0);
+            kc[i1] = f32_to_bf16(o1);
+          }
         }
-      }
-    } else {
-      const int g = r - hq - hkv;
-      const uint16_t* src = v_in + (int64_t(b) * hkv + g) * kHeadDim;
-      const int64_t blk = (int64_t(pid) * hkv + g) * kBlockElems;
-      const int64_t i0 = blk + v_block_index(slot, lane, fp8), i1 = blk + v_block_index(slot, lane + 64, fp8);
-      if (fp8) {
-        const float sc = v_scale[g];
-        v_cache[i0] = f32_to_e4m3(bf16_to_f32(src[lane]) / sc);
-        v_cache[i1] = f32_to_e4m3(bf16_to_f32(src[lane + 64]) / sc);
       } else {
-        uint16_t* vc = reinterpret_cast<uint16_t*>(v_cache);
-        vc[i0] = src[lane];
-        vc[i1] = src[lane + 64];
+        const int g = r - hq - hkv;
+        const int64_t blk = (int64_t(pid) * hkv + g) * kBlockElems;
+        const int64_t i0 = blk + v_block_index(slot, lane, fp8), i1 = blk + v_block_index(slot, lane + 64, fp8);
+        if (fp8) {
+          const float sc = v_scale[g];
+          v_cache[i0] = f32_to_e4m3(x0[i] / sc);
+          v_cache[i1] = f32_to_e4m3(x1[i] / sc);
+        } else {
+          uint16_t* vc = reinterpret_cast<uint16_t*>(v_cache);
+          vc[i0] = f32_to_bf16(x0[i]);
+          vc[i1] = f32_to_bf16(x1[i]);
+        }
       }
     }
   }
