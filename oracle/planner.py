@@ -38,6 +38,17 @@ tiles [C'[s] + c, C'[s] + c + n_s) it owns. c = 0 is the plain partition above.
 A worker whose range covers only virtual positions of a sequence gets no item
 for it, and may get no item at all.
 
+Dynamic tail (bitbyai.com, same section: the scheduler evaluates progress
+dynamically). The persistent workers do not all run at the same speed, so the
+last part of the work is not given to anyone in advance: with tail_den d > 0,
+the last T = N' // d positions are cut into D = ceil(T / tail_chunk) chunks that
+workers claim at run time, each the moment it has finished what it holds. The
+first A = N' - T positions are split evenly over the W' workers as above
+(W' still from N'). Virtual worker v < W' owns [v*A // W', (v+1)*A // W'),
+virtual worker W' + c owns [A + c*T // D, A + (c+1)*T // D); items, split ranks
+and slots follow the virtual workers in order, so the result does not depend on
+which worker claims which chunk. tail_den 0 is the plan without a tail.
+
 Static split-KV (the comparison the pages describe in the same section):
 flavour "splits" fixes the number of splits per sequence,
 S_split = clamp(ceil(W / S), 1, max_pages), chunk_s = ceil(n_s / S_split);
@@ -64,7 +75,7 @@ def active_workers(N, num_workers, min_tiles):
     return min(num_workers, max(1, N // min_tiles))
 
 
-def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1, item_cost=0):
+def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1, item_cost=0, tail_den=0, tail_chunk=1):
     n = tile_counts(seq_lens, hkv)
     S = len(n)
     C = [0] * (S + 1)
@@ -77,13 +88,18 @@ def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1, item_cost=0):
         start[s + 1] = start[s] + (n[s] + item_cost if n[s] > 0 else 0)
     Np = start[S]
     Wp = 0 if N == 0 else min(num_workers, max(1, Np // min_tiles))
+    T = Np // tail_den if (tail_den > 0 and N > 0) else 0     # positions of the dynamic tail
+    A = Np - T
+    D = -(-T // tail_chunk) if T > 0 else 0
+    bounds = [w * A // Wp for w in range(Wp)] + [A + c * T // D for c in range(D)] + [Np]
+    V = Wp + D                                   # virtual workers: W' static, then D chunks
 
-    items = []                                   # (worker, s, t0, t1)
+    items = []                                   # (virtual worker, s, t0, t1)
     worker_off = [0]
     first = 0                                    # first sequence not wholly before the worker
-    for w in range(Wp):
-        a = w * Np // Wp
-        e = (w + 1) * Np // Wp
+    for w in range(V):
+        a = bounds[w]
+        e = bounds[w + 1]
         while first < S and start[first + 1] <= a:
             first += 1
         s = first
@@ -110,7 +126,7 @@ def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1, item_cost=0):
     slots = [partial_base[s] + k if num_splits[s] > 1 else -1
              for (_, s, _, _), k in zip(items, split)]
     return dict(
-        C=C, N=N, Np=Np, S=S, Wp=Wp, n_items=len(items), worker_off=worker_off,
+        C=C, N=N, Np=Np, S=S, Wp=Wp, D=D, V=V, n_items=len(items), worker_off=worker_off,
         item_s=[it[1] for it in items], item_t0=[it[2] for it in items],
         item_t1=[it[3] for it in items], item_split=split, item_slot=slots,
         num_splits=num_splits, partial_base=partial_base, n_partials=acc,

@@ -102,6 +102,101 @@ def test_item_cost_properties(seed):
             assert all(p[k] == q[k] for k in q)
 
 
+def test_hand_worked_dynamic_tail_plans():
+    g = json.load(open(os.path.join(GOLDEN, "plan_dynamic_tail.json")))
+    for case in g["cases"]:
+        p = op.balanced_plan(case["seq_lens"], case["hkv"], case["num_workers"], case["min_tiles"],
+                             case["item_cost"], case["tail_den"], case["tail_chunk"])
+        for key in ("Np", "Wp", "D", "V", "worker_off", "item_s", "item_t0", "item_t1", "item_split",
+                    "item_slot", "num_splits", "partial_base", "n_partials", "merge_list"):
+            assert p[key] == case[key], key
+
+
+def brute_force_tail_plan(seq_lens, hkv, W, min_tiles, cost, tail_den, tail_chunk):
+    """Position by position: lay out the list, give each position to the last virtual
+    worker (W' static ranges, then D tail chunks) whose boundary is at or before it,
+    found by scanning the boundaries, then group real tiles by (virtual worker, sequence)."""
+    seqs = [-(-int(L) // 64) for L in seq_lens for _ in range(hkv)]
+    layout = []
+    for s, n in enumerate(seqs):
+        if n:
+            layout += [None] * cost + [(s, t) for t in range(n)]
+    Np = len(layout)
+    if sum(seqs) == 0:
+        return []
+    Wp = min(W, max(1, Np // min_tiles))
+    T = Np // tail_den if tail_den else 0
+    D = -(-T // tail_chunk) if T else 0
+    A = Np - T
+    bounds = []
+    for w in range(Wp):
+        bounds.append((w * A) // Wp)
+    for c in range(D):
+        bounds.append(A + (c * T) // D)
+    groups = {}
+    for k, e in enumerate(layout):
+        v = max(i for i in range(len(bounds)) if bounds[i] <= k)
+        if e is not None:
+            groups.setdefault((v, e[0]), []).append(e[1])
+    return [(v, s, ts[0], ts[-1] + 1) for (v, s), ts in sorted(groups.items())]
+
+
+def test_dynamic_tail_against_brute_force_random():
+    rng = np.random.default_rng(2)
+    for trial in range(300):
+        B = int(rng.integers(1, 9))
+        hkv = int(rng.integers(1, 4))
+        lens = rng.choice([0, 1, 63, 64, 65, 127, 128, 129, 500, 1000, 3000], size=B)
+        W = int(rng.integers(1, 30))
+        mt = int(rng.integers(1, 4))
+        c = int(rng.integers(0, 4))
+        den = int(rng.integers(2, 9))
+        ch = int(rng.integers(1, 5))
+        p = op.balanced_plan(lens, hkv, W, mt, c, den, ch)
+        items = []
+        for v in range(p["V"]):
+            for i in range(p["worker_off"][v], p["worker_off"][v + 1]):
+                items.append((v, p["item_s"][i], p["item_t0"][i], p["item_t1"][i]))
+        assert items == brute_force_tail_plan(lens, hkv, W, mt, c, den, ch)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_dynamic_tail_properties(seed):
+    """Every tile once; static ranges share A evenly, chunks share T evenly and hold at
+    most tail_chunk positions; slots of a sequence consecutive in virtual-worker order."""
+    rng = np.random.default_rng(200 + seed)
+    for trial in range(200):
+        B = int(rng.integers(1, 30))
+        hkv = int(rng.integers(1, 5))
+        lens = rng.integers(0, 6000, size=B)
+        W = int(rng.integers(1, 400))
+        c = int(rng.integers(0, 6))
+        den = int(rng.integers(2, 17))
+        ch = int(rng.integers(1, 9))
+        p = op.balanced_plan(lens, hkv, W, 1, c, den, ch)
+        n = op.tile_counts(lens, hkv)
+        if p["N"] == 0:
+            assert p["V"] == 0 and p["n_items"] == 0
+            continue
+        Np, Wp, D = p["Np"], p["Wp"], p["D"]
+        T = Np // den
+        assert D == -(-T // ch) and p["V"] == Wp + D
+        cover = [np.zeros(x, int) for x in n]
+        for s, t0, t1 in zip(p["item_s"], p["item_t0"], p["item_t1"]):
+            cover[s][t0:t1] += 1
+        assert all((x == 1).all() for x in cover)
+        if D:
+            sizes = [(i + 1) * T // D - i * T // D for i in range(D)]
+            assert max(sizes) <= ch and max(sizes) - min(sizes) <= 1
+        per_seq = {}
+        for i, s in enumerate(p["item_s"]):
+            per_seq.setdefault(s, []).append(i)
+        for s, idx in per_seq.items():
+            assert [p["item_split"][i] for i in idx] == list(range(len(idx)))
+            if len(idx) > 1:
+                assert [p["item_slot"][i] for i in idx] == list(range(p["partial_base"][s], p["partial_base"][s] + len(idx)))
+
+
 def brute_force_plan(seq_lens, hkv, W, min_tiles):
     """Enumerate global tiles one by one: owner worker by scanning the worker
     boundaries, owner sequence by scanning the sequence boundaries, then group."""
