@@ -41,8 +41,9 @@ for it, and may get no item at all.
 Dynamic tail (bitbyai.com, same section: the scheduler evaluates progress
 dynamically). The persistent workers do not all run at the same speed, so the
 last part of the work is not given to anyone in advance: with tail_den d > 0,
-the last T = N' // d positions are cut into D = ceil(T / tail_chunk) chunks that
-workers claim at run time, each the moment it has finished what it holds. The
+the last T = N' // d positions are cut into D = min(ceil(T / tail_chunk), 4 W) chunks
+(at most four per worker, so the work list has a size bound) that workers claim
+at run time, each the moment it has finished what it holds. The
 first A = N' - T positions are split evenly over the W' workers as above
 (W' still from N'). Virtual worker v < W' owns [v*A // W', (v+1)*A // W'),
 virtual worker W' + c owns [A + c*T // D, A + (c+1)*T // D); items, split ranks
@@ -90,7 +91,7 @@ def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1, item_cost=0, tail_den
     Wp = 0 if N == 0 else min(num_workers, max(1, Np // min_tiles))
     T = Np // tail_den if (tail_den > 0 and N > 0) else 0     # positions of the dynamic tail
     A = Np - T
-    D = -(-T // tail_chunk) if T > 0 else 0
+    D = min(-(-T // tail_chunk), 4 * num_workers) if T > 0 else 0
     bounds = [w * A // Wp for w in range(Wp)] + [A + c * T // D for c in range(D)] + [Np]
     V = Wp + D                                   # virtual workers: W' static, then D chunks
 

@@ -126,7 +126,7 @@ def brute_force_tail_plan(seq_lens, hkv, W, min_tiles, cost, tail_den, tail_chun
         return []
     Wp = min(W, max(1, Np // min_tiles))
     T = Np // tail_den if tail_den else 0
-    D = -(-T // tail_chunk) if T else 0
+    D = min(-(-T // tail_chunk), 4 * W) if T else 0
     A = Np - T
     bounds = []
     for w in range(Wp):
@@ -180,14 +180,15 @@ def test_dynamic_tail_properties(seed):
             continue
         Np, Wp, D = p["Np"], p["Wp"], p["D"]
         T = Np // den
-        assert D == -(-T // ch) and p["V"] == Wp + D
+        assert D == min(-(-T // ch), 4 * W) and p["V"] == Wp + D
         cover = [np.zeros(x, int) for x in n]
         for s, t0, t1 in zip(p["item_s"], p["item_t0"], p["item_t1"]):
             cover[s][t0:t1] += 1
         assert all((x == 1).all() for x in cover)
         if D:
             sizes = [(i + 1) * T // D - i * T // D for i in range(D)]
-            assert max(sizes) <= ch and max(sizes) - min(sizes) <= 1
+            assert max(sizes) - min(sizes) <= 1
+            assert max(sizes) <= ch or D == 4 * W
         per_seq = {}
         for i, s in enumerate(p["item_s"]):
             per_seq.setdefault(s, []).append(i)
