@@ -44,11 +44,13 @@ last part of the work is not given to anyone in advance: with tail_den d > 0,
 the last T = N' // d positions are cut into D = min(ceil(T / tail_chunk), 4 W) chunks
 (at most four per worker, so the work list has a size bound) that workers claim
 at run time, each the moment it has finished what it holds. The
-first A = N' - T positions are split evenly over the W' workers as above
-(W' still from N'). Virtual worker v < W' owns [v*A // W', (v+1)*A // W'),
-virtual worker W' + c owns [A + c*T // D, A + (c+1)*T // D); items, split ranks
-and slots follow the virtual workers in order, so the result does not depend on
-which worker claims which chunk. tail_den 0 is the plan without a tail.
+first A = N' - T positions are split evenly over W_s = min(W', A) workers
+(W' still from N'; a worker left without a static position goes straight to
+the chunks, so every virtual worker owns at least one position). Virtual
+worker v < W_s owns [v*A // W_s, (v+1)*A // W_s), virtual worker W_s + c owns
+[A + c*T // D, A + (c+1)*T // D); items, split ranks and slots follow the
+virtual workers in order, so the result does not depend on which worker claims
+which chunk. tail_den 0 is the plan without a tail (then W_s = W').
 
 Static split-KV (the comparison the pages describe in the same section):
 flavour "splits" fixes the number of splits per sequence,
@@ -92,8 +94,9 @@ def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1, item_cost=0, tail_den
     T = Np // tail_den if (tail_den > 0 and N > 0) else 0     # positions of the dynamic tail
     A = Np - T
     D = min(-(-T // tail_chunk), 4 * num_workers) if T > 0 else 0
-    bounds = [w * A // Wp for w in range(Wp)] + [A + c * T // D for c in range(D)] + [Np]
-    V = Wp + D                                   # virtual workers: W' static, then D chunks
+    Ws = min(Wp, A)                              # workers with a static range
+    bounds = [w * A // Ws for w in range(Ws)] + [A + c * T // D for c in range(D)] + [Np]
+    V = Ws + D                                   # virtual workers: W_s static, then D chunks
 
     items = []                                   # (virtual worker, s, t0, t1)
     worker_off = [0]
@@ -127,7 +130,7 @@ def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1, item_cost=0, tail_den
     slots = [partial_base[s] + k if num_splits[s] > 1 else -1
              for (_, s, _, _), k in zip(items, split)]
     return dict(
-        C=C, N=N, Np=Np, S=S, Wp=Wp, D=D, V=V, n_items=len(items), worker_off=worker_off,
+        C=C, N=N, Np=Np, S=S, Wp=Wp, Ws=Ws, D=D, V=V, n_items=len(items), worker_off=worker_off,
         item_s=[it[1] for it in items], item_t0=[it[2] for it in items],
         item_t1=[it[3] for it in items], item_split=split, item_slot=slots,
         num_splits=num_splits, partial_base=partial_base, n_partials=acc,

@@ -107,14 +107,14 @@ def test_hand_worked_dynamic_tail_plans():
     for case in g["cases"]:
         p = op.balanced_plan(case["seq_lens"], case["hkv"], case["num_workers"], case["min_tiles"],
                              case["item_cost"], case["tail_den"], case["tail_chunk"])
-        for key in ("Np", "Wp", "D", "V", "worker_off", "item_s", "item_t0", "item_t1", "item_split",
+        for key in ("Np", "Wp", "Ws", "D", "V", "worker_off", "item_s", "item_t0", "item_t1", "item_split",
                     "item_slot", "num_splits", "partial_base", "n_partials", "merge_list"):
             assert p[key] == case[key], key
 
 
 def brute_force_tail_plan(seq_lens, hkv, W, min_tiles, cost, tail_den, tail_chunk):
     """Position by position: lay out the list, give each position to the last virtual
-    worker (W' static ranges, then D tail chunks) whose boundary is at or before it,
+    worker (W_s static ranges, then D tail chunks) whose boundary is at or before it,
     found by scanning the boundaries, then group real tiles by (virtual worker, sequence)."""
     seqs = [-(-int(L) // 64) for L in seq_lens for _ in range(hkv)]
     layout = []
@@ -128,9 +128,10 @@ def brute_force_tail_plan(seq_lens, hkv, W, min_tiles, cost, tail_den, tail_chun
     T = Np // tail_den if tail_den else 0
     D = min(-(-T // tail_chunk), 4 * W) if T else 0
     A = Np - T
+    Ws = min(Wp, A)
     bounds = []
-    for w in range(Wp):
-        bounds.append((w * A) // Wp)
+    for w in range(Ws):
+        bounds.append((w * A) // Ws)
     for c in range(D):
         bounds.append(A + (c * T) // D)
     groups = {}
@@ -180,7 +181,11 @@ def test_dynamic_tail_properties(seed):
             continue
         Np, Wp, D = p["Np"], p["Wp"], p["D"]
         T = Np // den
-        assert D == min(-(-T // ch), 4 * W) and p["V"] == Wp + D
+        Ws = p["Ws"]
+        assert D == min(-(-T // ch), 4 * W) and Ws == min(Wp, Np - T) and p["V"] == Ws + D
+        # every virtual worker owns at least one position
+        bounds = [v * (Np - T) // Ws for v in range(Ws)] + [Np - T + i * T // D for i in range(D)] + [Np]
+        assert all(bounds[v] < bounds[v + 1] for v in range(p["V"]))
         cover = [np.zeros(x, int) for x in n]
         for s, t0, t1 in zip(p["item_s"], p["item_t0"], p["item_t1"]):
             cover[s][t0:t1] += 1
