@@ -201,8 +201,8 @@ def trace_main(args):
             e1.record()
             torch.cuda.synchronize()
             ipw, tiles = None, None
-            if sched == "balanced":
-                pa = d.plan_arrays()
+            pa = d.plan_arrays() if sched == "balanced" else None
+            if pa is not None and pa["D"] == 0:       # with a dynamic tail, items meet workers at run time
                 off = np.array(pa["worker_off"])
                 ipw = np.diff(off)
                 sz = np.array(pa["item_t1"]) - np.array(pa["item_t0"])

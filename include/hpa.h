@@ -83,7 +83,8 @@ enum {
   HPA_DEVERR_SEQ_LEN = 1,      /* seq_len < 0 or > max_pages_per_seq * 64 */
   HPA_DEVERR_PAGE_ID = 2,      /* page id outside [0, num_pages) */
   HPA_DEVERR_PROLOGUE = 4,     /* append position outside the page table */
-  HPA_DEVERR_PLAN = 8          /* attention launched with a different worker count than planned */
+  HPA_DEVERR_PLAN = 8          /* attention launched with a different worker count than planned,
+                                  or a plan workspace that is not a plan */
 };
 
 typedef struct {
@@ -101,11 +102,13 @@ typedef struct {
 /* Byte offsets of the arrays inside a plan workspace (for inspection and tests).
  * All arrays are int32. header[0..15]: 0 W' (active workers), 1 N (tiles),
  * 2 S (sequences), 3 n_items, 4 n_merge, 5 n_partials, 6 sticky error word,
- * 7 W (workers the plan was made for). */
+ * 7 W (workers the plan was made for), 8 D (tail chunks), 9 Ws (workers with a
+ * static range). worker_off has Ws + D + 1 entries: the items of static worker
+ * v < Ws, then those of tail chunk c (virtual worker Ws + c). */
 typedef struct {
   size_t header, C, worker_off, item_s, item_t0, item_t1, item_split, item_slot,
          num_splits, partial_base, merge_list, total_bytes;
-  int32_t max_items;           /* W + S */
+  int32_t max_items;           /* 5 W + S: at most 4 W tail chunks */
 } hpa_plan_layout;
 
 /* Default worker count of a schedule on a device: compute units x workgroups of
@@ -121,7 +124,7 @@ hpa_status hpa_plan_workspace_size(const hpa_attn_desc* desc, int32_t num_worker
 hpa_status hpa_plan_workspace_layout(const hpa_attn_desc* desc, int32_t num_workers,
                                      hpa_plan_layout* layout);
 
-/* Size of the partial-result workspace: (W + S) slots of Hq/Hkv x 128 fp32
+/* Size of the partial-result workspace: (5 W + S) slots of Hq/Hkv x 128 fp32
  * accumulators plus a max and a sum per head. Enough for every schedule. */
 hpa_status hpa_partial_workspace_size(const hpa_attn_desc* desc, int32_t num_workers, size_t* bytes);
 
@@ -137,17 +140,28 @@ hpa_status hpa_partial_workspace_size(const hpa_attn_desc* desc, int32_t num_wor
  * tiles among them, cut at sequence boundaries (a worker may get none); then
  * split ranks, partial slots and the list of sequences to merge. item_cost 0 is
  * the plain even split of the tiles. 0 <= item_cost <= 64.
+ * Dynamic tail (same section: the scheduler evaluates progress as it runs;
+ * tail_den > 0): the last T = N' / tail_den positions are not assigned ahead of
+ * time but cut into D = min(ceil(T / tail_chunk), 4 W) chunks that the persistent
+ * workers claim on a device counter whenever they run out of work; the first
+ * A = N' - T positions are split as above over Ws = min(W', A) workers. Items,
+ * split ranks and slots follow the virtual workers (Ws static ranges, then the
+ * chunks) in order, so results do not depend on who claims which chunk.
+ * tail_den = 0: no tail (Ws = W', D = 0). tail_den >= 0, tail_chunk >= 1.
+ * The planner also returns the claim counters to zero.
  * seq_lens stays on the device (no host synchronisation). The plan workspace
  * must be zero-filled before its first use (it holds the sticky error word,
  * which hpa_plan never clears). */
 hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t num_workers,
-                    int32_t min_tiles_per_worker, int32_t item_cost, void* plan_ws,
-                    size_t plan_ws_bytes, hipStream_t stream);
+                    int32_t min_tiles_per_worker, int32_t item_cost, int32_t tail_den,
+                    int32_t tail_chunk, void* plan_ws, size_t plan_ws_bytes, hipStream_t stream);
 
-/* The item cost and minimum tiles per worker the fused schedule plans with; an
- * hpa_plan call with these values gives the fused schedule's items exactly. */
+/* The item cost, minimum tiles per worker and dynamic tail the fused schedules
+ * plan with; an hpa_plan call with these values gives their items exactly. */
 #define HPA_FUSED_ITEM_COST 4
 #define HPA_FUSED_MIN_TILES 1
+#define HPA_FUSED_TAIL_DEN 0
+#define HPA_FUSED_TAIL_CHUNK 1
 
 /* Flags of hpa_decode_attn. The default (0) runs both launches. */
 enum {
@@ -169,7 +183,10 @@ enum {
  * the workgroup completing a group folds it (and the one completing the last
  * group folds the group results) in the merge kernel's order; no workgroup
  * waits on another, and the counters in plan_ws return to zero. All balanced
- * schedules produce identical bits. The static schedules
+ * schedules produce identical bits. Their persistent workers claim the tail
+ * chunks of the plan (hpa_plan's dynamic tail; HPA_FUSED_TAIL_DEN for the fused
+ * schedules) on a counter in plan_ws that the last workgroup to finish returns
+ * to zero, so calls sharing one plan_ws must not overlap. The static schedules
  * ignore the plan (plan_ws may still be given to receive device errors; NULL
  * otherwise) and size their grid from num_workers. k_scale/v_scale are
  * required for E4M3 caches and ignored for bf16. partial_ws must hold

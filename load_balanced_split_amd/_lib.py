@@ -26,7 +26,7 @@ HPA_SCHED_BALANCED_SINGLE = 4
 SCHED = {"balanced": 0, "static_splits": 1, "static_chunk": 2, "fused": 3, "single": 4}
 DEVERR_SEQ_LEN, DEVERR_PAGE_ID, DEVERR_PROLOGUE, DEVERR_PLAN = 1, 2, 4, 8
 ATTN_NO_MERGE, ATTN_MERGE_ONLY = 1, 2
-HEADER_SLOTS = dict(Wp=0, N=1, S=2, n_items=3, n_merge=4, n_partials=5, error=6, W=7)
+HEADER_SLOTS = dict(Wp=0, N=1, S=2, n_items=3, n_merge=4, n_partials=5, error=6, W=7, D=8, Ws=9)
 
 
 def _header_define(name: str) -> int:
@@ -39,6 +39,8 @@ def _header_define(name: str) -> int:
 # what the fused schedule plans with (hpa_plan with these gives its items exactly)
 FUSED_ITEM_COST = _header_define("HPA_FUSED_ITEM_COST")
 FUSED_MIN_TILES = _header_define("HPA_FUSED_MIN_TILES")
+FUSED_TAIL_DEN = _header_define("HPA_FUSED_TAIL_DEN")
+FUSED_TAIL_CHUNK = _header_define("HPA_FUSED_TAIL_CHUNK")
 
 
 class HpaError(RuntimeError):
@@ -81,7 +83,7 @@ def lib() -> ctypes.CDLL:
             "hpa_plan_workspace_size": [D, _I, ctypes.POINTER(ctypes.c_size_t)],
             "hpa_plan_workspace_layout": [D, _I, ctypes.POINTER(PlanLayout)],
             "hpa_partial_workspace_size": [D, _I, ctypes.POINTER(ctypes.c_size_t)],
-            "hpa_plan": [D, _P, _I, _I, _I, _P, ctypes.c_size_t, _P],
+            "hpa_plan": [D, _P, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P],
             "hpa_decode_attn": [D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I, _P, ctypes.c_size_t,
                                 _P, ctypes.c_size_t, _P, _I, _P],
             "hpa_decode_prologue": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
@@ -159,9 +161,11 @@ def hpa_partial_workspace_size(desc: AttnDesc, num_workers: int = 0) -> int:
     return n.value
 
 
-def hpa_plan(desc, seq_lens, num_workers, min_tiles_per_worker, item_cost, plan_ws, stream=None):
+def hpa_plan(desc, seq_lens, num_workers, min_tiles_per_worker, item_cost, tail_den, tail_chunk, plan_ws,
+             stream=None):
     _check(lib().hpa_plan(ctypes.byref(desc), _ptr(seq_lens), num_workers, min_tiles_per_worker, item_cost,
-                          _ptr(plan_ws), plan_ws.numel() * plan_ws.element_size(), _stream(stream)), "hpa_plan")
+                          tail_den, tail_chunk, _ptr(plan_ws), plan_ws.numel() * plan_ws.element_size(),
+                          _stream(stream)), "hpa_plan")
 
 
 def hpa_decode_attn(desc, sched, q, k_cache, v_cache, k_scale, v_scale, seq_lens, page_table,

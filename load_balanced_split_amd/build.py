@@ -13,9 +13,13 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhpa.so")
 SOURCES = ["plan.hip", "attn.hip", "prologue.hip", "host.cpp"]
 # Packed-fp32 VALU ops are kept out of every kernel (the compiler would otherwise
-# form v_pk_* from scalar float code).
+# form v_pk_* from scalar float code). The atomic optimizer is off: it turns a
+# one-lane counter update into a wave reduction that waits for the returned value
+# at once (s_waitcnt vmcnt(0)), which would drain the K/V stream in flight at
+# every work claim; without it the wait lands where the value is used.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None", "-I", INCLUDE, "-I", CSRC]
 
 
 def hipcc():

@@ -164,6 +164,66 @@ struct CombineLds {
   float l[kWaves][kMaxGroup];
   float o[kWaves][kMaxGroup][kORow];
   int flag;                   // an arrival count, broadcast to the workgroup
+  int claim[2];               // dynamic tail: claimed chunk, broadcast (two slots, alternating)
+};
+
+// Global view of a device pointer: atomics through it are global_* instructions,
+// counted on the vector memory counter only (a flat one also holds up LDS waits).
+typedef __attribute__((address_space(1))) int32_t gint32_t;
+
+// Sticky device error bits in the plan header (callers check a.plan when it may be null).
+__device__ inline void report_error(const AttnArgs& a, int bits) {
+  __hip_atomic_fetch_or((gint32_t*)(a.plan + a.po.header + H_ERR), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Dynamic tail: the last positions of the plan are cut into D chunks that the
+// persistent workers claim one at a time on a device-scope counter, each when it
+// runs out of work, so faster workers end up with more of them. Claims return
+// 0, 1, 2, ...; one at or past D means the queue is empty. When the source hands
+// out the last item a worker holds it sets `want`; the worker's next stream then
+// issues the claim (one lane of wave 0) just before a unit's loads and puts the
+// returned chunk into LDS right after the previous unit's compute, whose wait
+// already covers it, so the claim never drains the K/V stream. take() (one
+// barrier) reads it when the next item is needed. The last workgroup to finish
+// returns both counters to 0, so the next launch starts from an empty count.
+struct TailQueue {
+  int32_t* ctr;           // [chunks claimed, workgroups finished]
+  int* slots;             // CombineLds::claim
+  int D;
+  int k = 0;              // claims taken (selects the slot)
+  bool want = false;      // uniform: a claim is wanted and not issued yet
+  bool issued = false;    // uniform: claim k is in its LDS slot (or on its way there)
+  bool empty = false;
+
+  __device__ bool open() const { return D > 0 && !empty; }
+  // a global (not flat) atomic: it is counted on the vector memory counter only
+  __device__ int fetch() const {
+    return __hip_atomic_fetch_add((gint32_t*)ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ int* slot() const { return slots + (k & 1); }
+  // uniform; the next chunk, or -1 once the queue is empty
+  __device__ int take() {
+    if (!issued && threadIdx.x == 0) *slot() = fetch();       // not issued ahead: claim now
+    __syncthreads();   // claims k and k + 2 share a slot: claim k + 1's barrier separates them
+    const int c = __builtin_amdgcn_readfirstlane(*slot());
+    ++k;
+    want = issued = false;
+    if (c >= D) {
+      empty = true;
+      return -1;
+    }
+    return c;
+  }
+  // called once by each of the `participants` workgroups after its last take()
+  __device__ void finish(int participants) const {
+    gint32_t* g = (gint32_t*)ctr;
+    if (D > 0 && threadIdx.x == 0 &&
+        __hip_atomic_fetch_add(g + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == participants - 1) {
+      // every other workgroup's last claim returned before it counted itself in
+      __hip_atomic_store(g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(g + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 };
 
 // Scalar view of read-only device arrays: a load through it returns one value
@@ -197,6 +257,7 @@ struct Worker {
   CombineLds& lds;
   uint32_t units_done = 0;
   uint64_t* trec = nullptr;   // instrumented build: this wave's record
+  TailQueue tq{};             // the dynamic tail (D = 0: none)
   int titem = 0;
   int lane, wave, m16, j;
   uint32_t loff;         // per-lane byte offset inside each 1 KB load
@@ -343,7 +404,7 @@ struct Worker {
     st.L = it.L >= 0 ? it.L : sload(a.seq_lens, st.b);
     st.kscale = FP8 ? sloadf(a.k_scale, st.g) : 1.f;
     st.vscale = FP8 ? sloadf(a.v_scale, st.g) : 1.f;
-    if (!st.valid && threadIdx.x == 0 && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PLAN);
+    if (!st.valid && threadIdx.x == 0 && a.plan) report_error(a, HPA_DEVERR_PLAN);
     return st;
   }
 
@@ -392,7 +453,7 @@ struct Worker {
   }
 
   __device__ void report_bad_page() const {
-    if (lane == 0 && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PAGE_ID);
+    if (lane == 0 && a.plan) report_error(a, HPA_DEVERR_PAGE_ID);
   }
 
   // Stream this wave's units of item st; unit `wave` is already in bufA (okA: it
@@ -408,13 +469,25 @@ struct Worker {
     bool any_bad = false;
     rsrc_t rk, rv;
     int pidA = -1;
+    // a wanted tail claim: issued before this item's second unit's loads, stored to
+    // LDS after its first unit's compute (wave 0's first unit exists in every item)
+    bool claim = tq.want;
+    const bool claimer = claim && wave == 0 && lane == 0;
+    int ticket = 0;
     for (int u = wave;; u += 2 * kWaves) {
       const int uB = u + kWaves, uA = uB + kWaves;
       const bool okB = unit_rsrc(st, nu, uB, pidB, rk, rv);
       any_bad |= uB < nu && !okB;
+      if (claim && claimer) ticket = tq.fetch();
       issue(bufB, rk, rv, uB % C::UPT);
       if (uA < nu) pidA = page_of(st, uA);
       if (okA) compute(bufA, q, tok0(st, u), st.L, qk_scale, m_run, l_part, o);
+      if (claim) {
+        if (claimer) *tq.slot() = ticket;
+        tq.want = false;
+        tq.issued = true;
+        claim = false;
+      }
       if (uA < nu) {
         okA = unit_rsrc(st, nu, uA, pidA, rk, rv);
         any_bad |= !okA;
@@ -595,7 +668,7 @@ struct Worker {
     using C = Cfg<FP8>;
     start_stamp(0);
     Item it;
-    if (!src.next(it)) return;
+    if (!src.next(it, tq)) return;
     start_stamp(1);
     ItemState st = open(it);
     load_q(st, q);
@@ -609,7 +682,7 @@ struct Worker {
     issue(bufA, rk, rv, wave % C::UPT);
     start_stamp(3);
     Item nit;
-    bool more = src.next(nit);
+    bool more = src.next(nit, tq);
     for (;;) {
       ItemState nst{};
       int npid = -1, npidB = -1;
@@ -620,7 +693,7 @@ struct Worker {
         npidB = page_of(nst, wave + kWaves);
       }
       Item nnit;
-      const bool more2 = more && src.next(nnit);
+      const bool more2 = more && src.next(nnit, tq);
       float m_run = -INFINITY, l_part = 0.f;
       f32x4 o[8];
 #pragma unroll
@@ -643,15 +716,30 @@ struct Worker {
 };
 
 // Items of worker w from the planner's work list (scalar loads; next() only
-// issues them, the entry is checked when the driver opens it).
+// issues them, the entry is checked when the driver opens it), then those of
+// the tail chunks it claims (virtual workers Ws + c).
 struct PlanSource {
   const AttnArgs& a;
   int i, i1;
-  __device__ bool next(Item& it) {
-    if (i >= i1) return false;
+  int Ws, cap;
+  bool bad = false;   // a chunk's item range did not fit the work list (reported by the caller:
+                      // a one-lane branch here would make the compiler treat i as divergent)
+  __device__ bool next(Item& it, TailQueue& q) {
+    while (i >= i1) {
+      if (!q.open()) return false;
+      const int c = q.take();
+      if (c < 0) return false;
+      i = sload(a.plan, a.po.worker_off + Ws + c);
+      i1 = sload(a.plan, a.po.worker_off + Ws + c + 1);
+      if (i < 0 || i1 < i || i1 > cap) {
+        bad = true;
+        i1 = i;
+      }
+    }
     it = Item{sload(a.plan, a.po.item_s + i), sload(a.plan, a.po.item_t0 + i), sload(a.plan, a.po.item_t1 + i),
               sload(a.plan, a.po.item_slot + i), -1, 0, 0};
     ++i;
+    if (i == i1 && q.open()) q.want = true;   // the last item held: claim the next chunk
     return true;
   }
 };
@@ -661,21 +749,32 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_balanced_
   __shared__ CombineLds lds;
   WaveTrace tr(a);
   const int w = blockIdx.x;
-  if (sload(a.plan, a.po.header + H_W) != static_cast<int>(gridDim.x)) {
-    if (w == 0 && threadIdx.x == 0) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PLAN);
+  const int W = gridDim.x;
+  const int Wp = sload(a.plan, a.po.header + H_WP), Ws = sload(a.plan, a.po.header + H_WS);
+  const int D = sload(a.plan, a.po.header + H_ND);
+  if (sload(a.plan, a.po.header + H_W) != W || Wp < 0 || Wp > W || Ws < 0 || Ws > Wp || D < 0 ||
+      D > kTailChunksPerWorker * W) {
+    if (w == 0 && threadIdx.x == 0) report_error(a, HPA_DEVERR_PLAN);
     return;
   }
-  if (w >= sload(a.plan, a.po.header + H_WP)) return;
-  int i0 = sload(a.plan, a.po.worker_off + w), i1 = sload(a.plan, a.po.worker_off + w + 1);
-  const int cap = a.workers + a.batch * a.hkv;      // the work list holds at most W + S items
-  if (i0 < 0 || i1 < i0 || i1 > cap) {
-    if (threadIdx.x == 0) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_PLAN);
-    return;
+  if (w >= Wp) return;
+  const int cap = (1 + kTailChunksPerWorker) * W + a.batch * a.hkv;   // the work list's size bound
+  int i0 = 0, i1 = 0;
+  if (w < Ws) {
+    i0 = sload(a.plan, a.po.worker_off + w);
+    i1 = sload(a.plan, a.po.worker_off + w + 1);
+    if (i0 < 0 || i1 < i0 || i1 > cap) {
+      if (threadIdx.x == 0) report_error(a, HPA_DEVERR_PLAN);
+      i1 = i0;                            // still take part in the tail, so its counters return to 0
+    }
   }
-  PlanSource src{a, i0, i1};
+  PlanSource src{a, i0, i1, Ws, cap};
   Worker<FP8> r(a, lds);
   r.trec = tr.rec;
+  r.tq = TailQueue{a.qctr, lds.claim, D};
   r.run(src);
+  r.tq.finish(Wp);
+  if (src.bad && threadIdx.x == 0) report_error(a, HPA_DEVERR_PLAN);
   tr.units = r.units_done;
 }
 
@@ -683,7 +782,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_balanced_
 struct SingleSource {
   Item item;
   bool given;
-  __device__ bool next(Item& it) {
+  __device__ bool next(Item& it, TailQueue&) {
     if (given) return false;
     given = true;
     it = item;
@@ -699,7 +798,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a
   const int b = s / a.hkv;
   int L = a.seq_lens[b];
   if (L < 0 || L > a.max_pages * kPage) {
-    if (k == 0 && threadIdx.x == 0 && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_SEQ_LEN);
+    if (k == 0 && threadIdx.x == 0 && a.plan) report_error(a, HPA_DEVERR_SEQ_LEN);
     return;
   }
   const int n = (L + kPage - 1) / kPage;
@@ -747,35 +846,49 @@ template <bool INMERGE>
 struct FusedSource {
   const AttnArgs& a;
   const FusedPlanLds& P;
-  int w, Wp, N, S;
-  bool small;
+  Partition part;
+  int S;
+  int v;                      // the virtual worker whose positions [pos, e) are being walked
   int pos, e, s;
   // positions [C[s], C[s+1]) of a non-empty sequence: item_cost virtual ones, then its tiles
-  __device__ bool next(Item& it) {
-    while (pos < e) {
-      const int c0 = __builtin_amdgcn_readfirstlane(P.C[s]);
-      const int c1 = __builtin_amdgcn_readfirstlane(P.C[s + 1]);
-      if (c1 > c0) {
-        const int r0 = c0 + a.item_cost;
-        const int t1 = min(e, c1), lo = max(pos, r0);
-        pos = t1;
-        if (lo < t1) {
-          const int first = __builtin_amdgcn_readfirstlane(owner_of_tile(r0, Wp, N, small));
-          const int split = w - first;
-          const int ns = __builtin_amdgcn_readfirstlane(owner_of_tile(c1 - 1, Wp, N, small)) - first + 1;
-          const int pb = __builtin_amdgcn_readfirstlane(P.PB[s]);
-          it = Item{s, lo - r0, t1 - r0, ns > 1 ? pb + split : -1, __builtin_amdgcn_readfirstlane(P.L[s]), ns, pb};
-          if (!INMERGE && split == 0 && threadIdx.x == 0) {   // record for the merge kernel
-            a.plan[a.po.num_splits + s] = ns;
-            a.plan[a.po.partial_base + s] = pb;
+  __device__ bool next(Item& it, TailQueue& q) {
+    for (;;) {
+      while (pos < e) {
+        const int c0 = __builtin_amdgcn_readfirstlane(P.C[s]);
+        const int c1 = __builtin_amdgcn_readfirstlane(P.C[s + 1]);
+        if (c1 > c0) {
+          const int r0 = c0 + a.item_cost;
+          const int t1 = min(e, c1), lo = max(pos, r0);
+          pos = t1;
+          if (lo < t1) {
+            const int first = __builtin_amdgcn_readfirstlane(part.owner(r0));
+            const int split = v - first;
+            const int ns = __builtin_amdgcn_readfirstlane(part.owner(c1 - 1)) - first + 1;
+            const int pb = __builtin_amdgcn_readfirstlane(P.PB[s]);
+            it = Item{s, lo - r0, t1 - r0, ns > 1 ? pb + split : -1, __builtin_amdgcn_readfirstlane(P.L[s]), ns, pb};
+            // the last item held: claim the next chunk (the next sequence's tiles start
+            // item_cost positions after this item's end). Set before the one-lane store
+            // below: after it, the compiler takes the flag, and with it the item
+            // index, for divergent and reads the page table with vector loads.
+            if (pos + a.item_cost >= e && q.open()) q.want = true;
+            if (!INMERGE && split == 0 && threadIdx.x == 0) {   // record for the merge kernel
+              a.plan[a.po.num_splits + s] = ns;
+              a.plan[a.po.partial_base + s] = pb;
+            }
+            ++s;
+            return true;
           }
-          ++s;
-          return true;
         }
+        ++s;
       }
-      ++s;
+      if (!q.open()) return false;
+      const int c = q.take();
+      if (c < 0) return false;
+      v = part.Ws + c;
+      pos = part.begin(v);
+      e = part.begin(v + 1);
+      s = __builtin_amdgcn_readfirstlane(seq_of_tile(P.C, S, pos));
     }
-    return false;
   }
 };
 
@@ -788,8 +901,9 @@ constexpr int kRegPlanChunks = kRegPlanSeqs / 64;
 
 struct RegPlan {
   int L[kRegPlanChunks], C[kRegPlanChunks], n[kRegPlanChunks], PB[kRegPlanChunks];
-  int N, Wp;
-  bool small, bad;
+  int N;
+  Partition part;
+  bool bad;
 
   // chunks at or past S (a uniform test) are skipped whole: their lanes would hold
   // no sequence, and nothing reads them
@@ -817,8 +931,7 @@ struct RegPlan {
       carry += __builtin_amdgcn_readlane(incl, 63);
     }
     N = carry;
-    Wp = N == 0 ? 0 : min(W, max(1, N / a.min_tiles));
-    small = small_products(N, Wp);
+    part = Partition::make(N, N, W, a.min_tiles, a.tail_den, a.tail_chunk);
     bad = __builtin_amdgcn_ballot_w64(bad_lane) != 0;
     carry = 0;
 #pragma unroll
@@ -827,7 +940,7 @@ struct RegPlan {
       int v = 0;
       if (n[k] > 0) {
         const int r0 = C[k] + a.item_cost;
-        const int ns = owner_of_tile(r0 + n[k] - 1, Wp, N, small) - owner_of_tile(r0, Wp, N, small) + 1;
+        const int ns = part.owner(r0 + n[k] - 1) - part.owner(r0) + 1;
         v = ns > 1 ? ns : 0;
       }
       const int incl = wave_incl_scan(v);
@@ -846,20 +959,19 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int S = a.batch * a.hkv, nch = (S + 63) / 64;
   const int W = gridDim.x, w = blockIdx.x;
-  int N, Wp, bad, pos = 0, pend = 0, s0 = 0;
-  bool small;
+  int N, bad, pos = 0, pend = 0, s0 = 0;
+  Partition part;
   if (S <= kRegPlanSeqs) {
     RegPlan R;
     R.build(a, S, W, lane);
     N = R.N;
-    Wp = R.Wp;
-    small = R.small;
+    part = R.part;
     bad = R.bad;
-    if (w < Wp) {
-      // this worker's positions and the sequence holding the first one (largest s
-      // with C[s] <= pos: C is non-decreasing, so count the lanes at or below pos)
-      pos = __builtin_amdgcn_readfirstlane(range_begin(w, Wp, N, small));
-      pend = __builtin_amdgcn_readfirstlane(range_begin(w + 1, Wp, N, small));
+    if (w < part.Ws) {
+      // this worker's static positions and the sequence holding the first one (largest
+      // s with C[s] <= pos: C is non-decreasing, so count the lanes at or below pos)
+      pos = __builtin_amdgcn_readfirstlane(part.begin(w));
+      pend = __builtin_amdgcn_readfirstlane(part.begin(w + 1));
       int cnt = 0;
 #pragma unroll
       for (int k = 0; k < kRegPlanChunks; ++k)
@@ -903,8 +1015,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
     N = add_chunk_offsets(P, P.C, S, nch, lane, wave);
     if (threadIdx.x == 0) P.C[S] = N;
     __syncthreads();
-    Wp = __builtin_amdgcn_readfirstlane(N == 0 ? 0 : min(W, max(1, N / a.min_tiles)));
-    small = small_products(N, Wp);
+    part = Partition::make(N, N, W, a.min_tiles, a.tail_den, a.tail_chunk);
     // partial-slot bases: exclusive prefix of (num_splits > 1 ? num_splits : 0)
     for (int ch = wave; ch < nch; ch += kWaves) {
       const int s = ch * 64 + lane;
@@ -912,7 +1023,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
       if (s < S) {
         const int c0 = P.C[s], c1 = P.C[s + 1];
         if (c1 > c0) {
-          const int ns = owner_of_tile(c1 - 1, Wp, N, small) - owner_of_tile(c0 + a.item_cost, Wp, N, small) + 1;
+          const int ns = part.owner(c1 - 1) - part.owner(c0 + a.item_cost) + 1;
           v = ns > 1 ? ns : 0;
         }
       }
@@ -923,13 +1034,13 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
     __syncthreads();
     add_chunk_offsets(P, P.PB, S, nch, lane, wave);
     __syncthreads();
-    if (w < Wp) {
-      pos = __builtin_amdgcn_readfirstlane(range_begin(w, Wp, N, small));
-      pend = __builtin_amdgcn_readfirstlane(range_begin(w + 1, Wp, N, small));
+    if (w < part.Ws) {
+      pos = __builtin_amdgcn_readfirstlane(part.begin(w));
+      pend = __builtin_amdgcn_readfirstlane(part.begin(w + 1));
       s0 = __builtin_amdgcn_readfirstlane(seq_of_tile(P.C, S, pos));
     }
   }
-  if (w == 0 && threadIdx.x == 0 && bad && a.plan) atomicOr(&a.plan[a.po.header + H_ERR], HPA_DEVERR_SEQ_LEN);
+  if (w == 0 && threadIdx.x == 0 && bad && a.plan) report_error(a, HPA_DEVERR_SEQ_LEN);
   // empty (or invalid) sequences own no tile: their zero rows are spread over the workers
   for (int s = w; s < S; s += W) {
     if (P.C[s + 1] == P.C[s]) {
@@ -938,11 +1049,14 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
       for (int i = threadIdx.x; i < a.group * kHeadDim; i += kAttnThreads) row[i] = 0;
     }
   }
-  if (w >= Wp) return;
-  FusedSource<INMERGE> src{a, P, w, Wp, N, S, small, pos, pend, __builtin_amdgcn_readfirstlane(s0)};
+  if (w >= part.Wp) return;
+  // workers without a static range go straight to the tail chunks
+  FusedSource<INMERGE> src{a, P, part, S, w, pos, pend, __builtin_amdgcn_readfirstlane(s0)};
   Worker<FP8, INMERGE> r(a, lds);
   r.trec = tr.rec;
+  r.tq = TailQueue{a.qctr, lds.claim, part.D};
   r.run(src);
+  r.tq.finish(part.Wp);
   tr.units = r.units_done;
 }
 

@@ -162,18 +162,20 @@ hpa_status hpa_partial_workspace_size(const hpa_attn_desc* desc, int32_t num_wor
   int32_t W = 0;
   if ((st = resolve_workers(num_workers, -1, &W)) != HPA_OK) return st;
   const int64_t S = int64_t(desc->batch) * desc->num_kv_heads;
-  *bytes = static_cast<size_t>(hpa::partial_layout(W + S, desc->num_q_heads / desc->num_kv_heads).total_bytes +
+  *bytes = static_cast<size_t>(hpa::partial_layout(hpa::max_slots(W, S), desc->num_q_heads / desc->num_kv_heads).total_bytes +
                                hpa::trace_bytes(W + S));
   return HPA_OK;
 }
 
 hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t num_workers,
-                    int32_t min_tiles_per_worker, int32_t item_cost, void* plan_ws, size_t plan_ws_bytes,
-                    hipStream_t stream) {
+                    int32_t min_tiles_per_worker, int32_t item_cost, int32_t tail_den, int32_t tail_chunk,
+                    void* plan_ws, size_t plan_ws_bytes, hipStream_t stream) {
   hpa_status st = check_desc(desc);
   if (st != HPA_OK) return st;
   if (min_tiles_per_worker < 1) return fail(HPA_ERR_INVALID_ARG, "min_tiles_per_worker %d < 1", min_tiles_per_worker);
   if (item_cost < 0 || item_cost > 64) return fail(HPA_ERR_INVALID_ARG, "item_cost %d outside [0, 64]", item_cost);
+  if (tail_den < 0) return fail(HPA_ERR_INVALID_ARG, "tail_den %d < 0", tail_den);
+  if (tail_chunk < 1) return fail(HPA_ERR_INVALID_ARG, "tail_chunk %d < 1", tail_chunk);
   if (!plan_ws) return fail(HPA_ERR_INVALID_ARG, "plan_ws is NULL");
   if (desc->batch > 0 && !seq_lens) return fail(HPA_ERR_INVALID_ARG, "seq_lens is NULL");
   int32_t W = 0;
@@ -182,7 +184,8 @@ hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t 
   if (plan_ws_bytes < static_cast<size_t>(o.total * 4))
     return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)(o.total * 4));
   if (hpa::launch_plan(seq_lens, desc->batch, desc->num_kv_heads, desc->max_pages_per_seq, W,
-                       min_tiles_per_worker, item_cost, static_cast<int32_t*>(plan_ws), o, stream) != hipSuccess)
+                       min_tiles_per_worker, item_cost, tail_den, tail_chunk, static_cast<int32_t*>(plan_ws), o,
+                       stream) != hipSuccess)
     return fail(HPA_ERR_LAUNCH, "planner launch failed");
   return HPA_OK;
 }
@@ -213,7 +216,7 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   if ((st = resolve_workers(num_workers, static_cast<int>(sched), &W)) != HPA_OK) return st;
   const int64_t S = int64_t(desc->batch) * desc->num_kv_heads;
   const int G = desc->num_q_heads / desc->num_kv_heads;
-  const hpa::PartialLayout pl = hpa::partial_layout(W + S, G);
+  const hpa::PartialLayout pl = hpa::partial_layout(hpa::max_slots(W, S), G);
   const int64_t need = pl.total_bytes + hpa::trace_bytes(W + S);
   if (partial_ws_bytes < static_cast<size_t>(need))
     return fail(HPA_ERR_WORKSPACE, "partial workspace %zu bytes < %lld", partial_ws_bytes, (long long)need);
@@ -237,6 +240,7 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   a.plan = static_cast<int32_t*>(plan_ws);
   a.gctr = a.plan ? a.plan + po.gctr : nullptr;
   a.sctr = a.plan ? a.plan + po.sctr : nullptr;
+  a.qctr = a.plan ? a.plan + po.qctr : nullptr;
   char* pw = static_cast<char*>(partial_ws);
   a.part_acc = reinterpret_cast<float*>(pw + pl.acc);
   a.part_m = reinterpret_cast<float*>(pw + pl.m);
@@ -252,11 +256,13 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   a.num_pages = desc->num_pages;
   a.sm_scale = desc->sm_scale;
   a.workers = W;
-  a.slots = W + S;
+  a.slots = static_cast<int>(hpa::max_slots(W, S));
 
   const bool do_attn = !(flags & HPA_ATTN_MERGE_ONLY), do_merge = !(flags & HPA_ATTN_NO_MERGE);
   a.min_tiles = HPA_FUSED_MIN_TILES;
   a.item_cost = HPA_FUSED_ITEM_COST;
+  a.tail_den = HPA_FUSED_TAIL_DEN;
+  a.tail_chunk = HPA_FUSED_TAIL_CHUNK;
   if (sched == HPA_SCHED_BALANCED || sched == HPA_SCHED_BALANCED_FUSED || sched == HPA_SCHED_BALANCED_SINGLE) {
     if (sched == HPA_SCHED_BALANCED_SINGLE) {
       // one launch: the persistent kernel plans, attends and merges (flags have no effect)

@@ -50,24 +50,29 @@ __host__ __device__ inline int v_block_index(int t, int d, bool fp8) {
 
 // Header slots of the plan workspace (int32).
 enum : int {
-  H_WP = 0, H_N = 1, H_S = 2, H_NITEMS = 3, H_NMERGE = 4, H_NPART = 5, H_ERR = 6, H_W = 7
+  H_WP = 0, H_N = 1, H_S = 2, H_NITEMS = 3, H_NMERGE = 4, H_NPART = 5, H_ERR = 6, H_W = 7, H_ND = 8, H_WS = 9
 };
 
 // Offsets of the plan arrays, in int32 elements.
 struct PlanOffsets {
   int64_t header, C, worker_off, item_s, item_t0, item_t1, item_split, item_slot,
-          num_splits, partial_base, merge_list, ne, gctr, sctr, total;
+          num_splits, partial_base, merge_list, ne, gctr, sctr, qctr, total;
   int32_t max_items;
 };
+
+// A dynamic tail has at most this many chunks per worker, so a plan for W
+// workers has at most (1 + kTailChunksPerWorker) W virtual workers.
+constexpr int kTailChunksPerWorker = 4;
 
 inline PlanOffsets plan_offsets(int64_t S, int64_t W) {
   PlanOffsets o{};
   auto al = [](int64_t x) { return (x + 63) & ~int64_t(63); };   // 256-byte aligned arrays
-  const int64_t mi = W + S;
+  const int64_t V = (1 + kTailChunksPerWorker) * W;                // virtual workers, at most
+  const int64_t mi = V + S;
   int64_t p = 0;
   o.header = p;       p += al(kHeaderInts);
   o.C = p;            p += al(S + 1);
-  o.worker_off = p;   p += al(W + 1);
+  o.worker_off = p;   p += al(V + 1);
   o.item_s = p;       p += al(mi);
   o.item_t0 = p;      p += al(mi);
   o.item_t1 = p;      p += al(mi);
@@ -82,6 +87,9 @@ inline PlanOffsets plan_offsets(int64_t S, int64_t W) {
   // returned to 0 by the workgroup that sees the last arrival
   o.gctr = p;         p += al(mi);
   o.sctr = p;         p += al(S);
+  // dynamic tail: chunks claimed so far, workgroups finished; the last workgroup to
+  // finish returns both to 0 (the planner clears them too)
+  o.qctr = p;         p += al(2);
   o.total = p;
   o.max_items = static_cast<int32_t>(mi);
   return o;
@@ -102,6 +110,10 @@ inline PartialLayout partial_layout(int64_t slots, int64_t G) {
   return p;
 }
 
+// Partial slots a launch may need: one per item, and a plan has at most one item
+// per (virtual worker, sequence boundary): (1 + kTailChunksPerWorker) W + S.
+inline int64_t max_slots(int64_t W, int64_t S) { return (1 + kTailChunksPerWorker) * W + S; }
+
 // Split results of one sequence are combined in a fixed order: contiguous groups
 // of kMergeGroup splits are folded in split order with a running max, then the
 // group results are folded in group order.
@@ -119,6 +131,7 @@ struct AttnArgs {
   int32_t* plan;               // plan workspace (may be null for static schedules)
   int32_t* gctr;               // in-kernel merge arrival counters (fused schedule), in plan
   int32_t* sctr;
+  int32_t* qctr;               // dynamic tail counters [claimed, finished], in plan
   float* part_acc;
   float* part_m;
   float* part_l;
@@ -126,13 +139,14 @@ struct AttnArgs {
   PlanOffsets po;
   int batch, hq, hkv, group, max_pages, num_pages;
   int workers;                 // W the kernels were launched for (plan header must agree)
-  int64_t slots;               // partial slots available (W + S)
+  int64_t slots;               // partial slots available (max_slots(W, S))
   float sm_scale;
   // static schedules
   int static_splits;           // S_split
   int static_chunk;            // fixed chunk (flavour "chunk"), 0 for flavour "splits"
   int min_tiles;               // fused schedule: minimum tiles per active worker
   int item_cost;               // fused schedule: virtual tiles charged per item
+  int tail_den, tail_chunk;    // fused schedule: dynamic tail (last 1/tail_den of the positions)
   // instrumented builds only: per-wave records [block][wave][kTraceWords]
   uint64_t* trace;
 };
@@ -176,6 +190,40 @@ __device__ inline bool small_products(int N, int Wp) {
   return (int64_t(N) + 1) * (int64_t(Wp) + 1) < (int64_t(1) << 31);
 }
 
+// The balanced partition of Np positions (N real tiles) with a dynamic tail: the
+// last T = Np / tail_den positions (none without a tail) are cut into D chunks
+// claimed at run time, the first A = Np - T are split evenly over Ws = min(Wp, A)
+// static workers (Wp active workers), so every virtual worker owns at least one
+// position. Virtual worker v < Ws is static worker v, virtual worker Ws + c is chunk c.
+struct Partition {
+  int Np, Wp, Ws, A, T, D;
+  bool small_a, small_t;      // exact 32-bit products
+
+  __device__ static Partition make(int N, int Np, int W, int min_tiles, int tail_den, int tail_chunk) {
+    Partition p;
+    p.Np = Np;
+    p.Wp = N == 0 ? 0 : min(W, max(1, Np / min_tiles));
+    p.T = (tail_den > 0 && N > 0) ? Np / tail_den : 0;
+    p.A = Np - p.T;
+    p.Ws = min(p.Wp, p.A);
+    p.D = p.T > 0 ? min((p.T + tail_chunk - 1) / tail_chunk, kTailChunksPerWorker * W) : 0;
+    p.small_a = small_products(p.A, p.Ws);
+    p.small_t = small_products(p.T, p.D);
+    return p;
+  }
+  __device__ int V() const { return Ws + D; }
+  // first position of virtual worker v, 0 <= v <= V (begin(V) = Np)
+  __device__ int begin(int v) const {
+    if (v < Ws) return range_begin(v, Ws, A, small_a);
+    return A + (v == Ws ? 0 : range_begin(v - Ws, D, T, small_t));
+  }
+  // virtual worker owning position p, 0 <= p < Np
+  __device__ int owner(int p) const {
+    if (p < A) return owner_of_tile(p, Ws, A, small_a);
+    return Ws + owner_of_tile(p - A, D, T, small_t);
+  }
+};
+
 // Largest s in [0, S) with C[s] <= t, for 0 <= t < C[S].
 __device__ inline int seq_of_tile(const int32_t* C, int S, int t) {
   int lo = 0, hi = S - 1;
@@ -204,7 +252,8 @@ __device__ inline int wave_incl_scan(int x) {
 
 // Launch wrappers (defined in the .hip files). Return hipSuccess or the launch error.
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_pages, int num_workers,
-                       int min_tiles, int item_cost, int32_t* plan, const PlanOffsets& po, hipStream_t stream);
+                       int min_tiles, int item_cost, int tail_den, int tail_chunk, int32_t* plan,
+                       const PlanOffsets& po, hipStream_t stream);
 hipError_t launch_attn_balanced(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream);
 hipError_t launch_attn_static(const AttnArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_attn_fused(const AttnArgs& a, bool fp8, bool merge_in_kernel, int num_workers, hipStream_t stream);

@@ -16,9 +16,14 @@
 // sequences before s), its real tiles at [P[s] + c, P[s+1]); N' = P[S]. Worker w
 // owns positions [w*N'/W', (w+1)*N'/W'), W' = min(W, max(1, N'/min_tiles)), and
 // its items are the real tiles it owns; c = 0 is the plain even split.
-// Every quantity is closed-form, so no thread walks another worker's range:
-//   worker owning position p  = floor(((p+1) * W' - 1) / N')
-//   first worker of sequence s = owner of P[s] + c, last = owner of P[s+1] - 1.
+// Dynamic tail (same section: the scheduler evaluates progress as it goes): the
+// last T = N' / tail_den positions are cut into D chunks that workers claim at run
+// time; the first A = N' - T are split over Ws = min(W', A) static workers. The
+// plan lists virtual workers v < Ws + D (static ranges, then chunks) in order, so
+// it does not depend on who claims which chunk. tail_den 0: no tail, Ws = W'.
+// Every quantity is closed-form (Partition), so no thread walks another worker's
+// range: the first virtual worker of sequence s owns position P[s] + c, the last
+// owns P[s+1] - 1, and all those between hold part of s.
 #include "hpa_internal.hpp"
 
 namespace hpa {
@@ -64,7 +69,7 @@ __device__ inline int seq_of_pos(const int32_t* C, const int32_t* NE, int c, int
 template <bool LDS>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ seq_lens, int B, int Hkv, int max_pages, int W, int min_tiles,
-    int cost, int32_t* __restrict__ ws, PlanOffsets po) {
+    int cost, int tail_den, int tail_chunk, int32_t* __restrict__ ws, PlanOffsets po) {
   __shared__ int2 tmp[kPlanThreads / 64 + 1];
   __shared__ int sh_bad;
   __shared__ int sC[LDS ? kPlanLdsSeqs + 1 : 1];
@@ -108,8 +113,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   __syncthreads();
   const int N = carry;
   const int Np = N + cost * carry_ne;               // positions: real plus virtual tiles
-  const int Wp = N == 0 ? 0 : min(W, max(1, Np / min_tiles));
-  const bool small = small_products(Np, Wp);
+  const Partition part = Partition::make(N, Np, W, min_tiles, tail_den, tail_chunk);
+  const int V = part.V();
   auto P = [&](int s) { return C[s] + cost * NE[s]; };
 
   // 2. splits per sequence, partial slot bases, merge list
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     int ns = 0;
     if (s < S) {
       if (C[s + 1] > C[s])
-        ns = owner_of_tile(P(s + 1) - 1, Wp, Np, small) - owner_of_tile(P(s) + cost, Wp, Np, small) + 1;
+        ns = part.owner(P(s + 1) - 1) - part.owner(P(s) + cost) + 1;
       num_splits[s] = ns;
     }
     int ex_p, ex_m, tot_p, tot_m;
@@ -135,16 +140,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     carry_m += tot_m;
   }
 
-  // 3. items per worker and their CSR offsets
+  // 3. items per virtual worker and their CSR offsets
   int32_t* woff = ws + po.worker_off;
   int carry_i = 0;
   int my_off = 0;                     // worker tid's first item (kept when one pass covers all workers)
-  for (int base = 0; base < Wp; base += kPlanThreads) {
+  for (int base = 0; base < V; base += kPlanThreads) {
     const int w = base + tid;
     int cnt = 0;
-    if (w < Wp) {
-      const int a = range_begin(w, Wp, Np, small);
-      const int e = range_begin(w + 1, Wp, Np, small);
+    if (w < V) {
+      const int a = part.begin(w), e = part.begin(w + 1);
       // sf / sl hold positions a / e - 1 (both non-empty); the sequences between them
       // lie inside [a, e); sf and sl count when their real tiles start before e
       const int sf = seq_of_pos(C, NE, cost, S, a), sl = seq_of_pos(C, NE, cost, S, e - 1);
@@ -152,10 +156,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     }
     int ex, unused, tot, unused_t;
     block_exclusive_scan2(cnt, 0, tmp, ex, unused, tot, unused_t);
-    if (w < Wp) woff[w] = my_off = carry_i + ex;
+    if (w < V) woff[w] = my_off = carry_i + ex;
     carry_i += tot;
   }
-  if (tid == 0) woff[Wp] = carry_i;
+  if (tid == 0) woff[V] = carry_i;
   __syncthreads();
 
   // 4. emit items, worker by worker, in sequence order
@@ -164,17 +168,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   int32_t* it1 = ws + po.item_t1;
   int32_t* isp = ws + po.item_split;
   int32_t* isl = ws + po.item_slot;
-  for (int w = tid; w < Wp; w += kPlanThreads) {
-    const int a = range_begin(w, Wp, Np, small);
-    const int e = range_begin(w + 1, Wp, Np, small);
+  for (int w = tid; w < V; w += kPlanThreads) {
+    const int a = part.begin(w), e = part.begin(w + 1);
     int s = seq_of_pos(C, NE, cost, S, a);
-    int pos = Wp <= kPlanThreads ? my_off : woff[w];
+    int pos = V <= kPlanThreads ? my_off : woff[w];
     for (; s < S && P(s) < e; ++s) {
       if (C[s + 1] == C[s]) continue;
       const int r0 = P(s) + cost, r1 = P(s + 1);      // the real tiles of s
       const int lo = max(a, r0), hi = min(e, r1);
       if (lo >= hi) continue;
-      const int split = w - owner_of_tile(r0, Wp, Np, small);
+      const int split = w - part.owner(r0);
       is[pos] = s;
       it0[pos] = lo - r0;
       it1[pos] = hi - r0;
@@ -194,7 +197,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     }
   }
   if (tid == 0) {
-    hdr[H_WP] = Wp;
+    hdr[H_WP] = part.Wp;
+    hdr[H_WS] = part.Ws;
+    hdr[H_ND] = part.D;
+    ws[po.qctr] = 0;
+    ws[po.qctr + 1] = 0;
     hdr[H_N] = N;
     hdr[H_S] = S;
     hdr[H_NITEMS] = carry_i;
@@ -210,13 +217,14 @@ __global__ void clear_word_kernel(int32_t* w) { *w = 0; }
 }  // namespace
 
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_pages, int num_workers,
-                       int min_tiles, int item_cost, int32_t* plan, const PlanOffsets& po, hipStream_t stream) {
+                       int min_tiles, int item_cost, int tail_den, int tail_chunk, int32_t* plan,
+                       const PlanOffsets& po, hipStream_t stream) {
   if (int64_t(batch) * hkv <= kPlanLdsSeqs)
     hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch, hkv,
-                       max_pages, num_workers, min_tiles, item_cost, plan, po);
+                       max_pages, num_workers, min_tiles, item_cost, tail_den, tail_chunk, plan, po);
   else
     hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch, hkv,
-                       max_pages, num_workers, min_tiles, item_cost, plan, po);
+                       max_pages, num_workers, min_tiles, item_cost, tail_den, tail_chunk, plan, po);
   return hipGetLastError();
 }
 

@@ -68,9 +68,11 @@ class DeviceStep:
             return self.q_rot, self.lens_after
         return self.q, self.seq_lens
 
-    def plan(self, min_tiles: int = _lib.FUSED_MIN_TILES, item_cost: int = _lib.FUSED_ITEM_COST, stream=None):
+    def plan(self, min_tiles: int = _lib.FUSED_MIN_TILES, item_cost: int = _lib.FUSED_ITEM_COST,
+             tail_den: int = _lib.FUSED_TAIL_DEN, tail_chunk: int = _lib.FUSED_TAIL_CHUNK, stream=None):
         _, lens = self.attn_inputs()
-        _lib.hpa_plan(self.desc, lens, self.num_workers, min_tiles, item_cost, self.plan_ws, stream)
+        _lib.hpa_plan(self.desc, lens, self.num_workers, min_tiles, item_cost, tail_den, tail_chunk,
+                      self.plan_ws, stream)
 
     def attend(self, sched: str = "balanced", stream=None, flags: int = 0):
         q, lens = self.attn_inputs()
@@ -81,12 +83,13 @@ class DeviceStep:
                              self.out, flags, stream)
 
     def step(self, sched: str = "balanced", min_tiles: int = _lib.FUSED_MIN_TILES,
-             item_cost: int = _lib.FUSED_ITEM_COST, stream=None):
+             item_cost: int = _lib.FUSED_ITEM_COST, tail_den: int = _lib.FUSED_TAIL_DEN,
+             tail_chunk: int = _lib.FUSED_TAIL_CHUNK, stream=None):
         """The whole hot path of one decode step; returns the bf16 output tensor."""
         if self.w.has_prologue:
             self.prologue(stream)
         if sched == "balanced":
-            self.plan(min_tiles, item_cost, stream)
+            self.plan(min_tiles, item_cost, tail_den, tail_chunk, stream)
         self.attend(sched, stream)
         return self.out
 
@@ -99,9 +102,10 @@ class DeviceStep:
         ws = self.plan_ws.cpu().numpy().view(np.int32)
         hdr = ws[lay["header"] // 4: lay["header"] // 4 + 16]
         Wp, N, S, nit, nm, npart = (int(x) for x in hdr[:6])
+        D, Ws = int(hdr[8]), int(hdr[9])
         g = lambda key, n: ws[lay[key] // 4: lay[key] // 4 + n].tolist()
-        return dict(Wp=Wp, N=N, S=S, n_items=nit, n_partials=npart, error=int(hdr[6]), W=int(hdr[7]),
-                    C=g("C", S + 1), worker_off=g("worker_off", Wp + 1), item_s=g("item_s", nit),
+        return dict(Wp=Wp, Ws=Ws, D=D, V=Ws + D, N=N, S=S, n_items=nit, n_partials=npart, error=int(hdr[6]),
+                    W=int(hdr[7]), C=g("C", S + 1), worker_off=g("worker_off", Ws + D + 1), item_s=g("item_s", nit),
                     item_t0=g("item_t0", nit), item_t1=g("item_t1", nit), item_split=g("item_split", nit),
                     item_slot=g("item_slot", nit), num_splits=g("num_splits", S),
                     partial_base=g("partial_base", S), merge_list=g("merge_list", nm))
@@ -116,7 +120,7 @@ class DeviceStep:
         w = self.w
         S = w.batch * w.hkv
         W = self.last_workers
-        base = (W + S) * (w.hq // w.hkv) * (128 + 2) * 4
+        base = (5 * W + S) * (w.hq // w.hkv) * (128 + 2) * 4     # after the partial slots
         raw = self.partial_ws[base:].cpu().numpy()
         n = (W + S) * _lib.TRACE_WAVES * _lib.TRACE_WORDS
         return raw[: n * 8].view(np.uint64).reshape(W + S, _lib.TRACE_WAVES, _lib.TRACE_WORDS)

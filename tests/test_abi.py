@@ -50,27 +50,29 @@ def test_descriptor_validation(L, field, value, status):
 def test_workspace_sizes_and_layout(L):
     d = _desc()
     lay = _lib.hpa_plan_workspace_layout(d, 512)
-    assert lay["max_items"] == 512 + 4
+    assert lay["max_items"] == 5 * 512 + 4        # at most 4 W tail chunks
     offs = [lay[k] for k in ("header", "C", "worker_off", "item_s", "item_t0", "item_t1", "item_split",
                              "item_slot", "num_splits", "partial_base", "merge_list")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert _lib.hpa_plan_workspace_size(d, 512) == lay["total_bytes"]
-    # (W + S) slots x G heads x (128 acc + m + l) fp32
-    assert _lib.hpa_partial_workspace_size(d, 512) == (512 + 4) * 8 * (128 + 2) * 4
+    # (5 W + S) slots x G heads x (128 acc + m + l) fp32
+    assert _lib.hpa_partial_workspace_size(d, 512) == (5 * 512 + 4) * 8 * (128 + 2) * 4
 
 
 def test_calls_reject_bad_arguments_before_launching(L):
     d = _desc()
     with pytest.raises(_lib.HpaError) as e:
-        L_status = L.hpa_plan(ctypes.byref(d), None, 512, 1, 0, None, 0, None)
+        L_status = L.hpa_plan(ctypes.byref(d), None, 512, 1, 0, 0, 1, None, 0, None)
         _lib._check(L_status, "hpa_plan")
     assert e.value.status == 1
     # undersized plan workspace -> HPA_ERR_WORKSPACE, nothing launched
     fake = ctypes.c_void_p(0x1000)
-    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, fake, 16, None) == 3
-    assert L.hpa_plan(ctypes.byref(d), fake, 512, 0, 0, fake, 1 << 30, None) == 1     # min_tiles < 1
-    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, -1, fake, 1 << 30, None) == 1    # item cost < 0
-    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 65, fake, 1 << 30, None) == 1    # item cost > 64
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, 0, 1, fake, 16, None) == 3
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 0, 0, 0, 1, fake, 1 << 30, None) == 1     # min_tiles < 1
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, -1, 0, 1, fake, 1 << 30, None) == 1    # item cost < 0
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 65, 0, 1, fake, 1 << 30, None) == 1    # item cost > 64
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, -1, 1, fake, 1 << 30, None) == 1    # tail_den < 0
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, 8, 0, fake, 1 << 30, None) == 1     # tail_chunk < 1
     # balanced attention without a plan, fp8 without scales
     args = [fake] * 7
     assert L.hpa_decode_attn(ctypes.byref(d), 0, *args, 512, None, 0, fake, 1 << 30, fake, 0, None) == 1

@@ -33,7 +33,7 @@ def gpu():
     return torch.device("cuda")
 
 
-def device_plan(lens, hkv, W, min_tiles, item_cost=0):
+def device_plan(lens, hkv, W, min_tiles, item_cost=0, tail_den=0, tail_chunk=1):
     """Run the GPU planner on a length vector; return its arrays as host lists."""
     B = len(lens)
     maxp = max(1, max([(int(L) + 63) // 64 for L in lens] or [1]))
@@ -41,40 +41,42 @@ def device_plan(lens, hkv, W, min_tiles, item_cost=0):
     size = _lib.hpa_plan_workspace_size(desc, W)
     ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
     sl = torch.tensor(np.asarray(lens, np.int32), device="cuda")
-    _lib.hpa_plan(desc, sl, W, min_tiles, item_cost, ws)
+    _lib.hpa_plan(desc, sl, W, min_tiles, item_cost, tail_den, tail_chunk, ws)
     torch.cuda.synchronize()
     lay = _lib.hpa_plan_workspace_layout(desc, W)
     h = ws.cpu().numpy().view(np.int32)
     hdr = h[:16]
     Wp, N, S, nit, nm, npart = (int(x) for x in hdr[:6])
+    D, Ws = int(hdr[8]), int(hdr[9])
     g = lambda k, n: h[lay[k] // 4: lay[k] // 4 + n].tolist()
-    return dict(Wp=Wp, N=N, S=S, n_items=nit, n_partials=npart, err=int(hdr[6]),
-                C=g("C", S + 1), worker_off=g("worker_off", Wp + 1), item_s=g("item_s", nit),
+    return dict(Wp=Wp, Ws=Ws, D=D, N=N, S=S, n_items=nit, n_partials=npart, err=int(hdr[6]),
+                C=g("C", S + 1), worker_off=g("worker_off", Ws + D + 1), item_s=g("item_s", nit),
                 item_t0=g("item_t0", nit), item_t1=g("item_t1", nit), item_split=g("item_split", nit),
                 item_slot=g("item_slot", nit), num_splits=g("num_splits", S),
                 partial_base=g("partial_base", S), merge_list=g("merge_list", nm))
 
 
-def check_plan(lens, hkv, W, mt, cost=0):
-    got = device_plan(lens, hkv, W, mt, cost)
-    want = op.balanced_plan(lens, hkv, W, mt, cost)
+def check_plan(lens, hkv, W, mt, cost=0, den=0, chunk=1):
+    got = device_plan(lens, hkv, W, mt, cost, den, chunk)
+    want = op.balanced_plan(lens, hkv, W, mt, cost, den, chunk)
     assert got["err"] == 0
-    for k in ("Wp", "N", "n_items", "n_partials") + PLAN_KEYS:
-        assert got[k] == want[k], (k, lens, hkv, W, mt)
+    for k in ("Wp", "Ws", "D", "N", "n_items", "n_partials") + PLAN_KEYS:
+        assert got[k] == want[k], (k, lens, hkv, W, mt, cost, den, chunk)
 
 
 # ---------------------------------------------------------------- planner ---
 
+@pytest.mark.parametrize("tail", [(0, 1), (8, 8), (3, 1)])
 @pytest.mark.parametrize("cost", [0, 3])
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("W,mt", [(0, 1), (1, 1), (7, 1), (512, 1), (512, 4), (1024, 1), (3000, 2)])
-def test_plan_bit_exact_workload_lengths(cfg, W, mt, cost):
+def test_plan_bit_exact_workload_lengths(cfg, W, mt, cost, tail):
     lens = inputs.config_lengths_only(cfg) + (1 if cfg == 4 else 0)
     hkv = 4 if cfg == 3 else 1
     if W == 0:
         W = _lib.hpa_default_num_workers(0)
-    print(f"plan cfg{cfg} W={W} mt={mt} cost={cost}", flush=True)
-    check_plan(lens.tolist(), hkv, W, mt, cost)
+    print(f"plan cfg{cfg} W={W} mt={mt} cost={cost} tail={tail}", flush=True)
+    check_plan(lens.tolist(), hkv, W, mt, cost, *tail)
 
 
 def test_plan_bit_exact_random_lengths():
@@ -89,12 +91,18 @@ def test_plan_bit_exact_random_lengths():
         W = int(rng.integers(1, 4000))
         mt = int(rng.integers(1, 6))
         cost = int(rng.integers(0, 6)) if trial % 2 else 0
-        check_plan(lens.tolist(), hkv, W, mt, cost)
+        den = int(rng.integers(1, 17)) if trial % 3 else 0
+        chunk = int(rng.integers(1, 40))
+        check_plan(lens.tolist(), hkv, W, mt, cost, den, chunk)
     check_plan([0, 0, 0], 2, 16, 1)              # N == 0: no active workers
     check_plan([0, 0, 0], 2, 16, 1, 4)
     check_plan([5000], 1, 100000 // 64, 1)       # W > N tiles
     check_plan([64, 64], 1, 4, 1, 2)             # workers owning only virtual tiles get no item
     check_plan([64] * 40, 1, 300, 1, 64)         # the largest cost
+    check_plan([192], 1, 4, 1, 0, 2, 1)          # fewer static workers than active ones
+    check_plan([5000, 64, 0, 3000], 2, 9, 1, 2, 1, 1)   # everything in the tail, 4 W chunks
+    check_plan([5000, 64, 0, 3000], 2, 9, 1, 2, 1, 1000)  # everything in one chunk
+    check_plan([0, 0], 1, 9, 1, 0, 4, 2)         # N == 0 with a tail
 
 
 # -------------------------------------------------------------- attention ---
@@ -277,7 +285,7 @@ def test_device_errors_are_reported_not_faulted():
     torch.cuda.synchronize()
     assert d.device_error(clear=True) & _lib.DEVERR_SEQ_LEN
     # attention launched with a different worker count than the plan
-    _lib.hpa_plan(d.desc, d.seq_lens, 5, 1, 0, d.plan_ws)
+    _lib.hpa_plan(d.desc, d.seq_lens, 5, 1, 0, 0, 1, d.plan_ws)
     d.attend("balanced")
     torch.cuda.synchronize()
     assert d.device_error(clear=True) & _lib.DEVERR_PLAN
@@ -322,6 +330,57 @@ def test_single_launch_merge_counters_reset_across_steps():
     d.step("single")
     torch.cuda.synchronize()
     assert torch.equal(d.out, want2)
+    assert d.device_error() == 0
+
+
+@pytest.mark.parametrize("tail", [(0, 1), (1, 1), (2, 3), (8, 8), (4, 1000)])
+def test_planned_dynamic_tails_against_oracle(tail):
+    """Any dynamic tail (none, the whole list claimed tile by tile, one chunk, ...) gives
+    the oracle's output; the fused schedules (which use their own fixed tail) agree with
+    the planner run with theirs."""
+    from load_balanced_split_amd.runner import DeviceStep
+    w = inputs.build_workload("tail", [9000, 64, 3000, 1, 0, 700, 130, 4096], 8, 2, "bf16", seed=21, poison=True)
+    ref = oracle_out(w)
+    for W in (1, 7, 40):
+        d = DeviceStep(w, num_workers=W)
+        print(f"tail {tail} W={W}", flush=True)
+        d.step("balanced", tail_den=tail[0], tail_chunk=tail[1])
+        torch.cuda.synchronize()
+        assert d.device_error() == 0
+        assert_within(d.output_f64(), ref, "bf16", f"tail {tail} W={W}")
+        pa = d.plan_arrays()
+        want = op.balanced_plan(w.seq_lens.tolist(), w.hkv, W, _lib.FUSED_MIN_TILES, _lib.FUSED_ITEM_COST, *tail)
+        assert (pa["Ws"], pa["D"], pa["n_items"]) == (want["Ws"], want["D"], want["n_items"])
+
+
+def test_tail_claim_counters_reset_across_launches():
+    """Tail chunks are claimed on a counter in the plan workspace that the last workgroup
+    returns to zero: repeated launches on one plan (no planner call in between) keep
+    giving the same bits, and so do the fused schedules when they plan with a tail."""
+    from load_balanced_split_amd.runner import DeviceStep
+    w = inputs.build_workload("claims", [20000, 64, 3000, 1, 700, 129], 8, 2, "fp8", seed=13)
+    d = DeviceStep(w, num_workers=31)
+    d.step("balanced", tail_den=3, tail_chunk=2)
+    torch.cuda.synchronize()
+    want = d.out.clone()
+    assert d.plan_arrays()["D"] > 0
+    for rep in range(4):
+        d.out.zero_()
+        d.attend("balanced")
+        torch.cuda.synchronize()
+        assert torch.equal(d.out, want), rep
+    assert d.device_error() == 0
+    if _lib.FUSED_TAIL_DEN == 0:
+        return
+    d.step("balanced")
+    torch.cuda.synchronize()
+    want = d.out.clone()
+    for rep in range(3):
+        for sched in ("fused", "single", "balanced"):
+            d.out.zero_()
+            d.attend(sched)
+            torch.cuda.synchronize()
+            assert torch.equal(d.out, want), (rep, sched)
     assert d.device_error() == 0
 
 
