@@ -521,30 +521,52 @@ struct Worker {
         *reinterpret_cast<f32x4*>(&lds.o[wave][m16][16 * n + 4 * j]) = o[n];
     }
     __syncthreads();
-    // a fixed trip count keeps the number of stores static, so the wait for the
-    // next item's first unit (issued before this combine) stays exact
+    // thread t combines dims d0 .. d0 + 3 of head (t / 32) (+ 8 per pass): all of a
+    // pass's LDS reads are issued before the first is used, and each output is one
+    // 8-byte (bf16 row) or 16-byte (partial) store
+    constexpr int kQuads = kHeadDim / 4, kHeadsPerPass = kAttnThreads / kQuads;
+    const int d0 = 4 * (threadIdx.x % kQuads);
 #pragma unroll
-    for (int r = 0; r < kMaxGroup * kHeadDim / kAttnThreads; ++r) {
-      const int idx = threadIdx.x + r * kAttnThreads;
-      if (!st.valid || idx >= a.group * kHeadDim) break;
-      const int hh = idx >> 7, d = idx & (kHeadDim - 1);
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds.m[w][hh]);
-      float Ls = 0.f, acc = 0.f;
+    for (int pass = 0; pass < kMaxGroup / kHeadsPerPass; ++pass) {
+      const int hh = pass * kHeadsPerPass + static_cast<int>(threadIdx.x / kQuads);
+      if (!st.valid || hh >= a.group) break;
+      float mw[kWaves], lw[kWaves];
+      f32x4 ow[kWaves];
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float f = __builtin_amdgcn_exp2f(lds.m[w][hh] - M);   // 0 for idle waves
-        Ls += f * lds.l[w][hh];
-        acc += f * lds.o[w][hh][d];
+        mw[w] = lds.m[w][hh];
+        lw[w] = lds.l[w][hh];
+        ow[w] = *reinterpret_cast<const f32x4*>(&lds.o[w][hh][d0]);
       }
-      acc *= st.vscale;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
+      float Ls = 0.f;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(mw[w] - M);   // 0 for idle waves
+        Ls += f * lw[w];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += f * ow[w][e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] *= st.vscale;
       if (st.it.slot < 0) {
-        a.out[(int64_t(st.b) * a.hq + st.g * a.group + hh) * kHeadDim + d] = f32_to_bf16_rne(acc / Ls);
+        uint2 packed;
+        packed.x = f32_to_bf16_rne(acc[0] / Ls) | (uint32_t(f32_to_bf16_rne(acc[1] / Ls)) << 16);
+        packed.y = f32_to_bf16_rne(acc[2] / Ls) | (uint32_t(f32_to_bf16_rne(acc[3] / Ls)) << 16);
+        *reinterpret_cast<uint2*>(a.out + (int64_t(st.b) * a.hq + st.g * a.group + hh) * kHeadDim + d0) = packed;
       } else {
         const int64_t sl = st.it.slot;
-        store_partial(a.part_acc + (sl * a.group + hh) * kHeadDim + d, acc);
-        if (d == 0) {
+        float* pa = a.part_acc + (sl * a.group + hh) * kHeadDim + d0;
+        if (INMERGE) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) store_partial(pa + e, acc[e]);
+        } else {
+          *reinterpret_cast<f32x4*>(pa) = acc;
+        }
+        if (d0 == 0) {
           store_partial(a.part_m + sl * a.group + hh, M);
           store_partial(a.part_l + sl * a.group + hh, Ls);
         }
