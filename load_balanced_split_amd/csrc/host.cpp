@@ -42,6 +42,9 @@ hpa_status check_desc(const hpa_attn_desc* d) {
   if (int64_t(d->max_pages_per_seq) * hpa::kPage > INT32_MAX / 2)
     return fail(HPA_ERR_INVALID_ARG, "max_pages_per_seq %d too large", d->max_pages_per_seq);
   if (d->num_pages < 0) return fail(HPA_ERR_INVALID_ARG, "num_pages %d < 0", d->num_pages);
+  if (int64_t(d->batch) * d->num_kv_heads > hpa::kMaxSeqs)
+    return fail(HPA_ERR_INVALID_ARG, "batch x num_kv_heads %lld > %lld", (long long)(int64_t(d->batch) * d->num_kv_heads),
+                (long long)hpa::kMaxSeqs);
   if (d->kv_dtype != HPA_KV_BF16 && d->kv_dtype != HPA_KV_FP8_E4M3)
     return fail(HPA_ERR_INVALID_ARG, "kv_dtype %d", static_cast<int>(d->kv_dtype));
   if (!(d->sm_scale > 0.f)) return fail(HPA_ERR_INVALID_ARG, "sm_scale must be > 0");
@@ -63,6 +66,8 @@ bool is_static(hpa_sched s) { return s == HPA_SCHED_STATIC_SPLITS || s == HPA_SC
 // largest default over all schedules (workspace sizing).
 hpa_status resolve_workers(int32_t requested, int sched, int32_t* out) {
   if (requested < 0) return fail(HPA_ERR_INVALID_ARG, "num_workers %d < 0", requested);
+  if (requested > hpa::kMaxWorkers)
+    return fail(HPA_ERR_INVALID_ARG, "num_workers %d > %lld", requested, (long long)hpa::kMaxWorkers);
   if (requested > 0) {
     *out = requested;
     return HPA_OK;
@@ -130,18 +135,18 @@ hpa_status hpa_plan_workspace_layout(const hpa_attn_desc* desc, int32_t num_work
   int32_t W = 0;
   if ((st = resolve_workers(num_workers, -1, &W)) != HPA_OK) return st;
   const hpa::PlanOffsets o = hpa::plan_offsets(int64_t(desc->batch) * desc->num_kv_heads, W);
-  layout->header = o.header * 4;
-  layout->C = o.C * 4;
-  layout->worker_off = o.worker_off * 4;
-  layout->item_s = o.item_s * 4;
-  layout->item_t0 = o.item_t0 * 4;
-  layout->item_t1 = o.item_t1 * 4;
-  layout->item_split = o.item_split * 4;
-  layout->item_slot = o.item_slot * 4;
-  layout->num_splits = o.num_splits * 4;
-  layout->partial_base = o.partial_base * 4;
-  layout->merge_list = o.merge_list * 4;
-  layout->total_bytes = o.total * 4;
+  layout->header = size_t(o.header) * 4;
+  layout->C = size_t(o.C) * 4;
+  layout->worker_off = size_t(o.worker_off) * 4;
+  layout->item_s = size_t(o.item_s) * 4;
+  layout->item_t0 = size_t(o.item_t0) * 4;
+  layout->item_t1 = size_t(o.item_t1) * 4;
+  layout->item_split = size_t(o.item_split) * 4;
+  layout->item_slot = size_t(o.item_slot) * 4;
+  layout->num_splits = size_t(o.num_splits) * 4;
+  layout->partial_base = size_t(o.partial_base) * 4;
+  layout->merge_list = size_t(o.merge_list) * 4;
+  layout->total_bytes = size_t(o.total) * 4;
   layout->max_items = o.max_items;
   return HPA_OK;
 }
@@ -181,8 +186,8 @@ hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t 
   int32_t W = 0;
   if ((st = resolve_workers(num_workers, HPA_SCHED_BALANCED, &W)) != HPA_OK) return st;
   const hpa::PlanOffsets o = hpa::plan_offsets(int64_t(desc->batch) * desc->num_kv_heads, W);
-  if (plan_ws_bytes < static_cast<size_t>(o.total * 4))
-    return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)(o.total * 4));
+  if (plan_ws_bytes < size_t(o.total) * 4)
+    return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)o.total * 4);
   if (hpa::launch_plan(seq_lens, desc->batch, desc->num_kv_heads, desc->max_pages_per_seq, W,
                        min_tiles_per_worker, item_cost, tail_den, tail_chunk, static_cast<int32_t*>(plan_ws), o,
                        stream) != hipSuccess)
@@ -223,10 +228,10 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   const hpa::PlanOffsets po = hpa::plan_offsets(S, W);
   if (sched == HPA_SCHED_BALANCED || sched == HPA_SCHED_BALANCED_FUSED || sched == HPA_SCHED_BALANCED_SINGLE) {
     if (!plan_ws) return fail(HPA_ERR_INVALID_ARG, "balanced schedules need plan_ws");
-    if (plan_ws_bytes < static_cast<size_t>(po.total * 4))
-      return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)(po.total * 4));
-  } else if (plan_ws && plan_ws_bytes < static_cast<size_t>(po.total * 4)) {
-    return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)(po.total * 4));
+    if (plan_ws_bytes < size_t(po.total) * 4)
+      return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)po.total * 4);
+  } else if (plan_ws && plan_ws_bytes < size_t(po.total) * 4) {
+    return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)po.total * 4);
   }
 
   hpa::AttnArgs a{};

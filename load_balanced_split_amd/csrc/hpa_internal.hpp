@@ -54,8 +54,13 @@ enum : int {
 };
 
 // Offsets of the plan arrays, in int32 elements.
+// Offsets are int32 (kernel arguments are read at launch, so they are kept small):
+// with at most kMaxSeqs sequences and kMaxWorkers workers the plan stays far below
+// 2^31 ints.
+constexpr int64_t kMaxSeqs = int64_t(1) << 24;      // batch x KV heads
+constexpr int64_t kMaxWorkers = int64_t(1) << 20;
 struct PlanOffsets {
-  int64_t header, C, worker_off, item_s, item_t0, item_t1, item_split, item_slot,
+  int32_t header, C, worker_off, item_s, item_t0, item_t1, item_split, item_slot,
           num_splits, partial_base, merge_list, ne, gctr, sctr, qctr, total;
   int32_t max_items;
 };
@@ -69,28 +74,28 @@ inline PlanOffsets plan_offsets(int64_t S, int64_t W) {
   auto al = [](int64_t x) { return (x + 63) & ~int64_t(63); };   // 256-byte aligned arrays
   const int64_t V = (1 + kTailChunksPerWorker) * W;                // virtual workers, at most
   const int64_t mi = V + S;
-  int64_t p = 0;
-  o.header = p;       p += al(kHeaderInts);
-  o.C = p;            p += al(S + 1);
-  o.worker_off = p;   p += al(V + 1);
-  o.item_s = p;       p += al(mi);
-  o.item_t0 = p;      p += al(mi);
-  o.item_t1 = p;      p += al(mi);
-  o.item_split = p;   p += al(mi);
-  o.item_slot = p;    p += al(mi);
-  o.num_splits = p;   p += al(S);
-  o.partial_base = p; p += al(S);
-  o.merge_list = p;   p += al(S);
-  o.ne = p;           p += al(S + 1);
+  int64_t p = 0;   // every value below fits in int32 for S <= kMaxSeqs, W <= kMaxWorkers
+  o.header = static_cast<int32_t>(p);       p += al(kHeaderInts);
+  o.C = static_cast<int32_t>(p);            p += al(S + 1);
+  o.worker_off = static_cast<int32_t>(p);   p += al(V + 1);
+  o.item_s = static_cast<int32_t>(p);       p += al(mi);
+  o.item_t0 = static_cast<int32_t>(p);      p += al(mi);
+  o.item_t1 = static_cast<int32_t>(p);      p += al(mi);
+  o.item_split = static_cast<int32_t>(p);   p += al(mi);
+  o.item_slot = static_cast<int32_t>(p);    p += al(mi);
+  o.num_splits = static_cast<int32_t>(p);   p += al(S);
+  o.partial_base = static_cast<int32_t>(p); p += al(S);
+  o.merge_list = static_cast<int32_t>(p);   p += al(S);
+  o.ne = static_cast<int32_t>(p);           p += al(S + 1);
   // arrival counters of the in-kernel merge (fused schedule): one per split group,
   // indexed by the group's first partial slot, and one per sequence; each is
   // returned to 0 by the workgroup that sees the last arrival
-  o.gctr = p;         p += al(mi);
-  o.sctr = p;         p += al(S);
+  o.gctr = static_cast<int32_t>(p);         p += al(mi);
+  o.sctr = static_cast<int32_t>(p);         p += al(S);
   // dynamic tail: chunks claimed so far, workgroups finished; the last workgroup to
   // finish returns both to 0 (the planner clears them too)
-  o.qctr = p;         p += al(2);
-  o.total = p;
+  o.qctr = static_cast<int32_t>(p);         p += al(2);
+  o.total = static_cast<int32_t>(p);
   o.max_items = static_cast<int32_t>(mi);
   return o;
 }

@@ -73,6 +73,12 @@ def test_calls_reject_bad_arguments_before_launching(L):
     assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 65, 0, 1, fake, 1 << 30, None) == 1    # item cost > 64
     assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, -1, 1, fake, 1 << 30, None) == 1    # tail_den < 0
     assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, 8, 0, fake, 1 << 30, None) == 1     # tail_chunk < 1
+    # sizes beyond the 32-bit plan offsets: more than 2^20 workers, 2^24 sequences
+    n = ctypes.c_size_t(0)
+    assert L.hpa_plan_workspace_size(ctypes.byref(d), (1 << 20) + 1, ctypes.byref(n)) == 1
+    assert L.hpa_plan(ctypes.byref(d), fake, (1 << 20) + 1, 1, 0, 0, 1, fake, 1 << 30, None) == 1
+    big = _desc(batch=1 << 22, num_q_heads=8, num_kv_heads=8)
+    assert L.hpa_plan_workspace_size(ctypes.byref(big), 512, ctypes.byref(n)) == 1
     # balanced attention without a plan, fp8 without scales
     args = [fake] * 7
     assert L.hpa_decode_attn(ctypes.byref(d), 0, *args, 512, None, 0, fake, 1 << 30, fake, 0, None) == 1
