@@ -1093,32 +1093,51 @@ constexpr int kMergeDims = kHeadDim;
 constexpr int kMergeQuads = kMergeDims / 4;
 constexpr int kMergeLanes = kMergeThreads / kMergeQuads;
 
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int mode) {
+// The merge kernel's own arguments: everything it reads, in two 64-byte lines, so
+// the launch arguments cost one round trip.
+struct MergeArgs {
+  const int32_t* seq_lens;
+  const int32_t* plan;
+  const float* part_acc;
+  const float* part_m;
+  const float* part_l;
+  uint16_t* out;
+  int num_splits, partial_base, header;   // plan offsets (int32 words)
+  int hkv, hq, group, max_pages, workers;
+  int slots, static_splits, static_chunk;
+};
+
+template <MergeMode MODE>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   __shared__ float gm[kMergeLanes], gl[kMergeLanes];
   __shared__ f32x4 gacc[kMergeLanes][kMergeQuads];
   const int hh = blockIdx.y, d0 = blockIdx.z * kMergeDims;
   const int s = blockIdx.x;
-  // every fact this block needs is one scalar load away from its sequence index
+  // every fact this block needs is one scalar load away from its sequence index,
+  // and all of those loads go out together
   const int L = sload(a.seq_lens, s / a.hkv);
-  int n, base;
-  if (mode == MERGE_STATIC) {
+  int n = 0, base = 0, planned_w = a.workers;
+  if constexpr (MODE != MERGE_STATIC) {
+    n = sload(a.plan, a.num_splits + s);
+    base = sload(a.plan, a.partial_base + s);
+    if constexpr (MODE == MERGE_PLAN) planned_w = sload(a.plan, a.header + H_W);
+  }
+  if constexpr (MODE == MERGE_STATIC) {
     if (L < 0 || L > a.max_pages * kPage) return;
     const int nt = (L + kPage - 1) / kPage;
     const int chunk = nt == 0 ? 1 : (a.static_chunk > 0 ? a.static_chunk : (nt + a.static_splits - 1) / a.static_splits);
     n = (nt + chunk - 1) / chunk;
     base = s * a.static_splits;
-  } else {
-    n = sload(a.plan, a.po.num_splits + s);
-    base = sload(a.plan, a.po.partial_base + s);
-    if (mode == MERGE_FUSED) {
-      // zero rows of empty requests were written by the attention kernel; the others
-      // read the split count and slot base recorded by their split-0 worker
-      if (L <= 0 || L > a.max_pages * kPage) return;
-    } else if (sload(a.plan, a.po.header + H_W) != a.workers) {
-      return;                               // a plan made for another launch shape
-    }
   }
-  if (n == 1 || n < 0 || (n > 1 && (base < 0 || base + n > a.slots))) return;
+  // One test on all loaded values (bitwise, not short-circuit), so that all three
+  // loads are issued before the first wait. Fused schedule: zero rows of empty
+  // requests were written by the attention kernel, the others read the split count
+  // and slot base recorded by their split-0 worker. Planned: skip a plan made for
+  // another launch shape.
+  bool skip = (n == 1) | (n < 0) | ((n > 1) & ((base < 0) | (base + n > a.slots)));
+  if constexpr (MODE == MERGE_FUSED) skip |= (L <= 0) | (L > a.max_pages * kPage);
+  if constexpr (MODE == MERGE_PLAN) skip |= planned_w != a.workers;
+  if (skip) return;
   const int b = s / a.hkv, g = s - b * a.hkv;
   uint16_t* orow = a.out + (int64_t(b) * a.hq + g * a.group + hh) * kHeadDim + d0;
   const int tid = threadIdx.x;
@@ -1224,8 +1243,17 @@ hipError_t launch_attn_fused(const AttnArgs& a, bool fp8, bool merge_in_kernel, 
 hipError_t launch_merge(const AttnArgs& a, MergeMode mode, hipStream_t stream) {
   const int S = a.batch * a.hkv;
   if (S == 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(S, a.group, kHeadDim / kMergeDims), dim3(kMergeThreads), 0, stream, a,
-                     static_cast<int>(mode));
+  const MergeArgs m{a.seq_lens, a.plan, a.part_acc, a.part_m, a.part_l, a.out,
+                    a.po.num_splits, a.po.partial_base, a.po.header,
+                    a.hkv, a.hq, a.group, a.max_pages, a.workers,
+                    static_cast<int>(a.slots), a.static_splits, a.static_chunk};
+  const dim3 grid(S, a.group, kHeadDim / kMergeDims);
+  if (mode == MERGE_PLAN)
+    hipLaunchKernelGGL(merge_kernel<MERGE_PLAN>, grid, dim3(kMergeThreads), 0, stream, m);
+  else if (mode == MERGE_FUSED)
+    hipLaunchKernelGGL(merge_kernel<MERGE_FUSED>, grid, dim3(kMergeThreads), 0, stream, m);
+  else
+    hipLaunchKernelGGL(merge_kernel<MERGE_STATIC>, grid, dim3(kMergeThreads), 0, stream, m);
   return hipGetLastError();
 }
 
