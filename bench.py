@@ -275,9 +275,13 @@ def main():
         eager[s] = copies[0].out.clone()
         assert copies[0].device_error() == 0
 
+    spread = {}
+
     def graph_time(sched):
         """Seconds per step: one HIP graph holds one step per copy (R steps), replayed
-        back to back, so host launch cost is paid once per R steps."""
+        back to back, so host launch cost is paid once per R steps. Also keeps the
+        10th/50th/90th percentile of the per-step time over the replays (HIP events
+        around each replay on the launch stream)."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for d in copies:
@@ -287,11 +291,17 @@ def main():
             g.replay()
         torch.cuda.synchronize()
         reps = max(1, args.steps // R)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         t0 = time.perf_counter()
+        ev[0].record(stream)
         for i in range(reps):
             g.replay()
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        per_step = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 / R for i in range(reps))
+        q = lambda f: per_step[min(len(per_step) - 1, int(f * len(per_step)))]
+        spread[sched] = [round(q(0.1), 2), round(q(0.5), 2), round(q(0.9), 2)]
         # every copy's graph output equals the eager output, bit for bit
         for d in copies:
             assert torch.equal(d.out, eager[sched]), f"graph replay of {sched} differs from eager"
@@ -299,8 +309,9 @@ def main():
         return (t1 - t0) / (reps * R)
 
     def kernel_times(sched):
-        """Average duration (ms) of each launch kind, from HIP events on the launch stream
-        around a loop of back-to-back launches of that kind alone (rotating copies)."""
+        """Average duration (ms) of each launch kind: HIP events on the launch stream
+        around the replay of a graph of event_steps back-to-back launches of that kind
+        alone (rotating copies), so that short kernels are not bound by host submission."""
         kinds = (["prologue"] if w.has_prologue else []) + (["plan"] if sched == "balanced" else [])
         kinds += ["attn"] if sched == "single" else ["attn", "merge"]    # single: one launch merges too
         launch = {
@@ -313,13 +324,20 @@ def main():
         for kind in kinds:
             for i in range(R):
                 launch[kind](copies[i])
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(args.event_steps):
+                    launch[kind](copies[i % R])
+            g.replay()
+            torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for i in range(args.event_steps):
-                launch[kind](copies[i % R])
+            g.replay()
             e1.record(stream)
             torch.cuda.synchronize()
             res[kind] = e0.elapsed_time(e1) / args.event_steps
+            del g
         for d in copies:
             assert torch.equal(d.out, eager[sched])
         return res
@@ -351,9 +369,12 @@ def main():
                    "rotating_copies": R, "kv_bytes": kv_bytes,
                    "algorithmic_bytes": alg_bytes},
         "us_per_step": round(us, 2),
+        "us_per_step_p10_p50_p90": spread[head],
         "kv_frac_of_peak": round(kv_gbps / PEAK_HBM_GBPS, 4),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in ev.items()},
         "attn_plus_merge_kv_gbps": round(kv_bytes / ((ev["attn"] + ev.get("merge", 0.0)) * 1e-3) / 1e9, 1),
+        "attn_plus_merge_kv_frac": round(kv_bytes / ((ev["attn"] + ev.get("merge", 0.0)) * 1e-3) / 1e9
+                                         / PEAK_HBM_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": attn_kernel_name(head, w.kv_dtype),
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
