@@ -88,6 +88,11 @@ __device__ inline u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), POLICY);
 }
 
+template <int POLICY = kPolicyDefault>
+__device__ inline float bload_f32(rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), 0, POLICY));
+}
+
 __device__ inline int bload_i32(rsrc_t r, uint32_t soff) {
   return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(r, 0, static_cast<int>(soff), 0));
 }
@@ -578,13 +583,11 @@ struct Worker {
 
   // Partials are read by other workgroups in the in-kernel merge: there every
   // access to them is device-coherent (sc1: the compiler's agent-scope atomic
-  // store/load), so no L2-wide write-back or invalidate is ever needed.
+  // store here, sc1 buffer loads in arrive()), so no L2-wide write-back or
+  // invalidate is ever needed.
   __device__ static void store_partial(float* p, float v) {
     if (INMERGE) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else *p = v;
-  }
-  __device__ static float load_partial(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // In-kernel merge of split sequences (fused schedule). A split's partial is
@@ -620,7 +623,12 @@ struct Worker {
     const int ngrp = (n + kMergeGroup - 1) / kMergeGroup;
     if (count_in(a.gctr + gslot) != gsize - 1) return;
     if (threadIdx.x == 0) __hip_atomic_store(a.gctr + gslot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Partials are read with device-coherent (sc1) buffer loads -- what the relaxed
+    // agent-scope atomic loads compile to, without their ordering: every load of a
+    // fold goes out before the first is used.
     const rsrc_t racc = make_rsrc(a.part_acc, static_cast<uint32_t>(int64_t(a.slots) * G * kHeadDim * 4));
+    const rsrc_t rm = make_rsrc(a.part_m, static_cast<uint32_t>(int64_t(a.slots) * G * 4));
+    const rsrc_t rl = make_rsrc(a.part_l, static_cast<uint32_t>(int64_t(a.slots) * G * 4));
     // one thread per (head, 4-dim quad)
     for (int idx = threadIdx.x; idx < G * (kHeadDim / 4); idx += kAttnThreads) {
       const int hh = idx / (kHeadDim / 4), q4 = idx % (kHeadDim / 4);
@@ -629,8 +637,8 @@ struct Worker {
 #pragma unroll
       for (int i = 0; i < kMergeGroup; ++i) {
         const int64_t r = int64_t(gslot + min(i, gsize - 1)) * G + hh;   // in bounds; extra ones unused
-        mk[i] = load_partial(a.part_m + r);
-        lk[i] = load_partial(a.part_l + r);
+        mk[i] = bload_f32<kPolicyAgent>(rm, static_cast<uint32_t>(r * 4));
+        lk[i] = bload_f32<kPolicyAgent>(rl, static_cast<uint32_t>(r * 4));
         ak[i] = __builtin_bit_cast(f32x4, bload16<kPolicyAgent>(racc, static_cast<uint32_t>((r * kHeadDim + 4 * q4) * 4), 0));
       }
       float M = -INFINITY, L = 0.f;
@@ -657,14 +665,25 @@ struct Worker {
     if (ngrp == 1) return;
     if (count_in(a.sctr + st.it.s) != ngrp - 1) return;
     if (threadIdx.x == 0) __hip_atomic_store(a.sctr + st.it.s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    constexpr int kFoldBatch = 8;     // group results loaded together, then folded in order
     for (int idx = threadIdx.x; idx < G * (kHeadDim / 4); idx += kAttnThreads) {
       const int hh = idx / (kHeadDim / 4), q4 = idx % (kHeadDim / 4);
       float FM = -INFINITY, FL = 0.f;
       f32x4 FA = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int g = 0; g < ngrp; ++g) {
-        const int64_t r = int64_t(pb + g * kMergeGroup) * G + hh;
-        const f32x4 ag = __builtin_bit_cast(f32x4, bload16<kPolicyAgent>(racc, static_cast<uint32_t>((r * kHeadDim + 4 * q4) * 4), 0));
-        fold(FM, FL, FA, load_partial(a.part_m + r), load_partial(a.part_l + r), ag);
+      for (int g0 = 0; g0 < ngrp; g0 += kFoldBatch) {
+        float mg[kFoldBatch], lg[kFoldBatch];
+        f32x4 ag[kFoldBatch];
+#pragma unroll
+        for (int i = 0; i < kFoldBatch; ++i) {
+          const int g = min(g0 + i, ngrp - 1);                          // in bounds; extra ones unused
+          const int64_t r = int64_t(pb + g * kMergeGroup) * G + hh;
+          mg[i] = bload_f32<kPolicyAgent>(rm, static_cast<uint32_t>(r * 4));
+          lg[i] = bload_f32<kPolicyAgent>(rl, static_cast<uint32_t>(r * 4));
+          ag[i] = __builtin_bit_cast(f32x4, bload16<kPolicyAgent>(racc, static_cast<uint32_t>((r * kHeadDim + 4 * q4) * 4), 0));
+        }
+#pragma unroll
+        for (int i = 0; i < kFoldBatch; ++i)
+          if (g0 + i < ngrp) fold(FM, FL, FA, mg[i], lg[i], ag[i]);
       }
       write_row(st, hh, q4, FL, FA);
     }
