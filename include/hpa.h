@@ -159,7 +159,7 @@ hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t 
 /* The item cost, minimum tiles per worker and dynamic tail the fused schedules
  * plan with; an hpa_plan call with these values gives their items exactly. */
 #define HPA_FUSED_ITEM_COST 4
-#define HPA_FUSED_MIN_TILES 1
+#define HPA_FUSED_MIN_TILES 12
 #define HPA_FUSED_TAIL_DEN 0
 #define HPA_FUSED_TAIL_CHUNK 1
 

@@ -107,7 +107,7 @@ def test_plan_bit_exact_random_lengths():
 
 # -------------------------------------------------------------- attention ---
 
-def run_and_compare(w, sched="balanced", W=0, min_tiles=1, ref=None, what=""):
+def run_and_compare(w, sched="balanced", W=0, min_tiles=_lib.FUSED_MIN_TILES, ref=None, what=""):
     from load_balanced_split_amd.runner import DeviceStep
     d = DeviceStep(w, num_workers=W)
     print(f"attn {what} {w.name} sched={sched} W={d.num_workers}", flush=True)
