@@ -951,6 +951,14 @@ struct RegPlan {
   __device__ void build(const AttnArgs& a, int S, int W, int lane) {
     int carry = 0;
     bool bad_lane = false;
+    // every chunk's lengths are requested before the first is used (one round trip);
+    // lanes past S read the last sequence's length (in bounds, S >= 1) and drop it
+    int Lraw[kRegPlanChunks];
+#pragma unroll
+    for (int k = 0; k < kRegPlanChunks; ++k) {
+      const int s = min(64 * k + lane, S - 1);
+      Lraw[k] = a.seq_lens[a.hkv == 1 ? s : s / a.hkv];
+    }
 #pragma unroll
     for (int k = 0; k < kRegPlanChunks; ++k) {
       L[k] = n[k] = C[k] = PB[k] = 0;
@@ -958,7 +966,7 @@ struct RegPlan {
       const int s = 64 * k + lane;
       int Lk = 0;
       if (s < S) {
-        Lk = a.seq_lens[a.hkv == 1 ? s : s / a.hkv];
+        Lk = Lraw[k];
         if (Lk < 0 || Lk > a.max_pages * kPage) {
           bad_lane = true;
           Lk = 0;
