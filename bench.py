@@ -312,9 +312,13 @@ def main():
         """Average duration (ms) of each launch kind: HIP events on the launch stream
         around the replay of a graph of event_steps back-to-back launches of that kind
         alone (rotating copies), so that short kernels are not bound by host submission."""
-        kinds = (["prologue"] if w.has_prologue else []) + (["plan"] if sched == "balanced" else [])
+        if w.has_prologue and sched == "balanced":
+            kinds = ["prologue+plan"]                                   # one launch (runner.step)
+        else:
+            kinds = (["prologue"] if w.has_prologue else []) + (["plan"] if sched == "balanced" else [])
         kinds += ["attn"] if sched == "single" else ["attn", "merge"]    # single: one launch merges too
         launch = {
+            "prologue+plan": lambda d: d.prologue_plan(),
             "prologue": lambda d: d.prologue(),
             "plan": lambda d: d.plan(),
             "attn": lambda d: d.attend(sched, flags=_lib.ATTN_NO_MERGE),

@@ -220,6 +220,27 @@ hpa_status hpa_decode_prologue(const hpa_attn_desc* desc, const void* q_in, cons
                                const float* k_scale, const float* v_scale, void* q_out,
                                int32_t* seq_lens_out, void* plan_ws, hipStream_t stream);
 
+/* Prologue and planner in one launch (bitbyai.com "vLLM × HPC-Ops …",
+ * "Breaking Down the Kernels": the prologue is fused to save launches, and the
+ * scheduler runs every step): everything hpa_decode_prologue does, plus the work
+ * list hpa_plan would make over seq_lens_out with the same parameters -- bit for
+ * bit, including for requests whose append fails (their length stays what
+ * seq_lens_out held). One extra workgroup plans from positions + 1 while the
+ * others append, so no launch waits for another; batches of more than 3072
+ * sequences plan in a second launch after the appends. Then run
+ * hpa_decode_attn(HPA_SCHED_BALANCED) with the same num_workers. Argument rules
+ * are those of the two calls; plan_ws is required and receives
+ * HPA_DEVERR_PROLOGUE and HPA_DEVERR_SEQ_LEN. */
+hpa_status hpa_decode_prologue_plan(const hpa_attn_desc* desc, const void* q_in, const void* k_in,
+                                    const void* v_in, const float* q_norm_w, const float* k_norm_w,
+                                    float eps, double rope_theta, const int32_t* positions,
+                                    const int32_t* page_table, void* k_cache, void* v_cache,
+                                    const float* k_scale, const float* v_scale, void* q_out,
+                                    int32_t* seq_lens_out, int32_t num_workers,
+                                    int32_t min_tiles_per_worker, int32_t item_cost, int32_t tail_den,
+                                    int32_t tail_chunk, void* plan_ws, size_t plan_ws_bytes,
+                                    hipStream_t stream);
+
 /* Synchronises the stream, then reads (and, if clear != 0, zeroes) the sticky
  * device error word of a plan workspace. */
 hpa_status hpa_read_device_error(void* plan_ws, int32_t* code, int32_t clear, hipStream_t stream);

@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
                                 _P, ctypes.c_size_t, _P, _I, _P],
             "hpa_decode_prologue": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
                                     _P, _P, _P, _P, _P, _P, _P, _P],
+            "hpa_decode_prologue_plan": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
+                                         _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P],
             "hpa_read_device_error": [_P, ctypes.POINTER(ctypes.c_int32), _I, _P],
             "hpa_status_string": [ctypes.c_int],
             "hpa_last_error_message": [],
@@ -187,6 +189,18 @@ def hpa_decode_prologue(desc, q_in, k_in, v_in, q_norm_w, k_norm_w, eps, rope_th
                                      _ptr(page_table), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                      _ptr(v_scale), _ptr(q_out), _ptr(seq_lens_out), _ptr(plan_ws),
                                      _stream(stream)), "hpa_decode_prologue")
+
+
+def hpa_decode_prologue_plan(desc, q_in, k_in, v_in, q_norm_w, k_norm_w, eps, rope_theta, positions,
+                             page_table, k_cache, v_cache, k_scale, v_scale, q_out, seq_lens_out, num_workers,
+                             min_tiles_per_worker, item_cost, tail_den, tail_chunk, plan_ws, stream=None):
+    _check(lib().hpa_decode_prologue_plan(ctypes.byref(desc), _ptr(q_in), _ptr(k_in), _ptr(v_in),
+                                          _ptr(q_norm_w), _ptr(k_norm_w), eps, rope_theta, _ptr(positions),
+                                          _ptr(page_table), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                          _ptr(v_scale), _ptr(q_out), _ptr(seq_lens_out), num_workers,
+                                          min_tiles_per_worker, item_cost, tail_den, tail_chunk, _ptr(plan_ws),
+                                          plan_ws.numel() * plan_ws.element_size(), _stream(stream)),
+           "hpa_decode_prologue_plan")
 
 
 def hpa_read_device_error(plan_ws, clear: bool = False, stream=None) -> int:

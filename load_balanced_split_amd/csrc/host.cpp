@@ -315,7 +315,46 @@ hpa_status hpa_decode_prologue(const hpa_attn_desc* desc, const void* q_in, cons
   if (hpa::launch_prologue(*desc, static_cast<const uint16_t*>(q_in), static_cast<const uint16_t*>(k_in),
                            static_cast<const uint16_t*>(v_in), q_norm_w, k_norm_w, eps, rope_theta, positions,
                            page_table, static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), k_scale,
-                           v_scale, static_cast<uint16_t*>(q_out), seq_lens_out, err, stream) != hipSuccess)
+                           v_scale, static_cast<uint16_t*>(q_out), seq_lens_out, err, nullptr, stream) != hipSuccess)
+    return fail(HPA_ERR_LAUNCH, "prologue launch failed");
+  return HPA_OK;
+}
+
+hpa_status hpa_decode_prologue_plan(const hpa_attn_desc* desc, const void* q_in, const void* k_in,
+                                    const void* v_in, const float* q_norm_w, const float* k_norm_w, float eps,
+                                    double rope_theta, const int32_t* positions, const int32_t* page_table,
+                                    void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+                                    void* q_out, int32_t* seq_lens_out, int32_t num_workers,
+                                    int32_t min_tiles_per_worker, int32_t item_cost, int32_t tail_den,
+                                    int32_t tail_chunk, void* plan_ws, size_t plan_ws_bytes, hipStream_t stream) {
+  hpa_status st = check_desc(desc);
+  if (st != HPA_OK) return st;
+  if (min_tiles_per_worker < 1) return fail(HPA_ERR_INVALID_ARG, "min_tiles_per_worker %d < 1", min_tiles_per_worker);
+  if (item_cost < 0 || item_cost > 64) return fail(HPA_ERR_INVALID_ARG, "item_cost %d outside [0, 64]", item_cost);
+  if (tail_den < 0) return fail(HPA_ERR_INVALID_ARG, "tail_den %d < 0", tail_den);
+  if (tail_chunk < 1) return fail(HPA_ERR_INVALID_ARG, "tail_chunk %d < 1", tail_chunk);
+  if (!plan_ws) return fail(HPA_ERR_INVALID_ARG, "plan_ws is NULL");
+  if (desc->batch == 0) return HPA_OK;
+  if (!q_in || !k_in || !v_in || !q_norm_w || !k_norm_w || !positions || !page_table || !k_cache || !v_cache ||
+      !q_out || !seq_lens_out)
+    return fail(HPA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (desc->kv_dtype == HPA_KV_FP8_E4M3 && (!k_scale || !v_scale))
+    return fail(HPA_ERR_INVALID_ARG, "E4M3 cache needs k_scale and v_scale");
+  if (static_cast<const void*>(positions) == static_cast<const void*>(seq_lens_out))
+    return fail(HPA_ERR_INVALID_ARG, "positions and seq_lens_out must not alias");
+  if (!(eps >= 0.f) || !(rope_theta > 0.0)) return fail(HPA_ERR_INVALID_ARG, "eps < 0 or rope_theta <= 0");
+  int32_t W = 0;
+  if ((st = resolve_workers(num_workers, HPA_SCHED_BALANCED, &W)) != HPA_OK) return st;
+  const hpa::PlanOffsets o = hpa::plan_offsets(int64_t(desc->batch) * desc->num_kv_heads, W);
+  if (plan_ws_bytes < size_t(o.total) * 4)
+    return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)o.total * 4);
+  int32_t* ws = static_cast<int32_t*>(plan_ws);
+  const hpa::PlanArgs pa{ws, o, W, min_tiles_per_worker, item_cost, tail_den, tail_chunk};
+  if (hpa::launch_prologue(*desc, static_cast<const uint16_t*>(q_in), static_cast<const uint16_t*>(k_in),
+                           static_cast<const uint16_t*>(v_in), q_norm_w, k_norm_w, eps, rope_theta, positions,
+                           page_table, static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), k_scale,
+                           v_scale, static_cast<uint16_t*>(q_out), seq_lens_out, ws + o.header + hpa::H_ERR, &pa,
+                           stream) != hipSuccess)
     return fail(HPA_ERR_LAUNCH, "prologue launch failed");
   return HPA_OK;
 }

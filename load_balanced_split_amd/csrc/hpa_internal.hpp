@@ -267,12 +267,18 @@ enum MergeMode : int { MERGE_PLAN = 0, MERGE_STATIC = 1, MERGE_FUSED = 2 };
 hipError_t launch_merge(const AttnArgs& a, MergeMode mode, hipStream_t stream);
 constexpr int kFusedMaxSeqs = 2048;  // sequences (B x Hkv) the fused schedule plans in LDS
 constexpr int kRegPlanSeqs = 256;    // up to this many, every wave plans in registers instead
+// The planner's arguments when the prologue launch also plans (hpa_decode_prologue_plan).
+struct PlanArgs {
+  int32_t* ws;
+  PlanOffsets po;
+  int workers, min_tiles, item_cost, tail_den, tail_chunk;
+};
 hipError_t launch_prologue(const hpa_attn_desc& d, const uint16_t* q_in, const uint16_t* k_in,
                            const uint16_t* v_in, const float* q_norm_w, const float* k_norm_w,
                            float eps, double rope_theta, const int32_t* positions,
                            const int32_t* page_table, uint8_t* k_cache, uint8_t* v_cache,
                            const float* k_scale, const float* v_scale, uint16_t* q_out,
-                           int32_t* seq_lens_out, int32_t* err_word, hipStream_t stream);
+                           int32_t* seq_lens_out, int32_t* err_word, const PlanArgs* plan, hipStream_t stream);
 hipError_t launch_clear_word(int32_t* word, hipStream_t stream);
 int attn_blocks_per_cu(bool fp8);         // persistent attention kernels
 int attn_static_blocks_per_cu(bool fp8);  // static split-KV attention kernel

@@ -7,11 +7,14 @@
 //
 // One workgroup per request; each wave takes whole head rows (Hq query rows,
 // Hkv key rows, Hkv value rows). Lane i owns the rotation pair (i, i + 64).
+// With PLAN, workgroup 0 runs the balanced planner (plan_block.hpp) over the
+// lengths after this launch's appends while workgroups 1..B append; it starts
+// first because it runs longest.
 // RMSNorm (Zhang & Sennrich 2019): y = x / sqrt(mean(x^2) + eps) * w, fp32.
 // RoPE (Su et al. 2021, rotate-half form): angle_i = pos * theta^(-i/64) is
 // formed and reduced modulo 2*pi in fp64 (positions reach 131072, where an fp32
 // angle would be off by ~0.016 rad); sine, cosine and the rotation are fp32.
-#include "hpa_internal.hpp"
+#include "plan_block.hpp"
 
 #include <cmath>
 
@@ -60,6 +63,24 @@ __device__ inline float wave_sum(float v) {
 // any of its arithmetic, so a pass costs one memory round trip).
 constexpr int kProRowsPerPass = 4;
 
+// Request b's live length once this launch's append is done: position + 1 when
+// the append is valid (the prologue writes exactly that to seq_lens_out), else the
+// unchanged seq_lens_out[b] (no workgroup writes it then) -- so the plan equals
+// hpa_plan over seq_lens_out bit for bit.
+struct LensAfterAppend {
+  const int32_t* positions;
+  const int32_t* page_table;
+  const int32_t* seq_lens_out;
+  int max_pages, num_pages;
+  __device__ int operator()(int b) const {
+    const int pos = positions[b];
+    int pid = -1;
+    if (pos >= 0 && pos < max_pages * kPage) pid = page_table[int64_t(b) * max_pages + pos / kPage];
+    return (pid >= 0 && pid < num_pages) ? pos + 1 : seq_lens_out[b];
+  }
+};
+
+template <bool PLAN>
 __global__ __launch_bounds__(kProThreads) void prologue_kernel(
     const uint16_t* __restrict__ q_in, const uint16_t* __restrict__ k_in,
     const uint16_t* __restrict__ v_in, const float* __restrict__ q_norm_w,
@@ -67,8 +88,16 @@ __global__ __launch_bounds__(kProThreads) void prologue_kernel(
     const int32_t* __restrict__ positions, const int32_t* __restrict__ page_table,
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, uint16_t* __restrict__ q_out, int32_t* __restrict__ seq_lens_out,
-    int32_t* err_word, int hq, int hkv, int max_pages, int num_pages, int fp8) {
-  const int b = blockIdx.x;
+    int32_t* err_word, int hq, int hkv, int max_pages, int num_pages, int fp8, PlanArgs pa) {
+  if constexpr (PLAN) {
+    if (blockIdx.x == 0) {
+      plan_block<kProThreads, true>(LensAfterAppend{positions, page_table, seq_lens_out, max_pages, num_pages},
+                                    static_cast<int>(gridDim.x) - 1, hkv, max_pages, pa.workers, pa.min_tiles,
+                                    pa.item_cost, pa.tail_den, pa.tail_chunk, pa.ws, pa.po);
+      return;
+    }
+  }
+  const int b = static_cast<int>(blockIdx.x) - (PLAN ? 1 : 0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kProWaves = kProThreads / 64;
   const int rows = hq + 2 * hkv;
@@ -165,13 +194,26 @@ hipError_t launch_prologue(const hpa_attn_desc& d, const uint16_t* q_in, const u
                            float eps, double rope_theta, const int32_t* positions,
                            const int32_t* page_table, uint8_t* k_cache, uint8_t* v_cache,
                            const float* k_scale, const float* v_scale, uint16_t* q_out,
-                           int32_t* seq_lens_out, int32_t* err_word, hipStream_t stream) {
+                           int32_t* seq_lens_out, int32_t* err_word, const PlanArgs* plan, hipStream_t stream) {
   if (d.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(prologue_kernel, dim3(d.batch), dim3(kProThreads), 0, stream, q_in, k_in, v_in,
-                     q_norm_w, k_norm_w, eps, rope_theta, positions, page_table, k_cache, v_cache,
-                     k_scale, v_scale, q_out, seq_lens_out, err_word, d.num_q_heads, d.num_kv_heads,
-                     d.max_pages_per_seq, d.num_pages, d.kv_dtype == HPA_KV_FP8_E4M3 ? 1 : 0);
-  return hipGetLastError();
+  const int fp8 = d.kv_dtype == HPA_KV_FP8_E4M3 ? 1 : 0;
+  const bool together = plan && int64_t(d.batch) * d.num_kv_heads <= kPlanLdsSeqs;
+  if (together) {
+    hipLaunchKernelGGL(prologue_kernel<true>, dim3(d.batch + 1), dim3(kProThreads), 0, stream, q_in, k_in, v_in,
+                       q_norm_w, k_norm_w, eps, rope_theta, positions, page_table, k_cache, v_cache, k_scale,
+                       v_scale, q_out, seq_lens_out, err_word, d.num_q_heads, d.num_kv_heads, d.max_pages_per_seq,
+                       d.num_pages, fp8, *plan);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(prologue_kernel<false>, dim3(d.batch), dim3(kProThreads), 0, stream, q_in, k_in, v_in,
+                     q_norm_w, k_norm_w, eps, rope_theta, positions, page_table, k_cache, v_cache, k_scale,
+                     v_scale, q_out, seq_lens_out, err_word, d.num_q_heads, d.num_kv_heads, d.max_pages_per_seq,
+                     d.num_pages, fp8, PlanArgs{});
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !plan) return e;
+  // batches too large for the planner's LDS arrays: plan after the appends instead
+  return launch_plan(seq_lens_out, d.batch, d.num_kv_heads, d.max_pages_per_seq, plan->workers, plan->min_tiles,
+                     plan->item_cost, plan->tail_den, plan->tail_chunk, plan->ws, plan->po, stream);
 }
 
 }  // namespace hpa

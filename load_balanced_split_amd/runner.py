@@ -63,6 +63,17 @@ class DeviceStep:
                                  self.v_cache, self.k_scale, self.v_scale, self.q_rot, self.lens_after,
                                  self.plan_ws, stream)
 
+    def prologue_plan(self, min_tiles: int = _lib.FUSED_MIN_TILES, item_cost: int = _lib.FUSED_ITEM_COST,
+                      tail_den: int = _lib.FUSED_TAIL_DEN, tail_chunk: int = _lib.FUSED_TAIL_CHUNK, stream=None):
+        """The prologue and the planner in one launch (the plan hpa_plan would make over
+        the lengths after the append)."""
+        w = self.w
+        _lib.hpa_decode_prologue_plan(self.desc, self.q_new, self.k_new, self.v_new, self.q_norm_w,
+                                      self.k_norm_w, w.eps, w.rope_theta, self.seq_lens, self.page_table,
+                                      self.k_cache, self.v_cache, self.k_scale, self.v_scale, self.q_rot,
+                                      self.lens_after, self.num_workers, min_tiles, item_cost, tail_den,
+                                      tail_chunk, self.plan_ws, stream)
+
     def attn_inputs(self):
         if self.w.has_prologue:
             return self.q_rot, self.lens_after
@@ -84,12 +95,17 @@ class DeviceStep:
 
     def step(self, sched: str = "balanced", min_tiles: int = _lib.FUSED_MIN_TILES,
              item_cost: int = _lib.FUSED_ITEM_COST, tail_den: int = _lib.FUSED_TAIL_DEN,
-             tail_chunk: int = _lib.FUSED_TAIL_CHUNK, stream=None):
-        """The whole hot path of one decode step; returns the bf16 output tensor."""
-        if self.w.has_prologue:
-            self.prologue(stream)
-        if sched == "balanced":
-            self.plan(min_tiles, item_cost, tail_den, tail_chunk, stream)
+             tail_chunk: int = _lib.FUSED_TAIL_CHUNK, stream=None, prologue_plans: bool = True):
+        """The whole hot path of one decode step; returns the bf16 output tensor. With a
+        prologue, the planned schedule plans inside the prologue launch unless
+        prologue_plans is False (then: prologue launch, planner launch)."""
+        if self.w.has_prologue and sched == "balanced" and prologue_plans:
+            self.prologue_plan(min_tiles, item_cost, tail_den, tail_chunk, stream)
+        else:
+            if self.w.has_prologue:
+                self.prologue(stream)
+            if sched == "balanced":
+                self.plan(min_tiles, item_cost, tail_den, tail_chunk, stream)
         self.attend(sched, stream)
         return self.out
 

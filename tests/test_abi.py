@@ -95,6 +95,19 @@ def test_calls_reject_bad_arguments_before_launching(L):
     # prologue: aliasing positions / seq_lens_out is refused
     assert L.hpa_decode_prologue(ctypes.byref(d), fake, fake, fake, fake, fake, 1e-6, 1e6, fake, fake, fake,
                                  fake, None, None, fake, fake, None, None) == 1
+    # prologue + plan: the rules of both calls, and plan_ws is required
+    P = [fake] * 5
+    pro = lambda desc, W, mt, cost, den, ch, ws, nbytes: L.hpa_decode_prologue_plan(
+        ctypes.byref(desc), *P, 1e-6, 1e6, fake, fake, fake, fake, None, None, fake,
+        ctypes.c_void_p(0x2000), W, mt, cost, den, ch, ws, nbytes, None)
+    assert pro(d, 512, 1, 4, 0, 1, None, 0) == 1                       # no plan workspace
+    assert pro(d, 512, 1, 4, 0, 1, fake, 16) == 3                      # workspace too small
+    assert pro(d, 512, 0, 4, 0, 1, fake, 1 << 30) == 1                 # min_tiles < 1
+    assert pro(d, 512, 1, 65, 0, 1, fake, 1 << 30) == 1                # item cost > 64
+    assert pro(d, 512, 1, 4, 1, 0, fake, 1 << 30) == 1                 # tail_chunk < 1
+    assert pro(d8, 512, 1, 4, 0, 1, fake, 1 << 30) == 1                # E4M3 without scales
+    assert L.hpa_decode_prologue_plan(ctypes.byref(d), *P, 1e-6, 1e6, fake, fake, fake, fake, None, None, fake,
+                                      fake, 512, 1, 4, 0, 1, fake, 1 << 30, None) == 1   # positions = seq_lens_out
     # default worker count: an unknown schedule or a NULL output is refused before any device query
     n = ctypes.c_int32(0)
     assert L.hpa_default_num_workers(0, 7, ctypes.byref(n)) == 1

@@ -229,6 +229,65 @@ def test_fp8_prologue_workload():
         assert_within(d.output_f64(), ref, "fp8", f"cfg4 {sched}")
 
 
+def _plan_of(d):
+    pa = d.plan_arrays()
+    return {k: pa[k] for k in ("Wp", "Ws", "D", "N", "S", "n_items", "n_partials") + PLAN_KEYS}
+
+
+def _prologue_plan_matches_separate(w, W=0, break_request=None):
+    """One launch (prologue + planner) against two (prologue, then hpa_plan over
+    seq_lens_out): same plan, same output bits, and the oracle's plan over the
+    appended lengths."""
+    from load_balanced_split_amd.runner import DeviceStep
+    one, two = DeviceStep(w, num_workers=W), DeviceStep(w, num_workers=W)
+    for d in (one, two):
+        d.lens_after.copy_(d.seq_lens)               # what a failed append leaves in place
+        if break_request is not None:
+            b = break_request
+            d.page_table[b, int(w.seq_lens[b]) // 64] = w.num_pages + 3
+    print(f"prologue+plan {w.name} B={w.batch} hkv={w.hkv} W={one.num_workers}", flush=True)
+    one.step("balanced")
+    two.step("balanced", prologue_plans=False)
+    torch.cuda.synchronize()
+    assert _plan_of(one) == _plan_of(two)
+    # a failed append leaves that request's rotated q unwritten: compare the others
+    keep = [b for b in range(w.batch) if b != break_request]
+    assert torch.equal(one.out[keep], two.out[keep])
+    assert torch.equal(one.lens_after, two.lens_after)
+    want = op.balanced_plan(one.lens_after.cpu().numpy().tolist(), w.hkv, one.num_workers,
+                            _lib.FUSED_MIN_TILES, _lib.FUSED_ITEM_COST, _lib.FUSED_TAIL_DEN, _lib.FUSED_TAIL_CHUNK)
+    got = _plan_of(one)
+    for k in ("Wp", "Ws", "D", "n_items", "n_partials") + PLAN_KEYS:
+        assert got[k] == want[k], k
+    return one, two
+
+
+def test_prologue_plan_one_launch_equals_two():
+    w = inputs.config_workload(4)
+    one, _ = _prologue_plan_matches_separate(w)
+    assert one.device_error() == 0
+    # and the fused schedule on the same appended cache gives the same bits
+    one.attend("fused")
+    torch.cuda.synchronize()
+    fused = one.out.clone()
+    one.attend("balanced")
+    torch.cuda.synchronize()
+    assert torch.equal(one.out, fused)
+
+
+def test_prologue_plan_failed_append_and_large_batch():
+    """A request whose append fails keeps its old length in the plan (and the error is
+    reported); above 3072 sequences the plan is made by a second launch."""
+    w = inputs.build_workload("pplan", [0, 5, 63, 64, 127, 128, 1000, 4000], 16, 2, "bf16", seed=19,
+                              prologue=True, poison=True)
+    one, two = _prologue_plan_matches_separate(w, W=13, break_request=3)
+    assert one.device_error(clear=True) & _lib.DEVERR_PROLOGUE
+    lens = np.random.default_rng(20).integers(0, 100, size=3100)
+    wl = inputs.build_workload("pplan_big", lens, 8, 1, "bf16", seed=21, prologue=True)
+    one, _ = _prologue_plan_matches_separate(wl, W=100)
+    assert one.device_error() == 0
+
+
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 def test_bf16_and_fp8_prologue_small(kv_dtype):
     w = inputs.build_workload("pro", [0, 5, 63, 64, 127, 128, 1000, 4000], 16, 2, kv_dtype, seed=9,
