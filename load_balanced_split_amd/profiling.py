@@ -2,6 +2,7 @@
 
     python -m load_balanced_split_amd.profiling stats <rocprof-dir> <title> <command>
     python -m load_balanced_split_amd.profiling pmc <fetch-dir> <write-dir> <title> <command>
+    python -m load_balanced_split_amd.profiling counters <title> <command> <pmc-dir>...
 
 `stats` reads a `--kernel-trace --stats` run (CSV or rocpd database) and prints
 per-kernel call counts and durations. `pmc` reads two `--pmc` runs (FETCH_SIZE,
@@ -10,7 +11,9 @@ WRITE_SIZE on the fill that `bench.py --pmc-run` launches over a buffer of known
 size (each touches the buffer once in one direction), and prints the HBM bytes
 per launch of each kernel, plus a JSON block that bench.py reads back (tagged
 with a hash of the kernel sources, so a stale reading is never reported for
-changed kernels).
+changed kernels). `counters` reads any number of `--pmc` runs and prints, per kernel,
+the mean over dispatches of every counter they hold, with the ratios derived from
+them (L2 hit rate, instructions per wave by kind).
 """
 
 import csv
@@ -76,8 +79,8 @@ def _pmc_rows(d, counter):
     rows = []
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
-            if r.get("Counter_Name") == counter:
-                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+            if counter is None or r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"]), r.get("Counter_Name")))
     if rows:
         return rows
     for f in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
@@ -85,7 +88,7 @@ def _pmc_rows(d, counter):
         try:
             q = ("select k.name, sum(p.value) from pmc_events p join kernels k on p.event_id = k.id "
                  "where p.counter_name = ? group by p.event_id")
-            rows += list(db.execute(q, (counter,)))
+            rows += [(n, v, counter) for n, v in db.execute(q, (counter,))]
         except sqlite3.Error:
             pass
     return rows
@@ -94,7 +97,7 @@ def _pmc_rows(d, counter):
 def pmc(fetch_dir, write_dir, title, command):
     per = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        for name, kib in _pmc_rows(d, counter):
+        for name, kib, _ in _pmc_rows(d, counter):
             per.setdefault(short_name(name), {}).setdefault(counter, []).append(kib)
     rd, wr = per.get("calib_read:reduce_kernel"), per.get("calib_write:fill")
     if not rd or not wr or "FETCH_SIZE" not in rd or "WRITE_SIZE" not in wr:
@@ -120,6 +123,44 @@ def pmc(fetch_dir, write_dir, title, command):
     return "\n".join(lines)
 
 
+def counters(title, command, dirs):
+    """Per-kernel means of every counter in the given `--pmc` runs. Counters are summed
+    over their dimensions within a dispatch (SE, XCC, instance), then averaged over the
+    dispatches of each kernel."""
+    per = {}
+    for d in dirs:
+        disp = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), short_name(r["Kernel_Name"]),
+                       r["Counter_Name"])
+                disp[key] = disp.get(key, 0.0) + float(r["Counter_Value"])
+        for (_, k, c), v in disp.items():
+            per.setdefault(k, {}).setdefault(c, []).append(v)
+    names = sorted({c for v in per.values() for c in v})
+    lines = [f"# {title}", "", f"command: {command}", "",
+             "mean per dispatch; derived: l2_hit = TCC_HIT / (TCC_HIT + TCC_MISS), "
+             "per-wave counts = SQ_INSTS_* / SQ_WAVES", ""]
+    for k, v in sorted(per.items()):
+        if k.startswith("calib_") or k.startswith("__amd"):
+            continue
+        m = {c: sum(x) / len(x) for c, x in v.items()}
+        lines.append(f"{k}  (dispatches: {max(len(x) for x in v.values())})")
+        for c in names:
+            if c in m:
+                lines.append(f"    {c:28s} {m[c]:16.4g}")
+        hit, miss = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
+        if hit is not None and miss is not None and hit + miss > 0:
+            lines.append(f"    {'l2_hit':28s} {hit / (hit + miss):16.3f}")
+        waves = m.get("SQ_WAVES")
+        if waves:
+            for c in names:
+                if c.startswith("SQ_INSTS_") and c in m:
+                    lines.append(f"    {c.lower()[3:] + '_per_wave':28s} {m[c] / waves:16.1f}")
+        lines.append("")
+    return "\n".join(lines)
+
+
 def read_traffic(summary_path, kernel):
     """HBM bytes per launch of `kernel` from a pmc summary, or None when the summary is
     missing or was taken on different kernel sources."""
@@ -141,5 +182,7 @@ if __name__ == "__main__":
         print(stats(sys.argv[2], sys.argv[3], sys.argv[4]))
     elif mode == "pmc":
         print(pmc(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5]))
+    elif mode == "counters":
+        print(counters(sys.argv[2], sys.argv[3], sys.argv[4:]))
     else:
         raise SystemExit(__doc__)
