@@ -57,13 +57,17 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--trace", action="store_true",
                    help="use the instrumented build and report per-CU busy time (tail balance) instead")
+    p.add_argument("--products", choices=["mfma", "valu"], default="mfma",
+                   help="library build: MFMA products (the library) or the comparison build whose "
+                        "attention kernels compute Q.K^T and P.V with VALU dot products")
     p.add_argument("--pmc-run", action="store_true",
                    help="short run for rocprofv3 counter passes: 1 GiB calibration read and write "
-                        "kernels, then a few steps of each balanced schedule over rotating copies")
+                        "kernels, then a few steps of each schedule over rotating copies")
     return p.parse_args()
 
 
 def pmc_main(args):
+    os.environ["HPA_PRODUCTS"] = args.products
     import torch
     from load_balanced_split_amd import _lib, inputs
     from load_balanced_split_amd.profiling import CALIBRATION_BYTES
@@ -80,7 +84,7 @@ def pmc_main(args):
         _ = buf.sum()
     torch.cuda.synchronize()
     del buf
-    for sched in ("balanced", "fused", "single"):
+    for sched in ("balanced", "fused", "single", "static_splits", "static_chunk"):
         for rep in range(2):
             for d in copies:
                 d.step(sched)
@@ -242,6 +246,7 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU, "
               "see the sharding note in DESIGN.md", file=sys.stderr)
         sys.exit(2)
+    os.environ["HPA_PRODUCTS"] = args.products
     import torch
     from load_balanced_split_amd import _lib, inputs
     from load_balanced_split_amd.runner import DeviceStep
@@ -370,7 +375,7 @@ def main():
         "data": "synthetic (seeded; shapes and length mix of the pages' kernel benchmark)",
         "config": {"workload": inputs.CONFIG_NAMES[args.workload], "schedule": SCHED_NAMES[head],
                    "num_workers": W, "static_num_workers": copies[0].static_workers,
-                   "rotating_copies": R, "kv_bytes": kv_bytes,
+                   "products": args.products, "rotating_copies": R, "kv_bytes": kv_bytes,
                    "algorithmic_bytes": alg_bytes},
         "us_per_step": round(us, 2),
         "us_per_step_p10_p50_p90": spread[head],
@@ -382,7 +387,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": attn_kernel_name(head, w.kv_dtype),
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic_per_launch(head, w.kv_dtype, args.workload)},
+                     "traffic": traffic_per_launch(head, w.kv_dtype, args.workload, args.products)},
     }
     if pro_bytes:
         result["config"]["prologue_bytes"] = pro_bytes
@@ -421,11 +426,14 @@ def attn_kernel_name(sched, kv_dtype):
     return f"{base}<{'bf16' if kv_dtype == 'bf16' else 'fp8'}>"
 
 
-def traffic_per_launch(sched, kv_dtype, workload):
+def traffic_per_launch(sched, kv_dtype, workload, products="mfma"):
     """HBM bytes per launch of the headline attention kernel from the committed
-    rocprofv3 counter summary of this workload; None when there is none or it was
-    taken on other kernel sources."""
+    rocprofv3 counter summary of this workload; None when there is none, when it
+    was taken on other kernel sources, or for the VALU-product build (the summary
+    covers the library's MFMA kernels)."""
     from load_balanced_split_amd.profiling import read_traffic
+    if products != "mfma":
+        return None
     fp8 = "false" if kv_dtype == "bf16" else "true"
     key = f"attn_fused_kernel<{fp8},false>" if sched == "fused" else f"attn_balanced_kernel<{fp8}>"
     path = os.path.join(ROOT, "profiles", f"attn_hbm_traffic_{WORKLOAD_KEYS[workload]}.txt")

@@ -14,9 +14,17 @@ import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 # HPA_TRACE=1 selects the instrumented build (per-wave timestamps and CU ids of
-# the attention kernels, written after the partial results in the workspace).
+# the attention kernels, written after the partial results in the workspace);
+# HPA_PRODUCTS=valu the comparison build whose attention kernels compute both
+# products with VALU dot products instead of MFMA (query groups of up to 8 heads).
 TRACE = os.environ.get("HPA_TRACE", "0") == "1"
-LIB_PATH = os.path.join(PKG, "libhpa_trace.so" if TRACE else "libhpa.so")
+PRODUCTS = os.environ.get("HPA_PRODUCTS", "mfma")
+if PRODUCTS not in ("mfma", "valu"):
+    raise ValueError(f"HPA_PRODUCTS={PRODUCTS!r}: expected mfma or valu")
+if TRACE and PRODUCTS != "mfma":
+    raise ValueError("HPA_TRACE=1 and HPA_PRODUCTS=valu select different builds")
+LIB_PATH = os.path.join(PKG, "libhpa_trace.so" if TRACE else
+                        "libhpa_valu.so" if PRODUCTS == "valu" else "libhpa.so")
 TRACE_WAVES, TRACE_WORDS, TRACE_START, TRACE_ITEMS, TRACE_UNITS = 4, 68, 4, 4, 48
 HEADER = os.path.join(os.path.dirname(PKG), "include", "hpa.h")
 

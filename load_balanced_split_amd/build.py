@@ -10,7 +10,6 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-LIB = os.path.join(PKG, "libhpa.so")
 SOURCES = ["plan.hip", "attn.hip", "prologue.hip", "host.cpp"]
 # Packed-fp32 VALU ops are kept out of every kernel (the compiler would otherwise
 # form v_pk_* from scalar float code). The atomic optimizer is off: it turns a
@@ -29,15 +28,22 @@ def hipcc():
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-TRACE_LIB = os.path.join(PKG, "libhpa_trace.so")
+# Library variants: the product build, the instrumented build (per-wave realtime
+# stamps and CU ids of the attention kernels) and the comparison build whose
+# attention kernels compute Q.K^T and P.V with VALU dot products instead of MFMA.
+VARIANTS = {
+    "product": ("libhpa.so", "_build", []),
+    "trace": ("libhpa_trace.so", "_build_trace", ["-DHPA_TRACE=1"]),
+    "valu": ("libhpa_valu.so", "_build_valu", ["-DHPA_VALU_PRODUCTS=1"]),
+}
+TRACE_LIB = os.path.join(PKG, VARIANTS["trace"][0])
 
 
-def build(verbose: bool = False, trace: bool = False) -> str:
-    """Compile libhpa.so, or with trace=True the instrumented libhpa_trace.so
-    (per-wave realtime stamps and CU ids of the attention kernels)."""
+def build(verbose: bool = False, trace: bool = False, variant: str = "product") -> str:
+    """Compile one variant of the library (trace=True is variant "trace")."""
     cc = hipcc()
-    objdir = os.path.join(PKG, "_build_trace" if trace else "_build")
-    extra = ["-DHPA_TRACE=1"] if trace else []
+    name, objdir, extra = VARIANTS["trace" if trace else variant]
+    objdir = os.path.join(PKG, objdir)
     os.makedirs(objdir, exist_ok=True)
 
     def compile_one(src):
@@ -54,7 +60,7 @@ def build(verbose: bool = False, trace: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    target = TRACE_LIB if trace else LIB
+    target = os.path.join(PKG, name)
     tmp = target + ".tmp"
     cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -65,5 +71,5 @@ def build(verbose: bool = False, trace: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
-    print(build(verbose=True, trace=True))
+    for v in VARIANTS:
+        print(build(verbose=True, variant=v))

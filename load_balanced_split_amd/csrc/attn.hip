@@ -26,6 +26,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 namespace hpa {
 namespace {
@@ -91,10 +92,6 @@ __device__ inline u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
 template <int POLICY = kPolicyDefault>
 __device__ inline float bload_f32(rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), 0, POLICY));
-}
-
-__device__ inline int bload_i32(rsrc_t r, uint32_t soff) {
-  return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(r, 0, static_cast<int>(soff), 0));
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -164,13 +161,47 @@ __device__ inline void fold(float& M, float& L, f32x4& A, float mk, float lk, co
 }
 
 // Shared state of the 4 waves for the end-of-item combine.
+// Per-wave exchange areas of the VALU products: the item's q for every head at
+// each lane group's dims [c][j][h], the scores of one unit before their sum over
+// lane groups [block][row][j][h], and P [k-step][j][h]. Empty in MFMA builds.
+struct ValuLds {
+  bf16x8 q[kWaves][4][4][kValuMaxGroup];
+  float s[kWaves][4][16][4][kValuMaxGroup];
+  bf16x8 p[kWaves][2][4][kValuMaxGroup];
+};
+struct NoValuLds {};
+
 struct CombineLds {
   float m[kWaves][kMaxGroup];
   float l[kWaves][kMaxGroup];
   float o[kWaves][kMaxGroup][kORow];
   int flag;                   // an arrival count, broadcast to the workgroup
   int claim[2];               // dynamic tail: claimed chunk, broadcast (two slots, alternating)
+  [[no_unique_address]] std::conditional_t<kValuProducts, ValuLds, NoValuLds> v;
 };
+
+// Accumulator registers per lane. MFMA: the 8 C tiles of O^T[16 d x 16 heads]
+// (lane: head m16, dims 16 n + 4 j .. + 3). VALU products: o(h, n) = element n % 4
+// of register 2 h + n / 4, dim 16 n + m16 of head h, summed over the lane's tokens only.
+constexpr int kAccRegs = kValuProducts ? 2 * kValuMaxGroup : 8;
+
+// a . b + acc over 8 bf16 pairs, in fp32 (VALU dot2 instructions)
+[[maybe_unused]] __device__ inline float dot8(bf16x8 a, bf16x8 b, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(b, b, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(b, b, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(b, b, 4, 5), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(b, b, 6, 7), acc, false);
+  return acc;
+}
+
+// Orders a wave's LDS accesses around an exchange between its own lanes (LDS
+// executes one wave's instructions in order; this keeps the compiler from
+// moving them across).
+[[maybe_unused]] __device__ inline void wave_lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Global view of a device pointer: atomics through it are global_* instructions,
 // counted on the vector memory counter only (a flat one also holds up LDS waits).
@@ -311,18 +342,106 @@ struct Worker {
     }
   }
 
+  // the VALU products' LDS (only ever used in builds that have it)
+  __device__ ValuLds& vl() const { return *reinterpret_cast<ValuLds*>(&lds.v); }
+
+  // VALU products: the current item's q for every head, where each lane group
+  // reads it (lane (h, j) holds head h at lane group j's dims).
+  __device__ void valu_stage_q(const bf16x8 (&qc)[4]) {
+    if constexpr (kValuProducts) {
+      if (m16 < kValuMaxGroup) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vl().q[wave][c][j][m16] = qc[c];
+      }
+      wave_lds_sync();
+    }
+  }
+
+  // VALU products: S^T in the MFMA C layout (lane (h, j): tokens row_token(b, 4 j + i)
+  // of head h). Lane (m16, j) first sums its 32 dims of token row m16 for every head,
+  // then the four lane groups' sums of each (token, head) meet in LDS.
+  __device__ void valu_scores(const UnitBuf& buf, f32x4 (&sc)[Cfg<FP8>::NBLK]) {
+    if constexpr (kValuProducts) {
+      using C = Cfg<FP8>;
+      float part[C::NBLK][kValuMaxGroup];
+#pragma unroll
+      for (int b = 0; b < C::NBLK; ++b)
+#pragma unroll
+        for (int h = 0; h < kValuMaxGroup; ++h) part[b][h] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bf16x8 qh[kValuMaxGroup];
+#pragma unroll
+        for (int h = 0; h < kValuMaxGroup; ++h) qh[h] = vl().q[wave][c][j][h];
+#pragma unroll
+        for (int b = 0; b < C::NBLK; ++b) {
+          const bf16x8 kb = k_operand(buf, b, c);
+#pragma unroll
+          for (int h = 0; h < kValuMaxGroup; ++h) part[b][h] = dot8(kb, qh[h], part[b][h]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < C::NBLK; ++b) {
+        f32x4* dst = reinterpret_cast<f32x4*>(&vl().s[wave][b][m16][j][0]);
+        dst[0] = f32x4{part[b][0], part[b][1], part[b][2], part[b][3]};
+        dst[1] = f32x4{part[b][4], part[b][5], part[b][6], part[b][7]};
+      }
+      wave_lds_sync();
+      const int h = m16 & (kValuMaxGroup - 1);
+#pragma unroll
+      for (int b = 0; b < C::NBLK; ++b) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float* r = &vl().s[wave][b][4 * j + i][0][h];
+          const float x = (r[0] + r[kValuMaxGroup]) + (r[2 * kValuMaxGroup] + r[3 * kValuMaxGroup]);
+          sc[b][i] = m16 < kValuMaxGroup ? x : 0.f;
+        }
+      }
+    }
+  }
+
+  // VALU products: o(h, n) += sum over the lane's tokens of P(token, h) V(token, 16 n + m16);
+  // lane (m16, j) takes P of its tokens for every head from lanes (h, j) through LDS.
+  __device__ void valu_pv(const UnitBuf& buf, const bf16x8 (&pk)[Cfg<FP8>::KSTEPS], f32x4 (&o)[kAccRegs]) {
+    if constexpr (kValuProducts) {
+      using C = Cfg<FP8>;
+      if (m16 < kValuMaxGroup) {
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) vl().p[wave][ks][j][m16] = pk[ks];
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks) {
+        bf16x8 ph[kValuMaxGroup];
+#pragma unroll
+        for (int h = 0; h < kValuMaxGroup; ++h) ph[h] = vl().p[wave][ks][j][h];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const bf16x8 vn = v_operand(buf, n, ks);
+#pragma unroll
+          for (int h = 0; h < kValuMaxGroup; ++h)
+            o[2 * h + (n >> 2)][n & 3] = dot8(vn, ph[h], o[2 * h + (n >> 2)][n & 3]);
+        }
+      }
+    }
+  }
+
   // Online-softmax update with one unit: tokens [tok0, tok0 + UNIT) of the sequence.
   __device__ void compute(UnitBuf& buf, const bf16x8 (&q)[4], int tok0, int L, float qk_scale,
-                          float& m_run, float& l_part, f32x4 (&o)[8]) {
+                          float& m_run, float& l_part, f32x4 (&o)[kAccRegs]) {
     using C = Cfg<FP8>;
 
     f32x4 sc[C::NBLK];
+    if constexpr (kValuProducts) {
+      valu_scores(buf, sc);
+    } else {
 #pragma unroll
-    for (int b = 0; b < C::NBLK; ++b) {
-      sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < C::NBLK; ++b) {
+        sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        sc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(buf, b, c), q[c], sc[b], 0, 0, 0);
+        for (int c = 0; c < 4; ++c)
+          sc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(buf, b, c), q[c], sc[b], 0, 0, 0);
+      }
     }
     const bool partial = tok0 + C::UNIT > L;
     float mx = -INFINITY;
@@ -352,8 +471,18 @@ struct Worker {
       }
     }
     l_part = l_part * alpha + psum;
+    if constexpr (kValuProducts) {
+      // head h's factor sits in lane h (lane group 0)
 #pragma unroll
-    for (int n = 0; n < 8; ++n) o[n] *= alpha;
+      for (int h = 0; h < kValuMaxGroup; ++h) {
+        const float ah = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
+        o[2 * h] *= ah;
+        o[2 * h + 1] *= ah;
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < 8; ++n) o[n] *= alpha;
+    }
     bf16x8 pk[C::KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
@@ -381,11 +510,15 @@ struct Worker {
         }
       }
     }
+    if constexpr (kValuProducts) {
+      valu_pv(buf, pk, o);
+    } else {
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+      for (int n = 0; n < 8; ++n) {
 #pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks)
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand(buf, n, ks), pk[ks], o[n], 0, 0, 0);
+        for (int ks = 0; ks < C::KSTEPS; ++ks)
+          o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand(buf, n, ks), pk[ks], o[n], 0, 0, 0);
+      }
     }
     if (kTraceBuild) {   // the unit's data has been consumed by now
       if (trec && lane == 0 && units_done < kTraceUnits)
@@ -467,8 +600,9 @@ struct Worker {
   // unit of st, that slot takes its first unit of the next item (nst, npid), so
   // on return bufA holds it. Returns whether that unit exists.
   __device__ bool stream(const ItemState& st, bool okA, int pidB, float& m_run, float& l_part,
-                         f32x4 (&o)[8], bool more, const ItemState& nst, int npid) {
+                         f32x4 (&o)[kAccRegs], bool more, const ItemState& nst, int npid) {
     using C = Cfg<FP8>;
+    valu_stage_q(q);
     const int nu = units(st);
     const float qk_scale = a.sm_scale * kLog2e * st.kscale;
     bool any_bad = false;
@@ -513,10 +647,30 @@ struct Worker {
 
   // The 4 waves' (m, l, acc) meet in LDS; one log-sum-exp combine; the output row
   // (unsplit sequence) or a partial slot (split sequence) is written.
-  __device__ void combine(const ItemState& st, float m_run, float l_part, const f32x4 (&o)[8]) {
+  __device__ void combine(const ItemState& st, float m_run, float l_part, const f32x4 (&o)[kAccRegs]) {
     float l_tot = l_part + __shfl_xor(l_part, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
-    if (m16 < a.group) {
+    if constexpr (kValuProducts) {
+      if (m16 < a.group && j == 0) {
+        lds.m[wave][m16] = m_run;
+        lds.l[wave][m16] = l_tot;
+      }
+      // sum o(h, n) over the four lane groups; lane group 0 stores dim 16 n + m16 of each head
+#pragma unroll
+      for (int r = 0; r < kAccRegs; ++r) {
+        f32x4 x = o[r];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] += __shfl_xor(x[e], 16, 64);
+          x[e] += __shfl_xor(x[e], 32, 64);
+        }
+        const int h = r >> 1;
+        if (j == 0 && h < a.group) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lds.o[wave][h][16 * (4 * (r & 1) + e) + m16] = x[e];
+        }
+      }
+    } else if (m16 < a.group) {
       if (j == 0) {
         lds.m[wave][m16] = m_run;
         lds.l[wave][m16] = l_tot;
@@ -736,9 +890,9 @@ struct Worker {
       Item nnit;
       const bool more2 = more && src.next(nnit, tq);
       float m_run = -INFINITY, l_part = 0.f;
-      f32x4 o[8];
+      f32x4 o[kAccRegs];
 #pragma unroll
-      for (int n = 0; n < 8; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < kAccRegs; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
       stamp(0);
       okA = stream(st, okA, pidB, m_run, l_part, o, more, nst, npid);
       stamp(1);

@@ -38,6 +38,9 @@ hpa_status check_desc(const hpa_attn_desc* d) {
                 d->num_kv_heads);
   if (d->num_q_heads / d->num_kv_heads > hpa::kMaxGroup)
     return fail(HPA_ERR_UNSUPPORTED, "group size %d > 16", d->num_q_heads / d->num_kv_heads);
+  if (hpa::kValuProducts && d->num_q_heads / d->num_kv_heads > hpa::kValuMaxGroup)
+    return fail(HPA_ERR_UNSUPPORTED, "group size %d > %d (VALU-product build)", d->num_q_heads / d->num_kv_heads,
+                hpa::kValuMaxGroup);
   if (d->max_pages_per_seq < 1) return fail(HPA_ERR_INVALID_ARG, "max_pages_per_seq %d < 1", d->max_pages_per_seq);
   if (int64_t(d->max_pages_per_seq) * hpa::kPage > INT32_MAX / 2)
     return fail(HPA_ERR_INVALID_ARG, "max_pages_per_seq %d too large", d->max_pages_per_seq);

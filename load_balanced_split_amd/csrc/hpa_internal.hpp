@@ -176,6 +176,18 @@ constexpr bool kTraceBuild = false;
 #endif
 inline int64_t trace_bytes(int64_t blocks) { return kTraceBuild ? blocks * kWaves * kTraceWords * 8 : 0; }
 
+// Comparison builds (HPA_VALU_PRODUCTS) compute both products of the attention
+// kernels, Q.K^T and P.V, with VALU bf16 dot products instead of MFMA, from the
+// same registers and the same cache layout, for up to kValuMaxGroup query heads
+// per KV head. Such a library exists to measure the MFMA choice; it is otherwise
+// identical.
+#ifdef HPA_VALU_PRODUCTS
+constexpr bool kValuProducts = true;
+#else
+constexpr bool kValuProducts = false;
+#endif
+constexpr int kValuMaxGroup = 8;
+
 // Closed forms of the balanced partition, shared by the planner kernel and the
 // in-kernel planning of the fused schedule. Worker w owns global positions
 // [w*N/W', (w+1)*N/W'); the owner of position t is floor(((t+1)*W' - 1)/N)

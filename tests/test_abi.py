@@ -116,3 +116,21 @@ def test_calls_reject_bad_arguments_before_launching(L):
     d0 = _desc(batch=0)
     assert L.hpa_decode_attn(ctypes.byref(d0), 1, None, None, None, None, None, None, None, 512, None, 0,
                              None, 0, None, 0, None) == 0
+
+
+def test_valu_product_build_exports_and_limits(L):
+    """The comparison build (VALU products) exports the same symbols and refuses
+    query groups larger than 8 heads, which the library build accepts."""
+    import os
+    path = os.path.join(os.path.dirname(_lib.LIB_PATH), "libhpa_valu.so")
+    if not os.path.exists(path):
+        pytest.skip("libhpa_valu.so not built")
+    V = ctypes.CDLL(path)
+    for n in _lib.declared_symbols():
+        assert hasattr(V, n), n
+    n = ctypes.c_size_t(0)
+    for hq, status_valu in ((8, 0), (16, 2)):
+        d = _desc(num_q_heads=hq)
+        V.hpa_plan_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        assert V.hpa_plan_workspace_size(ctypes.byref(d), 512, ctypes.byref(n)) == status_valu
+        assert L.hpa_plan_workspace_size(ctypes.byref(d), 512, ctypes.byref(n)) == 0
