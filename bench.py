@@ -54,6 +54,7 @@ def parse():
     p.add_argument("--event-steps", type=int, default=60)
     p.add_argument("--no-static", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-probe", action="store_true", help="skip the plain streaming-read probe")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--trace", action="store_true",
                    help="use the instrumented build and report per-CU busy time (tail balance) instead")
@@ -412,9 +413,45 @@ def main():
                      "balanced_speedup": round(t / step_s, 3),
                      "balanced_attn_speedup": round(e["attn"] / ev["attn"], 3)}
         result["static_split_kv"] = st
+    if not args.no_probe:
+        probe = stream_read_probe(stream)
+        probe["attn_frac_of_probe"] = round(achieved / probe["gbps"], 4)
+        result["stream_read_probe"] = probe
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, kv_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def stream_read_probe(stream, gib=4, launches=10):
+    """Plain streaming-read bandwidth of this GPU (the library's read probe: 16-byte
+    non-temporal loads, one contiguous slice per workgroup) over a buffer far larger
+    than the caches; the best of a few workgroup counts, timed with HIP events
+    around a graph of back-to-back launches."""
+    import torch
+    from load_balanced_split_amd import _lib
+    buf = torch.zeros(gib << 28, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    best = None
+    for wgs in (512, 1024, 2048, 4096):
+        _lib.hpa_probe_stream_read(buf, wgs, sink)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(launches):
+                _lib.hpa_probe_stream_read(buf, wgs, sink)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbps = buf.numel() * 4 * launches / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if best is None or gbps > best["gbps"]:
+            best = {"gbps": round(gbps, 1), "workgroups": wgs, "bytes": buf.numel() * 4}
+        del g
+    del buf
+    return best
 
 
 SCHED_NAMES = {"fused": "balanced_fused", "balanced": "balanced_planned"}

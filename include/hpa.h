@@ -245,6 +245,19 @@ hpa_status hpa_decode_prologue_plan(const hpa_attn_desc* desc, const void* q_in,
  * device error word of a plan workspace. */
 hpa_status hpa_read_device_error(void* plan_ws, int32_t* code, int32_t clear, hipStream_t stream);
 
+/* Measurement aid (not part of the attention path): reads `bytes` of device
+ * memory at `buf` once and computes nothing from it, so its duration gives the
+ * plain streaming-read bandwidth of this GPU, the practical ceiling for the
+ * HBM-bound attention kernel. `bytes` must be a positive multiple of 16 and
+ * `buf` 16-byte aligned. Each of `workgroups` workgroups (0: four per compute
+ * unit of the current device) of 256 threads reads one contiguous slice with
+ * 16-byte non-temporal loads, 8 in flight per lane. `sink` (device, at least
+ * `workgroups` int32) receives a word only if a slice's XOR equals a fixed
+ * constant, which keeps the loads without writing in practice. Asynchronous on
+ * `stream`. */
+hpa_status hpa_probe_stream_read(const void* buf, size_t bytes, int32_t workgroups, int32_t* sink,
+                                 hipStream_t stream);
+
 const char* hpa_status_string(hpa_status status);
 /* Message of the last non-OK status returned on the calling thread. */
 const char* hpa_last_error_message(void);

@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
             "hpa_decode_prologue_plan": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
                                          _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P],
             "hpa_read_device_error": [_P, ctypes.POINTER(ctypes.c_int32), _I, _P],
+            "hpa_probe_stream_read": [_P, ctypes.c_size_t, _I, _P, _P],
             "hpa_status_string": [ctypes.c_int],
             "hpa_last_error_message": [],
         }
@@ -216,6 +217,15 @@ def hpa_read_device_error(plan_ws, clear: bool = False, stream=None) -> int:
     _check(lib().hpa_read_device_error(_ptr(plan_ws), ctypes.byref(code), 1 if clear else 0, _stream(stream)),
            "hpa_read_device_error")
     return code.value
+
+
+def hpa_probe_stream_read(buf, workgroups: int = 0, sink=None, stream=None) -> None:
+    """Read all of `buf` (a device tensor) once with the library's plain-read probe."""
+    import torch
+    if sink is None:
+        sink = torch.zeros(max(workgroups, 4096), dtype=torch.int32, device=buf.device)
+    _check(lib().hpa_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), workgroups, _ptr(sink),
+                                       _stream(stream)), "hpa_probe_stream_read")
 
 
 def hpa_status_string(status: int) -> str:

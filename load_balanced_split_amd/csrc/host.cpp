@@ -375,4 +375,22 @@ hpa_status hpa_read_device_error(void* plan_ws, int32_t* code, int32_t clear, hi
   return HPA_OK;
 }
 
+hpa_status hpa_probe_stream_read(const void* buf, size_t bytes, int32_t workgroups, int32_t* sink,
+                                 hipStream_t stream) {
+  if (!buf || !sink) return fail(HPA_ERR_INVALID_ARG, "buf or sink is NULL");
+  if (bytes == 0 || bytes % 16 != 0) return fail(HPA_ERR_INVALID_ARG, "bytes %zu not a positive multiple of 16", bytes);
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return fail(HPA_ERR_INVALID_ARG, "buf not 16-byte aligned");
+  if (workgroups < 0 || workgroups > (1 << 20)) return fail(HPA_ERR_INVALID_ARG, "workgroups %d", workgroups);
+  if (workgroups == 0) {
+    int device = 0, cus = 0;
+    if (hipGetDevice(&device) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
+      return fail(HPA_ERR_DEVICE, "compute unit count query failed");
+    workgroups = 4 * cus;
+  }
+  if (hpa::launch_stream_read(buf, bytes, workgroups, sink, stream) != hipSuccess)
+    return fail(HPA_ERR_LAUNCH, "stream-read probe launch failed");
+  return HPA_OK;
+}
+
 }  // extern "C"

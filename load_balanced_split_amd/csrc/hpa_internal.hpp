@@ -292,6 +292,7 @@ hipError_t launch_prologue(const hpa_attn_desc& d, const uint16_t* q_in, const u
                            const float* k_scale, const float* v_scale, uint16_t* q_out,
                            int32_t* seq_lens_out, int32_t* err_word, const PlanArgs* plan, hipStream_t stream);
 hipError_t launch_clear_word(int32_t* word, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, int32_t* sink, hipStream_t stream);
 int attn_blocks_per_cu(bool fp8);         // persistent attention kernels
 int attn_static_blocks_per_cu(bool fp8);  // static split-KV attention kernel
 

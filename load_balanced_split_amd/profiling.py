@@ -3,6 +3,7 @@
     python -m load_balanced_split_amd.profiling stats <rocprof-dir> <title> <command>
     python -m load_balanced_split_amd.profiling pmc <fetch-dir> <write-dir> <title> <command>
     python -m load_balanced_split_amd.profiling counters <title> <command> <pmc-dir>...
+    python -m load_balanced_split_amd.profiling balance <title> <command> <trace-json>...
 
 `stats` reads a `--kernel-trace --stats` run (CSV or rocpd database) and prints
 per-kernel call counts and durations. `pmc` reads two `--pmc` runs (FETCH_SIZE,
@@ -13,7 +14,9 @@ per launch of each kernel, plus a JSON block that bench.py reads back (tagged
 with a hash of the kernel sources, so a stale reading is never reported for
 changed kernels). `counters` reads any number of `--pmc` runs and prints, per kernel,
 the mean over dispatches of every counter they hold, with the ratios derived from
-them (L2 hit rate, instructions per wave by kind).
+them (L2 hit rate, instructions per wave by kind). `balance` tabulates the
+per-CU busy time of `bench.py --trace` runs (instrumented build: per-wave
+realtime stamps and hardware CU ids of one attention launch per schedule).
 """
 
 import csv
@@ -161,6 +164,34 @@ def counters(title, command, dirs):
     return "\n".join(lines)
 
 
+def balance(title, command, files):
+    cols = [("makespan_us", "makespan"), ("cu_busy_mean_us", "busy_mean"), ("cu_busy_max_us", "busy_max"),
+            ("cu_busy_min_us", "busy_min"), ("cu_busy_max_over_mean", "max/mean"), ("utilisation", "util"),
+            ("worker_end_p50_us", "end_p50"), ("worker_end_p99_us", "end_p99"), ("workgroups", "wgs"),
+            ("cus", "cus")]
+    lines = [f"# {title}", "", f"command: {command}", "",
+             "one attention launch per schedule (the shortest of 5), times in us on the 100 MHz realtime "
+             "counter; busy = union of a CU's wave intervals; util = mean busy / makespan", ""]
+    for f in files:
+        data = None
+        for line in open(f):
+            if line.startswith("{"):
+                data = json.loads(line)
+        if data is None:
+            raise SystemExit(f"{f}: no JSON line")
+        lines.append(f"## {data['workload']} (W = {data['num_workers']})")
+        lines.append(f"{'schedule':16s}" + "".join(f"{h:>11s}" for _, h in cols))
+        for sched in ("balanced", "fused", "single", "static_splits", "static_chunk"):
+            r = data.get(sched)
+            if r:
+                lines.append(f"{sched:16s}" + "".join(f"{r.get(k, float('nan')):>11}" for k, _ in cols))
+        xcd = data.get("fused", {}).get("worker_end_mean_by_xcd_us")
+        if xcd:
+            lines.append("fused: mean worker end by XCD (us): " + ", ".join(f"{k}: {v}" for k, v in xcd.items()))
+        lines.append("")
+    return "\n".join(lines)
+
+
 def read_traffic(summary_path, kernel):
     """HBM bytes per launch of `kernel` from a pmc summary, or None when the summary is
     missing or was taken on different kernel sources."""
@@ -184,5 +215,7 @@ if __name__ == "__main__":
         print(pmc(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5]))
     elif mode == "counters":
         print(counters(sys.argv[2], sys.argv[3], sys.argv[4:]))
+    elif mode == "balance":
+        print(balance(sys.argv[2], sys.argv[3], sys.argv[4:]))
     else:
         raise SystemExit(__doc__)

@@ -134,3 +134,14 @@ def test_valu_product_build_exports_and_limits(L):
         V.hpa_plan_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         assert V.hpa_plan_workspace_size(ctypes.byref(d), 512, ctypes.byref(n)) == status_valu
         assert L.hpa_plan_workspace_size(ctypes.byref(d), 512, ctypes.byref(n)) == 0
+
+
+def test_stream_read_probe_validation(L):
+    buf, sink = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    f = L.hpa_probe_stream_read
+    assert f(buf, 17, 4, sink, None) == 1                     # not a multiple of 16
+    assert f(buf, 0, 4, sink, None) == 1                      # empty
+    assert f(ctypes.c_void_p(4100), 64, 4, sink, None) == 1   # misaligned
+    assert f(None, 64, 4, sink, None) == 1
+    assert f(buf, 64, 4, None, None) == 1
+    assert f(buf, 64, -1, sink, None) == 1

@@ -478,3 +478,20 @@ def test_all_empty_and_zero_batch():
         d.step(sched)
         torch.cuda.synchronize()
         assert np.all(d.output_f64() == 0)
+
+
+def test_stream_read_probe_reads_every_slice():
+    """The plain-read probe covers the whole buffer, ragged last slice included: a
+    slice whose XOR equals the probe's constant (only the buffer's last 16 bytes are
+    non-zero) is the only one that writes its sink word."""
+    n16 = 1000
+    buf = torch.zeros(n16 * 4, dtype=torch.int32, device="cuda")
+    buf[-4] = int(np.array(0x9E3779B9, np.uint32).view(np.int32))
+    for wgs, hit in ((3, 2), (1, 0), (7, 6)):
+        sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+        print(f"probe wgs={wgs}", flush=True)
+        _lib.hpa_probe_stream_read(buf, wgs, sink)
+        torch.cuda.synchronize()
+        want = np.zeros(16, np.int32)
+        want[hit] = buf[-4].item()
+        assert np.array_equal(sink.cpu().numpy(), want), (wgs, sink.cpu().numpy())
