@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for paged decode attention.
+"""Seeded synthetic inputs for paged decode attention (and for the router GEMM:
+``router_workload`` at the end).
 
 This module only draws random numbers and lays them out in the cache formats the
 library consumes. It holds none of the attention, softmax, planning, RMSNorm or
@@ -295,3 +296,26 @@ def config_workload(index: int, seed: int = 0, poison: bool = False) -> Workload
 def config_lengths_only(index: int, seed: int = 0) -> np.ndarray:
     """The lengths a workload would draw, without building its cache."""
     return config_lengths(index, np.random.default_rng(seed))
+
+
+# ------------------------------------------------------------------ router ---
+
+@dataclasses.dataclass
+class RouterWorkload:
+    """Inputs of the split-precision router GEMM: activations x (bf16 bits,
+    [tokens, hidden]) and the router weight w (fp32, [experts, hidden])."""
+    name: str
+    tokens: int
+    experts: int
+    hidden: int
+    x: np.ndarray
+    w: np.ndarray
+
+
+def router_workload(tokens: int, experts: int, hidden: int, seed: int = 0, name: str = "router") -> RouterWorkload:
+    """x ~ N(0, 1) rounded to bf16 by PyTorch's cast; w ~ N(0, 1/hidden) in fp32, so
+    that logits are of order 1. Draw order: x, then w, from one default_rng(seed)."""
+    rng = np.random.default_rng(seed)
+    x = bf16_bits(rng.standard_normal((tokens, hidden), dtype=np.float32))
+    w = (rng.standard_normal((experts, hidden), dtype=np.float32) / np.float32(math.sqrt(hidden))).astype(np.float32)
+    return RouterWorkload(name=name, tokens=tokens, experts=experts, hidden=hidden, x=x, w=w)

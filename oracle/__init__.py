@@ -16,6 +16,9 @@ Sources the oracle follows (cited by page title and section):
   Tencent Hunyuan", section "Breaking Down the Kernels": a per-step
   load-balanced decode scheduler replacing static KV partitioning, and a fused
   prologue doing RoPE, query-key normalisation and the KV write.
+* xiaodao.ai (same page), section "从实验表走到 SLA，还差一轮负载测试": the
+  router GEMM keeps its top-k expert choice by splitting its fp32 weight into a
+  bf16 high part and a bf16 residual, two tensor-core products summed.
 * openai-hub.com, "腾讯混元HPC-Ops升级：五大算子直击推理痛点", section
   "五大算子覆盖了哪些场景": the illustrative variable-length attention call on
   a paged KV cache.
@@ -29,6 +32,9 @@ Modules:
 * ``planner``   the balanced work list (bit-exact contract) and the static
                 split-KV partitions used for comparison
 * ``prologue``  RMSNorm, rotate-half RoPE, E4M3 quantise and paged append
+* ``router``    the split-precision router GEMM (fp32 weight as bf16 high part +
+                bf16 residual), exact logits, top-k, its error bound and the
+                page's checks (error, greedy choice, cosine similarity)
 
 Parity status of every function is listed in each module's header.
 """
