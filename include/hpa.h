@@ -245,6 +245,48 @@ hpa_status hpa_decode_prologue_plan(const hpa_attn_desc* desc, const void* q_in,
  * device error word of a plan workspace. */
 hpa_status hpa_read_device_error(void* plan_ws, int32_t* code, int32_t clear, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Split-precision router GEMM (xiaodao.ai, "HPC-Ops 把 TPOT 降 48.8%，用户未必快一半",
+ * section "从实验表走到 SLA，还差一轮负载测试": the router keeps its top-k expert
+ * choice by splitting its fp32 weight into a bf16 high part and a bf16 residual
+ * and summing two tensor-core products).
+ *
+ * logits[t][e] = sum_k x[t][k] * (hi[e][k] + lo[e][k]), hi = bf16 nearest to W
+ * (ties to even), lo = bf16 nearest to W - hi; every product is exact in fp32 and
+ * the sums are fp32 accumulations (MFMA), so |logit - x.W| stays within
+ * sum_k |x_k||W_k - hi_k - lo_k| + gamma_n sum_k |x_k|(|hi_k| + |lo_k|), n = 2H + 64,
+ * gamma_n = n 2^-24 / (1 - n 2^-24). One pass (hi only) is the plain bf16 router.
+ * The top-k experts of a token are its k largest logits, equal logits ordered by
+ * the lower expert index, listed from the largest down. Inputs must be finite.
+ *
+ * Shapes: tokens T in [0, 2^20], experts E a multiple of 16 in [16, 1024],
+ * hidden H a multiple of 32 in [32, 65536], top_k in [0, min(32, E)].
+ * ------------------------------------------------------------------------- */
+
+/* Splits and lays out the router weight once: w (device, fp32 [E][H] row-major,
+ * 16-byte aligned) -> packed (device, E * H * 4 bytes, 16-byte aligned): for each
+ * 16-expert x 32-dim tile, the hi half then the lo half, each in the order the
+ * GEMM's 16-byte loads read (tile = (e/16)(H/32) + k/32, lane = 16((k%32)/8) + e%16;
+ * hi at byte 2048 tile + 16 lane + 2 (k%8), lo 1024 bytes after it). Caller-owned
+ * memory; asynchronous on `stream`. */
+hpa_status hpa_router_pack_weights(const float* w, int32_t num_experts, int32_t hidden, void* packed,
+                                   hipStream_t stream);
+
+/* Bytes of device workspace hpa_router_gemm needs for this shape (fp32 partial
+ * sums of the split K ranges; 0 when tokens == 0). */
+hpa_status hpa_router_workspace_size(int32_t tokens, int32_t num_experts, int32_t hidden, size_t* bytes);
+
+/* x (device, bf16 [T][H] row-major, 16-byte aligned), packed (from
+ * hpa_router_pack_weights) -> logits (device, fp32 [T][E]) and, if top_k > 0,
+ * topk_idx (device, int32 [T][top_k]) and topk_val (device, fp32 [T][top_k]).
+ * passes = 2 for the split weight, 1 for its high part alone. workspace: device,
+ * 16-byte aligned, at least hpa_router_workspace_size bytes. Results are
+ * deterministic (fixed summation order). Host-side validation returns a non-OK
+ * status and launches nothing; asynchronous on `stream`. */
+hpa_status hpa_router_gemm(const void* x, const void* packed, int32_t tokens, int32_t num_experts,
+                           int32_t hidden, int32_t passes, float* logits, int32_t top_k, int32_t* topk_idx,
+                           float* topk_val, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Measurement aid (not part of the attention path): reads `bytes` of device
  * memory at `buf` once and computes nothing from it, so its duration gives the
  * plain streaming-read bandwidth of this GPU, the practical ceiling for the

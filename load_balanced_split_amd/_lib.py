@@ -100,6 +100,9 @@ def lib() -> ctypes.CDLL:
                                          _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P],
             "hpa_read_device_error": [_P, ctypes.POINTER(ctypes.c_int32), _I, _P],
             "hpa_probe_stream_read": [_P, ctypes.c_size_t, _I, _P, _P],
+            "hpa_router_pack_weights": [_P, _I, _I, _P, _P],
+            "hpa_router_workspace_size": [_I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
+            "hpa_router_gemm": [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, ctypes.c_size_t, _P],
             "hpa_status_string": [ctypes.c_int],
             "hpa_last_error_message": [],
         }
@@ -226,6 +229,28 @@ def hpa_probe_stream_read(buf, workgroups: int = 0, sink=None, stream=None) -> N
         sink = torch.zeros(max(workgroups, 4096), dtype=torch.int32, device=buf.device)
     _check(lib().hpa_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), workgroups, _ptr(sink),
                                        _stream(stream)), "hpa_probe_stream_read")
+
+
+def hpa_router_pack_weights(w, packed, stream=None) -> None:
+    """w: fp32 [E, H] device tensor -> packed (uint8 device tensor of E * H * 4 bytes)."""
+    E, H = w.shape
+    _check(lib().hpa_router_pack_weights(_ptr(w), E, H, _ptr(packed), _stream(stream)), "hpa_router_pack_weights")
+
+
+def hpa_router_workspace_size(tokens: int, experts: int, hidden: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().hpa_router_workspace_size(tokens, experts, hidden, ctypes.byref(n)), "hpa_router_workspace_size")
+    return n.value
+
+
+def hpa_router_gemm(x, packed, experts: int, passes: int, logits, top_k: int, topk_idx, topk_val, workspace,
+                    stream=None) -> None:
+    """x: bf16 [T, H] device tensor; logits fp32 [T, E]; topk_idx int32 / topk_val fp32 [T, top_k]."""
+    T, H = x.shape
+    _check(lib().hpa_router_gemm(_ptr(x), _ptr(packed), T, experts, H, passes, _ptr(logits), top_k,
+                                 _ptr(topk_idx) if top_k else None, _ptr(topk_val) if top_k else None,
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "hpa_router_gemm")
 
 
 def hpa_status_string(status: int) -> str:

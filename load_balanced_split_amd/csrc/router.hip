@@ -1,0 +1,279 @@
+// Split-precision router GEMM for gfx950: logits[t][e] = x[t] . W[e] with the fp32
+// router weight W carried as a bf16 high part plus a bf16 residual, each multiplied
+// on MFMA and accumulated in fp32, then the top-k experts of every token.
+//
+// Method: xiaodao.ai "HPC-Ops 把 TPOT 降 48.8%，用户未必快一半", section
+// "从实验表走到 SLA，还差一轮负载测试" -- the router keeps its top-k expert choice
+// by splitting its fp32 weight into a bf16 high part and a bf16 residual and
+// summing two tensor-core products. hi = bf16 nearest to W, lo = bf16 nearest to
+// W - hi (exact in fp32), so hi + lo carries 16 significant bits of W and every
+// product with a bf16 activation is exact in fp32.
+//
+// Packed weight (written once by router_pack_kernel; both halves of one 16-expert
+// x 32-dim tile side by side, the tile in MFMA A-operand order): for expert e and
+// dim k, with tile = (e / 16) * (H / 32) + k / 32 and lane = 16 * ((k % 32) / 8) + e % 16,
+//   hi at byte 2048 * tile + 16 * lane + 2 * (k % 8), lo 1024 bytes further.
+// A wave's 16-byte load of one tile half is one contiguous 1 KB.
+//
+// GEMM (router_gemm_kernel<ME, NT, PASSES>): each wave computes C^T[16 ME experts x
+// 16 NT tokens] over one K range with v_mfma_f32_16x16x32_bf16 (A = weight tile,
+// B = x^T: lane (token n16, group j) holds x[token][32 kc + 8 j .. + 8]), the next
+// k-chunk's loads always issued before the current chunk is multiplied. The 4 waves
+// of a workgroup take 4 consecutive K ranges of the same tile and add their results
+// in LDS in wave order; the workgroup stores one partial sum per logit. Rows past
+// the last token read zeros (buffer bounds) and are not stored.
+//
+// Reduction and top-k (router_topk_kernel, one workgroup per token): the partial
+// sums of a logit are added in partial order, the logits stored, then k rounds of a
+// block argmax (larger value first, equal values to the lower expert index).
+#include "hpa_internal.hpp"
+
+namespace hpa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kBufDword3 = 0x00020000;
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), kBufDword3);
+}
+
+__device__ inline u32x4 bload16(rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), 0, 0);
+}
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (NaN stays NaN)
+__device__ inline uint32_t bf16_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// One thread per 8 consecutive dims of one expert: both halves of 8 weights.
+__global__ __launch_bounds__(256) void router_pack_kernel(const float* __restrict__ w, int E, int H,
+                                                          uint8_t* __restrict__ packed) {
+  const int64_t g = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int groups = H / 8;
+  if (g >= int64_t(E) * groups) return;
+  const int e = static_cast<int>(g / groups), k0 = static_cast<int>(g % groups) * 8;
+  const f32x4* src = reinterpret_cast<const f32x4*>(w + int64_t(e) * H + k0);
+  const f32x4 a = src[0], b = src[1];
+  const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  u32x4 hi, lo;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t h2 = 0, l2 = 0;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float x = v[2 * p + s];
+      const uint32_t h = bf16_rne(x);
+      const float r = x - __builtin_bit_cast(float, h << 16);     // exact: x and h agree in their top 8 bits
+      h2 |= h << (16 * s);
+      l2 |= bf16_rne(r) << (16 * s);
+    }
+    hi[p] = h2;
+    lo[p] = l2;
+  }
+  const int64_t tile = int64_t(e / 16) * (H / 32) + k0 / 32;
+  const int lane = 16 * ((k0 % 32) / 8) + e % 16;
+  uint8_t* dst = packed + tile * 2048 + 16 * lane;
+  *reinterpret_cast<u32x4*>(dst) = hi;
+  *reinterpret_cast<u32x4*>(dst + 1024) = lo;
+}
+
+template <int ME, int NT>
+struct Frag {
+  u32x4 hi[ME], lo[ME], x[NT];
+};
+
+template <int ME, int NT, int PASSES>
+__global__ __launch_bounds__(256) void router_gemm_kernel(RouterArgs a) {
+  __shared__ f32x4 red[4][ME * NT][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int m16 = lane & 15, j = lane >> 4;
+  const RouterPlan& p = a.p;
+  const int nkc = a.H / 32;
+  const int wg = blockIdx.x;
+  const int ksg = wg % p.partial_slots;
+  const int rest = wg / p.partial_slots;
+  const int eg = rest % p.n_eg, tg = rest / p.n_eg;
+  const int ks = 4 * ksg + wave;
+  const int c0 = min(ks * p.kw, nkc), c1 = min(c0 + p.kw, nkc);
+  const int eb0 = eg * ME, tok0 = tg * 16 * NT;
+  const int rows = min(a.T - tok0, 16 * NT);
+  const rsrc_t rw = make_rsrc(a.packed, static_cast<uint32_t>(int64_t(a.E) * a.H * 4));
+  const rsrc_t rx = make_rsrc(a.x + int64_t(tok0) * a.H, static_cast<uint32_t>(rows * a.H * 2));
+
+  auto load = [&](Frag<ME, NT>& f, int kc) {
+#pragma unroll
+    for (int me = 0; me < ME; ++me) {
+      const uint32_t off = static_cast<uint32_t>((int64_t(eb0 + me) * nkc + kc) * 2048 + 16 * lane);
+      f.hi[me] = bload16(rw, off);
+      if (PASSES == 2) f.lo[me] = bload16(rw, off + 1024);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      f.x[nt] = bload16(rx, static_cast<uint32_t>(((16 * nt + m16) * a.H + 32 * kc + 8 * j) * 2));
+  };
+  f32x4 acc[ME][NT];
+#pragma unroll
+  for (int me = 0; me < ME; ++me)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[me][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mul = [&](const Frag<ME, NT>& f) {
+#pragma unroll
+    for (int me = 0; me < ME; ++me)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[me][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.hi[me]), as_bf16x8(f.x[nt]), acc[me][nt], 0, 0, 0);
+        if (PASSES == 2)
+          acc[me][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.lo[me]), as_bf16x8(f.x[nt]), acc[me][nt], 0, 0, 0);
+      }
+  };
+  Frag<ME, NT> fa, fb;
+  int kc = c0;
+  if (kc < c1) load(fa, kc);
+  while (kc < c1) {
+    if (kc + 1 < c1) load(fb, kc + 1);
+    mul(fa);
+    if (++kc >= c1) break;
+    if (kc + 1 < c1) load(fa, kc + 1);
+    mul(fb);
+    ++kc;
+  }
+#pragma unroll
+  for (int me = 0; me < ME; ++me)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) red[wave][me * NT + nt][lane] = acc[me][nt];
+  __syncthreads();
+  // thread -> (tile, lane) entries; the 4 waves' results added in wave order
+  for (int idx = threadIdx.x; idx < ME * NT * 64; idx += 256) {
+    const int r = idx / 64, l = idx % 64;
+    const int me = r / NT, nt = r % NT;
+    const int tok = 16 * nt + (l & 15);
+    if (tok >= rows) continue;
+    f32x4 s = red[0][r][l];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) s += red[w][r][l];
+    const int e = 16 * (eb0 + me) + 4 * (l >> 4);
+    *reinterpret_cast<f32x4*>(a.part + (int64_t(ksg) * a.T + tok0 + tok) * a.E + e) = s;
+  }
+}
+
+// (value, expert) order of the top-k: larger value first, equal values by lower index
+__device__ inline bool better(float v, int i, float w, int k) { return v > w || (v == w && i < k); }
+
+__global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a) {
+  constexpr int Q = kRouterMaxExperts / 256;
+  constexpr int kBatch = 8;
+  __shared__ float bv[2][4];
+  __shared__ int bi[2][4];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slots = a.p.partial_slots;
+  float v[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int e = threadIdx.x + 256 * q;
+    v[q] = -INFINITY;
+    if (e >= a.E) continue;
+    const float* src = a.part + int64_t(t) * a.E + e;
+    const int64_t stride = int64_t(a.T) * a.E;
+    float s = 0.f;
+    for (int s0 = 0; s0 < slots; s0 += kBatch) {
+      float pv[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) pv[i] = s0 + i < slots ? src[(s0 + i) * stride] : 0.f;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (s0 + i < slots) s += pv[i];
+    }
+    v[q] = s;
+    a.logits[int64_t(t) * a.E + e] = s;
+  }
+  if (a.top_k == 0) return;
+  bool taken[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) taken[q] = false;
+  for (int r = 0; r < a.top_k; ++r) {
+    float bvv = -INFINITY;
+    int bii = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int e = threadIdx.x + 256 * q;
+      if (e < a.E && !taken[q] && better(v[q], e, bvv, bii)) {
+        bvv = v[q];
+        bii = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bvv, off, 64);
+      const int oi = __shfl_xor(bii, off, 64);
+      if (better(ov, oi, bvv, bii)) {
+        bvv = ov;
+        bii = oi;
+      }
+    }
+    if (lane == 0) {
+      bv[r & 1][wave] = bvv;
+      bi[r & 1][wave] = bii;
+    }
+    __syncthreads();
+    float wv = bv[r & 1][0];
+    int wi = bi[r & 1][0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      if (better(bv[r & 1][w], bi[r & 1][w], wv, wi)) {
+        wv = bv[r & 1][w];
+        wi = bi[r & 1][w];
+      }
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (threadIdx.x + 256 * q == wi) taken[q] = true;
+    if (threadIdx.x == 0) {
+      a.topk_idx[int64_t(t) * a.top_k + r] = wi;
+      a.topk_val[int64_t(t) * a.top_k + r] = wv;
+    }
+  }
+}
+
+template <int ME, int NT>
+void gemm_launch(const RouterArgs& a, hipStream_t stream) {
+  if (a.passes == 2)
+    hipLaunchKernelGGL((router_gemm_kernel<ME, NT, 2>), dim3(a.p.workgroups), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((router_gemm_kernel<ME, NT, 1>), dim3(a.p.workgroups), dim3(256), 0, stream, a);
+}
+
+}  // namespace
+
+hipError_t launch_router_pack(const float* w, int experts, int hidden, uint8_t* packed, hipStream_t stream) {
+  const int64_t threads = int64_t(experts) * (hidden / 8);
+  hipLaunchKernelGGL(router_pack_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream, w,
+                     experts, hidden, packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
+  if (a.p.me == 1 && a.p.nt == 1) gemm_launch<1, 1>(a, stream);
+  else if (a.p.me == 1 && a.p.nt == 4) gemm_launch<1, 4>(a, stream);
+  else gemm_launch<2, 4>(a, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(router_topk_kernel, dim3(a.T), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace hpa

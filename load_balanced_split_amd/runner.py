@@ -143,3 +143,41 @@ class DeviceStep:
 
     def output_f64(self) -> np.ndarray:
         return self.out.float().cpu().numpy().astype(np.float64)
+
+
+class RouterStep:
+    """A router workload (inputs.RouterWorkload) resident in HBM: activations, the
+    fp32 weight, its packed split form, logits, top-k outputs and the workspace."""
+
+    def __init__(self, rw, top_k: int = 8, device: str = "cuda"):
+        import torch
+        self.torch = torch
+        self.rw = rw
+        self.top_k = top_k
+        dev = torch.device(device)
+        T, E, H = rw.tokens, rw.experts, rw.hidden
+        self.x = torch.from_numpy(np.ascontiguousarray(rw.x).view(np.int16)).view(torch.bfloat16).to(dev)
+        self.w = torch.from_numpy(np.ascontiguousarray(rw.w, np.float32)).to(dev)
+        self.packed = torch.empty(E * H * 4, dtype=torch.uint8, device=dev)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        self.topk_idx = torch.empty((T, max(top_k, 1)), dtype=torch.int32, device=dev)
+        self.topk_val = torch.empty((T, max(top_k, 1)), dtype=torch.float32, device=dev)
+        ws = _lib.hpa_router_workspace_size(T, E, H)
+        self.workspace = torch.empty(max(ws, 16) // 4, dtype=torch.float32, device=dev)
+        self.pack()
+
+    def pack(self):
+        _lib.hpa_router_pack_weights(self.w, self.packed)
+
+    def run(self, passes: int = 2, packed=None):
+        _lib.hpa_router_gemm(self.x, self.packed if packed is None else packed, self.rw.experts, passes,
+                             self.logits, self.top_k, self.topk_idx[:, :self.top_k] if self.top_k else None,
+                             self.topk_val[:, :self.top_k] if self.top_k else None, self.workspace)
+
+    def results(self):
+        """(logits fp64 [T, E], top-k indices int64 [T, k], top-k values fp64 [T, k])."""
+        self.torch.cuda.synchronize()
+        k = self.top_k
+        return (self.logits.cpu().numpy().astype(np.float64),
+                self.topk_idx[:, :k].cpu().numpy().astype(np.int64),
+                self.topk_val[:, :k].cpu().numpy().astype(np.float64))

@@ -145,3 +145,31 @@ def test_stream_read_probe_validation(L):
     assert f(None, 64, 4, sink, None) == 1
     assert f(buf, 64, 4, None, None) == 1
     assert f(buf, 64, -1, sink, None) == 1
+
+
+def test_router_validation_and_workspace_size(L):
+    n = ctypes.c_size_t(0)
+    ws = L.hpa_router_workspace_size
+    assert ws(1, 256, 7168, ctypes.byref(n)) == 0
+    # one token, 16 expert blocks: 112 K ranges of 2 chunks, 4 per workgroup -> 28 partial sums per logit
+    assert n.value == 28 * 1 * 256 * 4
+    assert ws(0, 256, 7168, ctypes.byref(n)) == 0 and n.value == 0
+    assert ws(4096, 256, 7168, ctypes.byref(n)) == 0 and n.value == 2 * 4096 * 256 * 4
+    for T, E, H, status in ((1, 8, 64, 2), (1, 1040, 64, 2), (1, 24, 64, 2), (1, 16, 48, 2), (1, 16, 0, 2),
+                            (1, 16, 1 << 17, 2), (-1, 16, 64, 1), ((1 << 20) + 1, 16, 64, 1)):
+        assert ws(T, E, H, ctypes.byref(n)) == status, (T, E, H)
+    p, q = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    g = L.hpa_router_gemm
+    big = ctypes.c_size_t(1 << 30)
+    assert g(p, p, 4, 64, 64, 3, q, 2, q, q, p, big, None) == 1            # passes
+    assert g(p, p, 4, 64, 64, 2, q, 33, q, q, p, big, None) == 1           # top_k > 32
+    assert g(p, p, 4, 16, 64, 2, q, 17, q, q, p, big, None) == 1           # top_k > experts
+    assert g(p, p, 4, 64, 64, 2, q, 2, None, q, p, big, None) == 1         # top-k outputs missing
+    assert g(None, p, 4, 64, 64, 2, q, 2, q, q, p, big, None) == 1
+    assert g(ctypes.c_void_p(4100), p, 4, 64, 64, 2, q, 2, q, q, p, big, None) == 1   # misaligned x
+    assert g(p, p, 4, 64, 64, 2, q, 2, q, q, p, ctypes.c_size_t(16), None) == 3       # workspace
+    assert g(None, None, 0, 64, 64, 2, None, 0, None, None, None, ctypes.c_size_t(0), None) == 0   # no tokens
+    pk = L.hpa_router_pack_weights
+    assert pk(None, 64, 64, p, None) == 1
+    assert pk(ctypes.c_void_p(4100), 64, 64, p, None) == 1
+    assert pk(p, 20, 64, p, None) == 2
