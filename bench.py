@@ -55,6 +55,7 @@ def parse():
     p.add_argument("--no-static", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probe", action="store_true", help="skip the plain streaming-read probe")
+    p.add_argument("--no-router", action="store_true", help="skip the split-precision router GEMM")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--trace", action="store_true",
                    help="use the instrumented build and report per-CU busy time (tail balance) instead")
@@ -413,6 +414,8 @@ def main():
                      "balanced_speedup": round(t / step_s, 3),
                      "balanced_attn_speedup": round(e["attn"] / ev["attn"], 3)}
         result["static_split_kv"] = st
+    if not args.no_router:
+        result["router_gemm"] = router_bench(args, stream)
     if not args.no_probe:
         probe = stream_read_probe(stream)
         probe["attn_frac_of_probe"] = round(achieved / probe["gbps"], 4)
@@ -420,6 +423,83 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, kv_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+PEAK_BF16_TFLOPS = 2500.0
+ROUTER_SHAPES = [(1, 256, 7168), (64, 256, 7168), (4096, 256, 7168)]
+ROUTER_TOP_K = 8
+
+
+def router_bytes_flops(T, E, H, passes, k=ROUTER_TOP_K):
+    """Algorithmic HBM bytes (the weight halves read, x read, logits and top-k written)
+    and MFMA flops of one router call."""
+    nbytes = E * H * 2 * passes + T * H * 2 + T * E * 4 + T * k * 8
+    return nbytes, 2 * passes * T * E * H
+
+
+def router_bench(args, stream):
+    """The split-precision router GEMM (pack once, then GEMM + top-k per call) on
+    synthetic bf16 activations and an fp32 weight: per shape the time of one call,
+    both kernels, replayed from a HIP graph over rotating copies (weights and
+    activations read from HBM), its roofline, and PyTorch's fp32 GEMM + top-k on the
+    same data for context."""
+    import torch
+    from load_balanced_split_amd import inputs
+    from load_balanced_split_amd.runner import RouterStep
+    out = {}
+    for T, E, H in ROUTER_SHAPES:
+        rw = inputs.router_workload(T, E, H, seed=T)
+        foot = E * H * 4 + T * H * 2 + T * E * 4
+        R = min(64, max(2, math.ceil(2 * MALL_BYTES / foot) + 1))
+        steps = [RouterStep(rw, top_k=ROUTER_TOP_K) for _ in range(R)]
+        res = {"tokens": T, "experts": E, "hidden": H, "top_k": ROUTER_TOP_K, "rotating_copies": R}
+        for passes in (2, 1):
+            for s in steps:
+                s.run(passes)
+            torch.cuda.synchronize()
+            ref = steps[0].logits.clone()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in steps:
+                    s.run(passes)
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(2, math.ceil(40 / R))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * R)
+            assert torch.equal(steps[0].logits, ref), "router graph replay differs from eager"
+            nbytes, flops = router_bytes_flops(T, E, H, passes)
+            t_hbm, t_mfma = nbytes / (PEAK_HBM_GBPS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12)
+            if t_hbm >= t_mfma:
+                roof = {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                        "unit": "GB/s"}
+            else:
+                roof = {"bound": "mfma", "achieved": round(flops / (us * 1e-6) / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s"}
+            roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+            res[f"passes{passes}"] = {"us_per_call": round(us, 2), "roofline": roof}
+            del g
+        # context: PyTorch's fp32 GEMM on the fp32 weight, then torch.topk
+        xf = steps[0].x.float()
+        wt = steps[0].w
+        for _ in range(3):
+            torch.topk(xf @ wt.t(), ROUTER_TOP_K, dim=1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            torch.topk(xf @ wt.t(), ROUTER_TOP_K, dim=1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["torch_fp32_gemm_topk_us"] = round(e0.elapsed_time(e1) * 1e3 / 20, 2)
+        out[f"T{T}"] = res
+        del steps
+    return out
 
 
 def stream_read_probe(stream, gib=4, launches=10):

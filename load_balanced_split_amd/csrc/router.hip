@@ -24,8 +24,9 @@
 // the last token read zeros (buffer bounds) and are not stored.
 //
 // Reduction and top-k (router_topk_kernel, one workgroup per token): the partial
-// sums of a logit are added in partial order, the logits stored, then k rounds of a
-// block argmax (larger value first, equal values to the lower expert index).
+// sums of a logit are added in partial order and the logits stored; the top-k
+// (larger value first, equal values to the lower expert index) by ranks counted in
+// LDS, first within segments of 64 experts, then among the segments' k best.
 #include "hpa_internal.hpp"
 
 namespace hpa {
@@ -172,79 +173,101 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(RouterArgs a) {
 }
 
 // (value, expert) order of the top-k: larger value first, equal values by lower index
-__device__ inline bool better(float v, int i, float w, int k) { return v > w || (v == w && i < k); }
+// (branch-free: evaluated per lane, without divergent control flow)
+__device__ inline bool better(float v, int i, float w, int k) { return (v > w) | ((v == w) & (i < k)); }
 
+// One workgroup per token, Q experts per thread (E <= 256 Q): every logit's partial
+// sums (loads of a batch issued together at clamped, in-bounds addresses, added in
+// partial order), the logits stored; then the top-k in two rank passes over LDS,
+// ranks counted in the token's order (larger value first, equal values by lower
+// expert index). Pass 1: each logit's rank within its segment of 64 experts; the
+// k best of every segment survive (every global top-k logit does). Pass 2: each
+// survivor's rank among the survivors, which for the global top-k is the global
+// rank and for every other survivor is at least k; those below k are written at
+// their rank.
+template <int Q>
 __global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a) {
-  constexpr int Q = kRouterMaxExperts / 256;
-  constexpr int kBatch = 8;
-  __shared__ float bv[2][4];
-  __shared__ int bi[2][4];
+  constexpr int kBatch = 32 / Q;
+  constexpr int kSegs = kRouterMaxExperts / 64;
+  __shared__ f32x4 lv[kRouterMaxExperts / 4];
+  __shared__ float sv[kSegs * kRouterMaxTopK];
+  __shared__ int si[kSegs * kRouterMaxTopK];
   const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slots = a.p.partial_slots;
+  const int64_t stride = int64_t(a.T) * a.E;
+  const float* base = a.part + int64_t(t) * a.E;
   float v[Q];
+  int id[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int e = threadIdx.x + 256 * q;
-    v[q] = -INFINITY;
-    if (e >= a.E) continue;
-    const float* src = a.part + int64_t(t) * a.E + e;
-    const int64_t stride = int64_t(a.T) * a.E;
-    float s = 0.f;
-    for (int s0 = 0; s0 < slots; s0 += kBatch) {
-      float pv[kBatch];
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) pv[i] = s0 + i < slots ? src[(s0 + i) * stride] : 0.f;
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i)
-        if (s0 + i < slots) s += pv[i];
-    }
-    v[q] = s;
-    a.logits[int64_t(t) * a.E + e] = s;
+    v[q] = 0.f;
+    id[q] = e < a.E ? e : -1;
   }
-  if (a.top_k == 0) return;
-  bool taken[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) taken[q] = false;
-  for (int r = 0; r < a.top_k; ++r) {
-    float bvv = -INFINITY;
-    int bii = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int e = threadIdx.x + 256 * q;
-      if (e < a.E && !taken[q] && better(v[q], e, bvv, bii)) {
-        bvv = v[q];
-        bii = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bvv, off, 64);
-      const int oi = __shfl_xor(bii, off, 64);
-      if (better(ov, oi, bvv, bii)) {
-        bvv = ov;
-        bii = oi;
-      }
-    }
-    if (lane == 0) {
-      bv[r & 1][wave] = bvv;
-      bi[r & 1][wave] = bii;
-    }
-    __syncthreads();
-    float wv = bv[r & 1][0];
-    int wi = bi[r & 1][0];
-#pragma unroll
-    for (int w = 1; w < 4; ++w)
-      if (better(bv[r & 1][w], bi[r & 1][w], wv, wi)) {
-        wv = bv[r & 1][w];
-        wi = bi[r & 1][w];
-      }
+  for (int s0 = 0; s0 < slots; s0 += kBatch) {
+    float pv[Q][kBatch];
 #pragma unroll
     for (int q = 0; q < Q; ++q)
-      if (threadIdx.x + 256 * q == wi) taken[q] = true;
-    if (threadIdx.x == 0) {
-      a.topk_idx[int64_t(t) * a.top_k + r] = wi;
-      a.topk_val[int64_t(t) * a.top_k + r] = wv;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        pv[q][i] = base[min(s0 + i, slots - 1) * stride + max(id[q], 0)];
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (s0 + i < slots) v[q] += pv[q][i];
+  }
+  float* lvf = reinterpret_cast<float*>(lv);
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+    if (id[q] >= 0) {
+      a.logits[int64_t(t) * a.E + id[q]] = v[q];
+      lvf[id[q]] = v[q];
+    }
+  const int k = a.top_k;
+  if (k == 0) return;
+  const int nseg = (a.E + 63) / 64;
+  for (int c = threadIdx.x; c < nseg * k; c += 256) si[c] = -1;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    if (id[q] < 0) continue;
+    const int seg = id[q] / 64;
+    const int n4 = min(64, a.E - 64 * seg) / 4;       // E is a multiple of 16
+    int rank = 0;
+    f32x4 w[16];                                      // the segment's LDS reads all in flight
+#pragma unroll
+    for (int u = 0; u < 16; ++u) w[u] = lv[16 * seg + min(u, n4 - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) rank += int((u < n4) & better(w[u][c], 64 * seg + 4 * u + c, v[q], id[q]));
+    if (rank < k) {
+      sv[seg * k + rank] = v[q];
+      si[seg * k + rank] = id[q];
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < nseg * k; c += 256) {
+    const int ic = si[c];
+    if (ic < 0) continue;
+    const float vc = sv[c];
+    const int n = nseg * k;
+    int rank = 0;
+    for (int d0 = 0; d0 < n; d0 += 16) {             // 16 survivors' LDS reads in flight
+      float v2[16];
+      int i2[16];
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        v2[d] = sv[min(d0 + d, n - 1)];
+        i2[d] = d0 + d < n ? si[min(d0 + d, n - 1)] : -1;
+      }
+#pragma unroll
+      for (int d = 0; d < 16; ++d) rank += int((i2[d] >= 0) & better(v2[d], i2[d], vc, ic));
+    }
+    if (rank < k) {
+      a.topk_idx[int64_t(t) * k + rank] = ic;
+      a.topk_val[int64_t(t) * k + rank] = vc;
     }
   }
 }
@@ -272,7 +295,9 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
   else gemm_launch<2, 4>(a, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(router_topk_kernel, dim3(a.T), dim3(256), 0, stream, a);
+  if (a.E <= 256) hipLaunchKernelGGL(router_topk_kernel<1>, dim3(a.T), dim3(256), 0, stream, a);
+  else if (a.E <= 512) hipLaunchKernelGGL(router_topk_kernel<2>, dim3(a.T), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(router_topk_kernel<4>, dim3(a.T), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
