@@ -303,9 +303,12 @@ constexpr int kRouterMaxTokens = 1 << 20;
 constexpr int kRouterTargetWaves = 4096;   // 4 per SIMD of 256 compute units
 struct RouterPlan {
   int me, nt;            // 16-expert blocks and 16-token blocks per wave
-  int kw;                // 32-dim k-chunks per K range (one K range per wave)
+  int wx;                // 1: a workgroup's 4 waves take 4 expert groups of one K range (they
+                         // share the token fragments through L1); 0: 4 K ranges of one tile
+                         // (added in LDS)
+  int kw;                // 32-dim k-chunks per K range
   int n_eg, n_tg;        // expert groups (me blocks) and token groups (nt blocks)
-  int partial_slots;     // workgroups per tile = partial sums per logit (4 K ranges each)
+  int partial_slots;     // partial sums per logit
   int64_t workgroups;
   static RouterPlan make(int tokens, int experts, int hidden) {
     RouterPlan p{};
@@ -314,7 +317,18 @@ struct RouterPlan {
     p.me = tokens > 64 && neb % 2 == 0 ? 2 : 1;
     p.n_eg = neb / p.me;
     p.n_tg = (tokens + 16 * p.nt - 1) / (16 * p.nt);
+    p.wx = tokens > 64 && p.n_eg % 4 == 0 ? 1 : 0;
     const int64_t tiles = int64_t(p.n_eg) * p.n_tg;
+    if (p.wx) {
+      // workgroups of 4 expert groups; enough K ranges for ~2 workgroups per compute unit
+      const int64_t wg_tiles = tiles / 4;
+      int64_t ranges = (kRouterTargetWaves / 8 + wg_tiles - 1) / wg_tiles;
+      ranges = std::min<int64_t>(std::max<int64_t>(ranges, 1), std::max(1, nkc / 8));
+      p.kw = static_cast<int>((nkc + ranges - 1) / ranges);
+      p.partial_slots = static_cast<int>(ranges);
+      p.workgroups = wg_tiles * ranges;
+      return p;
+    }
     int64_t ranges = tiles > 0 ? (kRouterTargetWaves + tiles - 1) / tiles : 1;
     ranges = std::min<int64_t>(std::max<int64_t>(ranges, 1), std::max(1, nkc / 2));   // at least 2 chunks each
     ranges = (ranges + 3) / 4 * 4;

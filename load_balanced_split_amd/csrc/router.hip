@@ -18,15 +18,19 @@
 // GEMM (router_gemm_kernel<ME, NT, PASSES>): each wave computes C^T[16 ME experts x
 // 16 NT tokens] over one K range with v_mfma_f32_16x16x32_bf16 (A = weight tile,
 // B = x^T: lane (token n16, group j) holds x[token][32 kc + 8 j .. + 8]), the next
-// k-chunk's loads always issued before the current chunk is multiplied. The 4 waves
-// of a workgroup take 4 consecutive K ranges of the same tile and add their results
-// in LDS in wave order; the workgroup stores one partial sum per logit. Rows past
-// the last token read zeros (buffer bounds) and are not stored.
+// k-chunk's loads always issued before the current chunk is multiplied. For few
+// tokens the 4 waves of a workgroup take 4 consecutive K ranges of the same tile and
+// add their results in LDS in wave order (one partial sum per logit per workgroup);
+// for many tokens (WX) they take 4 expert groups of the same tokens and K range, so
+// the token fragments they all load are shared through L1, and each wave stores its
+// own partial sums. Rows past the last token read zeros (buffer bounds) and are not
+// stored.
 //
 // Reduction and top-k (router_topk_kernel, one workgroup per token): the partial
 // sums of a logit are added in partial order and the logits stored; the top-k
-// (larger value first, equal values to the lower expert index) by ranks counted in
-// LDS, first within segments of 64 experts, then among the segments' k best.
+// (larger value first, equal values to the lower expert index) by ranks of 64-bit
+// (value, expert) keys in LDS, within 64-expert segments and then among the
+// segments' k largest.
 #include "hpa_internal.hpp"
 
 namespace hpa {
@@ -47,8 +51,8 @@ __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(ub, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), kBufDword3);
 }
 
-__device__ inline u32x4 bload16(rsrc_t r, uint32_t voff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), 0, 0);
+__device__ inline u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -97,9 +101,9 @@ struct Frag {
   u32x4 hi[ME], lo[ME], x[NT];
 };
 
-template <int ME, int NT, int PASSES>
+template <int ME, int NT, int PASSES, bool WX>
 __global__ __launch_bounds__(256) void router_gemm_kernel(RouterArgs a) {
-  __shared__ f32x4 red[4][ME * NT][64];
+  __shared__ f32x4 red[WX ? 1 : 4][WX ? 1 : ME * NT][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int m16 = lane & 15, j = lane >> 4;
@@ -108,24 +112,33 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(RouterArgs a) {
   const int wg = blockIdx.x;
   const int ksg = wg % p.partial_slots;
   const int rest = wg / p.partial_slots;
-  const int eg = rest % p.n_eg, tg = rest / p.n_eg;
-  const int ks = 4 * ksg + wave;
+  // WX: the 4 waves take expert groups 4 q .. 4 q + 3 of K range ksg; otherwise K ranges
+  // 4 ksg .. 4 ksg + 3 of expert group eg
+  const int n_egw = WX ? p.n_eg / 4 : p.n_eg;
+  const int eg = WX ? 4 * (rest % n_egw) + wave : rest % n_egw, tg = rest / n_egw;
+  const int ks = WX ? ksg : 4 * ksg + wave;
   const int c0 = min(ks * p.kw, nkc), c1 = min(c0 + p.kw, nkc);
   const int eb0 = eg * ME, tok0 = tg * 16 * NT;
   const int rows = min(a.T - tok0, 16 * NT);
   const rsrc_t rw = make_rsrc(a.packed, static_cast<uint32_t>(int64_t(a.E) * a.H * 4));
   const rsrc_t rx = make_rsrc(a.x + int64_t(tok0) * a.H, static_cast<uint32_t>(rows * a.H * 2));
 
+  // lane-constant parts of the offsets in VGPRs, the chunk's part in the scalar offset
+  uint32_t xoff[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) xoff[nt] = static_cast<uint32_t>(((16 * nt + m16) * a.H + 8 * j) * 2);
+  const uint32_t woff = 16 * lane;
   auto load = [&](Frag<ME, NT>& f, int kc) {
+    const uint32_t kx = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(64 * kc));
 #pragma unroll
     for (int me = 0; me < ME; ++me) {
-      const uint32_t off = static_cast<uint32_t>((int64_t(eb0 + me) * nkc + kc) * 2048 + 16 * lane);
-      f.hi[me] = bload16(rw, off);
-      if (PASSES == 2) f.lo[me] = bload16(rw, off + 1024);
+      const uint32_t tw = static_cast<uint32_t>(
+          __builtin_amdgcn_readfirstlane(static_cast<int>((int64_t(eb0 + me) * nkc + kc) * 2048)));
+      f.hi[me] = bload16(rw, woff, tw);
+      if (PASSES == 2) f.lo[me] = bload16(rw, woff + 1024, tw);
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      f.x[nt] = bload16(rx, static_cast<uint32_t>(((16 * nt + m16) * a.H + 32 * kc + 8 * j) * 2));
+    for (int nt = 0; nt < NT; ++nt) f.x[nt] = bload16(rx, xoff[nt], kx);
   };
   f32x4 acc[ME][NT];
 #pragma unroll
@@ -142,56 +155,91 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(RouterArgs a) {
           acc[me][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.lo[me]), as_bf16x8(f.x[nt]), acc[me][nt], 0, 0, 0);
       }
   };
-  Frag<ME, NT> fa, fb;
-  int kc = c0;
-  if (kc < c1) load(fa, kc);
-  while (kc < c1) {
-    if (kc + 1 < c1) load(fb, kc + 1);
-    mul(fa);
-    if (++kc >= c1) break;
-    if (kc + 1 < c1) load(fa, kc + 1);
-    mul(fb);
-    ++kc;
+  // a ring of kDepth fragments: the loads of chunk kc + kDepth - 1 go out before chunk
+  // kc is multiplied (chunk indices clamped into the range, so every load is issued
+  // and in bounds). The steady loop has no branch around a load or a product, so the
+  // waits before each product count only that fragment's loads; the last < kDepth
+  // chunks, already loaded, are multiplied after it.
+  constexpr int kDepth = 3;
+  if (c0 < c1) {
+    Frag<ME, NT> f[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d) load(f[d], min(c0 + d, c1 - 1));
+    int kc = c0;
+    for (; kc + kDepth <= c1; kc += kDepth) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        load(f[(d + kDepth - 1) % kDepth], min(kc + d + kDepth - 1, c1 - 1));
+        __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the products
+        mul(f[d]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d)
+      if (kc + d < c1) mul(f[d]);
   }
+  if constexpr (WX) {
 #pragma unroll
-  for (int me = 0; me < ME; ++me)
+    for (int me = 0; me < ME; ++me)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) red[wave][me * NT + nt][lane] = acc[me][nt];
-  __syncthreads();
-  // thread -> (tile, lane) entries; the 4 waves' results added in wave order
-  for (int idx = threadIdx.x; idx < ME * NT * 64; idx += 256) {
-    const int r = idx / 64, l = idx % 64;
-    const int me = r / NT, nt = r % NT;
-    const int tok = 16 * nt + (l & 15);
-    if (tok >= rows) continue;
-    f32x4 s = red[0][r][l];
+      for (int nt = 0; nt < NT; ++nt) {
+        const int tok = 16 * nt + m16;
+        if (tok < rows)
+          *reinterpret_cast<f32x4*>(a.part + (int64_t(ksg) * a.T + tok0 + tok) * a.E + 16 * (eb0 + me) + 4 * j) =
+              acc[me][nt];
+      }
+  } else {
 #pragma unroll
-    for (int w = 1; w < 4; ++w) s += red[w][r][l];
-    const int e = 16 * (eb0 + me) + 4 * (l >> 4);
-    *reinterpret_cast<f32x4*>(a.part + (int64_t(ksg) * a.T + tok0 + tok) * a.E + e) = s;
+    for (int me = 0; me < ME; ++me)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) red[wave][me * NT + nt][lane] = acc[me][nt];
+    __syncthreads();
+    // thread -> (tile, lane) entries; the 4 waves' results added in wave order
+    for (int idx = threadIdx.x; idx < ME * NT * 64; idx += 256) {
+      const int r = idx / 64, l = idx % 64;
+      const int me = r / NT, nt = r % NT;
+      const int tok = 16 * nt + (l & 15);
+      if (tok >= rows) continue;
+      f32x4 s = red[0][r][l];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) s += red[w][r][l];
+      const int e = 16 * (eb0 + me) + 4 * (l >> 4);
+      *reinterpret_cast<f32x4*>(a.part + (int64_t(ksg) * a.T + tok0 + tok) * a.E + e) = s;
+    }
   }
 }
 
-// (value, expert) order of the top-k: larger value first, equal values by lower index
-// (branch-free: evaluated per lane, without divergent control flow)
-__device__ inline bool better(float v, int i, float w, int k) { return (v > w) | ((v == w) & (i < k)); }
+
+// A logit and its expert as one 64-bit key whose unsigned order is the top-k
+// order: the float's bits mapped to an order-preserving uint32 (-0 taken as +0)
+// above the complement of the expert index (equal values: lower index first).
+// Key 0 is below every real key and stands for "no candidate".
+__device__ inline uint64_t topk_key(float v, int e) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (uint64_t(o) << 32) | uint32_t(~e);
+}
+__device__ inline float key_value(uint64_t k) {
+  const uint32_t o = uint32_t(k >> 32);
+  return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ inline int key_expert(uint64_t k) { return int(~uint32_t(k)); }
 
 // One workgroup per token, Q experts per thread (E <= 256 Q): every logit's partial
 // sums (loads of a batch issued together at clamped, in-bounds addresses, added in
-// partial order), the logits stored; then the top-k in two rank passes over LDS,
-// ranks counted in the token's order (larger value first, equal values by lower
-// expert index). Pass 1: each logit's rank within its segment of 64 experts; the
-// k best of every segment survive (every global top-k logit does). Pass 2: each
-// survivor's rank among the survivors, which for the global top-k is the global
-// rank and for every other survivor is at least k; those below k are written at
-// their rank.
+// partial order), the logits stored; then the top-k by ranks over the keys in LDS
+// (keys are distinct, so a rank is the count of larger keys). Pass 1: each key's
+// rank within its segment of 64 experts; the k largest of every segment survive
+// (every global top-k key does). Pass 2: each survivor's rank among the survivors,
+// which for the global top-k is its global rank and for every other survivor is at
+// least k; those below k are written at their rank.
 template <int Q>
 __global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a) {
   constexpr int kBatch = 32 / Q;
   constexpr int kSegs = kRouterMaxExperts / 64;
-  __shared__ f32x4 lv[kRouterMaxExperts / 4];
-  __shared__ float sv[kSegs * kRouterMaxTopK];
-  __shared__ int si[kSegs * kRouterMaxTopK];
+  __shared__ uint64_t lk[kRouterMaxExperts];
+  __shared__ uint64_t sk[kSegs * kRouterMaxTopK];
   const int t = blockIdx.x;
   const int slots = a.p.partial_slots;
   const int64_t stride = int64_t(a.T) * a.E;
@@ -217,67 +265,59 @@ __global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a) {
       for (int i = 0; i < kBatch; ++i)
         if (s0 + i < slots) v[q] += pv[q][i];
   }
-  float* lvf = reinterpret_cast<float*>(lv);
+  uint64_t key[Q];
 #pragma unroll
-  for (int q = 0; q < Q; ++q)
+  for (int q = 0; q < Q; ++q) {
+    key[q] = 0;
     if (id[q] >= 0) {
       a.logits[int64_t(t) * a.E + id[q]] = v[q];
-      lvf[id[q]] = v[q];
+      key[q] = topk_key(v[q], id[q]);
+      lk[id[q]] = key[q];
     }
+  }
   const int k = a.top_k;
   if (k == 0) return;
-  const int nseg = (a.E + 63) / 64;
-  for (int c = threadIdx.x; c < nseg * k; c += 256) si[c] = -1;
+  const int nseg = (a.E + 63) / 64, ns = nseg * k;
+  for (int c = threadIdx.x; c < ns; c += 256) sk[c] = 0;
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     if (id[q] < 0) continue;
     const int seg = id[q] / 64;
-    const int n4 = min(64, a.E - 64 * seg) / 4;       // E is a multiple of 16
+    const int n = min(64, a.E - 64 * seg);          // a multiple of 16
+    uint64_t w[64];
+#pragma unroll
+    for (int j = 0; j < 64; ++j) w[j] = lk[64 * seg + min(j, n - 1)];
     int rank = 0;
-    f32x4 w[16];                                      // the segment's LDS reads all in flight
 #pragma unroll
-    for (int u = 0; u < 16; ++u) w[u] = lv[16 * seg + min(u, n4 - 1)];
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) rank += int((u < n4) & better(w[u][c], 64 * seg + 4 * u + c, v[q], id[q]));
-    if (rank < k) {
-      sv[seg * k + rank] = v[q];
-      si[seg * k + rank] = id[q];
-    }
+    for (int j = 0; j < 64; ++j) rank += int((j < n) & (w[j] > key[q]));
+    if (rank < k) sk[seg * k + rank] = key[q];
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < nseg * k; c += 256) {
-    const int ic = si[c];
-    if (ic < 0) continue;
-    const float vc = sv[c];
-    const int n = nseg * k;
+  for (int c = threadIdx.x; c < ns; c += 256) {
+    const uint64_t kc = sk[c];
+    if (kc == 0) continue;
     int rank = 0;
-    for (int d0 = 0; d0 < n; d0 += 16) {             // 16 survivors' LDS reads in flight
-      float v2[16];
-      int i2[16];
+    for (int d0 = 0; d0 < ns; d0 += 16) {
+      uint64_t w[16];
 #pragma unroll
-      for (int d = 0; d < 16; ++d) {
-        v2[d] = sv[min(d0 + d, n - 1)];
-        i2[d] = d0 + d < n ? si[min(d0 + d, n - 1)] : -1;
-      }
+      for (int d = 0; d < 16; ++d) w[d] = sk[min(d0 + d, ns - 1)];
 #pragma unroll
-      for (int d = 0; d < 16; ++d) rank += int((i2[d] >= 0) & better(v2[d], i2[d], vc, ic));
+      for (int d = 0; d < 16; ++d) rank += int((d0 + d < ns) & (w[d] > kc));
     }
     if (rank < k) {
-      a.topk_idx[int64_t(t) * k + rank] = ic;
-      a.topk_val[int64_t(t) * k + rank] = vc;
+      a.topk_idx[int64_t(t) * k + rank] = key_expert(kc);
+      a.topk_val[int64_t(t) * k + rank] = key_value(kc);
     }
   }
 }
 
-template <int ME, int NT>
+template <int ME, int NT, bool WX>
 void gemm_launch(const RouterArgs& a, hipStream_t stream) {
   if (a.passes == 2)
-    hipLaunchKernelGGL((router_gemm_kernel<ME, NT, 2>), dim3(a.p.workgroups), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((router_gemm_kernel<ME, NT, 2, WX>), dim3(a.p.workgroups), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((router_gemm_kernel<ME, NT, 1>), dim3(a.p.workgroups), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((router_gemm_kernel<ME, NT, 1, WX>), dim3(a.p.workgroups), dim3(256), 0, stream, a);
 }
 
 }  // namespace
@@ -290,9 +330,10 @@ hipError_t launch_router_pack(const float* w, int experts, int hidden, uint8_t* 
 }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
-  if (a.p.me == 1 && a.p.nt == 1) gemm_launch<1, 1>(a, stream);
-  else if (a.p.me == 1 && a.p.nt == 4) gemm_launch<1, 4>(a, stream);
-  else gemm_launch<2, 4>(a, stream);
+  if (a.p.me == 1 && a.p.nt == 1) gemm_launch<1, 1, false>(a, stream);
+  else if (a.p.me == 1 && a.p.nt == 4) gemm_launch<1, 4, false>(a, stream);
+  else if (a.p.wx) gemm_launch<2, 4, true>(a, stream);
+  else gemm_launch<2, 4, false>(a, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.E <= 256) hipLaunchKernelGGL(router_topk_kernel<1>, dim3(a.T), dim3(256), 0, stream, a);
