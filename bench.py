@@ -64,7 +64,8 @@ def parse():
                         "attention kernels compute Q.K^T and P.V with VALU dot products")
     p.add_argument("--pmc-run", action="store_true",
                    help="short run for rocprofv3 counter passes: 1 GiB calibration read and write "
-                        "kernels, then a few steps of each schedule over rotating copies")
+                        "kernels, a few steps of each schedule over rotating copies, then the router "
+                        "GEMM at its three shapes")
     return p.parse_args()
 
 
@@ -91,7 +92,16 @@ def pmc_main(args):
             for d in copies:
                 d.step(sched)
         torch.cuda.synchronize()
-    print(json.dumps({"pmc_run": True, "workload": args.workload, "copies": len(copies)}), flush=True)
+    del copies
+    # the router GEMM at its three shapes (kernels named by their tile shape)
+    from load_balanced_split_amd.runner import RouterStep
+    for T, E, H in ROUTER_SHAPES:
+        r = RouterStep(inputs.router_workload(T, E, H, seed=T), top_k=ROUTER_TOP_K)
+        for passes in (2, 2, 1):
+            r.run(passes)
+        torch.cuda.synchronize()
+        del r
+    print(json.dumps({"pmc_run": True, "workload": args.workload}), flush=True)
 
 
 def balance_report(rec, items_per_worker=None):
