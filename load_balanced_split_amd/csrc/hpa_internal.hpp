@@ -301,11 +301,15 @@ constexpr int kRouterMaxTopK = 32;
 constexpr int kRouterMaxHidden = 1 << 16;
 constexpr int kRouterMaxTokens = 1 << 20;
 constexpr int kRouterTargetWaves = 4096;   // 4 per SIMD of 256 compute units
+constexpr int kRouterTiledMinTokens = 256; // above this, LDS-staged 128 x 128 tiles
+constexpr int kRouterTiledTargetWgs = 512; // two such workgroups per compute unit
 struct RouterPlan {
   int me, nt;            // 16-expert blocks and 16-token blocks per wave
   int wx;                // 1: a workgroup's 4 waves take 4 expert groups of one K range (they
                          // share the token fragments through L1); 0: 4 K ranges of one tile
                          // (added in LDS)
+  int tiled;             // 1: 128-expert x 128-token workgroup tiles staged through LDS
+                         // (many tokens; n_eg, n_tg then count such tiles)
   int kw;                // 32-dim k-chunks per K range
   int n_eg, n_tg;        // expert groups (me blocks) and token groups (nt blocks)
   int partial_slots;     // partial sums per logit
@@ -318,6 +322,19 @@ struct RouterPlan {
     p.n_eg = neb / p.me;
     p.n_tg = (tokens + 16 * p.nt - 1) / (16 * p.nt);
     p.wx = tokens > 64 && p.n_eg % 4 == 0 ? 1 : 0;
+    if (tokens > kRouterTiledMinTokens && experts % 128 == 0) {
+      p.tiled = 1;
+      p.wx = 0;
+      p.n_eg = experts / 128;
+      p.n_tg = (tokens + 127) / 128;
+      const int64_t t = int64_t(p.n_eg) * p.n_tg;
+      int64_t ranges = (kRouterTiledTargetWgs + t - 1) / t;
+      ranges = std::min<int64_t>(std::max<int64_t>(ranges, 1), std::max(1, nkc / 8));
+      p.kw = static_cast<int>((nkc + ranges - 1) / ranges);
+      p.partial_slots = static_cast<int>(ranges);
+      p.workgroups = t * ranges;
+      return p;
+    }
     const int64_t tiles = int64_t(p.n_eg) * p.n_tg;
     if (p.wx) {
       // workgroups of 4 expert groups; enough K ranges for ~2 workgroups per compute unit

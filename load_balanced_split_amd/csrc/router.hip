@@ -211,6 +211,135 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(RouterArgs a) {
 }
 
 
+// Many tokens: 128 experts x 128 tokens per workgroup over one K range. Each K-step
+// (32 dims) of both weight halves (8 tiles x 2 KB, copied as they lie in the packed
+// layout) and of x (128 tokens x 64 bytes, rearranged into 8 B-operand tiles of 1 KB)
+// is staged in LDS, in two alternating stages; the global loads of a K-step go out
+// two K-steps ahead into registers. Waves 2 x 2: wave (we, wt) multiplies expert
+// blocks 4 we .. 4 we + 3 with token blocks 4 wt .. 4 wt + 3 (16 accumulators), so
+// every fragment read from LDS feeds 4 (or 8) MFMAs. One barrier per K-step: the
+// stage a K-step reads was written before the previous barrier, the stage it writes
+// was last read before it.
+template <int PASSES>
+__global__ __launch_bounds__(256) void router_gemm_tiled_kernel(RouterArgs a) {
+  constexpr int kWPieces = PASSES == 2 ? 4 : 2;     // 16-byte weight pieces per thread per K-step
+  constexpr int kXPieces = 2;
+  constexpr int kXBase = 16384;                     // x tiles after the 8 weight pairs
+  constexpr int kStage = 16384 + 8192;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
+  const int we = wave & 1, wt = wave >> 1;
+  const RouterPlan& p = a.p;
+  const int nkc = a.H / 32;
+  const int wg = blockIdx.x;
+  const int ks = wg % p.partial_slots, rest = wg / p.partial_slots;
+  const int eg = rest % p.n_eg, tg = rest / p.n_eg;
+  const int c0 = min(ks * p.kw, nkc), c1 = min(c0 + p.kw, nkc);
+  const int eb0 = eg * 8, tok0 = tg * 128;
+  const int rows = min(a.T - tok0, 128);
+  const rsrc_t rw = make_rsrc(a.packed, static_cast<uint32_t>(int64_t(a.E) * a.H * 4));
+  const rsrc_t rx = make_rsrc(a.x + int64_t(tok0) * a.H, static_cast<uint32_t>(rows * a.H * 2));
+  // piece i of the weight: both halves (PASSES 2: 128 pieces per 2 KB pair) or the hi
+  // half only (64 pieces per pair); piece i of x: token c / 4, dims 8 (c % 4) .. + 8
+  uint32_t wsrc[kWPieces], wdst[kWPieces], xsrc[kXPieces], xdst[kXPieces];
+#pragma unroll
+  for (int i = 0; i < kWPieces; ++i) {
+    const int pc = i * 256 + tid;
+    const int per = PASSES == 2 ? 128 : 64;
+    const int eb = pc / per, r = (pc % per) * 16;
+    wsrc[i] = static_cast<uint32_t>(int64_t(eb0 + eb) * nkc * 2048 + r);
+    wdst[i] = static_cast<uint32_t>(eb * per * 16 + r);       // LDS: the staged halves packed
+  }
+#pragma unroll
+  for (int i = 0; i < kXPieces; ++i) {
+    const int c = i * 256 + tid;
+    const int t = c / 4, jj = c % 4;
+    xsrc[i] = static_cast<uint32_t>((t * a.H + 8 * jj) * 2);
+    xdst[i] = static_cast<uint32_t>(kXBase + (t / 16) * 1024 + (16 * jj + t % 16) * 16);
+  }
+  struct Stg {
+    u32x4 w[kWPieces], x[kXPieces];
+  };
+  auto gload = [&](Stg& g, int kc) {
+    const uint32_t sw = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(kc * 2048));
+    const uint32_t sx = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(kc * 64));
+#pragma unroll
+    for (int i = 0; i < kWPieces; ++i) g.w[i] = bload16(rw, wsrc[i], sw);
+#pragma unroll
+    for (int i = 0; i < kXPieces; ++i) g.x[i] = bload16(rx, xsrc[i], sx);
+  };
+  auto swrite = [&](const Stg& g, int stage) {
+    uint8_t* st = lds + stage * kStage;
+#pragma unroll
+    for (int i = 0; i < kWPieces; ++i) *reinterpret_cast<u32x4*>(st + wdst[i]) = g.w[i];
+#pragma unroll
+    for (int i = 0; i < kXPieces; ++i) *reinterpret_cast<u32x4*>(st + xdst[i]) = g.x[i];
+  };
+  // all of this wave's LDS accesses complete, then the workgroup barrier (global loads
+  // in flight are not waited for)
+  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int ie = 0; ie < 4; ++ie)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) acc[ie][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int stage) {
+    const uint8_t* st = lds + stage * kStage;
+    u32x4 ah[4], al[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pair = (4 * we + i) * (PASSES == 2 ? 2048 : 1024);
+      ah[i] = *reinterpret_cast<const u32x4*>(st + pair + 16 * lane);
+      if (PASSES == 2) al[i] = *reinterpret_cast<const u32x4*>(st + pair + 1024 + 16 * lane);
+      b[i] = *reinterpret_cast<const u32x4*>(st + kXBase + (4 * wt + i) * 1024 + 16 * lane);
+    }
+#pragma unroll
+    for (int ie = 0; ie < 4; ++ie)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        acc[ie][it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah[ie]), as_bf16x8(b[it]), acc[ie][it], 0, 0, 0);
+        if (PASSES == 2)
+          acc[ie][it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al[ie]), as_bf16x8(b[it]), acc[ie][it], 0, 0, 0);
+      }
+  };
+  if (c0 < c1) {
+    Stg ga, gb;
+    gload(ga, c0);
+    gload(gb, min(c0 + 1, c1 - 1));
+    swrite(ga, 0);
+    barrier();
+    int kc = c0;
+    for (; kc + 2 <= c1; kc += 2) {
+      // stage 0 holds K-step kc, gb holds kc + 1 (the scheduling barriers keep each
+      // K-step's global loads ahead of the products before it is written to LDS)
+      gload(ga, min(kc + 2, c1 - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0);
+      __builtin_amdgcn_sched_barrier(0);
+      swrite(gb, 1);
+      barrier();
+      // stage 1 holds kc + 1, ga holds kc + 2
+      gload(gb, min(kc + 3, c1 - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(1);
+      __builtin_amdgcn_sched_barrier(0);
+      swrite(ga, 0);
+      barrier();
+    }
+    if (kc < c1) compute(0);
+  }
+#pragma unroll
+  for (int ie = 0; ie < 4; ++ie)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int tok = 16 * (4 * wt + it) + (lane & 15);
+      if (tok < rows)
+        *reinterpret_cast<f32x4*>(a.part + (int64_t(ks) * a.T + tok0 + tok) * a.E + 16 * (eb0 + 4 * we + ie) +
+                                  4 * (lane >> 4)) = acc[ie][it];
+    }
+}
+
 // A logit and its expert as one 64-bit key whose unsigned order is the top-k
 // order: the float's bits mapped to an order-preserving uint32 (-0 taken as +0)
 // above the complement of the expert index (equal values: lower index first).
@@ -330,7 +459,12 @@ hipError_t launch_router_pack(const float* w, int experts, int hidden, uint8_t* 
 }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
-  if (a.p.me == 1 && a.p.nt == 1) gemm_launch<1, 1, false>(a, stream);
+  if (a.p.tiled) {
+    if (a.passes == 2)
+      hipLaunchKernelGGL(router_gemm_tiled_kernel<2>, dim3(a.p.workgroups), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(router_gemm_tiled_kernel<1>, dim3(a.p.workgroups), dim3(256), 0, stream, a);
+  } else if (a.p.me == 1 && a.p.nt == 1) gemm_launch<1, 1, false>(a, stream);
   else if (a.p.me == 1 && a.p.nt == 4) gemm_launch<1, 4, false>(a, stream);
   else if (a.p.wx) gemm_launch<2, 4, true>(a, stream);
   else gemm_launch<2, 4, false>(a, stream);

@@ -154,8 +154,8 @@ def test_router_validation_and_workspace_size(L):
     # one token, 16 expert blocks: 112 K ranges of 2 chunks, 4 per workgroup -> 28 partial sums per logit
     assert n.value == 28 * 1 * 256 * 4
     assert ws(0, 256, 7168, ctypes.byref(n)) == 0 and n.value == 0
-    # many tokens: workgroups of 4 expert groups x 64 tokens, 4 K ranges -> 4 partial sums
-    assert ws(4096, 256, 7168, ctypes.byref(n)) == 0 and n.value == 4 * 4096 * 256 * 4
+    # many tokens: 128 x 128 tiles (2 x 32 of them), 8 K ranges for 512 workgroups -> 8 partial sums
+    assert ws(4096, 256, 7168, ctypes.byref(n)) == 0 and n.value == 8 * 4096 * 256 * 4
     for T, E, H, status in ((1, 8, 64, 2), (1, 1040, 64, 2), (1, 24, 64, 2), (1, 16, 48, 2), (1, 16, 0, 2),
                             (1, 16, 1 << 17, 2), (-1, 16, 64, 1), ((1 << 20) + 1, 16, 64, 1)):
         assert ws(T, E, H, ctypes.byref(n)) == status, (T, E, H)
