@@ -31,7 +31,7 @@
 // (larger value first, equal values to the lower expert index) by ranks of 64-bit
 // (value, expert) keys in LDS, within 64-expert segments and then among the
 // segments' k largest.
-#include "hpa_internal.hpp"
+#include "router_internal.hpp"
 
 namespace hpa {
 namespace {

@@ -34,7 +34,7 @@ CALIBRATION_BYTES = 1 << 30          # bench.py --pmc-run copies this many bytes
 
 # sources of kernels that no attention-path launch runs (the router GEMM, the read
 # probe): a change there leaves the attention path's counter readings valid
-_NOT_ATTENTION = {"router.hip", "probe.hip"}
+_NOT_ATTENTION = {"router.hip", "router_internal.hpp", "router_host.cpp", "probe.hip"}
 
 
 def source_hash() -> str:
