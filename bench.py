@@ -255,8 +255,9 @@ def main():
     if args.pmc_run:
         return pmc_main(args)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU, "
-              "see the sharding note in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path is measured on one "
+              "GPU's share of the work; across GPUs each would plan and attend only its own requests' tiles",
+              file=sys.stderr)
         sys.exit(2)
     os.environ["HPA_PRODUCTS"] = args.products
     import torch
