@@ -15,16 +15,17 @@
 //   hi at byte 2048 * tile + 16 * lane + 2 * (k % 8), lo 1024 bytes further.
 // A wave's 16-byte load of one tile half is one contiguous 1 KB.
 //
-// GEMM (router_gemm_kernel<ME, NT, PASSES>): each wave computes C^T[16 ME experts x
-// 16 NT tokens] over one K range with v_mfma_f32_16x16x32_bf16 (A = weight tile,
-// B = x^T: lane (token n16, group j) holds x[token][32 kc + 8 j .. + 8]), the next
-// k-chunk's loads always issued before the current chunk is multiplied. For few
-// tokens the 4 waves of a workgroup take 4 consecutive K ranges of the same tile and
-// add their results in LDS in wave order (one partial sum per logit per workgroup);
-// for many tokens (WX) they take 4 expert groups of the same tokens and K range, so
-// the token fragments they all load are shared through L1, and each wave stores its
-// own partial sums. Rows past the last token read zeros (buffer bounds) and are not
-// stored.
+// GEMM, few and medium token counts (router_gemm_kernel<ME, NT, PASSES, WX>): each
+// wave computes C^T[16 ME experts x 16 NT tokens] over one K range with
+// v_mfma_f32_16x16x32_bf16 (A = weight tile, B = x^T: lane (token n16, group j) holds
+// x[token][32 kc + 8 j .. + 8]) straight from registers, the loads of k-chunk kc + 2
+// in flight while chunk kc is multiplied. Few tokens: the 4 waves of a workgroup take
+// 4 consecutive K ranges of the same tile and add their results in LDS in wave order
+// (one partial sum per logit per workgroup); medium (WX): they take 4 expert groups
+// of the same tokens and K range, so the token fragments they all load are shared
+// through L1, and each wave stores its own partial sums. Many tokens
+// (router_gemm_tiled_kernel): 128 x 128 workgroup tiles staged through LDS (below).
+// Rows past the last token read zeros (buffer bounds) and are not stored.
 //
 // Reduction and top-k (router_topk_kernel, one workgroup per token): the partial
 // sums of a logit are added in partial order and the logits stored; the top-k
