@@ -878,6 +878,7 @@ struct Worker {
     start_stamp(3);
     Item nit;
     bool more = src.next(nit, tq);
+    src.fix(st.it);              // a source may settle the first item's partial slot only now
     for (;;) {
       ItemState nst{};
       int npid = -1, npidB = -1;
@@ -937,6 +938,7 @@ struct PlanSource {
     if (i == i1 && q.open()) q.want = true;   // the last item held: claim the next chunk
     return true;
   }
+  __device__ void fix(Item&) const {}
 };
 
 template <bool FP8>
@@ -983,6 +985,7 @@ struct SingleSource {
     it = item;
     return true;
   }
+  __device__ void fix(Item&) const {}
 };
 
 template <bool FP8>
@@ -1040,13 +1043,55 @@ __device__ inline int add_chunk_offsets(FusedPlanLds& P, int* arr, int S, int nc
 template <bool INMERGE>
 struct FusedSource {
   const AttnArgs& a;
-  const FusedPlanLds& P;
+  FusedPlanLds& P;
   Partition part;
   int S;
   int v;                      // the virtual worker whose positions [pos, e) are being walked
   int pos, e, s;
+  // Register plan: the partial-slot bases P.PB are not in LDS yet when the first item is
+  // handed out. They are computed (wave 0) and published, with one barrier, on the
+  // second call, i.e. behind the first unit's loads; fix() then settles the first
+  // item's slot (kSlotLater until then) and its record for the merge kernel.
+  bool pb_ready = true;
+  bool first_later = false;   // the first item's slot and record wait for fix()
+  int calls = 0;
+  int first_split = 0;
+  __device__ void publish_pb(int lane, int wave) {
+    if (wave == 0) {
+      int carry = 0;
+      for (int base = 0; base < S; base += 64) {
+        const int sq = base + lane;
+        int val = 0;
+        if (sq < S) {
+          const int c0 = P.C[sq], c1 = P.C[sq + 1];
+          if (c1 > c0) {
+            const int ns = part.owner(c1 - 1) - part.owner(c0 + a.item_cost) + 1;
+            val = ns > 1 ? ns : 0;
+          }
+        }
+        const int incl = wave_incl_scan(val);
+        if (sq < S) P.PB[sq] = carry + incl - val;
+        carry += __builtin_amdgcn_readlane(incl, 63);
+      }
+    }
+    __syncthreads();
+    pb_ready = true;
+  }
+  __device__ void fix(Item& it) {
+    if (!first_later) return;
+    first_later = false;
+    const int pb = __builtin_amdgcn_readfirstlane(P.PB[it.s]);
+    if (it.nsplit > 1) it.slot = pb + first_split;
+    it.pbase = pb;
+    if (!INMERGE && first_split == 0 && threadIdx.x == 0) {   // record for the merge kernel
+      a.plan[a.po.num_splits + it.s] = it.nsplit;
+      a.plan[a.po.partial_base + it.s] = pb;
+    }
+  }
   // positions [C[s], C[s+1]) of a non-empty sequence: item_cost virtual ones, then its tiles
   __device__ bool next(Item& it, TailQueue& q) {
+    if (!pb_ready && calls > 0) publish_pb(threadIdx.x & 63, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    ++calls;
     for (;;) {
       while (pos < e) {
         const int c0 = __builtin_amdgcn_readfirstlane(P.C[s]);
@@ -1059,6 +1104,16 @@ struct FusedSource {
             const int first = __builtin_amdgcn_readfirstlane(part.owner(r0));
             const int split = v - first;
             const int ns = __builtin_amdgcn_readfirstlane(part.owner(c1 - 1)) - first + 1;
+            if (!pb_ready) {          // only the first item: its slot is settled by fix()
+              first_split = split;
+              first_later = true;
+              // a split item's slot is only known once the bases are: an in-range
+              // placeholder until fix() (nothing reads it before)
+              it = Item{s, lo - r0, t1 - r0, ns > 1 ? 0 : -1, __builtin_amdgcn_readfirstlane(P.L[s]), ns, -1};
+              if (pos + a.item_cost >= e && q.open()) q.want = true;
+              ++s;
+              return true;
+            }
             const int pb = __builtin_amdgcn_readfirstlane(P.PB[s]);
             it = Item{s, lo - r0, t1 - r0, ns > 1 ? pb + split : -1, __builtin_amdgcn_readfirstlane(P.L[s]), ns, pb};
             // the last item held: claim the next chunk (the next sequence's tiles start
@@ -1091,11 +1146,12 @@ struct FusedSource {
 // evaluates the per-sequence prefix sums by itself (lane l of chunk k holds
 // sequence 64k + l; DPP scans, no LDS, no barrier); wave 0 then publishes them
 // to LDS. Same integer arithmetic as plan_kernel; C holds positions (tiles plus
-// item_cost virtual tiles per non-empty sequence), N their total.
+// item_cost virtual tiles per non-empty sequence), N their total. The partial-slot
+// bases are left to FusedSource, off the path to the first K/V loads.
 constexpr int kRegPlanChunks = kRegPlanSeqs / 64;
 
 struct RegPlan {
-  int L[kRegPlanChunks], C[kRegPlanChunks], n[kRegPlanChunks], PB[kRegPlanChunks];
+  int L[kRegPlanChunks], C[kRegPlanChunks], n[kRegPlanChunks];
   int N;
   Partition part;
   bool bad;
@@ -1115,7 +1171,7 @@ struct RegPlan {
     }
 #pragma unroll
     for (int k = 0; k < kRegPlanChunks; ++k) {
-      L[k] = n[k] = C[k] = PB[k] = 0;
+      L[k] = n[k] = C[k] = 0;
       if (64 * k >= S) continue;
       const int s = 64 * k + lane;
       int Lk = 0;
@@ -1136,20 +1192,6 @@ struct RegPlan {
     N = carry;
     part = Partition::make(N, N, W, a.min_tiles, a.tail_den, a.tail_chunk);
     bad = __builtin_amdgcn_ballot_w64(bad_lane) != 0;
-    carry = 0;
-#pragma unroll
-    for (int k = 0; k < kRegPlanChunks; ++k) {
-      if (64 * k >= S) continue;
-      int v = 0;
-      if (n[k] > 0) {
-        const int r0 = C[k] + a.item_cost;
-        const int ns = part.owner(r0 + n[k] - 1) - part.owner(r0) + 1;
-        v = ns > 1 ? ns : 0;
-      }
-      const int incl = wave_incl_scan(v);
-      PB[k] = carry + incl - v;
-      carry += __builtin_amdgcn_readlane(incl, 63);
-    }
   }
 };
 
@@ -1187,7 +1229,6 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
         const int s = 64 * k + lane;
         if (s < S) {
           P.C[s] = R.C[k];
-          P.PB[s] = R.PB[k];
           P.L[s] = R.L[k];
         }
       }
@@ -1255,6 +1296,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
   if (w >= part.Wp) return;
   // workers without a static range go straight to the tail chunks
   FusedSource<INMERGE> src{a, P, part, S, w, pos, pend, __builtin_amdgcn_readfirstlane(s0)};
+  src.pb_ready = S > kRegPlanSeqs;     // the register plan leaves the partial-slot bases for later
   Worker<FP8, INMERGE> r(a, lds);
   r.trec = tr.rec;
   r.tq = TailQueue{a.qctr, lds.claim, part.D};
