@@ -413,14 +413,20 @@ __global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a) {
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     if (id[q] < 0) continue;
-    const int seg = id[q] / 64;
+    const int seg = id[q] / 64;                      // the same for the whole wave
     const int n = min(64, a.E - 64 * seg);          // a multiple of 16
-    uint64_t w[64];
-#pragma unroll
-    for (int j = 0; j < 64; ++j) w[j] = lk[64 * seg + min(j, n - 1)];
     int rank = 0;
+    if (n == 64) {                                   // a full segment: fixed offsets, no masks
+      const uint64_t* sp = lk + 64 * seg;
 #pragma unroll
-    for (int j = 0; j < 64; ++j) rank += int((j < n) & (w[j] > key[q]));
+      for (int j = 0; j < 64; ++j) rank += int(sp[j] > key[q]);
+    } else {
+      uint64_t w[64];
+#pragma unroll
+      for (int j = 0; j < 64; ++j) w[j] = lk[64 * seg + min(j, n - 1)];
+#pragma unroll
+      for (int j = 0; j < 64; ++j) rank += int((j < n) & (w[j] > key[q]));
+    }
     if (rank < k) sk[seg * k + rank] = key[q];
   }
   __syncthreads();
