@@ -1373,25 +1373,33 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int ngrp = (n + kMergeGroup - 1) / kMergeGroup;
   float FM = -INFINITY, FL = 0.f;
   f32x4 FA = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int g0 = 0; g0 < ngrp; g0 += kMergeLanes) {
+  // A group's loads all go out before its first fold.
+  struct GroupLoads {
+    float m[kMergeGroup], l[kMergeGroup];
+    f32x4 acc[kMergeGroup];
+  };
+  auto load_group = [&](GroupLoads& gs, int gg) {
+    gg = min(gg, ngrp - 1);          // straight-line loads; a clamped group goes unused
+    const int k0 = gg * kMergeGroup, k1 = min(n, k0 + kMergeGroup);
+#pragma unroll
+    for (int i = 0; i < kMergeGroup; ++i) {
+      const int64_t r = (int64_t(base) + min(k0 + i, k1 - 1)) * G + hh;   // in bounds; extra ones unused
+      gs.m[i] = a.part_m[r];
+      gs.l[i] = a.part_l[r];
+      gs.acc[i] = *reinterpret_cast<const f32x4*>(a.part_acc + r * kHeadDim + d0 + 4 * q4);
+    }
+  };
+  // one pass: every lane group folds its group g0 + lj, then lane group 0 folds the
+  // pass's group results in group order
+  auto fold_pass = [&](const GroupLoads& gs, int g0) {
     const int gg = g0 + lj;
     float M = -INFINITY, L = 0.f;
     f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
     if (gg < ngrp) {
-      // all of the group's loads go out before the first fold: one round trip per group
       const int k0 = gg * kMergeGroup, k1 = min(n, k0 + kMergeGroup);
-      float mk[kMergeGroup], lk[kMergeGroup];
-      f32x4 ak[kMergeGroup];
-#pragma unroll
-      for (int i = 0; i < kMergeGroup; ++i) {
-        const int64_t r = (int64_t(base) + min(k0 + i, k1 - 1)) * G + hh;   // in bounds; extra ones unused
-        mk[i] = a.part_m[r];
-        lk[i] = a.part_l[r];
-        ak[i] = *reinterpret_cast<const f32x4*>(a.part_acc + r * kHeadDim + d0 + 4 * q4);
-      }
 #pragma unroll
       for (int i = 0; i < kMergeGroup; ++i)
-        if (k0 + i < k1) fold(M, L, A, mk[i], lk[i], ak[i]);
+        if (k0 + i < k1) fold(M, L, A, gs.m[i], gs.l[i], gs.acc[i]);
     }
     if (q4 == 0) {
       gm[lj] = M;
@@ -1404,6 +1412,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       for (int j = 0; j < cnt; ++j) fold(FM, FL, FA, gm[j], gl[j], gacc[j][q4]);
     }
     __syncthreads();
+  };
+  // the first two passes' loads go out together (up to 256 splits: one round trip)
+  GroupLoads ga, gb;
+  const bool two = ngrp > kMergeLanes;          // uniform
+  load_group(ga, lj);
+  if (two) load_group(gb, kMergeLanes + lj);
+  fold_pass(ga, 0);
+  if (two) fold_pass(gb, kMergeLanes);
+  for (int g0 = 2 * kMergeLanes; g0 < ngrp; g0 += kMergeLanes) {
+    load_group(ga, g0 + lj);
+    fold_pass(ga, g0);
   }
   if (lj == 0) {
 #pragma unroll
