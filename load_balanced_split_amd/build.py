@@ -18,7 +18,10 @@ SOURCES = ["plan.hip", "attn.hip", "prologue.hip", "probe.hip", "router.hip", "h
 # every work claim; without it the wait lands where the value is used.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None", "-I", INCLUDE, "-I", CSRC]
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+         # leading scalar kernel arguments arrive in SGPRs at dispatch
+         "-mllvm", "-amdgpu-kernarg-preload-count=16",
+         "-I", INCLUDE, "-I", CSRC]
 
 
 def hipcc():

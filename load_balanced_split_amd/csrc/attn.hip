@@ -1158,7 +1158,7 @@ struct RegPlan {
 
   // chunks at or past S (a uniform test) are skipped whole: their lanes would hold
   // no sequence, and nothing reads them
-  __device__ void build(const AttnArgs& a, int S, int W, int lane) {
+  __device__ void build(const AttnArgs& a, const int32_t* seq_lens, int hkv, int S, int W, int lane) {
     int carry = 0;
     bool bad_lane = false;
     // every chunk's lengths are requested before the first is used (one round trip);
@@ -1167,7 +1167,7 @@ struct RegPlan {
 #pragma unroll
     for (int k = 0; k < kRegPlanChunks; ++k) {
       const int s = min(64 * k + lane, S - 1);
-      Lraw[k] = a.seq_lens[a.hkv == 1 ? s : s / a.hkv];
+      Lraw[k] = seq_lens[hkv == 1 ? s : s / hkv];
     }
 #pragma unroll
     for (int k = 0; k < kRegPlanChunks; ++k) {
@@ -1195,20 +1195,24 @@ struct RegPlan {
   }
 };
 
+// seq_lens, batch and hkv also lead the argument list as scalars, which are preloaded
+// into SGPRs at dispatch (struct arguments are not): the lengths, the first loads of
+// the launch, do not wait for the argument block.
 template <bool FP8, bool INMERGE>
-__global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_kernel(const int32_t* seq_lens, int batch,
+                                                                                  int hkv, AttnArgs a) {
   __shared__ CombineLds lds;
   __shared__ FusedPlanLds P;
   WaveTrace tr(a);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int S = a.batch * a.hkv, nch = (S + 63) / 64;
+  const int S = batch * hkv, nch = (S + 63) / 64;
   const int W = gridDim.x, w = blockIdx.x;
   int N, bad, pos = 0, pend = 0, s0 = 0;
   Partition part;
   if (S <= kRegPlanSeqs) {
     RegPlan R;
-    R.build(a, S, W, lane);
+    R.build(a, seq_lens, hkv, S, W, lane);
     N = R.N;
     part = R.part;
     bad = R.bad;
@@ -1242,7 +1246,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
       const int s = ch * 64 + lane;
       int n = 0;
       if (s < S) {
-        int L = a.seq_lens[s / a.hkv];
+        int L = seq_lens[s / hkv];
         if (L < 0 || L > a.max_pages * kPage) {
           bad = 1;
           L = 0;
@@ -1330,20 +1334,26 @@ struct MergeArgs {
   int slots, static_splits, static_chunk;
 };
 
+// The arrays and offsets the first loads need also lead the argument list as scalars:
+// leading scalar arguments are preloaded into SGPRs at dispatch (struct arguments are
+// not), so the metadata loads do not wait for the argument block.
 template <MergeMode MODE>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int32_t* seq_lens, const int32_t* plan,
+                                                              const float* part_acc, const float* part_m,
+                                                              const float* part_l, int hkv, int off_splits,
+                                                              int off_base, MergeArgs a) {
   __shared__ float gm[kMergeLanes], gl[kMergeLanes];
   __shared__ f32x4 gacc[kMergeLanes][kMergeQuads];
   const int hh = blockIdx.y, d0 = blockIdx.z * kMergeDims;
   const int s = blockIdx.x;
   // every fact this block needs is one scalar load away from its sequence index,
   // and all of those loads go out together
-  const int L = sload(a.seq_lens, s / a.hkv);
+  const int L = sload(seq_lens, s / hkv);
   int n = 0, base = 0, planned_w = a.workers;
   if constexpr (MODE != MERGE_STATIC) {
-    n = sload(a.plan, a.num_splits + s);
-    base = sload(a.plan, a.partial_base + s);
-    if constexpr (MODE == MERGE_PLAN) planned_w = sload(a.plan, a.header + H_W);
+    n = sload(plan, off_splits + s);
+    base = sload(plan, off_base + s);
+    if constexpr (MODE == MERGE_PLAN) planned_w = sload(plan, a.header + H_W);
   }
   if constexpr (MODE == MERGE_STATIC) {
     if (L < 0 || L > a.max_pages * kPage) return;
@@ -1384,9 +1394,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int i = 0; i < kMergeGroup; ++i) {
       const int64_t r = (int64_t(base) + min(k0 + i, k1 - 1)) * G + hh;   // in bounds; extra ones unused
-      gs.m[i] = a.part_m[r];
-      gs.l[i] = a.part_l[r];
-      gs.acc[i] = *reinterpret_cast<const f32x4*>(a.part_acc + r * kHeadDim + d0 + 4 * q4);
+      gs.m[i] = part_m[r];
+      gs.l[i] = part_l[r];
+      gs.acc[i] = *reinterpret_cast<const f32x4*>(part_acc + r * kHeadDim + d0 + 4 * q4);
     }
   };
   // one pass: every lane group folds its group g0 + lj, then lane group 0 folds the
@@ -1472,13 +1482,13 @@ hipError_t launch_attn_static(const AttnArgs& a, bool fp8, hipStream_t stream) {
 
 hipError_t launch_attn_fused(const AttnArgs& a, bool fp8, bool merge_in_kernel, int num_workers, hipStream_t stream) {
   if (fp8 && merge_in_kernel)
-    hipLaunchKernelGGL((attn_fused_kernel<true, true>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fused_kernel<true, true>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a.seq_lens, a.batch, a.hkv, a);
   else if (fp8)
-    hipLaunchKernelGGL((attn_fused_kernel<true, false>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fused_kernel<true, false>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a.seq_lens, a.batch, a.hkv, a);
   else if (merge_in_kernel)
-    hipLaunchKernelGGL((attn_fused_kernel<false, true>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fused_kernel<false, true>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a.seq_lens, a.batch, a.hkv, a);
   else
-    hipLaunchKernelGGL((attn_fused_kernel<false, false>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fused_kernel<false, false>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a.seq_lens, a.batch, a.hkv, a);
   return hipGetLastError();
 }
 
@@ -1491,11 +1501,14 @@ hipError_t launch_merge(const AttnArgs& a, MergeMode mode, hipStream_t stream) {
                     static_cast<int>(a.slots), a.static_splits, a.static_chunk};
   const dim3 grid(S, a.group, kHeadDim / kMergeDims);
   if (mode == MERGE_PLAN)
-    hipLaunchKernelGGL(merge_kernel<MERGE_PLAN>, grid, dim3(kMergeThreads), 0, stream, m);
+    hipLaunchKernelGGL(merge_kernel<MERGE_PLAN>, grid, dim3(kMergeThreads), 0, stream, m.seq_lens, m.plan, m.part_acc,
+                       m.part_m, m.part_l, m.hkv, m.num_splits, m.partial_base, m);
   else if (mode == MERGE_FUSED)
-    hipLaunchKernelGGL(merge_kernel<MERGE_FUSED>, grid, dim3(kMergeThreads), 0, stream, m);
+    hipLaunchKernelGGL(merge_kernel<MERGE_FUSED>, grid, dim3(kMergeThreads), 0, stream, m.seq_lens, m.plan, m.part_acc,
+                       m.part_m, m.part_l, m.hkv, m.num_splits, m.partial_base, m);
   else
-    hipLaunchKernelGGL(merge_kernel<MERGE_STATIC>, grid, dim3(kMergeThreads), 0, stream, m);
+    hipLaunchKernelGGL(merge_kernel<MERGE_STATIC>, grid, dim3(kMergeThreads), 0, stream, m.seq_lens, m.plan, m.part_acc,
+                       m.part_m, m.part_l, m.hkv, m.num_splits, m.partial_base, m);
   return hipGetLastError();
 }
 
