@@ -1337,7 +1337,9 @@ struct MergeArgs {
 // The arrays and offsets the first loads need also lead the argument list as scalars:
 // leading scalar arguments are preloaded into SGPRs at dispatch (struct arguments are
 // not), so the metadata loads do not wait for the argument block.
-template <MergeMode MODE>
+// TWO: the first two passes' loads go out together (a second register set: fewer
+// blocks per CU, so it is launched only when the grid has at most one block per CU).
+template <MergeMode MODE, bool TWO>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int32_t* seq_lens, const int32_t* plan,
                                                               const float* part_acc, const float* part_m,
                                                               const float* part_l, int hkv, int off_splits,
@@ -1389,7 +1391,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int32_t* seq
     f32x4 acc[kMergeGroup];
   };
   auto load_group = [&](GroupLoads& gs, int gg) {
-    gg = min(gg, ngrp - 1);          // straight-line loads; a clamped group goes unused
+    if (gg >= ngrp) return;          // lane groups past the last group load nothing
     const int k0 = gg * kMergeGroup, k1 = min(n, k0 + kMergeGroup);
 #pragma unroll
     for (int i = 0; i < kMergeGroup; ++i) {
@@ -1423,14 +1425,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int32_t* seq
     }
     __syncthreads();
   };
-  // the first two passes' loads go out together (up to 256 splits: one round trip)
+  // TWO: the first two passes' loads go out together (up to 256 splits: one round trip)
   GroupLoads ga, gb;
-  const bool two = ngrp > kMergeLanes;          // uniform
+  const bool two = TWO && ngrp > kMergeLanes;   // uniform
   load_group(ga, lj);
   if (two) load_group(gb, kMergeLanes + lj);
   fold_pass(ga, 0);
   if (two) fold_pass(gb, kMergeLanes);
-  for (int g0 = 2 * kMergeLanes; g0 < ngrp; g0 += kMergeLanes) {
+  for (int g0 = (two ? 2 : 1) * kMergeLanes; g0 < ngrp; g0 += kMergeLanes) {
     load_group(ga, g0 + lj);
     fold_pass(ga, g0);
   }
@@ -1500,15 +1502,16 @@ hipError_t launch_merge(const AttnArgs& a, MergeMode mode, hipStream_t stream) {
                     a.hkv, a.hq, a.group, a.max_pages, a.workers,
                     static_cast<int>(a.slots), a.static_splits, a.static_chunk};
   const dim3 grid(S, a.group, kHeadDim / kMergeDims);
+  const bool two = int64_t(S) * a.group <= a.workers;   // at most one block per worker (CU)
   if (mode == MERGE_PLAN)
-    hipLaunchKernelGGL(merge_kernel<MERGE_PLAN>, grid, dim3(kMergeThreads), 0, stream, m.seq_lens, m.plan, m.part_acc,
-                       m.part_m, m.part_l, m.hkv, m.num_splits, m.partial_base, m);
+    hipLaunchKernelGGL((two ? merge_kernel<MERGE_PLAN, true> : merge_kernel<MERGE_PLAN, false>), grid, dim3(kMergeThreads), 0,
+                       stream, m.seq_lens, m.plan, m.part_acc, m.part_m, m.part_l, m.hkv, m.num_splits, m.partial_base, m);
   else if (mode == MERGE_FUSED)
-    hipLaunchKernelGGL(merge_kernel<MERGE_FUSED>, grid, dim3(kMergeThreads), 0, stream, m.seq_lens, m.plan, m.part_acc,
-                       m.part_m, m.part_l, m.hkv, m.num_splits, m.partial_base, m);
+    hipLaunchKernelGGL((two ? merge_kernel<MERGE_FUSED, true> : merge_kernel<MERGE_FUSED, false>), grid, dim3(kMergeThreads), 0,
+                       stream, m.seq_lens, m.plan, m.part_acc, m.part_m, m.part_l, m.hkv, m.num_splits, m.partial_base, m);
   else
-    hipLaunchKernelGGL(merge_kernel<MERGE_STATIC>, grid, dim3(kMergeThreads), 0, stream, m.seq_lens, m.plan, m.part_acc,
-                       m.part_m, m.part_l, m.hkv, m.num_splits, m.partial_base, m);
+    hipLaunchKernelGGL((two ? merge_kernel<MERGE_STATIC, true> : merge_kernel<MERGE_STATIC, false>), grid, dim3(kMergeThreads), 0,
+                       stream, m.seq_lens, m.plan, m.part_acc, m.part_m, m.part_l, m.hkv, m.num_splits, m.partial_base, m);
   return hipGetLastError();
 }
 
