@@ -103,31 +103,31 @@ struct Frag {
 };
 
 template <int ME, int NT, int PASSES, bool WX>
-__global__ __launch_bounds__(256) void router_gemm_kernel(RouterArgs a) {
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* x, const uint8_t* packed, int T, int E,
+                                                          int H, int slots, int n_eg, int kw, RouterArgs a) {
   __shared__ f32x4 red[WX ? 1 : 4][WX ? 1 : ME * NT][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int m16 = lane & 15, j = lane >> 4;
-  const RouterPlan& p = a.p;
-  const int nkc = a.H / 32;
+  const int nkc = H / 32;
   const int wg = blockIdx.x;
-  const int ksg = wg % p.partial_slots;
-  const int rest = wg / p.partial_slots;
+  const int ksg = wg % slots;
+  const int rest = wg / slots;
   // WX: the 4 waves take expert groups 4 q .. 4 q + 3 of K range ksg; otherwise K ranges
   // 4 ksg .. 4 ksg + 3 of expert group eg
-  const int n_egw = WX ? p.n_eg / 4 : p.n_eg;
+  const int n_egw = WX ? n_eg / 4 : n_eg;
   const int eg = WX ? 4 * (rest % n_egw) + wave : rest % n_egw, tg = rest / n_egw;
   const int ks = WX ? ksg : 4 * ksg + wave;
-  const int c0 = min(ks * p.kw, nkc), c1 = min(c0 + p.kw, nkc);
+  const int c0 = min(ks * kw, nkc), c1 = min(c0 + kw, nkc);
   const int eb0 = eg * ME, tok0 = tg * 16 * NT;
-  const int rows = min(a.T - tok0, 16 * NT);
-  const rsrc_t rw = make_rsrc(a.packed, static_cast<uint32_t>(int64_t(a.E) * a.H * 4));
-  const rsrc_t rx = make_rsrc(a.x + int64_t(tok0) * a.H, static_cast<uint32_t>(rows * a.H * 2));
+  const int rows = min(T - tok0, 16 * NT);
+  const rsrc_t rw = make_rsrc(packed, static_cast<uint32_t>(int64_t(E) * H * 4));
+  const rsrc_t rx = make_rsrc(x + int64_t(tok0) * H, static_cast<uint32_t>(rows * H * 2));
 
   // lane-constant parts of the offsets in VGPRs, the chunk's part in the scalar offset
   uint32_t xoff[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) xoff[nt] = static_cast<uint32_t>(((16 * nt + m16) * a.H + 8 * j) * 2);
+  for (int nt = 0; nt < NT; ++nt) xoff[nt] = static_cast<uint32_t>(((16 * nt + m16) * H + 8 * j) * 2);
   const uint32_t woff = 16 * lane;
   auto load = [&](Frag<ME, NT>& f, int kc) {
     const uint32_t kx = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(64 * kc));
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(RouterArgs a) {
       for (int nt = 0; nt < NT; ++nt) {
         const int tok = 16 * nt + m16;
         if (tok < rows)
-          *reinterpret_cast<f32x4*>(a.part + (int64_t(ksg) * a.T + tok0 + tok) * a.E + 16 * (eb0 + me) + 4 * j) =
+          *reinterpret_cast<f32x4*>(a.part + (int64_t(ksg) * T + tok0 + tok) * E + 16 * (eb0 + me) + 4 * j) =
               acc[me][nt];
       }
   } else {
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(RouterArgs a) {
 #pragma unroll
       for (int w = 1; w < 4; ++w) s += red[w][r][l];
       const int e = 16 * (eb0 + me) + 4 * (l >> 4);
-      *reinterpret_cast<f32x4*>(a.part + (int64_t(ksg) * a.T + tok0 + tok) * a.E + e) = s;
+      *reinterpret_cast<f32x4*>(a.part + (int64_t(ksg) * T + tok0 + tok) * E + e) = s;
     }
   }
 }
@@ -365,22 +365,22 @@ __device__ inline int key_expert(uint64_t k) { return int(~uint32_t(k)); }
 // which for the global top-k is its global rank and for every other survivor is at
 // least k; those below k are written at their rank.
 template <int Q>
-__global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a) {
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* part, int T, int E, int slots,
+                                                          RouterArgs a) {
   constexpr int kBatch = 32 / Q;
   constexpr int kSegs = kRouterMaxExperts / 64;
   __shared__ uint64_t lk[kRouterMaxExperts];
   __shared__ uint64_t sk[kSegs * kRouterMaxTopK];
   const int t = blockIdx.x;
-  const int slots = a.p.partial_slots;
-  const int64_t stride = int64_t(a.T) * a.E;
-  const float* base = a.part + int64_t(t) * a.E;
+    const int64_t stride = int64_t(T) * E;
+  const float* base = part + int64_t(t) * E;
   float v[Q];
   int id[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int e = threadIdx.x + 256 * q;
     v[q] = 0.f;
-    id[q] = e < a.E ? e : -1;
+    id[q] = e < E ? e : -1;
   }
   for (int s0 = 0; s0 < slots; s0 += kBatch) {
     float pv[Q][kBatch];
@@ -400,21 +400,21 @@ __global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a) {
   for (int q = 0; q < Q; ++q) {
     key[q] = 0;
     if (id[q] >= 0) {
-      a.logits[int64_t(t) * a.E + id[q]] = v[q];
+      a.logits[int64_t(t) * E + id[q]] = v[q];
       key[q] = topk_key(v[q], id[q]);
       lk[id[q]] = key[q];
     }
   }
   const int k = a.top_k;
   if (k == 0) return;
-  const int nseg = (a.E + 63) / 64, ns = nseg * k;
+  const int nseg = (E + 63) / 64, ns = nseg * k;
   for (int c = threadIdx.x; c < ns; c += 256) sk[c] = 0;
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     if (id[q] < 0) continue;
     const int seg = id[q] / 64;                      // the same for the whole wave
-    const int n = min(64, a.E - 64 * seg);          // a multiple of 16
+    const int n = min(64, E - 64 * seg);          // a multiple of 16
     int rank = 0;
     if (n == 64) {                                   // a full segment: fixed offsets, no masks
       const uint64_t* sp = lk + 64 * seg;
@@ -451,9 +451,11 @@ __global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a) {
 template <int ME, int NT, bool WX>
 void gemm_launch(const RouterArgs& a, hipStream_t stream) {
   if (a.passes == 2)
-    hipLaunchKernelGGL((router_gemm_kernel<ME, NT, 2, WX>), dim3(a.p.workgroups), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((router_gemm_kernel<ME, NT, 2, WX>), dim3(a.p.workgroups), dim3(256), 0, stream, a.x,
+                       a.packed, a.T, a.E, a.H, a.p.partial_slots, a.p.n_eg, a.p.kw, a);
   else
-    hipLaunchKernelGGL((router_gemm_kernel<ME, NT, 1, WX>), dim3(a.p.workgroups), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((router_gemm_kernel<ME, NT, 1, WX>), dim3(a.p.workgroups), dim3(256), 0, stream, a.x,
+                       a.packed, a.T, a.E, a.H, a.p.partial_slots, a.p.n_eg, a.p.kw, a);
 }
 
 }  // namespace
@@ -477,9 +479,12 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
   else gemm_launch<2, 4, false>(a, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.E <= 256) hipLaunchKernelGGL(router_topk_kernel<1>, dim3(a.T), dim3(256), 0, stream, a);
-  else if (a.E <= 512) hipLaunchKernelGGL(router_topk_kernel<2>, dim3(a.T), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(router_topk_kernel<4>, dim3(a.T), dim3(256), 0, stream, a);
+  if (a.E <= 256) hipLaunchKernelGGL(router_topk_kernel<1>, dim3(a.T), dim3(256), 0, stream, a.part, a.T, a.E,
+                       a.p.partial_slots, a);
+  else if (a.E <= 512) hipLaunchKernelGGL(router_topk_kernel<2>, dim3(a.T), dim3(256), 0, stream, a.part, a.T, a.E,
+                       a.p.partial_slots, a);
+  else hipLaunchKernelGGL(router_topk_kernel<4>, dim3(a.T), dim3(256), 0, stream, a.part, a.T, a.E,
+                       a.p.partial_slots, a);
   return hipGetLastError();
 }
 
