@@ -75,7 +75,8 @@ typedef enum {
                                    one launch less); at most 2048 sequences */
   HPA_SCHED_BALANCED_SINGLE = 4 /* as FUSED, and split sequences are merged inside the
                                    same kernel by the workgroup that completes them
-                                   (one launch per step) */
+                                   (one launch per step); refused (HPA_ERR_UNSUPPORTED)
+                                   when the partial workspace reaches 4 GiB */
 } hpa_sched;
 
 /* Sticky device error bits (hpa_read_device_error). */
@@ -83,8 +84,9 @@ enum {
   HPA_DEVERR_SEQ_LEN = 1,      /* seq_len < 0 or > max_pages_per_seq * 64 */
   HPA_DEVERR_PAGE_ID = 2,      /* page id outside [0, num_pages) */
   HPA_DEVERR_PROLOGUE = 4,     /* append position outside the page table */
-  HPA_DEVERR_PLAN = 8          /* attention launched with a different worker count than planned,
-                                  or a plan workspace that is not a plan */
+  HPA_DEVERR_PLAN = 8          /* attention launched with another worker count, batch or KV-head
+                                  count than the plan was made for, or a plan workspace that is
+                                  not a plan (nothing of that plan is read) */
 };
 
 typedef struct {
@@ -103,8 +105,9 @@ typedef struct {
  * All arrays are int32. header[0..15]: 0 W' (active workers), 1 N (tiles),
  * 2 S (sequences), 3 n_items, 4 n_merge, 5 n_partials, 6 sticky error word,
  * 7 W (workers the plan was made for), 8 D (tail chunks), 9 Ws (workers with a
- * static range). worker_off has Ws + D + 1 entries: the items of static worker
- * v < Ws, then those of tail chunk c (virtual worker Ws + c). */
+ * static range), 10 B and 11 Hkv (the batch and KV-head count it was made
+ * for). worker_off has Ws + D + 1 entries: the items of static worker v < Ws,
+ * then those of tail chunk c (virtual worker Ws + c). */
 typedef struct {
   size_t header, C, worker_off, item_s, item_t0, item_t1, item_split, item_slot,
          num_splits, partial_base, merge_list, total_bytes;
@@ -169,8 +172,20 @@ enum {
   HPA_ATTN_MERGE_ONLY = 2   /* launch only the merge of an earlier HPA_ATTN_NO_MERGE call */
 };
 
-/* Decode attention: out[b, h] = softmax(sm_scale * q K^T) V over the first
+/* Decode attention over the paged cache (openai-hub.com "腾讯混元HPC-Ops升级：五大算子
+ * 直击推理痛点", section "五大算子覆盖了哪些场景": variable-length attention reading a
+ * paged KV cache; xiaodao.ai "HPC-Ops 把 TPOT 降 48.8%，用户未必快一半", section
+ * "为什么 batch 越大，数字越漂亮": the balanced split-KV schedule and the two static
+ * ones it is compared with; bitbyai.com "vLLM × HPC-Ops …", section "Breaking
+ * Down the Kernels": persistent, load-balanced decode attention):
+ * out[b, h] = softmax(sm_scale * q K^T) V over the first
  * seq_lens[b] tokens of request b (a zero row when seq_lens[b] == 0).
+ * Arguments: desc as above; q, k_cache, v_cache, seq_lens, page_table, out in the
+ * layouts at the top of this file (device memory, caller-owned, never freed or
+ * kept); num_workers 0 = the schedule's default; plan_ws / partial_ws: device
+ * workspaces of at least the sizes the queries return. A plan whose header names
+ * another worker count, batch or KV-head count than this call is refused on the
+ * device (HPA_DEVERR_PLAN; no output row of the balanced schedule is written).
  * HPA_SCHED_BALANCED runs the persistent kernel over the plan made by hpa_plan
  * with the same num_workers, then the merge kernel. HPA_SCHED_BALANCED_FUSED
  * needs no hpa_plan call: the persistent kernel evaluates the planner's closed

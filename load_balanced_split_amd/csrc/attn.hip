@@ -207,9 +207,10 @@ constexpr int kAccRegs = kValuProducts ? 2 * kValuMaxGroup : 8;
 // counted on the vector memory counter only (a flat one also holds up LDS waits).
 typedef __attribute__((address_space(1))) int32_t gint32_t;
 
-// Sticky device error bits in the plan header (callers check a.plan when it may be null).
+// Sticky device error bits (in the plan header, or where the caller redirected them;
+// callers check a.err when it may be null).
 __device__ inline void report_error(const AttnArgs& a, int bits) {
-  __hip_atomic_fetch_or((gint32_t*)(a.plan + a.po.header + H_ERR), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_or((gint32_t*)a.err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Dynamic tail: the last positions of the plan are cut into D chunks that the
@@ -542,7 +543,7 @@ struct Worker {
     st.L = it.L >= 0 ? it.L : sload(a.seq_lens, st.b);
     st.kscale = FP8 ? sloadf(a.k_scale, st.g) : 1.f;
     st.vscale = FP8 ? sloadf(a.v_scale, st.g) : 1.f;
-    if (!st.valid && threadIdx.x == 0 && a.plan) report_error(a, HPA_DEVERR_PLAN);
+    if (!st.valid && threadIdx.x == 0 && a.err) report_error(a, HPA_DEVERR_PLAN);
     return st;
   }
 
@@ -591,7 +592,7 @@ struct Worker {
   }
 
   __device__ void report_bad_page() const {
-    if (lane == 0 && a.plan) report_error(a, HPA_DEVERR_PAGE_ID);
+    if (lane == 0 && a.err) report_error(a, HPA_DEVERR_PAGE_ID);
   }
 
   // Stream this wave's units of item st; unit `wave` is already in bufA (okA: it
@@ -949,8 +950,11 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_balanced_
   const int W = gridDim.x;
   const int Wp = sload(a.plan, a.po.header + H_WP), Ws = sload(a.plan, a.po.header + H_WS);
   const int D = sload(a.plan, a.po.header + H_ND);
-  if (sload(a.plan, a.po.header + H_W) != W || Wp < 0 || Wp > W || Ws < 0 || Ws > Wp || D < 0 ||
-      D > kTailChunksPerWorker * W) {
+  // a plan made for another launch shape (worker count, batch or KV heads) is refused
+  // before any of its arrays is read: they sit at offsets that depend on that shape
+  if (sload(a.plan, a.po.header + H_W) != W || sload(a.plan, a.po.header + H_B) != a.batch ||
+      sload(a.plan, a.po.header + H_HKV) != a.hkv || sload(a.plan, a.po.header + H_S) != a.batch * a.hkv ||
+      Wp < 0 || Wp > W || Ws < 0 || Ws > Wp || D < 0 || D > kTailChunksPerWorker * W) {
     if (w == 0 && threadIdx.x == 0) report_error(a, HPA_DEVERR_PLAN);
     return;
   }
@@ -996,7 +1000,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_static_kernel(AttnArgs a
   const int b = s / a.hkv;
   int L = a.seq_lens[b];
   if (L < 0 || L > a.max_pages * kPage) {
-    if (k == 0 && threadIdx.x == 0 && a.plan) report_error(a, HPA_DEVERR_SEQ_LEN);
+    if (k == 0 && threadIdx.x == 0 && a.err) report_error(a, HPA_DEVERR_SEQ_LEN);
     return;
   }
   const int n = (L + kPage - 1) / kPage;
@@ -1288,7 +1292,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
       s0 = __builtin_amdgcn_readfirstlane(seq_of_tile(P.C, S, pos));
     }
   }
-  if (w == 0 && threadIdx.x == 0 && bad && a.plan) report_error(a, HPA_DEVERR_SEQ_LEN);
+  if (w == 0 && threadIdx.x == 0 && bad && a.err) report_error(a, HPA_DEVERR_SEQ_LEN);
   // empty (or invalid) sequences own no tile: their zero rows are spread over the workers
   for (int s = w; s < S; s += W) {
     if (P.C[s + 1] == P.C[s]) {
@@ -1332,6 +1336,7 @@ struct MergeArgs {
   int num_splits, partial_base, header;   // plan offsets (int32 words)
   int hkv, hq, group, max_pages, workers;
   int slots, static_splits, static_chunk;
+  int batch;
 };
 
 // The arrays and offsets the first loads need also lead the argument list as scalars:
@@ -1351,11 +1356,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int32_t* seq
   // every fact this block needs is one scalar load away from its sequence index,
   // and all of those loads go out together
   const int L = sload(seq_lens, s / hkv);
-  int n = 0, base = 0, planned_w = a.workers;
+  int n = 0, base = 0, planned_w = a.workers, planned_b = a.batch, planned_hkv = hkv;
   if constexpr (MODE != MERGE_STATIC) {
     n = sload(plan, off_splits + s);
     base = sload(plan, off_base + s);
-    if constexpr (MODE == MERGE_PLAN) planned_w = sload(plan, a.header + H_W);
+    if constexpr (MODE == MERGE_PLAN) {
+      planned_w = sload(plan, a.header + H_W);
+      planned_b = sload(plan, a.header + H_B);
+      planned_hkv = sload(plan, a.header + H_HKV);
+    }
   }
   if constexpr (MODE == MERGE_STATIC) {
     if (L < 0 || L > a.max_pages * kPage) return;
@@ -1371,7 +1380,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int32_t* seq
   // another launch shape.
   bool skip = (n == 1) | (n < 0) | ((n > 1) & ((base < 0) | (base + n > a.slots)));
   if constexpr (MODE == MERGE_FUSED) skip |= (L <= 0) | (L > a.max_pages * kPage);
-  if constexpr (MODE == MERGE_PLAN) skip |= planned_w != a.workers;
+  if constexpr (MODE == MERGE_PLAN) skip |= (planned_w != a.workers) | (planned_b != a.batch) | (planned_hkv != hkv);
   if (skip) return;
   const int b = s / a.hkv, g = s - b * a.hkv;
   uint16_t* orow = a.out + (int64_t(b) * a.hq + g * a.group + hh) * kHeadDim + d0;
@@ -1500,7 +1509,7 @@ hipError_t launch_merge(const AttnArgs& a, MergeMode mode, hipStream_t stream) {
   const MergeArgs m{a.seq_lens, a.plan, a.part_acc, a.part_m, a.part_l, a.out,
                     a.po.num_splits, a.po.partial_base, a.po.header,
                     a.hkv, a.hq, a.group, a.max_pages, a.workers,
-                    static_cast<int>(a.slots), a.static_splits, a.static_chunk};
+                    static_cast<int>(a.slots), a.static_splits, a.static_chunk, a.batch};
   const dim3 grid(S, a.group, kHeadDim / kMergeDims);
   const bool two = int64_t(S) * a.group <= a.workers;   // at most one block per worker (CU)
   if (mode == MERGE_PLAN)

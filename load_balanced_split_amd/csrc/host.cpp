@@ -218,6 +218,33 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
                            const int32_t* seq_lens, const int32_t* page_table, int32_t num_workers,
                            void* plan_ws, size_t plan_ws_bytes, void* partial_ws, size_t partial_ws_bytes,
                            void* out, int32_t flags, hipStream_t stream) {
+  return hpa::decode_attn(desc, sched, q, k_cache, v_cache, k_scale, v_scale, seq_lens, page_table, num_workers,
+                          plan_ws, plan_ws_bytes, partial_ws, partial_ws_bytes, out, flags, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace hpa {
+
+hpa_status attn_workspace_bytes(const hpa_attn_desc* desc, hpa_sched sched, int32_t num_workers, int32_t* workers,
+                                size_t* plan_bytes, size_t* partial_bytes) {
+  hpa_status st = check_desc(desc);
+  if (st != HPA_OK) return st;
+  int32_t W = 0;
+  if ((st = resolve_workers(num_workers, static_cast<int>(sched), &W)) != HPA_OK) return st;
+  const int64_t S = int64_t(desc->batch) * desc->num_kv_heads;
+  const int G = desc->num_q_heads / desc->num_kv_heads;
+  *workers = W;
+  *plan_bytes = size_t(plan_offsets(S, W).total) * 4;
+  *partial_bytes = static_cast<size_t>(partial_layout(max_slots(W, S), G).total_bytes + trace_bytes(W + S));
+  return HPA_OK;
+}
+
+hpa_status decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const void* q, const void* k_cache,
+                       const void* v_cache, const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                       const int32_t* page_table, int32_t num_workers, void* plan_ws, size_t plan_ws_bytes,
+                       void* partial_ws, size_t partial_ws_bytes, void* out, int32_t flags,
+                       const AttnRedirect* redirect, hipStream_t stream) {
   hpa_status st = check_desc(desc);
   if (st != HPA_OK) return st;
   if (sched != HPA_SCHED_BALANCED && sched != HPA_SCHED_STATIC_SPLITS && sched != HPA_SCHED_STATIC_CHUNK &&
@@ -243,6 +270,11 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   const int64_t need = pl.total_bytes + hpa::trace_bytes(W + S);
   if (partial_ws_bytes < static_cast<size_t>(need))
     return fail(HPA_ERR_WORKSPACE, "partial workspace %zu bytes < %lld", partial_ws_bytes, (long long)need);
+  // the in-kernel merge addresses the partials through buffer resources with 32-bit
+  // byte offsets
+  if (sched == HPA_SCHED_BALANCED_SINGLE && pl.l + hpa::max_slots(W, S) * G * 4 > int64_t(UINT32_MAX))
+    return fail(HPA_ERR_UNSUPPORTED, "single-launch schedule: partial workspace of %lld bytes needs 32-bit offsets",
+                (long long)pl.total_bytes);
   const hpa::PlanOffsets po = hpa::plan_offsets(S, W);
   if (sched == HPA_SCHED_BALANCED || sched == HPA_SCHED_BALANCED_FUSED || sched == HPA_SCHED_BALANCED_SINGLE) {
     if (!plan_ws) return fail(HPA_ERR_INVALID_ARG, "balanced schedules need plan_ws");
@@ -261,9 +293,15 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
   a.seq_lens = seq_lens;
   a.page_table = page_table;
   a.plan = static_cast<int32_t*>(plan_ws);
+  a.err = a.plan ? a.plan + po.header + hpa::H_ERR : nullptr;
   a.gctr = a.plan ? a.plan + po.gctr : nullptr;
   a.sctr = a.plan ? a.plan + po.sctr : nullptr;
   a.qctr = a.plan ? a.plan + po.qctr : nullptr;
+  if (redirect) {
+    a.err = redirect->err;
+    a.gctr = redirect->gctr;
+    a.sctr = redirect->sctr;
+  }
   char* pw = static_cast<char*>(partial_ws);
   a.part_acc = reinterpret_cast<float*>(pw + pl.acc);
   a.part_m = reinterpret_cast<float*>(pw + pl.m);
@@ -312,6 +350,10 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
     return fail(HPA_ERR_LAUNCH, "merge launch failed");
   return HPA_OK;
 }
+
+}  // namespace hpa
+
+extern "C" {
 
 hpa_status hpa_decode_prologue(const hpa_attn_desc* desc, const void* q_in, const void* k_in, const void* v_in,
                                const float* q_norm_w, const float* k_norm_w, float eps, double rope_theta,

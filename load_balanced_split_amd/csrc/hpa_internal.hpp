@@ -51,7 +51,8 @@ __host__ __device__ inline int v_block_index(int t, int d, bool fp8) {
 
 // Header slots of the plan workspace (int32).
 enum : int {
-  H_WP = 0, H_N = 1, H_S = 2, H_NITEMS = 3, H_NMERGE = 4, H_NPART = 5, H_ERR = 6, H_W = 7, H_ND = 8, H_WS = 9
+  H_WP = 0, H_N = 1, H_S = 2, H_NITEMS = 3, H_NMERGE = 4, H_NPART = 5, H_ERR = 6, H_W = 7, H_ND = 8, H_WS = 9,
+  H_B = 10, H_HKV = 11
 };
 
 // Offsets of the plan arrays, in int32 elements.
@@ -135,6 +136,7 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const int32_t* page_table;
   int32_t* plan;               // plan workspace (may be null for static schedules)
+  int32_t* err;                // sticky device error word (may be null: errors are dropped)
   int32_t* gctr;               // in-kernel merge arrival counters (fused schedule), in plan
   int32_t* sctr;
   int32_t* qctr;               // dynamic tail counters [claimed, finished], in plan
@@ -294,6 +296,25 @@ hipError_t launch_prologue(const hpa_attn_desc& d, const uint16_t* q_in, const u
                            int32_t* seq_lens_out, int32_t* err_word, const PlanArgs* plan, hipStream_t stream);
 hipError_t launch_clear_word(int32_t* word, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, int32_t* sink, hipStream_t stream);
+
+// Where the allocation-free entry point puts what normally lives in the plan
+// workspace at shape-dependent offsets: the error word and the in-kernel merge's
+// arrival counters (which must be zero at every launch, so they stay at one place).
+struct AttnRedirect {
+  int32_t* err;
+  int32_t* gctr;
+  int32_t* sctr;
+};
+// hpa_decode_attn's body (host.cpp); redirect may be null.
+hpa_status decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const void* q, const void* k_cache,
+                       const void* v_cache, const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                       const int32_t* page_table, int32_t num_workers, void* plan_ws, size_t plan_ws_bytes,
+                       void* partial_ws, size_t partial_ws_bytes, void* out, int32_t flags,
+                       const AttnRedirect* redirect, hipStream_t stream);
+// Validates desc, resolves num_workers (0: the schedule's default) and returns the
+// plan and partial workspace bytes hpa_decode_attn needs for that worker count.
+hpa_status attn_workspace_bytes(const hpa_attn_desc* desc, hpa_sched sched, int32_t num_workers, int32_t* workers,
+                                size_t* plan_bytes, size_t* partial_bytes);
 
 // Records a message for hpa_last_error_message() on this thread and returns st
 // (defined in host.cpp; for the entry points of other source files).

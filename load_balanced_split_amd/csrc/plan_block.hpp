@@ -208,6 +208,8 @@ __device__ void plan_block(const Lens& lens, int B, int Hkv, int max_pages, int 
     ws[po.qctr + 1] = 0;
     hdr[H_N] = N;
     hdr[H_S] = S;
+    hdr[H_B] = B;
+    hdr[H_HKV] = Hkv;
     hdr[H_NITEMS] = carry_i;
     hdr[H_NMERGE] = carry_m;
     hdr[H_NPART] = carry_p;

@@ -112,6 +112,16 @@ def test_calls_reject_bad_arguments_before_launching(L):
     n = ctypes.c_int32(0)
     assert L.hpa_default_num_workers(0, 7, ctypes.byref(n)) == 1
     assert L.hpa_default_num_workers(0, 0, None) == 1
+    # single-launch schedule: partials the in-kernel merge cannot address with 32-bit
+    # offsets (16 heads per KV head, 200k workers: > 4 GiB of partial slots) are refused
+    d16 = _desc(num_q_heads=16)
+    huge = ctypes.c_size_t(1 << 40)
+    assert L.hpa_decode_attn(ctypes.byref(d16), 4, fake, fake, fake, None, None, fake, fake, 200000, fake, huge,
+                             fake, huge, fake, 0, None) == 2
+    assert "32-bit" in _lib.hpa_last_error_message()
+    # the same shape on the fused schedule (merge kernel) passes that check
+    assert L.hpa_decode_attn(ctypes.byref(d16), 3, fake, fake, fake, None, None, fake, fake, 200000, None, 0,
+                             fake, huge, fake, 0, None) == 1            # ... and stops at the missing plan_ws
     # empty batch is a no-op
     d0 = _desc(batch=0)
     assert L.hpa_decode_attn(ctypes.byref(d0), 1, None, None, None, None, None, None, None, 512, None, 0,

@@ -22,7 +22,7 @@ def gpu():
     _lib.lib()
 
 
-def _replays(step, other, out, reps=3):
+def _replays(step, other, out, reps=3, scrub=None):
     step()
     torch.cuda.synchronize()
     ref = [t.clone() for t in out]
@@ -34,6 +34,8 @@ def _replays(step, other, out, reps=3):
         torch.cuda.synchronize()
         for t in out:
             t.zero_()
+        if scrub is not None:
+            scrub()                               # outside the graph: stale data turns into NaN
         g.replay()
         torch.cuda.synchronize()
         for t, r in zip(out, ref):
@@ -51,7 +53,8 @@ def test_attention_step_graph_replays_match_eager(kv_dtype, prologue):
     d = DeviceStep(w)
     for sched in ("balanced", "fused", "single"):
         print(f"graph {kv_dtype} prologue={prologue} {sched}", flush=True)
-        _replays(lambda: d.step(sched), lambda: d.step("static_splits"), [d.out])
+        _replays(lambda: d.step(sched), lambda: d.step("static_splits"), [d.out],
+                 scrub=(lambda: d.partial_ws.fill_(0xFF)) if sched == "single" else None)
         assert d.device_error() == 0
 
 

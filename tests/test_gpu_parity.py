@@ -111,6 +111,8 @@ def run_and_compare(w, sched="balanced", W=0, min_tiles=_lib.FUSED_MIN_TILES, re
     from load_balanced_split_amd.runner import DeviceStep
     d = DeviceStep(w, num_workers=W)
     print(f"attn {what} {w.name} sched={sched} W={d.num_workers}", flush=True)
+    if sched == "single":
+        scrub_partials(d)
     d.step(sched, min_tiles)
     torch.cuda.synchronize()
     assert d.device_error() == 0
@@ -119,6 +121,13 @@ def run_and_compare(w, sched="balanced", W=0, min_tiles=_lib.FUSED_MIN_TILES, re
     got = d.output_f64()
     r = assert_within(got, ref, w.kv_dtype, f"{w.name} {sched} W={W}")
     return got, r, d
+
+
+def scrub_partials(d):
+    """Fill the partial workspace with NaN (all bits set) before a single-launch step:
+    a fold that read a partial before its producer's stores were visible would then
+    give a non-finite or different output instead of an earlier run's equal bits."""
+    d.partial_ws.fill_(0xFF)
 
 
 def oracle_out(w):
@@ -350,6 +359,33 @@ def test_device_errors_are_reported_not_faulted():
     assert d.device_error(clear=True) & _lib.DEVERR_PLAN
 
 
+def test_plan_for_another_batch_shape_is_refused():
+    """A plan made for B = 3 (or for the same B x Hkv split differently) used by a
+    B = 4 launch with the same worker count: the device reports HPA_DEVERR_PLAN and
+    neither the attention nor the merge kernel writes an output row."""
+    from load_balanced_split_amd.runner import DeviceStep
+    w = inputs.build_workload("shape", [700, 64, 3000, 129], 8, 1, "bf16", seed=18)
+    d = DeviceStep(w, num_workers=6)
+    d.step("balanced")
+    torch.cuda.synchronize()
+    assert d.device_error() == 0
+    good = d.out.clone()
+    for B, hkv, hq in ((3, 1, 8), (2, 2, 16)):
+        desc = _lib.make_desc(B, hq, hkv, w.max_pages, w.num_pages)
+        lens = d.seq_lens[:B].contiguous()
+        print(f"plan shape B={B} hkv={hkv} against B=4 hkv=1", flush=True)
+        _lib.hpa_plan(desc, lens, 6, _lib.FUSED_MIN_TILES, _lib.FUSED_ITEM_COST, 0, 1, d.plan_ws)
+        d.out.fill_(7.0)
+        d.attend("balanced")
+        torch.cuda.synchronize()
+        assert d.device_error(clear=True) & _lib.DEVERR_PLAN, (B, hkv)
+        assert torch.all(d.out == 7.0), (B, hkv)
+    # a plan of the right shape works again on the same workspace
+    d.step("balanced")
+    torch.cuda.synchronize()
+    assert d.device_error() == 0 and torch.equal(d.out, good)
+
+
 @pytest.mark.parametrize("hkv", [1, 2])
 def test_fused_schedule_both_planners(hkv):
     """Up to 256 sequences the fused kernel plans in registers, above that in LDS: both
@@ -378,6 +414,7 @@ def test_single_launch_merge_counters_reset_across_steps():
     want = d.out.clone()
     for rep in range(4):
         d.out.zero_()
+        scrub_partials(d)
         d.step("single")
         torch.cuda.synchronize()
         assert torch.equal(d.out, want), rep
@@ -386,6 +423,7 @@ def test_single_launch_merge_counters_reset_across_steps():
     d.step("balanced")
     torch.cuda.synchronize()
     want2 = d.out.clone()
+    scrub_partials(d)
     d.step("single")
     torch.cuda.synchronize()
     assert torch.equal(d.out, want2)
@@ -437,6 +475,8 @@ def test_tail_claim_counters_reset_across_launches():
     for rep in range(3):
         for sched in ("fused", "single", "balanced"):
             d.out.zero_()
+            if sched == "single":
+                scrub_partials(d)
             d.attend(sched)
             torch.cuda.synchronize()
             assert torch.equal(d.out, want), (rep, sched)
