@@ -216,6 +216,27 @@ hpa_status hpa_decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const voi
                            size_t plan_ws_bytes, void* partial_ws, size_t partial_ws_bytes,
                            void* out, int32_t flags, hipStream_t stream);
 
+/* Allocation-free hpa_decode_attn, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The plan and partial workspaces are taken from a device array of
+ * 32 MiB that the library holds on every GPU it runs on until the process ends;
+ * the call itself allocates nothing. Same arguments and results as
+ * hpa_decode_attn without plan_ws / partial_ws / flags, for the schedules that
+ * need no hpa_plan call: HPA_SCHED_BALANCED_FUSED, HPA_SCHED_BALANCED_SINGLE,
+ * HPA_SCHED_STATIC_SPLITS, HPA_SCHED_STATIC_CHUNK (others: HPA_ERR_INVALID_ARG).
+ * Limits: at most 4096 workers and 2048 sequences (batch x KV heads), and both
+ * workspaces together within the array (e.g. 256 workers, 2048 sequences, 16
+ * query heads per KV head fit); beyond them HPA_ERR_UNSUPPORTED, nothing
+ * launched. device_error (device int32, may be NULL) receives the sticky
+ * HPA_DEVERR_* bits instead of a plan workspace. The first call on a device looks
+ * up the array's device address and clears its counters on `stream`. Every call
+ * on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (other streams, other threads) race and must not be issued. */
+hpa_status hpa_decode_attn_noalloc(const hpa_attn_desc* desc, hpa_sched sched, const void* q,
+                                   const void* k_cache, const void* v_cache, const float* k_scale,
+                                   const float* v_scale, const int32_t* seq_lens, const int32_t* page_table,
+                                   int32_t num_workers, void* out, int32_t* device_error, hipStream_t stream);
+
 /* Fused decode prologue (bitbyai.com "vLLM × HPC-Ops …", "Breaking Down the
  * Kernels"): for each request b at position pos = positions[b]:
  *   q_out[b,h] = RoPE(RMSNorm(q_in[b,h]; q_norm_w, eps), pos)     (bf16)

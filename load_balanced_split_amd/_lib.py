@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "hpa_plan": [D, _P, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P],
             "hpa_decode_attn": [D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I, _P, ctypes.c_size_t,
                                 _P, ctypes.c_size_t, _P, _I, _P],
+            "hpa_decode_attn_noalloc": [D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P],
             "hpa_decode_prologue": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
                                     _P, _P, _P, _P, _P, _P, _P, _P],
             "hpa_decode_prologue_plan": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
@@ -191,6 +192,15 @@ def hpa_decode_attn(desc, sched, q, k_cache, v_cache, k_scale, v_scale, seq_lens
                                  num_workers, _ptr(plan_ws), pbytes, _ptr(partial_ws),
                                  partial_ws.numel() * partial_ws.element_size(), _ptr(out), flags,
                                  _stream(stream)), "hpa_decode_attn")
+
+
+def hpa_decode_attn_noalloc(desc, sched, q, k_cache, v_cache, k_scale, v_scale, seq_lens, page_table,
+                            num_workers, out, device_error=None, stream=None):
+    sched = SCHED[sched] if isinstance(sched, str) else int(sched)
+    _check(lib().hpa_decode_attn_noalloc(ctypes.byref(desc), sched, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens), _ptr(page_table),
+                                         num_workers, _ptr(out), _ptr(device_error), _stream(stream)),
+           "hpa_decode_attn_noalloc")
 
 
 def hpa_decode_prologue(desc, q_in, k_in, v_in, q_norm_w, k_norm_w, eps, rope_theta, positions,

@@ -122,6 +122,15 @@ def test_calls_reject_bad_arguments_before_launching(L):
     # the same shape on the fused schedule (merge kernel) passes that check
     assert L.hpa_decode_attn(ctypes.byref(d16), 3, fake, fake, fake, None, None, fake, fake, 200000, None, 0,
                              fake, huge, fake, 0, None) == 1            # ... and stops at the missing plan_ws
+    # allocation-free call: schedules that need a plan, and shapes beyond its scratch array,
+    # are refused before anything touches the device
+    na = lambda desc, sched, W: L.hpa_decode_attn_noalloc(ctypes.byref(desc), sched, fake, fake, fake, None, None,
+                                                          fake, fake, W, fake, None, None)
+    assert na(d, 0, 64) == 1                                          # HPA_SCHED_BALANCED needs hpa_plan
+    assert na(d, 3, 5000) == 2                                        # more than 4096 workers
+    assert na(_desc(batch=3000), 3, 64) == 2                          # more than 2048 sequences
+    assert na(_desc(batch=2048, num_q_heads=16), 4, 4096) == 2        # workspaces beyond 32 MiB
+    assert na(_desc(batch=0), 3, 64) == 0                             # empty batch: nothing to do
     # empty batch is a no-op
     d0 = _desc(batch=0)
     assert L.hpa_decode_attn(ctypes.byref(d0), 1, None, None, None, None, None, None, None, 512, None, 0,
