@@ -28,6 +28,8 @@
  *  out             [B, Hq, 128]                    bf16
  *  k_cache         [num_pages, Hkv, 8192]          bf16 or OCP E4M3 codes, tiled page blocks
  *  v_cache         [num_pages, Hkv, 8192]          bf16 or OCP E4M3 codes, tiled page blocks
+ *                  (the row-major page [num_pages, Hkv, 64, 128] in another element
+ *                  order; hpa_kv_pack_pages converts row-major pages to it)
  *  k_scale,v_scale [Hkv]                           fp32 (E4M3 caches only; value = code * scale)
  *  seq_lens        [B]                             int32, live KV length per request
  *  page_table      [B, max_pages_per_seq]          int32 physical page of each 64-token tile
@@ -113,6 +115,24 @@ typedef struct {
          num_splits, partial_base, merge_list, total_bytes;
   int32_t max_items;           /* 5 W + S: at most 4 W tail chunks */
 } hpa_plan_layout;
+
+/* Row-major pages -> tiled page blocks (openai-hub.com "腾讯混元HPC-Ops升级：五大算子
+ * 直击推理痛点", section "五大算子覆盖了哪些场景": the attention call reads a paged
+ * KV cache; the pages fix no in-page order). k_rows, v_rows: device,
+ * [count, Hkv, 64, 128] row-major pages (token-major, dims innermost) of bf16
+ * values or OCP E4M3 codes (desc->kv_dtype), 16-byte aligned. For i < count,
+ * block (pages[i], g) of k_cache / v_cache ([num_pages, Hkv, 8192], the tiled
+ * order above) receives page i of head g, element by element (no arithmetic:
+ * the bytes move). pages: device int32 [count], or NULL for the whole pool
+ * (count == num_pages, page i -> block i); with NULL the source may be the
+ * cache itself (conversion in place: every block is read whole before it is
+ * written). A page id outside [0, num_pages) is skipped and sets
+ * HPA_DEVERR_PAGE_ID in device_error (device int32, may be NULL). Only
+ * desc->num_kv_heads, num_pages, head_dim, page_size and kv_dtype are read.
+ * One launch on `stream`; nothing allocated. */
+hpa_status hpa_kv_pack_pages(const hpa_attn_desc* desc, const void* k_rows, const void* v_rows,
+                             const int32_t* pages, int32_t count, void* k_cache, void* v_cache,
+                             int32_t* device_error, hipStream_t stream);
 
 /* Default worker count of a schedule on a device: compute units x workgroups of
  * that schedule's attention kernel that fit on one CU at once (cached per device).

@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "hpa_plan": [D, _P, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P],
             "hpa_decode_attn": [D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I, _P, ctypes.c_size_t,
                                 _P, ctypes.c_size_t, _P, _I, _P],
+            "hpa_kv_pack_pages": [D, _P, _P, _P, _I, _P, _P, _P, _P],
             "hpa_decode_attn_noalloc": [D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P],
             "hpa_decode_prologue": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
                                     _P, _P, _P, _P, _P, _P, _P, _P],
@@ -192,6 +193,15 @@ def hpa_decode_attn(desc, sched, q, k_cache, v_cache, k_scale, v_scale, seq_lens
                                  num_workers, _ptr(plan_ws), pbytes, _ptr(partial_ws),
                                  partial_ws.numel() * partial_ws.element_size(), _ptr(out), flags,
                                  _stream(stream)), "hpa_decode_attn")
+
+
+def hpa_kv_pack_pages(desc, k_rows, v_rows, pages, k_cache, v_cache, device_error=None, stream=None):
+    """Row-major [count, Hkv, 64, 128] pages -> tiled blocks pages[i] of the caches (pages None:
+    the whole pool, page i -> block i; may then be the caches themselves)."""
+    count = desc.num_pages if pages is None else pages.numel()
+    _check(lib().hpa_kv_pack_pages(ctypes.byref(desc), _ptr(k_rows), _ptr(v_rows), _ptr(pages), count,
+                                   _ptr(k_cache), _ptr(v_cache), _ptr(device_error), _stream(stream)),
+           "hpa_kv_pack_pages")
 
 
 def hpa_decode_attn_noalloc(desc, sched, q, k_cache, v_cache, k_scale, v_scale, seq_lens, page_table,

@@ -140,6 +140,30 @@ def tile_v(x: np.ndarray, kv_dtype: str) -> np.ndarray:
     return np.ascontiguousarray(y).reshape(*lead, PAGE * HEAD_DIM)
 
 
+def _untile(y: np.ndarray, shape, perm) -> np.ndarray:
+    lead = y.shape[:-1]
+    k = len(lead)
+    stored = [shape[i] for i in perm]
+    x = y.reshape(*lead, *stored)
+    inv = [perm.index(i) for i in range(len(perm))]
+    x = x.transpose(*range(k), *(k + i for i in inv))
+    return np.ascontiguousarray(x).reshape(*lead, PAGE, HEAD_DIM)
+
+
+def untile_k(y: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """[..., 8192] tiled K blocks -> [..., 64, 128] logical (row-major) pages: tile_k undone."""
+    if kv_dtype == "bf16":
+        return _untile(y, (2, 4, 2, 4, 4, 4, 8), (0, 2, 4, 5, 1, 3, 6))
+    return _untile(y, (4, 4, 4, 2, 4, 16), (1, 3, 4, 0, 2, 5))
+
+
+def untile_v(y: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """[..., 8192] tiled V blocks -> [..., 64, 128] logical (row-major) pages: tile_v undone."""
+    if kv_dtype == "bf16":
+        return _untile(y, (2, 4, 8, 8, 16), (0, 3, 1, 4, 2))
+    return _untile(y, (4, 16, 8, 16), (2, 0, 3, 1))
+
+
 def _draw_pool(rng, num_pages, hkv):
     """Standard normal float32 [num_pages, hkv, 64, D], drawn in page chunks."""
     out = np.empty((num_pages, hkv, PAGE, HEAD_DIM), np.float32)

@@ -131,6 +131,16 @@ def test_calls_reject_bad_arguments_before_launching(L):
     assert na(_desc(batch=3000), 3, 64) == 2                          # more than 2048 sequences
     assert na(_desc(batch=2048, num_q_heads=16), 4, 4096) == 2        # workspaces beyond 32 MiB
     assert na(_desc(batch=0), 3, 64) == 0                             # empty batch: nothing to do
+    # row-major page packing: count must cover the pool without a page list, no in-place
+    # conversion through a page list, 16-byte aligned pointers, head_dim 128
+    pk = lambda desc, kr, pages, n, kc: L.hpa_kv_pack_pages(ctypes.byref(desc), kr, kr, pages, n, kc, kc, None, None)
+    other = ctypes.c_void_p(0x20000)
+    assert pk(d, fake, None, 15, other) == 1                      # num_pages is 16
+    assert pk(d, fake, fake, 4, fake) == 1                        # in place with a page list
+    assert pk(d, ctypes.c_void_p(0x1004), None, 16, other) == 1   # misaligned
+    assert pk(d, fake, fake, -1, other) == 1
+    assert pk(_desc(head_dim=64), fake, None, 16, other) == 2
+    assert pk(d, fake, fake, 0, other) == 0                       # nothing to pack
     # empty batch is a no-op
     d0 = _desc(batch=0)
     assert L.hpa_decode_attn(ctypes.byref(d0), 1, None, None, None, None, None, None, None, 512, None, 0,

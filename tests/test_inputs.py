@@ -50,3 +50,18 @@ def test_fp8_scales_cover_pool():
     assert (w.k_cache & 0x7F).max() <= 0x7E            # no NaN codes, 448 reached
     assert ((w.k_cache & 0x7F) == 0x7E).any()
     assert w.page_table[1, 700 // 64] >= 0              # page for the appended token exists
+
+
+def test_untile_undoes_tile_and_matches_the_layout_formulas():
+    """untile_k / untile_v (the row-major pages a caller of hpa_kv_pack_pages holds)
+    invert tile_k / tile_v, and agree with the element-by-element layout decoder."""
+    from oracle.kv_layout import page_rows
+    rng = np.random.default_rng(3)
+    for dt, top, dtype in (("bf16", 65535, np.uint16), ("fp8", 255, np.uint8)):
+        x = rng.integers(0, top, size=(3, 2, 64, 128)).astype(dtype)
+        for tile, untile, kind in ((inputs.tile_k, inputs.untile_k, "k"), (inputs.tile_v, inputs.untile_v, "v")):
+            y = tile(x, dt)
+            assert np.array_equal(untile(y, dt), x)
+            for p in range(3):
+                for g in range(2):
+                    assert np.array_equal(page_rows(y[p, g], kind, dt), x[p, g])
