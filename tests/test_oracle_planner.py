@@ -325,3 +325,13 @@ def test_skewed_workload_static_vs_balanced_shape():
     st = op.static_partition(lens, 1, 512, 2048, "splits")
     assert st["S_split"] == 16
     assert max(t1 - t0 for _, _, t0, t1, _ in st["items"]) == 128
+
+
+def test_static_partitions_hand_worked():
+    """Both static flavours against a hand-worked case in which they differ (a
+    'chunk' partition that split nothing, or split like 'splits', fails)."""
+    g = json.load(open(os.path.join(GOLDEN, "static_partitions.json")))
+    for flavour in ("splits", "chunk"):
+        p = op.static_partition(g["seq_lens"], g["hkv"], g["num_workers"], g["max_pages"], flavour)
+        assert p["S_split"] == g["S_split"]
+        assert [list(it) for it in p["items"]] == g[flavour], flavour
