@@ -915,6 +915,7 @@ struct Worker {
 // Items of worker w from the planner's work list (scalar loads; next() only
 // issues them, the entry is checked when the driver opens it), then those of
 // the tail chunks it claims (virtual workers Ws + c).
+template <bool INMERGE = false>
 struct PlanSource {
   const AttnArgs& a;
   int i, i1;
@@ -935,6 +936,13 @@ struct PlanSource {
     }
     it = Item{sload(a.plan, a.po.item_s + i), sload(a.plan, a.po.item_t0 + i), sload(a.plan, a.po.item_t1 + i),
               sload(a.plan, a.po.item_slot + i), -1, 0, 0};
+    if constexpr (INMERGE) {
+      // the in-kernel merge needs the sequence's split count and slot base (a bad
+      // sequence index is caught when the item is opened; read sequence 0 then)
+      const int sq = (it.s >= 0 && it.s < a.batch * a.hkv) ? it.s : 0;
+      it.nsplit = sload(a.plan, a.po.num_splits + sq);
+      it.pbase = sload(a.plan, a.po.partial_base + sq);
+    }
     ++i;
     if (i == i1 && q.open()) q.want = true;   // the last item held: claim the next chunk
     return true;
@@ -942,7 +950,7 @@ struct PlanSource {
   __device__ void fix(Item&) const {}
 };
 
-template <bool FP8>
+template <bool FP8, bool INMERGE>
 __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_balanced_kernel(AttnArgs a) {
   __shared__ CombineLds lds;
   WaveTrace tr(a);
@@ -958,6 +966,17 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_balanced_
     if (w == 0 && threadIdx.x == 0) report_error(a, HPA_DEVERR_PLAN);
     return;
   }
+  if constexpr (INMERGE) {
+    // no merge kernel follows: empty (or invalid) sequences get their zero rows here
+    const int S = a.batch * a.hkv;
+    for (int s = w; s < S; s += W) {
+      if (sload(a.plan, a.po.num_splits + s) == 0) {
+        const int b = s / a.hkv, g = s - b * a.hkv;
+        uint16_t* row = a.out + (int64_t(b) * a.hq + g * a.group) * kHeadDim;
+        for (int i = threadIdx.x; i < a.group * kHeadDim; i += kAttnThreads) row[i] = 0;
+      }
+    }
+  }
   if (w >= Wp) return;
   const int cap = (1 + kTailChunksPerWorker) * W + a.batch * a.hkv;   // the work list's size bound
   int i0 = 0, i1 = 0;
@@ -969,8 +988,8 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_balanced_
       i1 = i0;                            // still take part in the tail, so its counters return to 0
     }
   }
-  PlanSource src{a, i0, i1, Ws, cap};
-  Worker<FP8> r(a, lds);
+  PlanSource<INMERGE> src{a, i0, i1, Ws, cap};
+  Worker<FP8, INMERGE> r(a, lds);
   r.trec = tr.rec;
   r.tq = TailQueue{a.qctr, lds.claim, D};
   r.run(src);
@@ -1455,15 +1474,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int32_t* seq
 
 int attn_blocks_per_cu(bool fp8) {
   int nb = 0, nf = 0;
-  hipError_t e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_balanced_kernel<true>, kAttnThreads, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_balanced_kernel<false>, kAttnThreads, 0);
+  hipError_t e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_balanced_kernel<true, false>, kAttnThreads, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_balanced_kernel<false, false>, kAttnThreads, 0);
+  int nm = 0;
+  hipError_t h = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nm, attn_balanced_kernel<true, true>, kAttnThreads, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nm, attn_balanced_kernel<false, true>, kAttnThreads, 0);
   hipError_t f = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, attn_fused_kernel<true, false>, kAttnThreads, 0)
                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, attn_fused_kernel<false, false>, kAttnThreads, 0);
   int ns = 0;
   hipError_t g = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&ns, attn_fused_kernel<true, true>, kAttnThreads, 0)
                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&ns, attn_fused_kernel<false, true>, kAttnThreads, 0);
-  if (e != hipSuccess || f != hipSuccess || g != hipSuccess || nb <= 0 || nf <= 0 || ns <= 0) return 1;
-  return std::min(nb, std::min(nf, ns));
+  if (e != hipSuccess || f != hipSuccess || g != hipSuccess || h != hipSuccess || nb <= 0 || nf <= 0 || ns <= 0 ||
+      nm <= 0)
+    return 1;
+  return std::min(std::min(nb, nm), std::min(nf, ns));
 }
 
 int attn_static_blocks_per_cu(bool fp8) {
@@ -1473,11 +1497,16 @@ int attn_static_blocks_per_cu(bool fp8) {
   return (e != hipSuccess || n <= 0) ? 1 : n;
 }
 
-hipError_t launch_attn_balanced(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream) {
-  if (fp8)
-    hipLaunchKernelGGL(attn_balanced_kernel<true>, dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+hipError_t launch_attn_balanced(const AttnArgs& a, bool fp8, bool merge_in_kernel, int num_workers,
+                                hipStream_t stream) {
+  if (fp8 && merge_in_kernel)
+    hipLaunchKernelGGL((attn_balanced_kernel<true, true>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+  else if (fp8)
+    hipLaunchKernelGGL((attn_balanced_kernel<true, false>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+  else if (merge_in_kernel)
+    hipLaunchKernelGGL((attn_balanced_kernel<false, true>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_balanced_kernel<false>, dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_balanced_kernel<false, false>), dim3(num_workers), dim3(kAttnThreads), 0, stream, a);
   return hipGetLastError();
 }
 

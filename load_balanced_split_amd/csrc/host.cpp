@@ -250,10 +250,6 @@ hpa_status decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const void* q
   if (sched != HPA_SCHED_BALANCED && sched != HPA_SCHED_STATIC_SPLITS && sched != HPA_SCHED_STATIC_CHUNK &&
       sched != HPA_SCHED_BALANCED_FUSED && sched != HPA_SCHED_BALANCED_SINGLE)
     return fail(HPA_ERR_INVALID_ARG, "sched %d", static_cast<int>(sched));
-  if ((sched == HPA_SCHED_BALANCED_FUSED || sched == HPA_SCHED_BALANCED_SINGLE) &&
-      int64_t(desc->batch) * desc->num_kv_heads > hpa::kFusedMaxSeqs)
-    return fail(HPA_ERR_UNSUPPORTED, "fused schedule plans at most %d sequences (batch x kv heads)",
-                hpa::kFusedMaxSeqs);
 
   if (flags & ~(HPA_ATTN_NO_MERGE | HPA_ATTN_MERGE_ONLY) || flags == (HPA_ATTN_NO_MERGE | HPA_ATTN_MERGE_ONLY))
     return fail(HPA_ERR_INVALID_ARG, "flags %d", flags);
@@ -325,15 +321,25 @@ hpa_status decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const void* q
   a.tail_den = HPA_FUSED_TAIL_DEN;
   a.tail_chunk = HPA_FUSED_TAIL_CHUNK;
   if (sched == HPA_SCHED_BALANCED || sched == HPA_SCHED_BALANCED_FUSED || sched == HPA_SCHED_BALANCED_SINGLE) {
+    // Batches of more than kFusedMaxSeqs sequences do not fit the fused kernels' LDS
+    // plan: the planner kernel writes the same work list (the fused parameters) to
+    // plan_ws first and the planned kernels run over it -- identical items, slots and
+    // output bits, one launch more.
+    const bool via_plan = sched != HPA_SCHED_BALANCED && S > hpa::kFusedMaxSeqs;
+    if (via_plan && (sched == HPA_SCHED_BALANCED_SINGLE || do_attn) &&
+        hpa::launch_plan(seq_lens, desc->batch, desc->num_kv_heads, desc->max_pages_per_seq, W, a.min_tiles,
+                         a.item_cost, a.tail_den, a.tail_chunk, a.plan, po, stream) != hipSuccess)
+      return fail(HPA_ERR_LAUNCH, "planner launch failed");
     if (sched == HPA_SCHED_BALANCED_SINGLE) {
-      // one launch: the persistent kernel plans, attends and merges (flags have no effect)
-      if (hpa::launch_attn_fused(a, fp8, true, W, stream) != hipSuccess)
+      // one launch (two above kFusedMaxSeqs): plan, attend and merge (flags have no effect)
+      if ((via_plan ? hpa::launch_attn_balanced(a, fp8, true, W, stream)
+                    : hpa::launch_attn_fused(a, fp8, true, W, stream)) != hipSuccess)
         return fail(HPA_ERR_LAUNCH, "attention launch failed");
       return HPA_OK;
     }
-    const bool fused = sched == HPA_SCHED_BALANCED_FUSED;
+    const bool fused = sched == HPA_SCHED_BALANCED_FUSED && !via_plan;
     if (do_attn && (fused ? hpa::launch_attn_fused(a, fp8, false, W, stream)
-                          : hpa::launch_attn_balanced(a, fp8, W, stream)) != hipSuccess)
+                          : hpa::launch_attn_balanced(a, fp8, false, W, stream)) != hipSuccess)
       return fail(HPA_ERR_LAUNCH, "attention launch failed");
     if (do_merge && hpa::launch_merge(a, fused ? hpa::MERGE_FUSED : hpa::MERGE_PLAN, stream) != hipSuccess)
       return fail(HPA_ERR_LAUNCH, "merge launch failed");

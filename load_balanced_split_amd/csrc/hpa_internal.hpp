@@ -274,13 +274,15 @@ __device__ inline int wave_incl_scan(int x) {
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_pages, int num_workers,
                        int min_tiles, int item_cost, int tail_den, int tail_chunk, int32_t* plan,
                        const PlanOffsets& po, hipStream_t stream);
-hipError_t launch_attn_balanced(const AttnArgs& a, bool fp8, int num_workers, hipStream_t stream);
+hipError_t launch_attn_balanced(const AttnArgs& a, bool fp8, bool merge_in_kernel, int num_workers,
+                                hipStream_t stream);
 hipError_t launch_attn_static(const AttnArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_attn_fused(const AttnArgs& a, bool fp8, bool merge_in_kernel, int num_workers, hipStream_t stream);
 // merge modes: which schedule produced the partials
 enum MergeMode : int { MERGE_PLAN = 0, MERGE_STATIC = 1, MERGE_FUSED = 2 };
 hipError_t launch_merge(const AttnArgs& a, MergeMode mode, hipStream_t stream);
-constexpr int kFusedMaxSeqs = 2048;  // sequences (B x Hkv) the fused schedule plans in LDS
+constexpr int kFusedMaxSeqs = 2048;  // sequences (B x Hkv) the fused schedules plan in LDS; larger
+                                     // batches plan in the workspace first (one launch more)
 constexpr int kRegPlanSeqs = 256;    // up to this many, every wave plans in registers instead
 // The planner's arguments when the prologue launch also plans (hpa_decode_prologue_plan).
 struct PlanArgs {
