@@ -8,17 +8,21 @@ launch, same work list, same output bits) is reported beside it. The default
 workload is the skewed batch (1 x 131072 + 31 x 4096 tokens, 8:1 GQA, head dim
 128, 64-token pages, bf16 KV), where the pages report their kernel-level gain.
 
-Timing:
-* headline: K steps (rounded down to a multiple of R) replayed from one HIP
-  graph holding R steps, back to back, bracketed by a device synchronise; the
-  batch is held in R copies used round-robin so that
-  R - 1 other copies (more than twice the 256 MB Infinity Cache) are read
-  between two uses of the same bytes -- each step reads its KV from HBM.
-* per kernel: for each launch kind (planner, attention, merge) a loop of
-  back-to-back launches of that kind alone over the same rotating copies,
+Timing (every workload 0-4 by default; the headline is --workload, default 2):
+* whole steps: HIP graphs holding at least 10 consecutive steps (whole
+  rotations over R copies of the batch, used round-robin so that R - 1 other
+  copies -- more than twice the 256 MB Infinity Cache -- are read between two
+  uses of the same bytes: each step reads its KV from HBM). The replays are
+  queued behind a bounded spin kernel, with HIP events between them, so each
+  event span is GPU time only. The headline value is the mean over exactly
+  --steps steps; every per_config entry times at least 100 steps, and
+  p10/p50/p90 are over replays (a replay's span over its steps).
+* per kernel: for each launch kind (prologue, planner, attention, merge) a graph
+  of back-to-back launches of that kind alone over the same rotating copies,
   bracketed by HIP events on the launch stream; average = span / launches.
-* comparison: the same two passes for the static split-KV schedules.
-* CPU baseline: the fp64 oracle timed on the host on the same batch.
+* comparison: the same for the static split-KV schedules.
+* CPU baseline: the fp64 oracle timed on the host on the same batch (a bounded
+  number of whole-batch runs; one thread as well for workloads 0-2).
 
 Prints ONE JSON line.
 """
@@ -46,7 +50,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", type=int, default=2, help="0..4 (2 = skewed 1x128K + 31x4K)")
+    p.add_argument("--workload", type=int, default=2, help="headline workload 0..4 (2 = skewed 1x128K + 31x4K)")
+    p.add_argument("--workloads", type=int, nargs="*", default=[0, 1, 2, 3, 4],
+                   help="workloads measured for the per_config block (the headline one always)")
+    p.add_argument("--only-headline", action="store_true", help="measure the headline workload only")
     p.add_argument("--num-workers", type=int, default=0)
     p.add_argument("--schedule", choices=["fused", "balanced"], default="fused",
                    help="headline balanced schedule: planner inside the persistent kernel (fused) "
@@ -56,7 +63,6 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probe", action="store_true", help="skip the plain streaming-read probe")
     p.add_argument("--no-router", action="store_true", help="skip the split-precision router GEMM")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--trace", action="store_true",
                    help="use the instrumented build and report per-CU busy time (tail balance) instead")
     p.add_argument("--products", choices=["mfma", "valu"], default="mfma",
@@ -248,93 +254,120 @@ def algorithmic_bytes(w):
     return kv, kv + other, pro
 
 
-def main():
-    args = parse()
-    if args.trace:
-        return trace_main(args)
-    if args.pmc_run:
-        return pmc_main(args)
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path is measured on one "
-              "GPU's share of the work; across GPUs each would plan and attend only its own requests' tiles",
-              file=sys.stderr)
-        sys.exit(2)
-    os.environ["HPA_PRODUCTS"] = args.products
+class Timer:
+    """GPU time of back-to-back steps.
+
+    Steps are captured in HIP graphs of several consecutive steps each (rotating
+    over the copies). The replays are enqueued behind a spin kernel that holds
+    the GPU for a few milliseconds (torch.cuda._sleep, bounded), so the host has
+    queued every replay and event before the GPU reaches them: the span between
+    two consecutive events is the GPU time of one replay's steps, with no host
+    submission gap in it. A sample is one replay: its span over its step count.
+    """
+
+    BATCH = 40
+
+    def __init__(self, stream):
+        import torch
+        self.torch, self.stream = torch, stream
+        # calibrate the spin kernel: cycles per microsecond
+        torch.cuda._sleep(1000)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.cuda._sleep(2_000_000)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_us = 2_000_000 / max(1.0, e0.elapsed_time(e1) * 1e3)
+        self.sleep_cycles = int(per_us * 4000)          # ~4 ms of spinning per batch
+
+    def run(self, plan):
+        """plan: [(graph, steps it holds)] replayed in order; returns [(span_us, steps)]."""
+        torch = self.torch
+        out = []
+        for b0 in range(0, len(plan), self.BATCH):
+            part = plan[b0:b0 + self.BATCH]
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(part) + 1)]
+            torch.cuda.synchronize()
+            torch.cuda._sleep(self.sleep_cycles)
+            ev[0].record(self.stream)
+            for i, (g, _) in enumerate(part):
+                g.replay()
+                ev[i + 1].record(self.stream)
+            torch.cuda.synchronize()
+            out += [(ev[i].elapsed_time(ev[i + 1]) * 1e3, n) for i, (_, n) in enumerate(part)]
+        return out
+
+
+GRAPH_STEPS = 10      # at least this many consecutive steps per captured graph
+
+
+def pct(xs, f):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))]
+
+
+def measure_workload(idx, args, stream, timer, steps, headline):
+    """Every schedule on one workload: per-step times of whole steps (HIP events),
+    per-kernel averages, the attention kernel's roofline, static split-KV beside it
+    and the oracle on the host cores."""
     import torch
     from load_balanced_split_amd import _lib, inputs
     from load_balanced_split_amd.runner import DeviceStep
-
-    assert torch.cuda.is_available(), "no GPU"
-    _lib.lib()                               # fails loudly if libhpa.so is missing
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w = inputs.config_workload(args.workload)
+    t_build = time.perf_counter()
+    w = inputs.config_workload(idx)
     kv_bytes, alg_bytes, pro_bytes = algorithmic_bytes(w)
     pool_bytes = w.k_cache.nbytes + w.v_cache.nbytes
-    R = max(2, math.ceil(2 * MALL_BYTES / max(pool_bytes, 1)) + 1)
-    R = min(R, 16)
-    # num_workers 0: each schedule takes the library's default for it
+    R = min(16, max(2, math.ceil(2 * MALL_BYTES / max(pool_bytes, 1)) + 1))
     copies = [DeviceStep(w, num_workers=args.num_workers, device="cuda:0") for _ in range(R)]
     W = copies[0].num_workers
-    print(f"[bench] workload {args.workload} ({w.name}): KV {kv_bytes / 1e6:.1f} MB, {R} copies, W={W}",
-          file=sys.stderr, flush=True)
-    stream = torch.cuda.current_stream()
-
-    def run_step(d, sched):
-        d.step(sched)
-
-    # eager reference outputs (also the warm-up of every code path)
-    scheds = ["balanced", "fused", "single"] + ([] if args.no_static else ["static_splits", "static_chunk"])
+    print(f"[bench] workload {idx} ({w.name}): KV {kv_bytes / 1e6:.1f} MB, {R} copies, W={W}, "
+          f"built in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
+    head = args.schedule
+    scheds = ["fused", "balanced", "single"] + ([] if args.no_static else ["static_splits", "static_chunk"])
     eager = {}
     for s in scheds:
         for d in copies:
-            run_step(d, s)
+            d.step(s)
         torch.cuda.synchronize()
         eager[s] = copies[0].out.clone()
-        assert copies[0].device_error() == 0
+        assert copies[0].device_error() == 0, (idx, s)
 
-    spread = {}
+    # steps per graph: whole rotations over the copies, at least GRAPH_STEPS
+    per_graph = R * math.ceil(GRAPH_STEPS / R)
 
-    def graph_time(sched):
-        """Seconds per step: one HIP graph holds one step per copy (R steps), replayed
-        back to back, so host launch cost is paid once per R steps. Also keeps the
-        10th/50th/90th percentile of the per-step time over the replays (HIP events
-        around each replay on the launch stream)."""
+    def capture(sched, n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for d in copies:
-                run_step(d, sched)
+            for i in range(n):
+                copies[i % R].step(sched)
+        return g
+
+    def step_times(sched, n):
+        """n steps exactly: full graphs of per_graph steps, then one graph of the rest;
+        returns the samples [(span_us, steps)]."""
+        full = capture(sched, per_graph)
+        rest = n % per_graph
+        plan = [(full, per_graph)] * (n // per_graph)
+        if rest:
+            plan.append((capture(sched, rest), rest))
         torch.cuda.synchronize()
-        for i in range(max(1, args.warmup // R)):
-            g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, args.steps // R)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        t0 = time.perf_counter()
-        ev[0].record(stream)
-        for i in range(reps):
-            g.replay()
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        per_step = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 / R for i in range(reps))
-        q = lambda f: per_step[min(len(per_step) - 1, int(f * len(per_step)))]
-        spread[sched] = [round(q(0.1), 2), round(q(0.5), 2), round(q(0.9), 2)]
-        # every copy's graph output equals the eager output, bit for bit
-        for d in copies:
+        timer.run([(full, per_graph)] * max(1, math.ceil(args.warmup / per_graph)))   # warm-up
+        samples = timer.run(plan)
+        for d in copies:                                  # every replay equals the eager output
             assert torch.equal(d.out, eager[sched]), f"graph replay of {sched} differs from eager"
-        del g
-        return (t1 - t0) / (reps * R)
+        del plan, full
+        return samples
 
     def kernel_times(sched):
-        """Average duration (ms) of each launch kind: HIP events on the launch stream
+        """Average duration (us) of each launch kind: HIP events on the launch stream
         around the replay of a graph of event_steps back-to-back launches of that kind
-        alone (rotating copies), so that short kernels are not bound by host submission."""
+        alone (rotating copies)."""
         if w.has_prologue and sched == "balanced":
-            kinds = ["prologue+plan"]                                   # one launch (runner.step)
+            kinds = ["prologue+plan"]
         else:
             kinds = (["prologue"] if w.has_prologue else []) + (["plan"] if sched == "balanced" else [])
-        kinds += ["attn"] if sched == "single" else ["attn", "merge"]    # single: one launch merges too
+        kinds += ["attn"] if sched == "single" else ["attn", "merge"]
         launch = {
             "prologue+plan": lambda d: d.prologue_plan(),
             "prologue": lambda d: d.prologue(),
@@ -358,81 +391,130 @@ def main():
             g.replay()
             e1.record(stream)
             torch.cuda.synchronize()
-            res[kind] = e0.elapsed_time(e1) / args.event_steps
+            res[kind] = round(e0.elapsed_time(e1) * 1e3 / args.event_steps, 2)
             del g
         for d in copies:
             assert torch.equal(d.out, eager[sched])
         return res
 
-    # the balanced method -- headline schedule, the other balanced schedule beside it
-    head = args.schedule
-    other = "balanced" if head == "fused" else "fused"
-    step_s = graph_time(head)
-    ev = kernel_times(head)
-    us = step_s * 1e6
-    kv_gbps = kv_bytes / step_s / 1e9
-    attn_s = ev["attn"] * 1e-3
-    achieved = alg_bytes / attn_s / 1e9
+    def summary(samples):
+        steps = sum(n for _, n in samples)
+        mean = sum(t for t, _ in samples) / steps
+        per = [t / n for t, n in samples]
+        return {"steps": steps, "samples": len(samples), "steps_per_sample": per_graph,
+                "us_per_step": round(mean, 2),
+                "us_p10_p50_p90": [round(pct(per, f), 2) for f in (0.1, 0.5, 0.9)],
+                "kv_gbps": round(kv_bytes / (mean * 1e-6) / 1e9, 1),
+                "kv_frac_of_peak": round(kv_bytes / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+    ent = {"workload": inputs.CONFIG_NAMES[idx], "num_workers": W, "static_num_workers": copies[0].static_workers,
+           "rotating_copies": R, "kv_bytes": kv_bytes, "algorithmic_bytes": alg_bytes}
+    if pro_bytes:
+        ent["prologue_bytes"] = pro_bytes
+    ent[SCHED_NAMES[head]] = summary(step_times(head, max(100, steps)))
+    # exactly the requested number of steps (the headline value)
+    exact = summary(step_times(head, steps)) if headline else None
+    kt = kernel_times(head)
+    ent[SCHED_NAMES[head]]["kernel_us"] = kt
+    attn_us = kt["attn"]
+    am = attn_us + kt.get("merge", 0.0)
+    ent["attn_kv_frac"] = round(kv_bytes / (attn_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
+    ent["attn_plus_merge_kv_frac"] = round(kv_bytes / (am * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
+    ent["roofline"] = {"bound": "hbm", "kernel": attn_kernel_name(head, w.kv_dtype),
+                       "achieved": round(alg_bytes / (attn_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                       "unit": "GB/s", "frac": round(alg_bytes / (attn_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                       "traffic": traffic_per_launch(head, w.kv_dtype, idx, args.products)}
+    for other in ("balanced", "single", "fused"):
+        if other == head:
+            continue
+        e = summary(step_times(other, max(100, steps)))
+        e["kernel_us"] = kernel_times(other)
+        ent[SCHED_NAMES[other]] = e
+    if not args.no_static:
+        st = {}
+        for s in ("static_splits", "static_chunk"):
+            e = summary(step_times(s, max(100, steps)))
+            k = kernel_times(s)
+            e.update({"attn_us": k["attn"], "merge_us": k["merge"],
+                      "balanced_speedup": round(e["us_per_step"] / ent[SCHED_NAMES[head]]["us_per_step"], 3),
+                      "balanced_attn_speedup": round(k["attn"] / attn_us, 3)})
+            st[s] = e
+        ent["static_split_kv"] = st
+    del copies
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        ent["cpu_baseline"] = cpu_baseline(w, kv_bytes, CPU_BUDGET_S[idx], single_thread=idx <= 2)
+    return ent, exact, w
+
+
+def main():
+    args = parse()
+    if args.trace:
+        return trace_main(args)
+    if args.pmc_run:
+        return pmc_main(args)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path is measured on one "
+              "GPU's share of the work; across GPUs each would plan and attend only its own requests' tiles",
+              file=sys.stderr)
+        sys.exit(2)
+    os.environ["HPA_PRODUCTS"] = args.products
+    import torch
+    from load_balanced_split_amd import _lib, inputs
+
+    assert torch.cuda.is_available(), "no GPU"
+    _lib.lib()                               # fails loudly if libhpa.so is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    timer = Timer(stream)
+    workloads = [args.workload] if args.only_headline else sorted(set(args.workloads) | {args.workload})
+    per_config = {}
+    head_w = exact = None
+    for idx in workloads:
+        ent, exact_k, w = measure_workload(idx, args, stream, timer, args.steps, idx == args.workload)
+        per_config[WORKLOAD_KEYS[idx]] = ent
+        if idx == args.workload:
+            head_w, exact = w, exact_k
+    head = per_config[WORKLOAD_KEYS[args.workload]]
+    hs = head[SCHED_NAMES[args.schedule]]
+    mean_us = exact["us_per_step"]
     result = {
         "metric": METRIC,
-        "value": round(kv_gbps, 1),
+        "value": round(head["kv_bytes"] / (mean_us * 1e-6) / 1e9, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": max(1, args.steps // R) * R,
+        "steps": exact["steps"],
         "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 5),
+        "ms_per_step": round(mean_us * 1e-3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 q/out",
+        "dtype": "bf16" if head_w.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 q/out",
         "data": "synthetic (seeded; shapes and length mix of the pages' kernel benchmark)",
-        "config": {"workload": inputs.CONFIG_NAMES[args.workload], "schedule": SCHED_NAMES[head],
-                   "num_workers": W, "static_num_workers": copies[0].static_workers,
-                   "products": args.products, "rotating_copies": R, "kv_bytes": kv_bytes,
-                   "algorithmic_bytes": alg_bytes},
-        "us_per_step": round(us, 2),
-        "us_per_step_p10_p50_p90": spread[head],
-        "kv_frac_of_peak": round(kv_gbps / PEAK_HBM_GBPS, 4),
-        "kernel_us": {k: round(v * 1e3, 2) for k, v in ev.items()},
-        "attn_plus_merge_kv_gbps": round(kv_bytes / ((ev["attn"] + ev.get("merge", 0.0)) * 1e-3) / 1e9, 1),
-        "attn_plus_merge_kv_frac": round(kv_bytes / ((ev["attn"] + ev.get("merge", 0.0)) * 1e-3) / 1e9
-                                         / PEAK_HBM_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": attn_kernel_name(head, w.kv_dtype),
-                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic_per_launch(head, w.kv_dtype, args.workload, args.products)},
+        "config": {"workload": head["workload"], "schedule": SCHED_NAMES[args.schedule],
+                   "num_workers": head["num_workers"], "products": args.products,
+                   "rotating_copies": head["rotating_copies"], "kv_bytes": head["kv_bytes"],
+                   "algorithmic_bytes": head["algorithmic_bytes"]},
+        "us_per_step": round(mean_us, 2),
+        "us_per_step_p10_p50_p90": exact["us_p10_p50_p90"],
+        "timing": f"HIP events around graph replays of {exact['steps_per_sample']} consecutive steps, queued "
+                  "behind a spin kernel; value and ms_per_step: mean over exactly `steps` steps; "
+                  "percentiles over replays (per_config: at least 100 steps)",
+        "kv_frac_of_peak": round(head["kv_bytes"] / (mean_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "kernel_us": hs["kernel_us"],
+        "attn_plus_merge_kv_frac": head["attn_plus_merge_kv_frac"],
+        "roofline": head["roofline"],
     }
-    if pro_bytes:
-        result["config"]["prologue_bytes"] = pro_bytes
-    # the other balanced schedule: same work list and bits, planner inside / outside the kernel
-    tf = graph_time(other)
-    ef = kernel_times(other)
-    result[SCHED_NAMES[other]] = {"us_per_step": round(tf * 1e6, 2), "kv_gbps": round(kv_bytes / tf / 1e9, 1),
-                                  "kernel_us": {k: round(v * 1e3, 2) for k, v in ef.items()},
-                                  "kv_frac_of_peak": round(kv_bytes / tf / 1e9 / PEAK_HBM_GBPS, 4)}
-    # single launch: planner, attention and merge in one persistent kernel
-    t1 = graph_time("single")
-    e1 = kernel_times("single")
-    result["balanced_single_launch"] = {"us_per_step": round(t1 * 1e6, 2), "kv_gbps": round(kv_bytes / t1 / 1e9, 1),
-                                        "kernel_us": {k: round(v * 1e3, 2) for k, v in e1.items()}}
-    if not args.no_static:
-        st = {}
-        for s in scheds[3:]:
-            t = graph_time(s)
-            e = kernel_times(s)
-            st[s] = {"us_per_step": round(t * 1e6, 2), "attn_us": round(e["attn"] * 1e3, 2),
-                     "merge_us": round(e["merge"] * 1e3, 2),
-                     "balanced_speedup": round(t / step_s, 3),
-                     "balanced_attn_speedup": round(e["attn"] / ev["attn"], 3)}
-        result["static_split_kv"] = st
+    if "cpu_baseline" in head:
+        result["cpu_baseline"] = head["cpu_baseline"]
+    result["per_config"] = per_config
     if not args.no_router:
         result["router_gemm"] = router_bench(args, stream)
     if not args.no_probe:
         probe = stream_read_probe(stream)
-        probe["attn_frac_of_probe"] = round(achieved / probe["gbps"], 4)
+        probe["attn_frac_of_probe"] = round(head["roofline"]["achieved"] / probe["gbps"], 4)
         result["stream_read_probe"] = probe
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, kv_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
@@ -545,7 +627,7 @@ def stream_read_probe(stream, gib=4, launches=10):
     return best
 
 
-SCHED_NAMES = {"fused": "balanced_fused", "balanced": "balanced_planned"}
+SCHED_NAMES = {"fused": "balanced_fused", "balanced": "balanced_planned", "single": "balanced_single_launch"}
 WORKLOAD_KEYS = {0: "tiny", 1: "uniform", 2: "skewed", 3: "mix", 4: "fp8_prologue"}
 
 
@@ -569,8 +651,14 @@ def traffic_per_launch(sched, kv_dtype, workload, products="mfma"):
     return None if t is None else int(round(t))
 
 
-def cpu_baseline(w, kv_bytes, budget_s):
-    """The fp64 oracle, as it stands, on the host cores over the same batch."""
+# seconds of oracle time per workload (each a bounded sample: whole batches, repeated)
+CPU_BUDGET_S = {0: 2.0, 1: 3.0, 2: 6.0, 3: 8.0, 4: 8.0}
+
+
+def cpu_baseline(w, kv_bytes, budget_s, single_thread=False):
+    """The fp64 oracle, as it stands, on the host: the whole batch, repeated within a
+    time budget (median). It runs with a BLAS pool of one thread per CPU this process
+    may use; cores = that count, avg_busy_threads = process CPU time / wall time."""
     import threadpoolctl
     from oracle import attention as oa
     from oracle import prologue as opro
@@ -584,26 +672,31 @@ def cpu_baseline(w, kv_bytes, budget_s):
             oa.decode_attention(w.q, w.k_cache, w.v_cache, w.seq_lens, w.page_table, w.hkv, w.sm_scale,
                                 w.kv_dtype, w.k_scale, w.v_scale)
 
-    def timed(budget):
+    def timed(budget, threads):
         times = []
-        t_end = time.perf_counter() + budget
-        while True:
-            t0 = time.perf_counter()
-            once()
-            times.append(time.perf_counter() - t0)
-            if time.perf_counter() > t_end or len(times) >= 50:
-                break
-        return float(np.median(times)), len(times)
+        with threadpoolctl.threadpool_limits(threads):
+            c0, t_end = time.process_time(), time.perf_counter() + budget
+            w0 = time.perf_counter()
+            while True:
+                t0 = time.perf_counter()
+                once()
+                times.append(time.perf_counter() - t0)
+                if time.perf_counter() > t_end or len(times) >= 50:
+                    break
+            busy = (time.process_time() - c0) / max(1e-9, time.perf_counter() - w0)
+        return float(np.median(times)), len(times), busy
 
-    t, n = timed(budget_s)
-    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
-    with threadpoolctl.threadpool_limits(1):
-        t1, n1 = timed(budget_s / 3)
-    return {"value": round(kv_bytes / t / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "us_per_step": round(t * 1e6, 1),
-            "sample": f"the whole batch, {n} runs (median), numpy fp64 gather-then-softmax",
-            "single_thread": {"value": round(kv_bytes / t1 / 1e9, 3), "us_per_step": round(t1 * 1e6, 1),
-                              "runs": n1}}
+    cpus = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    t, n, busy = timed(budget_s, cpus)
+    out = {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": cpus, "kind": "oracle",
+           "us_per_step": round(t * 1e6, 1), "os_cpu_count": os.cpu_count(),
+           "avg_busy_threads": round(busy, 2),
+           "sample": f"the whole batch, {n} runs (median), numpy fp64 gather-then-softmax"}
+    if single_thread:
+        t1, n1, _ = timed(budget_s / 2, 1)
+        out["single_thread"] = {"value": round(kv_bytes / t1 / 1e9, 4), "us_per_step": round(t1 * 1e6, 1),
+                                "runs": n1, "cores": 1}
+    return out
 
 
 if __name__ == "__main__":

@@ -74,7 +74,8 @@ typedef enum {
   HPA_SCHED_STATIC_CHUNK = 2,  /* fixed split size, grid sized for the longest */
   HPA_SCHED_BALANCED_FUSED = 3, /* the same balanced work list, computed inside the
                                    persistent kernel from seq_lens (no hpa_plan call,
-                                   one launch less); at most 2048 sequences */
+                                   one launch less); above 2048 sequences (B x Hkv)
+                                   the planner kernel runs first, into plan_ws */
   HPA_SCHED_BALANCED_SINGLE = 4 /* as FUSED, and split sequences are merged inside the
                                    same kernel by the workgroup that completes them
                                    (one launch per step); refused (HPA_ERR_UNSUPPORTED)
