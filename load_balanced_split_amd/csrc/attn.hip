@@ -1063,6 +1063,14 @@ __device__ inline int add_chunk_offsets(FusedPlanLds& P, int* arr, int S, int nc
   return total;
 }
 
+// The fused schedules always plan with the library's fixed parameters: as
+// compile-time constants the partition's divisions by them become multiplies
+// and the tail code (no tail) drops out.
+constexpr int kFusedCost = HPA_FUSED_ITEM_COST;
+constexpr int kFusedMinTiles = HPA_FUSED_MIN_TILES;
+constexpr int kFusedTailDen = HPA_FUSED_TAIL_DEN;
+constexpr int kFusedTailChunk = HPA_FUSED_TAIL_CHUNK;
+
 template <bool INMERGE>
 struct FusedSource {
   const AttnArgs& a;
@@ -1071,6 +1079,12 @@ struct FusedSource {
   int S;
   int v;                      // the virtual worker whose positions [pos, e) are being walked
   int pos, e, s;
+  // First item served from the register plan (no LDS read, no barrier, no division
+  // before its loads): sequence s, positions [r0, c1) of it, [lo, t1) its part; its
+  // split rank and split count are settled by fix().
+  bool reg_first = false;
+  int rf_c0 = 0, rf_c1 = 0, rf_lo = 0, rf_t1 = 0, rf_L = 0;
+  bool split_later = false;
   // Register plan: the partial-slot bases P.PB are not in LDS yet when the first item is
   // handed out. They are computed (wave 0) and published, with one barrier, on the
   // second call, i.e. behind the first unit's loads; fix() then settles the first
@@ -1088,7 +1102,7 @@ struct FusedSource {
         if (sq < S) {
           const int c0 = P.C[sq], c1 = P.C[sq + 1];
           if (c1 > c0) {
-            const int ns = part.owner(c1 - 1) - part.owner(c0 + a.item_cost) + 1;
+            const int ns = part.owner(c1 - 1) - part.owner(c0 + kFusedCost) + 1;
             val = ns > 1 ? ns : 0;
           }
         }
@@ -1103,6 +1117,13 @@ struct FusedSource {
   __device__ void fix(Item& it) {
     if (!first_later) return;
     first_later = false;
+    if (split_later) {        // the register-served first item: its split rank and count now
+      split_later = false;
+      const int first = __builtin_amdgcn_readfirstlane(part.owner(rf_c0 + kFusedCost));
+      first_split = v - first;
+      it.nsplit = __builtin_amdgcn_readfirstlane(part.owner(rf_c1 - 1)) - first + 1;
+      if (it.nsplit <= 1) it.slot = -1;
+    }
     const int pb = __builtin_amdgcn_readfirstlane(P.PB[it.s]);
     if (it.nsplit > 1) it.slot = pb + first_split;
     it.pbase = pb;
@@ -1114,13 +1135,22 @@ struct FusedSource {
   // positions [C[s], C[s+1]) of a non-empty sequence: item_cost virtual ones, then its tiles
   __device__ bool next(Item& it, TailQueue& q) {
     if (!pb_ready && calls > 0) publish_pb(threadIdx.x & 63, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
-    ++calls;
+    if (calls++ == 0 && reg_first) {
+      // a split item's slot is only known once the bases are: an in-range placeholder
+      // until fix() (nothing reads it before); a single item's slot becomes -1 there
+      it = Item{s, rf_lo - rf_c0 - kFusedCost, rf_t1 - rf_c0 - kFusedCost, 0, rf_L, 0, -1};
+      first_later = split_later = true;
+      pos = rf_t1;
+      if (pos + kFusedCost >= e && q.open()) q.want = true;
+      ++s;
+      return true;
+    }
     for (;;) {
       while (pos < e) {
         const int c0 = __builtin_amdgcn_readfirstlane(P.C[s]);
         const int c1 = __builtin_amdgcn_readfirstlane(P.C[s + 1]);
         if (c1 > c0) {
-          const int r0 = c0 + a.item_cost;
+          const int r0 = c0 + kFusedCost;
           const int t1 = min(e, c1), lo = max(pos, r0);
           pos = t1;
           if (lo < t1) {
@@ -1133,7 +1163,7 @@ struct FusedSource {
               // a split item's slot is only known once the bases are: an in-range
               // placeholder until fix() (nothing reads it before)
               it = Item{s, lo - r0, t1 - r0, ns > 1 ? 0 : -1, __builtin_amdgcn_readfirstlane(P.L[s]), ns, -1};
-              if (pos + a.item_cost >= e && q.open()) q.want = true;
+              if (pos + kFusedCost >= e && q.open()) q.want = true;
               ++s;
               return true;
             }
@@ -1143,7 +1173,7 @@ struct FusedSource {
             // item_cost positions after this item's end). Set before the one-lane store
             // below: after it, the compiler takes the flag, and with it the item
             // index, for divergent and reads the page table with vector loads.
-            if (pos + a.item_cost >= e && q.open()) q.want = true;
+            if (pos + kFusedCost >= e && q.open()) q.want = true;
             if (!INMERGE && split == 0 && threadIdx.x == 0) {   // record for the merge kernel
               a.plan[a.po.num_splits + s] = ns;
               a.plan[a.po.partial_base + s] = pb;
@@ -1207,13 +1237,13 @@ struct RegPlan {
       }
       L[k] = Lk;
       n[k] = tiles_of(Lk);
-      const int np = n[k] > 0 ? n[k] + a.item_cost : 0;   // positions: virtual tiles first
+      const int np = n[k] > 0 ? n[k] + kFusedCost : 0;   // positions: virtual tiles first
       const int incl = wave_incl_scan(np);
       C[k] = carry + incl - np;
       carry += __builtin_amdgcn_readlane(incl, 63);
     }
     N = carry;
-    part = Partition::make(N, N, W, a.min_tiles, a.tail_den, a.tail_chunk);
+    part = Partition::make(N, N, W, kFusedMinTiles, kFusedTailDen, kFusedTailChunk);
     bad = __builtin_amdgcn_ballot_w64(bad_lane) != 0;
   }
 };
@@ -1233,12 +1263,24 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
   const int W = gridDim.x, w = blockIdx.x;
   int N, bad, pos = 0, pend = 0, s0 = 0;
   Partition part;
+  // register plan: the first item, read straight from the registers (rf_*), and
+  // whether the LDS copy of the plan may be read before the next barrier (no)
+  bool reg_first = false, lds_ready = true;
+  int rf_c0 = 0, rf_c1 = 0, rf_lo = 0, rf_t1 = 0, rf_L = 0;
   if (S <= kRegPlanSeqs) {
     RegPlan R;
     R.build(a, seq_lens, hkv, S, W, lane);
     N = R.N;
     part = R.part;
     bad = R.bad;
+    // lane value x of sequence q (wave-uniform q < S): chunk q / 64, lane q % 64
+    auto at = [&](const int (&x)[kRegPlanChunks], int q) {
+      int v = 0;
+#pragma unroll
+      for (int k = 0; k < kRegPlanChunks; ++k)
+        if (64 * k < S && (q >> 6) == k) v = __builtin_amdgcn_readlane(x[k], q & 63);
+      return v;
+    };
     if (w < part.Ws) {
       // this worker's static positions and the sequence holding the first one (largest
       // s with C[s] <= pos: C is non-decreasing, so count the lanes at or below pos)
@@ -1249,6 +1291,23 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
       for (int k = 0; k < kRegPlanChunks; ++k)
         if (64 * k < S) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(64 * k + lane < S && R.C[k] <= pos));
       s0 = cnt - 1;
+      // pos lies in [C[s0], C[s0+1]): s0 is non-empty; its real tiles are the positions
+      // [C[s0] + cost, C[s0+1]); the first item is their part inside [pos, pend) if any
+      rf_c0 = at(R.C, s0);
+      const int n0 = at(R.n, s0);
+      rf_c1 = rf_c0 + (n0 > 0 ? n0 + kFusedCost : 0);
+      rf_lo = max(pos, rf_c0 + kFusedCost);
+      rf_t1 = min(pend, rf_c1);
+      rf_L = at(R.L, s0);
+      reg_first = rf_lo < rf_t1;
+    }
+    // empty (or invalid) sequences own no tile: their zero rows are spread over the workers
+    for (int q = w; q < S; q += W) {
+      if (at(R.n, q) == 0) {
+        const int b = q / a.hkv, g = q - b * a.hkv;
+        uint16_t* row = a.out + (int64_t(b) * a.hq + g * a.group) * kHeadDim;
+        for (int i = threadIdx.x; i < a.group * kHeadDim; i += kAttnThreads) row[i] = 0;
+      }
     }
     if (wave == 0) {
 #pragma unroll
@@ -1261,7 +1320,14 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
       }
       if (lane == 0) P.C[S] = N;
     }
-    __syncthreads();
+    // The other waves read this LDS copy only after the barrier the source takes on its
+    // second call (behind the first unit's loads), or right here if the first item is
+    // not served from registers.
+    lds_ready = false;
+    if (!reg_first) {
+      __syncthreads();
+      lds_ready = true;
+    }
   } else {
     // tile counts and their chunk-local exclusive prefix sums
     bad = 0;
@@ -1275,7 +1341,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
           L = 0;
         }
         n = tiles_of(L);
-        if (n > 0) n += a.item_cost;                 // positions: virtual tiles first
+        if (n > 0) n += kFusedCost;                  // positions: virtual tiles first
         P.L[s] = L;
       }
       const int x = wave_incl_scan(n);
@@ -1286,7 +1352,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
     N = add_chunk_offsets(P, P.C, S, nch, lane, wave);
     if (threadIdx.x == 0) P.C[S] = N;
     __syncthreads();
-    part = Partition::make(N, N, W, a.min_tiles, a.tail_den, a.tail_chunk);
+    part = Partition::make(N, N, W, kFusedMinTiles, kFusedTailDen, kFusedTailChunk);
     // partial-slot bases: exclusive prefix of (num_splits > 1 ? num_splits : 0)
     for (int ch = wave; ch < nch; ch += kWaves) {
       const int s = ch * 64 + lane;
@@ -1294,7 +1360,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
       if (s < S) {
         const int c0 = P.C[s], c1 = P.C[s + 1];
         if (c1 > c0) {
-          const int ns = part.owner(c1 - 1) - part.owner(c0 + a.item_cost) + 1;
+          const int ns = part.owner(c1 - 1) - part.owner(c0 + kFusedCost) + 1;
           v = ns > 1 ? ns : 0;
         }
       }
@@ -1312,18 +1378,27 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
     }
   }
   if (w == 0 && threadIdx.x == 0 && bad && a.err) report_error(a, HPA_DEVERR_SEQ_LEN);
-  // empty (or invalid) sequences own no tile: their zero rows are spread over the workers
-  for (int s = w; s < S; s += W) {
-    if (P.C[s + 1] == P.C[s]) {
-      const int b = s / a.hkv, g = s - b * a.hkv;
-      uint16_t* row = a.out + (int64_t(b) * a.hq + g * a.group) * kHeadDim;
-      for (int i = threadIdx.x; i < a.group * kHeadDim; i += kAttnThreads) row[i] = 0;
+  if (S > kRegPlanSeqs) {
+    // empty (or invalid) sequences own no tile: their zero rows are spread over the workers
+    for (int s = w; s < S; s += W) {
+      if (P.C[s + 1] == P.C[s]) {
+        const int b = s / a.hkv, g = s - b * a.hkv;
+        uint16_t* row = a.out + (int64_t(b) * a.hq + g * a.group) * kHeadDim;
+        for (int i = threadIdx.x; i < a.group * kHeadDim; i += kAttnThreads) row[i] = 0;
+      }
     }
   }
   if (w >= part.Wp) return;
   // workers without a static range go straight to the tail chunks
   FusedSource<INMERGE> src{a, P, part, S, w, pos, pend, __builtin_amdgcn_readfirstlane(s0)};
   src.pb_ready = S > kRegPlanSeqs;     // the register plan leaves the partial-slot bases for later
+  src.reg_first = reg_first;
+  src.rf_c0 = rf_c0;
+  src.rf_c1 = rf_c1;
+  src.rf_lo = rf_lo;
+  src.rf_t1 = rf_t1;
+  src.rf_L = rf_L;
+  (void)lds_ready;
   Worker<FP8, INMERGE> r(a, lds);
   r.trec = tr.rec;
   r.tq = TailQueue{a.qctr, lds.claim, part.D};
@@ -1339,7 +1414,8 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
 // schedule's partials combine with the same arithmetic in the same order.
 // Empty sequences get a zero row.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeDims = kHeadDim;
+constexpr int kMergeDims = kHeadDim;   // head dims per merge block (splitting them measured slower:
+                                       // the merge is bound by dispatch and round trips, not bytes)
 constexpr int kMergeQuads = kMergeDims / 4;
 constexpr int kMergeLanes = kMergeThreads / kMergeQuads;
 

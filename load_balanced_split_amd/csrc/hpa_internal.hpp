@@ -202,6 +202,12 @@ __device__ inline int owner_of_tile(int t, int Wp, int N, bool small) {
 }
 
 __device__ inline int range_begin(int w, int Wp, int N, bool small) {
+  // a power-of-two worker count (one worker per CU: 256 on MI355X) divides by a shift
+  if ((Wp & (Wp - 1)) == 0) {
+    const int sh = __builtin_ctz(static_cast<uint32_t>(Wp));
+    if (small) return static_cast<int>((static_cast<uint32_t>(w) * N) >> sh);
+    return static_cast<int>((int64_t(w) * N) >> sh);
+  }
   if (small) return static_cast<int>(static_cast<uint32_t>(w) * N / static_cast<uint32_t>(Wp));
   return static_cast<int>(int64_t(w) * N / Wp);
 }
