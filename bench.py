@@ -200,30 +200,43 @@ def item_phase_report(rec, item_tiles=None):
 
 
 def trace_main(args):
-    """Per-CU busy time of the attention kernel, balanced vs static split-KV."""
+    """Per-CU busy time of the attention kernel: the balanced schedules (planned in
+    every item order, with the merge kernel or merged in-kernel; fused; single
+    launch) against static split-KV. The traced launch reads a copy of the batch
+    that R - 1 other copies have been read after, so its KV comes from HBM."""
     os.environ["HPA_TRACE"] = "1"
     import torch
     from load_balanced_split_amd import _lib, inputs
     from load_balanced_split_amd.runner import DeviceStep
     _lib.lib()
     w = inputs.config_workload(args.workload)
-    d = DeviceStep(w, num_workers=args.num_workers)
-    W = d.num_workers
+    pool_bytes = w.k_cache.nbytes + w.v_cache.nbytes
+    R = min(16, max(2, math.ceil(2 * MALL_BYTES / max(pool_bytes, 1)) + 1))
+    copies = [DeviceStep(w, num_workers=args.num_workers) for _ in range(R)]
+    W = copies[0].num_workers
     out = {"metric": "attention tail balance (instrumented build)", "workload": inputs.CONFIG_NAMES[args.workload],
-           "num_workers": W, "realtime_clock_mhz": REALTIME_MHZ}
-    for sched in ("balanced", "fused", "single", "static_splits", "static_chunk"):
+           "num_workers": W, "realtime_clock_mhz": REALTIME_MHZ, "rotating_copies": R}
+    runs = [("balanced", 0), ("balanced", 1), ("balanced", 2), ("balanced_inmerge", 0), ("balanced_inmerge", 2),
+            ("fused", 0), ("single", 0), ("static_splits", 0), ("static_chunk", 0)]
+    for sched, order in runs:
+        one_launch = sched in ("single", "balanced_inmerge")
         reps = []
         for r in range(5):
-            d.step(sched)                     # planner (if any) and a full step first
+            for c in copies:                          # copy 0 (plan included), then every other copy
+                c.step(sched, item_order=order)
             torch.cuda.synchronize()
-            d.partial_ws.zero_()              # partials and the record area of the traced launch
+            d = copies[0]
+            d.partial_ws.zero_()                      # the per-wave record area after the partials
+            if one_launch:                            # partials NaN-filled for the in-kernel merges
+                S, G = w.batch * w.hkv, w.hq // w.hkv
+                d.partial_ws[: (5 * W + S) * G * (128 + 2) * 4].fill_(0xFF)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            d.attend(sched, flags=_lib.ATTN_NO_MERGE)
+            d.attend(sched, flags=0 if one_launch else _lib.ATTN_NO_MERGE)
             e1.record()
             torch.cuda.synchronize()
             ipw, tiles = None, None
-            pa = d.plan_arrays() if sched == "balanced" else None
+            pa = d.plan_arrays() if sched.startswith("balanced") else None
             if pa is not None and pa["D"] == 0:       # with a dynamic tail, items meet workers at run time
                 off = np.array(pa["worker_off"])
                 ipw = np.diff(off)
@@ -234,7 +247,9 @@ def trace_main(args):
             rep["items"] = item_phase_report(recs, tiles)
             rep["launch_event_us"] = round(e0.elapsed_time(e1) * 1e3, 2)
             reps.append(rep)
-        out[sched] = min(reps, key=lambda x: x["makespan_us"])
+        out[sched + (f"_order{order}" if order else "")] = min(reps, key=lambda x: x["makespan_us"])
+        print(f"[trace] {sched} order {order}: makespan {out[sched + (f'_order{order}' if order else '')]['makespan_us']}",
+              file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 

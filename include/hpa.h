@@ -172,16 +172,24 @@ hpa_status hpa_partial_workspace_size(const hpa_attn_desc* desc, int32_t num_wor
  * split ranks and slots follow the virtual workers (Ws static ranges, then the
  * chunks) in order, so results do not depend on who claims which chunk.
  * tail_den = 0: no tail (Ws = W', D = 0). tail_den >= 0, tail_chunk >= 1.
+ * Item order (same section: the scheduler prioritizes nearly-finished short
+ * requests): item_order 0 lists each worker's items in list order; 1 lists the
+ * sequences a worker holds whole (the short requests it finishes alone) first,
+ * then its pieces of split sequences; 2 the pieces first, then the whole ones
+ * (their partial results are complete sooner). Each class stays in list order;
+ * split ranks, partial slots and so the output bits are the same in every order.
  * The planner also returns the claim counters to zero.
  * seq_lens stays on the device (no host synchronisation). The plan workspace
  * must be zero-filled before its first use (it holds the sticky error word,
  * which hpa_plan never clears). */
 hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t num_workers,
                     int32_t min_tiles_per_worker, int32_t item_cost, int32_t tail_den,
-                    int32_t tail_chunk, void* plan_ws, size_t plan_ws_bytes, hipStream_t stream);
+                    int32_t tail_chunk, int32_t item_order, void* plan_ws, size_t plan_ws_bytes,
+                    hipStream_t stream);
 
 /* The item cost, minimum tiles per worker and dynamic tail the fused schedules
- * plan with; an hpa_plan call with these values gives their items exactly. */
+ * plan with; an hpa_plan call with these values (and item_order 0) gives their
+ * items exactly. */
 #define HPA_FUSED_ITEM_COST 4
 #define HPA_FUSED_MIN_TILES 12
 #define HPA_FUSED_TAIL_DEN 0
@@ -190,7 +198,10 @@ hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t 
 /* Flags of hpa_decode_attn. The default (0) runs both launches. */
 enum {
   HPA_ATTN_NO_MERGE = 1,    /* launch only the attention kernel (partials + unsplit rows) */
-  HPA_ATTN_MERGE_ONLY = 2   /* launch only the merge of an earlier HPA_ATTN_NO_MERGE call */
+  HPA_ATTN_MERGE_ONLY = 2,  /* launch only the merge of an earlier HPA_ATTN_NO_MERGE call */
+  HPA_ATTN_MERGE_IN_KERNEL = 4  /* HPA_SCHED_BALANCED only: the planned kernel merges split
+                                   sequences itself, as HPA_SCHED_BALANCED_SINGLE does (one
+                                   launch); not with the two flags above */
 };
 
 /* Decode attention over the paged cache (openai-hub.com "腾讯混元HPC-Ops升级：五大算子
@@ -295,8 +306,8 @@ hpa_status hpa_decode_prologue_plan(const hpa_attn_desc* desc, const void* q_in,
                                     const float* k_scale, const float* v_scale, void* q_out,
                                     int32_t* seq_lens_out, int32_t num_workers,
                                     int32_t min_tiles_per_worker, int32_t item_cost, int32_t tail_den,
-                                    int32_t tail_chunk, void* plan_ws, size_t plan_ws_bytes,
-                                    hipStream_t stream);
+                                    int32_t tail_chunk, int32_t item_order, void* plan_ws,
+                                    size_t plan_ws_bytes, hipStream_t stream);
 
 /* Synchronises the stream, then reads (and, if clear != 0, zeroes) the sticky
  * device error word of a plan workspace. */

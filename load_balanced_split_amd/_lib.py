@@ -33,7 +33,7 @@ HPA_SCHED_BALANCED, HPA_SCHED_STATIC_SPLITS, HPA_SCHED_STATIC_CHUNK, HPA_SCHED_B
 HPA_SCHED_BALANCED_SINGLE = 4
 SCHED = {"balanced": 0, "static_splits": 1, "static_chunk": 2, "fused": 3, "single": 4}
 DEVERR_SEQ_LEN, DEVERR_PAGE_ID, DEVERR_PROLOGUE, DEVERR_PLAN = 1, 2, 4, 8
-ATTN_NO_MERGE, ATTN_MERGE_ONLY = 1, 2
+ATTN_NO_MERGE, ATTN_MERGE_ONLY, ATTN_MERGE_IN_KERNEL = 1, 2, 4
 HEADER_SLOTS = dict(Wp=0, N=1, S=2, n_items=3, n_merge=4, n_partials=5, error=6, W=7, D=8, Ws=9)
 
 
@@ -91,7 +91,7 @@ def lib() -> ctypes.CDLL:
             "hpa_plan_workspace_size": [D, _I, ctypes.POINTER(ctypes.c_size_t)],
             "hpa_plan_workspace_layout": [D, _I, ctypes.POINTER(PlanLayout)],
             "hpa_partial_workspace_size": [D, _I, ctypes.POINTER(ctypes.c_size_t)],
-            "hpa_plan": [D, _P, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P],
+            "hpa_plan": [D, _P, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P],
             "hpa_decode_attn": [D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I, _P, ctypes.c_size_t,
                                 _P, ctypes.c_size_t, _P, _I, _P],
             "hpa_kv_pack_pages": [D, _P, _P, _P, _I, _P, _P, _P, _P],
@@ -99,7 +99,7 @@ def lib() -> ctypes.CDLL:
             "hpa_decode_prologue": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
                                     _P, _P, _P, _P, _P, _P, _P, _P],
             "hpa_decode_prologue_plan": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
-                                         _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P],
+                                         _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P],
             "hpa_read_device_error": [_P, ctypes.POINTER(ctypes.c_int32), _I, _P],
             "hpa_probe_stream_read": [_P, ctypes.c_size_t, _I, _P, _P],
             "hpa_router_pack_weights": [_P, _I, _I, _P, _P],
@@ -178,9 +178,9 @@ def hpa_partial_workspace_size(desc: AttnDesc, num_workers: int = 0) -> int:
 
 
 def hpa_plan(desc, seq_lens, num_workers, min_tiles_per_worker, item_cost, tail_den, tail_chunk, plan_ws,
-             stream=None):
+             stream=None, item_order=0):
     _check(lib().hpa_plan(ctypes.byref(desc), _ptr(seq_lens), num_workers, min_tiles_per_worker, item_cost,
-                          tail_den, tail_chunk, _ptr(plan_ws), plan_ws.numel() * plan_ws.element_size(),
+                          tail_den, tail_chunk, item_order, _ptr(plan_ws), plan_ws.numel() * plan_ws.element_size(),
                           _stream(stream)), "hpa_plan")
 
 
@@ -225,12 +225,14 @@ def hpa_decode_prologue(desc, q_in, k_in, v_in, q_norm_w, k_norm_w, eps, rope_th
 
 def hpa_decode_prologue_plan(desc, q_in, k_in, v_in, q_norm_w, k_norm_w, eps, rope_theta, positions,
                              page_table, k_cache, v_cache, k_scale, v_scale, q_out, seq_lens_out, num_workers,
-                             min_tiles_per_worker, item_cost, tail_den, tail_chunk, plan_ws, stream=None):
+                             min_tiles_per_worker, item_cost, tail_den, tail_chunk, plan_ws, stream=None,
+                             item_order=0):
     _check(lib().hpa_decode_prologue_plan(ctypes.byref(desc), _ptr(q_in), _ptr(k_in), _ptr(v_in),
                                           _ptr(q_norm_w), _ptr(k_norm_w), eps, rope_theta, _ptr(positions),
                                           _ptr(page_table), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                           _ptr(v_scale), _ptr(q_out), _ptr(seq_lens_out), num_workers,
-                                          min_tiles_per_worker, item_cost, tail_den, tail_chunk, _ptr(plan_ws),
+                                          min_tiles_per_worker, item_cost, tail_den, tail_chunk, item_order,
+                                          _ptr(plan_ws),
                                           plan_ws.numel() * plan_ws.element_size(), _stream(stream)),
            "hpa_decode_prologue_plan")
 

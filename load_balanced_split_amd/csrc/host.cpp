@@ -192,13 +192,14 @@ hpa_status hpa_partial_workspace_size(const hpa_attn_desc* desc, int32_t num_wor
 
 hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t num_workers,
                     int32_t min_tiles_per_worker, int32_t item_cost, int32_t tail_den, int32_t tail_chunk,
-                    void* plan_ws, size_t plan_ws_bytes, hipStream_t stream) {
+                    int32_t item_order, void* plan_ws, size_t plan_ws_bytes, hipStream_t stream) {
   hpa_status st = check_desc(desc);
   if (st != HPA_OK) return st;
   if (min_tiles_per_worker < 1) return fail(HPA_ERR_INVALID_ARG, "min_tiles_per_worker %d < 1", min_tiles_per_worker);
   if (item_cost < 0 || item_cost > 64) return fail(HPA_ERR_INVALID_ARG, "item_cost %d outside [0, 64]", item_cost);
   if (tail_den < 0) return fail(HPA_ERR_INVALID_ARG, "tail_den %d < 0", tail_den);
   if (tail_chunk < 1) return fail(HPA_ERR_INVALID_ARG, "tail_chunk %d < 1", tail_chunk);
+  if (item_order < 0 || item_order > 2) return fail(HPA_ERR_INVALID_ARG, "item_order %d outside [0, 2]", item_order);
   if (!plan_ws) return fail(HPA_ERR_INVALID_ARG, "plan_ws is NULL");
   if (desc->batch > 0 && !seq_lens) return fail(HPA_ERR_INVALID_ARG, "seq_lens is NULL");
   int32_t W = 0;
@@ -207,8 +208,8 @@ hpa_status hpa_plan(const hpa_attn_desc* desc, const int32_t* seq_lens, int32_t 
   if (plan_ws_bytes < size_t(o.total) * 4)
     return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)o.total * 4);
   if (hpa::launch_plan(seq_lens, desc->batch, desc->num_kv_heads, desc->max_pages_per_seq, W,
-                       min_tiles_per_worker, item_cost, tail_den, tail_chunk, static_cast<int32_t*>(plan_ws), o,
-                       stream) != hipSuccess)
+                       min_tiles_per_worker, item_cost, tail_den, tail_chunk, item_order,
+                       static_cast<int32_t*>(plan_ws), o, stream) != hipSuccess)
     return fail(HPA_ERR_LAUNCH, "planner launch failed");
   return HPA_OK;
 }
@@ -251,8 +252,12 @@ hpa_status decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const void* q
       sched != HPA_SCHED_BALANCED_FUSED && sched != HPA_SCHED_BALANCED_SINGLE)
     return fail(HPA_ERR_INVALID_ARG, "sched %d", static_cast<int>(sched));
 
-  if (flags & ~(HPA_ATTN_NO_MERGE | HPA_ATTN_MERGE_ONLY) || flags == (HPA_ATTN_NO_MERGE | HPA_ATTN_MERGE_ONLY))
+  if (flags & ~(HPA_ATTN_NO_MERGE | HPA_ATTN_MERGE_ONLY | HPA_ATTN_MERGE_IN_KERNEL) ||
+      (flags & (HPA_ATTN_NO_MERGE | HPA_ATTN_MERGE_ONLY)) == (HPA_ATTN_NO_MERGE | HPA_ATTN_MERGE_ONLY) ||
+      ((flags & HPA_ATTN_MERGE_IN_KERNEL) &&
+       (sched != HPA_SCHED_BALANCED || (flags & (HPA_ATTN_NO_MERGE | HPA_ATTN_MERGE_ONLY)))))
     return fail(HPA_ERR_INVALID_ARG, "flags %d", flags);
+  const bool in_kernel_merge = sched == HPA_SCHED_BALANCED_SINGLE || (flags & HPA_ATTN_MERGE_IN_KERNEL);
   if (desc->batch == 0) return HPA_OK;
   if (!q || !k_cache || !v_cache || !seq_lens || !page_table || !out || !partial_ws)
     return fail(HPA_ERR_INVALID_ARG, "a required pointer is NULL");
@@ -268,7 +273,7 @@ hpa_status decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const void* q
     return fail(HPA_ERR_WORKSPACE, "partial workspace %zu bytes < %lld", partial_ws_bytes, (long long)need);
   // the in-kernel merge addresses the partials through buffer resources with 32-bit
   // byte offsets
-  if (sched == HPA_SCHED_BALANCED_SINGLE && pl.l + hpa::max_slots(W, S) * G * 4 > int64_t(UINT32_MAX))
+  if (in_kernel_merge && pl.l + hpa::max_slots(W, S) * G * 4 > int64_t(UINT32_MAX))
     return fail(HPA_ERR_UNSUPPORTED, "single-launch schedule: partial workspace of %lld bytes needs 32-bit offsets",
                 (long long)pl.total_bytes);
   const hpa::PlanOffsets po = hpa::plan_offsets(S, W);
@@ -328,12 +333,17 @@ hpa_status decode_attn(const hpa_attn_desc* desc, hpa_sched sched, const void* q
     const bool via_plan = sched != HPA_SCHED_BALANCED && S > hpa::kFusedMaxSeqs;
     if (via_plan && (sched == HPA_SCHED_BALANCED_SINGLE || do_attn) &&
         hpa::launch_plan(seq_lens, desc->batch, desc->num_kv_heads, desc->max_pages_per_seq, W, a.min_tiles,
-                         a.item_cost, a.tail_den, a.tail_chunk, a.plan, po, stream) != hipSuccess)
+                         a.item_cost, a.tail_den, a.tail_chunk, 0, a.plan, po, stream) != hipSuccess)
       return fail(HPA_ERR_LAUNCH, "planner launch failed");
     if (sched == HPA_SCHED_BALANCED_SINGLE) {
       // one launch (two above kFusedMaxSeqs): plan, attend and merge (flags have no effect)
       if ((via_plan ? hpa::launch_attn_balanced(a, fp8, true, W, stream)
                     : hpa::launch_attn_fused(a, fp8, true, W, stream)) != hipSuccess)
+        return fail(HPA_ERR_LAUNCH, "attention launch failed");
+      return HPA_OK;
+    }
+    if (sched == HPA_SCHED_BALANCED && in_kernel_merge) {   // the plan from hpa_plan, merged in-kernel
+      if (hpa::launch_attn_balanced(a, fp8, true, W, stream) != hipSuccess)
         return fail(HPA_ERR_LAUNCH, "attention launch failed");
       return HPA_OK;
     }
@@ -392,13 +402,15 @@ hpa_status hpa_decode_prologue_plan(const hpa_attn_desc* desc, const void* q_in,
                                     void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
                                     void* q_out, int32_t* seq_lens_out, int32_t num_workers,
                                     int32_t min_tiles_per_worker, int32_t item_cost, int32_t tail_den,
-                                    int32_t tail_chunk, void* plan_ws, size_t plan_ws_bytes, hipStream_t stream) {
+                                    int32_t tail_chunk, int32_t item_order, void* plan_ws, size_t plan_ws_bytes,
+                                    hipStream_t stream) {
   hpa_status st = check_desc(desc);
   if (st != HPA_OK) return st;
   if (min_tiles_per_worker < 1) return fail(HPA_ERR_INVALID_ARG, "min_tiles_per_worker %d < 1", min_tiles_per_worker);
   if (item_cost < 0 || item_cost > 64) return fail(HPA_ERR_INVALID_ARG, "item_cost %d outside [0, 64]", item_cost);
   if (tail_den < 0) return fail(HPA_ERR_INVALID_ARG, "tail_den %d < 0", tail_den);
   if (tail_chunk < 1) return fail(HPA_ERR_INVALID_ARG, "tail_chunk %d < 1", tail_chunk);
+  if (item_order < 0 || item_order > 2) return fail(HPA_ERR_INVALID_ARG, "item_order %d outside [0, 2]", item_order);
   if (!plan_ws) return fail(HPA_ERR_INVALID_ARG, "plan_ws is NULL");
   if (desc->batch == 0) return HPA_OK;
   if (!q_in || !k_in || !v_in || !q_norm_w || !k_norm_w || !positions || !page_table || !k_cache || !v_cache ||
@@ -415,7 +427,7 @@ hpa_status hpa_decode_prologue_plan(const hpa_attn_desc* desc, const void* q_in,
   if (plan_ws_bytes < size_t(o.total) * 4)
     return fail(HPA_ERR_WORKSPACE, "plan workspace %zu bytes < %lld", plan_ws_bytes, (long long)o.total * 4);
   int32_t* ws = static_cast<int32_t*>(plan_ws);
-  const hpa::PlanArgs pa{ws, o, W, min_tiles_per_worker, item_cost, tail_den, tail_chunk};
+  const hpa::PlanArgs pa{ws, o, W, min_tiles_per_worker, item_cost, tail_den, tail_chunk, item_order};
   if (hpa::launch_prologue(*desc, static_cast<const uint16_t*>(q_in), static_cast<const uint16_t*>(k_in),
                            static_cast<const uint16_t*>(v_in), q_norm_w, k_norm_w, eps, rope_theta, positions,
                            page_table, static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), k_scale,

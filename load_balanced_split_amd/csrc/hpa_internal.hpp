@@ -278,7 +278,7 @@ __device__ inline int wave_incl_scan(int x) {
 
 // Launch wrappers (defined in the .hip files). Return hipSuccess or the launch error.
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_pages, int num_workers,
-                       int min_tiles, int item_cost, int tail_den, int tail_chunk, int32_t* plan,
+                       int min_tiles, int item_cost, int tail_den, int tail_chunk, int order, int32_t* plan,
                        const PlanOffsets& po, hipStream_t stream);
 hipError_t launch_attn_balanced(const AttnArgs& a, bool fp8, bool merge_in_kernel, int num_workers,
                                 hipStream_t stream);
@@ -294,7 +294,7 @@ constexpr int kRegPlanSeqs = 256;    // up to this many, every wave plans in reg
 struct PlanArgs {
   int32_t* ws;
   PlanOffsets po;
-  int workers, min_tiles, item_cost, tail_den, tail_chunk;
+  int workers, min_tiles, item_cost, tail_den, tail_chunk, order;
 };
 hipError_t launch_prologue(const hpa_attn_desc& d, const uint16_t* q_in, const uint16_t* k_in,
                            const uint16_t* v_in, const float* q_norm_w, const float* k_norm_w,

@@ -13,9 +13,9 @@ struct SeqLens {
 template <bool LDS>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ seq_lens, int B, int Hkv, int max_pages, int W, int min_tiles,
-    int cost, int tail_den, int tail_chunk, int32_t* __restrict__ ws, PlanOffsets po) {
+    int cost, int tail_den, int tail_chunk, int order, int32_t* __restrict__ ws, PlanOffsets po) {
   plan_block<kPlanThreads, LDS>(SeqLens{seq_lens}, B, Hkv, max_pages, W, min_tiles, cost, tail_den, tail_chunk,
-                                ws, po);
+                                order, ws, po);
 }
 
 __global__ void clear_word_kernel(int32_t* w) { *w = 0; }
@@ -23,14 +23,14 @@ __global__ void clear_word_kernel(int32_t* w) { *w = 0; }
 }  // namespace
 
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int hkv, int max_pages, int num_workers,
-                       int min_tiles, int item_cost, int tail_den, int tail_chunk, int32_t* plan,
+                       int min_tiles, int item_cost, int tail_den, int tail_chunk, int order, int32_t* plan,
                        const PlanOffsets& po, hipStream_t stream) {
   if (int64_t(batch) * hkv <= kPlanLdsSeqs)
     hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch, hkv,
-                       max_pages, num_workers, min_tiles, item_cost, tail_den, tail_chunk, plan, po);
+                       max_pages, num_workers, min_tiles, item_cost, tail_den, tail_chunk, order, plan, po);
   else
     hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch, hkv,
-                       max_pages, num_workers, min_tiles, item_cost, tail_den, tail_chunk, plan, po);
+                       max_pages, num_workers, min_tiles, item_cost, tail_den, tail_chunk, order, plan, po);
   return hipGetLastError();
 }
 

@@ -73,7 +73,7 @@ __device__ inline int seq_of_pos(const int32_t* C, const int32_t* NE, int c, int
 // append); everything else as in hpa_plan.
 template <int NT, bool LDS, class Lens>
 __device__ void plan_block(const Lens& lens, int B, int Hkv, int max_pages, int W, int min_tiles, int cost,
-                           int tail_den, int tail_chunk, int32_t* __restrict__ ws, const PlanOffsets& po) {
+                           int tail_den, int tail_chunk, int order, int32_t* __restrict__ ws, const PlanOffsets& po) {
   __shared__ int2 tmp[NT / 64 + 1];
   __shared__ int sh_bad;
   __shared__ int sC[LDS ? kPlanLdsSeqs + 1 : 1];
@@ -166,7 +166,9 @@ __device__ void plan_block(const Lens& lens, int B, int Hkv, int max_pages, int 
   if (tid == 0) woff[V] = carry_i;
   __syncthreads();
 
-  // 4. emit items, worker by worker, in sequence order
+  // 4. emit items, worker by worker, in sequence order -- or (order 1 / 2) in two passes:
+  // the sequences a worker holds whole, then the pieces of split ones (1), or the
+  // reverse (2); each pass in sequence order. Ranks and slots do not depend on it.
   int32_t* is = ws + po.item_s;
   int32_t* it0 = ws + po.item_t0;
   int32_t* it1 = ws + po.item_t1;
@@ -174,20 +176,24 @@ __device__ void plan_block(const Lens& lens, int B, int Hkv, int max_pages, int 
   int32_t* isl = ws + po.item_slot;
   for (int w = tid; w < V; w += NT) {
     const int a = part.begin(w), e = part.begin(w + 1);
-    int s = seq_of_pos(C, NE, cost, S, a);
+    const int s_first = seq_of_pos(C, NE, cost, S, a);
     int pos = V <= NT ? my_off : woff[w];
-    for (; s < S && P(s) < e; ++s) {
-      if (C[s + 1] == C[s]) continue;
-      const int r0 = P(s) + cost, r1 = P(s + 1);      // the real tiles of s
-      const int lo = max(a, r0), hi = min(e, r1);
-      if (lo >= hi) continue;
-      const int split = w - part.owner(r0);
-      is[pos] = s;
-      it0[pos] = lo - r0;
-      it1[pos] = hi - r0;
-      isp[pos] = split;
-      isl[pos] = num_splits[s] > 1 ? pbase[s] + split : -1;
-      ++pos;
+    for (int pass = 0; pass < (order ? 2 : 1); ++pass) {
+      const bool want_whole = (order == 1) == (pass == 0);
+      for (int s = s_first; s < S && P(s) < e; ++s) {
+        if (C[s + 1] == C[s]) continue;
+        if (order && (num_splits[s] == 1) != want_whole) continue;
+        const int r0 = P(s) + cost, r1 = P(s + 1);      // the real tiles of s
+        const int lo = max(a, r0), hi = min(e, r1);
+        if (lo >= hi) continue;
+        const int split = w - part.owner(r0);
+        is[pos] = s;
+        it0[pos] = lo - r0;
+        it1[pos] = hi - r0;
+        isp[pos] = split;
+        isl[pos] = num_splits[s] > 1 ? pbase[s] + split : -1;
+        ++pos;
+      }
     }
   }
   if (LDS) {

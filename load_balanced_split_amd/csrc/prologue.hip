@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kProThreads) void prologue_kernel(
     if (blockIdx.x == 0) {
       plan_block<kProThreads, true>(LensAfterAppend{positions, page_table, seq_lens_out, max_pages, num_pages},
                                     static_cast<int>(gridDim.x) - 1, hkv, max_pages, pa.workers, pa.min_tiles,
-                                    pa.item_cost, pa.tail_den, pa.tail_chunk, pa.ws, pa.po);
+                                    pa.item_cost, pa.tail_den, pa.tail_chunk, pa.order, pa.ws, pa.po);
       return;
     }
   }
@@ -213,7 +213,7 @@ hipError_t launch_prologue(const hpa_attn_desc& d, const uint16_t* q_in, const u
   if (e != hipSuccess || !plan) return e;
   // batches too large for the planner's LDS arrays: plan after the appends instead
   return launch_plan(seq_lens_out, d.batch, d.num_kv_heads, d.max_pages_per_seq, plan->workers, plan->min_tiles,
-                     plan->item_cost, plan->tail_den, plan->tail_chunk, plan->ws, plan->po, stream);
+                     plan->item_cost, plan->tail_den, plan->tail_chunk, plan->order, plan->ws, plan->po, stream);
 }
 
 }  // namespace hpa

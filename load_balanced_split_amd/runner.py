@@ -64,7 +64,8 @@ class DeviceStep:
                                  self.plan_ws, stream)
 
     def prologue_plan(self, min_tiles: int = _lib.FUSED_MIN_TILES, item_cost: int = _lib.FUSED_ITEM_COST,
-                      tail_den: int = _lib.FUSED_TAIL_DEN, tail_chunk: int = _lib.FUSED_TAIL_CHUNK, stream=None):
+                      tail_den: int = _lib.FUSED_TAIL_DEN, tail_chunk: int = _lib.FUSED_TAIL_CHUNK, stream=None,
+                      item_order: int = 0):
         """The prologue and the planner in one launch (the plan hpa_plan would make over
         the lengths after the append)."""
         w = self.w
@@ -72,7 +73,7 @@ class DeviceStep:
                                       self.k_norm_w, w.eps, w.rope_theta, self.seq_lens, self.page_table,
                                       self.k_cache, self.v_cache, self.k_scale, self.v_scale, self.q_rot,
                                       self.lens_after, self.num_workers, min_tiles, item_cost, tail_den,
-                                      tail_chunk, self.plan_ws, stream)
+                                      tail_chunk, self.plan_ws, stream, item_order)
 
     def attn_inputs(self):
         if self.w.has_prologue:
@@ -80,32 +81,39 @@ class DeviceStep:
         return self.q, self.seq_lens
 
     def plan(self, min_tiles: int = _lib.FUSED_MIN_TILES, item_cost: int = _lib.FUSED_ITEM_COST,
-             tail_den: int = _lib.FUSED_TAIL_DEN, tail_chunk: int = _lib.FUSED_TAIL_CHUNK, stream=None):
+             tail_den: int = _lib.FUSED_TAIL_DEN, tail_chunk: int = _lib.FUSED_TAIL_CHUNK, stream=None,
+             item_order: int = 0):
         _, lens = self.attn_inputs()
         _lib.hpa_plan(self.desc, lens, self.num_workers, min_tiles, item_cost, tail_den, tail_chunk,
-                      self.plan_ws, stream)
+                      self.plan_ws, stream, item_order)
 
     def attend(self, sched: str = "balanced", stream=None, flags: int = 0):
+        """sched: a schedule name of _lib.SCHED, or "balanced_inmerge" (the planned
+        schedule with HPA_ATTN_MERGE_IN_KERNEL: one launch over the plan)."""
         q, lens = self.attn_inputs()
         W = self.static_workers if sched.startswith("static") else self.num_workers
         self.last_workers = W
+        if sched == "balanced_inmerge":
+            sched, flags = "balanced", flags | _lib.ATTN_MERGE_IN_KERNEL
         _lib.hpa_decode_attn(self.desc, sched, q, self.k_cache, self.v_cache, self.k_scale, self.v_scale,
                              lens, self.page_table, W, self.plan_ws, self.partial_ws,
                              self.out, flags, stream)
 
     def step(self, sched: str = "balanced", min_tiles: int = _lib.FUSED_MIN_TILES,
              item_cost: int = _lib.FUSED_ITEM_COST, tail_den: int = _lib.FUSED_TAIL_DEN,
-             tail_chunk: int = _lib.FUSED_TAIL_CHUNK, stream=None, prologue_plans: bool = True):
+             tail_chunk: int = _lib.FUSED_TAIL_CHUNK, stream=None, prologue_plans: bool = True,
+             item_order: int = 0):
         """The whole hot path of one decode step; returns the bf16 output tensor. With a
-        prologue, the planned schedule plans inside the prologue launch unless
+        prologue, the planned schedules plan inside the prologue launch unless
         prologue_plans is False (then: prologue launch, planner launch)."""
-        if self.w.has_prologue and sched == "balanced" and prologue_plans:
-            self.prologue_plan(min_tiles, item_cost, tail_den, tail_chunk, stream)
+        planned = sched in ("balanced", "balanced_inmerge")
+        if self.w.has_prologue and planned and prologue_plans:
+            self.prologue_plan(min_tiles, item_cost, tail_den, tail_chunk, stream, item_order)
         else:
             if self.w.has_prologue:
                 self.prologue(stream)
-            if sched == "balanced":
-                self.plan(min_tiles, item_cost, tail_den, tail_chunk, stream)
+            if planned:
+                self.plan(min_tiles, item_cost, tail_den, tail_chunk, stream, item_order)
         self.attend(sched, stream)
         return self.out
 

@@ -52,6 +52,19 @@ worker v < W_s owns [v*A // W_s, (v+1)*A // W_s), virtual worker W_s + c owns
 virtual workers in order, so the result does not depend on which worker claims
 which chunk. tail_den 0 is the plan without a tail (then W_s = W').
 
+Item order within a worker (bitbyai.com, same section: the scheduler
+prioritizes nearly-finished short requests while spreading longer ones evenly
+over the grid). The partition above already spreads long sequences evenly;
+what is left to choose is the order in which a worker runs the items it holds.
+item_order 0 runs them in list (position) order. item_order 1 runs first the
+sequences it holds whole -- the short requests, finished by this worker alone,
+which write their output directly -- and then the pieces of sequences shared
+with other workers. item_order 2 is the reverse choice: the shared pieces
+first, so that the partial results of split sequences are complete sooner.
+Both keep list order inside each of the two classes. An item's split rank is
+its rank in list order, so the order never changes a split rank, a partial
+slot or the combine order: the output is the same bits in every order.
+
 Static split-KV (the comparison the pages describe in the same section):
 flavour "splits" fixes the number of splits per sequence,
 S_split = clamp(ceil(W / S), 1, max_pages), chunk_s = ceil(n_s / S_split);
@@ -78,7 +91,7 @@ def active_workers(N, num_workers, min_tiles):
     return min(num_workers, max(1, N // min_tiles))
 
 
-def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1, item_cost=0, tail_den=0, tail_chunk=1):
+def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1, item_cost=0, tail_den=0, tail_chunk=1, item_order=0):
     n = tile_counts(seq_lens, hkv)
     S = len(n)
     C = [0] * (S + 1)
@@ -129,6 +142,19 @@ def balanced_plan(seq_lens, hkv, num_workers, min_tiles=1, item_cost=0, tail_den
             acc += num_splits[s]
     slots = [partial_base[s] + k if num_splits[s] > 1 else -1
              for (_, s, _, _), k in zip(items, split)]
+    if item_order:
+        # within each virtual worker: a stable partition into the items of sequences it
+        # holds whole (unsplit) and the pieces of split sequences; order 1 runs the whole
+        # ones first, order 2 the pieces first; ranks and slots travel with their items
+        order = []
+        for w in range(V):
+            idx = list(range(worker_off[w], worker_off[w + 1]))
+            whole = [i for i in idx if num_splits[items[i][1]] == 1]
+            piece = [i for i in idx if num_splits[items[i][1]] != 1]
+            order += whole + piece if item_order == 1 else piece + whole
+        items = [items[i] for i in order]
+        split = [split[i] for i in order]
+        slots = [slots[i] for i in order]
     return dict(
         C=C, N=N, Np=Np, S=S, Wp=Wp, Ws=Ws, D=D, V=V, n_items=len(items), worker_off=worker_off,
         item_s=[it[1] for it in items], item_t0=[it[2] for it in items],

@@ -62,21 +62,22 @@ def test_workspace_sizes_and_layout(L):
 def test_calls_reject_bad_arguments_before_launching(L):
     d = _desc()
     with pytest.raises(_lib.HpaError) as e:
-        L_status = L.hpa_plan(ctypes.byref(d), None, 512, 1, 0, 0, 1, None, 0, None)
+        L_status = L.hpa_plan(ctypes.byref(d), None, 512, 1, 0, 0, 1, 0, None, 0, None)
         _lib._check(L_status, "hpa_plan")
     assert e.value.status == 1
     # undersized plan workspace -> HPA_ERR_WORKSPACE, nothing launched
     fake = ctypes.c_void_p(0x1000)
-    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, 0, 1, fake, 16, None) == 3
-    assert L.hpa_plan(ctypes.byref(d), fake, 512, 0, 0, 0, 1, fake, 1 << 30, None) == 1     # min_tiles < 1
-    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, -1, 0, 1, fake, 1 << 30, None) == 1    # item cost < 0
-    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 65, 0, 1, fake, 1 << 30, None) == 1    # item cost > 64
-    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, -1, 1, fake, 1 << 30, None) == 1    # tail_den < 0
-    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, 8, 0, fake, 1 << 30, None) == 1     # tail_chunk < 1
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, 0, 1, 0, fake, 16, None) == 3
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 0, 0, 0, 1, 0, fake, 1 << 30, None) == 1     # min_tiles < 1
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, -1, 0, 1, 0, fake, 1 << 30, None) == 1    # item cost < 0
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 65, 0, 1, 0, fake, 1 << 30, None) == 1    # item cost > 64
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, -1, 1, 0, fake, 1 << 30, None) == 1    # tail_den < 0
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, 8, 0, 0, fake, 1 << 30, None) == 1     # tail_chunk < 1
+    assert L.hpa_plan(ctypes.byref(d), fake, 512, 1, 0, 0, 1, 3, fake, 1 << 30, None) == 1     # item_order > 2
     # sizes beyond the 32-bit plan offsets: more than 2^20 workers, 2^24 sequences
     n = ctypes.c_size_t(0)
     assert L.hpa_plan_workspace_size(ctypes.byref(d), (1 << 20) + 1, ctypes.byref(n)) == 1
-    assert L.hpa_plan(ctypes.byref(d), fake, (1 << 20) + 1, 1, 0, 0, 1, fake, 1 << 30, None) == 1
+    assert L.hpa_plan(ctypes.byref(d), fake, (1 << 20) + 1, 1, 0, 0, 1, 0, fake, 1 << 30, None) == 1
     big = _desc(batch=1 << 22, num_q_heads=8, num_kv_heads=8)
     assert L.hpa_plan_workspace_size(ctypes.byref(big), 512, ctypes.byref(n)) == 1
     # balanced attention without a plan, fp8 without scales
@@ -88,8 +89,11 @@ def test_calls_reject_bad_arguments_before_launching(L):
     # partial workspace too small
     assert L.hpa_decode_attn(ctypes.byref(d), 1, fake, fake, fake, None, None, fake, fake, 512, None, 0,
                              fake, 100, fake, 0, None) == 3
-    # unknown flags, or both halves switched off
-    for bad in (3, 4, -1):
+    # unknown flags, both halves switched off, the in-kernel merge flag off the planned schedule
+    # or with a half switched off
+    assert L.hpa_decode_attn(ctypes.byref(d), 0, fake, fake, fake, None, None, fake, fake, 512, fake, 1 << 30,
+                             fake, 1 << 30, fake, 5, None) == 1
+    for bad in (3, 4, 8, -1):
         assert L.hpa_decode_attn(ctypes.byref(d), 1, fake, fake, fake, None, None, fake, fake, 512, None, 0,
                                  fake, 1 << 30, fake, bad, None) == 1
     # prologue: aliasing positions / seq_lens_out is refused
@@ -99,7 +103,7 @@ def test_calls_reject_bad_arguments_before_launching(L):
     P = [fake] * 5
     pro = lambda desc, W, mt, cost, den, ch, ws, nbytes: L.hpa_decode_prologue_plan(
         ctypes.byref(desc), *P, 1e-6, 1e6, fake, fake, fake, fake, None, None, fake,
-        ctypes.c_void_p(0x2000), W, mt, cost, den, ch, ws, nbytes, None)
+        ctypes.c_void_p(0x2000), W, mt, cost, den, ch, 0, ws, nbytes, None)
     assert pro(d, 512, 1, 4, 0, 1, None, 0) == 1                       # no plan workspace
     assert pro(d, 512, 1, 4, 0, 1, fake, 16) == 3                      # workspace too small
     assert pro(d, 512, 0, 4, 0, 1, fake, 1 << 30) == 1                 # min_tiles < 1
@@ -107,7 +111,7 @@ def test_calls_reject_bad_arguments_before_launching(L):
     assert pro(d, 512, 1, 4, 1, 0, fake, 1 << 30) == 1                 # tail_chunk < 1
     assert pro(d8, 512, 1, 4, 0, 1, fake, 1 << 30) == 1                # E4M3 without scales
     assert L.hpa_decode_prologue_plan(ctypes.byref(d), *P, 1e-6, 1e6, fake, fake, fake, fake, None, None, fake,
-                                      fake, 512, 1, 4, 0, 1, fake, 1 << 30, None) == 1   # positions = seq_lens_out
+                                      fake, 512, 1, 4, 0, 1, 0, fake, 1 << 30, None) == 1   # positions = seq_lens_out
     # default worker count: an unknown schedule or a NULL output is refused before any device query
     n = ctypes.c_int32(0)
     assert L.hpa_default_num_workers(0, 7, ctypes.byref(n)) == 1

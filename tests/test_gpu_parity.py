@@ -33,7 +33,7 @@ def gpu():
     return torch.device("cuda")
 
 
-def device_plan(lens, hkv, W, min_tiles, item_cost=0, tail_den=0, tail_chunk=1):
+def device_plan(lens, hkv, W, min_tiles, item_cost=0, tail_den=0, tail_chunk=1, item_order=0):
     """Run the GPU planner on a length vector; return its arrays as host lists."""
     B = len(lens)
     maxp = max(1, max([(int(L) + 63) // 64 for L in lens] or [1]))
@@ -41,7 +41,7 @@ def device_plan(lens, hkv, W, min_tiles, item_cost=0, tail_den=0, tail_chunk=1):
     size = _lib.hpa_plan_workspace_size(desc, W)
     ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
     sl = torch.tensor(np.asarray(lens, np.int32), device="cuda")
-    _lib.hpa_plan(desc, sl, W, min_tiles, item_cost, tail_den, tail_chunk, ws)
+    _lib.hpa_plan(desc, sl, W, min_tiles, item_cost, tail_den, tail_chunk, ws, item_order=item_order)
     torch.cuda.synchronize()
     lay = _lib.hpa_plan_workspace_layout(desc, W)
     h = ws.cpu().numpy().view(np.int32)
@@ -56,12 +56,12 @@ def device_plan(lens, hkv, W, min_tiles, item_cost=0, tail_den=0, tail_chunk=1):
                 partial_base=g("partial_base", S), merge_list=g("merge_list", nm))
 
 
-def check_plan(lens, hkv, W, mt, cost=0, den=0, chunk=1):
-    got = device_plan(lens, hkv, W, mt, cost, den, chunk)
-    want = op.balanced_plan(lens, hkv, W, mt, cost, den, chunk)
+def check_plan(lens, hkv, W, mt, cost=0, den=0, chunk=1, order=0):
+    got = device_plan(lens, hkv, W, mt, cost, den, chunk, order)
+    want = op.balanced_plan(lens, hkv, W, mt, cost, den, chunk, order)
     assert got["err"] == 0
     for k in ("Wp", "Ws", "D", "N", "n_items", "n_partials") + PLAN_KEYS:
-        assert got[k] == want[k], (k, lens, hkv, W, mt, cost, den, chunk)
+        assert got[k] == want[k], (k, lens, hkv, W, mt, cost, den, chunk, order)
 
 
 # ---------------------------------------------------------------- planner ---
@@ -76,7 +76,8 @@ def test_plan_bit_exact_workload_lengths(cfg, W, mt, cost, tail):
     if W == 0:
         W = _lib.hpa_default_num_workers(0)
     print(f"plan cfg{cfg} W={W} mt={mt} cost={cost} tail={tail}", flush=True)
-    check_plan(lens.tolist(), hkv, W, mt, cost, *tail)
+    for order in (0, 1, 2):
+        check_plan(lens.tolist(), hkv, W, mt, cost, *tail, order)
 
 
 def test_plan_bit_exact_random_lengths():
@@ -93,7 +94,7 @@ def test_plan_bit_exact_random_lengths():
         cost = int(rng.integers(0, 6)) if trial % 2 else 0
         den = int(rng.integers(1, 17)) if trial % 3 else 0
         chunk = int(rng.integers(1, 40))
-        check_plan(lens.tolist(), hkv, W, mt, cost, den, chunk)
+        check_plan(lens.tolist(), hkv, W, mt, cost, den, chunk, trial % 3)
     check_plan([0, 0, 0], 2, 16, 1)              # N == 0: no active workers
     check_plan([0, 0, 0], 2, 16, 1, 4)
     check_plan([5000], 1, 100000 // 64, 1)       # W > N tiles
@@ -622,3 +623,27 @@ def test_fused_and_single_schedules_above_the_lds_plan_limit():
         torch.cuda.synchronize()
         assert d.device_error(clear=True) & _lib.DEVERR_SEQ_LEN, sched
         assert not bool(d.out[3].float().abs().sum()), sched        # a bad length gives a zero row
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_item_orders_and_in_kernel_merge_give_the_same_bits(cfg):
+    """Every item order, with the merge kernel or merged inside the planned kernel
+    (HPA_ATTN_MERGE_IN_KERNEL), gives the list-order planned schedule's bits (the
+    E4M3 workload plans inside the prologue launch; its append is idempotent); the
+    partial workspace is NaN-filled before every step."""
+    from load_balanced_split_amd.runner import DeviceStep
+    w = inputs.config_workload(cfg)
+    d = DeviceStep(w)
+    d.step("balanced")
+    torch.cuda.synchronize()
+    want = d.out.clone()
+    assert_within(d.output_f64(), oracle_out(w), w.kv_dtype, f"cfg{cfg}")
+    for order in (0, 1, 2):
+        for sched in ("balanced", "balanced_inmerge"):
+            print(f"cfg{cfg} order {order} {sched}", flush=True)
+            d.out.zero_()
+            scrub_partials(d)
+            d.step(sched, item_order=order)
+            torch.cuda.synchronize()
+            assert d.device_error() == 0
+            assert torch.equal(d.out, want), (order, sched)

@@ -335,3 +335,45 @@ def test_static_partitions_hand_worked():
         p = op.static_partition(g["seq_lens"], g["hkv"], g["num_workers"], g["max_pages"], flavour)
         assert p["S_split"] == g["S_split"]
         assert [list(it) for it in p["items"]] == g[flavour], flavour
+
+
+def test_hand_worked_item_orders():
+    """Item orders on a hand-worked case: ranks and slots travel with their items."""
+    g = json.load(open(os.path.join(GOLDEN, "plan_item_order.json")))
+    for case in g["cases"]:
+        p = op.balanced_plan(case["seq_lens"], case["hkv"], case["num_workers"], case["min_tiles"],
+                             case["item_cost"], 0, 1, case["item_order"])
+        for key in ("worker_off", "item_s", "item_t0", "item_t1", "item_split", "item_slot", "num_splits",
+                    "partial_base"):
+            assert p[key] == case[key], (case["item_order"], key)
+
+
+def test_item_orders_permute_only_within_workers():
+    """Any order holds the same (worker, item) set as list order, each worker's items
+    split into whole sequences and shared pieces in the stated order, each class in
+    sequence order, with unchanged ranks and slots."""
+    rng = np.random.default_rng(7)
+    for trial in range(300):
+        B = int(rng.integers(0, 40))
+        hkv = int(rng.integers(1, 4))
+        lens = rng.integers(0, 4000, size=B)
+        lens[rng.random(B) < 0.2] = 0
+        W = int(rng.integers(1, 200))
+        mt, c = int(rng.integers(1, 5)), int(rng.integers(0, 6))
+        den = int(rng.integers(0, 5)) if trial % 2 else 0
+        ch = int(rng.integers(1, 9))
+        base = op.balanced_plan(lens, hkv, W, mt, c, den, ch, 0)
+        for order in (1, 2):
+            p = op.balanced_plan(lens, hkv, W, mt, c, den, ch, order)
+            assert p["worker_off"] == base["worker_off"] and p["n_items"] == base["n_items"]
+            for w in range(p["V"]):
+                lo, hi = p["worker_off"][w], p["worker_off"][w + 1]
+                got = list(zip(*(p[k][lo:hi] for k in ("item_s", "item_t0", "item_t1", "item_split", "item_slot"))))
+                want = list(zip(*(base[k][lo:hi] for k in ("item_s", "item_t0", "item_t1", "item_split", "item_slot"))))
+                assert sorted(got) == sorted(want)
+                split = [p["num_splits"][it[0]] > 1 for it in got]
+                first = [not x for x in split] if order == 1 else split
+                assert first == sorted(first, reverse=True)          # one class, then the other
+                for cls in (True, False):
+                    ss = [it[0] for it, x in zip(got, split) if x == cls]
+                    assert ss == sorted(ss)
