@@ -660,7 +660,7 @@ def traffic_per_launch(sched, kv_dtype, workload, products="mfma"):
     if products != "mfma":
         return None
     fp8 = "false" if kv_dtype == "bf16" else "true"
-    key = f"attn_fused_kernel<{fp8},false>" if sched == "fused" else f"attn_balanced_kernel<{fp8}>"
+    key = f"attn_fused_kernel<{fp8},false>" if sched == "fused" else f"attn_balanced_kernel<{fp8},false>"
     path = os.path.join(ROOT, "profiles", f"attn_hbm_traffic_{WORKLOAD_KEYS[workload]}.txt")
     t = read_traffic(path, key)
     return None if t is None else int(round(t))

@@ -32,16 +32,17 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CALIBRATION_BYTES = 1 << 30          # bench.py --pmc-run copies this many bytes
 
 
-# sources of kernels that no attention-path launch runs (the router GEMM, the read
-# probe): a change there leaves the attention path's counter readings valid
-_NOT_ATTENTION = {"router.hip", "router_internal.hpp", "router_host.cpp", "probe.hip"}
+# sources of kernels that no attention-path launch runs (the router GEMM, the MoE
+# pipeline, the read probe, the page packer, the allocation-free wrapper): a change
+# there leaves the attention path's counter readings valid
+_NOT_ATTENTION = ("router", "moe", "probe", "pack", "noalloc")
 
 
 def source_hash() -> str:
     """Hash of the sources the attention path's kernels and launches are built from."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
-        if os.path.basename(f) not in _NOT_ATTENTION:
+        if not os.path.basename(f).startswith(_NOT_ATTENTION):
             h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
@@ -188,11 +189,10 @@ def balance(title, command, files):
         if data is None:
             raise SystemExit(f"{f}: no JSON line")
         lines.append(f"## {data['workload']} (W = {data['num_workers']})")
-        lines.append(f"{'schedule':16s}" + "".join(f"{h:>11s}" for _, h in cols))
-        for sched in ("balanced", "fused", "single", "static_splits", "static_chunk"):
-            r = data.get(sched)
-            if r:
-                lines.append(f"{sched:16s}" + "".join(f"{r.get(k, float('nan')):>11}" for k, _ in cols))
+        lines.append(f"{'schedule':24s}" + "".join(f"{h:>11s}" for _, h in cols))
+        for sched, r in data.items():
+            if isinstance(r, dict) and "makespan_us" in r:
+                lines.append(f"{sched:24s}" + "".join(f"{r.get(k, float('nan')):>11}" for k, _ in cols))
         xcd = data.get("fused", {}).get("worker_end_mean_by_xcd_us")
         if xcd:
             lines.append("fused: mean worker end by XCD (us): " + ", ".join(f"{k}: {v}" for k, v in xcd.items()))
