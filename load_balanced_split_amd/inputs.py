@@ -343,3 +343,62 @@ def router_workload(tokens: int, experts: int, hidden: int, seed: int = 0, name:
     x = bf16_bits(rng.standard_normal((tokens, hidden), dtype=np.float32))
     w = (rng.standard_normal((experts, hidden), dtype=np.float32) / np.float32(math.sqrt(hidden))).astype(np.float32)
     return RouterWorkload(name=name, tokens=tokens, experts=experts, hidden=hidden, x=x, w=w)
+
+
+# ------------------------------------------------------------------- MoE ---
+
+@dataclasses.dataclass
+class MoeWorkload:
+    """Inputs of the fused FP8 MoE layer: hidden states x (bf16 bits, [T, H]), the
+    routing (expert ids [T, K] int32, weights [T, K] fp32), the expert weights as OCP
+    E4M3 codes with one fp32 scale per output channel: W1 [E, 2I, H] (gate rows, then
+    up rows) with s1 [E, 2I], W2 [E, H, I] with s2 [E, H]."""
+    name: str
+    tokens: int
+    experts: int
+    top_k: int
+    hidden: int
+    inter: int
+    x: np.ndarray
+    ids: np.ndarray
+    weights: np.ndarray
+    w1: np.ndarray
+    s1: np.ndarray
+    w2: np.ndarray
+    s2: np.ndarray
+
+    def weight_bytes_read(self) -> int:
+        """Bytes of W1 and W2 codes of the experts some token is routed to."""
+        used = np.unique(self.ids[(self.ids >= 0) & (self.ids < self.experts)])
+        return int(len(used)) * 3 * self.inter * self.hidden
+
+
+def _per_row_fp8(rng, rows, cols, std):
+    """N(0, std^2) float32 rows -> (E4M3 codes, fp32 scale amax / 448 per row)."""
+    f = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(std)
+    s = (np.abs(f).max(axis=1) / np.float32(E4M3_MAX)).astype(np.float32)
+    return e4m3_codes(f / s[:, None]), s
+
+
+def moe_workload(tokens: int, experts: int, top_k: int, hidden: int, inter: int, seed: int = 0,
+                 name: str = "moe") -> MoeWorkload:
+    """x ~ N(0, 1) -> bf16; routing: per token the top_k of E N(0, 1) logits (distinct
+    experts, largest first) with softmax weights over those k; W1 ~ N(0, 1/H), W2 ~ N(0, 1/I),
+    each row quantised to E4M3 with scale amax / 448 (PyTorch's casts). Draw order, one
+    default_rng(seed): x, logits, then W1 and W2 expert by expert."""
+    rng = np.random.default_rng(seed)
+    x = bf16_bits(rng.standard_normal((tokens, hidden), dtype=np.float32))
+    logits = rng.standard_normal((tokens, experts), dtype=np.float32)
+    ids = np.argsort(-logits, axis=1, kind="stable")[:, :top_k].astype(np.int32)
+    top = np.take_along_axis(logits, ids, axis=1).astype(np.float64)
+    ew = np.exp(top - top.max(axis=1, keepdims=True))
+    weights = (ew / ew.sum(axis=1, keepdims=True)).astype(np.float32)
+    w1 = np.empty((experts, 2 * inter, hidden), np.uint8)
+    s1 = np.empty((experts, 2 * inter), np.float32)
+    w2 = np.empty((experts, hidden, inter), np.uint8)
+    s2 = np.empty((experts, hidden), np.float32)
+    for e in range(experts):
+        w1[e], s1[e] = _per_row_fp8(rng, 2 * inter, hidden, 1.0 / math.sqrt(hidden))
+        w2[e], s2[e] = _per_row_fp8(rng, hidden, inter, 1.0 / math.sqrt(inter))
+    return MoeWorkload(name=name, tokens=tokens, experts=experts, top_k=top_k, hidden=hidden, inter=inter,
+                       x=x, ids=ids, weights=weights, w1=w1, s1=s1, w2=w2, s2=s2)

@@ -35,6 +35,10 @@ Modules:
 * ``router``    the split-precision router GEMM (fp32 weight as bf16 high part +
                 bf16 residual), exact logits, top-k, its error bound and the
                 page's checks (error, greedy choice, cosine similarity)
+* ``moe``       the fused FP8 MoE layer of a decode batch: per-token FP8
+                quantisation, Gate-Up, SwiGLU, requantisation, Down, the
+                weighted top-k merge (xiaodao.ai page, MoE paragraph of
+                "为什么 batch 越大，数字越漂亮"; bitbyai.com page, MoE backend)
 
 Parity status of every function is listed in each module's header.
 """
