@@ -63,6 +63,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probe", action="store_true", help="skip the plain streaming-read probe")
     p.add_argument("--no-router", action="store_true", help="skip the split-precision router GEMM")
+    p.add_argument("--no-moe", action="store_true", help="skip the fused FP8 MoE layer")
     p.add_argument("--trace", action="store_true",
                    help="use the instrumented build and report per-CU busy time (tail balance) instead")
     p.add_argument("--products", choices=["mfma", "valu"], default="mfma",
@@ -526,6 +527,8 @@ def main():
     result["per_config"] = per_config
     if not args.no_router:
         result["router_gemm"] = router_bench(args, stream)
+    if not args.no_moe:
+        result["fused_moe"] = moe_bench(args, stream)
     if not args.no_probe:
         probe = stream_read_probe(stream)
         probe["attn_frac_of_probe"] = round(head["roofline"]["achieved"] / probe["gbps"], 4)
@@ -607,6 +610,70 @@ def router_bench(args, stream):
         res["torch_fp32_gemm_topk_us"] = round(e0.elapsed_time(e1) * 1e3 / 20, 2)
         out[f"T{T}"] = res
         del steps
+    return out
+
+
+MOE_SHAPE = dict(experts=128, top_k=8, hidden=2048, inter=768)
+MOE_TOKENS = (1, 32, 128)
+
+
+def moe_bytes(mw):
+    """Algorithmic HBM bytes of one MoE call: the E4M3 weights and per-channel scales of
+    the experts some token is routed to, the hidden states, the routing and the output."""
+    used = np.unique(mw.ids[(mw.ids >= 0) & (mw.ids < mw.experts)])
+    n_used = len(used)
+    w = n_used * (3 * mw.inter * mw.hidden + (2 * mw.inter + mw.hidden) * 4)
+    return w + 2 * mw.tokens * mw.hidden * 2 + mw.tokens * mw.top_k * 8, n_used
+
+
+def moe_bench(args, stream):
+    """The fused FP8 MoE layer at decode batch sizes (128 experts, top 8, hidden 2048,
+    inter 768; synthetic weights and routing): one call = Gate-Up, Down and merge
+    launches, replayed from a HIP graph over copies of the weights in separate buffers
+    (more than twice the Infinity Cache between two uses of the same bytes), so the
+    weights come from HBM; roofline against the HBM peak."""
+    import torch
+    from load_balanced_split_amd import inputs
+    from load_balanced_split_amd.runner import MoeStep
+    out = {}
+    base = None
+    for T in MOE_TOKENS:
+        mw = inputs.moe_workload(T, seed=T, **MOE_SHAPE)
+        if base is None:
+            base = mw                                      # the weights, drawn once
+        else:
+            mw.w1, mw.s1, mw.w2, mw.s2 = base.w1, base.s1, base.w2, base.s2
+        nbytes, n_used = moe_bytes(mw)
+        touched = n_used * 3 * mw.inter * mw.hidden
+        R = min(16, max(2, math.ceil(2 * MALL_BYTES / touched) + 1))
+        steps = [MoeStep(mw) for _ in range(R)]
+        for st in steps:
+            st.run()
+        torch.cuda.synchronize()
+        ref = steps[0].out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for st in steps:
+                st.run()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(2, math.ceil(40 / R))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * R)
+        assert torch.equal(steps[0].out, ref), "MoE graph replay differs from eager"
+        assert int(steps[0].err.item()) == 0
+        gbps = nbytes / (us * 1e-6) / 1e9
+        out[f"T{T}"] = {"tokens": T, **MOE_SHAPE, "experts_used": n_used, "rotating_copies": R,
+                        "us_per_call": round(us, 2), "algorithmic_bytes": nbytes,
+                        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}}
+        del g, steps
+        torch.cuda.empty_cache()
     return out
 
 

@@ -87,9 +87,10 @@ enum {
   HPA_DEVERR_SEQ_LEN = 1,      /* seq_len < 0 or > max_pages_per_seq * 64 */
   HPA_DEVERR_PAGE_ID = 2,      /* page id outside [0, num_pages) */
   HPA_DEVERR_PROLOGUE = 4,     /* append position outside the page table */
-  HPA_DEVERR_PLAN = 8          /* attention launched with another worker count, batch or KV-head
+  HPA_DEVERR_PLAN = 8,         /* attention launched with another worker count, batch or KV-head
                                   count than the plan was made for, or a plan workspace that is
                                   not a plan (nothing of that plan is read) */
+  HPA_DEVERR_MOE_EXPERT = 16   /* an MoE routing id outside [0, experts) (that slot adds nothing) */
 };
 
 typedef struct {
@@ -354,6 +355,39 @@ hpa_status hpa_router_workspace_size(int32_t tokens, int32_t num_experts, int32_
 hpa_status hpa_router_gemm(const void* x, const void* packed, int32_t tokens, int32_t num_experts,
                            int32_t hidden, int32_t passes, float* logits, int32_t top_k, int32_t* topk_idx,
                            float* topk_val, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Fused FP8 MoE layer for decode batches (xiaodao.ai, "HPC-Ops 把 TPOT 降 48.8%，
+ * 用户未必快一半", section "为什么 batch 越大，数字越漂亮", the MoE paragraph: the
+ * routing index, Gate-Up, activation with requantisation, Down GEMM and the top-k
+ * merge as one chain with no standalone gather; bitbyai.com "vLLM × HPC-Ops …",
+ * section "Breaking Down the Kernels", MoE backend: FP8 expert GEMMs with the token
+ * rearrangement, activation and result gathering fused).
+ *
+ * For token t and slot k, e = topk_ids[t][k], w = topk_weights[t][k]:
+ *   x8, sx = E4M3 codes and scale of x[t]: sx = max|x[t]| / 448, x8 = E4M3(x[t] / sx)
+ *   g[j]   = sx * s1[e][j] * sum_h x8[h] W1[e][j][h]           (j < 2I; gate j < I, up I + i)
+ *   a[i]   = silu(g[i]) * g[I + i]
+ *   a8, sa = E4M3 codes and scale of a (sa = max|a| / 448)
+ *   y[n]   = sa * s2[e][n] * sum_i a8[i] W2[e][n][i]
+ *   out[t] = bf16( sum over k, in k order, of w * y )
+ * (E4M3: OCP, nearest value, ties to even, saturating; fp32 arithmetic, fp32
+ * accumulation of exact products; zero rows give zero scales and codes). A slot
+ * whose expert id is outside [0, experts) adds nothing and sets
+ * HPA_DEVERR_MOE_EXPERT in device_error (device int32, may be NULL).
+ * Layouts (row-major, device, 16-byte aligned): x, out [T][H] bf16; topk_ids [T][K]
+ * int32; topk_weights [T][K] fp32; w1 [E][2I][H] E4M3 codes (gate rows, then up
+ * rows), s1 [E][2I] fp32; w2 [E][H][I] E4M3 codes, s2 [E][H] fp32. Shapes: tokens
+ * 0 .. 1024, experts 1 .. 1024, top_k 1 .. 16, hidden and inter multiples of 128 up
+ * to 4096, tokens x top_k <= 16384 (others: HPA_ERR_UNSUPPORTED, nothing launched).
+ * workspace: at least hpa_moe_workspace_size bytes (the fp32 activations, their
+ * slice maxima and the weighted per-slot results). Three launches on `stream`,
+ * nothing allocated; results are deterministic. */
+hpa_status hpa_moe_workspace_size(int32_t tokens, int32_t top_k, int32_t hidden, int32_t inter, size_t* bytes);
+hpa_status hpa_moe_fused(const void* x, const int32_t* topk_ids, const float* topk_weights, const void* w1,
+                         const float* s1, const void* w2, const float* s2, int32_t tokens, int32_t experts,
+                         int32_t top_k, int32_t hidden, int32_t inter, void* out, void* workspace,
+                         size_t workspace_bytes, int32_t* device_error, hipStream_t stream);
 
 /* Measurement aid (not part of the attention path): reads `bytes` of device
  * memory at `buf` once and computes nothing from it, so its duration gives the

@@ -32,7 +32,7 @@ HPA_KV_BF16, HPA_KV_FP8_E4M3 = 0, 1
 HPA_SCHED_BALANCED, HPA_SCHED_STATIC_SPLITS, HPA_SCHED_STATIC_CHUNK, HPA_SCHED_BALANCED_FUSED = 0, 1, 2, 3
 HPA_SCHED_BALANCED_SINGLE = 4
 SCHED = {"balanced": 0, "static_splits": 1, "static_chunk": 2, "fused": 3, "single": 4}
-DEVERR_SEQ_LEN, DEVERR_PAGE_ID, DEVERR_PROLOGUE, DEVERR_PLAN = 1, 2, 4, 8
+DEVERR_SEQ_LEN, DEVERR_PAGE_ID, DEVERR_PROLOGUE, DEVERR_PLAN, DEVERR_MOE_EXPERT = 1, 2, 4, 8, 16
 ATTN_NO_MERGE, ATTN_MERGE_ONLY, ATTN_MERGE_IN_KERNEL = 1, 2, 4
 HEADER_SLOTS = dict(Wp=0, N=1, S=2, n_items=3, n_merge=4, n_partials=5, error=6, W=7, D=8, Ws=9)
 
@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
             "hpa_decode_attn": [D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I, _P, ctypes.c_size_t,
                                 _P, ctypes.c_size_t, _P, _I, _P],
             "hpa_kv_pack_pages": [D, _P, _P, _P, _I, _P, _P, _P, _P],
+            "hpa_moe_workspace_size": [_I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
+            "hpa_moe_fused": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, ctypes.c_size_t, _P, _P],
             "hpa_decode_attn_noalloc": [D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P],
             "hpa_decode_prologue": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
                                     _P, _P, _P, _P, _P, _P, _P, _P],
@@ -273,6 +275,24 @@ def hpa_router_gemm(x, packed, experts: int, passes: int, logits, top_k: int, to
                                  _ptr(topk_idx) if top_k else None, _ptr(topk_val) if top_k else None,
                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "hpa_router_gemm")
+
+
+def hpa_moe_workspace_size(tokens: int, top_k: int, hidden: int, inter: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().hpa_moe_workspace_size(tokens, top_k, hidden, inter, ctypes.byref(n)), "hpa_moe_workspace_size")
+    return n.value
+
+
+def hpa_moe_fused(x, topk_ids, topk_weights, w1, s1, w2, s2, experts: int, inter: int, out, workspace,
+                  device_error=None, stream=None) -> None:
+    """x bf16 [T, H]; ids int32 / weights fp32 [T, K]; w1 uint8 [E, 2I, H], s1 fp32 [E, 2I];
+    w2 uint8 [E, H, I], s2 fp32 [E, H]; out bf16 [T, H]."""
+    T, H = x.shape
+    K = topk_ids.shape[1]
+    _check(lib().hpa_moe_fused(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w1), _ptr(s1), _ptr(w2), _ptr(s2),
+                               T, experts, K, H, inter, _ptr(out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _ptr(device_error), _stream(stream)),
+           "hpa_moe_fused")
 
 
 def hpa_status_string(status: int) -> str:

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = ["plan.hip", "attn.hip", "prologue.hip", "probe.hip", "router.hip", "noalloc.hip", "pack.hip", "host.cpp",
+SOURCES = ["plan.hip", "attn.hip", "prologue.hip", "probe.hip", "router.hip", "noalloc.hip", "pack.hip", "moe.hip", "host.cpp",
            "router_host.cpp"]
 # Packed-fp32 VALU ops are kept out of every kernel (the compiler would otherwise
 # form v_pk_* from scalar float code). The atomic optimizer is off: it turns a

@@ -189,3 +189,33 @@ class RouterStep:
         return (self.logits.cpu().numpy().astype(np.float64),
                 self.topk_idx[:, :k].cpu().numpy().astype(np.int64),
                 self.topk_val[:, :k].cpu().numpy().astype(np.float64))
+
+
+class MoeStep:
+    """An MoE workload (inputs.MoeWorkload) resident in HBM: hidden states, routing,
+    E4M3 expert weights with their scales, the output and the workspace."""
+
+    def __init__(self, mw, device: str = "cuda"):
+        import torch
+        self.torch = torch
+        self.mw = mw
+        dev = torch.device(device)
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        self.x = up(mw.x.view(np.int16)).view(torch.bfloat16)
+        self.ids = up(mw.ids)
+        self.weights = up(mw.weights)
+        self.w1, self.s1 = up(mw.w1), up(mw.s1)
+        self.w2, self.s2 = up(mw.w2), up(mw.s2)
+        self.out = torch.empty((mw.tokens, mw.hidden), dtype=torch.bfloat16, device=dev)
+        ws = _lib.hpa_moe_workspace_size(mw.tokens, mw.top_k, mw.hidden, mw.inter)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run(self, stream=None):
+        mw = self.mw
+        _lib.hpa_moe_fused(self.x, self.ids, self.weights, self.w1, self.s1, self.w2, self.s2, mw.experts, mw.inter,
+                           self.out, self.workspace, self.err, stream)
+        return self.out
+
+    def output_f64(self) -> np.ndarray:
+        return self.out.float().cpu().numpy().astype(np.float64)

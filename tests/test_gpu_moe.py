@@ -1,0 +1,101 @@
+"""GPU parity of the fused FP8 MoE layer (hpa_moe_fused, through the C ABI) against
+the oracle.
+
+Tolerance (derived from the arithmetic; the pages give none for this path): both
+sides take the same E4M3 decisions for the tokens (fp32 scale and division on
+both), and every FP8 x FP8 product is exact in fp32, so Gate-Up differs only by the
+fp32 summation order (relative ~H 2^-24 of the sum of magnitudes). SwiGLU then
+differs by a few fp32 ulps, and the requantised activation codes can differ by one
+code where a / sa lies within that distance of a rounding midpoint (rare); each
+such code moves one of I terms of a Down row by at most one E4M3 step (2^-3
+relative). With outputs of order 0.1-1, |gpu - ref| <= 1e-2 + 1e-2 |ref| per
+element (the bf16 rounding of the output, 2^-9 relative, included) covers these and
+fails any wrong term. The fp32 activations are checked against the oracle's at
+1e-4 relative to the row's largest magnitude."""
+
+import numpy as np
+import pytest
+
+from load_balanced_split_amd import _lib, inputs
+from oracle import moe as om
+from tests.helpers import ensure_built
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ATOL = RTOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ensure_built()
+    _lib.lib()
+
+
+def _check(mw, tokens=None, act=True):
+    from load_balanced_split_amd.runner import MoeStep
+    d = MoeStep(mw)
+    print(f"moe T={mw.tokens} E={mw.experts} K={mw.top_k} H={mw.hidden} I={mw.inter}", flush=True)
+    d.workspace.fill_(0xFF)                     # NaN everywhere the kernels do not write
+    d.run()
+    torch.cuda.synchronize()
+    got = d.output_f64()
+    assert np.all(np.isfinite(got))
+    rows = range(mw.tokens) if tokens is None else tokens
+    sel = list(rows)
+    ref, det = om.fused_moe(mw.x[sel], mw.ids[sel], mw.weights[sel], mw.w1, mw.s1, mw.w2, mw.s2, details=True)
+    err = np.abs(got[sel] - ref)
+    ratio = float(np.max(err / (ATOL + RTOL * np.abs(ref))))
+    print(f"   max |err| {err.max():.3e}, max err/tol {ratio:.3f}, max |ref| {np.abs(ref).max():.3f}", flush=True)
+    assert ratio <= 1.0
+    if act:
+        ws = d.workspace.cpu().numpy()
+        a_gpu = ws[: mw.tokens * mw.top_k * mw.inter * 4].view(np.float32).reshape(mw.tokens, mw.top_k, mw.inter)
+        for i, t in enumerate(sel):
+            for k in range(mw.top_k):
+                if (i, k) in det["act"]:
+                    want = det["act"][(i, k)]
+                    scale = max(np.abs(want).max(), 1e-30)
+                    assert np.max(np.abs(a_gpu[t, k] - want)) <= 1e-4 * scale, (t, k)
+    assert int(d.err.item()) == 0
+    return d, got
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 1, 128, 128), (5, 4, 2, 256, 128), (33, 16, 8, 384, 256),
+                                   (17, 8, 3, 128, 384), (64, 32, 4, 512, 256)])
+def test_moe_small_shapes_against_oracle(shape):
+    T, E, K, H, I = shape
+    _check(inputs.moe_workload(T, E, K, H, I, seed=sum(shape)))
+
+
+def test_moe_decode_shape_sampled_tokens():
+    """The benchmark's decode shape (32 tokens, 128 experts, top 8, hidden 2048, inter
+    768) on sampled tokens, and two runs give identical bits."""
+    mw = inputs.moe_workload(32, 128, 8, 2048, 768, seed=0)
+    d, got = _check(mw, tokens=[0, 7, 19, 31], act=True)
+    d.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(d.output_f64(), got)
+
+
+def test_moe_edge_cases():
+    """A zero token gives a zero row; an expert id out of range adds nothing and is
+    reported; a token routed twice to one expert adds both slots; more than 16 tokens
+    on one expert span several pair blocks."""
+    from load_balanced_split_amd.runner import MoeStep
+    mw = inputs.moe_workload(40, 6, 3, 256, 128, seed=9)
+    mw.x[3] = 0
+    mw.ids[5, 1] = mw.ids[5, 0]                 # the same expert twice
+    mw.ids[:, 2] = 2                             # every token on expert 2 (40 > 16 pairs)
+    mw.ids[5, 2] = 2
+    mw.ids[0, 0], mw.ids[1, 2] = 6, -1           # out of range: skipped
+    d = MoeStep(mw)
+    d.run()
+    torch.cuda.synchronize()
+    assert int(d.err.item()) & _lib.DEVERR_MOE_EXPERT
+    got = d.output_f64()
+    ref = om.fused_moe(mw.x, mw.ids, mw.weights, mw.w1, mw.s1, mw.w2, mw.s2)
+    assert np.all(np.abs(got - ref) <= ATOL + RTOL * np.abs(ref))
+    assert not got[3].any()
