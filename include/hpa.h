@@ -380,9 +380,10 @@ hpa_status hpa_router_gemm(const void* x, const void* packed, int32_t tokens, in
  * rows), s1 [E][2I] fp32; w2 [E][H][I] E4M3 codes, s2 [E][H] fp32. Shapes: tokens
  * 0 .. 1024, experts 1 .. 1024, top_k 1 .. 16, hidden and inter multiples of 128 up
  * to 4096, tokens x top_k <= 16384 (others: HPA_ERR_UNSUPPORTED, nothing launched).
- * workspace: at least hpa_moe_workspace_size bytes (the fp32 activations, their
- * slice maxima and the weighted per-slot results). Three launches on `stream`,
- * nothing allocated; results are deterministic. */
+ * workspace: at least hpa_moe_workspace_size bytes (token codes, the routing
+ * index, the fp32 activations and their codes, the weighted per-slot results).
+ * Five launches on `stream` (quantise + routing index, Gate-Up, requantise, Down,
+ * merge), nothing allocated; results are deterministic. */
 hpa_status hpa_moe_workspace_size(int32_t tokens, int32_t top_k, int32_t hidden, int32_t inter, size_t* bytes);
 hpa_status hpa_moe_fused(const void* x, const int32_t* topk_ids, const float* topk_weights, const void* w1,
                          const float* s1, const void* w2, const float* s2, int32_t tokens, int32_t experts,

@@ -9,28 +9,29 @@
 // Kernels" (MoE backend): token rearrangement, FP8 expert GEMMs, activation and
 // result gathering fused to avoid intermediate HBM round trips and launches.
 //
-// Three launches, no gather, no sort:
-//  moe_gate_up_kernel  workgroup (expert e, block of 16 of its pairs, 64 of I): finds
-//      its pairs by scanning the routing ids (pairs p = t K + k with ids[p] == e, in
-//      p order), reads the tokens' bf16 rows by index and quantises them to E4M3 in
-//      LDS (scale amax / 448 per token), multiplies with 64 gate and 64 up rows of W1
-//      on v_mfma_f32_16x16x128_f8f6f4, and in the epilogue applies the per-channel
-//      scales and SwiGLU; it writes the fp32 activation slice and the slice's amax.
-//  moe_down_kernel     workgroup (expert e, block of 16 pairs, 64 of H): requantises
-//      its pairs' activations to E4M3 as they come into LDS (scale = the row amax /
-//      448, the amax taken over the slices' maxima), multiplies with 64 rows of W2
-//      and writes y * scale * routing weight per pair.
-//  moe_merge_kernel    out[t] = sum over k, in k order, of the pair results -> bf16.
+// The chain (no gather: tokens and activations are read in place by pair index):
+//  moe_prepare_kernel   blocks 0 .. T-1 quantise one token row each to E4M3 (scale
+//      amax / 448); block T builds the routing index: the pairs p = t K + k grouped
+//      by expert (each group in pair order, by a counting sort) and the table of
+//      pair blocks (expert, first pair, up to 16 pairs).
+//  moe_gate_up_kernel   one wave per (pair block, 16 rows of I): 16 gate and 16 up
+//      rows of W1 against the block's token codes on v_mfma_f32_16x16x128_f8f6f4,
+//      per-channel and token scales, SwiGLU; writes the fp32 activations and the
+//      largest magnitude of each 16-wide slice.
+//  moe_quant_act_kernel one block per pair: the activation row's scale (max of its
+//      slice maxima / 448) and E4M3 codes.
+//  moe_down_kernel      one wave per (pair block, 16 rows of H): 16 rows of W2
+//      against the block's activation codes; scales and routing weight applied.
+//  moe_merge_kernel     out[t] = sum over k, in k order, of the pair results -> bf16.
 //
-// Both products: A = weight rows (16 per wave), B = quantised activations of 16
-// pairs (LDS); per 128-wide k chunk a lane holds 32 consecutive bytes of its row
-// (16-byte loads, whole 128-byte lines of each weight row) and one MFMA consumes
-// them. A and B use the same lane -> k assignment, so the product is the plain
-// sum over k. Weight bytes are read once per (expert, pair block) from HBM with
-// the streaming policy.
+// Products: A = 16 weight rows, B = 16 pairs; per 128-wide k chunk a lane (row or
+// pair m, group q) holds the 32 bytes [128 c + 32 q, + 32) of its row, both operands
+// alike, and one MFMA consumes them -- the plain sum over k. A workgroup is one wave
+// so that a batch with a few active experts still spreads over every CU.
 #include "hpa_internal.hpp"
 #include "moe_internal.hpp"
 
+#include <algorithm>
 #include <cmath>
 
 namespace hpa {
@@ -43,9 +44,10 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kMoeThreads = 256;
 constexpr int kPairsPerBlock = 16;
-constexpr int kLdsPad = 16;          // bytes after every LDS row: 16-byte reads of 16 rows hit distinct banks
 constexpr int kBufDword3 = 0x00020000;
-constexpr int kPolicyStream = 2;
+// weight loads keep the default cache policy: the two 16-byte halves of a lane's 32
+// bytes are separate instructions over the same lines, and the second must find them
+constexpr int kPolicyWeights = 0;
 
 __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t p = reinterpret_cast<uint64_t>(base);
@@ -56,7 +58,7 @@ __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 
 __device__ inline u32x4 wload16(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), kPolicyStream);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), kPolicyWeights);
 }
 
 // fp32 -> OCP E4M3 code: nearest value, ties to even mantissa, saturating at 448.
@@ -94,288 +96,298 @@ __device__ inline uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// The pairs of expert e with rank [16 pb, 16 pb + 16) among its pairs (in pair order),
-// found by wave 0 scanning the routing ids; returns how many (<= 0: none).
-__device__ int find_pairs(const MoeArgs& a, int e, int pb, int* pairs, int* count) {
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x < 64) {
-    const int lo = kPairsPerBlock * pb, hi = lo + kPairsPerBlock;
-    int found = 0;
-    for (int base = 0; base < a.P && found < hi; base += 64 * 8) {
-      int v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int p = base + 64 * j + lane;
-        v[j] = p < a.P ? a.ids[p] : -1;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool hit = v[j] == e;
-        const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
-        const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
-        const int idx = found + below;
-        if (hit && idx >= lo && idx < hi) pairs[idx - lo] = base + 64 * j + lane;
-        found += __builtin_popcountll(m);
-      }
-    }
-    if (lane == 0) *count = min(kPairsPerBlock, found - lo);
-  }
-  __syncthreads();
-  return __builtin_amdgcn_readfirstlane(*count);
-}
 
-// Gate-Up + SwiGLU. Grid: experts x pair blocks x I / 64.
-__global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(MoeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];   // [16][H + pad] E4M3 codes
-  __shared__ int pairs[kPairsPerBlock];
-  __shared__ int count;
-  __shared__ float sx[kPairsPerBlock];
-  __shared__ float wmax[4][kPairsPerBlock];
-  const int it = blockIdx.x % a.IT, rest = blockIdx.x / a.IT;
-  const int pb0 = rest % a.PB, e = rest / a.PB;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int rs = a.H + kLdsPad;
-  // pair chunks pb0, pb0 + PB, ...: with distinct experts per token an expert has at
-  // most T pairs and the first chunk is the only one; repeated ids take more turns
-  for (int pb = pb0;; pb += a.PB) {
-    const int n = find_pairs(a, e, pb, pairs, &count);
-    if (n <= 0) return;
-    // the tokens' rows, quantised: wave w takes rows w, w + 4, ...; lane l holds 16-byte
-    // pieces l, l + 64, ... of the row (8 bf16 each)
-    const int pieces = a.H / 8;
-    for (int r = wave; r < kPairsPerBlock; r += 4) {
-      uint8_t* dst = xs + r * rs;
-      if (r >= n) {                                   // padding rows multiply as zeros
-        for (int c = lane; c < pieces; c += 64) *reinterpret_cast<uint2*>(dst + 8 * c) = make_uint2(0, 0);
-        if (lane == 0) sx[r] = 0.f;
-        continue;
-      }
-      const int t = pairs[r] / a.K;
-      const uint16_t* row = a.x + int64_t(t) * a.H;
-      u32x4 v[kMoeMaxHidden / 512];
-      float amax = 0.f;
+// Quantise one token row (blocks 0 .. T-1), or build the routing index (block T).
+__global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
+  __shared__ float red[4];
+  __shared__ int cnt[kMoeMaxExperts + 1];
+  __shared__ int run[kMoeMaxExperts];
+  __shared__ int chunk[kMoeThreads];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (blockIdx.x < static_cast<unsigned>(a.T)) {
+    const int t = blockIdx.x;
+    const int pieces = a.H / 8;                               // 16-byte pieces of 8 bf16
+    const uint16_t* row = a.x + int64_t(t) * a.H;
+    u32x4 v[kMoeMaxHidden / 8 / kMoeThreads];
+    float amax = 0.f;
 #pragma unroll
-      for (int j = 0; j < kMoeMaxHidden / 512; ++j)
-        if (j * 64 + lane < pieces) v[j] = *reinterpret_cast<const u32x4*>(row + 8 * (j * 64 + lane));
-#pragma unroll
-      for (int j = 0; j < kMoeMaxHidden / 512; ++j) {
-        if (j * 64 + lane >= pieces) continue;
+    for (int j = 0; j < kMoeMaxHidden / 8 / kMoeThreads; ++j) {
+      const int c = j * kMoeThreads + tid;
+      if (c < pieces) {
+        v[j] = *reinterpret_cast<const u32x4*>(row + 8 * c);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           amax = fmaxf(amax, fabsf(__builtin_bit_cast(float, v[j][d] << 16)));
           amax = fmaxf(amax, fabsf(__builtin_bit_cast(float, v[j][d] & 0xffff0000u)));
         }
       }
-      amax = wave_max(amax);
-      const float s = amax / 448.0f;
-      if (lane == 0) sx[r] = s;
+    }
+    amax = wave_max(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax / 448.0f;
+    if (tid == 0) a.sx[t] = s;
 #pragma unroll
-      for (int j = 0; j < kMoeMaxHidden / 512; ++j) {
-        if (j * 64 + lane >= pieces) continue;
-        uint32_t w[2] = {0, 0};
-        if (s > 0.f) {
+    for (int j = 0; j < kMoeMaxHidden / 8 / kMoeThreads; ++j) {
+      const int c = j * kMoeThreads + tid;
+      if (c >= pieces) continue;
+      uint32_t w[2] = {0, 0};
+      if (s > 0.f) {
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const float lo = __builtin_bit_cast(float, v[j][d] << 16);
-            const float hi = __builtin_bit_cast(float, v[j][d] & 0xffff0000u);
-            w[d / 2] |= (e4m3_code(lo / s) | (e4m3_code(hi / s) << 8)) << (16 * (d % 2));
-          }
+        for (int d = 0; d < 4; ++d) {
+          const float lo = __builtin_bit_cast(float, v[j][d] << 16);
+          const float hi = __builtin_bit_cast(float, v[j][d] & 0xffff0000u);
+          w[d / 2] |= (e4m3_code(lo / s) | (e4m3_code(hi / s) << 8)) << (16 * (d % 2));
         }
-        *reinterpret_cast<uint2*>(dst + 8 * (j * 64 + lane)) = make_uint2(w[0], w[1]);
       }
+      *reinterpret_cast<uint2*>(a.x8 + int64_t(t) * a.H + 8 * c) = make_uint2(w[0], w[1]);
+    }
+    return;
+  }
+  // routing index: counts per expert, their prefix (list offsets) and the pair blocks
+  for (int e = tid; e < a.E; e += kMoeThreads) cnt[e] = 0;
+  __syncthreads();
+  bool bad = false;
+  for (int p = tid; p < a.P; p += kMoeThreads) {
+    const int e = a.ids[p];
+    if (e >= 0 && e < a.E) atomicAdd(&cnt[e], 1);
+    else bad = true;
+  }
+  if (bad && a.err) __hip_atomic_fetch_or(a.err, HPA_DEVERR_MOE_EXPERT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (tid < 64) {                   // wave 0: exclusive prefixes of counts and of block counts
+    int carry = 0, bcarry = 0;
+    for (int base = 0; base < a.E; base += 64) {
+      const int e = base + lane;
+      const int c = e < a.E ? cnt[e] : 0;
+      const int nb = (c + kPairsPerBlock - 1) / kPairsPerBlock;
+      int x = c, y = nb;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int xs = __shfl_up(x, o, 64), ys = __shfl_up(y, o, 64);
+        if (lane >= o) {
+          x += xs;
+          y += ys;
+        }
+      }
+      if (e < a.E) {
+        run[e] = carry + x - c;
+        for (int b = 0; b < nb; ++b) {          // this expert's pair blocks
+          const int g = bcarry + y - nb + b;
+          a.blk[g] = e;
+          a.blk[a.P + g] = carry + x - c + kPairsPerBlock * b;
+          a.blk[2 * a.P + g] = min(kPairsPerBlock, c - kPairsPerBlock * b);
+        }
+      }
+      carry += __shfl(x, 63, 64);
+      bcarry += __shfl(y, 63, 64);
+    }
+    if (lane == 0) *a.nblk = bcarry;
+  }
+  __syncthreads();
+  // place the pairs, 256 at a time in pair order: rank = earlier pairs of the same expert
+  for (int base = 0; base < a.P; base += kMoeThreads) {
+    const int p = base + tid;
+    int e = p < a.P ? a.ids[p] : -1;
+    if (e >= a.E) e = -1;
+    chunk[tid] = e;
+    __syncthreads();
+    int rank = 0, slot = 0;
+    if (e >= 0) {
+      for (int j = 0; j < tid; ++j) rank += chunk[j] == e;
+      slot = run[e] + rank;
     }
     __syncthreads();
-    // 16 gate rows and the matching 16 up rows per wave; lane (m, q) holds row m's bytes
-    // [128 c + 32 q, + 32) of every chunk c
-    const int m16 = lane & 15, q = lane >> 4;
-    const int g0 = it * 64 + 16 * wave;                      // first gate row of this wave (< I)
-    const int nch = a.H / 128;
-    const uint8_t* w1e = a.w1 + int64_t(e) * 2 * a.I * a.H;
-    const rsrc_t rw = make_rsrc(w1e, static_cast<uint32_t>(int64_t(2) * a.I * a.H));
-    const uint32_t og = static_cast<uint32_t>((g0 + m16) * a.H + 32 * q);
-    const uint32_t ou = static_cast<uint32_t>((a.I + g0 + m16) * a.H + 32 * q);
-    f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = accg;
-    constexpr int kDepth = 4;
-    u32x4 ag[kDepth][2], au[kDepth][2];
-    auto load = [&](int slot, int c) {
-      const uint32_t sc = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(128 * c));
-      ag[slot][0] = wload16(rw, og, sc);
-      ag[slot][1] = wload16(rw, og + 16, sc);
-      au[slot][0] = wload16(rw, ou, sc);
-      au[slot][1] = wload16(rw, ou + 16, sc);
-    };
-    // chunk c lives in ring slot c % kDepth; slots are compile-time (the loop is unrolled
-    // by kDepth), and the loads of chunk c + kDepth - 1 go out before chunk c is used
-    auto mul = [&](int slot, int c) {
-      const uint8_t* brow = xs + m16 * rs + 128 * c + 32 * q;
-      const i32x8 B = operand(*reinterpret_cast<const u32x4*>(brow), *reinterpret_cast<const u32x4*>(brow + 16));
-      accg = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(ag[slot][0], ag[slot][1]), B, accg,
-                                                              0, 0, 0, 0, 0, 0);
-      accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(au[slot][0], au[slot][1]), B, accu,
-                                                              0, 0, 0, 0, 0, 0);
-    };
-#pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d) load(d, min(d, nch - 1));
-    int c = 0;
-    for (; c + kDepth <= nch; c += kDepth) {
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        load((d + kDepth - 1) % kDepth, min(c + d + kDepth - 1, nch - 1));
-        mul(d, c + d);
-      }
+    if (e >= 0) {
+      a.list[slot] = p;
+      atomicAdd(&run[e], 1);
     }
-#pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d)
-      if (c + d < nch) mul(d, c + d);
-    // epilogue: lane (m16, q) holds gate / up rows g0 + 4 q + i (i < 4) of pair slot m16
-    const float* s1e = a.s1 + int64_t(e) * 2 * a.I;
-    const f32x4 sg = *reinterpret_cast<const f32x4*>(s1e + g0 + 4 * q);
-    const f32x4 su = *reinterpret_cast<const f32x4*>(s1e + a.I + g0 + 4 * q);
-    const float sxm = sx[m16];
-    f32x4 act;
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float g = accg[i] * sxm * sg[i];
-      const float u = accu[i] * sxm * su[i];
-      act[i] = g / (1.0f + expf(-g)) * u;
-      amax = fmaxf(amax, fabsf(act[i]));
-    }
-    const bool valid = m16 < n;
-    const int p = valid ? pairs[m16] : 0;
-    if (valid) *reinterpret_cast<f32x4*>(a.act + int64_t(p) * a.I + g0 + 4 * q) = act;
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-    if (q == 0) wmax[wave][m16] = amax;
     __syncthreads();
-    if (threadIdx.x < n) {
-      const int r = threadIdx.x;
-      const float mx = fmaxf(fmaxf(wmax[0][r], wmax[1][r]), fmaxf(wmax[2][r], wmax[3][r]));
-      a.amax[int64_t(pairs[r]) * a.IT + it] = mx;
-    }
-    __syncthreads();                  // pairs, sx, wmax and the LDS rows are rewritten next turn
   }
 }
 
-// Down + scales + routing weight. Grid: experts x pair blocks x H / 64.
-__global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(MoeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t as8[];   // [16][I + pad] E4M3 codes
-  __shared__ int pairs[kPairsPerBlock];
-  __shared__ int count;
-  __shared__ float sa[kPairsPerBlock];
-  const int ht = blockIdx.x % a.HT, rest = blockIdx.x / a.HT;
-  const int pb0 = rest % a.PB, e = rest / a.PB;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int rs = a.I + kLdsPad;
-  for (int pb = pb0;; pb += a.PB) {   // pair chunks as in the Gate-Up kernel
-    const int n = find_pairs(a, e, pb, pairs, &count);
-    if (n <= 0) return;
-    // activation rows, requantised: lane l holds 4-float pieces l, l + 64, ...
-    const int pieces = a.I / 4;
-    for (int r = wave; r < kPairsPerBlock; r += 4) {
-      uint8_t* dst = as8 + r * rs;
-      if (r >= n) {
-        for (int c = lane; c < pieces; c += 64) *reinterpret_cast<uint32_t*>(dst + 4 * c) = 0;
-        continue;
-      }
-      const int p = pairs[r];
-      float amax = 0.f;
-      for (int j = lane; j < a.IT; j += 64) amax = fmaxf(amax, a.amax[int64_t(p) * a.IT + j]);
-      amax = wave_max(amax);
-      const float s = amax / 448.0f;
-      if (lane == 0) sa[r] = s;
-      const float* row = a.act + int64_t(p) * a.I;
-      f32x4 v[kMoeMaxInter / 256];
+// Gate-Up + SwiGLU: one wave per (pair block, 16 rows of I).
+__global__ __launch_bounds__(64) void moe_gate_up_kernel(MoeArgs a) {
+  const int ib = blockIdx.x % (a.I / 16), gb = blockIdx.x / (a.I / 16);
+  if (gb >= *a.nblk) return;
+  const int e = a.blk[gb], first = a.blk[a.P + gb], n = a.blk[2 * a.P + gb];
+  const int lane = threadIdx.x, m16 = lane & 15, q = lane >> 4;
+  const bool valid = m16 < n;
+  const int p = valid ? a.list[first + m16] : 0;
+  const int t = p / a.K;
+  const int nch = a.H / 128;
+  const rsrc_t rw = make_rsrc(a.w1 + int64_t(e) * 2 * a.I * a.H, static_cast<uint32_t>(int64_t(2) * a.I * a.H));
+  const rsrc_t rx = make_rsrc(a.x8, static_cast<uint32_t>(int64_t(a.T) * a.H));
+  const int g0 = ib * 16;
+  const uint32_t og = static_cast<uint32_t>((g0 + m16) * a.H + 32 * q);
+  const uint32_t ou = static_cast<uint32_t>((a.I + g0 + m16) * a.H + 32 * q);
+  // padding pair columns read past the buffer: zeros
+  const uint32_t ox = valid ? static_cast<uint32_t>(t * a.H + 32 * q) : 0x80000000u;
+  f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = accg;
+  constexpr int kDepth = 4;
+  u32x4 ag[kDepth][2], au[kDepth][2], bx[kDepth][2];
+  auto load = [&](int slot, int c) {
+    const uint32_t sc = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(128 * c));
+    ag[slot][0] = wload16(rw, og, sc);
+    ag[slot][1] = wload16(rw, og + 16, sc);
+    au[slot][0] = wload16(rw, ou, sc);
+    au[slot][1] = wload16(rw, ou + 16, sc);
+    bx[slot][0] = wload16(rx, ox, sc);
+    bx[slot][1] = wload16(rx, ox + 16, sc);
+  };
+  auto mul = [&](int slot) {
+    const i32x8 B = operand(bx[slot][0], bx[slot][1]);
+    accg = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(ag[slot][0], ag[slot][1]), B, accg,
+                                                            0, 0, 0, 0, 0, 0);
+    accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(au[slot][0], au[slot][1]), B, accu,
+                                                            0, 0, 0, 0, 0, 0);
+  };
+  // chunk c lives in ring slot c % kDepth (compile-time: the loop is unrolled by kDepth);
+  // the loads of chunk c + kDepth - 1 go out before chunk c is multiplied
 #pragma unroll
-      for (int j = 0; j < kMoeMaxInter / 256; ++j)
-        if (j * 64 + lane < pieces) v[j] = *reinterpret_cast<const f32x4*>(row + 4 * (j * 64 + lane));
+  for (int d = 0; d < kDepth - 1; ++d) load(d, min(d, nch - 1));
+  int c = 0;
+  for (; c + kDepth <= nch; c += kDepth) {
 #pragma unroll
-      for (int j = 0; j < kMoeMaxInter / 256; ++j) {
-        if (j * 64 + lane >= pieces) continue;
-        uint32_t w = 0;
-        if (s > 0.f) {
-#pragma unroll
-          for (int d = 0; d < 4; ++d) w |= e4m3_code(v[j][d] / s) << (8 * d);
-        }
-        *reinterpret_cast<uint32_t*>(dst + 4 * (j * 64 + lane)) = w;
-      }
+    for (int d = 0; d < kDepth; ++d) {
+      load((d + kDepth - 1) % kDepth, min(c + d + kDepth - 1, nch - 1));
+      mul(d);
     }
-    __syncthreads();
-    const int m16 = lane & 15, q = lane >> 4;
-    const int n0 = ht * 64 + 16 * wave;                       // first output row of this wave (< H)
-    const int nch = a.I / 128;
-    const uint8_t* w2e = a.w2 + int64_t(e) * a.H * a.I;
-    const rsrc_t rw = make_rsrc(w2e, static_cast<uint32_t>(int64_t(a.H) * a.I));
-    const uint32_t ow = static_cast<uint32_t>((n0 + m16) * a.I + 32 * q);
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int kDepth = 4;
-    u32x4 aw[kDepth][2];
-    auto load = [&](int slot, int c) {
-      const uint32_t sc = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(128 * c));
-      aw[slot][0] = wload16(rw, ow, sc);
-      aw[slot][1] = wload16(rw, ow + 16, sc);
-    };
-    auto mul = [&](int slot, int c) {
-      const uint8_t* brow = as8 + m16 * rs + 128 * c + 32 * q;
-      const i32x8 B = operand(*reinterpret_cast<const u32x4*>(brow), *reinterpret_cast<const u32x4*>(brow + 16));
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(aw[slot][0], aw[slot][1]), B, acc,
-                                                             0, 0, 0, 0, 0, 0);
-    };
+  }
 #pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d) load(d, min(d, nch - 1));
-    int c = 0;
-    for (; c + kDepth <= nch; c += kDepth) {
+  for (int d = 0; d < kDepth - 1; ++d)
+    if (c + d < nch) mul(d);
+  // lane (m16, q) holds gate / up rows g0 + 4 q + i (i < 4) of pair column m16
+  const float* s1e = a.s1 + int64_t(e) * 2 * a.I;
+  const f32x4 sg = *reinterpret_cast<const f32x4*>(s1e + g0 + 4 * q);
+  const f32x4 su = *reinterpret_cast<const f32x4*>(s1e + a.I + g0 + 4 * q);
+  const float sxm = valid ? a.sx[t] : 0.f;
+  f32x4 act;
+  float amax = 0.f;
 #pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        load((d + kDepth - 1) % kDepth, min(c + d + kDepth - 1, nch - 1));
-        mul(d, c + d);
-      }
+  for (int i = 0; i < 4; ++i) {
+    const float g = accg[i] * sxm * sg[i];
+    const float u = accu[i] * sxm * su[i];
+    act[i] = g / (1.0f + expf(-g)) * u;
+    amax = fmaxf(amax, fabsf(act[i]));
+  }
+  if (valid) *reinterpret_cast<f32x4*>(a.act + int64_t(p) * a.I + g0 + 4 * q) = act;
+  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  if (valid && q == 0) a.amax[int64_t(p) * (a.I / 16) + ib] = amax;
+}
+
+// Requantise one pair's activation row: scale = max of its slice maxima / 448.
+__global__ __launch_bounds__(kMoeThreads) void moe_quant_act_kernel(MoeArgs a) {
+  __shared__ float red[4];
+  const int p = blockIdx.x;
+  const int e = a.ids[p];
+  if (e < 0 || e >= a.E) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float amax = 0.f;
+  for (int j = tid; j < a.I / 16; j += kMoeThreads) amax = fmaxf(amax, a.amax[int64_t(p) * (a.I / 16) + j]);
+  amax = wave_max(amax);
+  if (lane == 0) red[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax / 448.0f;
+  if (tid == 0) a.sa[p] = s;
+  const float* row = a.act + int64_t(p) * a.I;
+  for (int c = tid; c < a.I / 4; c += kMoeThreads) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(row + 4 * c);
+    uint32_t w = 0;
+    if (s > 0.f) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) w |= e4m3_code(v[d] / s) << (8 * d);
     }
-#pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d)
-      if (c + d < nch) mul(d, c + d);
-    if (m16 < n) {
-      const int p = pairs[m16];
-      const f32x4 s2 = *reinterpret_cast<const f32x4*>(a.s2 + int64_t(e) * a.H + n0 + 4 * q);
-      const float f = sa[m16] * a.wts[p];
-      f32x4 y;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = acc[i] * f * s2[i];
-      *reinterpret_cast<f32x4*>(a.ybuf + int64_t(p) * a.H + n0 + 4 * q) = y;
-    }
-    __syncthreads();                  // pairs, sa and the LDS rows are rewritten next turn
+    *reinterpret_cast<uint32_t*>(a.act8 + int64_t(p) * a.I + 4 * c) = w;
   }
 }
 
-// out[t][n .. n + 3] = bf16 of the sum over k (in k order) of the pair results; pairs
-// whose expert id is outside [0, E) add nothing (and report an error).
+// Down + scales + routing weight: one wave per (pair block, 16 rows of H).
+__global__ __launch_bounds__(64) void moe_down_kernel(MoeArgs a) {
+  const int nb = blockIdx.x % (a.H / 16), gb = blockIdx.x / (a.H / 16);
+  if (gb >= *a.nblk) return;
+  const int e = a.blk[gb], first = a.blk[a.P + gb], n = a.blk[2 * a.P + gb];
+  const int lane = threadIdx.x, m16 = lane & 15, q = lane >> 4;
+  const bool valid = m16 < n;
+  const int p = valid ? a.list[first + m16] : 0;
+  const int nch = a.I / 128;
+  const rsrc_t rw = make_rsrc(a.w2 + int64_t(e) * a.H * a.I, static_cast<uint32_t>(int64_t(a.H) * a.I));
+  const rsrc_t ra = make_rsrc(a.act8, static_cast<uint32_t>(int64_t(a.P) * a.I));
+  const int n0 = nb * 16;
+  const uint32_t ow = static_cast<uint32_t>((n0 + m16) * a.I + 32 * q);
+  const uint32_t oa = valid ? static_cast<uint32_t>(p * a.I + 32 * q) : 0x80000000u;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int kDepth = 4;
+  u32x4 aw[kDepth][2], ba[kDepth][2];
+  auto load = [&](int slot, int c) {
+    const uint32_t sc = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(128 * c));
+    aw[slot][0] = wload16(rw, ow, sc);
+    aw[slot][1] = wload16(rw, ow + 16, sc);
+    ba[slot][0] = wload16(ra, oa, sc);
+    ba[slot][1] = wload16(ra, oa + 16, sc);
+  };
+  auto mul = [&](int slot) {
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(aw[slot][0], aw[slot][1]),
+                                                           operand(ba[slot][0], ba[slot][1]), acc, 0, 0, 0, 0, 0, 0);
+  };
+#pragma unroll
+  for (int d = 0; d < kDepth - 1; ++d) load(d, min(d, nch - 1));
+  int c = 0;
+  for (; c + kDepth <= nch; c += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      load((d + kDepth - 1) % kDepth, min(c + d + kDepth - 1, nch - 1));
+      mul(d);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < kDepth - 1; ++d)
+    if (c + d < nch) mul(d);
+  if (valid) {
+    const f32x4 s2 = *reinterpret_cast<const f32x4*>(a.s2 + int64_t(e) * a.H + n0 + 4 * q);
+    const float f = a.sa[p] * a.wts[p];
+    f32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = acc[i] * f * s2[i];
+    *reinterpret_cast<f32x4*>(a.ybuf + int64_t(p) * a.H + n0 + 4 * q) = y;
+  }
+}
+
+// out[t][n .. n + 3] = bf16 of the sum over k (in k order) of the pair results; slots
+// whose expert id is outside [0, E) add nothing (the routing block reported them).
 __global__ __launch_bounds__(kMoeThreads) void moe_merge_kernel(MoeArgs a) {
   const int t = blockIdx.y;
   const int nq = blockIdx.x * kMoeThreads + threadIdx.x;     // 4-dim piece
   if (4 * nq >= a.H) return;
   f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-  bool bad = false;
   for (int k = 0; k < a.K; ++k) {
     const int p = t * a.K + k;
     const int e = a.ids[p];
-    if (e < 0 || e >= a.E) {
-      bad = true;
-      continue;
-    }
+    if (e < 0 || e >= a.E) continue;
     s += *reinterpret_cast<const f32x4*>(a.ybuf + int64_t(p) * a.H + 4 * nq);
   }
   uint2 o;
   o.x = f32_to_bf16(s[0]) | (uint32_t(f32_to_bf16(s[1])) << 16);
   o.y = f32_to_bf16(s[2]) | (uint32_t(f32_to_bf16(s[3])) << 16);
   *reinterpret_cast<uint2*>(a.out + int64_t(t) * a.H + 4 * nq) = o;
-  if (bad && nq == 0 && a.err)
-    __hip_atomic_fetch_or(a.err, HPA_DEVERR_MOE_EXPERT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
+
+hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(moe_prepare_kernel, dim3(a.T + 1), dim3(kMoeThreads), 0, stream, a);
+  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.I / 16))), dim3(64), 0,
+                     stream, a);
+  hipLaunchKernelGGL(moe_quant_act_kernel, dim3(a.P), dim3(kMoeThreads), 0, stream, a);
+  hipLaunchKernelGGL(moe_down_kernel, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.H / 16))), dim3(64), 0,
+                     stream, a);
+  hipLaunchKernelGGL(moe_merge_kernel, dim3((a.H / 4 + kMoeThreads - 1) / kMoeThreads, a.T), dim3(kMoeThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
 
 hpa_status moe_check_shape(int32_t tokens, int32_t experts, int32_t top_k, int32_t hidden, int32_t inter) {
   if (tokens < 0 || tokens > kMoeMaxTokens) return report_status(HPA_ERR_UNSUPPORTED, "tokens %d (0 .. %d)", tokens,
@@ -392,28 +404,6 @@ hpa_status moe_check_shape(int32_t tokens, int32_t experts, int32_t top_k, int32
     return report_status(HPA_ERR_UNSUPPORTED, "tokens x top_k %lld > %d", (long long)(int64_t(tokens) * top_k),
                          kMoeMaxPairs);
   return HPA_OK;
-}
-
-hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
-  const size_t lds1 = size_t(kPairsPerBlock) * (a.H + kLdsPad);
-  const size_t lds2 = size_t(kPairsPerBlock) * (a.I + kLdsPad);
-  // rows of up to 4096 bytes take just over 64 KB of LDS: raise the kernels' limit once
-  static const hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_gate_up_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_down_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    return e;
-  }();
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(static_cast<unsigned>(int64_t(a.E) * a.PB * a.IT)), dim3(kMoeThreads),
-                     lds1, stream, a);
-  hipLaunchKernelGGL(moe_down_kernel, dim3(static_cast<unsigned>(int64_t(a.E) * a.PB * a.HT)), dim3(kMoeThreads), lds2,
-                     stream, a);
-  hipLaunchKernelGGL(moe_merge_kernel, dim3((a.H / 4 + kMoeThreads - 1) / kMoeThreads, a.T), dim3(kMoeThreads), 0,
-                     stream, a);
-  return hipGetLastError();
 }
 
 }  // namespace hpa
@@ -451,8 +441,15 @@ extern "C" hpa_status hpa_moe_fused(const void* x, const int32_t* topk_ids, cons
   a.s1 = s1;
   a.w2 = static_cast<const uint8_t*>(w2);
   a.s2 = s2;
+  a.x8 = reinterpret_cast<uint8_t*>(wb + ws.x8);
+  a.sx = reinterpret_cast<float*>(wb + ws.sx);
+  a.list = reinterpret_cast<int32_t*>(wb + ws.list);
+  a.blk = reinterpret_cast<int32_t*>(wb + ws.blk);
+  a.nblk = reinterpret_cast<int32_t*>(wb + ws.nblk);
   a.act = reinterpret_cast<float*>(wb + ws.act);
   a.amax = reinterpret_cast<float*>(wb + ws.amax);
+  a.act8 = reinterpret_cast<uint8_t*>(wb + ws.act8);
+  a.sa = reinterpret_cast<float*>(wb + ws.sa);
   a.ybuf = reinterpret_cast<float*>(wb + ws.ybuf);
   a.out = static_cast<uint16_t*>(out);
   a.err = device_error;
@@ -462,9 +459,8 @@ extern "C" hpa_status hpa_moe_fused(const void* x, const int32_t* topk_ids, cons
   a.H = hidden;
   a.I = inter;
   a.P = tokens * top_k;
-  a.PB = (tokens + 15) / 16;
-  a.IT = inter / 64;
-  a.HT = hidden / 64;
+  // pair blocks: at most one partial block per expert with pairs, and never more than pairs
+  a.BMAX = std::min<int>(a.P, (a.P + 15) / 16 + std::min(experts, a.P));
   if (launch_moe(a, stream) != hipSuccess) return report_status(HPA_ERR_LAUNCH, "MoE launch failed");
   return HPA_OK;
 }

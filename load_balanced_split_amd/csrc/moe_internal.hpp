@@ -24,26 +24,42 @@ struct MoeArgs {
   const float* s1;         // [E][2I]
   const uint8_t* w2;       // [E][H][I] E4M3
   const float* s2;         // [E][H]
+  uint8_t* x8;             // [T][H] the tokens' E4M3 codes
+  float* sx;               // [T] their scales
+  int32_t* list;           // [P] pairs grouped by expert, each group in pair order
+  int32_t* blk;            // [3][P] pair blocks of up to 16 pairs: expert, first list index, count
+  int32_t* nblk;           // [1] number of pair blocks
   float* act;              // [P][I] fp32 SwiGLU output
-  float* amax;             // [P][I / 64] largest |act| of each 64-wide slice
+  float* amax;             // [P][I / 16] largest |act| of each 16-wide slice
+  uint8_t* act8;           // [P][I] requantised activations
+  float* sa;               // [P] their scales
   float* ybuf;             // [P][H] fp32 weighted Down output of each pair
   uint16_t* out;           // [T][H] bf16
   int32_t* err;            // sticky device error word (may be null)
-  int T, E, K, H, I, P, PB, IT, HT;
+  int T, E, K, H, I, P, BMAX;
 };
 
+// Workspace arrays (byte offsets, 256-byte aligned).
 struct MoeWorkspace {
-  size_t act, amax, ybuf, total;
+  size_t x8, sx, list, blk, nblk, act, amax, act8, sa, ybuf, total;
 };
 
 inline MoeWorkspace moe_workspace(int64_t T, int64_t K, int64_t H, int64_t I) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t P = static_cast<size_t>(T * K);
   MoeWorkspace w{};
-  w.act = 0;
-  w.amax = al(P * I * 4);
-  w.ybuf = w.amax + al(P * (I / 64) * 4);
-  w.total = w.ybuf + al(P * H * 4);
+  size_t o = 0;
+  w.x8 = o;   o += al(T * H);
+  w.sx = o;   o += al(T * 4);
+  w.list = o; o += al(P * 4);
+  w.blk = o;  o += al(3 * P * 4);
+  w.nblk = o; o += al(4);
+  w.act = o;  o += al(P * I * 4);
+  w.amax = o; o += al(P * (I / 16) * 4);
+  w.act8 = o; o += al(P * I);
+  w.sa = o;   o += al(P * 4);
+  w.ybuf = o; o += al(P * H * 4);
+  w.total = o;
   return w;
 }
 

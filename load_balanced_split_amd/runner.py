@@ -219,3 +219,14 @@ class MoeStep:
 
     def output_f64(self) -> np.ndarray:
         return self.out.float().cpu().numpy().astype(np.float64)
+
+    def activations(self) -> np.ndarray:
+        """The fp32 SwiGLU outputs [T, K, I] the last call left in the workspace (after
+        the token codes and scales and the routing index, each array 256-byte aligned)."""
+        mw = self.mw
+        al = lambda x: (x + 255) // 256 * 256
+        T, K, H, I = mw.tokens, mw.top_k, mw.hidden, mw.inter
+        P = T * K
+        off = al(T * H) + al(T * 4) + al(P * 4) + al(3 * P * 4) + al(4)
+        raw = self.workspace.cpu().numpy()
+        return raw[off: off + P * I * 4].view(np.float32).reshape(T, K, I)

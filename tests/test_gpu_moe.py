@@ -51,8 +51,7 @@ def _check(mw, tokens=None, act=True):
     print(f"   max |err| {err.max():.3e}, max err/tol {ratio:.3f}, max |ref| {np.abs(ref).max():.3f}", flush=True)
     assert ratio <= 1.0
     if act:
-        ws = d.workspace.cpu().numpy()
-        a_gpu = ws[: mw.tokens * mw.top_k * mw.inter * 4].view(np.float32).reshape(mw.tokens, mw.top_k, mw.inter)
+        a_gpu = d.activations()
         for i, t in enumerate(sel):
             for k in range(mw.top_k):
                 if (i, k) in det["act"]:
