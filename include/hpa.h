@@ -375,15 +375,26 @@ hpa_status hpa_router_gemm(const void* x, const void* packed, int32_t tokens, in
  * accumulation of exact products; zero rows give zero scales and codes). A slot
  * whose expert id is outside [0, experts) adds nothing and sets
  * HPA_DEVERR_MOE_EXPERT in device_error (device int32, may be NULL).
- * Layouts (row-major, device, 16-byte aligned): x, out [T][H] bf16; topk_ids [T][K]
- * int32; topk_weights [T][K] fp32; w1 [E][2I][H] E4M3 codes (gate rows, then up
- * rows), s1 [E][2I] fp32; w2 [E][H][I] E4M3 codes, s2 [E][H] fp32. Shapes: tokens
+ * Layouts (device, 16-byte aligned): x, out [T][H] bf16; topk_ids [T][K] int32;
+ * topk_weights [T][K] fp32; w1 = W1 [E][2I][H] E4M3 codes (gate rows, then up rows)
+ * and w2 = W2 [E][H][I] as packed by hpa_moe_pack_weights; s1 [E][2I], s2 [E][H]
+ * fp32 (row-major). Shapes: tokens
  * 0 .. 1024, experts 1 .. 1024, top_k 1 .. 16, hidden and inter multiples of 128 up
  * to 4096, tokens x top_k <= 16384 (others: HPA_ERR_UNSUPPORTED, nothing launched).
  * workspace: at least hpa_moe_workspace_size bytes (token codes, the routing
  * index, the fp32 activations and their codes, the weighted per-slot results).
  * Five launches on `stream` (quantise + routing index, Gate-Up, requantise, Down,
  * merge), nothing allocated; results are deterministic. */
+/* Packs row-major E4M3 expert weights w [E][rows][cols] (device, 16-byte aligned)
+ * into the tiled order hpa_moe_fused reads (packed: device, E * rows * cols bytes,
+ * 16-byte aligned, another buffer): tile (e, rb, c) holds rows 16 rb .. + 16 and
+ * cols 128 c .. + 128 at byte ((e rows/16 + rb) cols/128 + c) * 2048; inside it, for
+ * row m and col 32 q + j (q < 4, j < 32) of the tile, lane l = m + 16 q: byte 16 l + j
+ * for j < 16, 1024 + 16 l + j - 16 otherwise -- so every 16-byte-per-lane load of a
+ * wave reads one contiguous 1 KB. rows a multiple of 16 up to 8192 (W1: 2I, W2: H),
+ * cols a multiple of 128 up to 4096 (W1: H, W2: I). Once per weight; one launch. */
+hpa_status hpa_moe_pack_weights(const void* w, int32_t experts, int32_t rows, int32_t cols, void* packed,
+                                hipStream_t stream);
 hpa_status hpa_moe_workspace_size(int32_t tokens, int32_t top_k, int32_t hidden, int32_t inter, size_t* bytes);
 hpa_status hpa_moe_fused(const void* x, const int32_t* topk_ids, const float* topk_weights, const void* w1,
                          const float* s1, const void* w2, const float* s2, int32_t tokens, int32_t experts,

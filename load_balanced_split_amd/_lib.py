@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
                                 _P, ctypes.c_size_t, _P, _I, _P],
             "hpa_kv_pack_pages": [D, _P, _P, _P, _I, _P, _P, _P, _P],
             "hpa_moe_workspace_size": [_I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
+            "hpa_moe_pack_weights": [_P, _I, _I, _I, _P, _P],
             "hpa_moe_fused": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, ctypes.c_size_t, _P, _P],
             "hpa_decode_attn_noalloc": [D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P],
             "hpa_decode_prologue": [D, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_double, _P, _P,
@@ -275,6 +276,12 @@ def hpa_router_gemm(x, packed, experts: int, passes: int, logits, top_k: int, to
                                  _ptr(topk_idx) if top_k else None, _ptr(topk_val) if top_k else None,
                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "hpa_router_gemm")
+
+
+def hpa_moe_pack_weights(w, packed, stream=None) -> None:
+    """w: uint8 E4M3 codes [E, rows, cols] (row-major) -> packed (uint8, same size)."""
+    E, rows, cols = w.shape
+    _check(lib().hpa_moe_pack_weights(_ptr(w), E, rows, cols, _ptr(packed), _stream(stream)), "hpa_moe_pack_weights")
 
 
 def hpa_moe_workspace_size(tokens: int, top_k: int, hidden: int, inter: int) -> int:

@@ -45,9 +45,9 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kMoeThreads = 256;
 constexpr int kPairsPerBlock = 16;
 constexpr int kBufDword3 = 0x00020000;
-// weight loads keep the default cache policy: the two 16-byte halves of a lane's 32
-// bytes are separate instructions over the same lines, and the second must find them
-constexpr int kPolicyWeights = 0;
+// Weights are packed (hpa_moe_pack_weights): every 16-byte-per-lane load of a wave
+// reads one contiguous 1 KB, whole lines read once, so they stream (nt).
+constexpr int kPolicyWeights = 2;
 
 __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t p = reinterpret_cast<uint64_t>(base);
@@ -59,6 +59,11 @@ __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 
 __device__ inline u32x4 wload16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), kPolicyWeights);
+}
+
+// activation codes (small, re-read by many waves): default policy
+__device__ inline u32x4 aload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
 }
 
 // fp32 -> OCP E4M3 code: nearest value, ties to even mantissa, saturating at 448.
@@ -220,8 +225,9 @@ __global__ __launch_bounds__(64) void moe_gate_up_kernel(MoeArgs a) {
   const rsrc_t rw = make_rsrc(a.w1 + int64_t(e) * 2 * a.I * a.H, static_cast<uint32_t>(int64_t(2) * a.I * a.H));
   const rsrc_t rx = make_rsrc(a.x8, static_cast<uint32_t>(int64_t(a.T) * a.H));
   const int g0 = ib * 16;
-  const uint32_t og = static_cast<uint32_t>((g0 + m16) * a.H + 32 * q);
-  const uint32_t ou = static_cast<uint32_t>((a.I + g0 + m16) * a.H + 32 * q);
+  // packed tiles of row block rb: 2 KB per 128-wide chunk, chunks consecutive
+  const uint32_t og = static_cast<uint32_t>(ib * nch * 2048 + 16 * lane);
+  const uint32_t ou = static_cast<uint32_t>((a.I / 16 + ib) * nch * 2048 + 16 * lane);
   // padding pair columns read past the buffer: zeros
   const uint32_t ox = valid ? static_cast<uint32_t>(t * a.H + 32 * q) : 0x80000000u;
   f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = accg;
@@ -229,12 +235,13 @@ __global__ __launch_bounds__(64) void moe_gate_up_kernel(MoeArgs a) {
   u32x4 ag[kDepth][2], au[kDepth][2], bx[kDepth][2];
   auto load = [&](int slot, int c) {
     const uint32_t sc = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(128 * c));
-    ag[slot][0] = wload16(rw, og, sc);
-    ag[slot][1] = wload16(rw, og + 16, sc);
-    au[slot][0] = wload16(rw, ou, sc);
-    au[slot][1] = wload16(rw, ou + 16, sc);
-    bx[slot][0] = wload16(rx, ox, sc);
-    bx[slot][1] = wload16(rx, ox + 16, sc);
+    const uint32_t st = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(2048 * c));
+    ag[slot][0] = wload16(rw, og, st);
+    ag[slot][1] = wload16(rw, og + 1024, st);
+    au[slot][0] = wload16(rw, ou, st);
+    au[slot][1] = wload16(rw, ou + 1024, st);
+    bx[slot][0] = aload16(rx, ox, sc);
+    bx[slot][1] = aload16(rx, ox + 16, sc);
   };
   auto mul = [&](int slot) {
     const i32x8 B = operand(bx[slot][0], bx[slot][1]);
@@ -317,17 +324,18 @@ __global__ __launch_bounds__(64) void moe_down_kernel(MoeArgs a) {
   const rsrc_t rw = make_rsrc(a.w2 + int64_t(e) * a.H * a.I, static_cast<uint32_t>(int64_t(a.H) * a.I));
   const rsrc_t ra = make_rsrc(a.act8, static_cast<uint32_t>(int64_t(a.P) * a.I));
   const int n0 = nb * 16;
-  const uint32_t ow = static_cast<uint32_t>((n0 + m16) * a.I + 32 * q);
+  const uint32_t ow = static_cast<uint32_t>(nb * nch * 2048 + 16 * lane);   // packed row block nb
   const uint32_t oa = valid ? static_cast<uint32_t>(p * a.I + 32 * q) : 0x80000000u;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int kDepth = 4;
   u32x4 aw[kDepth][2], ba[kDepth][2];
   auto load = [&](int slot, int c) {
     const uint32_t sc = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(128 * c));
-    aw[slot][0] = wload16(rw, ow, sc);
-    aw[slot][1] = wload16(rw, ow + 16, sc);
-    ba[slot][0] = wload16(ra, oa, sc);
-    ba[slot][1] = wload16(ra, oa + 16, sc);
+    const uint32_t st = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(2048 * c));
+    aw[slot][0] = wload16(rw, ow, st);
+    aw[slot][1] = wload16(rw, ow + 1024, st);
+    ba[slot][0] = aload16(ra, oa, sc);
+    ba[slot][1] = aload16(ra, oa + 16, sc);
   };
   auto mul = [&](int slot) {
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(aw[slot][0], aw[slot][1]),
@@ -375,6 +383,25 @@ __global__ __launch_bounds__(kMoeThreads) void moe_merge_kernel(MoeArgs a) {
   *reinterpret_cast<uint2*>(a.out + int64_t(t) * a.H + 4 * nq) = o;
 }
 
+// Packs row-major E4M3 weights [E][N][K] into MFMA-operand tiles: tile (e, rb, c) =
+// rows 16 rb .. + 16 and dims 128 c .. + 128, at ((e N/16 + rb) K/128 + c) 2048 bytes;
+// inside it lane l = m + 16 q (row m) holds dims 128 c + 32 q .. + 32, its first 16
+// bytes at 16 l and its last 16 at 1024 + 16 l. One thread per 16-byte piece.
+__global__ __launch_bounds__(kMoeThreads) void moe_pack_kernel(const uint8_t* __restrict__ w, int E, int N, int K,
+                                                               uint8_t* __restrict__ packed) {
+  const int64_t o = int64_t(blockIdx.x) * kMoeThreads + threadIdx.x;     // output piece
+  const int64_t total = int64_t(E) * N * K / 16;
+  if (o >= total) return;
+  const int64_t tile = o / 128;
+  const int j = static_cast<int>(o % 128), half = j / 64, l = j % 64;
+  const int nchunk = K / 128;
+  const int c = static_cast<int>(tile % nchunk);
+  const int64_t erb = tile / nchunk;                                      // e * N/16 + rb
+  const int64_t row = erb * 16 + (l % 16);                                 // e * N + 16 rb + m
+  const int64_t col = int64_t(128) * c + 32 * (l / 16) + 16 * half;
+  *reinterpret_cast<u32x4*>(packed + 16 * o) = *reinterpret_cast<const u32x4*>(w + row * K + col);
+}
+
 }  // namespace
 
 hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
@@ -407,6 +434,25 @@ hpa_status moe_check_shape(int32_t tokens, int32_t experts, int32_t top_k, int32
 }
 
 }  // namespace hpa
+
+extern "C" hpa_status hpa_moe_pack_weights(const void* w, int32_t experts, int32_t rows, int32_t cols, void* packed,
+                                            hipStream_t stream) {
+  using namespace hpa;
+  if (experts < 1 || experts > kMoeMaxExperts || rows < 16 || rows % 16 != 0 || rows > 2 * kMoeMaxInter ||
+      cols < 128 || cols % 128 != 0 || cols > kMoeMaxHidden)
+    return report_status(HPA_ERR_UNSUPPORTED, "experts %d, rows %d, cols %d (rows a multiple of 16 up to %d, cols "
+                         "a multiple of 128 up to %d)", experts, rows, cols, 2 * kMoeMaxInter, kMoeMaxHidden);
+  if (!w || !packed) return report_status(HPA_ERR_INVALID_ARG, "w or packed is NULL");
+  if (reinterpret_cast<uintptr_t>(w) % 16 != 0 || reinterpret_cast<uintptr_t>(packed) % 16 != 0)
+    return report_status(HPA_ERR_INVALID_ARG, "w and packed must be 16-byte aligned");
+  if (w == packed) return report_status(HPA_ERR_INVALID_ARG, "w and packed must not be the same buffer");
+  const int64_t pieces = int64_t(experts) * rows * cols / 16;
+  hipLaunchKernelGGL(moe_pack_kernel, dim3(static_cast<unsigned>((pieces + kMoeThreads - 1) / kMoeThreads)),
+                     dim3(kMoeThreads), 0, stream, static_cast<const uint8_t*>(w), experts, rows, cols,
+                     static_cast<uint8_t*>(packed));
+  if (hipGetLastError() != hipSuccess) return report_status(HPA_ERR_LAUNCH, "MoE pack launch failed");
+  return HPA_OK;
+}
 
 extern "C" hpa_status hpa_moe_workspace_size(int32_t tokens, int32_t top_k, int32_t hidden, int32_t inter,
                                              size_t* bytes) {

@@ -204,8 +204,13 @@ class MoeStep:
         self.x = up(mw.x.view(np.int16)).view(torch.bfloat16)
         self.ids = up(mw.ids)
         self.weights = up(mw.weights)
-        self.w1, self.s1 = up(mw.w1), up(mw.s1)
-        self.w2, self.s2 = up(mw.w2), up(mw.s2)
+        # the E4M3 weights row-major as drawn, then packed once into the tiled order
+        self.w1_rows, self.s1 = up(mw.w1), up(mw.s1)
+        self.w2_rows, self.s2 = up(mw.w2), up(mw.s2)
+        self.w1 = torch.empty_like(self.w1_rows)
+        self.w2 = torch.empty_like(self.w2_rows)
+        _lib.hpa_moe_pack_weights(self.w1_rows, self.w1)
+        _lib.hpa_moe_pack_weights(self.w2_rows, self.w2)
         self.out = torch.empty((mw.tokens, mw.hidden), dtype=torch.bfloat16, device=dev)
         ws = _lib.hpa_moe_workspace_size(mw.tokens, mw.top_k, mw.hidden, mw.inter)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)

@@ -98,3 +98,26 @@ def test_moe_edge_cases():
     ref = om.fused_moe(mw.x, mw.ids, mw.weights, mw.w1, mw.s1, mw.w2, mw.s2)
     assert np.all(np.abs(got - ref) <= ATOL + RTOL * np.abs(ref))
     assert not got[3].any()
+
+
+def test_moe_weight_packing_layout():
+    """hpa_moe_pack_weights places byte (e, r, col) of a row-major [E][rows][cols] array
+    at tile ((e rows/16 + r/16) cols/128 + col/128) * 2048, lane l = r%16 + 16 q with
+    q = (col%128)/32, byte 16 l + j (j = col%32 < 16) or 1024 + 16 l + j - 16."""
+    E, R, C = 3, 48, 384
+    w = np.random.default_rng(1).integers(0, 256, size=(E, R, C), dtype=np.uint8)
+    wd = torch.from_numpy(w).cuda()
+    packed = torch.empty_like(wd)
+    _lib.hpa_moe_pack_weights(wd, packed)
+    torch.cuda.synchronize()
+    got = packed.cpu().numpy().reshape(-1)
+    e, r, col = np.meshgrid(np.arange(E), np.arange(R), np.arange(C), indexing="ij")
+    tile = (e * (R // 16) + r // 16) * (C // 128) + col // 128
+    lane = r % 16 + 16 * ((col % 128) // 32)
+    j = col % 32
+    dest = tile * 2048 + np.where(j < 16, 16 * lane + j, 1024 + 16 * lane + j - 16)
+    assert np.array_equal(np.sort(dest.reshape(-1)), np.arange(E * R * C))   # a permutation
+    assert np.array_equal(got[dest], w)
+    with pytest.raises(RuntimeError):
+        _lib.hpa_moe_pack_weights(torch.empty((1, 24, 128), dtype=torch.uint8, device="cuda"),
+                                  torch.empty((1, 24, 128), dtype=torch.uint8, device="cuda"))
