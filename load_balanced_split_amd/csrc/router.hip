@@ -27,11 +27,12 @@
 // (router_gemm_tiled_kernel): 128 x 128 workgroup tiles staged through LDS (below).
 // Rows past the last token read zeros (buffer bounds) and are not stored.
 //
-// Reduction and top-k (router_topk_kernel, one workgroup per token): the partial
-// sums of a logit are added in partial order and the logits stored; the top-k
-// (larger value first, equal values to the lower expert index) by ranks of 64-bit
-// (value, expert) keys in LDS, within 64-expert segments and then among the
-// segments' k largest.
+// Reduction and top-k: the partial sums of a logit are added in partial order and
+// the logits stored; the top-k (larger value first, equal values to the lower
+// expert index) over 64-bit (value, expert) keys. Few tokens (router_topk_wg_kernel,
+// one workgroup per token): ranks of the keys in LDS, within 64-expert segments and
+// then among the segments' k largest. Many tokens (router_topk_kernel, one wave per
+// token): k rounds of a wave-wide maximum.
 #include "router_internal.hpp"
 
 namespace hpa {
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* x, con
 // stage a K-step reads was written before the previous barrier, the stage it writes
 // was last read before it.
 template <int PASSES>
-__global__ __launch_bounds__(256) void router_gemm_tiled_kernel(RouterArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_gemm_tiled_kernel(RouterArgs a) {
   constexpr int kWPieces = PASSES == 2 ? 4 : 2;     // 16-byte weight pieces per thread per K-step
   constexpr int kXPieces = 2;
   constexpr int kXBase = 16384;                     // x tiles after the 8 weight pairs
@@ -252,12 +253,17 @@ __global__ __launch_bounds__(256) void router_gemm_tiled_kernel(RouterArgs a) {
     wsrc[i] = static_cast<uint32_t>(int64_t(eb0 + eb) * nkc * 2048 + r);
     wdst[i] = static_cast<uint32_t>(eb * per * 16 + r);       // LDS: the staged halves packed
   }
+  // x piece c: token block c / 64, fragment lane l = c % 64 (token 16 (c / 64) + l % 16,
+  // dims 8 (l / 16) .. + 8), written at 16 l of its block's 1 KB: a wave's LDS stores
+  // are one contiguous 1 KB (no bank conflicts), its global loads the same 16 rows x
+  // 64 bytes in any lane order
 #pragma unroll
   for (int i = 0; i < kXPieces; ++i) {
     const int c = i * 256 + tid;
-    const int t = c / 4, jj = c % 4;
+    const int tb = c / 64, l = c % 64;
+    const int t = 16 * tb + l % 16, jj = l / 16;
     xsrc[i] = static_cast<uint32_t>((t * a.H + 8 * jj) * 2);
-    xdst[i] = static_cast<uint32_t>(kXBase + (t / 16) * 1024 + (16 * jj + t % 16) * 16);
+    xdst[i] = static_cast<uint32_t>(kXBase + tb * 1024 + 16 * l);
   }
   struct Stg {
     u32x4 w[kWPieces], x[kXPieces];
@@ -304,31 +310,37 @@ __global__ __launch_bounds__(256) void router_gemm_tiled_kernel(RouterArgs a) {
           acc[ie][it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al[ie]), as_bf16x8(b[it]), acc[ie][it], 0, 0, 0);
       }
   };
+  // A ring of kDepth register stages: the global loads of K-step kc + kDepth go out
+  // while K-step kc is multiplied, kDepth - 1 K-steps before they are written to LDS
+  // (loads past the range are clamped to its last K-step: issued, in bounds, unused).
+  // Ring slots and LDS stages are compile-time indices: the loop is unrolled by
+  // kUnroll, a multiple of both kDepth and 2, and the last partial round is guarded
+  // by a uniform test around each whole step.
+  constexpr int kDepth = 3;
+  constexpr int kUnroll = kDepth % 2 == 0 ? kDepth : 2 * kDepth;
   if (c0 < c1) {
-    Stg ga, gb;
-    gload(ga, c0);
-    gload(gb, min(c0 + 1, c1 - 1));
-    swrite(ga, 0);
+    Stg g[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) gload(g[d], min(c0 + d, c1 - 1));
+    swrite(g[0], 0);
     barrier();
+    auto step = [&](int kc, int d) {
+      // LDS stage d % 2 holds K-step kc; ring slot d % kDepth has been written to it
+      gload(g[d % kDepth], min(kc + kDepth, c1 - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(d % 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kc + 1 < c1) swrite(g[(d + 1) % kDepth], (d + 1) % 2);
+      barrier();
+    };
     int kc = c0;
-    for (; kc + 2 <= c1; kc += 2) {
-      // stage 0 holds K-step kc, gb holds kc + 1 (the scheduling barriers keep each
-      // K-step's global loads ahead of the products before it is written to LDS)
-      gload(ga, min(kc + 2, c1 - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(0);
-      __builtin_amdgcn_sched_barrier(0);
-      swrite(gb, 1);
-      barrier();
-      // stage 1 holds kc + 1, ga holds kc + 2
-      gload(gb, min(kc + 3, c1 - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(1);
-      __builtin_amdgcn_sched_barrier(0);
-      swrite(ga, 0);
-      barrier();
+    for (; kc + kUnroll <= c1; kc += kUnroll) {
+#pragma unroll
+      for (int d = 0; d < kUnroll; ++d) step(kc + d, d);
     }
-    if (kc < c1) compute(0);
+#pragma unroll
+    for (int d = 0; d < kUnroll; ++d)
+      if (kc + d < c1) step(kc + d, d);
   }
 #pragma unroll
   for (int ie = 0; ie < 4; ++ie)
@@ -356,7 +368,14 @@ __device__ inline float key_value(uint64_t k) {
 }
 __device__ inline int key_expert(uint64_t k) { return int(~uint32_t(k)); }
 
-// One workgroup per token, Q experts per thread (E <= 256 Q): every logit's partial
+// Many tokens: one wave per token (four per workgroup), 4 Q experts per lane:
+// lane l holds experts 256 j + 4 l + r (j < Q, r < 4). Every logit is the sum of its
+// partial sums in partial order (the loads of a batch of partials issued together,
+// at clamped in-bounds addresses), stored as 16-byte rows. The top-k then takes k
+// rounds of a wave-wide maximum over the lanes' largest remaining keys; keys are
+// distinct, so exactly one lane owns each maximum and drops it, and lane r keeps
+// the r-th result for one store at the end.
+// Few tokens: one workgroup per token, Q experts per thread (E <= 256 Q): every logit's partial
 // sums (loads of a batch issued together at clamped, in-bounds addresses, added in
 // partial order), the logits stored; then the top-k by ranks over the keys in LDS
 // (keys are distinct, so a rank is the count of larger keys). Pass 1: each key's
@@ -365,14 +384,14 @@ __device__ inline int key_expert(uint64_t k) { return int(~uint32_t(k)); }
 // which for the global top-k is its global rank and for every other survivor is at
 // least k; those below k are written at their rank.
 template <int Q>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* part, int T, int E, int slots,
+__global__ __launch_bounds__(256) void router_topk_wg_kernel(const float* part, int T, int E, int slots,
                                                           RouterArgs a) {
   constexpr int kBatch = 32 / Q;
   constexpr int kSegs = kRouterMaxExperts / 64;
   __shared__ uint64_t lk[kRouterMaxExperts];
   __shared__ uint64_t sk[kSegs * kRouterMaxTopK];
   const int t = blockIdx.x;
-    const int64_t stride = int64_t(T) * E;
+  const int64_t stride = int64_t(T) * E;
   const float* base = part + int64_t(t) * E;
   float v[Q];
   int id[Q];
@@ -448,6 +467,99 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* part, int
   }
 }
 
+// max of a 64-bit key with the key of another lane of its row (DPP control CTRL: a
+// permutation within quads or a rotation within the row of 16, so every source lane
+// exists)
+template <int CTRL>
+__device__ inline uint64_t dpp_max(uint64_t x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(x)), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(x >> 32)), CTRL, 0xF, 0xF, false);
+  const uint64_t y = (uint64_t(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+  return y > x ? y : x;
+}
+
+// the wave's largest key, in every lane: the maximum within rows of 16 (quad swaps
+// 1 and 2, then row rotations by 4 and 8), then across the four rows' first lanes
+__device__ inline uint64_t wave_max_key(uint64_t x) {
+  x = dpp_max<0xB1>(x);     // quad_perm [1, 0, 3, 2]
+  x = dpp_max<0x4E>(x);     // quad_perm [2, 3, 0, 1]
+  x = dpp_max<0x124>(x);    // row_ror 4
+  x = dpp_max<0x128>(x);    // row_ror 8
+  uint64_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x)), 16 * r);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x >> 32)), 16 * r);
+    const uint64_t y = (uint64_t(hi) << 32) | lo;
+    m = y > m ? y : m;
+  }
+  return m;
+}
+
+template <int Q>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* part, int T, int E, int slots,
+                                                          RouterArgs a) {
+  constexpr int kBatch = 32 / Q;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;                                 // whole waves
+  const int64_t stride = int64_t(T) * E;
+  const float* base = part + int64_t(t) * E;
+  f32x4 v[Q];
+  int e0[Q];
+#pragma unroll
+  for (int j = 0; j < Q; ++j) {
+    e0[j] = 256 * j + 4 * lane;
+    v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int s0 = 0; s0 < slots; s0 += kBatch) {
+    f32x4 pv[Q][kBatch];
+#pragma unroll
+    for (int j = 0; j < Q; ++j)
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        pv[j][i] = *reinterpret_cast<const f32x4*>(base + min(s0 + i, slots - 1) * stride + min(e0[j], E - 4));
+    __builtin_amdgcn_sched_barrier(0);       // every load of the batch before the first sum
+#pragma unroll
+    for (int j = 0; j < Q; ++j)
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (s0 + i < slots) v[j] += pv[j][i];
+      }
+  }
+  uint64_t key[4 * Q];
+#pragma unroll
+  for (int j = 0; j < Q; ++j) {
+    const bool ok = e0[j] < E;                        // E is a multiple of 16: all four or none
+    if (ok) *reinterpret_cast<f32x4*>(a.logits + int64_t(t) * E + e0[j]) = v[j];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) key[4 * j + r] = ok ? topk_key(v[j][r], e0[j] + r) : 0;
+  }
+  const int k = a.top_k;
+  uint64_t mine = 0;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = 0;
+    int bi = 0;
+#pragma unroll
+    for (int c = 0; c < 4 * Q; ++c)
+      if (key[c] > best) {
+        best = key[c];
+        bi = c;
+      }
+    const uint64_t m = wave_max_key(best);
+    if (best == m) {                                  // the owner of this maximum
+#pragma unroll
+      for (int c = 0; c < 4 * Q; ++c)
+        if (c == bi) key[c] = 0;
+    }
+    if (lane == r) mine = m;
+  }
+  if (lane < k) {
+    a.topk_idx[int64_t(t) * k + lane] = key_expert(mine);
+    a.topk_val[int64_t(t) * k + lane] = key_value(mine);
+  }
+}
+
 template <int ME, int NT, bool WX>
 void gemm_launch(const RouterArgs& a, hipStream_t stream) {
   if (a.passes == 2)
@@ -479,11 +591,22 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
   else gemm_launch<2, 4, false>(a, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.E <= 256) hipLaunchKernelGGL(router_topk_kernel<1>, dim3(a.T), dim3(256), 0, stream, a.part, a.T, a.E,
+  if (a.T <= kRouterWaveTopkMinTokens) {
+    // few tokens: the ranking of one token spread over a workgroup is the shorter chain
+    if (a.E <= 256) hipLaunchKernelGGL(router_topk_wg_kernel<1>, dim3(a.T), dim3(256), 0, stream, a.part, a.T, a.E,
+                         a.p.partial_slots, a);
+    else if (a.E <= 512) hipLaunchKernelGGL(router_topk_wg_kernel<2>, dim3(a.T), dim3(256), 0, stream, a.part, a.T,
+                              a.E, a.p.partial_slots, a);
+    else hipLaunchKernelGGL(router_topk_wg_kernel<4>, dim3(a.T), dim3(256), 0, stream, a.part, a.T, a.E,
+                            a.p.partial_slots, a);
+    return hipGetLastError();
+  }
+  const dim3 grid((a.T + 3) / 4);
+  if (a.E <= 256) hipLaunchKernelGGL(router_topk_kernel<1>, grid, dim3(256), 0, stream, a.part, a.T, a.E,
                        a.p.partial_slots, a);
-  else if (a.E <= 512) hipLaunchKernelGGL(router_topk_kernel<2>, dim3(a.T), dim3(256), 0, stream, a.part, a.T, a.E,
+  else if (a.E <= 512) hipLaunchKernelGGL(router_topk_kernel<2>, grid, dim3(256), 0, stream, a.part, a.T, a.E,
                        a.p.partial_slots, a);
-  else hipLaunchKernelGGL(router_topk_kernel<4>, dim3(a.T), dim3(256), 0, stream, a.part, a.T, a.E,
+  else hipLaunchKernelGGL(router_topk_kernel<4>, grid, dim3(256), 0, stream, a.part, a.T, a.E,
                        a.p.partial_slots, a);
   return hipGetLastError();
 }

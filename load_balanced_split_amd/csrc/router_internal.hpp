@@ -19,6 +19,7 @@ constexpr int kRouterMaxTokens = 1 << 20;
 constexpr int kRouterTargetWaves = 4096;   // 4 per SIMD of 256 compute units
 constexpr int kRouterTiledMinTokens = 256; // above this, LDS-staged 128 x 128 tiles
 constexpr int kRouterTiledTargetWgs = 512; // two such workgroups per compute unit
+constexpr int kRouterWaveTopkMinTokens = 512;  // above this, one wave (not one workgroup) per token's top-k
 struct RouterPlan {
   int me, nt;            // 16-expert blocks and 16-token blocks per wave
   int wx;                // 1: a workgroup's 4 waves take 4 expert groups of one K range (they

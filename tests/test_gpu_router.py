@@ -104,9 +104,20 @@ def test_router_edge_cases():
     for t in range(20):
         pos = [list(idx[t]).index(e) for e in (3, 7, 30)]
         assert pos == sorted(pos)
-    # top_k == experts, top_k == 0, and a second run is bit-identical
+    # the same with enough tokens for the one-wave-per-token top-k
+    rw = inputs.router_workload(600, 32, 256, seed=19)
+    rw.w[7] = rw.w[3]
+    rw.w[30] = rw.w[3]
+    r, (logits, idx, _) = run(rw, 2, top_k=32)
+    assert np.array_equal(logits[:, 3], logits[:, 7]) and np.array_equal(logits[:, 3], logits[:, 30])
+    for t in range(0, 600, 37):
+        pos = [list(idx[t]).index(e) for e in (3, 7, 30)]
+        assert pos == sorted(pos)
+    # top_k == experts, top_k == 0 (both top-k kernels), and a second run is bit-identical
     check(inputs.router_workload(3, 16, 64, seed=1), 2, top_k=16)
     check(inputs.router_workload(3, 16, 64, seed=1), 2, top_k=0)
+    check(inputs.router_workload(700, 16, 64, seed=4), 2, top_k=16)
+    check(inputs.router_workload(700, 16, 64, seed=4), 2, top_k=0)
     rw = inputs.router_workload(100, 256, 1024, seed=2)
     r, (l_a, i_a, _) = run(rw, 2)
     r.run(2)
