@@ -107,7 +107,6 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
   __shared__ float red[4];
   __shared__ int cnt[kMoeMaxExperts + 1];
   __shared__ int run[kMoeMaxExperts];
-  __shared__ int chunk[kMoeThreads];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (blockIdx.x < static_cast<unsigned>(a.T)) {
     const int t = blockIdx.x;
@@ -153,11 +152,24 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
   // routing index: counts per expert, their prefix (list offsets) and the pair blocks
   for (int e = tid; e < a.E; e += kMoeThreads) cnt[e] = 0;
   __syncthreads();
+  // the ids are read in batches of 16 per thread, all loads of a batch issued together
+  constexpr int kIdBatch = 16;
   bool bad = false;
-  for (int p = tid; p < a.P; p += kMoeThreads) {
-    const int e = a.ids[p];
-    if (e >= 0 && e < a.E) atomicAdd(&cnt[e], 1);
-    else bad = true;
+  for (int base = 0; base < a.P; base += kIdBatch * kMoeThreads) {
+    int v[kIdBatch];
+#pragma unroll
+    for (int i = 0; i < kIdBatch; ++i) {
+      const int p = base + i * kMoeThreads + tid;
+      v[i] = p < a.P ? a.ids[p] : 0;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kIdBatch; ++i) {
+      if (base + i * kMoeThreads >= a.P) break;               // uniform
+      if (base + i * kMoeThreads + tid >= a.P) continue;
+      if (v[i] >= 0 && v[i] < a.E) atomicAdd(&cnt[v[i]], 1);
+      else bad = true;
+    }
   }
   if (bad && a.err) __hip_atomic_fetch_or(a.err, HPA_DEVERR_MOE_EXPERT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -191,24 +203,38 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
     if (lane == 0) *a.nblk = bcarry;
   }
   __syncthreads();
-  // place the pairs, 256 at a time in pair order: rank = earlier pairs of the same expert
-  for (int base = 0; base < a.P; base += kMoeThreads) {
-    const int p = base + tid;
-    int e = p < a.P ? a.ids[p] : -1;
-    if (e >= a.E) e = -1;
-    chunk[tid] = e;
-    __syncthreads();
-    int rank = 0, slot = 0;
-    if (e >= 0) {
-      for (int j = 0; j < tid; ++j) rank += chunk[j] == e;
-      slot = run[e] + rank;
+  // place the pairs in pair order, 64 at a time by wave 0: the lanes holding the same
+  // expert are found by matching the bits of expert + 1 (0: skipped) with ballots; a
+  // pair's slot is its expert's running count plus the matching lanes below it, and
+  // the lowest of those lanes advances the count (LDS accesses of a wave stay in order)
+  if (tid < 64) {
+    for (int base = 0; base < a.P; base += kIdBatch * 64) {
+      int v[kIdBatch];
+#pragma unroll
+      for (int i = 0; i < kIdBatch; ++i) {
+        const int p = base + 64 * i + lane;
+        v[i] = p < a.P ? a.ids[p] : -1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kIdBatch; ++i) {
+        if (base + 64 * i >= a.P) break;                     // uniform
+        const int p = base + 64 * i + lane;
+        const int e = v[i] >= 0 && v[i] < a.E ? v[i] : -1;
+        const uint32_t key = static_cast<uint32_t>(e + 1);
+        uint64_t same = ~0ull;
+#pragma unroll
+        for (int b = 0; b < 11; ++b) {                       // kMoeMaxExperts + 1 < 2^11
+          const uint64_t ones = __ballot((key >> b) & 1u);
+          same &= ((key >> b) & 1u) ? ones : ~ones;
+        }
+        const uint64_t below = same & ((1ull << lane) - 1ull);
+        if (e >= 0) {
+          a.list[run[e] + __popcll(below)] = p;
+          if (below == 0) run[e] += __popcll(same);
+        }
+      }
     }
-    __syncthreads();
-    if (e >= 0) {
-      a.list[slot] = p;
-      atomicAdd(&run[e], 1);
-    }
-    __syncthreads();
   }
 }
 
@@ -289,11 +315,12 @@ __global__ __launch_bounds__(64) void moe_gate_up_kernel(MoeArgs a) {
 __global__ __launch_bounds__(kMoeThreads) void moe_quant_act_kernel(MoeArgs a) {
   __shared__ float red[4];
   const int p = blockIdx.x;
-  const int e = a.ids[p];
-  if (e < 0 || e >= a.E) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float amax = 0.f;
-  for (int j = tid; j < a.I / 16; j += kMoeThreads) amax = fmaxf(amax, a.amax[int64_t(p) * (a.I / 16) + j]);
+  static_assert(kMoeMaxInter / 16 <= kMoeThreads, "one slice maximum per thread");
+  // the id and the slice maxima (one per thread) are loaded together
+  const int e = a.ids[p];
+  float amax = tid < a.I / 16 ? a.amax[int64_t(p) * (a.I / 16) + tid] : 0.f;
+  if (e < 0 || e >= a.E) return;                    // uniform: the whole block
   amax = wave_max(amax);
   if (lane == 0) red[wave] = amax;
   __syncthreads();
@@ -370,13 +397,20 @@ __global__ __launch_bounds__(kMoeThreads) void moe_merge_kernel(MoeArgs a) {
   const int t = blockIdx.y;
   const int nq = blockIdx.x * kMoeThreads + threadIdx.x;     // 4-dim piece
   if (4 * nq >= a.H) return;
+  // all ids, then all K rows, loaded before the first sum (two round trips); a row of
+  // a skipped slot is loaded (it is in the workspace) but not added
+  int e[kMoeMaxTopK];
+  f32x4 y[kMoeMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMoeMaxTopK; ++k) e[k] = k < a.K ? a.ids[t * a.K + k] : -1;
+#pragma unroll
+  for (int k = 0; k < kMoeMaxTopK; ++k)
+    y[k] = *reinterpret_cast<const f32x4*>(a.ybuf + int64_t(t * a.K + min(k, a.K - 1)) * a.H + 4 * nq);
+  __builtin_amdgcn_sched_barrier(0);
   f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < a.K; ++k) {
-    const int p = t * a.K + k;
-    const int e = a.ids[p];
-    if (e < 0 || e >= a.E) continue;
-    s += *reinterpret_cast<const f32x4*>(a.ybuf + int64_t(p) * a.H + 4 * nq);
-  }
+#pragma unroll
+  for (int k = 0; k < kMoeMaxTopK; ++k)
+    if (e[k] >= 0 && e[k] < a.E) s += y[k];
   uint2 o;
   o.x = f32_to_bf16(s[0]) | (uint32_t(f32_to_bf16(s[1])) << 16);
   o.y = f32_to_bf16(s[2]) | (uint32_t(f32_to_bf16(s[3])) << 16);
