@@ -108,6 +108,14 @@ def pmc_main(args):
             r.run(passes)
         torch.cuda.synchronize()
         del r
+    # the fused FP8 MoE layer at its decode batch sizes (weights packed once)
+    from load_balanced_split_amd.runner import MoeStep
+    for T in MOE_TOKENS:
+        m = MoeStep(inputs.moe_workload(T, seed=T, **MOE_SHAPE))
+        for _ in range(3):
+            m.run()
+        torch.cuda.synchronize()
+        del m
     print(json.dumps({"pmc_run": True, "workload": args.workload}), flush=True)
 
 

@@ -51,7 +51,8 @@ def short_name(name: str) -> str:
     """Library kernels as name<template args> without spaces (attn_fused_kernel<false,true>
     is the E4M3-less fused kernel with the in-kernel merge); calibration kernels tagged."""
     name = re.sub(r"\((?:hpa::)?(?:\(anonymous namespace\)::)?(\w+)\)", r"(\1)", name)   # enum casts
-    m = re.search(r"(attn_\w+_kernel|merge_kernel|plan_kernel|prologue_kernel|router_\w+_kernel|stream_read_kernel)"
+    m = re.search(r"(attn_\w+_kernel|merge_kernel|plan_kernel|prologue_kernel|router_\w+_kernel|moe_\w+_kernel|"
+                  r"stream_read_kernel)"
                   r"(<[^>]*>)?", name)
     if m:
         return m.group(1) + (m.group(2) or "").replace(" ", "")
