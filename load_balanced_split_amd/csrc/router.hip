@@ -228,7 +228,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int kXPieces = 2;
   constexpr int kXBase = 16384;                     // x tiles after the 8 weight pairs
   constexpr int kStage = 16384 + 8192;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+  constexpr int kStages = 3;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
   const int we = wave & 1, wt = wave >> 1;
@@ -291,48 +292,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int ie = 0; ie < 4; ++ie)
 #pragma unroll
     for (int it = 0; it < 4; ++it) acc[ie][it] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int stage) {
-    const uint8_t* st = lds + stage * kStage;
+  // a wave's MFMA operands of one K-step: its 4 expert blocks (hi, lo) and 4 token blocks
+  struct Frag {
     u32x4 ah[4], al[4], b[4];
+  };
+  auto fread = [&](Frag& f, int stage) {
+    const uint8_t* st = lds + stage * kStage;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pair = (4 * we + i) * (PASSES == 2 ? 2048 : 1024);
-      ah[i] = *reinterpret_cast<const u32x4*>(st + pair + 16 * lane);
-      if (PASSES == 2) al[i] = *reinterpret_cast<const u32x4*>(st + pair + 1024 + 16 * lane);
-      b[i] = *reinterpret_cast<const u32x4*>(st + kXBase + (4 * wt + i) * 1024 + 16 * lane);
+      f.ah[i] = *reinterpret_cast<const u32x4*>(st + pair + 16 * lane);
+      if (PASSES == 2) f.al[i] = *reinterpret_cast<const u32x4*>(st + pair + 1024 + 16 * lane);
+      f.b[i] = *reinterpret_cast<const u32x4*>(st + kXBase + (4 * wt + i) * 1024 + 16 * lane);
     }
+  };
+  // all hi products, then all lo products: the two products into one accumulator
+  // are 16 MFMAs apart, so none waits for the one before it
+  auto mfma = [&](const Frag& f) {
 #pragma unroll
     for (int ie = 0; ie < 4; ++ie)
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        acc[ie][it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah[ie]), as_bf16x8(b[it]), acc[ie][it], 0, 0, 0);
-        if (PASSES == 2)
-          acc[ie][it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al[ie]), as_bf16x8(b[it]), acc[ie][it], 0, 0, 0);
-      }
-  };
-  // A ring of kDepth register stages: the global loads of K-step kc + kDepth go out
-  // while K-step kc is multiplied, kDepth - 1 K-steps before they are written to LDS
-  // (loads past the range are clamped to its last K-step: issued, in bounds, unused).
-  // Ring slots and LDS stages are compile-time indices: the loop is unrolled by
-  // kUnroll, a multiple of both kDepth and 2, and the last partial round is guarded
-  // by a uniform test around each whole step.
-  constexpr int kDepth = 3;
-  constexpr int kUnroll = kDepth % 2 == 0 ? kDepth : 2 * kDepth;
-  if (c0 < c1) {
-    Stg g[kDepth];
+      for (int it = 0; it < 4; ++it)
+        acc[ie][it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.ah[ie]), as_bf16x8(f.b[it]), acc[ie][it], 0, 0, 0);
+    if (PASSES == 2) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) gload(g[d], min(c0 + d, c1 - 1));
-    swrite(g[0], 0);
+      for (int ie = 0; ie < 4; ++ie)
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+          acc[ie][it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.al[ie]), as_bf16x8(f.b[it]), acc[ie][it], 0, 0, 0);
+    }
+  };
+  // Three LDS stages and two fragment sets: while K-step kc is multiplied from
+  // registers, the fragments of kc + 1 are read from LDS (written one K-step earlier)
+  // and K-step kc + 2 is written from one register stage, whose global loads went
+  // out one K-step earlier (loads past the range are clamped to its last K-step:
+  // issued, in bounds, unused). One barrier per K-step: the stage written at kc was
+  // last read at kc - 2, the stage read at kc was written at kc - 1. Stage and
+  // fragment indices are compile-time: the loop is unrolled by 6, and the last
+  // partial round is guarded by a uniform test around each whole step.
+  if (c0 < c1) {
+    Stg g;
+    gload(g, c0);
+    swrite(g, 0);
+    gload(g, min(c0 + 1, c1 - 1));
+    swrite(g, 1);
+    gload(g, min(c0 + 2, c1 - 1));
     barrier();
+    Frag f[2];
+    fread(f[0], 0);
     auto step = [&](int kc, int d) {
-      // LDS stage d % 2 holds K-step kc; ring slot d % kDepth has been written to it
-      gload(g[d % kDepth], min(kc + kDepth, c1 - 1));
+      if (kc + 1 < c1) fread(f[(d + 1) % 2], (d + 1) % 3);
       __builtin_amdgcn_sched_barrier(0);
-      compute(d % 2);
+      mfma(f[d % 2]);
       __builtin_amdgcn_sched_barrier(0);
-      if (kc + 1 < c1) swrite(g[(d + 1) % kDepth], (d + 1) % 2);
+      if (kc + 2 < c1) swrite(g, (d + 2) % 3);
+      gload(g, min(kc + 3, c1 - 1));
       barrier();
     };
+    constexpr int kUnroll = 6;
     int kc = c0;
     for (; kc + kUnroll <= c1; kc += kUnroll) {
 #pragma unroll
