@@ -69,11 +69,13 @@ def test_moe_small_shapes_against_oracle(shape):
     _check(inputs.moe_workload(T, E, K, H, I, seed=sum(shape)))
 
 
-def test_moe_decode_shape_sampled_tokens():
-    """The benchmark's decode shape (32 tokens, 128 experts, top 8, hidden 2048, inter
-    768) on sampled tokens, and two runs give identical bits."""
-    mw = inputs.moe_workload(32, 128, 8, 2048, 768, seed=0)
-    d, got = _check(mw, tokens=[0, 7, 19, 31], act=True)
+@pytest.mark.parametrize("T", [1, 32, 128])
+def test_moe_decode_shape_sampled_tokens(T):
+    """The benchmark's decode shapes (1, 32 and 128 tokens, 128 experts, top 8, hidden
+    2048, inter 768, the bench's seeds) on sampled tokens, and two runs give identical
+    bits."""
+    mw = inputs.moe_workload(T, 128, 8, 2048, 768, seed=T)
+    d, got = _check(mw, tokens=sorted({0, T // 4, T // 2, T - 1}), act=True)
     d.run()
     torch.cuda.synchronize()
     assert np.array_equal(d.output_f64(), got)
