@@ -123,3 +123,13 @@ def test_moe_weight_packing_layout():
     with pytest.raises(RuntimeError):
         _lib.hpa_moe_pack_weights(torch.empty((1, 24, 128), dtype=torch.uint8, device="cuda"),
                                   torch.empty((1, 24, 128), dtype=torch.uint8, device="cuda"))
+
+
+def test_moe_maximum_sizes():
+    """The limits: 1024 tokens x top 16 (16384 pairs, the most the workspace plans for;
+    16 experts, so each has ~1024 pairs in ~64 pair blocks), sampled tokens; and hidden =
+    inter = 4096 (the largest rows) with every token checked."""
+    mw = inputs.moe_workload(1024, 16, 16, 256, 128, seed=21)
+    _check(mw, tokens=[0, 333, 777, 1023], act=True)
+    mw = inputs.moe_workload(3, 2, 2, 4096, 4096, seed=22)
+    _check(mw, act=True)
