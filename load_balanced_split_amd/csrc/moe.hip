@@ -48,6 +48,9 @@ constexpr int kBufDword3 = 0x00020000;
 // Weights are packed (hpa_moe_pack_weights): every 16-byte-per-lane load of a wave
 // reads one contiguous 1 KB, whole lines read once, so they stream (nt).
 constexpr int kPolicyWeights = 2;
+// Up to this many pairs (tokens x top_k) every pair is its own block and the routing
+// index is not built: one launch fewer, and a few pairs rarely share an expert.
+constexpr int kMoeDirectMaxPairs = 16;
 
 __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t p = reinterpret_cast<uint64_t>(base);
@@ -67,19 +70,16 @@ __device__ inline u32x4 aload16(rsrc_t r, uint32_t voff, uint32_t soff) {
 }
 
 // fp32 -> OCP E4M3 code: nearest value, ties to even mantissa, saturating at 448.
+// Subnormal range (below 2^-6): the nearest multiple of 2^-9. Normal range: the fp32
+// mantissa rounded to 3 bits, nearest, ties to even, by adding 2^19 - 1 plus the lowest
+// kept bit and shifting (a carry moves into the exponent, as it should), then the
+// exponent rebiased from 127 to 7 (subtracting 120 << 3).
 __device__ inline uint32_t e4m3_code(float x) {
   const uint32_t sign = __builtin_signbit(x) ? 0x80u : 0u;
   const float a = fminf(fabsf(x), 448.0f);
-  if (a < 0.015625f) return sign | static_cast<uint32_t>(rintf(a * 512.0f));   // subnormals, 2^-9 steps
-  int e;
-  frexpf(a, &e);                               // a = f 2^e, f in [0.5, 1)
-  int E = e - 1;
-  int qm = static_cast<int>(rintf(ldexpf(a, 3 - E)));   // 8 .. 16
-  if (qm == 16) {
-    qm = 8;
-    ++E;
-  }
-  return sign | static_cast<uint32_t>(((E + 7) << 3) | (qm - 8));
+  if (a < 0.015625f) return sign | static_cast<uint32_t>(rintf(a * 512.0f));
+  const uint32_t b = __builtin_bit_cast(uint32_t, a);
+  return sign | (((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - 960u);
 }
 
 // 32 bytes of E4M3 codes (two 16-byte pieces) as one operand of the 16x16x128 product:
@@ -238,15 +238,41 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
   }
 }
 
-// Gate-Up + SwiGLU: one wave per (pair block, 16 rows of I).
-__global__ __launch_bounds__(64) void moe_gate_up_kernel(MoeArgs a) {
-  const int ib = blockIdx.x % (a.I / 16), gb = blockIdx.x / (a.I / 16);
-  if (gb >= *a.nblk) return;
-  const int e = a.blk[gb], first = a.blk[a.P + gb], n = a.blk[2 * a.P + gb];
-  const int lane = threadIdx.x, m16 = lane & 15, q = lane >> 4;
+// Gate-Up + SwiGLU: one wave per (pair block, 16 rows of I). DIRECT (a few pairs, no
+// routing index): block gb is pair gb alone, a workgroup of 4 waves takes 4 row blocks
+// of it and quantises its token itself (the same arithmetic as the prepare kernel, so
+// the same codes and scale) into LDS, from where lane group q of column 0 takes each
+// chunk's 32 codes.
+constexpr int kDirectWaves = 4;
+template <bool DIRECT>
+__global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_kernel(MoeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t codes[DIRECT ? kMoeMaxHidden : 16];
+  __shared__ float red[kDirectWaves];
+  const int wave = DIRECT ? static_cast<int>(threadIdx.x >> 6) : 0;
+  const int nib = DIRECT ? a.I / (16 * kDirectWaves) : a.I / 16;   // workgroups per pair block
+  const int ib = (blockIdx.x % nib) * (DIRECT ? kDirectWaves : 1) + wave, gb = blockIdx.x / nib;
+  const int lane = threadIdx.x & 63, m16 = lane & 15, q = lane >> 4;
+  int e, n, p;
+  if constexpr (DIRECT) {
+    p = gb;
+    e = a.ids[p];
+    if (e < 0 || e >= a.E) {                     // adds nothing; reported once per pair
+      if (ib == 0 && lane == 0 && a.err)
+        __hip_atomic_fetch_or(a.err, HPA_DEVERR_MOE_EXPERT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    n = 1;
+  } else {
+    if (gb >= *a.nblk) return;
+    e = a.blk[gb];
+    const int first = a.blk[a.P + gb];
+    n = a.blk[2 * a.P + gb];
+    p = m16 < n ? a.list[first + m16] : 0;
+  }
   const bool valid = m16 < n;
-  const int p = valid ? a.list[first + m16] : 0;
+  if constexpr (DIRECT) p = valid ? p : 0;
   const int t = p / a.K;
+  float sdirect = 0.f;
   const int nch = a.H / 128;
   const rsrc_t rw = make_rsrc(a.w1 + int64_t(e) * 2 * a.I * a.H, static_cast<uint32_t>(int64_t(2) * a.I * a.H));
   const rsrc_t rx = make_rsrc(a.x8, static_cast<uint32_t>(int64_t(a.T) * a.H));
@@ -259,6 +285,54 @@ __global__ __launch_bounds__(64) void moe_gate_up_kernel(MoeArgs a) {
   f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = accg;
   constexpr int kDepth = 4;
   u32x4 ag[kDepth][2], au[kDepth][2], bx[kDepth][2];
+  auto quantise_token = [&] {
+    // the pair's token (the same for every thread): 8 bf16 per 16-byte piece, H / 8 <=
+    // 512 pieces, at most 2 per thread
+    constexpr int kThreads = 64 * kDirectWaves;
+    const uint16_t* row = a.x + int64_t(gb / a.K) * a.H;
+    const int pieces = a.H / 8;
+    u32x4 v[kMoeMaxHidden / 8 / kThreads];
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMoeMaxHidden / 8 / kThreads; ++j) {
+      const int c = j * kThreads + threadIdx.x;
+      if (c < pieces) {
+        v[j] = *reinterpret_cast<const u32x4*>(row + 8 * c);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          m = fmaxf(m, fabsf(__builtin_bit_cast(float, v[j][d] << 16)));
+          m = fmaxf(m, fabsf(__builtin_bit_cast(float, v[j][d] & 0xffff0000u)));
+        }
+      }
+    }
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kDirectWaves; ++w) m = fmaxf(m, red[w]);
+    sdirect = m / 448.0f;
+#pragma unroll
+    for (int j = 0; j < kMoeMaxHidden / 8 / kThreads; ++j) {
+      const int c = j * kThreads + threadIdx.x;
+      if (c >= pieces) continue;
+      uint32_t w[2] = {0, 0};
+      if (sdirect > 0.f) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const float lo = __builtin_bit_cast(float, v[j][d] << 16);
+          const float hi = __builtin_bit_cast(float, v[j][d] & 0xffff0000u);
+          w[d / 2] |= (e4m3_code(lo / sdirect) | (e4m3_code(hi / sdirect) << 8)) << (16 * (d % 2));
+        }
+      }
+      *reinterpret_cast<uint2*>(codes + 8 * c) = make_uint2(w[0], w[1]);
+    }
+    __syncthreads();
+  };
+  auto load_codes = [&](int slot, int c) {     // DIRECT: the token's codes from LDS
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    bx[slot][0] = valid ? *reinterpret_cast<const u32x4*>(codes + 128 * c + 32 * q) : z;
+    bx[slot][1] = valid ? *reinterpret_cast<const u32x4*>(codes + 128 * c + 32 * q + 16) : z;
+  };
   auto load = [&](int slot, int c) {
     const uint32_t sc = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(128 * c));
     const uint32_t st = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(2048 * c));
@@ -266,8 +340,12 @@ __global__ __launch_bounds__(64) void moe_gate_up_kernel(MoeArgs a) {
     ag[slot][1] = wload16(rw, og + 1024, st);
     au[slot][0] = wload16(rw, ou, st);
     au[slot][1] = wload16(rw, ou + 1024, st);
-    bx[slot][0] = aload16(rx, ox, sc);
-    bx[slot][1] = aload16(rx, ox + 16, sc);
+    if constexpr (DIRECT) {
+      load_codes(slot, c);
+    } else {
+      bx[slot][0] = aload16(rx, ox, sc);
+      bx[slot][1] = aload16(rx, ox + 16, sc);
+    }
   };
   auto mul = [&](int slot) {
     const i32x8 B = operand(bx[slot][0], bx[slot][1]);
@@ -277,9 +355,25 @@ __global__ __launch_bounds__(64) void moe_gate_up_kernel(MoeArgs a) {
                                                             0, 0, 0, 0, 0, 0);
   };
   // chunk c lives in ring slot c % kDepth (compile-time: the loop is unrolled by kDepth);
-  // the loads of chunk c + kDepth - 1 go out before chunk c is multiplied
+  // the loads of chunk c + kDepth - 1 go out before chunk c is multiplied. DIRECT: the
+  // first chunks' weight loads go out before the token is quantised, which hides the
+  // quantisation behind them.
+  if constexpr (DIRECT) {
 #pragma unroll
-  for (int d = 0; d < kDepth - 1; ++d) load(d, min(d, nch - 1));
+    for (int d = 0; d < kDepth - 1; ++d) {
+      const uint32_t st = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(2048 * min(d, nch - 1)));
+      ag[d][0] = wload16(rw, og, st);
+      ag[d][1] = wload16(rw, og + 1024, st);
+      au[d][0] = wload16(rw, ou, st);
+      au[d][1] = wload16(rw, ou + 1024, st);
+    }
+    quantise_token();
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d) load_codes(d, min(d, nch - 1));
+  } else {
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d) load(d, min(d, nch - 1));
+  }
   int c = 0;
   for (; c + kDepth <= nch; c += kDepth) {
 #pragma unroll
@@ -295,7 +389,7 @@ __global__ __launch_bounds__(64) void moe_gate_up_kernel(MoeArgs a) {
   const float* s1e = a.s1 + int64_t(e) * 2 * a.I;
   const f32x4 sg = *reinterpret_cast<const f32x4*>(s1e + g0 + 4 * q);
   const f32x4 su = *reinterpret_cast<const f32x4*>(s1e + a.I + g0 + 4 * q);
-  const float sxm = valid ? a.sx[t] : 0.f;
+  const float sxm = valid ? (DIRECT ? sdirect : a.sx[t]) : 0.f;
   f32x4 act;
   float amax = 0.f;
 #pragma unroll
@@ -339,14 +433,26 @@ __global__ __launch_bounds__(kMoeThreads) void moe_quant_act_kernel(MoeArgs a) {
   }
 }
 
-// Down + scales + routing weight: one wave per (pair block, 16 rows of H).
+// Down + scales + routing weight: one wave per (pair block, 16 rows of H); DIRECT:
+// block gb is pair gb alone.
+template <bool DIRECT>
 __global__ __launch_bounds__(64) void moe_down_kernel(MoeArgs a) {
   const int nb = blockIdx.x % (a.H / 16), gb = blockIdx.x / (a.H / 16);
-  if (gb >= *a.nblk) return;
-  const int e = a.blk[gb], first = a.blk[a.P + gb], n = a.blk[2 * a.P + gb];
   const int lane = threadIdx.x, m16 = lane & 15, q = lane >> 4;
+  int e, n, p;
+  if constexpr (DIRECT) {
+    e = a.ids[gb];
+    if (e < 0 || e >= a.E) return;
+    n = 1;
+    p = m16 < n ? gb : 0;
+  } else {
+    if (gb >= *a.nblk) return;
+    e = a.blk[gb];
+    const int first = a.blk[a.P + gb];
+    n = a.blk[2 * a.P + gb];
+    p = m16 < n ? a.list[first + m16] : 0;
+  }
   const bool valid = m16 < n;
-  const int p = valid ? a.list[first + m16] : 0;
   const int nch = a.I / 128;
   const rsrc_t rw = make_rsrc(a.w2 + int64_t(e) * a.H * a.I, static_cast<uint32_t>(int64_t(a.H) * a.I));
   const rsrc_t ra = make_rsrc(a.act8, static_cast<uint32_t>(int64_t(a.P) * a.I));
@@ -439,12 +545,20 @@ __global__ __launch_bounds__(kMoeThreads) void moe_pack_kernel(const uint8_t* __
 }  // namespace
 
 hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(moe_prepare_kernel, dim3(a.T + 1), dim3(kMoeThreads), 0, stream, a);
-  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.I / 16))), dim3(64), 0,
-                     stream, a);
-  hipLaunchKernelGGL(moe_quant_act_kernel, dim3(a.P), dim3(kMoeThreads), 0, stream, a);
-  hipLaunchKernelGGL(moe_down_kernel, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.H / 16))), dim3(64), 0,
-                     stream, a);
+  if (a.P <= kMoeDirectMaxPairs) {
+    // a few pairs: one pair per block, no routing index, tokens quantised in Gate-Up
+    hipLaunchKernelGGL(moe_gate_up_kernel<true>, dim3(static_cast<unsigned>(a.P * (a.I / (16 * kDirectWaves)))),
+                       dim3(64 * kDirectWaves), 0, stream, a);
+    hipLaunchKernelGGL(moe_quant_act_kernel, dim3(a.P), dim3(kMoeThreads), 0, stream, a);
+    hipLaunchKernelGGL(moe_down_kernel<true>, dim3(static_cast<unsigned>(a.P * (a.H / 16))), dim3(64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(moe_prepare_kernel, dim3(a.T + 1), dim3(kMoeThreads), 0, stream, a);
+    hipLaunchKernelGGL(moe_gate_up_kernel<false>, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.I / 16))), dim3(64),
+                       0, stream, a);
+    hipLaunchKernelGGL(moe_quant_act_kernel, dim3(a.P), dim3(kMoeThreads), 0, stream, a);
+    hipLaunchKernelGGL(moe_down_kernel<false>, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.H / 16))), dim3(64), 0,
+                       stream, a);
+  }
   hipLaunchKernelGGL(moe_merge_kernel, dim3((a.H / 4 + kMoeThreads - 1) / kMoeThreads, a.T), dim3(kMoeThreads), 0,
                      stream, a);
   return hipGetLastError();

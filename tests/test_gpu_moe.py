@@ -100,6 +100,21 @@ def test_moe_edge_cases():
     ref = om.fused_moe(mw.x, mw.ids, mw.weights, mw.w1, mw.s1, mw.w2, mw.s2)
     assert np.all(np.abs(got - ref) <= ATOL + RTOL * np.abs(ref))
     assert not got[3].any()
+    # the same cases with few enough pairs (<= 16) that every pair is its own block and
+    # Gate-Up quantises the tokens itself
+    mw = inputs.moe_workload(4, 6, 3, 256, 128, seed=10)
+    mw.x[1] = 0
+    mw.ids[2, 1] = mw.ids[2, 0]
+    mw.ids[0, 2], mw.ids[3, 0] = 6, -2
+    d = MoeStep(mw)
+    d.workspace.fill_(0xFF)
+    d.run()
+    torch.cuda.synchronize()
+    assert int(d.err.item()) & _lib.DEVERR_MOE_EXPERT
+    got = d.output_f64()
+    ref = om.fused_moe(mw.x, mw.ids, mw.weights, mw.w1, mw.s1, mw.w2, mw.s2)
+    assert np.all(np.isfinite(got)) and np.all(np.abs(got - ref) <= ATOL + RTOL * np.abs(ref))
+    assert not got[1].any()
 
 
 def test_moe_weight_packing_layout():
