@@ -235,3 +235,13 @@ class MoeStep:
         off = al(T * H) + al(T * 4) + al(P * 4) + al(3 * P * 4) + al(4)
         raw = self.workspace.cpu().numpy()
         return raw[off: off + P * I * 4].view(np.float32).reshape(T, K, I)
+
+    def token_codes(self):
+        """The tokens' E4M3 codes [T, H] and fp32 scales [T] at the start of the workspace
+        (written by the routing pass; calls of at most 16 pairs quantise inside Gate-Up and
+        leave them unwritten)."""
+        mw = self.mw
+        al = lambda x: (x + 255) // 256 * 256
+        T, H = mw.tokens, mw.hidden
+        raw = self.workspace.cpu().numpy()
+        return raw[:T * H].reshape(T, H).copy(), raw[al(T * H): al(T * H) + T * 4].view(np.float32).copy()

@@ -58,8 +58,17 @@ def _check(mw, tokens=None, act=True):
                     want = det["act"][(i, k)]
                     scale = max(np.abs(want).max(), 1e-30)
                     assert np.max(np.abs(a_gpu[t, k] - want)) <= 1e-4 * scale, (t, k)
+    if mw.tokens * mw.top_k > 16:           # the routing pass wrote the token codes: bit-exact
+        x8, sx = d.token_codes()
+        want8, wants = om.quantize_fp32(inputs_f32(mw.x))
+        assert np.array_equal(sx, wants) and np.array_equal(x8, want8)
     assert int(d.err.item()) == 0
     return d, got
+
+
+def inputs_f32(x_bits):
+    from oracle.formats import bf16_to_f64
+    return bf16_to_f64(x_bits).astype(np.float32)
 
 
 @pytest.mark.parametrize("shape", [(1, 4, 1, 128, 128), (5, 4, 2, 256, 128), (33, 16, 8, 384, 256),
