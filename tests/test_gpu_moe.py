@@ -157,3 +157,21 @@ def test_moe_maximum_sizes():
     _check(mw, tokens=[0, 333, 777, 1023], act=True)
     mw = inputs.moe_workload(3, 2, 2, 4096, 4096, seed=22)
     _check(mw, act=True)
+
+
+def test_moe_few_pair_path_equals_grouped_path():
+    """Two tokens x top 8 (16 pairs: every pair its own block, tokens quantised inside
+    Gate-Up) give the same bits as the same two tokens inside a three-token batch (24
+    pairs: the routing index, pairs grouped by expert with other tokens' pairs)."""
+    from load_balanced_split_amd.runner import MoeStep
+    big = inputs.moe_workload(3, 8, 8, 256, 256, seed=12)
+    small = inputs.moe_workload(2, 8, 8, 256, 256, seed=12)
+    small.x, small.ids, small.weights = big.x[:2].copy(), big.ids[:2].copy(), big.weights[:2].copy()
+    small.w1, small.s1, small.w2, small.s2 = big.w1, big.s1, big.w2, big.s2
+    outs = []
+    for mw in (small, big):
+        d = MoeStep(mw)
+        d.run()
+        torch.cuda.synchronize()
+        outs.append(d.output_f64()[:2])
+    assert np.array_equal(outs[0], outs[1])
