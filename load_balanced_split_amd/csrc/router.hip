@@ -484,33 +484,52 @@ __global__ __launch_bounds__(256) void router_topk_wg_kernel(const float* part, 
   }
 }
 
-// max of a 64-bit key with the key of another lane of its row (DPP control CTRL: a
-// permutation within quads or a rotation within the row of 16, so every source lane
-// exists)
+// v combined with the value of another lane of its row (DPP control CTRL: a permutation
+// within quads or a rotation within the row of 16, so every source lane exists)
 template <int CTRL>
-__device__ inline uint64_t dpp_max(uint64_t x) {
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(x)), CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(x >> 32)), CTRL, 0xF, 0xF, false);
-  const uint64_t y = (uint64_t(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
-  return y > x ? y : x;
+__device__ inline uint32_t dpp_umax(uint32_t v) {
+  const uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+  return o > v ? o : v;
+}
+template <int CTRL>
+__device__ inline int dpp_imin(int v) {
+  const int o = __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+  return o < v ? o : v;
 }
 
-// the wave's largest key, in every lane: the maximum within rows of 16 (quad swaps
-// 1 and 2, then row rotations by 4 and 8), then across the four rows' first lanes
-__device__ inline uint64_t wave_max_key(uint64_t x) {
-  x = dpp_max<0xB1>(x);     // quad_perm [1, 0, 3, 2]
-  x = dpp_max<0x4E>(x);     // quad_perm [2, 3, 0, 1]
-  x = dpp_max<0x124>(x);    // row_ror 4
-  x = dpp_max<0x128>(x);    // row_ror 8
-  uint64_t m = 0;
+// the wave's largest (smallest) value, in every lane: within rows of 16 (quad swaps 1
+// and 2, then row rotations by 4 and 8), then across the four rows' first lanes
+__device__ inline uint32_t wave_umax(uint32_t v) {
+  v = dpp_umax<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v = dpp_umax<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v = dpp_umax<0x124>(v);   // row_ror 4
+  v = dpp_umax<0x128>(v);   // row_ror 8
+  uint32_t m = 0;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x)), 16 * r);
-    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x >> 32)), 16 * r);
-    const uint64_t y = (uint64_t(hi) << 32) | lo;
+    const uint32_t y = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16 * r));
     m = y > m ? y : m;
   }
   return m;
+}
+__device__ inline int wave_imin(int v) {
+  v = dpp_imin<0xB1>(v);
+  v = dpp_imin<0x4E>(v);
+  v = dpp_imin<0x124>(v);
+  v = dpp_imin<0x128>(v);
+  int m = __builtin_amdgcn_readlane(v, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) m = min(m, __builtin_amdgcn_readlane(v, 16 * r));
+  return m;
+}
+
+// a logit's order-preserving 32-bit image (the high half of its key) and back
+__device__ inline uint32_t value_order(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float order_value(uint32_t o) {
+  return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
 template <int Q>
@@ -544,36 +563,44 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* part, int
         if (s0 + i < slots) v[j] += pv[j][i];
       }
   }
-  uint64_t key[4 * Q];
+  // per candidate: the value's order image (0: no candidate, below every real one)
+  // and the expert index
+  uint32_t ov[4 * Q];
 #pragma unroll
   for (int j = 0; j < Q; ++j) {
     const bool ok = e0[j] < E;                        // E is a multiple of 16: all four or none
     if (ok) *reinterpret_cast<f32x4*>(a.logits + int64_t(t) * E + e0[j]) = v[j];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) key[4 * j + r] = ok ? topk_key(v[j][r], e0[j] + r) : 0;
+    for (int r = 0; r < 4; ++r) ov[4 * j + r] = ok ? value_order(v[j][r]) : 0u;
   }
+  // k rounds: the wave's largest value; among the candidates holding it the lowest
+  // expert index (one holder -- the usual case -- is read from its lane, several are
+  // reduced); that candidate drops out, and lane r keeps round r's result
   const int k = a.top_k;
-  uint64_t mine = 0;
+  uint32_t mine_o = 0;
+  int mine_e = 0;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
-    int bi = 0;
+    uint32_t lb = 0;
+#pragma unroll
+    for (int c = 0; c < 4 * Q; ++c) lb = ov[c] > lb ? ov[c] : lb;
+    const uint32_t m = wave_umax(lb);
+    int low = 0x7fffffff;
 #pragma unroll
     for (int c = 0; c < 4 * Q; ++c)
-      if (key[c] > best) {
-        best = key[c];
-        bi = c;
-      }
-    const uint64_t m = wave_max_key(best);
-    if (best == m) {                                  // the owner of this maximum
+      if (ov[c] == m) low = min(low, 256 * (c / 4) + 4 * lane + c % 4);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(low != 0x7fffffff);
+    const int win = __popcll(hit) == 1 ? __builtin_amdgcn_readlane(low, __builtin_ctzll(hit)) : wave_imin(low);
 #pragma unroll
-      for (int c = 0; c < 4 * Q; ++c)
-        if (c == bi) key[c] = 0;
+    for (int c = 0; c < 4 * Q; ++c)
+      if (ov[c] == m && 256 * (c / 4) + 4 * lane + c % 4 == win) ov[c] = 0;
+    if (lane == r) {
+      mine_o = m;
+      mine_e = win;
     }
-    if (lane == r) mine = m;
   }
   if (lane < k) {
-    a.topk_idx[int64_t(t) * k + lane] = key_expert(mine);
-    a.topk_val[int64_t(t) * k + lane] = key_value(mine);
+    a.topk_idx[int64_t(t) * k + lane] = mine_e;
+    a.topk_val[int64_t(t) * k + lane] = order_value(mine_o);
   }
 }
 
