@@ -282,6 +282,11 @@ __global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_k
   const uint32_t ou = static_cast<uint32_t>((a.I / 16 + ib) * nch * 2048 + 16 * lane);
   // padding pair columns read past the buffer: zeros
   const uint32_t ox = valid ? static_cast<uint32_t>(t * a.H + 32 * q) : 0x80000000u;
+  // the epilogue's scales, requested before the weight stream
+  const float* s1e = a.s1 + int64_t(e) * 2 * a.I;
+  const f32x4 sg = *reinterpret_cast<const f32x4*>(s1e + g0 + 4 * q);
+  const f32x4 su = *reinterpret_cast<const f32x4*>(s1e + a.I + g0 + 4 * q);
+  const float sx_t = DIRECT ? 0.f : a.sx[t];
   f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = accg;
   constexpr int kDepth = 4;
   u32x4 ag[kDepth][2], au[kDepth][2], bx[kDepth][2];
@@ -386,10 +391,7 @@ __global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_k
   for (int d = 0; d < kDepth - 1; ++d)
     if (c + d < nch) mul(d);
   // lane (m16, q) holds gate / up rows g0 + 4 q + i (i < 4) of pair column m16
-  const float* s1e = a.s1 + int64_t(e) * 2 * a.I;
-  const f32x4 sg = *reinterpret_cast<const f32x4*>(s1e + g0 + 4 * q);
-  const f32x4 su = *reinterpret_cast<const f32x4*>(s1e + a.I + g0 + 4 * q);
-  const float sxm = valid ? (DIRECT ? sdirect : a.sx[t]) : 0.f;
+  const float sxm = valid ? (DIRECT ? sdirect : sx_t) : 0.f;
   f32x4 act;
   float amax = 0.f;
 #pragma unroll
@@ -459,6 +461,9 @@ __global__ __launch_bounds__(64) void moe_down_kernel(MoeArgs a) {
   const int n0 = nb * 16;
   const uint32_t ow = static_cast<uint32_t>(nb * nch * 2048 + 16 * lane);   // packed row block nb
   const uint32_t oa = valid ? static_cast<uint32_t>(p * a.I + 32 * q) : 0x80000000u;
+  // the epilogue's scales and weight, requested before the weight stream
+  const f32x4 s2 = *reinterpret_cast<const f32x4*>(a.s2 + int64_t(e) * a.H + n0 + 4 * q);
+  const float f = valid ? a.sa[p] * a.wts[p] : 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int kDepth = 4;
   u32x4 aw[kDepth][2], ba[kDepth][2];
@@ -488,8 +493,6 @@ __global__ __launch_bounds__(64) void moe_down_kernel(MoeArgs a) {
   for (int d = 0; d < kDepth - 1; ++d)
     if (c + d < nch) mul(d);
   if (valid) {
-    const f32x4 s2 = *reinterpret_cast<const f32x4*>(a.s2 + int64_t(e) * a.H + n0 + 4 * q);
-    const float f = a.sa[p] * a.wts[p];
     f32x4 y;
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = acc[i] * f * s2[i];
