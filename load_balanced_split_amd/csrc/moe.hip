@@ -250,7 +250,11 @@ __global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_k
   __shared__ float red[kDirectWaves];
   const int wave = DIRECT ? static_cast<int>(threadIdx.x >> 6) : 0;
   const int nib = DIRECT ? a.I / (16 * kDirectWaves) : a.I / 16;   // workgroups per pair block
-  const int ib = (blockIdx.x % nib) * (DIRECT ? kDirectWaves : 1) + wave, gb = blockIdx.x / nib;
+  // DIRECT: the pair is the fast index (the few pairs' first row blocks go out first);
+  // grouped: the row block is (measured faster there)
+  const int ib = (DIRECT ? static_cast<int>(blockIdx.x) / a.P : static_cast<int>(blockIdx.x) % nib) *
+                     (DIRECT ? kDirectWaves : 1) + wave;
+  const int gb = DIRECT ? static_cast<int>(blockIdx.x) % a.P : static_cast<int>(blockIdx.x) / nib;
   const int lane = threadIdx.x & 63, m16 = lane & 15, q = lane >> 4;
   int e, n, p;
   if constexpr (DIRECT) {
@@ -439,7 +443,8 @@ __global__ __launch_bounds__(kMoeThreads) void moe_quant_act_kernel(MoeArgs a) {
 // block gb is pair gb alone.
 template <bool DIRECT>
 __global__ __launch_bounds__(64) void moe_down_kernel(MoeArgs a) {
-  const int nb = blockIdx.x % (a.H / 16), gb = blockIdx.x / (a.H / 16);
+  const int nb = DIRECT ? static_cast<int>(blockIdx.x) / a.P : static_cast<int>(blockIdx.x) % (a.H / 16);
+  const int gb = DIRECT ? static_cast<int>(blockIdx.x) % a.P : static_cast<int>(blockIdx.x) / (a.H / 16);
   const int lane = threadIdx.x, m16 = lane & 15, q = lane >> 4;
   int e, n, p;
   if constexpr (DIRECT) {
