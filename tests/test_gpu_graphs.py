@@ -64,3 +64,15 @@ def test_router_graph_replays_match_eager():
         print(f"graph router T={T}", flush=True)
         r = RouterStep(inputs.router_workload(T, 256, 1024, seed=T), top_k=8)
         _replays(lambda: r.run(2), lambda: r.run(1), [r.logits, r.topk_idx, r.topk_val])
+
+
+def test_moe_graph_replays_match_eager():
+    """The fused MoE call, few-pair (one token) and grouped (20 tokens) paths, captured once
+    and replayed with a different batch's call and a NaN-filled workspace between replays."""
+    from load_balanced_split_amd.runner import MoeStep
+    other = MoeStep(inputs.moe_workload(3, 16, 4, 256, 128, seed=5))
+    for T in (1, 20):
+        print(f"graph moe T={T}", flush=True)
+        m = MoeStep(inputs.moe_workload(T, 16, 4, 256, 128, seed=T))
+        _replays(m.run, other.run, [m.out], scrub=lambda: m.workspace.fill_(0xFF))
+        assert int(m.err.item()) == 0
