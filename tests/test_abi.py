@@ -207,3 +207,46 @@ def test_router_validation_and_workspace_size(L):
     assert pk(None, 64, 64, p, None) == 1
     assert pk(ctypes.c_void_p(4100), 64, 64, p, None) == 1
     assert pk(p, 20, 64, p, None) == 2
+
+
+def test_moe_validation_and_workspace_size(L):
+    """The MoE calls refuse bad shapes, pointers and workspaces on the host, before any
+    launch (no GPU needed)."""
+    n = ctypes.c_size_t(0)
+    ws = L.hpa_moe_workspace_size
+    al = lambda x: (x + 255) // 256 * 256
+    T, K, H, I = 32, 8, 2048, 768
+    P = T * K
+    assert ws(T, K, H, I, ctypes.byref(n)) == 0
+    want = (al(T * H) + al(T * 4) + al(P * 4) + al(3 * P * 4) + al(4) + al(P * I * 4) + al(P * (I // 16) * 4)
+            + al(P * I) + al(P * 4) + al(P * H * 4))
+    assert n.value == want
+    for args, status in (((1025, 1, 128, 128), 2), ((1, 0, 128, 128), 2), ((1, 17, 128, 128), 2),
+                         ((1, 1, 64, 128), 2), ((1, 1, 128, 200), 2), ((1, 1, 4224, 128), 2),
+                         ((1024, 16, 128, 128), 0), ((-1, 1, 128, 128), 2)):
+        assert ws(*args, ctypes.byref(n)) == status, args
+    assert ws(1, 1, 128, 128, None) == 1
+    f = L.hpa_moe_fused
+    p, q = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    fp = ctypes.cast(p, ctypes.POINTER(ctypes.c_float))
+    ip = ctypes.cast(p, ctypes.POINTER(ctypes.c_int32))
+    big = ctypes.c_size_t(1 << 40)
+    ok = dict(x=p, ids=ip, wts=fp, w1=p, s1=fp, w2=p, s2=fp, T=4, E=8, K=2, H=128, I=128, out=q, ws=p,
+              bytes=big, err=None, stream=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["ids"], a["wts"], a["w1"], a["s1"], a["w2"], a["s2"], a["T"], a["E"], a["K"], a["H"],
+                 a["I"], a["out"], a["ws"], a["bytes"], a["err"], a["stream"])
+    assert call(E=1025) == 2 and call(K=0) == 2 and call(H=100) == 2 and call(T=1025) == 2
+    assert call(x=None) == 1 and call(out=None) == 1 and call(ws=None) == 1
+    assert call(out=ctypes.c_void_p(8200)) == 1                           # misaligned
+    assert call(bytes=ctypes.c_size_t(1024)) == 3                         # workspace too small
+    assert call(T=0) == 0                                                 # nothing to do, nothing launched
+    pk = L.hpa_moe_pack_weights
+    assert pk(p, 8, 24, 128, q, None) == 2                                # rows not a multiple of 16
+    assert pk(p, 8, 32, 100, q, None) == 2                                # cols not a multiple of 128
+    assert pk(p, 0, 32, 128, q, None) == 2
+    assert pk(None, 8, 32, 128, q, None) == 1
+    assert pk(p, 8, 32, 128, p, None) == 1                                # in place
+    assert pk(ctypes.c_void_p(4100), 8, 32, 128, q, None) == 1            # misaligned
