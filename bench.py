@@ -429,10 +429,13 @@ def measure_workload(idx, args, stream, timer, steps, headline):
                 "us_per_step": round(mean, 2),
                 "us_p10_p50_p90": [round(pct(per, f), 2) for f in (0.1, 0.5, 0.9)],
                 "kv_gbps": round(kv_bytes / (mean * 1e-6) / 1e9, 1),
-                "kv_frac_of_peak": round(kv_bytes / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+                "kv_frac_of_peak": round(kv_bytes / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                "alg_gbps": round((alg_bytes + pro_bytes) / (mean * 1e-6) / 1e9, 1)}
 
+    # context only: the products' flops (q.K and p.V, 2 flops per multiply-add) over the attended tokens
+    alg_gflop = round(float(w.attended_lens().astype(np.int64).sum()) * w.hq * 4 * 128 / 1e9, 3)
     ent = {"workload": inputs.CONFIG_NAMES[idx], "num_workers": W, "static_num_workers": copies[0].static_workers,
-           "rotating_copies": R, "kv_bytes": kv_bytes, "algorithmic_bytes": alg_bytes}
+           "rotating_copies": R, "kv_bytes": kv_bytes, "algorithmic_bytes": alg_bytes, "alg_gflop": alg_gflop}
     if pro_bytes:
         ent["prologue_bytes"] = pro_bytes
     ent[SCHED_NAMES[head]] = summary(step_times(head, max(100, steps)))
@@ -448,6 +451,10 @@ def measure_workload(idx, args, stream, timer, steps, headline):
                        "achieved": round(alg_bytes / (attn_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBPS,
                        "unit": "GB/s", "frac": round(alg_bytes / (attn_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
                        "traffic": traffic_per_launch(head, w.kv_dtype, idx, args.products)}
+    if ent["roofline"]["traffic"]:
+        # bytes the attention launch moves beyond the algorithmic ones (partial slots,
+        # metadata, re-reads)
+        ent["attn_overhead_bytes"] = ent["roofline"]["traffic"] - alg_bytes
     for other in ("balanced", "single", "fused"):
         if other == head:
             continue
@@ -526,10 +533,13 @@ def main():
                   "behind a spin kernel; value and ms_per_step: mean over exactly `steps` steps; "
                   "percentiles over replays (per_config: at least 100 steps)",
         "kv_frac_of_peak": round(head["kv_bytes"] / (mean_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "alg_gbps": round((head["algorithmic_bytes"] + head.get("prologue_bytes", 0)) / (mean_us * 1e-6) / 1e9, 1),
         "kernel_us": hs["kernel_us"],
         "attn_plus_merge_kv_frac": head["attn_plus_merge_kv_frac"],
         "roofline": head["roofline"],
     }
+    if "attn_overhead_bytes" in head:
+        result["attn_overhead_bytes"] = head["attn_overhead_bytes"]
     if "cpu_baseline" in head:
         result["cpu_baseline"] = head["cpu_baseline"]
     result["per_config"] = per_config
