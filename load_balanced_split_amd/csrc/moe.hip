@@ -23,6 +23,9 @@
 //  moe_down_kernel      one wave per (pair block, 16 rows of H): 16 rows of W2
 //      against the block's activation codes; scales and routing weight applied.
 //  moe_merge_kernel     out[t] = sum over k, in k order, of the pair results -> bf16.
+// With at most kMoeDirectMaxPairs pairs there is no routing index: every pair is its
+// own block, Gate-Up quantises the pair's token itself, and the prepare launch is
+// skipped (four launches).
 //
 // Products: A = 16 weight rows, B = 16 pairs; per 128-wide k chunk a lane (row or
 // pair m, group q) holds the 32 bytes [128 c + 32 q, + 32) of its row, both operands
