@@ -216,12 +216,9 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* x, con
 // Many tokens: 128 experts x 128 tokens per workgroup over one K range. Each K-step
 // (32 dims) of both weight halves (8 tiles x 2 KB, copied as they lie in the packed
 // layout) and of x (128 tokens x 64 bytes, rearranged into 8 B-operand tiles of 1 KB)
-// is staged in LDS, in two alternating stages; the global loads of a K-step go out
-// two K-steps ahead into registers. Waves 2 x 2: wave (we, wt) multiplies expert
+// is staged in LDS, in three rotating stages (below). Waves 2 x 2: wave (we, wt) multiplies expert
 // blocks 4 we .. 4 we + 3 with token blocks 4 wt .. 4 wt + 3 (16 accumulators), so
-// every fragment read from LDS feeds 4 (or 8) MFMAs. One barrier per K-step: the
-// stage a K-step reads was written before the previous barrier, the stage it writes
-// was last read before it.
+// every fragment read from LDS feeds 4 (or 8) MFMAs.
 template <int PASSES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_gemm_tiled_kernel(RouterArgs a) {
   constexpr int kWPieces = PASSES == 2 ? 4 : 2;     // 16-byte weight pieces per thread per K-step
