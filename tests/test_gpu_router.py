@@ -48,10 +48,10 @@ def check(rw, passes, top_k=8):
 
 # decode (K ranges per wave), medium (expert groups per wave) and LDS-tiled shapes (more
 # than 256 tokens, experts a multiple of 128), with ragged token counts and K ranges of
-# 1, 2 and 3 K-steps in the tiled pipeline
+# 1, 2 and 3 K-steps in the tiled pipeline; the largest hidden size (65536)
 SHAPES = [(1, 256, 7168), (5, 64, 96), (16, 16, 32), (17, 128, 256), (64, 256, 1024), (65, 48, 160),
           (300, 256, 2048), (8, 1024, 512), (33, 32, 64), (257, 128, 64), (1000, 384, 32), (300, 128, 96),
-          (520, 1024, 256)]
+          (520, 1024, 256), (3, 16, 65536)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
