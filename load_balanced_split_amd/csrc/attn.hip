@@ -1408,16 +1408,17 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
 }
 
 // Merge: block (s, h) combines the 128 dims of head h of sequence s; blocks of
-// unsplit sequences return at once. 256 threads = 32 dim-quads x 8 lane groups:
-// lane group j folds split groups j, j + 8, ... (16 consecutive splits each, in
+// unsplit sequences return at once. THREADS = 32 dim-quads x LANES lane groups:
+// lane group j folds split groups j, j + LANES, ... (16 consecutive splits each, in
 // order, with fold), then the group results are folded in group order, so every
-// schedule's partials combine with the same arithmetic in the same order.
-// Empty sequences get a zero row.
-constexpr int kMergeThreads = 256;
+// schedule's partials combine with the same arithmetic in the same order, whatever
+// the block size. Empty sequences get a zero row. Grids of at most one block per CU
+// take 256 threads and issue two passes' loads together (a long sequence's many
+// splits in one round trip); larger grids take 128 threads (measured: on 1024
+// blocks the merge takes 3.7 instead of 5.5 µs, on 256 blocks 6.0 instead of 4.4).
 constexpr int kMergeDims = kHeadDim;   // head dims per merge block (splitting them measured slower:
                                        // the merge is bound by dispatch and round trips, not bytes)
 constexpr int kMergeQuads = kMergeDims / 4;
-constexpr int kMergeLanes = kMergeThreads / kMergeQuads;
 
 // The merge kernel's own arguments: everything it reads, in two 64-byte lines, so
 // the launch arguments cost one round trip.
@@ -1440,10 +1441,12 @@ struct MergeArgs {
 // TWO: the first two passes' loads go out together (a second register set: fewer
 // blocks per CU, so it is launched only when the grid has at most one block per CU).
 template <MergeMode MODE, bool TWO>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int32_t* seq_lens, const int32_t* plan,
-                                                              const float* part_acc, const float* part_m,
-                                                              const float* part_l, int hkv, int off_splits,
-                                                              int off_base, MergeArgs a) {
+__global__ __launch_bounds__(TWO ? 256 : 128) void merge_kernel(const int32_t* seq_lens, const int32_t* plan,
+                                                                const float* part_acc, const float* part_m,
+                                                                const float* part_l, int hkv, int off_splits,
+                                                                int off_base, MergeArgs a) {
+  constexpr int kMergeThreads = TWO ? 256 : 128;
+  constexpr int kMergeLanes = kMergeThreads / kMergeQuads;
   __shared__ float gm[kMergeLanes], gl[kMergeLanes];
   __shared__ f32x4 gacc[kMergeLanes][kMergeQuads];
   const int hh = blockIdx.y, d0 = blockIdx.z * kMergeDims;
@@ -1618,13 +1621,13 @@ hipError_t launch_merge(const AttnArgs& a, MergeMode mode, hipStream_t stream) {
   const dim3 grid(S, a.group, kHeadDim / kMergeDims);
   const bool two = int64_t(S) * a.group <= a.workers;   // at most one block per worker (CU)
   if (mode == MERGE_PLAN)
-    hipLaunchKernelGGL((two ? merge_kernel<MERGE_PLAN, true> : merge_kernel<MERGE_PLAN, false>), grid, dim3(kMergeThreads), 0,
+    hipLaunchKernelGGL((two ? merge_kernel<MERGE_PLAN, true> : merge_kernel<MERGE_PLAN, false>), grid, dim3(two ? 256 : 128), 0,
                        stream, m.seq_lens, m.plan, m.part_acc, m.part_m, m.part_l, m.hkv, m.num_splits, m.partial_base, m);
   else if (mode == MERGE_FUSED)
-    hipLaunchKernelGGL((two ? merge_kernel<MERGE_FUSED, true> : merge_kernel<MERGE_FUSED, false>), grid, dim3(kMergeThreads), 0,
+    hipLaunchKernelGGL((two ? merge_kernel<MERGE_FUSED, true> : merge_kernel<MERGE_FUSED, false>), grid, dim3(two ? 256 : 128), 0,
                        stream, m.seq_lens, m.plan, m.part_acc, m.part_m, m.part_l, m.hkv, m.num_splits, m.partial_base, m);
   else
-    hipLaunchKernelGGL((two ? merge_kernel<MERGE_STATIC, true> : merge_kernel<MERGE_STATIC, false>), grid, dim3(kMergeThreads), 0,
+    hipLaunchKernelGGL((two ? merge_kernel<MERGE_STATIC, true> : merge_kernel<MERGE_STATIC, false>), grid, dim3(two ? 256 : 128), 0,
                        stream, m.seq_lens, m.plan, m.part_acc, m.part_m, m.part_l, m.hkv, m.num_splits, m.partial_base, m);
   return hipGetLastError();
 }
