@@ -646,8 +646,8 @@ def moe_bytes(mw):
 
 def moe_bench(args, stream):
     """The fused FP8 MoE layer at decode batch sizes (128 experts, top 8, hidden 2048,
-    inter 768; synthetic weights and routing): one call = Gate-Up, Down and merge
-    launches, replayed from a HIP graph over copies of the weights in separate buffers
+    inter 768; synthetic weights and routing): one call = the layer's launches (two at
+    one token, five at 32 and 128), replayed from a HIP graph over copies of the weights in separate buffers
     (more than twice the Infinity Cache between two uses of the same bytes), so the
     weights come from HBM; roofline against the HBM peak."""
     import torch

@@ -384,9 +384,10 @@ hpa_status hpa_router_gemm(const void* x, const void* packed, int32_t tokens, in
  * workspace: at least hpa_moe_workspace_size bytes (token codes, the routing
  * index, the fp32 activations and their codes, the weighted per-slot results).
  * Five launches on `stream` (quantise + routing index, Gate-Up, requantise, Down,
- * merge); four when tokens x top_k <= 16 (each pair its own block, the tokens
- * quantised inside Gate-Up, the token-code part of the workspace left unwritten).
- * Nothing allocated; results are deterministic and the same either way. */
+ * merge); two when tokens x top_k <= 16 (each pair its own block: Gate-Up quantises
+ * the tokens, Down requantises and merges; only the activations and their slice
+ * maxima are written to the workspace). Nothing allocated; results are
+ * deterministic and the same either way. */
 /* Packs row-major E4M3 expert weights w [E][rows][cols] (device, 16-byte aligned)
  * into the tiled order hpa_moe_fused reads (packed: device, E * rows * cols bytes,
  * 16-byte aligned, another buffer): tile (e, rb, c) holds rows 16 rb .. + 16 and

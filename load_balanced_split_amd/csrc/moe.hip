@@ -23,9 +23,12 @@
 //  moe_down_kernel      one wave per (pair block, 16 rows of H): 16 rows of W2
 //      against the block's activation codes; scales and routing weight applied.
 //  moe_merge_kernel     out[t] = sum over k, in k order, of the pair results -> bf16.
-// With at most kMoeDirectMaxPairs pairs there is no routing index: every pair is its
-// own block, Gate-Up quantises the pair's token itself, and the prepare launch is
-// skipped (four launches).
+// With at most kMoeDirectMaxPairs pairs there is no routing index and two launches:
+//  moe_gate_up_kernel<true>  every pair its own block; the workgroup quantises the
+//      pair's token itself.
+//  moe_down_direct_kernel    one workgroup per (token, 16 rows of H), one wave per slot
+//      of the token: requantisation, Down, scales and the merge in k order.
+// Both paths give the same bits.
 //
 // Products: A = 16 weight rows, B = 16 pairs; per 128-wide k chunk a lane (row or
 // pair m, group q) holds the 32 bytes [128 c + 32 q, + 32) of its row, both operands
@@ -52,7 +55,7 @@ constexpr int kBufDword3 = 0x00020000;
 // reads one contiguous 1 KB, whole lines read once, so they stream (nt).
 constexpr int kPolicyWeights = 2;
 // Up to this many pairs (tokens x top_k) every pair is its own block and the routing
-// index is not built: one launch fewer, and a few pairs rarely share an expert.
+// index is not built (a few pairs rarely share an expert): two launches instead of five.
 constexpr int kMoeDirectMaxPairs = 16;
 
 __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -115,40 +118,38 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
     const int t = blockIdx.x;
     const int pieces = a.H / 8;                               // 16-byte pieces of 8 bf16
     const uint16_t* row = a.x + int64_t(t) * a.H;
-    u32x4 v[kMoeMaxHidden / 8 / kMoeThreads];
+    // all loads first, with no branch (indexes past the row clamped to its last piece:
+    // the maximum is unchanged, the piece is stored again with the same codes)
+    constexpr int kPieces = kMoeMaxHidden / 8 / kMoeThreads;
+    u32x4 v[kPieces];
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) v[j] = *reinterpret_cast<const u32x4*>(row + 8 * min(j * kMoeThreads + tid, pieces - 1));
     float amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMoeMaxHidden / 8 / kMoeThreads; ++j) {
-      const int c = j * kMoeThreads + tid;
-      if (c < pieces) {
-        v[j] = *reinterpret_cast<const u32x4*>(row + 8 * c);
+    for (int j = 0; j < kPieces; ++j) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          amax = fmaxf(amax, fabsf(__builtin_bit_cast(float, v[j][d] << 16)));
-          amax = fmaxf(amax, fabsf(__builtin_bit_cast(float, v[j][d] & 0xffff0000u)));
-        }
+      for (int d = 0; d < 4; ++d) {
+        amax = fmaxf(amax, fabsf(__builtin_bit_cast(float, v[j][d] << 16)));
+        amax = fmaxf(amax, fabsf(__builtin_bit_cast(float, v[j][d] & 0xffff0000u)));
       }
     }
     amax = wave_max(amax);
     if (lane == 0) red[wave] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float s = amax / 448.0f;
+    const float s = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, amax / 448.0f)));
     if (tid == 0) a.sx[t] = s;
 #pragma unroll
-    for (int j = 0; j < kMoeMaxHidden / 8 / kMoeThreads; ++j) {
-      const int c = j * kMoeThreads + tid;
-      if (c >= pieces) continue;
+    for (int j = 0; j < kPieces; ++j) {
       uint32_t w[2] = {0, 0};
-      if (s > 0.f) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const float lo = __builtin_bit_cast(float, v[j][d] << 16);
-          const float hi = __builtin_bit_cast(float, v[j][d] & 0xffff0000u);
-          w[d / 2] |= (e4m3_code(lo / s) | (e4m3_code(hi / s) << 8)) << (16 * (d % 2));
-        }
+      for (int d = 0; d < 4; ++d) {
+        const float lo = __builtin_bit_cast(float, v[j][d] << 16);
+        const float hi = __builtin_bit_cast(float, v[j][d] & 0xffff0000u);
+        w[d / 2] |= (e4m3_code(lo / s) | (e4m3_code(hi / s) << 8)) << (16 * (d % 2));
       }
-      *reinterpret_cast<uint2*>(a.x8 + int64_t(t) * a.H + 8 * c) = make_uint2(w[0], w[1]);
+      const uint2 pk = s > 0.f ? make_uint2(w[0], w[1]) : make_uint2(0u, 0u);   // a zero token: codes 0
+      *reinterpret_cast<uint2*>(a.x8 + int64_t(t) * a.H + 8 * min(j * kMoeThreads + tid, pieces - 1)) = pk;
     }
     return;
   }
@@ -242,79 +243,87 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
 }
 
 // Gate-Up + SwiGLU: one wave per (pair block, 16 rows of I). DIRECT (a few pairs, no
-// routing index): block gb is pair gb alone, a workgroup of 4 waves takes 4 row blocks
-// of it and quantises its token itself (the same arithmetic as the prepare kernel, so
-// the same codes and scale) into LDS, from where lane group q of column 0 takes each
-// chunk's 32 codes.
-constexpr int kDirectWaves = 4;
+// routing index): block gb is pair gb alone, a workgroup of kDirectWaves waves takes
+// as many row blocks of it and quantises its token itself (the same arithmetic as the
+// prepare kernel, so the same codes and scale) into LDS, from where lane group q of
+// column 0 takes each chunk's 32 codes. The sizes and pointers the first loads need
+// come as leading arguments, which the launch preloads into scalar registers.
+constexpr int kDirectWaves = 2;
 template <bool DIRECT>
-__global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_kernel(MoeArgs a) {
+__global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_kernel(
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ w1, const uint16_t* __restrict__ x, int P, int K,
+    int E, int H, int I, MoeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t codes[DIRECT ? kMoeMaxHidden : 16];
   __shared__ float red[kDirectWaves];
   const int wave = DIRECT ? static_cast<int>(threadIdx.x >> 6) : 0;
-  const int nib = DIRECT ? a.I / (16 * kDirectWaves) : a.I / 16;   // workgroups per pair block
+  const int nib = DIRECT ? I / (16 * kDirectWaves) : I / 16;   // workgroups per pair block
   // DIRECT: the pair is the fast index (the few pairs' first row blocks go out first);
   // grouped: the row block is (measured faster there)
-  const int ib = (DIRECT ? static_cast<int>(blockIdx.x) / a.P : static_cast<int>(blockIdx.x) % nib) *
+  const int ib = (DIRECT ? static_cast<int>(blockIdx.x) / P : static_cast<int>(blockIdx.x) % nib) *
                      (DIRECT ? kDirectWaves : 1) + wave;
-  const int gb = DIRECT ? static_cast<int>(blockIdx.x) % a.P : static_cast<int>(blockIdx.x) / nib;
+  const int gb = DIRECT ? static_cast<int>(blockIdx.x) % P : static_cast<int>(blockIdx.x) / nib;
   const int lane = threadIdx.x & 63, m16 = lane & 15, q = lane >> 4;
   int e, n, p;
+  bool live = true;
   if constexpr (DIRECT) {
+    // no early exit for an id outside [0, E): the loads below do not wait for the
+    // test; such a pair streams expert 0, stores nothing and is reported once
     p = gb;
-    e = a.ids[p];
-    if (e < 0 || e >= a.E) {                     // adds nothing; reported once per pair
-      if (ib == 0 && lane == 0 && a.err)
-        __hip_atomic_fetch_or(a.err, HPA_DEVERR_MOE_EXPERT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
+    e = ids[p];
+    live = e >= 0 && e < E;
+    e = live ? e : 0;
     n = 1;
   } else {
     if (gb >= *a.nblk) return;
     e = a.blk[gb];
-    const int first = a.blk[a.P + gb];
-    n = a.blk[2 * a.P + gb];
+    const int first = a.blk[P + gb];
+    n = a.blk[2 * P + gb];
     p = m16 < n ? a.list[first + m16] : 0;
   }
   const bool valid = m16 < n;
   if constexpr (DIRECT) p = valid ? p : 0;
-  const int t = p / a.K;
+  const int t = p / K;
   float sdirect = 0.f;
-  const int nch = a.H / 128;
-  const rsrc_t rw = make_rsrc(a.w1 + int64_t(e) * 2 * a.I * a.H, static_cast<uint32_t>(int64_t(2) * a.I * a.H));
-  const rsrc_t rx = make_rsrc(a.x8, static_cast<uint32_t>(int64_t(a.T) * a.H));
+  const int nch = H / 128;
+  const rsrc_t rw = make_rsrc(w1 + int64_t(e) * 2 * I * H, static_cast<uint32_t>(int64_t(2) * I * H));
+  const rsrc_t rx = make_rsrc(a.x8, static_cast<uint32_t>(int64_t(a.T) * H));
   const int g0 = ib * 16;
   // packed tiles of row block rb: 2 KB per 128-wide chunk, chunks consecutive
   const uint32_t og = static_cast<uint32_t>(ib * nch * 2048 + 16 * lane);
-  const uint32_t ou = static_cast<uint32_t>((a.I / 16 + ib) * nch * 2048 + 16 * lane);
+  const uint32_t ou = static_cast<uint32_t>((I / 16 + ib) * nch * 2048 + 16 * lane);
   // padding pair columns read past the buffer: zeros
-  const uint32_t ox = valid ? static_cast<uint32_t>(t * a.H + 32 * q) : 0x80000000u;
+  const uint32_t ox = valid ? static_cast<uint32_t>(t * H + 32 * q) : 0x80000000u;
   // the epilogue's scales, requested before the weight stream
-  const float* s1e = a.s1 + int64_t(e) * 2 * a.I;
+  const float* s1e = a.s1 + int64_t(e) * 2 * I;
   const f32x4 sg = *reinterpret_cast<const f32x4*>(s1e + g0 + 4 * q);
-  const f32x4 su = *reinterpret_cast<const f32x4*>(s1e + a.I + g0 + 4 * q);
+  const f32x4 su = *reinterpret_cast<const f32x4*>(s1e + I + g0 + 4 * q);
   const float sx_t = DIRECT ? 0.f : a.sx[t];
   f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = accg;
-  constexpr int kDepth = 4;
+  constexpr int kDepth = DIRECT ? 8 : 4;   // DIRECT: few waves, each streams a whole pair's rows
   u32x4 ag[kDepth][2], au[kDepth][2], bx[kDepth][2];
+  // DIRECT: the pair's token (the same for every thread), 8 bf16 per 16-byte piece,
+  // H / 8 <= 512 pieces, kTokPieces per thread. Its loads go out first, so that waiting
+  // for them does not wait for the weight loads issued after them, and none of this
+  // branches (the compiler would move a load under a branch to its use and wait
+  // there): indexes past the row are clamped to its last piece, which leaves the
+  // maximum unchanged and stores that piece's codes again.
+  constexpr int kThreads = 64 * kDirectWaves;
+  constexpr int kTokPieces = DIRECT ? kMoeMaxHidden / 8 / kThreads : 1;
+  u32x4 tok[kTokPieces];
+  auto load_token = [&] {
+    const uint16_t* row = x + int64_t(gb / K) * H;
+#pragma unroll
+    for (int j = 0; j < kTokPieces; ++j)
+      tok[j] = *reinterpret_cast<const u32x4*>(row + 8 * min(j * kThreads + static_cast<int>(threadIdx.x), H / 8 - 1));
+  };
   auto quantise_token = [&] {
-    // the pair's token (the same for every thread): 8 bf16 per 16-byte piece, H / 8 <=
-    // 512 pieces, at most 2 per thread
-    constexpr int kThreads = 64 * kDirectWaves;
-    const uint16_t* row = a.x + int64_t(gb / a.K) * a.H;
-    const int pieces = a.H / 8;
-    u32x4 v[kMoeMaxHidden / 8 / kThreads];
     float m = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMoeMaxHidden / 8 / kThreads; ++j) {
-      const int c = j * kThreads + threadIdx.x;
-      if (c < pieces) {
-        v[j] = *reinterpret_cast<const u32x4*>(row + 8 * c);
+    for (int j = 0; j < kTokPieces; ++j) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          m = fmaxf(m, fabsf(__builtin_bit_cast(float, v[j][d] << 16)));
-          m = fmaxf(m, fabsf(__builtin_bit_cast(float, v[j][d] & 0xffff0000u)));
-        }
+      for (int d = 0; d < 4; ++d) {
+        m = fmaxf(m, fabsf(__builtin_bit_cast(float, tok[j][d] << 16)));
+        m = fmaxf(m, fabsf(__builtin_bit_cast(float, tok[j][d] & 0xffff0000u)));
       }
     }
     m = wave_max(m);
@@ -322,21 +331,18 @@ __global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_k
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kDirectWaves; ++w) m = fmaxf(m, red[w]);
-    sdirect = m / 448.0f;
+    sdirect = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, m / 448.0f)));
 #pragma unroll
-    for (int j = 0; j < kMoeMaxHidden / 8 / kThreads; ++j) {
-      const int c = j * kThreads + threadIdx.x;
-      if (c >= pieces) continue;
+    for (int j = 0; j < kTokPieces; ++j) {
       uint32_t w[2] = {0, 0};
-      if (sdirect > 0.f) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const float lo = __builtin_bit_cast(float, v[j][d] << 16);
-          const float hi = __builtin_bit_cast(float, v[j][d] & 0xffff0000u);
-          w[d / 2] |= (e4m3_code(lo / sdirect) | (e4m3_code(hi / sdirect) << 8)) << (16 * (d % 2));
-        }
+      for (int d = 0; d < 4; ++d) {
+        const float lo = __builtin_bit_cast(float, tok[j][d] << 16);
+        const float hi = __builtin_bit_cast(float, tok[j][d] & 0xffff0000u);
+        w[d / 2] |= (e4m3_code(lo / sdirect) | (e4m3_code(hi / sdirect) << 8)) << (16 * (d % 2));
       }
-      *reinterpret_cast<uint2*>(codes + 8 * c) = make_uint2(w[0], w[1]);
+      const uint2 pk = sdirect > 0.f ? make_uint2(w[0], w[1]) : make_uint2(0u, 0u);   // a zero token: codes 0
+      *reinterpret_cast<uint2*>(codes + 8 * min(j * kThreads + static_cast<int>(threadIdx.x), H / 8 - 1)) = pk;
     }
     __syncthreads();
   };
@@ -371,6 +377,8 @@ __global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_k
   // first chunks' weight loads go out before the token is quantised, which hides the
   // quantisation behind them.
   if constexpr (DIRECT) {
+    load_token();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = 0; d < kDepth - 1; ++d) {
       const uint32_t st = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(2048 * min(d, nch - 1)));
@@ -379,6 +387,7 @@ __global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_k
       au[d][0] = wload16(rw, ou, st);
       au[d][1] = wload16(rw, ou + 1024, st);
     }
+    __builtin_amdgcn_sched_barrier(0);
     quantise_token();
 #pragma unroll
     for (int d = 0; d < kDepth - 1; ++d) load_codes(d, min(d, nch - 1));
@@ -408,10 +417,15 @@ __global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_k
     act[i] = g / (1.0f + expf(-g)) * u;
     amax = fmaxf(amax, fabsf(act[i]));
   }
-  if (valid) *reinterpret_cast<f32x4*>(a.act + int64_t(p) * a.I + g0 + 4 * q) = act;
+  if (!live) {
+    if (ib == 0 && lane == 0 && a.err)
+      __hip_atomic_fetch_or(a.err, HPA_DEVERR_MOE_EXPERT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (valid) *reinterpret_cast<f32x4*>(a.act + int64_t(p) * I + g0 + 4 * q) = act;
   amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
   amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-  if (valid && q == 0) a.amax[int64_t(p) * (a.I / 16) + ib] = amax;
+  if (valid && q == 0) a.amax[int64_t(p) * (I / 16) + ib] = amax;
 }
 
 // Requantise one pair's activation row: scale = max of its slice maxima / 448.
@@ -420,48 +434,43 @@ __global__ __launch_bounds__(kMoeThreads) void moe_quant_act_kernel(MoeArgs a) {
   const int p = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   static_assert(kMoeMaxInter / 16 <= kMoeThreads, "one slice maximum per thread");
-  // the id and the slice maxima (one per thread) are loaded together
-  const int e = a.ids[p];
-  float amax = tid < a.I / 16 ? a.amax[int64_t(p) * (a.I / 16) + tid] : 0.f;
-  if (e < 0 || e >= a.E) return;                    // uniform: the whole block
-  amax = wave_max(amax);
+  constexpr int kPieces = kMoeMaxInter / 4 / kMoeThreads;       // pieces of 4 per thread
+  // the slice maxima (one per thread) and the row are loaded together, with no branch
+  // (indexes past the end clamped: the maximum is unchanged, the piece is stored again
+  // with the same codes). Every pair is requantised, also one whose expert id is
+  // outside [0, E): its row is in no pair block, so nothing reads its codes or scale.
+  const float amax_t = a.amax[int64_t(p) * (a.I / 16) + min(tid, a.I / 16 - 1)];
+  const float* row = a.act + int64_t(p) * a.I;
+  f32x4 v[kPieces];
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j) v[j] = *reinterpret_cast<const f32x4*>(row + 4 * min(j * kMoeThreads + tid, a.I / 4 - 1));
+  float amax = wave_max(amax_t);
   if (lane == 0) red[wave] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = amax / 448.0f;
+  const float s = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, amax / 448.0f)));
   if (tid == 0) a.sa[p] = s;
-  const float* row = a.act + int64_t(p) * a.I;
-  for (int c = tid; c < a.I / 4; c += kMoeThreads) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(row + 4 * c);
-    uint32_t w = 0;
-    if (s > 0.f) {
 #pragma unroll
-      for (int d = 0; d < 4; ++d) w |= e4m3_code(v[d] / s) << (8 * d);
-    }
-    *reinterpret_cast<uint32_t*>(a.act8 + int64_t(p) * a.I + 4 * c) = w;
+  for (int j = 0; j < kPieces; ++j) {
+    if (j * kMoeThreads >= a.I / 4) break;          // uniform
+    uint32_t w = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) w |= e4m3_code(v[j][d] / s) << (8 * d);
+    w = s > 0.f ? w : 0u;
+    *reinterpret_cast<uint32_t*>(a.act8 + int64_t(p) * a.I + 4 * min(j * kMoeThreads + tid, a.I / 4 - 1)) = w;
   }
 }
 
-// Down + scales + routing weight: one wave per (pair block, 16 rows of H); DIRECT:
-// block gb is pair gb alone.
-template <bool DIRECT>
+// Down + scales + routing weight: one wave per (pair block, 16 rows of H).
 __global__ __launch_bounds__(64) void moe_down_kernel(MoeArgs a) {
-  const int nb = DIRECT ? static_cast<int>(blockIdx.x) / a.P : static_cast<int>(blockIdx.x) % (a.H / 16);
-  const int gb = DIRECT ? static_cast<int>(blockIdx.x) % a.P : static_cast<int>(blockIdx.x) / (a.H / 16);
+  const int nb = static_cast<int>(blockIdx.x) % (a.H / 16);
+  const int gb = static_cast<int>(blockIdx.x) / (a.H / 16);
   const int lane = threadIdx.x, m16 = lane & 15, q = lane >> 4;
-  int e, n, p;
-  if constexpr (DIRECT) {
-    e = a.ids[gb];
-    if (e < 0 || e >= a.E) return;
-    n = 1;
-    p = m16 < n ? gb : 0;
-  } else {
-    if (gb >= *a.nblk) return;
-    e = a.blk[gb];
-    const int first = a.blk[a.P + gb];
-    n = a.blk[2 * a.P + gb];
-    p = m16 < n ? a.list[first + m16] : 0;
-  }
+  if (gb >= *a.nblk) return;
+  const int e = a.blk[gb];
+  const int first = a.blk[a.P + gb];
+  const int n = a.blk[2 * a.P + gb];
+  const int p = m16 < n ? a.list[first + m16] : 0;
   const bool valid = m16 < n;
   const int nch = a.I / 128;
   const rsrc_t rw = make_rsrc(a.w2 + int64_t(e) * a.H * a.I, static_cast<uint32_t>(int64_t(a.H) * a.I));
@@ -505,6 +514,123 @@ __global__ __launch_bounds__(64) void moe_down_kernel(MoeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = acc[i] * f * s2[i];
     *reinterpret_cast<f32x4*>(a.ybuf + int64_t(p) * a.H + n0 + 4 * q) = y;
+  }
+}
+
+// Few pairs: requantisation, Down and the top-k merge in one launch. Workgroup (token
+// t, 16 rows n0 .. n0 + 15 of H) has one wave per slot k of the token. Wave k takes the
+// activation scale of pair p = t K + k from the slice maxima Gate-Up wrote (the same
+// maximum as over the row), encodes the row into its own LDS region (the grouped
+// path's requantisation, same codes and scale), streams its expert's 16 rows of W2
+// against it, and the workgroup adds the K results in k order (the grouped path's
+// merge order, so both paths give the same bits). Dynamic LDS: K * I bytes.
+template <int VP>   // activation pieces of 4 per lane: I <= 256 VP
+__global__ __launch_bounds__(64 * kMoeMaxTopK) void moe_down_direct_kernel(const int32_t* __restrict__ ids, const uint8_t* __restrict__ w2,
+    const float* __restrict__ act, const float* __restrict__ amaxs, const float* __restrict__ wts, int T, int K, int H,
+    int I, MoeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int t = static_cast<int>(blockIdx.x) % T, nb = static_cast<int>(blockIdx.x) / T;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63, m16 = lane & 15, q = lane >> 4;
+  const int p = t * K + wave;
+  const int nch = I / 128, n0 = nb * 16;
+  // Everything the wave needs is requested before the first wait, and nothing is
+  // loaded under a branch (the compiler would move such a load to its use and wait
+  // there): the expert id; the slice maxima (I / 16 <= 64 kSlices; indexes past the end
+  // clamped to the last entry, which leaves the maximum unchanged) and the activation
+  // row (I / 4 pieces of 4, VP per lane, clamped alike), neither of which waits for
+  // the id; then, once the id is in, the
+  // epilogue's scales and the first weight chunks.
+  const int e = ids[p];
+  const float wt = wts[p];
+  constexpr int kSlices = VP / 4 > 0 ? VP / 4 : 1;
+  float sl[kSlices];
+  f32x4 v[VP];
+  const float* arow = act + int64_t(p) * I;
+  const float* mrow = amaxs + int64_t(p) * (I / 16);
+#pragma unroll
+  for (int j = 0; j < kSlices; ++j) sl[j] = mrow[min(j * 64 + lane, I / 16 - 1)];
+#pragma unroll
+  for (int j = 0; j < VP; ++j) v[j] = *reinterpret_cast<const f32x4*>(arow + 4 * min(j * 64 + lane, I / 4 - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  const bool live = e >= 0 && e < a.E;             // uniform in the wave
+  const int ee = live ? e : 0;                     // no valid expert: expert 0's rows, result unused
+  const rsrc_t rw = make_rsrc(w2 + int64_t(ee) * H * I, static_cast<uint32_t>(int64_t(H) * I));
+  const uint32_t ow = static_cast<uint32_t>(nb * nch * 2048 + 16 * lane);
+  const f32x4 s2 = *reinterpret_cast<const f32x4*>(a.s2 + int64_t(ee) * H + n0 + 4 * q);
+  constexpr int kDepth = 4;
+  u32x4 aw[kDepth][2], ba[kDepth][2];
+  auto wload = [&](int slot, int c) {
+    const uint32_t st = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(2048 * c));
+    aw[slot][0] = wload16(rw, ow, st);
+    aw[slot][1] = wload16(rw, ow + 1024, st);
+  };
+#pragma unroll
+  for (int d = 0; d < kDepth - 1; ++d) wload(d, min(d, nch - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < kSlices; ++j) amax = fmaxf(amax, sl[j]);
+  amax = wave_max(amax);
+  const float s = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, amax / 448.0f)));
+  const float f = live ? s * wt : 0.f;
+  uint8_t* codes = lds + wave * I;
+#pragma unroll
+  for (int j = 0; j < VP; ++j) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) w |= e4m3_code(v[j][d] / s) << (8 * d);
+    w = s > 0.f ? w : 0u;                            // a zero row: codes 0 (selected, not branched)
+    // a lane past the end stores the last piece's codes again (the same value; no
+    // branch, so the encode stays where the loads have landed)
+    *reinterpret_cast<uint32_t*>(codes + 4 * min(j * 64 + lane, I / 4 - 1)) = w;
+  }
+  __syncthreads();
+  // B operand: column 0 is the pair, lane group q takes each chunk's 32 codes
+  const bool col0 = m16 == 0;
+  auto cload = [&](int slot, int c) {
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    ba[slot][0] = col0 ? *reinterpret_cast<const u32x4*>(codes + 128 * c + 32 * q) : z;
+    ba[slot][1] = col0 ? *reinterpret_cast<const u32x4*>(codes + 128 * c + 32 * q + 16) : z;
+  };
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (live) {
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d) cload(d, min(d, nch - 1));
+    int c = 0;
+    for (; c + kDepth <= nch; c += kDepth) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int nx = min(c + d + kDepth - 1, nch - 1), slot = (d + kDepth - 1) % kDepth;
+        wload(slot, nx);
+        cload(slot, nx);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(aw[d][0], aw[d][1]),
+                                                               operand(ba[d][0], ba[d][1]), acc, 0, 0, 0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d)
+      if (c + d < nch)
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(aw[d][0], aw[d][1]),
+                                                               operand(ba[d][0], ba[d][1]), acc, 0, 0, 0, 0, 0, 0);
+  }
+  __syncthreads();                                 // every wave is done with its codes
+  // lane (0, q) holds rows n0 + 4 q + i; a slot with no valid expert stores +0, which
+  // leaves the sum (started at +0, so never -0) unchanged: the grouped merge skips it
+  float* ys = reinterpret_cast<float*>(lds);
+  if (col0) {
+    f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = acc[i] * f * s2[i];
+    }
+    *reinterpret_cast<f32x4*>(ys + wave * 16 + 4 * q) = y;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < 16) {
+    float sum = 0.f;
+    for (int k = 0; k < K; ++k) sum += ys[k * 16 + lane];
+    a.out[int64_t(t) * H + n0 + lane] = f32_to_bf16(sum);
   }
 }
 
@@ -557,19 +683,22 @@ __global__ __launch_bounds__(kMoeThreads) void moe_pack_kernel(const uint8_t* __
 
 hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
   if (a.P <= kMoeDirectMaxPairs) {
-    // a few pairs: one pair per block, no routing index, tokens quantised in Gate-Up
+    // a few pairs: one pair per block, no routing index; Gate-Up quantises the tokens,
+    // Down requantises the activations and merges
     hipLaunchKernelGGL(moe_gate_up_kernel<true>, dim3(static_cast<unsigned>(a.P * (a.I / (16 * kDirectWaves)))),
-                       dim3(64 * kDirectWaves), 0, stream, a);
-    hipLaunchKernelGGL(moe_quant_act_kernel, dim3(a.P), dim3(kMoeThreads), 0, stream, a);
-    hipLaunchKernelGGL(moe_down_kernel<true>, dim3(static_cast<unsigned>(a.P * (a.H / 16))), dim3(64), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(moe_prepare_kernel, dim3(a.T + 1), dim3(kMoeThreads), 0, stream, a);
-    hipLaunchKernelGGL(moe_gate_up_kernel<false>, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.I / 16))), dim3(64),
-                       0, stream, a);
-    hipLaunchKernelGGL(moe_quant_act_kernel, dim3(a.P), dim3(kMoeThreads), 0, stream, a);
-    hipLaunchKernelGGL(moe_down_kernel<false>, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.H / 16))), dim3(64), 0,
-                       stream, a);
+                       dim3(64 * kDirectWaves), 0, stream, a.ids, a.w1, a.x, a.P, a.K, a.E, a.H, a.I, a);
+    hipLaunchKernelGGL(a.I <= 1024 ? moe_down_direct_kernel<4>
+                       : a.I <= 2048 ? moe_down_direct_kernel<8> : moe_down_direct_kernel<kMoeMaxInter / 256>,
+                       dim3(static_cast<unsigned>(a.T * (a.H / 16))), dim3(64 * a.K), static_cast<size_t>(a.K) * a.I,
+                       stream, a.ids, a.w2, a.act, a.amax, a.wts, a.T, a.K, a.H, a.I, a);
+    return hipGetLastError();
   }
+  hipLaunchKernelGGL(moe_prepare_kernel, dim3(a.T + 1), dim3(kMoeThreads), 0, stream, a);
+  hipLaunchKernelGGL(moe_gate_up_kernel<false>, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.I / 16))), dim3(64),
+                     0, stream, a.ids, a.w1, a.x, a.P, a.K, a.E, a.H, a.I, a);
+  hipLaunchKernelGGL(moe_quant_act_kernel, dim3(a.P), dim3(kMoeThreads), 0, stream, a);
+  hipLaunchKernelGGL(moe_down_kernel, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.H / 16))), dim3(64), 0, stream,
+                     a);
   hipLaunchKernelGGL(moe_merge_kernel, dim3((a.H / 4 + kMoeThreads - 1) / kMoeThreads, a.T), dim3(kMoeThreads), 0,
                      stream, a);
   return hipGetLastError();

@@ -90,6 +90,18 @@ def test_moe_decode_shape_sampled_tokens(T):
     assert np.array_equal(d.output_f64(), got)
 
 
+@pytest.mark.parametrize("shape", [(1, 32, 16, 256, 4096), (2, 8, 8, 512, 2048), (16, 4, 1, 128, 384),
+                                   (1, 16, 8, 2048, 768)])
+def test_moe_few_pair_shapes(shape):
+    """Calls of at most 16 pairs (Gate-Up quantises the token; one Down launch
+    requantises, multiplies and merges, one workgroup of top_k waves per token and 16
+    rows): the widest workgroup (top 16, inter 4096: 1024 threads, 64 KB of codes), the
+    middle activation width, one-wave workgroups (16 tokens x top 1), the bench's
+    one-token shape on every row."""
+    T, E, K, H, I = shape
+    _check(inputs.moe_workload(T, E, K, H, I, seed=3 * sum(shape)))
+
+
 def test_moe_edge_cases():
     """A zero token gives a zero row; an expert id out of range adds nothing and is
     reported; a token routed twice to one expert adds both slots; more than 16 tokens
