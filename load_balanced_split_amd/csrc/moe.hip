@@ -24,7 +24,7 @@
 //      against the block's activation codes; scales and routing weight applied.
 //  moe_merge_kernel     out[t] = sum over k, in k order, of the pair results -> bf16.
 // With at most kMoeDirectMaxPairs pairs there is no routing index and two launches:
-//  moe_gate_up_kernel<true>  every pair its own block; the workgroup quantises the
+//  moe_gate_up_direct_kernel every pair its own block; the workgroup quantises the
 //      pair's token itself.
 //  moe_down_direct_kernel    one workgroup per (token, 16 rows of H), one wave per slot
 //      of the token: requantisation, Down, scales and the merge in k order.
@@ -246,13 +246,18 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
 // routing index): block gb is pair gb alone, a workgroup of kDirectWaves waves takes
 // as many row blocks of it and quantises its token itself (the same arithmetic as the
 // prepare kernel, so the same codes and scale) into LDS, from where lane group q of
-// column 0 takes each chunk's 32 codes. The sizes and pointers the first loads need
-// come as leading arguments, which the launch preloads into scalar registers.
+// column 0 takes each chunk's 32 codes. Grouped: the block's table entry, then its
+// pairs from the list, their token codes from the routing pass. The two kernels below
+// pass the pointers and sizes of their first loads as leading arguments, which the
+// launch preloads into scalar registers (struct arguments are not), and issue the
+// first weight chunks as soon as the expert id is in.
 constexpr int kDirectWaves = 2;
 template <bool DIRECT>
-__global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_kernel(
-    const int32_t* __restrict__ ids, const uint8_t* __restrict__ w1, const uint16_t* __restrict__ x, int P, int K,
-    int E, int H, int I, MoeArgs a) {
+__device__ __forceinline__ void gate_up(const int32_t* __restrict__ ids, const int32_t* __restrict__ nblk,
+                                        const int32_t* __restrict__ blk, const int32_t* __restrict__ list,
+                                        const uint8_t* __restrict__ w1, const uint16_t* __restrict__ x,
+                                        const uint8_t* __restrict__ x8, int P, int K, int E, int H, int I,
+                                        const MoeArgs& a) {
   __shared__ __attribute__((aligned(16))) uint8_t codes[DIRECT ? kMoeMaxHidden : 16];
   __shared__ float red[kDirectWaves];
   const int wave = DIRECT ? static_cast<int>(threadIdx.x >> 6) : 0;
@@ -263,41 +268,42 @@ __global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_k
                      (DIRECT ? kDirectWaves : 1) + wave;
   const int gb = DIRECT ? static_cast<int>(blockIdx.x) % P : static_cast<int>(blockIdx.x) / nib;
   const int lane = threadIdx.x & 63, m16 = lane & 15, q = lane >> 4;
-  int e, n, p;
+  int e, n, praw = 0;
   bool live = true;
   if constexpr (DIRECT) {
     // no early exit for an id outside [0, E): the loads below do not wait for the
     // test; such a pair streams expert 0, stores nothing and is reported once
-    p = gb;
-    e = ids[p];
+    e = ids[gb];
     live = e >= 0 && e < E;
     e = live ? e : 0;
     n = 1;
   } else {
-    if (gb >= *a.nblk) return;
-    e = a.blk[gb];
-    const int first = a.blk[P + gb];
-    n = a.blk[2 * P + gb];
-    p = m16 < n ? a.list[first + m16] : 0;
+    // the block count and the block's table entry in one round trip (gb < BMAX <= P:
+    // the entry is in bounds, also past the count); the empty asm takes all four
+    // values before the exit test, which keeps the entry's loads ahead of it
+    int nbk = *nblk, first;
+    e = blk[gb];
+    first = blk[P + gb];
+    n = blk[2 * P + gb];
+    asm volatile("" : "+s"(nbk), "+s"(e), "+s"(first), "+s"(n));
+    if (gb >= nbk) return;
+    praw = list[first + min(m16, n - 1)];          // a lane past the block re-reads its last pair
   }
   const bool valid = m16 < n;
-  if constexpr (DIRECT) p = valid ? p : 0;
-  const int t = p / K;
-  float sdirect = 0.f;
   const int nch = H / 128;
   const rsrc_t rw = make_rsrc(w1 + int64_t(e) * 2 * I * H, static_cast<uint32_t>(int64_t(2) * I * H));
-  const rsrc_t rx = make_rsrc(a.x8, static_cast<uint32_t>(int64_t(a.T) * H));
+  const rsrc_t rx = make_rsrc(x8, static_cast<uint32_t>(int64_t(a.T) * H));
   const int g0 = ib * 16;
   // packed tiles of row block rb: 2 KB per 128-wide chunk, chunks consecutive
   const uint32_t og = static_cast<uint32_t>(ib * nch * 2048 + 16 * lane);
   const uint32_t ou = static_cast<uint32_t>((I / 16 + ib) * nch * 2048 + 16 * lane);
-  // padding pair columns read past the buffer: zeros
-  const uint32_t ox = valid ? static_cast<uint32_t>(t * H + 32 * q) : 0x80000000u;
   // the epilogue's scales, requested before the weight stream
   const float* s1e = a.s1 + int64_t(e) * 2 * I;
   const f32x4 sg = *reinterpret_cast<const f32x4*>(s1e + g0 + 4 * q);
   const f32x4 su = *reinterpret_cast<const f32x4*>(s1e + I + g0 + 4 * q);
-  const float sx_t = DIRECT ? 0.f : a.sx[t];
+  int p = 0;
+  uint32_t ox = 0;                                   // grouped: set once the pair is in
+  float sx_t = 0.f, sdirect = 0.f;
   f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = accg;
   constexpr int kDepth = DIRECT ? 8 : 4;   // DIRECT: few waves, each streams a whole pair's rows
   u32x4 ag[kDepth][2], au[kDepth][2], bx[kDepth][2];
@@ -372,13 +378,7 @@ __global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_k
     accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(au[slot][0], au[slot][1]), B, accu,
                                                             0, 0, 0, 0, 0, 0);
   };
-  // chunk c lives in ring slot c % kDepth (compile-time: the loop is unrolled by kDepth);
-  // the loads of chunk c + kDepth - 1 go out before chunk c is multiplied. DIRECT: the
-  // first chunks' weight loads go out before the token is quantised, which hides the
-  // quantisation behind them.
-  if constexpr (DIRECT) {
-    load_token();
-    __builtin_amdgcn_sched_barrier(0);
+  auto wprologue = [&] {
 #pragma unroll
     for (int d = 0; d < kDepth - 1; ++d) {
       const uint32_t st = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(2048 * min(d, nch - 1)));
@@ -387,13 +387,34 @@ __global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_k
       au[d][0] = wload16(rw, ou, st);
       au[d][1] = wload16(rw, ou + 1024, st);
     }
+  };
+  // chunk c lives in ring slot c % kDepth (compile-time: the loop is unrolled by kDepth);
+  // the loads of chunk c + kDepth - 1 go out before chunk c is multiplied. The first
+  // chunks' weight loads go out before the token is quantised (DIRECT) or while the
+  // pair list is loading (grouped).
+  if constexpr (DIRECT) {
+    load_token();
+    __builtin_amdgcn_sched_barrier(0);
+    wprologue();
     __builtin_amdgcn_sched_barrier(0);
     quantise_token();
+    p = valid ? gb : 0;
 #pragma unroll
     for (int d = 0; d < kDepth - 1; ++d) load_codes(d, min(d, nch - 1));
   } else {
+    wprologue();
+    __builtin_amdgcn_sched_barrier(0);
+    p = valid ? praw : 0;
+    const int t = p / K;
+    // padding pair columns read past the buffer: zeros
+    ox = valid ? static_cast<uint32_t>(t * H + 32 * q) : 0x80000000u;
+    sx_t = a.sx[t];
 #pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d) load(d, min(d, nch - 1));
+    for (int d = 0; d < kDepth - 1; ++d) {
+      const uint32_t sc = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(128 * min(d, nch - 1)));
+      bx[d][0] = aload16(rx, ox, sc);
+      bx[d][1] = aload16(rx, ox + 16, sc);
+    }
   }
   int c = 0;
   for (; c + kDepth <= nch; c += kDepth) {
@@ -426,6 +447,21 @@ __global__ __launch_bounds__(DIRECT ? 64 * kDirectWaves : 64) void moe_gate_up_k
   amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
   amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
   if (valid && q == 0) a.amax[int64_t(p) * (I / 16) + ib] = amax;
+}
+
+__global__ __launch_bounds__(64 * kDirectWaves) void moe_gate_up_direct_kernel(
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ w1, const uint16_t* __restrict__ x, int P, int K,
+    int E, int H, int I, MoeArgs a) {
+  gate_up<true>(ids, nullptr, nullptr, nullptr, w1, x, nullptr, P, K, E, H, I, a);
+}
+
+__global__ __launch_bounds__(64) void moe_gate_up_kernel(const int32_t* __restrict__ nblk,
+                                                         const int32_t* __restrict__ blk,
+                                                         const int32_t* __restrict__ list,
+                                                         const uint8_t* __restrict__ w1,
+                                                         const uint8_t* __restrict__ x8, int P, int K, int H, int I,
+                                                         MoeArgs a) {
+  gate_up<false>(nullptr, nblk, blk, list, w1, nullptr, x8, P, K, a.E, H, I, a);
 }
 
 // Requantise one pair's activation row: scale = max of its slice maxima / 448.
@@ -461,29 +497,48 @@ __global__ __launch_bounds__(kMoeThreads) void moe_quant_act_kernel(MoeArgs a) {
   }
 }
 
-// Down + scales + routing weight: one wave per (pair block, 16 rows of H).
-__global__ __launch_bounds__(64) void moe_down_kernel(MoeArgs a) {
-  const int nb = static_cast<int>(blockIdx.x) % (a.H / 16);
-  const int gb = static_cast<int>(blockIdx.x) / (a.H / 16);
+// Down + scales + routing weight: one wave per (pair block, 16 rows of H). As in
+// Gate-Up: the first loads' pointers and sizes are preloaded arguments, the block count
+// and table entry come in one round trip, the first weight chunks go out while the
+// pair list is loading.
+__global__ __launch_bounds__(64) void moe_down_kernel(const int32_t* __restrict__ nblk, const int32_t* __restrict__ blk,
+                                                      const int32_t* __restrict__ list, const uint8_t* __restrict__ w2,
+                                                      const uint8_t* __restrict__ act8, int P, int H, int I,
+                                                      MoeArgs a) {
+  const int nb = static_cast<int>(blockIdx.x) % (H / 16);
+  const int gb = static_cast<int>(blockIdx.x) / (H / 16);
   const int lane = threadIdx.x, m16 = lane & 15, q = lane >> 4;
-  if (gb >= *a.nblk) return;
-  const int e = a.blk[gb];
-  const int first = a.blk[a.P + gb];
-  const int n = a.blk[2 * a.P + gb];
-  const int p = m16 < n ? a.list[first + m16] : 0;
+  int nbk = *nblk, e = blk[gb], first = blk[P + gb], n = blk[2 * P + gb];
+  asm volatile("" : "+s"(nbk), "+s"(e), "+s"(first), "+s"(n));   // all four before the exit test
+  if (gb >= nbk) return;
+  const int praw = list[first + min(m16, n - 1)];   // a lane past the block re-reads its last pair
   const bool valid = m16 < n;
-  const int nch = a.I / 128;
-  const rsrc_t rw = make_rsrc(a.w2 + int64_t(e) * a.H * a.I, static_cast<uint32_t>(int64_t(a.H) * a.I));
-  const rsrc_t ra = make_rsrc(a.act8, static_cast<uint32_t>(int64_t(a.P) * a.I));
+  const int nch = I / 128;
+  const rsrc_t rw = make_rsrc(w2 + int64_t(e) * H * I, static_cast<uint32_t>(int64_t(H) * I));
+  const rsrc_t ra = make_rsrc(act8, static_cast<uint32_t>(int64_t(P) * I));
   const int n0 = nb * 16;
   const uint32_t ow = static_cast<uint32_t>(nb * nch * 2048 + 16 * lane);   // packed row block nb
-  const uint32_t oa = valid ? static_cast<uint32_t>(p * a.I + 32 * q) : 0x80000000u;
-  // the epilogue's scales and weight, requested before the weight stream
-  const f32x4 s2 = *reinterpret_cast<const f32x4*>(a.s2 + int64_t(e) * a.H + n0 + 4 * q);
-  const float f = valid ? a.sa[p] * a.wts[p] : 0.f;
+  // the epilogue's scales, requested before the weight stream
+  const f32x4 s2 = *reinterpret_cast<const f32x4*>(a.s2 + int64_t(e) * H + n0 + 4 * q);
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int kDepth = 4;
   u32x4 aw[kDepth][2], ba[kDepth][2];
+#pragma unroll
+  for (int d = 0; d < kDepth - 1; ++d) {
+    const uint32_t st = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(2048 * min(d, nch - 1)));
+    aw[d][0] = wload16(rw, ow, st);
+    aw[d][1] = wload16(rw, ow + 1024, st);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int p = valid ? praw : 0;
+  const uint32_t oa = valid ? static_cast<uint32_t>(p * I + 32 * q) : 0x80000000u;
+  const float fsa = a.sa[p], fwt = a.wts[p];        // unconditional (p is a pair): no branch, no wait here
+#pragma unroll
+  for (int d = 0; d < kDepth - 1; ++d) {
+    const uint32_t sc = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(128 * min(d, nch - 1)));
+    ba[d][0] = aload16(ra, oa, sc);
+    ba[d][1] = aload16(ra, oa + 16, sc);
+  }
   auto load = [&](int slot, int c) {
     const uint32_t sc = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(128 * c));
     const uint32_t st = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(2048 * c));
@@ -496,8 +551,6 @@ __global__ __launch_bounds__(64) void moe_down_kernel(MoeArgs a) {
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(aw[slot][0], aw[slot][1]),
                                                            operand(ba[slot][0], ba[slot][1]), acc, 0, 0, 0, 0, 0, 0);
   };
-#pragma unroll
-  for (int d = 0; d < kDepth - 1; ++d) load(d, min(d, nch - 1));
   int c = 0;
   for (; c + kDepth <= nch; c += kDepth) {
 #pragma unroll
@@ -511,9 +564,10 @@ __global__ __launch_bounds__(64) void moe_down_kernel(MoeArgs a) {
     if (c + d < nch) mul(d);
   if (valid) {
     f32x4 y;
+    const float f = fsa * fwt;
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = acc[i] * f * s2[i];
-    *reinterpret_cast<f32x4*>(a.ybuf + int64_t(p) * a.H + n0 + 4 * q) = y;
+    *reinterpret_cast<f32x4*>(a.ybuf + int64_t(p) * H + n0 + 4 * q) = y;
   }
 }
 
@@ -685,7 +739,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
   if (a.P <= kMoeDirectMaxPairs) {
     // a few pairs: one pair per block, no routing index; Gate-Up quantises the tokens,
     // Down requantises the activations and merges
-    hipLaunchKernelGGL(moe_gate_up_kernel<true>, dim3(static_cast<unsigned>(a.P * (a.I / (16 * kDirectWaves)))),
+    hipLaunchKernelGGL(moe_gate_up_direct_kernel, dim3(static_cast<unsigned>(a.P * (a.I / (16 * kDirectWaves)))),
                        dim3(64 * kDirectWaves), 0, stream, a.ids, a.w1, a.x, a.P, a.K, a.E, a.H, a.I, a);
     hipLaunchKernelGGL(a.I <= 1024 ? moe_down_direct_kernel<4>
                        : a.I <= 2048 ? moe_down_direct_kernel<8> : moe_down_direct_kernel<kMoeMaxInter / 256>,
@@ -694,11 +748,11 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   hipLaunchKernelGGL(moe_prepare_kernel, dim3(a.T + 1), dim3(kMoeThreads), 0, stream, a);
-  hipLaunchKernelGGL(moe_gate_up_kernel<false>, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.I / 16))), dim3(64),
-                     0, stream, a.ids, a.w1, a.x, a.P, a.K, a.E, a.H, a.I, a);
+  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.I / 16))), dim3(64), 0,
+                     stream, a.nblk, a.blk, a.list, a.w1, a.x8, a.P, a.K, a.H, a.I, a);
   hipLaunchKernelGGL(moe_quant_act_kernel, dim3(a.P), dim3(kMoeThreads), 0, stream, a);
   hipLaunchKernelGGL(moe_down_kernel, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.H / 16))), dim3(64), 0, stream,
-                     a);
+                     a.nblk, a.blk, a.list, a.w2, a.act8, a.P, a.H, a.I, a);
   hipLaunchKernelGGL(moe_merge_kernel, dim3((a.H / 4 + kMoeThreads - 1) / kMoeThreads, a.T), dim3(kMoeThreads), 0,
                      stream, a);
   return hipGetLastError();
