@@ -111,8 +111,10 @@ __device__ inline uint16_t f32_to_bf16(float f) {
 // Quantise one token row (blocks 0 .. T-1), or build the routing index (block T).
 __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
   __shared__ float red[4];
-  __shared__ int cnt[kMoeMaxExperts + 1];
-  __shared__ int run[kMoeMaxExperts];
+  // routing block: pairs are placed by four waves, wave w taking the w-th quarter of the
+  // pair range; cntw[w][e] counts expert e's pairs in quarter w, then holds wave w's
+  // running slot for e
+  __shared__ int cntw[4][kMoeMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (blockIdx.x < static_cast<unsigned>(a.T)) {
     const int t = blockIdx.x;
@@ -153,8 +155,14 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
     }
     return;
   }
-  // routing index: counts per expert, their prefix (list offsets) and the pair blocks
-  for (int e = tid; e < a.E; e += kMoeThreads) cnt[e] = 0;
+  // routing index: counts per expert and quarter, their prefix (list offsets) and the
+  // pair blocks
+  static_assert(kMoeThreads == 4 * 64, "one wave per quarter");
+  const int Q = (a.P + 3) / 4;                      // pairs per quarter
+  for (int e = tid; e < a.E; e += kMoeThreads) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) cntw[w][e] = 0;
+  }
   __syncthreads();
   // the ids are read in batches of 16 per thread, all loads of a batch issued together
   constexpr int kIdBatch = 16;
@@ -170,8 +178,9 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
 #pragma unroll
     for (int i = 0; i < kIdBatch; ++i) {
       if (base + i * kMoeThreads >= a.P) break;               // uniform
-      if (base + i * kMoeThreads + tid >= a.P) continue;
-      if (v[i] >= 0 && v[i] < a.E) atomicAdd(&cnt[v[i]], 1);
+      const int p = base + i * kMoeThreads + tid;
+      if (p >= a.P) continue;
+      if (v[i] >= 0 && v[i] < a.E) atomicAdd(&cntw[p / Q][v[i]], 1);
       else bad = true;
     }
   }
@@ -181,7 +190,12 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
     int carry = 0, bcarry = 0;
     for (int base = 0; base < a.E; base += 64) {
       const int e = base + lane;
-      const int c = e < a.E ? cnt[e] : 0;
+      int cq[4] = {0, 0, 0, 0};
+      if (e < a.E) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) cq[w] = cntw[w][e];
+      }
+      const int c = cq[0] + cq[1] + cq[2] + cq[3];
       const int nb = (c + kPairsPerBlock - 1) / kPairsPerBlock;
       int x = c, y = nb;
 #pragma unroll
@@ -193,7 +207,14 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
         }
       }
       if (e < a.E) {
-        run[e] = carry + x - c;
+        // wave w's first slot for e: the expert's list offset plus its pairs in
+        // earlier quarters
+        int r = carry + x - c;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          cntw[w][e] = r;
+          r += cq[w];
+        }
         for (int b = 0; b < nb; ++b) {          // this expert's pair blocks
           const int g = bcarry + y - nb + b;
           a.blk[g] = e;
@@ -207,36 +228,37 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
     if (lane == 0) *a.nblk = bcarry;
   }
   __syncthreads();
-  // place the pairs in pair order, 64 at a time by wave 0: the lanes holding the same
-  // expert are found by matching the bits of expert + 1 (0: skipped) with ballots; a
-  // pair's slot is its expert's running count plus the matching lanes below it, and
-  // the lowest of those lanes advances the count (LDS accesses of a wave stay in order)
-  if (tid < 64) {
-    for (int base = 0; base < a.P; base += kIdBatch * 64) {
-      int v[kIdBatch];
+  // wave w places the pairs of its quarter in pair order, 64 at a time: the lanes
+  // holding the same expert are found by matching the bits of expert + 1 (0: skipped)
+  // with ballots; a pair's slot is the wave's running slot for its expert plus the
+  // matching lanes below it, and the lowest of those lanes advances it (LDS accesses of
+  // a wave stay in order; each wave has its own row of running slots)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int q0 = wv * Q, q1 = min(a.P, q0 + Q);
+  for (int base = q0; base < q1; base += kIdBatch * 64) {
+    int v[kIdBatch];
 #pragma unroll
-      for (int i = 0; i < kIdBatch; ++i) {
-        const int p = base + 64 * i + lane;
-        v[i] = p < a.P ? a.ids[p] : -1;
+    for (int i = 0; i < kIdBatch; ++i) {
+      const int p = base + 64 * i + lane;
+      v[i] = p < q1 ? a.ids[p] : -1;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kIdBatch; ++i) {
+      if (base + 64 * i >= q1) break;                        // uniform
+      const int p = base + 64 * i + lane;
+      const int e = v[i] >= 0 && v[i] < a.E ? v[i] : -1;
+      const uint32_t key = static_cast<uint32_t>(e + 1);
+      uint64_t same = ~0ull;
+#pragma unroll
+      for (int b = 0; b < 11; ++b) {                         // kMoeMaxExperts + 1 < 2^11
+        const uint64_t ones = __ballot((key >> b) & 1u);
+        same &= ((key >> b) & 1u) ? ones : ~ones;
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < kIdBatch; ++i) {
-        if (base + 64 * i >= a.P) break;                     // uniform
-        const int p = base + 64 * i + lane;
-        const int e = v[i] >= 0 && v[i] < a.E ? v[i] : -1;
-        const uint32_t key = static_cast<uint32_t>(e + 1);
-        uint64_t same = ~0ull;
-#pragma unroll
-        for (int b = 0; b < 11; ++b) {                       // kMoeMaxExperts + 1 < 2^11
-          const uint64_t ones = __ballot((key >> b) & 1u);
-          same &= ((key >> b) & 1u) ? ones : ~ones;
-        }
-        const uint64_t below = same & ((1ull << lane) - 1ull);
-        if (e >= 0) {
-          a.list[run[e] + __popcll(below)] = p;
-          if (below == 0) run[e] += __popcll(same);
-        }
+      const uint64_t below = same & ((1ull << lane) - 1ull);
+      if (e >= 0) {
+        a.list[cntw[wv][e] + __popcll(below)] = p;
+        if (below == 0) cntw[wv][e] += __popcll(same);
       }
     }
   }

@@ -236,6 +236,23 @@ class MoeStep:
         raw = self.workspace.cpu().numpy()
         return raw[off: off + P * I * 4].view(np.float32).reshape(T, K, I)
 
+    def routing(self):
+        """The routing index the routing pass left in the workspace (calls of more than 16
+        pairs): the pair list [P], the pair-block table (expert, first list index, count)
+        as three arrays of the block count's length."""
+        mw = self.mw
+        al = lambda x: (x + 255) // 256 * 256
+        T, K, H = mw.tokens, mw.top_k, mw.hidden
+        P = T * K
+        raw = self.workspace.cpu().numpy()
+        o = al(T * H) + al(T * 4)
+        lst = raw[o: o + P * 4].view(np.int32).copy()
+        o += al(P * 4)
+        blk = raw[o: o + 3 * P * 4].view(np.int32).reshape(3, P)
+        o += al(3 * P * 4)
+        n = int(raw[o: o + 4].view(np.int32)[0])
+        return lst, blk[0, :n].copy(), blk[1, :n].copy(), blk[2, :n].copy()
+
     def token_codes(self):
         """The tokens' E4M3 codes [T, H] and fp32 scales [T] at the start of the workspace
         (written by the routing pass; calls of at most 16 pairs quantise inside Gate-Up and

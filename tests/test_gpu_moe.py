@@ -62,8 +62,26 @@ def _check(mw, tokens=None, act=True):
         x8, sx = d.token_codes()
         want8, wants = om.quantize_fp32(inputs_f32(mw.x))
         assert np.array_equal(sx, wants) and np.array_equal(x8, want8)
+        _check_routing(d, mw)
     assert int(d.err.item()) == 0
     return d, got
+
+
+def _check_routing(d, mw):
+    """The routing index: every valid pair listed once, grouped by expert in expert
+    order and in pair order inside a group; the pair blocks cut each group into runs of
+    at most 16, in list order."""
+    lst, be, bf, bn = d.routing()
+    ids = mw.ids.reshape(-1)
+    want, blocks = [], []
+    for e in range(mw.experts):
+        pairs = np.flatnonzero(ids == e)
+        for j in range(0, len(pairs), 16):
+            blocks.append((e, len(want) + j, min(16, len(pairs) - j)))
+        want.extend(pairs.tolist())
+    n = len(want)
+    assert np.array_equal(lst[:n], np.array(want, dtype=np.int32))
+    assert list(zip(be.tolist(), bf.tolist(), bn.tolist())) == blocks
 
 
 def inputs_f32(x_bits):
@@ -121,6 +139,7 @@ def test_moe_edge_cases():
     ref = om.fused_moe(mw.x, mw.ids, mw.weights, mw.w1, mw.s1, mw.w2, mw.s2)
     assert np.all(np.abs(got - ref) <= ATOL + RTOL * np.abs(ref))
     assert not got[3].any()
+    _check_routing(d, mw)                        # out-of-range ids are not listed
     # the same cases with few enough pairs (<= 16) that every pair is its own block and
     # Gate-Up quantises the tokens itself
     mw = inputs.moe_workload(4, 6, 3, 256, 128, seed=10)
