@@ -14,10 +14,10 @@
 //      amax / 448); block T builds the routing index: the pairs p = t K + k grouped
 //      by expert (each group in pair order, by a counting sort) and the table of
 //      pair blocks (expert, first pair, up to 16 pairs).
-//  moe_gate_up_kernel   one wave per (pair block, 16 rows of I): 16 gate and 16 up
-//      rows of W1 against the block's token codes on v_mfma_f32_16x16x128_f8f6f4,
-//      per-channel and token scales, SwiGLU; writes the fp32 activations and the
-//      largest magnitude of each 16-wide slice.
+//  moe_gate_up_kernel   one wave per (pair block, 16 or 32 rows of I): for each 16-row
+//      block, 16 gate and 16 up rows of W1 against the block's token codes on
+//      v_mfma_f32_16x16x128_f8f6f4, per-channel and token scales, SwiGLU; writes the
+//      fp32 activations and the largest magnitude of each 16-wide slice.
 //  moe_quant_act_kernel one block per pair: the activation row's scale (max of its
 //      slice maxima / 448) and E4M3 codes.
 //  moe_down_kernel      one wave per (pair block, 32 rows of H): two 16-row tiles of W2
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_prepare_kernel(MoeArgs a) {
 // launch preloads into scalar registers (struct arguments are not), and issue the
 // first weight chunks as soon as the expert id is in.
 constexpr int kDirectWaves = 2;
-template <bool DIRECT>
+template <bool DIRECT, int NT>
 __device__ __forceinline__ void gate_up(const int32_t* __restrict__ ids, const int32_t* __restrict__ nblk,
                                         const int32_t* __restrict__ blk, const int32_t* __restrict__ list,
                                         const uint8_t* __restrict__ w1, const uint16_t* __restrict__ x,
@@ -282,12 +282,14 @@ __device__ __forceinline__ void gate_up(const int32_t* __restrict__ ids, const i
                                         const MoeArgs& a) {
   __shared__ __attribute__((aligned(16))) uint8_t codes[DIRECT ? kMoeMaxHidden : 16];
   __shared__ float red[kDirectWaves];
+  // grouped: NT consecutive row blocks per wave, sharing each token-code fragment
+  static_assert(!DIRECT || NT == 1, "one row block per wave in the few-pair kernel");
   const int wave = DIRECT ? static_cast<int>(threadIdx.x >> 6) : 0;
-  const int nib = DIRECT ? I / (16 * kDirectWaves) : I / 16;   // workgroups per pair block
+  const int nib = DIRECT ? I / (16 * kDirectWaves) : I / (16 * NT);   // workgroups per pair block
   // DIRECT: the pair is the fast index (the few pairs' first row blocks go out first);
   // grouped: the row block is (measured faster there)
   const int ib = (DIRECT ? static_cast<int>(blockIdx.x) / P : static_cast<int>(blockIdx.x) % nib) *
-                     (DIRECT ? kDirectWaves : 1) + wave;
+                     (DIRECT ? kDirectWaves : NT) + wave;          // the wave's first row block
   const int gb = DIRECT ? static_cast<int>(blockIdx.x) % P : static_cast<int>(blockIdx.x) / nib;
   const int lane = threadIdx.x & 63, m16 = lane & 15, q = lane >> 4;
   int e, n, praw = 0;
@@ -315,20 +317,24 @@ __device__ __forceinline__ void gate_up(const int32_t* __restrict__ ids, const i
   const int nch = H / 128;
   const rsrc_t rw = make_rsrc(w1 + int64_t(e) * 2 * I * H, static_cast<uint32_t>(int64_t(2) * I * H));
   const rsrc_t rx = make_rsrc(x8, static_cast<uint32_t>(int64_t(a.T) * H));
-  const int g0 = ib * 16;
   // packed tiles of row block rb: 2 KB per 128-wide chunk, chunks consecutive
-  const uint32_t og = static_cast<uint32_t>(ib * nch * 2048 + 16 * lane);
-  const uint32_t ou = static_cast<uint32_t>((I / 16 + ib) * nch * 2048 + 16 * lane);
+  uint32_t og[NT], ou[NT];
   // the epilogue's scales, requested before the weight stream
   const float* s1e = a.s1 + int64_t(e) * 2 * I;
-  const f32x4 sg = *reinterpret_cast<const f32x4*>(s1e + g0 + 4 * q);
-  const f32x4 su = *reinterpret_cast<const f32x4*>(s1e + I + g0 + 4 * q);
+  f32x4 sg[NT], su[NT], accg[NT], accu[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    og[j] = static_cast<uint32_t>((ib + j) * nch * 2048 + 16 * lane);
+    ou[j] = static_cast<uint32_t>((I / 16 + ib + j) * nch * 2048 + 16 * lane);
+    sg[j] = *reinterpret_cast<const f32x4*>(s1e + (ib + j) * 16 + 4 * q);
+    su[j] = *reinterpret_cast<const f32x4*>(s1e + I + (ib + j) * 16 + 4 * q);
+    accg[j] = accu[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   int p = 0;
   uint32_t ox = 0;                                   // grouped: set once the pair is in
   float sx_t = 0.f, sdirect = 0.f;
-  f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = accg;
   constexpr int kDepth = DIRECT ? 8 : 4;   // DIRECT: few waves, each streams a whole pair's rows
-  u32x4 ag[kDepth][2], au[kDepth][2], bx[kDepth][2];
+  u32x4 ag[kDepth][NT][2], au[kDepth][NT][2], bx[kDepth][2];
   // DIRECT: the pair's token (the same for every thread), 8 bf16 per 16-byte piece,
   // H / 8 <= 512 pieces, kTokPieces per thread. Its loads go out first, so that waiting
   // for them does not wait for the weight loads issued after them, and none of this
@@ -379,13 +385,19 @@ __device__ __forceinline__ void gate_up(const int32_t* __restrict__ ids, const i
     bx[slot][0] = valid ? *reinterpret_cast<const u32x4*>(codes + 128 * c + 32 * q) : z;
     bx[slot][1] = valid ? *reinterpret_cast<const u32x4*>(codes + 128 * c + 32 * q + 16) : z;
   };
+  auto wload = [&](int slot, int c) {
+    const uint32_t st = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(2048 * c));
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      ag[slot][j][0] = wload16(rw, og[j], st);
+      ag[slot][j][1] = wload16(rw, og[j] + 1024, st);
+      au[slot][j][0] = wload16(rw, ou[j], st);
+      au[slot][j][1] = wload16(rw, ou[j] + 1024, st);
+    }
+  };
   auto load = [&](int slot, int c) {
     const uint32_t sc = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(128 * c));
-    const uint32_t st = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(2048 * c));
-    ag[slot][0] = wload16(rw, og, st);
-    ag[slot][1] = wload16(rw, og + 1024, st);
-    au[slot][0] = wload16(rw, ou, st);
-    au[slot][1] = wload16(rw, ou + 1024, st);
+    wload(slot, c);
     if constexpr (DIRECT) {
       load_codes(slot, c);
     } else {
@@ -395,20 +407,17 @@ __device__ __forceinline__ void gate_up(const int32_t* __restrict__ ids, const i
   };
   auto mul = [&](int slot) {
     const i32x8 B = operand(bx[slot][0], bx[slot][1]);
-    accg = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(ag[slot][0], ag[slot][1]), B, accg,
-                                                            0, 0, 0, 0, 0, 0);
-    accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(au[slot][0], au[slot][1]), B, accu,
-                                                            0, 0, 0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      accg[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(ag[slot][j][0], ag[slot][j][1]), B, accg[j],
+                                                                 0, 0, 0, 0, 0, 0);
+      accu[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(au[slot][j][0], au[slot][j][1]), B, accu[j],
+                                                                 0, 0, 0, 0, 0, 0);
+    }
   };
   auto wprologue = [&] {
 #pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d) {
-      const uint32_t st = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(2048 * min(d, nch - 1)));
-      ag[d][0] = wload16(rw, og, st);
-      ag[d][1] = wload16(rw, og + 1024, st);
-      au[d][0] = wload16(rw, ou, st);
-      au[d][1] = wload16(rw, ou + 1024, st);
-    }
+    for (int d = 0; d < kDepth - 1; ++d) wload(d, min(d, nch - 1));
   };
   // chunk c lives in ring slot c % kDepth (compile-time: the loop is unrolled by kDepth);
   // the loads of chunk c + kDepth - 1 go out before chunk c is multiplied. The first
@@ -449,41 +458,48 @@ __device__ __forceinline__ void gate_up(const int32_t* __restrict__ ids, const i
 #pragma unroll
   for (int d = 0; d < kDepth - 1; ++d)
     if (c + d < nch) mul(d);
-  // lane (m16, q) holds gate / up rows g0 + 4 q + i (i < 4) of pair column m16
-  const float sxm = valid ? (DIRECT ? sdirect : sx_t) : 0.f;
-  f32x4 act;
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float g = accg[i] * sxm * sg[i];
-    const float u = accu[i] * sxm * su[i];
-    act[i] = g / (1.0f + expf(-g)) * u;
-    amax = fmaxf(amax, fabsf(act[i]));
-  }
   if (!live) {
     if (ib == 0 && lane == 0 && a.err)
       __hip_atomic_fetch_or(a.err, HPA_DEVERR_MOE_EXPERT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  if (valid) *reinterpret_cast<f32x4*>(a.act + int64_t(p) * I + g0 + 4 * q) = act;
-  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-  if (valid && q == 0) a.amax[int64_t(p) * (I / 16) + ib] = amax;
+  // lane (m16, q) holds gate / up rows 16 (ib + j) + 4 q + i (i < 4) of pair column m16
+  const float sxm = valid ? (DIRECT ? sdirect : sx_t) : 0.f;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    f32x4 act;
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float g = accg[j][i] * sxm * sg[j][i];
+      const float u = accu[j][i] * sxm * su[j][i];
+      act[i] = g / (1.0f + expf(-g)) * u;
+      amax = fmaxf(amax, fabsf(act[i]));
+    }
+    if (valid) *reinterpret_cast<f32x4*>(a.act + int64_t(p) * I + (ib + j) * 16 + 4 * q) = act;
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    if (valid && q == 0) a.amax[int64_t(p) * (I / 16) + ib + j] = amax;
+  }
 }
 
 __global__ __launch_bounds__(64 * kDirectWaves) void moe_gate_up_direct_kernel(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ w1, const uint16_t* __restrict__ x, int P, int K,
     int E, int H, int I, MoeArgs a) {
-  gate_up<true>(ids, nullptr, nullptr, nullptr, w1, x, nullptr, P, K, E, H, I, a);
+  gate_up<true, 1>(ids, nullptr, nullptr, nullptr, w1, x, nullptr, P, K, E, H, I, a);
 }
 
+// NT row blocks per wave: 2 pays where pair blocks are full enough to share their token
+// codes (128 tokens, 8 pairs per expert: 129.4 -> 126.3 us per call), 1 where they hold
+// a pair or two (32 tokens: 104 against 106 us)
+template <int NT>
 __global__ __launch_bounds__(64) void moe_gate_up_kernel(const int32_t* __restrict__ nblk,
                                                          const int32_t* __restrict__ blk,
                                                          const int32_t* __restrict__ list,
                                                          const uint8_t* __restrict__ w1,
                                                          const uint8_t* __restrict__ x8, int P, int K, int H, int I,
                                                          MoeArgs a) {
-  gate_up<false>(nullptr, nblk, blk, list, w1, nullptr, x8, P, K, a.E, H, I, a);
+  gate_up<false, NT>(nullptr, nblk, blk, list, w1, nullptr, x8, P, K, a.E, H, I, a);
 }
 
 // Requantise one pair's activation row: scale = max of its slice maxima / 448.
@@ -784,8 +800,10 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   hipLaunchKernelGGL(moe_prepare_kernel, dim3(a.T + 1), dim3(kMoeThreads), 0, stream, a);
-  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.I / 16))), dim3(64), 0,
-                     stream, a.nblk, a.blk, a.list, a.w1, a.x8, a.P, a.K, a.H, a.I, a);
+  const int gt = a.P >= 4 * a.E ? 2 : 1;           // row blocks per Gate-Up wave
+  hipLaunchKernelGGL(gt == 2 ? moe_gate_up_kernel<2> : moe_gate_up_kernel<1>,
+                     dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.I / (16 * gt)))), dim3(64), 0, stream, a.nblk, a.blk,
+                     a.list, a.w1, a.x8, a.P, a.K, a.H, a.I, a);
   hipLaunchKernelGGL(moe_quant_act_kernel, dim3(a.P), dim3(kMoeThreads), 0, stream, a);
   hipLaunchKernelGGL(moe_down_kernel<kDownTiles>, dim3(static_cast<unsigned>(int64_t(a.BMAX) * (a.H / (16 * kDownTiles)))),
                      dim3(64), 0, stream, a.nblk, a.blk, a.list, a.w2, a.act8, a.P, a.H, a.I, a);
