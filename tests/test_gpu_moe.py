@@ -90,8 +90,12 @@ def inputs_f32(x_bits):
 
 
 @pytest.mark.parametrize("shape", [(1, 4, 1, 128, 128), (5, 4, 2, 256, 128), (33, 16, 8, 384, 256),
-                                   (17, 8, 3, 128, 384), (64, 32, 4, 512, 256)])
+                                   (17, 8, 3, 128, 384), (64, 32, 4, 512, 256), (40, 1, 1, 128, 256),
+                                   (300, 1024, 2, 128, 128)])
 def test_moe_small_shapes_against_oracle(shape):
+    """Every token against the oracle. The grouped kernels take two row blocks per
+    Gate-Up wave when pairs >= 4 x experts (one expert holding all 40 pairs: three pair
+    blocks), one otherwise (1024 experts: the largest routing table)."""
     T, E, K, H, I = shape
     _check(inputs.moe_workload(T, E, K, H, I, seed=sum(shape)))
 
