@@ -8,9 +8,9 @@ the MFMA sums the products (measured: within ~4e-5 of the row's largest activati
 coarser than an fp32 sum). The requantised activation codes can then differ by one
 code where a / sa lies within that distance of a rounding midpoint (measured: 9 of
 5120 codes on a 20-token call); each such code moves one of I terms of a Down row by
-at most one E4M3 step (2^-3 relative). With outputs of order 0.1-1, |gpu - ref| <= 1e-2 + 1e-2 |ref| per
-element (the bf16 rounding of the output, 2^-9 relative, included) covers these and
-fails any wrong term. The fp32 activations are checked against the oracle's at
+at most one E4M3 step (2^-3 relative). With outputs of order 0.1-1,
+|gpu - ref| <= 1e-2 + 1e-2 |ref| per element (the bf16 rounding of the output, 2^-9
+relative, included) covers these and fails any wrong term. The fp32 activations are checked against the oracle's at
 1e-4 relative to the row's largest magnitude."""
 
 import numpy as np
