@@ -32,8 +32,10 @@
 //
 // Products: A = 16 weight rows, B = 16 pairs; per 128-wide k chunk a lane (row or
 // pair m, group q) holds the 32 bytes [128 c + 32 q, + 32) of its row, both operands
-// alike, and one MFMA consumes them -- the plain sum over k. A workgroup is one wave
-// so that a batch with a few active experts still spreads over every CU.
+// alike, and one MFMA consumes them -- the sum over k (the FP8 MFMA adds the 128
+// exact products of a chunk more coarsely than an fp32 sum would). The grouped
+// kernels' workgroups are one wave each so that a batch with a few active experts
+// still spreads over every CU.
 #include "hpa_internal.hpp"
 #include "moe_internal.hpp"
 
