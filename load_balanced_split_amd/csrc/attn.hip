@@ -148,9 +148,34 @@ struct Item {
   int nsplit, pbase;     // splits of sequence s and its first partial slot (fused schedule)
 };
 
-// One step of the split combine: fold (mk, lk, ak) into the running (M, L, A).
-// Every combine of split results goes through this function, in the order fixed
-// by kMergeGroup, so all schedules produce the same bits.
+// The split combine (m: running max in log2 units, l: sum of weights, acc: weighted
+// V sum). Every combine of split results goes through the two functions below, in
+// the order fixed by kMergeGroup and kMergeBlock, so all schedules produce the same
+// bits.
+//
+// reduce(): the first cnt of N results, max-first: M = their largest m; each result
+// weighted by 2^(m - M) (independent exponentials, not a chain through a running
+// max); l and acc summed in index order. Entries at or past cnt must hold finite
+// values (callers load a copy of a valid result there); they are weighted by 0.
+template <int N>
+__device__ inline void reduce(const float (&m)[N], const float (&l)[N], const f32x4 (&a)[N], int cnt, float& M,
+                              float& L, f32x4& A) {
+  float mx = m[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) mx = fmaxf(mx, i < cnt ? m[i] : -INFINITY);
+  L = 0.f;
+  A = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float w = i < cnt ? __builtin_amdgcn_exp2f(m[i] - mx) : 0.f;
+    L = fmaf(l[i], w, L);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) A[e] = fmaf(a[i][e], w, A[e]);
+  }
+  M = mx;
+}
+
+// fold (mk, lk, ak) into the running (M, L, A): the last level, over block results
 __device__ inline void fold(float& M, float& L, f32x4& A, float mk, float lk, const f32x4& ak) {
   const float Mn = fmaxf(M, mk);
   const float fo = __builtin_amdgcn_exp2f(M - Mn), fk = __builtin_amdgcn_exp2f(mk - Mn);
@@ -749,11 +774,11 @@ struct Worker {
   // complete in memory before its workgroup counts itself in (wait for its own
   // stores, barrier, one device-scope atomic add on the counter of its group of
   // kMergeGroup consecutive splits). The workgroup that sees the group's last
-  // arrival folds the group's splits in split order -- the merge kernel's group
-  // step -- and either writes the output (one group) or stores the group result
-  // in the group's first slot and counts the group in on the sequence's counter;
-  // the workgroup that sees the last group folds the group results in group
-  // order and writes the output. Counters are returned to 0 by whoever saw the
+  // arrival reduces the group's splits -- the merge kernel's group step -- and
+  // either writes the output (one group) or stores the group result in the
+  // group's first slot and counts the group in on the sequence's counter; the
+  // workgroup that sees the last group reduces the group results block by block,
+  // folds the blocks in order and writes the output. Counters are returned to 0 by whoever saw the
   // last arrival. Nothing waits on another workgroup.
   __device__ int count_in(int32_t* ctr) {
     __builtin_amdgcn_s_waitcnt(0);          // this thread's partial stores are complete
@@ -780,7 +805,7 @@ struct Worker {
     if (threadIdx.x == 0) __hip_atomic_store(a.gctr + gslot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // Partials are read with device-coherent (sc1) buffer loads -- what the relaxed
     // agent-scope atomic loads compile to, without their ordering: every load of a
-    // fold goes out before the first is used.
+    // reduction goes out before the first is used.
     const rsrc_t racc = make_rsrc(a.part_acc, static_cast<uint32_t>(int64_t(a.slots) * G * kHeadDim * 4));
     const rsrc_t rm = make_rsrc(a.part_m, static_cast<uint32_t>(int64_t(a.slots) * G * 4));
     const rsrc_t rl = make_rsrc(a.part_l, static_cast<uint32_t>(int64_t(a.slots) * G * 4));
@@ -796,14 +821,23 @@ struct Worker {
         lk[i] = bload_f32<kPolicyAgent>(rl, static_cast<uint32_t>(r * 4));
         ak[i] = __builtin_bit_cast(f32x4, bload16<kPolicyAgent>(racc, static_cast<uint32_t>((r * kHeadDim + 4 * q4) * 4), 0));
       }
-      float M = -INFINITY, L = 0.f;
-      f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < kMergeGroup; ++i)
-        if (i < gsize) fold(M, L, A, mk[i], lk[i], ak[i]);
+      float M, L;
+      f32x4 A;
+      reduce(mk, lk, ak, gsize, M, L, A);
       if (ngrp == 1) {
+        // the block and fold levels over the one group result, as the merge kernel
+        // takes them (its block reads copies of the one written slot)
+        float bm[kMergeBlock], bl[kMergeBlock];
+        f32x4 ba[kMergeBlock];
+#pragma unroll
+        for (int j = 0; j < kMergeBlock; ++j) {
+          bm[j] = M;
+          bl[j] = L;
+          ba[j] = A;
+        }
         float FM = -INFINITY, FL = 0.f;
         f32x4 FA = f32x4{0.f, 0.f, 0.f, 0.f};
+        reduce(bm, bl, ba, 1, M, L, A);
         fold(FM, FL, FA, M, L, A);
         write_row(st, hh, q4, FL, FA);
       } else {
@@ -820,25 +854,26 @@ struct Worker {
     if (ngrp == 1) return;
     if (count_in(a.sctr + st.it.s) != ngrp - 1) return;
     if (threadIdx.x == 0) __hip_atomic_store(a.sctr + st.it.s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    constexpr int kFoldBatch = 8;     // group results loaded together, then folded in order
+    // blocks of kMergeBlock group results: loaded together, reduced, folded in order
     for (int idx = threadIdx.x; idx < G * (kHeadDim / 4); idx += kAttnThreads) {
       const int hh = idx / (kHeadDim / 4), q4 = idx % (kHeadDim / 4);
       float FM = -INFINITY, FL = 0.f;
       f32x4 FA = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int g0 = 0; g0 < ngrp; g0 += kFoldBatch) {
-        float mg[kFoldBatch], lg[kFoldBatch];
-        f32x4 ag[kFoldBatch];
+      for (int b0 = 0; b0 < ngrp; b0 += kMergeBlock) {
+        float mg[kMergeBlock], lg[kMergeBlock];
+        f32x4 ag[kMergeBlock];
 #pragma unroll
-        for (int i = 0; i < kFoldBatch; ++i) {
-          const int g = min(g0 + i, ngrp - 1);                          // in bounds; extra ones unused
+        for (int i = 0; i < kMergeBlock; ++i) {
+          const int g = min(b0 + i, ngrp - 1);                          // copies of the block's last past it
           const int64_t r = int64_t(pb + g * kMergeGroup) * G + hh;
           mg[i] = bload_f32<kPolicyAgent>(rm, static_cast<uint32_t>(r * 4));
           lg[i] = bload_f32<kPolicyAgent>(rl, static_cast<uint32_t>(r * 4));
           ag[i] = __builtin_bit_cast(f32x4, bload16<kPolicyAgent>(racc, static_cast<uint32_t>((r * kHeadDim + 4 * q4) * 4), 0));
         }
-#pragma unroll
-        for (int i = 0; i < kFoldBatch; ++i)
-          if (g0 + i < ngrp) fold(FM, FL, FA, mg[i], lg[i], ag[i]);
+        float M, L;
+        f32x4 A;
+        reduce(mg, lg, ag, min(kMergeBlock, ngrp - b0), M, L, A);
+        fold(FM, FL, FA, M, L, A);
       }
       write_row(st, hh, q4, FL, FA);
     }
@@ -1409,10 +1444,10 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
 
 // Merge: block (s, h) combines the 128 dims of head h of sequence s; blocks of
 // unsplit sequences return at once. THREADS = 32 dim-quads x LANES lane groups:
-// lane group j folds split groups j, j + LANES, ... (16 consecutive splits each, in
-// order, with fold), then the group results are folded in group order, so every
-// schedule's partials combine with the same arithmetic in the same order, whatever
-// the block size. Empty sequences get a zero row. Grids of at most one block per CU
+// lane group j reduces split groups j, j + LANES, ... (16 consecutive splits each,
+// max-first), lane group 0 reduces each block of 16 group results the same way and
+// folds the block results in order, so every schedule's partials combine with the
+// same arithmetic in the same order, whatever the block size. Empty sequences get a zero row. Grids of at most one block per CU
 // take 256 threads and issue two passes' loads together (a long sequence's many
 // splits in one round trip); larger grids take 128 threads (measured: on 1024
 // blocks the merge takes 3.7 instead of 5.5 µs, on 256 blocks 6.0 instead of 4.4).
@@ -1447,8 +1482,8 @@ __global__ __launch_bounds__(TWO ? 256 : 128) void merge_kernel(const int32_t* s
                                                                 int off_base, MergeArgs a) {
   constexpr int kMergeThreads = TWO ? 256 : 128;
   constexpr int kMergeLanes = kMergeThreads / kMergeQuads;
-  __shared__ float gm[kMergeLanes], gl[kMergeLanes];
-  __shared__ f32x4 gacc[kMergeLanes][kMergeQuads];
+  __shared__ float gm[kMergeBlock], gl[kMergeBlock];
+  __shared__ f32x4 gacc[kMergeBlock][kMergeQuads];
   const int hh = blockIdx.y, d0 = blockIdx.z * kMergeDims;
   const int s = blockIdx.x;
   // every fact this block needs is one scalar load away from its sequence index,
@@ -1492,7 +1527,7 @@ __global__ __launch_bounds__(TWO ? 256 : 128) void merge_kernel(const int32_t* s
   const int ngrp = (n + kMergeGroup - 1) / kMergeGroup;
   float FM = -INFINITY, FL = 0.f;
   f32x4 FA = f32x4{0.f, 0.f, 0.f, 0.f};
-  // A group's loads all go out before its first fold.
+  // A group's loads all go out before its reduction.
   struct GroupLoads {
     float m[kMergeGroup], l[kMergeGroup];
     f32x4 acc[kMergeGroup];
@@ -1502,46 +1537,61 @@ __global__ __launch_bounds__(TWO ? 256 : 128) void merge_kernel(const int32_t* s
     const int k0 = gg * kMergeGroup, k1 = min(n, k0 + kMergeGroup);
 #pragma unroll
     for (int i = 0; i < kMergeGroup; ++i) {
-      const int64_t r = (int64_t(base) + min(k0 + i, k1 - 1)) * G + hh;   // in bounds; extra ones unused
+      const int64_t r = (int64_t(base) + min(k0 + i, k1 - 1)) * G + hh;   // in bounds; copies of the last past k1
       gs.m[i] = part_m[r];
       gs.l[i] = part_l[r];
       gs.acc[i] = *reinterpret_cast<const f32x4*>(part_acc + r * kHeadDim + d0 + 4 * q4);
     }
   };
-  // one pass: every lane group folds its group g0 + lj, then lane group 0 folds the
-  // pass's group results in group order
-  auto fold_pass = [&](const GroupLoads& gs, int g0) {
+  // one pass: every lane group reduces its group g0 + lj into the group's LDS slot;
+  // a pass that completes a block of kMergeBlock groups (or the last group) is
+  // followed by lane group 0 reducing the block and folding it into the result
+  auto group_pass = [&](const GroupLoads& gs, int g0) {
     const int gg = g0 + lj;
-    float M = -INFINITY, L = 0.f;
-    f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
     if (gg < ngrp) {
-      const int k0 = gg * kMergeGroup, k1 = min(n, k0 + kMergeGroup);
+      float M, L;
+      f32x4 A;
+      reduce(gs.m, gs.l, gs.acc, min(kMergeGroup, n - gg * kMergeGroup), M, L, A);
+      const int slot = gg % kMergeBlock;
+      if (q4 == 0) {
+        gm[slot] = M;
+        gl[slot] = L;
+      }
+      gacc[slot][q4] = A;
+    }
+    const int gend = g0 + kMergeLanes;            // uniform
+    if (gend % kMergeBlock == 0 || gend >= ngrp) {
+      __syncthreads();
+      if (lj == 0) {
+        const int b0 = g0 / kMergeBlock * kMergeBlock, bcnt = min(kMergeBlock, ngrp - b0);
+        float bm[kMergeBlock], bl[kMergeBlock];
+        f32x4 ba[kMergeBlock];
 #pragma unroll
-      for (int i = 0; i < kMergeGroup; ++i)
-        if (k0 + i < k1) fold(M, L, A, gs.m[i], gs.l[i], gs.acc[i]);
+        for (int j = 0; j < kMergeBlock; ++j) {
+          const int jj = min(j, bcnt - 1);         // written slots only
+          bm[j] = gm[jj];
+          bl[j] = gl[jj];
+          ba[j] = gacc[jj][q4];
+        }
+        float M, L;
+        f32x4 A;
+        reduce(bm, bl, ba, bcnt, M, L, A);
+        fold(FM, FL, FA, M, L, A);
+      }
+      __syncthreads();
     }
-    if (q4 == 0) {
-      gm[lj] = M;
-      gl[lj] = L;
-    }
-    gacc[lj][q4] = A;
-    __syncthreads();
-    if (lj == 0) {
-      const int cnt = min(kMergeLanes, ngrp - g0);
-      for (int j = 0; j < cnt; ++j) fold(FM, FL, FA, gm[j], gl[j], gacc[j][q4]);
-    }
-    __syncthreads();
   };
+  static_assert(kMergeBlock % kMergeLanes == 0, "a pass never straddles two blocks");
   // TWO: the first two passes' loads go out together (up to 256 splits: one round trip)
   GroupLoads ga, gb;
   const bool two = TWO && ngrp > kMergeLanes;   // uniform
   load_group(ga, lj);
   if (two) load_group(gb, kMergeLanes + lj);
-  fold_pass(ga, 0);
-  if (two) fold_pass(gb, kMergeLanes);
+  group_pass(ga, 0);
+  if (two) group_pass(gb, kMergeLanes);
   for (int g0 = (two ? 2 : 1) * kMergeLanes; g0 < ngrp; g0 += kMergeLanes) {
     load_group(ga, g0 + lj);
-    fold_pass(ga, g0);
+    group_pass(ga, g0);
   }
   if (lj == 0) {
 #pragma unroll

@@ -121,10 +121,14 @@ inline PartialLayout partial_layout(int64_t slots, int64_t G) {
 // per (virtual worker, sequence boundary): (1 + kTailChunksPerWorker) W + S.
 inline int64_t max_slots(int64_t W, int64_t S) { return (1 + kTailChunksPerWorker) * W + S; }
 
-// Split results of one sequence are combined in a fixed order: contiguous groups
-// of kMergeGroup splits are folded in split order with a running max, then the
-// group results are folded in group order.
+// Split results of one sequence are combined in a fixed order, in three levels:
+// contiguous groups of kMergeGroup splits, each reduced max-first (the group's
+// largest running max, then every split's weight 2^(m - max), then the weighted l
+// and acc summed in split order); contiguous blocks of kMergeBlock group results,
+// reduced the same way in group order; the block results folded in block order
+// with a running max, starting from the empty state.
 constexpr int kMergeGroup = 16;
+constexpr int kMergeBlock = 16;
 
 // Everything an attention kernel needs, passed by value.
 struct AttnArgs {
