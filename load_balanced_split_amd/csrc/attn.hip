@@ -1447,10 +1447,12 @@ __global__ __launch_bounds__(kAttnThreads, kAttnBlocksPerCu) void attn_fused_ker
 // lane group j reduces split groups j, j + LANES, ... (16 consecutive splits each,
 // max-first), lane group 0 reduces each block of 16 group results the same way and
 // folds the block results in order, so every schedule's partials combine with the
-// same arithmetic in the same order, whatever the block size. Empty sequences get a zero row. Grids of at most one block per CU
-// take 256 threads and issue two passes' loads together (a long sequence's many
-// splits in one round trip); larger grids take 128 threads (measured: on 1024
-// blocks the merge takes 3.7 instead of 5.5 µs, on 256 blocks 6.0 instead of 4.4).
+// same arithmetic in the same order, whatever the block size. Empty sequences get a
+// zero row. Grids of at most one block per CU take 256 threads and issue two
+// passes' loads together (a long sequence's many splits in one round trip); larger
+// grids take 128 threads (measured: on 1024 blocks the merge takes 3.7 instead of
+// 5.5 µs, on 256 blocks 6.0 instead of 4.4; 512 threads on 256 blocks, one pass for
+// up to 256 splits: 4.0 instead of 3.6).
 constexpr int kMergeDims = kHeadDim;   // head dims per merge block (splitting them measured slower:
                                        // the merge is bound by dispatch and round trips, not bytes)
 constexpr int kMergeQuads = kMergeDims / 4;
