@@ -185,6 +185,29 @@ def test_tiny_workload():
     run_and_compare(w, "balanced", W=4, ref=ref)
 
 
+@pytest.mark.parametrize("case", ["three_blocks_256_threads", "two_blocks_128_threads"])
+def test_many_splits_combine_blocks(case):
+    """One sequence split more than 256 ways: its 16-split groups form more than one
+    block of 16 group results, so every level of the combine runs (group, block, and
+    the in-order fold of block results), in the merge kernel (256-thread blocks with
+    two-pass prefetch, or 128-thread blocks whose block spans four passes) and in the
+    single-launch in-kernel merge. Planned, fused and single-launch bits agree and
+    match the oracle. The split counts come from the CPU planner."""
+    if case == "three_blocks_256_threads":
+        lens, hq, hkv, W = [80000, 700, 3000], 8, 1, 4000
+    else:
+        lens, hq, hkv, W = [40000] + [100] * 63, 32, 4, 2000
+    plan = op.balanced_plan(lens, hkv, W, _lib.FUSED_MIN_TILES, _lib.FUSED_ITEM_COST, 0, 1, 0)
+    groups = -(-max(plan["num_splits"]) // 16)
+    two = len(lens) * hkv * (hq // hkv) <= W          # the merge kernel's 256-thread blocks
+    assert groups > 16 and two == (case == "three_blocks_256_threads"), (groups, two)
+    w = inputs.build_workload("many_splits", lens, hq, hkv, "bf16", seed=61, poison=True)
+    ref = oracle_out(w)
+    outs = {s: run_and_compare(w, s, W, ref=ref, what=case)[0] for s in ("balanced", "fused", "single")}
+    assert np.array_equal(outs["balanced"], outs["fused"])
+    assert np.array_equal(outs["balanced"], outs["single"])
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_full_size_bf16_workloads(cfg):
     w = inputs.config_workload(cfg)
