@@ -4,6 +4,7 @@
     python -m load_balanced_split_amd.profiling pmc <fetch-dir> <write-dir> <title> <command>
     python -m load_balanced_split_amd.profiling counters <title> <command> <pmc-dir>...
     python -m load_balanced_split_amd.profiling balance <title> <command> <trace-json>...
+    python -m load_balanced_split_amd.profiling budget <title> <command> <trace-json> <bench-json> <workload>
 
 `stats` reads a `--kernel-trace --stats` run (CSV or rocpd database) and prints
 per-kernel call counts and durations. `pmc` reads two `--pmc` runs (FETCH_SIZE,
@@ -17,6 +18,9 @@ the mean over dispatches of every counter they hold, with the ratios derived fro
 them (L2 hit rate, instructions per wave by kind). `balance` tabulates the
 per-CU busy time of `bench.py --trace` runs (instrumented build: per-wave
 realtime stamps and hardware CU ids of one attention launch per schedule).
+`budget` splits one workload's fused step into phases: start-up, stream and tail
+from a `bench.py --trace` run, kernel and step times from a `bench.py` run (HIP
+events on the product build).
 """
 
 import csv
@@ -201,6 +205,57 @@ def balance(title, command, files):
     return "\n".join(lines)
 
 
+def _last_json(path):
+    data = None
+    for line in open(path):
+        if line.startswith("{"):
+            data = json.loads(line)
+    if data is None:
+        raise SystemExit(f"{path}: no JSON line")
+    return data
+
+
+def budget(title, command, trace_file, bench_file, workload):
+    """Per-phase budget of a workload's fused step. The instrumented build's start-up
+    stamps wait for all of a wave's loads so far, so its phases before the first
+    K/V issue run longer than in the product build; its launch is timed on its own."""
+    t = _last_json(trace_file)
+    f = t["fused"]
+    it = f["items"]
+    e = _last_json(bench_file)["per_config"][workload]
+    fs = e["balanced_fused"]
+    step, attn, merge = fs["us_per_step"], fs["kernel_us"]["attn"], fs["kernel_us"]["merge"]
+    su = it["startup_us (range, item, length, q+page ids)"]
+    issue, end50, span = it["first_issue_after_start_us"], f["worker_end_p50_us"], f["makespan_us"]
+    stream = end50 - issue      # us
+    xcd = f.get("worker_end_mean_by_xcd_us", {})
+    rows = [
+        ("dispatch -> worker start (p50 / max)", f"{f['worker_start_p50_us']} / {f['worker_start_max_us']}",
+         "hardware dispatch of the workgroups"),
+        ("work range known", su[0], "one HBM round trip (the lengths), then the closed-form partition"),
+        ("first item's q and page ids in registers", su[3], "a second dependent round trip (page-table entries, q)"),
+        ("first K/V loads issued", issue, "the third round trip (K/V) starts here"),
+        ("K/V stream to the median worker end", round(stream, 2),
+         f"all {e['kv_bytes'] / 1e6:.1f} MB from the first issue to the last worker end: "
+         f"{e['kv_bytes'] / (span - issue) / 1e3:.0f} GB/s"),
+        ("tail: median -> last worker end", round(span - end50, 2),
+         "mean worker end by XCD " + ", ".join(f"{k}: {v}" for k, v in xcd.items())),
+        ("instrumented launch (makespan)", span, "start-up stamps wait for each wave's loads"),
+        ("attention kernel (events)", attn, "product build"),
+        ("merge kernel (events)", merge, "launch, a round trip for split counts and slot bases, "
+                                         "one for the partials, the reduction, the stores"),
+        ("gaps between the two launches", round(step - attn - merge, 2), "graph replay of attention then merge"),
+        ("step (events)", step, f"{e['kv_bytes'] / step / 1e3:.0f} GB/s of K/V, "
+                                f"{e['kv_bytes'] / step / 1e3 / 8000:.3f} of 8 TB/s; attention + merge "
+                                f"{e['attn_plus_merge_kv_frac']}"),
+    ]
+    lines = [f"# {title}", "", f"command: {command}", "",
+             f"workload {t['workload']} (W = {t['num_workers']}); times in us from the kernel's first wave",
+             "", f"{'phase':44s}{'us':>14s}  bound / note"]
+    lines += [f"{name:44s}{str(v):>14s}  {note}" for name, v, note in rows]
+    return "\n".join(lines) + "\n"
+
+
 def read_traffic(summary_path, kernel):
     """HBM bytes per launch of `kernel` from a pmc summary, or None when the summary is
     missing or was taken on different kernel sources."""
@@ -226,5 +281,7 @@ if __name__ == "__main__":
         print(counters(sys.argv[2], sys.argv[3], sys.argv[4:]))
     elif mode == "balance":
         print(balance(sys.argv[2], sys.argv[3], sys.argv[4:]))
+    elif mode == "budget":
+        print(budget(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6]), end="")
     else:
         raise SystemExit(__doc__)

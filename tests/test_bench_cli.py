@@ -72,3 +72,23 @@ def test_profiling_summaries_on_synthetic_outputs(tmp_path):
                                           ("SQ_INSTS_VALU", 400.0))])
     text = profiling.counters("t", "c", [str(c)])
     assert "l2_hit" in text and "0.750" in text and "insts_valu_per_wave" in text
+
+
+def test_phase_budget_on_synthetic_runs(tmp_path):
+    """The per-phase budget: start-up stamps and worker ends from a trace run, kernel
+    and step times from a bench run; the derived spans are differences of the two."""
+    trace = {"workload": "w", "num_workers": 4, "fused": {
+        "worker_start_p50_us": 0.5, "worker_start_max_us": 0.9, "worker_end_p50_us": 20.0, "makespan_us": 23.0,
+        "worker_end_mean_by_xcd_us": {"0": 20.0, "1": 21.0},
+        "items": {"first_issue_after_start_us": 5.0, "startup_us (range, item, length, q+page ids)": [1.5, 2.0, 2.5, 4.0]}}}
+    bench = {"per_config": {"w": {"kv_bytes": 18_000_000, "attn_plus_merge_kv_frac": 0.5,
+                                  "balanced_fused": {"us_per_step": 30.0, "kernel_us": {"attn": 24.0, "merge": 4.0}}}}}
+    tf, bf = tmp_path / "t.json", tmp_path / "b.json"
+    tf.write_text("[bench] noise\n" + json.dumps(trace) + "\n")
+    bf.write_text(json.dumps(bench) + "\n")
+    text = profiling.budget("title", "cmd", str(tf), str(bf), "w")
+    rows = {l[:44].strip(): l[44:58].strip() for l in text.splitlines() if l[:1].isalpha() and "  " in l}
+    assert rows["K/V stream to the median worker end"] == "15.0"          # 20 - 5
+    assert rows["tail: median -> last worker end"] == "3.0"               # 23 - 20
+    assert rows["gaps between the two launches"] == "2.0"                 # 30 - 24 - 4
+    assert "1000 GB/s" in text                                            # 18 MB over 23 - 5 us
