@@ -228,8 +228,8 @@ enum {
  * kernel. HPA_SCHED_BALANCED_SINGLE merges inside the persistent kernel: a
  * split's partial is written with device-coherent stores, then its workgroup
  * counts itself in on an atomic counter of its group of 16 consecutive splits;
- * the workgroup completing a group folds it (and the one completing the last
- * group folds the group results) in the merge kernel's order; no workgroup
+ * the workgroup completing a group reduces it (and the one completing the last
+ * group reduces the group results) in the merge kernel's order; no workgroup
  * waits on another, and the counters in plan_ws return to zero. All balanced
  * schedules produce identical bits. Their persistent workers claim the tail
  * chunks of the plan (hpa_plan's dynamic tail; HPA_FUSED_TAIL_DEN for the fused
