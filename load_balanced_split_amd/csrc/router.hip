@@ -529,10 +529,12 @@ __device__ inline float order_value(uint32_t o) {
   return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-template <int Q>
+// BATCH partial slices are loaded together: 8 when there are at most 8 (the tiled
+// GEMM's K ranges), so no lane issues loads of clamped copies it does not add
+template <int Q, int BATCH>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* part, int T, int E, int slots,
                                                           RouterArgs a) {
-  constexpr int kBatch = 32 / Q;
+  constexpr int kBatch = BATCH;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;                                 // whole waves
@@ -643,12 +645,15 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const dim3 grid((a.T + 3) / 4);
-  if (a.E <= 256) hipLaunchKernelGGL(router_topk_kernel<1>, grid, dim3(256), 0, stream, a.part, a.T, a.E,
-                       a.p.partial_slots, a);
-  else if (a.E <= 512) hipLaunchKernelGGL(router_topk_kernel<2>, grid, dim3(256), 0, stream, a.part, a.T, a.E,
-                       a.p.partial_slots, a);
-  else hipLaunchKernelGGL(router_topk_kernel<4>, grid, dim3(256), 0, stream, a.part, a.T, a.E,
-                       a.p.partial_slots, a);
+  const bool few = a.p.partial_slots <= 8;
+  if (a.E <= 256)
+    hipLaunchKernelGGL((few ? router_topk_kernel<1, 8> : router_topk_kernel<1, 32>), grid, dim3(256), 0, stream, a.part,
+                       a.T, a.E, a.p.partial_slots, a);
+  else if (a.E <= 512)
+    hipLaunchKernelGGL((few ? router_topk_kernel<2, 8> : router_topk_kernel<2, 16>), grid, dim3(256), 0, stream, a.part,
+                       a.T, a.E, a.p.partial_slots, a);
+  else
+    hipLaunchKernelGGL((router_topk_kernel<4, 8>), grid, dim3(256), 0, stream, a.part, a.T, a.E, a.p.partial_slots, a);
   return hipGetLastError();
 }
 
