@@ -778,8 +778,8 @@ struct Worker {
   // either writes the output (one group) or stores the group result in the
   // group's first slot and counts the group in on the sequence's counter; the
   // workgroup that sees the last group reduces the group results block by block,
-  // folds the blocks in order and writes the output. Counters are returned to 0 by whoever saw the
-  // last arrival. Nothing waits on another workgroup.
+  // folds the blocks in order and writes the output. Counters are returned to 0 by
+  // whoever saw the last arrival. Nothing waits on another workgroup.
   __device__ int count_in(int32_t* ctr) {
     __builtin_amdgcn_s_waitcnt(0);          // this thread's partial stores are complete
     __syncthreads();
