@@ -92,3 +92,14 @@ def test_phase_budget_on_synthetic_runs(tmp_path):
     assert rows["tail: median -> last worker end"] == "3.0"               # 23 - 20
     assert rows["gaps between the two launches"] == "2.0"                 # 30 - 24 - 4
     assert "1000 GB/s" in text                                            # 18 MB over 23 - 5 us
+
+
+def test_committed_traffic_summaries_match_the_kernel_sources():
+    """bench.py reports an attention launch's measured HBM bytes only from a counter
+    summary taken on the current kernel sources; every committed summary must be one."""
+    import glob
+    files = sorted(glob.glob(os.path.join(ROOT, "profiles", "attn_hbm_traffic_*.txt")))
+    assert files
+    for f in files:
+        line = next(l for l in open(f) if l.startswith("json: "))
+        assert json.loads(line[6:])["source_hash"] == profiling.source_hash(), os.path.basename(f)
