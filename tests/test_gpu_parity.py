@@ -208,6 +208,22 @@ def test_many_splits_combine_blocks(case):
     assert np.array_equal(outs["balanced"], outs["single"])
 
 
+@pytest.mark.parametrize("W,splits", [(16, 16), (17, 17), (260, 256), (261, 257)])
+def test_combine_group_and_block_boundaries(W, splits):
+    """A sequence split exactly 16, 17, 256 and 257 ways: one full group, a group and a
+    single split, one full block of 16 groups, a block and a single group (plus a
+    short request and an empty one). Planned, fused and single-launch bits agree and
+    match the oracle; the split counts come from the CPU planner."""
+    lens = [38400, 100, 0]
+    plan = op.balanced_plan(lens, 1, W, _lib.FUSED_MIN_TILES, _lib.FUSED_ITEM_COST, 0, 1, 0)
+    assert plan["num_splits"][0] == splits
+    w = inputs.build_workload("combine_edges", lens, 8, 1, "bf16", seed=62, poison=True)
+    ref = oracle_out(w)
+    outs = {s: run_and_compare(w, s, W, ref=ref, what=f"{splits} splits")[0] for s in ("balanced", "fused", "single")}
+    assert np.array_equal(outs["balanced"], outs["fused"])
+    assert np.array_equal(outs["balanced"], outs["single"])
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_full_size_bf16_workloads(cfg):
     w = inputs.config_workload(cfg)
